@@ -1,0 +1,34 @@
+"""Compile the C oracle into oracle/liboracle.so (test infrastructure).
+
+Flags keep every binary32 addition a single IEEE operation: no fast-math,
+no floating-point contraction. OpenMP only splits the loop over output
+elements."""
+
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off",
+          "-fno-strict-aliasing", "-fopenmp", "-fPIC", "-shared",
+          "-Wall", "-Wextra", "-Werror"]
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp"
+    cmd = ["gcc", *CFLAGS, SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

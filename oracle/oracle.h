@@ -1,0 +1,76 @@
+/*
+ * oracle.h -- plain CPU reference of the Atom copy/reduce collectives.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the package smoke check and the
+ * benchmark's CPU-baseline leg may load this library. It shares no code,
+ * header, table or helper with the GPU library.
+ *
+ * Semantics follow "Purlin: Separating Orchestration from the Datapath of
+ * Collectives" (arXiv 2609.36954): a collective is a naming of an input and
+ * an output layout plus a copy or a reduction (abstract); Figure 4 gives the
+ * ReduceScatter, AllGather and AllToAll layouts; Figure 6 composes AllReduce
+ * from ReduceScatter and AllGather; Table 2 names the variable-length (V)
+ * variants. The reduction is a sum.
+ *
+ * Conventions
+ *  - P virtual ranks, 1 <= P <= 64. Buffers are host arrays.
+ *  - dtype: ORC_BF16 (raw uint16 bit patterns) or ORC_F32.
+ *  - Partitioned input x_r holds P partitions of n elements: partition k is
+ *    x_r[k*n, (k+1)*n).
+ *  - A sum is accumulated in binary32 in rank order 0..P-1, starting from the
+ *    value of rank 0, and rounded once to the element type (round to nearest,
+ *    ties to even). A NaN result becomes the quiet NaN (hi16 | 0x0040).
+ *  - Return value: 0 on success, -1 on a bad argument, -2 when out of memory.
+ *  - Loops over output elements may run on several OpenMP threads; each
+ *    element's own summation order never changes.
+ */
+#ifndef ORACLE_H
+#define ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORC_BF16 = 0, ORC_F32 = 1 };
+
+/* dst[i] = round_T(f32(s_0[i]) + f32(s_1[i]) + ... + f32(s_{P-1}[i])), m elements. */
+int orc_reduce(int P, int64_t m, int dtype, const void* const* srcs, void* dst);
+
+/* ReduceScatter: y_k[i] = sum over r of x_r[k*n + i]; y_k has n elements. */
+int orc_reduce_scatter(int P, int64_t n, int dtype, const void* const* x, void* const* y);
+
+/* AllGather: out_j[k*n + i] = z_k[i] for every destination j. */
+int orc_all_gather(int P, int64_t n, int64_t esize, const void* const* z, void* const* out);
+
+/* AllToAll: out_j[r*n + i] = x_r[j*n + i]. */
+int orc_all_to_all(int P, int64_t n, int64_t esize, const void* const* x, void* const* out);
+
+/* AllToAllV over rows of row_bytes bytes. C is P*P row-major, C[r*P + j] =
+ * rows that source r sends to destination j. Source r's rows are grouped by
+ * destination in destination order; out_j receives the segments of every
+ * source in source order and holds sum_r C[r][j] rows. */
+int orc_all_to_all_v(int P, const int64_t* C, int64_t row_bytes,
+                     const void* const* x, void* const* out);
+
+/* AllReduce composed as AllGather(ReduceScatter(x)): one rounding to T. */
+int orc_all_reduce(int P, int64_t n, int dtype, const void* const* x, void* const* out);
+
+/* ReduceScatterV: partition k has cnt[k] elements on every rank; partitions
+ * are packed in k order; y_k[i] = sum over r of x_r[o_k + i], o_k = sum_{k'<k} cnt[k']. */
+int orc_reduce_scatter_v(int P, const int64_t* cnt, int dtype,
+                         const void* const* x, void* const* y);
+
+/* AllGatherV: out_j[o_k + i] = z_k[i] (in bytes: element size esize). */
+int orc_all_gather_v(int P, const int64_t* cnt, int64_t esize,
+                     const void* const* z, void* const* out);
+
+/* Number of OpenMP threads the loops above use. */
+int orc_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ORACLE_H */

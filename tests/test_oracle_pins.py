@@ -1,0 +1,388 @@
+"""Pins of the oracle to facts outside itself.
+
+* Figure 4 of arXiv 2609.36954 (three ranks): ReduceScatter, AllGather and
+  AllToAll on self-identifying tags (tests/golden/fig4_three_ranks.json).
+* Figure 6: AllReduce equals AllGather applied to ReduceScatter.
+* Closed forms: P = 1 is the identity; P identical bf16 inputs sum to the
+  library rounding of the exact product P*x; integer-valued inputs sum
+  exactly, so the result is the library rounding of the exact integer sum.
+* Rank order: inputs whose sum depends on the order of additions.
+* Recursive-summation error bound (Higham, Accuracy and Stability of
+  Numerical Algorithms, sec. 4.2) against the exact rational sum.
+* Layout invariants: AllToAll twice is the identity; AllToAllV with the
+  transposed counts undoes AllToAllV; rows are conserved.
+* Mutation checks: plausible mistakes planted in copies of the oracle on the
+  CPU fail at least one of the pins above.
+"""
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from reduce_atom_03_amd import synth
+from tests._helpers import assert_bits_equal, bits_of
+
+
+def lib_bf16(x_f32: np.ndarray) -> np.ndarray:
+    """torch's float32 -> bfloat16 (round to nearest even), as uint16 bits."""
+    t = torch.from_numpy(np.ascontiguousarray(x_f32, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_to_f32(b: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(b).view(np.int16))
+    return t.view(torch.bfloat16).to(torch.float32).numpy()
+
+
+# ------------------------------------------------------------ implementations
+
+class Impl:
+    """The collectives as a bundle, so a pin can run on mutants too."""
+
+    def __init__(self, reduce_scatter, all_gather, all_to_all, all_reduce,
+                 reduce):
+        self.reduce_scatter = reduce_scatter
+        self.all_gather = all_gather
+        self.all_to_all = all_to_all
+        self.all_reduce = all_reduce
+        self.reduce = reduce
+
+
+REAL = Impl(oracle.reduce_scatter, oracle.all_gather, oracle.all_to_all,
+            oracle.all_reduce, oracle.reduce)
+
+
+# --------------------------------------------------------------------- pins
+
+def pin_fig4(impl, golden):
+    g = golden
+    xs = [np.asarray(v, dtype=np.float32) for v in g["inputs"]]
+    ys = impl.reduce_scatter(xs)
+    for k in range(g["P"]):
+        np.testing.assert_array_equal(ys[k], np.asarray(g["reduce_scatter"][k], np.float32))
+    outs = impl.all_gather(ys)
+    for j in range(g["P"]):
+        np.testing.assert_array_equal(
+            outs[j], np.asarray(g["all_gather_of_reduce_scatter"][j], np.float32))
+    outs = impl.all_to_all(xs)
+    for j in range(g["P"]):
+        np.testing.assert_array_equal(outs[j], np.asarray(g["all_to_all"][j], np.float32))
+    outs = impl.all_reduce(xs)
+    for j in range(g["P"]):
+        np.testing.assert_array_equal(
+            outs[j], np.asarray(g["all_gather_of_reduce_scatter"][j], np.float32))
+
+
+def pin_identical_inputs(impl):
+    """P copies of one bf16 vector: every partial sum k*x is exact in binary32
+    (8 significant bits times an integer below 2**16), so the result is the
+    rounding of the exact product P*x, taken here from torch."""
+    for P in (2, 3, 5, 8):
+        x = synth.draw(11, 0, 4096, "normal", synth.BF16)
+        got = impl.reduce([x] * P)
+        exact = np.float32(P) * bf16_to_f32(x)       # exact in binary32
+        assert_bits_equal(got, lib_bf16(exact), f"identical inputs P={P}")
+
+
+def pin_integer_inputs(impl):
+    """Integer-valued inputs: every partial sum is an exact integer, so the
+    result is the exact integer sum (fp32) or its rounding (bf16)."""
+    for P in (2, 4, 8, 16):
+        g = synth.rank_rng(12, P)
+        ints = [g.integers(-128, 129, size=2048) for _ in range(P)]
+        exact = np.sum(np.stack(ints).astype(np.int64), axis=0)
+        got = impl.reduce([lib_bf16(v.astype(np.float32)) for v in ints])
+        assert_bits_equal(got, lib_bf16(exact.astype(np.float32)),
+                          f"bf16 integer sum P={P}")
+        ints = [g.integers(-(1 << 20), (1 << 20) + 1, size=2048) for _ in range(P)]
+        exact = np.sum(np.stack(ints).astype(np.int64), axis=0)
+        got = impl.reduce([v.astype(np.float32) for v in ints])
+        np.testing.assert_array_equal(got, exact.astype(np.float32))
+
+
+def pin_rank_order(impl):
+    """bf16 (1, 2^-8, 2^-24, 2^-24): in rank order each 2^-24 is half an ulp
+    of 1 + 2^-8 in binary32 and ties to even, leaving 1 + 2^-8, which ties
+    to even again in bf16: 1.0. Any other grouping first forms 2^-23 and
+    ends at 1 + 2^-7.
+    fp32 (1, 2^-24, 2^-24, 2^-24): rank order stays at 1.0; a pairwise tree
+    gives 1 + 2^-23."""
+    vals = [1.0, 2.0 ** -8, 2.0 ** -24, 2.0 ** -24]
+    xs = [lib_bf16(np.array([v], np.float32)) for v in vals]
+    got = impl.reduce(xs)
+    assert bf16_to_f32(got)[0] == 1.0
+    assert bf16_to_f32(lib_bf16(np.array([1 + 2.0 ** -7], np.float32)))[0] == 1.0078125
+    vals = [1.0, 2.0 ** -24, 2.0 ** -24, 2.0 ** -24]
+    got = impl.reduce([np.array([v], np.float32) for v in vals])
+    assert got[0] == np.float32(1.0)
+    # The same inputs through ReduceScatter at P = 4, one element per partition.
+    xs = [np.full(4, v, np.float32) for v in vals]
+    for yk in impl.reduce_scatter(xs):
+        assert yk[0] == np.float32(1.0)
+
+
+def _ulp(x: float, mbits: int) -> Fraction:
+    """Spacing of the binade holding |x| (subnormal spacing below 2^-126)."""
+    ax = abs(Fraction(x))
+    if ax == 0:
+        return Fraction(2) ** (-126 - mbits)
+    e = ax.numerator.bit_length() - ax.denominator.bit_length()
+    if Fraction(2) ** e > ax:
+        e -= 1
+    return Fraction(2) ** (max(e, -126) - mbits)
+
+
+def pin_error_bound(impl, xs, dtype, samples=2000, seed=13):
+    """|result - exact| <= gamma_{P-1} * sum|x_r| + 1/2 ulp_T(result),
+    gamma_k = k u / (1 - k u), u = 2^-24 (recursive summation)."""
+    P = len(xs)
+    ys = impl.reduce_scatter(xs)
+    n = xs[0].size // P
+    g = synth.rank_rng(seed, 0)
+    flat = g.integers(0, P * n, size=min(samples, P * n))
+    u = Fraction(1, 1 << 24)
+    gamma = (P - 1) * u / (1 - (P - 1) * u)
+    mbits = 7 if dtype == synth.BF16 else 23
+    for e in flat.tolist():
+        k, i = divmod(e, n)
+        if dtype == synth.BF16:
+            terms = [Fraction(float(bf16_to_f32(x[e:e + 1])[0])) for x in xs]
+            res = float(bf16_to_f32(ys[k][i:i + 1])[0])
+        else:
+            terms = [Fraction(float(x[e])) for x in xs]
+            res = float(ys[k][i])
+        exact = sum(terms)
+        bound = gamma * sum(abs(t) for t in terms) + _ulp(res, mbits) / 2
+        assert abs(Fraction(res) - exact) <= bound, (e, res, float(exact))
+
+
+def pin_a2a_involution(impl):
+    for P in (2, 3, 8):
+        xs = [synth.mixed_bits(14, r, P * 5, synth.BF16) for r in range(P)]
+        back = impl.all_to_all(impl.all_to_all(xs))
+        for r in range(P):
+            assert_bits_equal(back[r], xs[r], "A2A twice", nan_by_class=False)
+
+
+def pin_ar_is_ag_of_rs(impl):
+    for dtype in (synth.BF16, synth.F32):
+        P = 8
+        xs = [synth.mixed_bits(15, r, P * 33, dtype, specials=False) for r in range(P)]
+        ar = impl.all_reduce(xs)
+        ag = impl.all_gather(impl.reduce_scatter(xs))
+        for j in range(P):
+            assert_bits_equal(ar[j], ag[j], "AR vs AG(RS)", nan_by_class=False)
+            assert_bits_equal(ar[j], ar[0], "AR outputs identical", nan_by_class=False)
+
+
+# ---------------------------------------------------------- tests: real oracle
+
+@pytest.fixture(scope="module")
+def fig4(golden_dir):
+    with open(os.path.join(golden_dir, "fig4_three_ranks.json")) as f:
+        return json.load(f)
+
+
+def test_fig4_three_ranks(fig4):
+    pin_fig4(REAL, fig4)
+
+
+def test_p1_is_identity():
+    for dtype in (synth.BF16, synth.F32):
+        x = synth.mixed_bits(16, 0, 257, dtype)
+        assert_bits_equal(REAL.reduce([x]), x, "P=1 reduce")
+        assert_bits_equal(REAL.reduce_scatter([x])[0], x, "P=1 RS")
+        assert_bits_equal(REAL.all_reduce([x])[0], x, "P=1 AR")
+        assert_bits_equal(REAL.all_gather([x])[0], x, "P=1 AG", nan_by_class=False)
+        assert_bits_equal(REAL.all_to_all([x])[0], x, "P=1 A2A", nan_by_class=False)
+
+
+def test_identical_inputs_closed_form():
+    pin_identical_inputs(REAL)
+
+
+def test_integer_inputs_closed_form():
+    pin_integer_inputs(REAL)
+
+
+def test_rank_order():
+    pin_rank_order(REAL)
+
+
+def test_error_bound_c1_shape():
+    pin_error_bound(REAL, synth.c1_inputs(P=4, n=4096), synth.F32)
+
+
+def test_error_bound_c2_shape():
+    pin_error_bound(REAL, synth.ranks(2, 8, 8 * 4096, "normal", synth.BF16), synth.BF16)
+
+
+def test_error_bound_c5_shape():
+    pin_error_bound(REAL, synth.c5_inputs(1), synth.BF16)
+
+
+def test_a2a_involution():
+    pin_a2a_involution(REAL)
+
+
+def test_ar_is_ag_of_rs():
+    pin_ar_is_ag_of_rs(REAL)
+
+
+def test_a2av_inverse_and_conservation():
+    for P in (2, 5, 8):
+        C = synth.random_counts(17 + P, P, 4)
+        row = 6
+        rows = C.sum(axis=1)
+        xs = synth.tagged_rows(P, [int(t) for t in rows], row)
+        ys = oracle.all_to_all_v(xs, C, row)
+        assert sum(y.size for y in ys) == sum(x.size for x in xs)
+        for j in range(P):
+            assert ys[j].size == int(C[:, j].sum()) * row
+        back = oracle.all_to_all_v(ys, C.T.copy(), row)
+        for r in range(P):
+            assert_bits_equal(back[r], xs[r], "A2AV round trip", nan_by_class=False)
+
+
+def test_a2av_uniform_equals_a2a():
+    P, n = 4, 6
+    xs = [synth.mixed_bits(18, r, P * n, synth.BF16) for r in range(P)]
+    C = np.full((P, P), n, dtype=np.int64)
+    a = oracle.all_to_all_v(xs, C, 1)
+    b = oracle.all_to_all(xs)
+    for j in range(P):
+        assert_bits_equal(a[j], b[j], "A2AV uniform", nan_by_class=False)
+
+
+def test_v_variants_reduce_to_uniform():
+    P, n = 4, 9
+    xs = [synth.mixed_bits(19, r, P * n, synth.BF16, specials=False) for r in range(P)]
+    a = oracle.reduce_scatter_v(xs, [n] * P)
+    b = oracle.reduce_scatter(xs)
+    for k in range(P):
+        assert_bits_equal(a[k], b[k], "RSV uniform")
+    zs = [synth.mixed_bits(20, k, n, synth.BF16) for k in range(P)]
+    a = oracle.all_gather_v(zs)
+    b = oracle.all_gather(zs)
+    for j in range(P):
+        assert_bits_equal(a[j], b[j], "AGV uniform", nan_by_class=False)
+
+
+def test_counts_draw_shape():
+    C = synth.c3_counts()
+    assert C.shape == (8, 8) and (C >= 0).all()
+    assert (C.sum(axis=1) == synth.C3_TOKENS).all()
+    np.testing.assert_array_equal(C, synth.c3_counts())
+
+
+# --------------------------------------------------------------- mutations
+
+def _np_reduce(xs, reverse=False, drop_last=False, trunc=False, pairwise=False):
+    """A numpy re-implementation of reduce with one planted mistake."""
+    P = len(xs)
+    is_bf16 = xs[0].dtype == np.uint16
+    f = [bf16_to_f32(x) if is_bf16 else x.astype(np.float32) for x in xs]
+    idx = list(range(P))[::-1] if reverse else list(range(P))
+    if drop_last and P > 1:
+        idx = idx[:-1]
+    with np.errstate(over="ignore", invalid="ignore"):
+        if pairwise:
+            vals = [f[r] for r in idx]
+            while len(vals) > 1:
+                nxt = [vals[i] + vals[i + 1] for i in range(0, len(vals) - 1, 2)]
+                if len(vals) % 2:
+                    nxt.append(vals[-1])
+                vals = nxt
+            acc = vals[0]
+        else:
+            acc = f[idx[0]].copy()
+            for r in idx[1:]:
+                acc = acc + f[r]
+    if not is_bf16:
+        return acc.astype(np.float32)
+    if trunc:
+        return (acc.view(np.uint32) >> 16).astype(np.uint16)
+    return lib_bf16(acc)
+
+
+def _mutant(rs_shift=0, **kw):
+    def red(xs):
+        return _np_reduce([np.ascontiguousarray(x) for x in xs], **kw)
+
+    def rs(xs):
+        P = len(xs)
+        n = xs[0].size // P
+        return [red([x[((k + rs_shift) % P) * n:((k + rs_shift) % P + 1) * n]
+                     for x in xs]) for k in range(P)]
+
+    return Impl(rs, REAL.all_gather, REAL.all_to_all,
+                lambda xs: REAL.all_gather(rs(xs)), red)
+
+
+def _a2a_wrong(xs):
+    """Mistake: destination j takes partition r of source j (a transpose slip)."""
+    P = len(xs)
+    n = xs[0].size // P
+    return [np.concatenate([xs[j][r * n:(r + 1) * n] for r in range(P)]) for j in range(P)]
+
+
+def _ag_wrong(zs):
+    """Mistake: blocks in reverse rank order."""
+    return [np.concatenate(zs[::-1]) for _ in zs]
+
+
+def _all_pins(impl, fig4):
+    pins = [
+        lambda: pin_fig4(impl, fig4),
+        lambda: pin_identical_inputs(impl),
+        lambda: pin_integer_inputs(impl),
+        lambda: pin_rank_order(impl),
+        lambda: pin_error_bound(impl, synth.c1_inputs(P=4, n=512), synth.F32, 300),
+        lambda: pin_error_bound(impl, synth.ranks(2, 8, 8 * 256, "normal", synth.BF16),
+                                synth.BF16, 300),
+        lambda: pin_a2a_involution(impl),
+        lambda: pin_ar_is_ag_of_rs(impl),
+    ]
+    failed = 0
+    for p in pins:
+        try:
+            p()
+        except AssertionError:
+            failed += 1
+    return failed
+
+
+MUTANTS = {
+    "reverse order": dict(reverse=True),
+    "pairwise tree": dict(pairwise=True),
+    "dropped last rank": dict(drop_last=True),
+    "truncating bf16": dict(trunc=True),
+    "wrong partition": dict(rs_shift=1),
+}
+
+
+def test_real_oracle_passes_every_pin(fig4):
+    assert _all_pins(REAL, fig4) == 0
+
+
+@pytest.mark.parametrize("name", list(MUTANTS))
+def test_planted_reduce_mistakes_are_caught(name, fig4):
+    assert _all_pins(_mutant(**MUTANTS[name]), fig4) >= 1, \
+        f"mutant '{name}' passed every pin"
+
+
+@pytest.mark.parametrize("which", ["a2a transpose slip", "ag reversed"])
+def test_planted_copy_mistakes_are_caught(which, fig4):
+    impl = Impl(REAL.reduce_scatter, REAL.all_gather, REAL.all_to_all,
+                REAL.all_reduce, REAL.reduce)
+    if which == "a2a transpose slip":
+        impl.all_to_all = _a2a_wrong
+    else:
+        impl.all_gather = _ag_wrong
+        impl.all_reduce = lambda xs: _ag_wrong(REAL.reduce_scatter(xs))
+    assert _all_pins(impl, fig4) >= 1
