@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Benchmark of the Atom copy/reduce collectives on one MI355X.
+
+A step is one pass over every collective of the hot path, each on its own
+resident synthetic input (bf16):
+
+  rs8     8-way ReduceScatter, 8 x 256 MiB (N(0,1), seed 2)
+  ar      fused one-shot AllReduce of the same 8 x 256 MiB
+  a2av    AllToAllV MoE dispatch, 8 x 4096 x 7168 (Dirichlet-multinomial counts, seed 3)
+  ag_zs   AllGather, zero staging, 8 partitions of 64 MiB (U[-1,1], seed 4)
+  ag_snac AllGather through SNAC, same input, 1 MiB chunks, 4-slot ring
+  dec     decode AllReduce, 8 x b x 7168 for b in 1, 2, 4, 8, 16 (N(0,0.02), seed 5)
+  ag_8k   AllGather, zero staging, 8 partitions of 8 KiB
+
+`value` is the step's credited bytes (every input element read once, every
+output element written once, a reduced element counted with its P reads)
+over the step time, in GB/s. Per-collective GB/s and fraction of the 8 TB/s
+HBM peak, the 8 KiB AllGather p50/p99 latency and the dominant kernel's
+roofline are reported alongside; the CPU oracle is timed on the same step
+as a baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12           # MI355X HBM3E, bytes/s
+MiB = 1 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--lat-iters", type=int, default=2000,
+                    help="event-timed samples of the 8 KiB AllGather")
+    ap.add_argument("--ag-mib", type=int, default=64, help="AllGather partition size (MiB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the P ranks are P buffers in one device's HBM "
+              "and no collective crosses GPUs; run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from reduce_atom_03_amd import atom as A
+    from reduce_atom_03_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def empty(n):
+        return torch.empty(n, dtype=torch.bfloat16, device=dev)
+
+    P = 8
+    t0 = time.time()
+    log("generating inputs ...")
+    # 8-way reduce / AllReduce: 8 x 256 MiB
+    c2 = synth.c2_inputs()
+    x2 = [up(x) for x in c2]
+    del c2
+    N2 = 1 << 27
+    n2 = N2 // P
+    ys = [empty(n2) for _ in range(P)]
+    ar_out = [empty(N2) for _ in range(P)]
+    # AllToAllV
+    C3 = synth.c3_counts()
+    c3 = synth.c3_inputs()
+    x3 = [up(x) for x in c3]
+    del c3
+    R3 = C3.sum(axis=0)
+    a2a_out = [empty(int(R3[j]) * synth.HIDDEN) for j in range(P)]
+    # AllGather
+    S = args.ag_mib * MiB
+    z4 = [up(z) for z in synth.c4_inputs(S, P)]
+    ag_out = [empty(P * S // 2) for _ in range(P)]
+    snac_cfg = A.config(flags=A.F_STAGED, chunk_bytes=1 * MiB, ring_slots=4)
+    # decode AllReduce
+    x5 = {b: [up(x) for x in synth.c5_inputs(b)] for b in (1, 2, 4, 8, 16)}
+    o5 = {b: [empty(b * synth.HIDDEN) for _ in range(P)] for b in (1, 2, 4, 8, 16)}
+    # 8 KiB AllGather
+    z8 = [up(z) for z in synth.c4_inputs(8 << 10, P)]
+    o8 = [empty(P * 4096) for _ in range(P)]
+    torch.cuda.synchronize()
+    log(f"inputs resident in HBM ({time.time() - t0:.1f} s)")
+
+    # Each row: (name, callable, credited bytes per call); CUs used per row
+    # is min(workgroups launched, 256).
+    cus = {}
+
+    def plan_bytes(lin, lout, op, cfg=None, name=None):
+        st, info = A.atom_plan_query(lin, lout, op, cfg)
+        assert st == A.OK
+        cus[name] = min(256, info.num_wgs)
+        return info.credited_bytes
+
+    L = A.layout
+    rows = []
+    lay = (L(A.PARTITIONED, x2, n2), L(A.SHARD, ys, n2))
+    rows.append(("rs8", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_SUM),
+                 plan_bytes(lay[0], lay[1], A.OP_SUM, name="rs8")))
+    lay = (L(A.PARTITIONED, x2, n2), L(A.GATHERED, ar_out, n2))
+    rows.append(("ar", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_SUM),
+                 plan_bytes(lay[0], lay[1], A.OP_SUM, name="ar")))
+    lay = (L(A.PARTITIONED, x3, 0, C3, synth.HIDDEN), L(A.TRANSPOSED, a2a_out, 0, None, synth.HIDDEN))
+    rows.append(("a2av", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_COPY),
+                 plan_bytes(lay[0], lay[1], A.OP_COPY, name="a2av")))
+    lay = (L(A.SHARD, z4, S // 2), L(A.GATHERED, ag_out, S // 2))
+    rows.append(("ag_zs", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_COPY),
+                 plan_bytes(lay[0], lay[1], A.OP_COPY, name="ag_zs")))
+    rows.append(("ag_snac", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_COPY, snac_cfg),
+                 plan_bytes(lay[0], lay[1], A.OP_COPY, snac_cfg, name="ag_snac")))
+    for b in (1, 2, 4, 8, 16):
+        lay = (L(A.PARTITIONED, x5[b], b * 896), L(A.GATHERED, o5[b], b * 896))
+        rows.append((f"dec_b{b}", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_SUM),
+                     plan_bytes(lay[0], lay[1], A.OP_SUM, name=f"dec_b{b}")))
+    lay8 = (L(A.SHARD, z8, 4096), L(A.GATHERED, o8, 4096))
+    ag8 = lambda l=lay8: A.atom_collective(l[0], l[1], A.OP_COPY)
+    rows.append(("ag_8k", ag8, plan_bytes(lay8[0], lay8[1], A.OP_COPY, name="ag_8k")))
+
+    step_bytes = sum(r[2] for r in rows)
+
+    for _ in range(args.warmup):
+        for _, fn, _ in rows:
+            fn()
+    assert A.atom_sync_status() == A.OK
+
+    K = args.steps
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in rows] for _ in range(K)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(K):
+        for i, (_, fn, _) in enumerate(rows):
+            ev[k][i][0].record(stream)
+            fn()
+            ev[k][i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    assert A.atom_sync_status() == A.OK
+
+    per_row = {}
+    for i, (name, _, nbytes) in enumerate(rows):
+        ms = np.array([ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(K)])
+        avg = float(ms.mean())
+        per_row[name] = {"ms": round(avg, 5), "ms_p50": round(float(np.median(ms)), 5),
+                         "credited_bytes": int(nbytes),
+                         "GBps": round(nbytes / (avg * 1e-3) / 1e9, 1),
+                         "frac_hbm": round(nbytes / (avg * 1e-3) / HBM_PEAK, 4)}
+    ms_step = wall * 1e3 / K
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+
+    # 8 KiB AllGather latency: event pair around each launch.
+    lat = []
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.lat_iters)]
+    for a, b in pairs:
+        a.record(stream)
+        ag8()
+        b.record(stream)
+    torch.cuda.synchronize()
+    lat = np.array([a.elapsed_time(b) * 1e3 for a, b in pairs])
+    # Host-side time per call of the same launch (submission cost).
+    t = time.perf_counter()
+    for _ in range(args.lat_iters):
+        ag8()
+    host_us = (time.perf_counter() - t) / args.lat_iters * 1e6
+    torch.cuda.synchronize()
+
+    # Dominant kernel: the collective taking the most time per step.
+    dom = max(per_row, key=lambda r: per_row[r]["ms"])
+    d = per_row[dom]
+    achieved = d["credited_bytes"] / (d["ms"] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(achieved * 1e9 / HBM_PEAK, 4),
+                "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args, C3, S, step_bytes)
+
+    out = {
+        "metric": "achieved HBM GB/s (% of peak) for 8-way reduce & AllToAll; p50 us at 8 KiB",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": ("one pass over: 8-way ReduceScatter and fused AllReduce of 8 x 256 MiB bf16; "
+                         "AllToAllV 8 x 4096 x 7168 bf16 (Dirichlet-multinomial counts); "
+                         f"AllGather 8 x {args.ag_mib} MiB (zero-staging and SNAC, 1 MiB chunks, 4 slots); "
+                         "decode AllReduce 8 x b x 7168 bf16, b = 1..16; AllGather 8 x 8 KiB"),
+            "P": P, "step_credited_bytes": int(step_bytes),
+        },
+        "reduce8_GBps": per_row["rs8"]["GBps"],
+        "reduce8_frac": per_row["rs8"]["frac_hbm"],
+        "a2a_GBps": per_row["a2av"]["GBps"],
+        "a2a_frac": per_row["a2av"]["frac_hbm"],
+        "p50_us_8KiB": round(float(np.percentile(lat, 50)), 2),
+        "p99_us_8KiB": round(float(np.percentile(lat, 99)), 2),
+        "host_us_per_call_8KiB": round(host_us, 2),
+        "cus_used": cus,
+        "rows": per_row,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(args, C3, S, credited):
+    """The oracle, as it stands, on the same step (same seeds and shapes, its
+    own OpenMP threads); GB/s on the same credited bytes."""
+    import oracle
+    from reduce_atom_03_amd import synth
+    log("timing the CPU oracle ...")
+    P = 8
+    c2 = synth.c2_inputs()
+    c3 = synth.c3_inputs()
+    z4 = synth.c4_inputs(S, P)
+    x5 = {b: synth.c5_inputs(b) for b in (1, 2, 4, 8, 16)}
+    z8 = synth.c4_inputs(8 << 10, P)
+    times = []
+    for _ in range(args.cpu_reps):
+        t = time.perf_counter()
+        oracle.reduce_scatter(c2)
+        oracle.all_reduce(c2)
+        oracle.all_to_all_v(c3, C3, synth.HIDDEN)
+        oracle.all_gather(z4)
+        oracle.all_gather(z4)
+        for b in (1, 2, 4, 8, 16):
+            oracle.all_reduce(x5[b])
+        oracle.all_gather(z8)
+        times.append(time.perf_counter() - t)
+    best = float(np.median(times))
+    return {"value": round(credited / best / 1e9, 2), "unit": "GB/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"the full step (same shapes and seeds), median of {args.cpu_reps} runs, "
+                      f"{best:.2f} s per step"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,202 @@
+/*
+ * atom.h -- C ABI of libatom, the Atom copy/reduce datapath for AMD MI355X
+ * (gfx950).
+ *
+ * Source of the semantics: "Purlin: Separating Orchestration from the
+ * Datapath of Collectives" (arXiv 2609.36954).
+ *  - Abstract: a collective is a naming of an input layout and an output
+ *    layout plus a copy or a reduction; the Atom datapath provides the two
+ *    primitives copy and reduce; SNAC (Stage, Notify, And Consume) derives
+ *    the coordination from the layouts.
+ *  - Figure 4: ReduceScatter combines partition k of every input into y_k at
+ *    rank k; AllGather places every y_k in rank order at every rank;
+ *    AllToAll gives rank j partition j of every source.
+ *  - Figure 6: AllReduce composed from ReduceScatter and AllGather, chunk by
+ *    chunk.
+ *  - Table 2: the variable-length (V) variants.
+ *  - Table 3: chunk size = bandwidth-delay product rounded to the closest
+ *    power of two.
+ *
+ * Here the P "ranks" are P buffers in one GPU's memory. The reduction is a
+ * sum accumulated in binary32 in rank order 0..P-1 and rounded once to the
+ * element type (round to nearest, ties to even).
+ *
+ * General conventions (every entry point)
+ *  - Device pointers are plain HIP device addresses (hipMalloc / torch CUDA
+ *    tensors) on the current HIP device. Host arrays (pointer lists, counts)
+ *    are read during the call and copied; the caller may free them on return.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Calls are
+ *    asynchronous and stream-ordered; device buffers must stay alive until
+ *    the stream has executed the call.
+ *  - Every argument is validated on the host before any HIP call, so invalid
+ *    arguments return ATOM_ERR_INVALID_ARG / ATOM_ERR_UNSUPPORTED without
+ *    touching the GPU. No entry point aborts or throws.
+ *  - Zero-sized work returns ATOM_OK without launching anything.
+ *  - Out of place only: an output byte range that overlaps any input range
+ *    or another output range is ATOM_ERR_INVALID_ARG.
+ *  - Any element-aligned pointer is accepted. 16-byte aligned buffers whose
+ *    partitions keep 16-byte alignment take the 128-bit vector path; others
+ *    take an element-wise path with the same results.
+ *  - Calls that use the per-device workspace (the SNAC staging ring and its
+ *    flags) are ordered by their stream; two such calls on different streams
+ *    of one device must not overlap in time.
+ */
+#ifndef ATOM_H
+#define ATOM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATOM_MAX_RANKS 16
+
+typedef enum atom_status {
+    ATOM_OK = 0,
+    ATOM_ERR_INVALID_ARG = 1,  /* malformed arguments, overlap, misalignment   */
+    ATOM_ERR_UNSUPPORTED = 2,  /* a layout/op pair that names no collective    */
+    ATOM_ERR_HIP = 3,          /* a HIP runtime call or a launch failed         */
+    ATOM_ERR_TIMEOUT = 4,      /* a SNAC wait exceeded its bound on the device  */
+    ATOM_ERR_NOMEM = 5         /* the workspace could not be allocated          */
+} atom_status;
+
+typedef enum atom_dtype {
+    ATOM_DT_BF16 = 0,          /* 2-byte bfloat16 */
+    ATOM_DT_F32 = 1            /* 4-byte IEEE binary32 */
+} atom_dtype;
+
+typedef enum atom_op {
+    ATOM_OP_COPY = 0,          /* move bits unchanged */
+    ATOM_OP_SUM = 1            /* binary32 sum in rank order, rounded once */
+} atom_op;
+
+/* How P buffers name a layout (Figure 4). n = part_elems (uniform case).
+ * PARTITIONED: buffer r holds P partitions of n elements, partition k at
+ *              element k*n. V form: buffer r holds P row segments, segment j
+ *              = counts[r*P+j] rows of row_elems elements, in j order.
+ * SHARD:       buffer k holds the single partition k (n elements).
+ * GATHERED:    every buffer holds all P partitions in rank order (P*n).
+ * TRANSPOSED:  buffer j holds partition j of every source, in source order
+ *              (P*n). V form: sum_r counts[r*P+j] rows, segment of source r
+ *              first for smaller r. */
+typedef enum atom_layout_kind {
+    ATOM_LAYOUT_PARTITIONED = 0,
+    ATOM_LAYOUT_SHARD = 1,
+    ATOM_LAYOUT_GATHERED = 2,
+    ATOM_LAYOUT_TRANSPOSED = 3
+} atom_layout_kind;
+
+typedef struct atom_layout {
+    atom_layout_kind kind;
+    int32_t nranks;            /* P, 1..ATOM_MAX_RANKS; must match across in/out */
+    void* const* bufs;         /* P device pointers (host array), caller-owned */
+    int64_t part_elems;        /* n, uniform case; ignored when counts != NULL */
+    const int64_t* counts;     /* NULL, or the V-variant counts (host array):
+                                  AllToAllV: P*P row-major, counts[r*P+j] rows
+                                  from source r to destination j;
+                                  ReduceScatterV / AllGatherV: P entries,
+                                  counts[k] rows in partition k. */
+    int64_t row_elems;         /* elements per row for counts (>= 1) */
+    atom_dtype dtype;          /* must match across in/out */
+} atom_layout;
+
+/* Execution options; NULL means defaults. Zero fields take defaults too. */
+#define ATOM_F_STAGED 0x1u     /* run through SNAC with a staging ring */
+#define ATOM_F_NO_NT  0x2u     /* use ordinary (cached) stores for outputs */
+typedef struct atom_config {
+    int64_t chunk_bytes;       /* SNAC chunk (notify unit); power of two in
+                                  [64 KiB, 16 MiB]; default 1 MiB */
+    int32_t stages;            /* 16-byte vectors in flight per lane: 1, 2, 4 or 8 */
+    int32_t num_wgs;           /* workgroups to launch; 0 = derived from size */
+    uint32_t flags;            /* ATOM_F_* */
+    int32_t ring_slots;        /* SNAC ring depth D: 1..16; default 4 */
+} atom_config;
+
+/* The collective that a pair of layouts and an op names (Figure 4/6,
+ * Table 2). */
+typedef enum atom_collective_kind {
+    ATOM_COLL_NONE = 0,
+    ATOM_COLL_REDUCE_SCATTER = 1,     /* PARTITIONED -> SHARD,      SUM  */
+    ATOM_COLL_ALL_GATHER = 2,         /* SHARD       -> GATHERED,   COPY */
+    ATOM_COLL_ALL_TO_ALL = 3,         /* PARTITIONED -> TRANSPOSED, COPY */
+    ATOM_COLL_ALL_TO_ALL_V = 4,       /* same, with P*P counts           */
+    ATOM_COLL_ALL_REDUCE = 5,         /* PARTITIONED -> GATHERED,   SUM  */
+    ATOM_COLL_REDUCE_SCATTER_V = 6,   /* RS with P partition counts      */
+    ATOM_COLL_ALL_GATHER_V = 7        /* AG with P partition counts      */
+} atom_collective_kind;
+
+/* What the planner derived, for inspection without a GPU. */
+typedef struct atom_plan_info {
+    atom_collective_kind kind;
+    int32_t nranks;
+    int32_t staged;            /* 1 when the call would run through SNAC */
+    int32_t vector_path;       /* 1 when every stream is 16-byte aligned */
+    int64_t elems_per_rank_in; /* elements of each input buffer */
+    int64_t elems_per_rank_out[ATOM_MAX_RANKS];  /* elements of each output */
+    int64_t credited_bytes;    /* algorithmic bytes: each input element read
+                                  once, each output element written once */
+    int64_t chunk_bytes;       /* SNAC chunk, when staged */
+    int64_t num_chunks;        /* SNAC chunks, when staged */
+    int32_t ring_slots;
+    int32_t num_wgs;           /* workgroups the launch would use */
+} atom_plan_info;
+
+/* Atom copy (abstract: the copy primitive). Copies `bytes` bytes from src to
+ * dst on `stream`. Both are device pointers; the ranges must not overlap.
+ * Returns ATOM_OK, ATOM_ERR_INVALID_ARG (NULL with bytes > 0, overlap) or
+ * ATOM_ERR_HIP. */
+atom_status atom_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+/* Atom reduce (abstract: the reduction primitive). dst[i] = sum over r of
+ * srcs[r][i], i < count, in binary32, rank order, one rounding to dtype.
+ * srcs is a host array of nsrcs (1..ATOM_MAX_RANKS) device pointers; dst
+ * must not overlap any source. op must be ATOM_OP_SUM (ATOM_OP_COPY with
+ * nsrcs == 1 is a copy). Returns ATOM_OK, ATOM_ERR_INVALID_ARG,
+ * ATOM_ERR_UNSUPPORTED or ATOM_ERR_HIP. */
+atom_status atom_reduce(void* dst, const void* const* srcs, int32_t nsrcs,
+                        int64_t count, atom_dtype dtype, atom_op op,
+                        void* stream);
+
+/* A collective named by its layouts and op (abstract; Figures 4 and 6;
+ * Table 2). The pair (in->kind, out->kind, op) selects the collective as
+ * listed at atom_collective_kind; other pairs return ATOM_ERR_UNSUPPORTED.
+ * Both layouts must agree on nranks, dtype and (V forms) counts/row_elems;
+ * out->counts may be NULL. With cfg->flags & ATOM_F_STAGED, AllGather and
+ * AllReduce run through SNAC: chunks of cfg->chunk_bytes are staged in a
+ * ring of cfg->ring_slots slots, notified through device-memory flags and
+ * consumed by other workgroups; the staged path needs 16-byte aligned
+ * buffers and partitions (else ATOM_ERR_UNSUPPORTED). Returns ATOM_OK,
+ * ATOM_ERR_INVALID_ARG, ATOM_ERR_UNSUPPORTED, ATOM_ERR_NOMEM or
+ * ATOM_ERR_HIP. A SNAC wait that runs out on the device is reported by
+ * atom_sync_status, not here (the call returns before the kernel runs). */
+atom_status atom_collective(const atom_layout* in, const atom_layout* out,
+                            atom_op op, const atom_config* cfg, void* stream);
+
+/* Validation and planning only, no HIP call: fills *info with what
+ * atom_collective would do. Same return codes as its validation step. */
+atom_status atom_plan_query(const atom_layout* in, const atom_layout* out,
+                            atom_op op, const atom_config* cfg,
+                            atom_plan_info* info);
+
+/* Synchronizes `stream`, then reads and clears this device's SNAC error
+ * word: ATOM_ERR_TIMEOUT if a wait timed out since the last check, else
+ * ATOM_OK (ATOM_ERR_HIP if the synchronization fails). */
+atom_status atom_sync_status(void* stream);
+
+/* Table 3: bandwidth-delay product R*tau in bytes rounded to the closest
+ * power of two (ties go to the larger). Returns 0 for non-positive input. */
+int64_t atom_bdp_chunk_bytes(double bytes_per_s, double round_trip_s);
+
+/* A static, human-readable name for a status code. */
+const char* atom_status_string(atom_status s);
+
+/* Library version, (major << 16) | minor. */
+int32_t atom_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATOM_H */

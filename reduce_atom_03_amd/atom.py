@@ -1,0 +1,298 @@
+"""Python binding of libatom (include/atom.h): argument marshalling only.
+
+Every entry point of the C ABI is exposed under the same name. Tensors are
+accepted where the C side takes device pointers; the default stream is
+torch's current stream on the tensors' device. There is no fallback: if the
+shared library is missing or fails to load, importing this module raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libatom.so")
+
+MAX_RANKS = 16
+
+# atom_status
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_TIMEOUT, ERR_NOMEM = range(6)
+# atom_dtype
+DT_BF16, DT_F32 = 0, 1
+# atom_op
+OP_COPY, OP_SUM = 0, 1
+# atom_layout_kind
+PARTITIONED, SHARD, GATHERED, TRANSPOSED = 0, 1, 2, 3
+# atom_config flags
+F_STAGED, F_NO_NT = 0x1, 0x2
+# atom_collective_kind
+COLL_NONE, COLL_REDUCE_SCATTER, COLL_ALL_GATHER, COLL_ALL_TO_ALL, \
+    COLL_ALL_TO_ALL_V, COLL_ALL_REDUCE, COLL_REDUCE_SCATTER_V, \
+    COLL_ALL_GATHER_V = range(8)
+
+
+class AtomLayout(ctypes.Structure):
+    _fields_ = [
+        ("kind", ctypes.c_int),
+        ("nranks", ctypes.c_int32),
+        ("bufs", ctypes.POINTER(ctypes.c_void_p)),
+        ("part_elems", ctypes.c_int64),
+        ("counts", ctypes.POINTER(ctypes.c_int64)),
+        ("row_elems", ctypes.c_int64),
+        ("dtype", ctypes.c_int),
+    ]
+
+
+class AtomConfig(ctypes.Structure):
+    _fields_ = [
+        ("chunk_bytes", ctypes.c_int64),
+        ("stages", ctypes.c_int32),
+        ("num_wgs", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+        ("ring_slots", ctypes.c_int32),
+    ]
+
+
+class AtomPlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("kind", ctypes.c_int),
+        ("nranks", ctypes.c_int32),
+        ("staged", ctypes.c_int32),
+        ("vector_path", ctypes.c_int32),
+        ("elems_per_rank_in", ctypes.c_int64),
+        ("elems_per_rank_out", ctypes.c_int64 * MAX_RANKS),
+        ("credited_bytes", ctypes.c_int64),
+        ("chunk_bytes", ctypes.c_int64),
+        ("num_chunks", ctypes.c_int64),
+        ("ring_slots", ctypes.c_int32),
+        ("num_wgs", ctypes.c_int32),
+    ]
+
+
+EXPORTS = ("atom_copy", "atom_reduce", "atom_collective", "atom_plan_query",
+           "atom_sync_status", "atom_bdp_chunk_bytes", "atom_status_string",
+           "atom_version")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"libatom not built: {LIB_PATH} is missing (run __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp = ctypes.c_void_p
+    lib.atom_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
+    lib.atom_copy.restype = ctypes.c_int
+    lib.atom_reduce.argtypes = [vp, ctypes.POINTER(vp), ctypes.c_int32, ctypes.c_int64,
+                                ctypes.c_int, ctypes.c_int, vp]
+    lib.atom_reduce.restype = ctypes.c_int
+    lp = ctypes.POINTER(AtomLayout)
+    lib.atom_collective.argtypes = [lp, lp, ctypes.c_int, ctypes.POINTER(AtomConfig), vp]
+    lib.atom_collective.restype = ctypes.c_int
+    lib.atom_plan_query.argtypes = [lp, lp, ctypes.c_int, ctypes.POINTER(AtomConfig),
+                                    ctypes.POINTER(AtomPlanInfo)]
+    lib.atom_plan_query.restype = ctypes.c_int
+    lib.atom_sync_status.argtypes = [vp]
+    lib.atom_sync_status.restype = ctypes.c_int
+    lib.atom_bdp_chunk_bytes.argtypes = [ctypes.c_double, ctypes.c_double]
+    lib.atom_bdp_chunk_bytes.restype = ctypes.c_int64
+    lib.atom_status_string.argtypes = [ctypes.c_int]
+    lib.atom_status_string.restype = ctypes.c_char_p
+    lib.atom_version.argtypes = []
+    lib.atom_version.restype = ctypes.c_int32
+    return lib
+
+
+lib = _load()
+
+
+class AtomError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {atom_status_string(status)} ({status})")
+        self.status = status
+
+
+# ------------------------------------------------------------- marshalling
+
+def _ptr(x) -> int:
+    """Device address of a tensor (or an int address as given)."""
+    if isinstance(x, int):
+        return x
+    if x is None:
+        return 0
+    return int(x.data_ptr())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return DT_BF16
+    if t.dtype == torch.float32:
+        return DT_F32
+    raise TypeError(f"libatom handles bfloat16 and float32, not {t.dtype}")
+
+
+def _stream(stream, like=None) -> int:
+    if stream is None:
+        import torch
+        dev = like.device if like is not None and hasattr(like, "device") else None
+        return int(torch.cuda.current_stream(dev).cuda_stream)
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+def _check(status: int, what: str, check: bool) -> int:
+    if check and status != OK:
+        raise AtomError(status, what)
+    return status
+
+
+def layout(kind: int, bufs: Sequence, part_elems: int = 0, counts=None,
+           row_elems: int = 1, dtype: Optional[int] = None) -> AtomLayout:
+    """An atom_layout over P buffers (tensors or int device addresses).
+    The returned structure keeps its pointer and count arrays alive."""
+    P = len(bufs)
+    arr = (ctypes.c_void_p * max(P, 1))(*[_ptr(b) for b in bufs])
+    if dtype is None:
+        dtype = _dtype_code(bufs[0])
+    lay = AtomLayout(kind=kind, nranks=P,
+                     bufs=ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)),
+                     part_elems=int(part_elems), row_elems=int(row_elems), dtype=dtype)
+    lay._keep = [arr]
+    if counts is not None:
+        flat = [int(c) for c in (counts.reshape(-1).tolist() if hasattr(counts, "reshape")
+                                 else _flatten(counts))]
+        carr = (ctypes.c_int64 * len(flat))(*flat)
+        lay.counts = ctypes.cast(carr, ctypes.POINTER(ctypes.c_int64))
+        lay._keep.append(carr)
+    return lay
+
+
+def _flatten(c):
+    out = []
+    for x in c:
+        if isinstance(x, (list, tuple)):
+            out.extend(x)
+        else:
+            out.append(x)
+    return out
+
+
+def config(chunk_bytes: int = 0, stages: int = 0, num_wgs: int = 0, flags: int = 0,
+           ring_slots: int = 0) -> AtomConfig:
+    return AtomConfig(chunk_bytes=chunk_bytes, stages=stages, num_wgs=num_wgs,
+                      flags=flags, ring_slots=ring_slots)
+
+
+# --------------------------------------------------------- the C entry points
+
+def atom_status_string(status: int) -> str:
+    return lib.atom_status_string(int(status)).decode()
+
+
+def atom_version() -> int:
+    return int(lib.atom_version())
+
+
+def atom_bdp_chunk_bytes(bytes_per_s: float, round_trip_s: float) -> int:
+    return int(lib.atom_bdp_chunk_bytes(float(bytes_per_s), float(round_trip_s)))
+
+
+def atom_copy(dst, src, nbytes: Optional[int] = None, stream=None, check: bool = True) -> int:
+    """Copy nbytes (default: all of src) from src to dst."""
+    if nbytes is None:
+        nbytes = src.numel() * src.element_size()
+    st = lib.atom_copy(_ptr(dst), _ptr(src), int(nbytes), _stream(stream, dst))
+    return _check(st, "atom_copy", check)
+
+
+def atom_reduce(dst, srcs: Sequence, count: Optional[int] = None, dtype: Optional[int] = None,
+                op: int = OP_SUM, stream=None, check: bool = True) -> int:
+    """dst[i] = sum over r of srcs[r][i] (binary32, rank order, one rounding)."""
+    n = len(srcs)
+    arr = (ctypes.c_void_p * max(n, 1))(*[_ptr(s) for s in srcs])
+    if count is None:
+        count = dst.numel()
+    if dtype is None:
+        dtype = _dtype_code(dst)
+    st = lib.atom_reduce(_ptr(dst), ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), n,
+                         int(count), dtype, op, _stream(stream, dst))
+    return _check(st, "atom_reduce", check)
+
+
+def atom_collective(inp: AtomLayout, out: AtomLayout, op: int, cfg: Optional[AtomConfig] = None,
+                    stream=None, check: bool = True) -> int:
+    st = lib.atom_collective(ctypes.byref(inp), ctypes.byref(out), op,
+                             ctypes.byref(cfg) if cfg is not None else None,
+                             _stream(stream))
+    return _check(st, "atom_collective", check)
+
+
+def atom_plan_query(inp: AtomLayout, out: AtomLayout, op: int,
+                    cfg: Optional[AtomConfig] = None):
+    """(status, AtomPlanInfo) without touching the GPU."""
+    info = AtomPlanInfo()
+    st = lib.atom_plan_query(ctypes.byref(inp), ctypes.byref(out), op,
+                             ctypes.byref(cfg) if cfg is not None else None,
+                             ctypes.byref(info))
+    return st, info
+
+
+def atom_sync_status(stream=None) -> int:
+    return int(lib.atom_sync_status(_stream(stream)))
+
+
+# ------------------------------------------------- collectives by layout name
+
+def reduce_scatter(xs: Sequence, ys: Sequence, cfg=None, stream=None, check=True) -> int:
+    """Figure 4 (top): y_k = sum over r of partition k of x_r."""
+    n = ys[0].numel()
+    return atom_collective(layout(PARTITIONED, xs, n), layout(SHARD, ys, n), OP_SUM, cfg,
+                           _stream(stream, ys[0]), check)
+
+
+def all_gather(zs: Sequence, outs: Sequence, cfg=None, stream=None, check=True) -> int:
+    """Figure 4 (top): every output holds all z_k in rank order."""
+    n = zs[0].numel()
+    return atom_collective(layout(SHARD, zs, n), layout(GATHERED, outs, n), OP_COPY, cfg,
+                           _stream(stream, outs[0]), check)
+
+
+def all_to_all(xs: Sequence, outs: Sequence, cfg=None, stream=None, check=True) -> int:
+    """Figure 4 (bottom): output j holds partition j of every source."""
+    n = xs[0].numel() // len(xs)
+    return atom_collective(layout(PARTITIONED, xs, n), layout(TRANSPOSED, outs, n), OP_COPY,
+                           cfg, _stream(stream, outs[0]), check)
+
+
+def all_to_all_v(xs: Sequence, outs: Sequence, counts, row_elems: int, cfg=None, stream=None,
+                 check=True) -> int:
+    """Table 2 (V): counts[r][j] rows of row_elems elements from r to j."""
+    return atom_collective(layout(PARTITIONED, xs, 0, counts, row_elems),
+                           layout(TRANSPOSED, outs, 0, None, row_elems), OP_COPY, cfg,
+                           _stream(stream, outs[0]), check)
+
+
+def all_reduce(xs: Sequence, outs: Sequence, cfg=None, stream=None, check=True) -> int:
+    """Figure 6: AllGather(ReduceScatter(x)); every output is the full sum."""
+    n = xs[0].numel() // len(xs)
+    return atom_collective(layout(PARTITIONED, xs, n), layout(GATHERED, outs, n), OP_SUM, cfg,
+                           _stream(stream, outs[0]), check)
+
+
+def reduce_scatter_v(xs: Sequence, ys: Sequence, counts, row_elems: int = 1, cfg=None,
+                     stream=None, check=True) -> int:
+    """Table 2 (V): partition k holds counts[k] rows on every rank."""
+    return atom_collective(layout(PARTITIONED, xs, 0, counts, row_elems),
+                           layout(SHARD, ys, 0, None, row_elems), OP_SUM, cfg,
+                           _stream(stream, ys[0]), check)
+
+
+def all_gather_v(zs: Sequence, outs: Sequence, counts, row_elems: int = 1, cfg=None,
+                 stream=None, check=True) -> int:
+    """Table 2 (V): z_k holds counts[k] rows; outputs hold all in rank order."""
+    return atom_collective(layout(SHARD, zs, 0, counts, row_elems),
+                           layout(GATHERED, outs, 0, None, row_elems), OP_COPY, cfg,
+                           _stream(stream, outs[0]), check)

@@ -1,0 +1,175 @@
+// abi.cpp -- the extern "C" entry points of libatom (declared in atom.h).
+//
+// Each call validates and plans on the host first (plan.cpp: no HIP call
+// before an argument is known good), then launches the planned kernel on
+// the caller's stream. The SNAC workspace is allocated per device on first
+// use and kept until the process ends.
+#include <hip/hip_runtime_api.h>
+
+#include <mutex>
+
+#include "launch.hpp"
+#include "plan.hpp"
+
+namespace atom {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_ws_mutex;
+Workspace g_ws[kMaxDevices];
+
+// The workspace of the current device, with a ring of at least ring_bytes.
+atom_status workspace(int64_t ring_bytes, Workspace** out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return ATOM_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace& ws = g_ws[dev];
+    if (!ws.ready) {
+        // ready[kMaxSlots], freed[kMaxSlots], ticket, error in one block.
+        char* flags = nullptr;
+        const size_t fbytes = 2 * kMaxSlots * sizeof(unsigned long long) + 2 * sizeof(unsigned int);
+        if (hipMalloc(&flags, fbytes) != hipSuccess)
+            return ATOM_ERR_NOMEM;
+        if (hipMemset(flags, 0, fbytes) != hipSuccess) {
+            (void)hipFree(flags);
+            return ATOM_ERR_HIP;
+        }
+        ws.ready = reinterpret_cast<unsigned long long*>(flags);
+        ws.freed = ws.ready + kMaxSlots;
+        ws.ticket = reinterpret_cast<unsigned int*>(ws.freed + kMaxSlots);
+        ws.error = ws.ticket + 1;
+    }
+    if (ws.ring_bytes < ring_bytes) {
+        // Growing the ring: wait for work that may still use the old one.
+        if (ws.ring) {
+            if (hipDeviceSynchronize() != hipSuccess)
+                return ATOM_ERR_HIP;
+            (void)hipFree(ws.ring);
+            ws.ring = nullptr;
+            ws.ring_bytes = 0;
+        }
+        char* ring = nullptr;
+        if (hipMalloc(&ring, static_cast<size_t>(ring_bytes)) != hipSuccess)
+            return ATOM_ERR_NOMEM;
+        ws.ring = ring;
+        ws.ring_bytes = ring_bytes;
+    }
+    *out = &ws;
+    return ATOM_OK;
+}
+
+atom_status run(const Plan& p, void* stream)
+{
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    switch (p.exec) {
+    case EX_NONE:
+        return ATOM_OK;
+    case EX_REDUCE:
+        e = launch_reduce(p, s);
+        break;
+    case EX_COPY:
+        e = launch_copy(p, s);
+        break;
+    case EX_SNAC_AG: {
+        Workspace* ws = nullptr;
+        atom_status st = workspace(p.ring_bytes, &ws);
+        if (st != ATOM_OK)
+            return st;
+        e = launch_snac_ag(p, *ws, s);
+        break;
+    }
+    default:
+        return ATOM_ERR_UNSUPPORTED;
+    }
+    return e == hipSuccess ? ATOM_OK : ATOM_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace atom
+
+extern "C" {
+
+atom_status atom_copy(void* dst, const void* src, size_t bytes, void* stream)
+{
+    atom::Plan p;
+    atom_status st = atom::plan_copy(dst, src, bytes, nullptr, &p);
+    return st == ATOM_OK ? atom::run(p, stream) : st;
+}
+
+atom_status atom_reduce(void* dst, const void* const* srcs, int32_t nsrcs, int64_t count,
+                        atom_dtype dtype, atom_op op, void* stream)
+{
+    atom::Plan p;
+    atom_status st = atom::plan_reduce(dst, srcs, nsrcs, count, dtype, op, nullptr, &p);
+    return st == ATOM_OK ? atom::run(p, stream) : st;
+}
+
+atom_status atom_collective(const atom_layout* in, const atom_layout* out, atom_op op,
+                            const atom_config* cfg, void* stream)
+{
+    atom::Plan p;
+    atom_status st = atom::plan_collective(in, out, op, cfg, &p);
+    return st == ATOM_OK ? atom::run(p, stream) : st;
+}
+
+atom_status atom_plan_query(const atom_layout* in, const atom_layout* out, atom_op op,
+                            const atom_config* cfg, atom_plan_info* info)
+{
+    if (!info)
+        return ATOM_ERR_INVALID_ARG;
+    atom::Plan p;
+    atom_status st = atom::plan_collective(in, out, op, cfg, &p);
+    if (st == ATOM_OK)
+        atom::plan_fill_info(p, info);
+    return st;
+}
+
+atom_status atom_sync_status(void* stream)
+{
+    if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)
+        return ATOM_ERR_HIP;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= atom::kMaxDevices)
+        return ATOM_ERR_HIP;
+    unsigned int* err = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(atom::g_ws_mutex);
+        err = atom::g_ws[dev].error;
+    }
+    if (!err)
+        return ATOM_OK;   // no SNAC call has run on this device
+    unsigned int host = 0;
+    if (hipMemcpy(&host, err, sizeof host, hipMemcpyDeviceToHost) != hipSuccess)
+        return ATOM_ERR_HIP;
+    if (host == 0)
+        return ATOM_OK;
+    const unsigned int zero = 0;
+    if (hipMemcpy(err, &zero, sizeof zero, hipMemcpyHostToDevice) != hipSuccess)
+        return ATOM_ERR_HIP;
+    return ATOM_ERR_TIMEOUT;
+}
+
+int64_t atom_bdp_chunk_bytes(double bytes_per_s, double round_trip_s)
+{
+    return atom::bdp_chunk_bytes(bytes_per_s, round_trip_s);
+}
+
+const char* atom_status_string(atom_status s)
+{
+    switch (s) {
+    case ATOM_OK: return "ok";
+    case ATOM_ERR_INVALID_ARG: return "invalid argument";
+    case ATOM_ERR_UNSUPPORTED: return "unsupported layout/op combination";
+    case ATOM_ERR_HIP: return "HIP runtime error";
+    case ATOM_ERR_TIMEOUT: return "SNAC wait timed out on the device";
+    case ATOM_ERR_NOMEM: return "workspace allocation failed";
+    }
+    return "unknown status";
+}
+
+int32_t atom_version(void) { return (0 << 16) | 1; }
+
+}  // extern "C"

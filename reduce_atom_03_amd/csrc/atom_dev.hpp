@@ -1,0 +1,105 @@
+// atom_dev.hpp -- device helpers for the gfx950 Atom kernels: 128-bit
+// global loads/stores (optionally non-temporal), bf16 widening and
+// round-to-nearest-even narrowing, and the agent-scope flag operations used
+// by SNAC.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kargs.hpp"
+
+namespace atom {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// ---- 16-byte memory operations (global_load/store_dwordx4) -------------
+
+__device__ __forceinline__ u32x4 ld16(const void* p)
+{
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Streaming read: each input byte is read exactly once, so the load is
+// marked non-temporal to keep it from displacing reusable cache lines.
+__device__ __forceinline__ u32x4 ld16_stream(const void* p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ void st16(void* p, u32x4 v, bool nt)
+{
+    if (nt)
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+    else
+        *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// ---- element conversions ----------------------------------------------
+
+// bf16 -> binary32 is exact: the bf16 pattern is the upper half of the
+// binary32 pattern. A 32-bit word holds two bf16, element 0 in the low half.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// Two binary32 -> two bf16 packed in one word (element 0 low), rounded to
+// nearest with ties to even by gfx950's v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    f32x2 f = {lo, hi};
+    bf16x2 h = __builtin_convertvector(f, bf16x2);
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x)
+{
+    return static_cast<uint16_t>(pack_bf16x2(x, 0.0f) & 0xFFFFu);
+}
+
+// ---- element access for the element-wise (unaligned) paths ------------
+
+template <typename T> struct Elem;
+template <> struct Elem<uint16_t> {   // bf16 storage
+    static constexpr int kSize = 2;
+    __device__ static float load(const void* base, int64_t i)
+    {
+        return bf16_bits_to_f32(static_cast<const uint16_t*>(base)[i]);
+    }
+    __device__ static void store(void* base, int64_t i, float v)
+    {
+        static_cast<uint16_t*>(base)[i] = f32_to_bf16_bits(v);
+    }
+};
+template <> struct Elem<float> {
+    static constexpr int kSize = 4;
+    __device__ static float load(const void* base, int64_t i) { return static_cast<const float*>(base)[i]; }
+    __device__ static void store(void* base, int64_t i, float v) { static_cast<float*>(base)[i] = v; }
+};
+
+// ---- SNAC flags ----------------------------------------------------------
+// Staged data written by one workgroup is consumed by workgroups that may
+// run on another XCD (another L2). Agent-scope release/acquire makes the
+// compiler emit the L2 write-back / invalidate needed across XCDs.
+
+__device__ __forceinline__ unsigned long long flag_load_acquire(const unsigned long long* f)
+{
+    return __hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ unsigned long long flag_load_relaxed(const unsigned long long* f)
+{
+    return __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void flag_add_release(unsigned long long* f, unsigned long long v)
+{
+    __hip_atomic_fetch_add(f, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void fence_acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+__device__ __forceinline__ void fence_release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+
+}  // namespace atom

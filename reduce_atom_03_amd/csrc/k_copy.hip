@@ -1,0 +1,171 @@
+// k_copy.hip -- the Atom copy primitive on gfx950.
+//
+// "Purlin: Separating Orchestration from the Datapath of Collectives"
+// (arXiv 2609.36954), abstract: the datapath provides a copy primitive.
+// Figure 4 gives the two copy layouts served here: AllGather (every rank
+// receives every partition in rank order) and AllToAll (rank j receives
+// partition j of every source, in source order); Table 2 adds their
+// variable-length forms.
+//
+// The work is a list of segments, each a contiguous byte range of one
+// source written to one destination (AllToAll(V)) or to every destination
+// (AllGather(V), one load feeding P stores). Segment offsets are derived in
+// the kernel from the row counts carried in the kernel arguments, so a
+// launch needs no descriptor upload. Segments are cut into tiles of
+// blockDim.x * U 16-byte slots; each lane issues its U loads back to back,
+// then its stores (non-temporal: outputs are not re-read).
+#include "atom_dev.hpp"
+#include "launch.hpp"
+
+namespace atom {
+
+namespace {
+
+struct Seg {
+    const char* src;
+    int64_t dst_off;   // byte offset in the destination(s)
+    int64_t bytes;
+    int dst;           // CK_EXCHANGE: destination index; CK_FANOUT: -1 (all)
+};
+
+// Largest s with seg_tile_begin[s] <= t (empty segments own no tile).
+__device__ __forceinline__ int seg_of_tile(const CopyArgs& a, int64_t t)
+{
+    int lo = 0, hi = a.nseg - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a.seg_tile_begin[mid] <= t)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ Seg seg_geometry(const CopyArgs& a, int s)
+{
+    Seg g;
+    g.bytes = static_cast<int64_t>(a.cnt[s]) * a.row_bytes;
+    if (a.kind == CK_FANOUT) {
+        int64_t rows = 0;
+        for (int k = 0; k < s; ++k)
+            rows += a.cnt[k];
+        g.src = static_cast<const char*>(a.src[s]);
+        g.dst_off = rows * a.row_bytes;
+        g.dst = -1;
+    } else {
+        const int r = s / a.P, j = s - r * a.P;
+        int64_t src_rows = 0, dst_rows = 0;
+        for (int jj = 0; jj < j; ++jj)       // source r's rows for earlier destinations
+            src_rows += a.cnt[r * a.P + jj];
+        for (int rr = 0; rr < r; ++rr)       // earlier sources' rows for destination j
+            dst_rows += a.cnt[rr * a.P + j];
+        g.src = static_cast<const char*>(a.src[r]) + src_rows * a.row_bytes;
+        g.dst_off = dst_rows * a.row_bytes;
+        g.dst = j;
+    }
+    return g;
+}
+
+template <typename W>
+__device__ __forceinline__ void copy_units(const CopyArgs& a, const Seg& g, int64_t from, int64_t to)
+{
+    // Element-wise bytes [from, to) of the segment, in units of sizeof(W).
+    for (int64_t b = from; b < to; b += sizeof(W)) {
+        const W v = *reinterpret_cast<const W*>(g.src + b);
+        if (g.dst >= 0) {
+            *reinterpret_cast<W*>(static_cast<char*>(a.dst[g.dst]) + g.dst_off + b) = v;
+        } else {
+            for (int q = 0; q < a.ndst; ++q)
+                *reinterpret_cast<W*>(static_cast<char*>(a.dst[q]) + g.dst_off + b) = v;
+        }
+    }
+}
+
+__device__ __forceinline__ void copy_bytes(const CopyArgs& a, const Seg& g, int64_t from, int64_t to)
+{
+    switch (a.esize) {
+    case 4: copy_units<uint32_t>(a, g, from, to); break;
+    case 2: copy_units<uint16_t>(a, g, from, to); break;
+    default: copy_units<uint8_t>(a, g, from, to); break;
+    }
+}
+
+template <int U>
+__global__ __launch_bounds__(256) void k_copy_vec(const CopyArgs a)
+{
+    const int lane = threadIdx.x;
+    const int nthr = blockDim.x;
+    const bool nt = a.nt_store != 0;
+    for (int64_t t = blockIdx.x; t < a.ntiles; t += gridDim.x) {
+        const int s = seg_of_tile(a, t);
+        const Seg g = seg_geometry(a, s);
+        const int64_t b0 = (t - a.seg_tile_begin[s]) * a.tile_bytes;   // tile start in segment
+        const char* sb = g.src + b0;
+        u32x4 x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t o = b0 + static_cast<int64_t>(u * nthr + lane) * kVecBytes;
+            if (o + kVecBytes <= g.bytes)
+                x[u] = ld16_stream(sb + static_cast<uint32_t>(u * nthr + lane) * kVecBytes);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t off = static_cast<uint32_t>(u * nthr + lane) * kVecBytes;
+            const int64_t o = b0 + off;
+            if (o + kVecBytes <= g.bytes) {
+                if (g.dst >= 0) {
+                    char* db = static_cast<char*>(a.dst[g.dst]) + g.dst_off + b0;
+                    st16(db + off, x[u], nt);
+                } else {
+                    for (int q = 0; q < a.ndst; ++q) {
+                        char* db = static_cast<char*>(a.dst[q]) + g.dst_off + b0;
+                        st16(db + off, x[u], nt);
+                    }
+                }
+            } else if (o < g.bytes) {
+                copy_bytes(a, g, o, g.bytes);   // the segment's last, partial slot
+            }
+        }
+    }
+}
+
+// Element-wise variant for unaligned buffers or rows (U = 1).
+__global__ __launch_bounds__(256) void k_copy_elem(const CopyArgs a)
+{
+    const int lane = threadIdx.x;
+    const int nthr = blockDim.x;
+    for (int64_t t = blockIdx.x; t < a.ntiles; t += gridDim.x) {
+        const int s = seg_of_tile(a, t);
+        const Seg g = seg_geometry(a, s);
+        const int64_t o = (t - a.seg_tile_begin[s]) * a.tile_bytes + static_cast<int64_t>(lane) * kVecBytes;
+        if (o < g.bytes)
+            copy_bytes(a, g, o, o + kVecBytes < g.bytes ? o + kVecBytes : g.bytes);
+    }
+    (void)nthr;
+}
+
+}  // namespace
+
+hipError_t launch_copy(const Plan& p, hipStream_t stream)
+{
+    if (p.grid < 1 || p.wg < 1 || p.wg > 256 || p.ca.nseg < 1)
+        return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(p.grid)), block(p.wg);
+    if (!p.vec) {
+        if (p.U != 1)
+            return hipErrorInvalidValue;
+        k_copy_elem<<<grid, block, 0, stream>>>(p.ca);
+        return hipGetLastError();
+    }
+    switch (p.U) {
+    case 1: k_copy_vec<1><<<grid, block, 0, stream>>>(p.ca); break;
+    case 2: k_copy_vec<2><<<grid, block, 0, stream>>>(p.ca); break;
+    case 4: k_copy_vec<4><<<grid, block, 0, stream>>>(p.ca); break;
+    case 8: k_copy_vec<8><<<grid, block, 0, stream>>>(p.ca); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace atom

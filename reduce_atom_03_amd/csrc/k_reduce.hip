@@ -1,0 +1,253 @@
+// k_reduce.hip -- the Atom reduce primitive on gfx950.
+//
+// "Purlin: Separating Orchestration from the Datapath of Collectives"
+// (arXiv 2609.36954), abstract: the datapath provides a reduction primitive;
+// Figure 4 (top) defines ReduceScatter as the sum of partition k over every
+// input, and Figure 6 composes AllReduce from ReduceScatter and AllGather.
+//
+// One kernel family serves the flat reduce, ReduceScatter(V) and the fused
+// one-shot AllReduce. Each lane owns 16-byte slots (8 bf16 or 4 fp32):
+// it issues the P source loads of U slots back to back (P*U 128-bit loads
+// in flight), widens to binary32, adds in rank order 0..P-1, rounds once to
+// the element type and writes the slot to one output (ReduceScatter) or to
+// every output (AllReduce: P stores of the same registers, so all outputs
+// are bitwise identical by construction). Inputs are read once with
+// non-temporal loads; outputs are streamed with non-temporal stores.
+//
+// Work is cut into tiles of blockDim.x * U slots within a part; a
+// workgroup walks tiles with a grid stride. A part's last partial slot is
+// reduced element by element by the lane that owns it.
+#include "atom_dev.hpp"
+#include "launch.hpp"
+
+namespace atom {
+
+namespace {
+
+template <typename T> struct Acc;
+
+template <> struct Acc<uint16_t> {   // 8 bf16 per slot
+    float v[8];
+    __device__ __forceinline__ void init(u32x4 x)
+    {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            v[2 * w] = bf16_lo(x[w]);
+            v[2 * w + 1] = bf16_hi(x[w]);
+        }
+    }
+    __device__ __forceinline__ void add(u32x4 x)
+    {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            v[2 * w] = v[2 * w] + bf16_lo(x[w]);
+            v[2 * w + 1] = v[2 * w + 1] + bf16_hi(x[w]);
+        }
+    }
+    __device__ __forceinline__ u32x4 pack() const
+    {
+        u32x4 r;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            r[w] = pack_bf16x2(v[2 * w], v[2 * w + 1]);
+        return r;
+    }
+};
+
+template <> struct Acc<float> {      // 4 fp32 per slot
+    float v[4];
+    __device__ __forceinline__ void init(u32x4 x)
+    {
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            v[w] = __uint_as_float(x[w]);
+    }
+    __device__ __forceinline__ void add(u32x4 x)
+    {
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            v[w] = v[w] + __uint_as_float(x[w]);
+    }
+    __device__ __forceinline__ u32x4 pack() const
+    {
+        u32x4 r;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            r[w] = __float_as_uint(v[w]);
+        return r;
+    }
+};
+
+// Part of tile t: the last part whose first tile is <= t.
+__device__ __forceinline__ int part_of_tile(const ReduceArgs& a, int64_t t)
+{
+    int k = 0;
+    while (k + 1 < a.nparts && t >= a.tile_begin[k + 1])
+        ++k;
+    return k;
+}
+
+// Element-wise sum of element i (absolute index into every source).
+template <typename T>
+__device__ __forceinline__ float sum_elem(const ReduceArgs& a, int64_t i)
+{
+    float acc = Elem<T>::load(a.src[0], i);
+    for (int r = 1; r < a.nsrc; ++r)
+        acc = acc + Elem<T>::load(a.src[r], i);
+    return acc;
+}
+
+template <typename T>
+__device__ __forceinline__ void store_elem(const ReduceArgs& a, int k, int64_t pbeg, int64_t i,
+                                           float v)
+{
+    if (a.mode == RM_SCATTER) {
+        Elem<T>::store(a.dst[k], i - pbeg, v);
+    } else {
+        for (int q = 0; q < a.ndst; ++q)
+            Elem<T>::store(a.dst[q], i, v);
+    }
+}
+
+template <typename T, int P, int U>
+__global__ __launch_bounds__(256) void k_reduce_vec(const ReduceArgs a)
+{
+    constexpr int VE = kVecBytes / sizeof(T);
+    const int lane = threadIdx.x;
+    const int nthr = blockDim.x;
+    const bool nt = a.nt_store != 0;
+    for (int64_t t = blockIdx.x; t < a.ntiles; t += gridDim.x) {
+        const int k = part_of_tile(a, t);
+        const int64_t pbeg = a.part_off[k];
+        const int64_t plen = a.part_off[k + 1] - pbeg;
+        const int64_t nfull = plen / VE;                       // whole slots in the part
+        const int64_t slot0 = (t - a.tile_begin[k]) * nthr * U; // first slot of the tile
+        // Uniform bases of this tile; lanes add 32-bit offsets.
+        const int64_t ebase = pbeg + slot0 * VE;                // absolute element index
+        const char* sb[P];
+#pragma unroll
+        for (int r = 0; r < P; ++r)
+            sb[r] = static_cast<const char*>(a.src[r]) + ebase * sizeof(T);
+
+        u32x4 x[U][P];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t s = slot0 + u * nthr + lane;
+            const uint32_t off = static_cast<uint32_t>(u * nthr + lane) * kVecBytes;
+            if (s < nfull) {
+#pragma unroll
+                for (int r = 0; r < P; ++r)
+                    x[u][r] = ld16_stream(sb[r] + off);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t s = slot0 + u * nthr + lane;
+            const uint32_t off = static_cast<uint32_t>(u * nthr + lane) * kVecBytes;
+            if (s < nfull) {
+                Acc<T> acc;
+                acc.init(x[u][0]);
+#pragma unroll
+                for (int r = 1; r < P; ++r)
+                    acc.add(x[u][r]);
+                const u32x4 y = acc.pack();
+                if (a.mode == RM_SCATTER) {
+                    char* db = static_cast<char*>(a.dst[k]) + slot0 * kVecBytes;
+                    st16(db + off, y, nt);
+                } else {
+                    for (int q = 0; q < a.ndst; ++q) {
+                        char* db = static_cast<char*>(a.dst[q]) + ebase * sizeof(T);
+                        st16(db + off, y, nt);
+                    }
+                }
+            } else if (s == nfull && nfull * VE < plen) {
+                // The part's last, partial slot.
+                for (int64_t i = pbeg + nfull * VE; i < pbeg + plen; ++i)
+                    store_elem<T>(a, k, pbeg, i, sum_elem<T>(a, i));
+            }
+        }
+    }
+}
+
+// Element-wise variant for buffers or partitions off 16-byte alignment.
+template <typename T>
+__global__ __launch_bounds__(256) void k_reduce_elem(const ReduceArgs a)
+{
+    constexpr int VE = kVecBytes / sizeof(T);
+    const int lane = threadIdx.x;
+    const int nthr = blockDim.x;
+    for (int64_t t = blockIdx.x; t < a.ntiles; t += gridDim.x) {
+        const int k = part_of_tile(a, t);
+        const int64_t pbeg = a.part_off[k];
+        const int64_t plen = a.part_off[k + 1] - pbeg;
+        const int64_t slot0 = (t - a.tile_begin[k]) * nthr;    // U = 1 on this path
+        const int64_t s = slot0 + lane;
+        for (int e = 0; e < VE; ++e) {
+            const int64_t i = s * VE + e;
+            if (i < plen)
+                store_elem<T>(a, k, pbeg, pbeg + i, sum_elem<T>(a, pbeg + i));
+        }
+    }
+}
+
+template <typename T, int P>
+hipError_t launch_vec_p(const Plan& p, hipStream_t stream)
+{
+    const dim3 grid(static_cast<unsigned>(p.grid)), block(p.wg);
+    switch (p.U) {
+    case 1: k_reduce_vec<T, P, 1><<<grid, block, 0, stream>>>(p.ra); break;
+    case 2:
+        if constexpr (2 * P <= 32) { k_reduce_vec<T, P, 2><<<grid, block, 0, stream>>>(p.ra); break; }
+        else return hipErrorInvalidValue;
+    case 4:
+        if constexpr (4 * P <= 32) { k_reduce_vec<T, P, 4><<<grid, block, 0, stream>>>(p.ra); break; }
+        else return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_vec(const Plan& p, hipStream_t stream)
+{
+    switch (p.P) {
+    case 1: return launch_vec_p<T, 1>(p, stream);
+    case 2: return launch_vec_p<T, 2>(p, stream);
+    case 3: return launch_vec_p<T, 3>(p, stream);
+    case 4: return launch_vec_p<T, 4>(p, stream);
+    case 5: return launch_vec_p<T, 5>(p, stream);
+    case 6: return launch_vec_p<T, 6>(p, stream);
+    case 7: return launch_vec_p<T, 7>(p, stream);
+    case 8: return launch_vec_p<T, 8>(p, stream);
+    case 9: return launch_vec_p<T, 9>(p, stream);
+    case 10: return launch_vec_p<T, 10>(p, stream);
+    case 11: return launch_vec_p<T, 11>(p, stream);
+    case 12: return launch_vec_p<T, 12>(p, stream);
+    case 13: return launch_vec_p<T, 13>(p, stream);
+    case 14: return launch_vec_p<T, 14>(p, stream);
+    case 15: return launch_vec_p<T, 15>(p, stream);
+    case 16: return launch_vec_p<T, 16>(p, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_reduce(const Plan& p, hipStream_t stream)
+{
+    if (p.ra.nsrc != p.P || p.grid < 1 || p.wg < 1 || p.wg > 256)
+        return hipErrorInvalidValue;
+    if (p.vec) {
+        // The vector path takes U from {1, 2, 4}; deeper requests are clamped
+        // by the planner so that U * P 16-byte values fit in registers.
+        return p.dtype == DT_BF16 ? launch_vec<uint16_t>(p, stream) : launch_vec<float>(p, stream);
+    }
+    const dim3 grid(static_cast<unsigned>(p.grid)), block(p.wg);
+    if (p.dtype == DT_BF16)
+        k_reduce_elem<uint16_t><<<grid, block, 0, stream>>>(p.ra);
+    else
+        k_reduce_elem<float><<<grid, block, 0, stream>>>(p.ra);
+    return hipGetLastError();
+}
+
+}  // namespace atom

@@ -1,0 +1,87 @@
+// kargs.hpp -- kernel argument blocks, shared by the host planner and the
+// kernels. Plain data only (no HIP types): the planner fills them on the
+// host, the launchers pass them by value, so a launch needs no device-side
+// descriptor upload. Each block stays well under 4 KiB of kernel arguments.
+#pragma once
+
+#include <stdint.h>
+
+namespace atom {
+
+constexpr int kMaxRanks = 16;
+constexpr int kMaxSegs = kMaxRanks * kMaxRanks;
+constexpr int kVecBytes = 16;          // one global_load/store_dwordx4
+
+enum DType : int32_t { DT_BF16 = 0, DT_F32 = 1 };
+
+// Reduce family: dst = sum over nsrc sources, element-wise, in rank order.
+// Part k covers source elements [part_off[k], part_off[k+1]).
+//  SCATTER: part k is written to dst[k] + (i - part_off[k])   (ReduceScatter(V),
+//           and the flat reduce with one part)
+//  FANOUT:  part k is written to dst[q] + i for every q < ndst (AllReduce)
+enum ReduceMode : int32_t { RM_SCATTER = 0, RM_FANOUT = 1 };
+
+struct ReduceArgs {
+    const void* src[kMaxRanks];
+    void* dst[kMaxRanks];
+    int64_t part_off[kMaxRanks + 1];   // elements
+    int64_t tile_begin[kMaxRanks + 1]; // first tile of each part; [nparts] = ntiles
+    int64_t ntiles;
+    int32_t nsrc;
+    int32_t ndst;
+    int32_t nparts;
+    int32_t mode;
+    int32_t nt_store;                  // 1: non-temporal output stores
+    int32_t pad_;
+};
+
+// Copy family. Segments are derived in the kernel from row counts:
+//  CK_FANOUT:  segment k < nseg_src is source src[k], cnt[k] rows, written
+//              to every dst[q] (q < ndst) at byte offset sum_{k'<k} cnt[k']
+//              * row_bytes (AllGather(V); atom_copy is one segment).
+//  CK_EXCHANGE: segment s = r*P + j moves cnt[s] rows from src[r] (after
+//              source r's rows for every j' < j) to dst[j] (after every
+//              source r' < r's rows for j)  (AllToAll(V)).
+enum CopyKind : int32_t { CK_FANOUT = 0, CK_EXCHANGE = 1 };
+
+struct CopyArgs {
+    const void* src[kMaxRanks];
+    void* dst[kMaxRanks];
+    int64_t row_bytes;
+    int64_t ntiles;
+    int64_t tile_bytes;                // bytes per tile (multiple of 16)
+    int32_t kind;
+    int32_t P;                         // ranks (segments: P or P*P)
+    int32_t nseg;
+    int32_t ndst;                      // fan-out count (CK_FANOUT)
+    int32_t esize;                     // element bytes for the element-wise path
+    int32_t nt_store;
+    int32_t cnt[kMaxSegs];             // rows per segment
+    int32_t seg_tile_begin[kMaxSegs + 1];
+};
+
+// SNAC AllGather (and the AllGather half of a staged AllReduce).
+struct SnacArgs {
+    const void* src[kMaxRanks];        // inputs (z_k, or x_r for AllReduce)
+    void* dst[kMaxRanks];              // outputs out_j
+    char* ring;                        // D slots of chunk_bytes
+    unsigned long long* ready;         // per slot: pieces staged (monotone in a call)
+    unsigned long long* freed;         // per slot: pieces consumed
+    unsigned int* ticket;              // task counter
+    unsigned int* error;               // nonzero after a wait timed out
+    int64_t part_bytes;                // bytes of each partition
+    int64_t chunk_bytes;
+    int64_t piece_bytes;               // chunk_bytes / pieces
+    int64_t nchunks_per_part;
+    int64_t nchunks;                   // P * nchunks_per_part
+    int64_t ntasks;
+    int64_t spin_limit;                // bounded waits (iterations of a short sleep)
+    int32_t P;
+    int32_t pieces;                    // G pieces per chunk
+    int32_t slots;                     // D
+    int32_t dtype;                     // for the reducing consumer
+    int32_t nt_store;
+    int32_t pad_;
+};
+
+}  // namespace atom

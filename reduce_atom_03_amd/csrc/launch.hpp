@@ -1,0 +1,25 @@
+// launch.hpp -- host launchers of the gfx950 kernels (one per kernel family).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include "plan.hpp"
+
+namespace atom {
+
+// Per-device SNAC workspace: the staging ring, the per-slot flags, the task
+// ticket and the error word. Owned by the library, allocated on first use.
+struct Workspace {
+    char* ring = nullptr;
+    int64_t ring_bytes = 0;
+    unsigned long long* ready = nullptr;   // kMaxSlots counters
+    unsigned long long* freed = nullptr;   // kMaxSlots counters
+    unsigned int* ticket = nullptr;
+    unsigned int* error = nullptr;
+};
+
+hipError_t launch_reduce(const Plan& p, hipStream_t stream);
+hipError_t launch_copy(const Plan& p, hipStream_t stream);
+hipError_t launch_snac_ag(const Plan& p, const Workspace& ws, hipStream_t stream);
+
+}  // namespace atom

@@ -1,0 +1,600 @@
+// plan.cpp -- host planner of libatom.
+//
+// From "Purlin: Separating Orchestration from the Datapath of Collectives"
+// (arXiv 2609.36954): the abstract specifies a collective as a naming of an
+// input and an output layout plus a copy or a reduction, and Table 1's
+// "Derivability" row asks that the orchestration follow from that
+// specification with no explicit schedule. This file is that derivation:
+// the layout pair and op select the collective (Figure 4, Figure 6,
+// Table 2), the buffer shapes follow from the partition size or the counts,
+// and the launch (tiles, grid, SNAC chunks) follows from the shapes.
+#include "plan.hpp"
+
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstring>
+
+namespace atom {
+
+namespace {
+
+struct Range {
+    uintptr_t lo, hi;   // [lo, hi)
+};
+
+int esize_of(atom_dtype d)
+{
+    switch (d) {
+    case ATOM_DT_BF16: return 2;
+    case ATOM_DT_F32: return 4;
+    }
+    return 0;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// a*b without overflow, for non-negative operands; false on overflow.
+bool mul_ok(int64_t a, int64_t b, int64_t* out)
+{
+    if (a < 0 || b < 0)
+        return false;
+    if (a != 0 && b > INT64_MAX / a)
+        return false;
+    *out = a * b;
+    return true;
+}
+
+struct Cfg {
+    int64_t chunk;
+    int32_t stages;    // 0 = pick by shape
+    int64_t num_wgs;   // 0 = pick by shape
+    uint32_t flags;
+    int32_t slots;
+};
+
+atom_status read_cfg(const atom_config* cfg, Cfg* c)
+{
+    c->chunk = kDefaultChunk;
+    c->stages = 0;
+    c->num_wgs = 0;
+    c->flags = 0;
+    c->slots = kDefaultSlots;
+    if (!cfg)
+        return ATOM_OK;
+    if (cfg->chunk_bytes != 0) {
+        if (!is_pow2(cfg->chunk_bytes) || cfg->chunk_bytes < kMinChunk || cfg->chunk_bytes > kMaxChunk)
+            return ATOM_ERR_INVALID_ARG;
+        c->chunk = cfg->chunk_bytes;
+    }
+    if (cfg->stages != 0) {
+        if (cfg->stages != 1 && cfg->stages != 2 && cfg->stages != 4 && cfg->stages != 8)
+            return ATOM_ERR_INVALID_ARG;
+        c->stages = cfg->stages;
+    }
+    if (cfg->num_wgs < 0)
+        return ATOM_ERR_INVALID_ARG;
+    c->num_wgs = std::min<int64_t>(cfg->num_wgs, kMaxGrid);
+    if (cfg->flags & ~(ATOM_F_STAGED | ATOM_F_NO_NT))
+        return ATOM_ERR_INVALID_ARG;
+    c->flags = cfg->flags;
+    if (cfg->ring_slots != 0) {
+        if (cfg->ring_slots < 1 || cfg->ring_slots > kMaxSlots)
+            return ATOM_ERR_INVALID_ARG;
+        c->slots = cfg->ring_slots;
+    }
+    return ATOM_OK;
+}
+
+// Outputs must be pairwise disjoint and disjoint from every input; inputs
+// may alias each other (they are only read). Empty ranges never overlap.
+bool disjoint(const Range* ins, int nin, const Range* outs, int nout)
+{
+    for (int o = 0; o < nout; ++o) {
+        if (outs[o].lo == outs[o].hi)
+            continue;
+        for (int i = 0; i < nin; ++i)
+            if (ins[i].lo != ins[i].hi && outs[o].lo < ins[i].hi && ins[i].lo < outs[o].hi)
+                return false;
+        for (int q = o + 1; q < nout; ++q)
+            if (outs[q].lo != outs[q].hi && outs[o].lo < outs[q].hi && outs[q].lo < outs[o].hi)
+                return false;
+    }
+    return true;
+}
+
+Range range_of(const void* p, int64_t bytes)
+{
+    uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, lo + static_cast<uintptr_t>(bytes)};
+}
+
+// A buffer is usable when it is element-aligned, and non-NULL unless empty.
+bool buffer_ok(const void* p, int64_t bytes, int esize)
+{
+    if (bytes == 0)
+        return true;
+    return p != nullptr && aligned(p, static_cast<uintptr_t>(esize));
+}
+
+// Vectors in flight per lane: enough loads outstanding to cover HBM latency
+// without exceeding the register file (U * nsrc 16-byte values per lane).
+// The reduce kernel is built for U in {1, 2, 4}.
+int32_t pick_u_reduce(int nsrc, int32_t stages)
+{
+    int32_t u = stages ? std::min<int32_t>(stages, 4) : (nsrc <= 2 ? 4 : (nsrc <= 8 ? 2 : 1));
+    while (u > 1 && u * nsrc > 32)
+        u /= 2;
+    return u;
+}
+
+int32_t pick_u_copy(int32_t stages) { return stages ? stages : 4; }
+
+int64_t pick_grid(int64_t ntiles, int64_t num_wgs)
+{
+    int64_t g = num_wgs > 0 ? num_wgs : kMaxGrid;
+    return std::max<int64_t>(1, std::min(ntiles, g));
+}
+
+// Reduce family launch from part boundaries (elements).
+void build_reduce(Plan* p, int nsrc, const void* const* srcs, int ndst, void* const* dsts,
+                  int nparts, const int64_t* part_off, int32_t mode, const Cfg& c)
+{
+    ReduceArgs& a = p->ra;
+    std::memset(&a, 0, sizeof a);
+    const int es = p->esize;
+    bool vec = true;
+    for (int r = 0; r < nsrc; ++r) {
+        a.src[r] = srcs[r];
+        vec = vec && aligned(srcs[r], kVecBytes);
+    }
+    for (int q = 0; q < ndst; ++q) {
+        a.dst[q] = dsts[q];
+        vec = vec && aligned(dsts[q], kVecBytes);
+    }
+    for (int k = 0; k <= nparts; ++k) {
+        a.part_off[k] = part_off[k];
+        vec = vec && ((part_off[k] * es) % kVecBytes == 0);
+    }
+    const int64_t ve = kVecBytes / es;   // elements per 16-byte slot
+    p->vec = vec ? 1 : 0;
+    p->U = vec ? pick_u_reduce(nsrc, c.stages) : 1;
+    p->wg = 256;
+    const int64_t slots_per_tile = static_cast<int64_t>(p->wg) * p->U;
+    int64_t t = 0;
+    for (int k = 0; k < nparts; ++k) {
+        a.tile_begin[k] = t;
+        const int64_t len = part_off[k + 1] - part_off[k];
+        t += ceil_div(ceil_div(len, ve), slots_per_tile);
+    }
+    a.tile_begin[nparts] = t;
+    a.ntiles = t;
+    a.nsrc = nsrc;
+    a.ndst = ndst;
+    a.nparts = nparts;
+    a.mode = mode;
+    a.nt_store = (c.flags & ATOM_F_NO_NT) ? 0 : 1;
+    p->grid = pick_grid(t, c.num_wgs);
+    p->exec = t > 0 ? EX_REDUCE : EX_NONE;
+}
+
+// Copy family launch. cnt[s] rows of row_bytes per segment.
+void build_copy(Plan* p, int32_t kind, int P, const void* const* srcs, int nsrc,
+                void* const* dsts, int ndst, const int64_t* cnt, int nseg, int64_t row_bytes,
+                int esize, const Cfg& c)
+{
+    CopyArgs& a = p->ca;
+    std::memset(&a, 0, sizeof a);
+    bool vec = (row_bytes % kVecBytes == 0) || nseg == 1;
+    for (int r = 0; r < nsrc; ++r) {
+        a.src[r] = srcs[r];
+        vec = vec && aligned(srcs[r], kVecBytes);
+    }
+    for (int q = 0; q < ndst; ++q) {
+        a.dst[q] = dsts[q];
+        vec = vec && aligned(dsts[q], kVecBytes);
+    }
+    p->vec = vec ? 1 : 0;
+    p->U = vec ? pick_u_copy(c.stages) : 1;
+    p->wg = 256;
+    a.tile_bytes = static_cast<int64_t>(p->wg) * p->U * kVecBytes;
+    int64_t t = 0;
+    for (int s = 0; s < nseg; ++s) {
+        a.cnt[s] = static_cast<int32_t>(cnt[s]);
+        a.seg_tile_begin[s] = static_cast<int32_t>(t);
+        t += ceil_div(cnt[s] * row_bytes, a.tile_bytes);
+    }
+    a.seg_tile_begin[nseg] = static_cast<int32_t>(t);
+    a.ntiles = t;
+    a.row_bytes = row_bytes;
+    a.kind = kind;
+    a.P = P;
+    a.nseg = nseg;
+    a.ndst = ndst;
+    a.esize = esize;
+    a.nt_store = (c.flags & ATOM_F_NO_NT) ? 0 : 1;
+    p->grid = pick_grid(t, c.num_wgs);
+    p->exec = t > 0 ? EX_COPY : EX_NONE;
+}
+
+// Limit that keeps per-segment tile indices in 32 bits.
+constexpr int64_t kMaxTiles = INT32_MAX;
+
+}  // namespace
+
+// --------------------------------------------------------------------------
+
+atom_status plan_copy(void* dst, const void* src, size_t bytes, const atom_config* cfg, Plan* p)
+{
+    Cfg c;
+    atom_status st = read_cfg(cfg, &c);
+    if (st != ATOM_OK)
+        return st;
+    if (bytes > static_cast<size_t>(INT64_MAX / 2))
+        return ATOM_ERR_INVALID_ARG;
+    const int64_t b = static_cast<int64_t>(bytes);
+    if (b > 0 && (dst == nullptr || src == nullptr))
+        return ATOM_ERR_INVALID_ARG;
+    Range ri = range_of(src, b), ro = range_of(dst, b);
+    if (!disjoint(&ri, 1, &ro, 1))
+        return ATOM_ERR_INVALID_ARG;
+    if (c.flags & ATOM_F_STAGED)
+        return ATOM_ERR_UNSUPPORTED;
+    *p = Plan();
+    p->kind = ATOM_COLL_NONE;
+    p->P = 1;
+    uintptr_t bits = reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src) |
+                     static_cast<uintptr_t>(b);
+    int es = (bits & 3) == 0 ? 4 : ((bits & 1) == 0 ? 2 : 1);
+    p->esize = es;
+    p->in_elems = b;
+    p->out_elems[0] = b;
+    p->credited_bytes = 2 * b;
+    if (b == 0)
+        return ATOM_OK;
+    if (ceil_div(b, 256 * kVecBytes) > kMaxTiles)
+        return ATOM_ERR_INVALID_ARG;
+    const void* srcs[1] = {src};
+    void* dsts[1] = {dst};
+    int64_t one = 1;
+    build_copy(p, CK_FANOUT, 1, srcs, 1, dsts, 1, &one, 1, b, es, c);
+    return ATOM_OK;
+}
+
+atom_status plan_reduce(void* dst, const void* const* srcs, int32_t nsrcs, int64_t count,
+                        atom_dtype dtype, atom_op op, const atom_config* cfg, Plan* p)
+{
+    Cfg c;
+    atom_status st = read_cfg(cfg, &c);
+    if (st != ATOM_OK)
+        return st;
+    const int es = esize_of(dtype);
+    if (es == 0 || srcs == nullptr || nsrcs < 1 || nsrcs > kMaxRanks || count < 0)
+        return ATOM_ERR_INVALID_ARG;
+    if (op != ATOM_OP_SUM && op != ATOM_OP_COPY)
+        return ATOM_ERR_INVALID_ARG;
+    if (op == ATOM_OP_COPY && nsrcs != 1)
+        return ATOM_ERR_UNSUPPORTED;
+    if (c.flags & ATOM_F_STAGED)
+        return ATOM_ERR_UNSUPPORTED;
+    int64_t bytes;
+    if (!mul_ok(count, es, &bytes))
+        return ATOM_ERR_INVALID_ARG;
+    Range ins[kMaxRanks];
+    for (int r = 0; r < nsrcs; ++r) {
+        if (!buffer_ok(srcs[r], bytes, es))
+            return ATOM_ERR_INVALID_ARG;
+        ins[r] = range_of(srcs[r], bytes);
+    }
+    if (!buffer_ok(dst, bytes, es))
+        return ATOM_ERR_INVALID_ARG;
+    Range ro = range_of(dst, bytes);
+    if (!disjoint(ins, nsrcs, &ro, 1))
+        return ATOM_ERR_INVALID_ARG;
+    *p = Plan();
+    p->kind = ATOM_COLL_NONE;
+    p->dtype = dtype == ATOM_DT_BF16 ? DT_BF16 : DT_F32;
+    p->esize = es;
+    p->P = nsrcs;
+    p->in_elems = count;
+    p->out_elems[0] = count;
+    p->credited_bytes = (static_cast<int64_t>(nsrcs) + 1) * bytes;
+    if (count == 0)
+        return ATOM_OK;
+    int64_t off[2] = {0, count};
+    void* dsts[1] = {dst};
+    build_reduce(p, nsrcs, srcs, 1, dsts, 1, off, RM_SCATTER, c);
+    return ATOM_OK;
+}
+
+atom_status plan_collective(const atom_layout* in, const atom_layout* out, atom_op op,
+                            const atom_config* cfg, Plan* p)
+{
+    Cfg c;
+    atom_status st = read_cfg(cfg, &c);
+    if (st != ATOM_OK)
+        return st;
+    if (!in || !out)
+        return ATOM_ERR_INVALID_ARG;
+    const int P = in->nranks;
+    if (P < 1 || P > kMaxRanks || out->nranks != P)
+        return ATOM_ERR_INVALID_ARG;
+    if (!in->bufs || !out->bufs)
+        return ATOM_ERR_INVALID_ARG;
+    const int es = esize_of(in->dtype);
+    if (es == 0 || out->dtype != in->dtype)
+        return ATOM_ERR_INVALID_ARG;
+    if (op != ATOM_OP_COPY && op != ATOM_OP_SUM)
+        return ATOM_ERR_INVALID_ARG;
+    auto kind_ok = [](atom_layout_kind k) {
+        return k == ATOM_LAYOUT_PARTITIONED || k == ATOM_LAYOUT_SHARD ||
+               k == ATOM_LAYOUT_GATHERED || k == ATOM_LAYOUT_TRANSPOSED;
+    };
+    if (!kind_ok(in->kind) || !kind_ok(out->kind))
+        return ATOM_ERR_INVALID_ARG;
+
+    // ---- which collective does the naming describe?
+    const bool v = in->counts != nullptr;
+    atom_collective_kind kind = ATOM_COLL_NONE;
+    if (in->kind == ATOM_LAYOUT_PARTITIONED && out->kind == ATOM_LAYOUT_SHARD && op == ATOM_OP_SUM)
+        kind = v ? ATOM_COLL_REDUCE_SCATTER_V : ATOM_COLL_REDUCE_SCATTER;
+    else if (in->kind == ATOM_LAYOUT_SHARD && out->kind == ATOM_LAYOUT_GATHERED && op == ATOM_OP_COPY)
+        kind = v ? ATOM_COLL_ALL_GATHER_V : ATOM_COLL_ALL_GATHER;
+    else if (in->kind == ATOM_LAYOUT_PARTITIONED && out->kind == ATOM_LAYOUT_TRANSPOSED &&
+             op == ATOM_OP_COPY)
+        kind = v ? ATOM_COLL_ALL_TO_ALL_V : ATOM_COLL_ALL_TO_ALL;
+    else if (in->kind == ATOM_LAYOUT_PARTITIONED && out->kind == ATOM_LAYOUT_GATHERED &&
+             op == ATOM_OP_SUM && !v)
+        kind = ATOM_COLL_ALL_REDUCE;
+    if (kind == ATOM_COLL_NONE)
+        return ATOM_ERR_UNSUPPORTED;
+
+    // ---- counts (V variants) or the uniform partition size
+    const int ncnt = (kind == ATOM_COLL_ALL_TO_ALL_V) ? P * P : P;
+    int64_t cnt[kMaxSegs];
+    int64_t row = 1;
+    int64_t n = 0;
+    if (v) {
+        if (in->row_elems < 1 || out->row_elems != in->row_elems)
+            return ATOM_ERR_INVALID_ARG;
+        row = in->row_elems;
+        for (int e = 0; e < ncnt; ++e) {
+            cnt[e] = in->counts[e];
+            if (cnt[e] < 0 || cnt[e] > INT32_MAX)
+                return ATOM_ERR_INVALID_ARG;
+            if (out->counts && out->counts[e] != cnt[e])
+                return ATOM_ERR_INVALID_ARG;
+        }
+    } else {
+        if (out->counts)
+            return ATOM_ERR_INVALID_ARG;
+        n = in->part_elems;
+        if (n < 0 || out->part_elems != n)
+            return ATOM_ERR_INVALID_ARG;
+    }
+    int64_t row_bytes;
+    if (!mul_ok(row, es, &row_bytes))
+        return ATOM_ERR_INVALID_ARG;
+
+    // ---- per-buffer element counts
+    int64_t in_el[kMaxRanks], out_el[kMaxRanks];
+    int64_t total = 0;   // elements of one "P*n" index space (per rank)
+    if (!v) {
+        if (!mul_ok(n, P, &total))
+            return ATOM_ERR_INVALID_ARG;
+    }
+    int64_t tmp;
+    switch (kind) {
+    case ATOM_COLL_REDUCE_SCATTER:
+        for (int r = 0; r < P; ++r) { in_el[r] = total; out_el[r] = n; }
+        break;
+    case ATOM_COLL_ALL_GATHER:
+        for (int r = 0; r < P; ++r) { in_el[r] = n; out_el[r] = total; }
+        break;
+    case ATOM_COLL_ALL_TO_ALL:
+    case ATOM_COLL_ALL_REDUCE:
+        for (int r = 0; r < P; ++r) { in_el[r] = total; out_el[r] = total; }
+        break;
+    case ATOM_COLL_REDUCE_SCATTER_V:
+    case ATOM_COLL_ALL_GATHER_V: {
+        int64_t rows = 0;
+        for (int k = 0; k < P; ++k)
+            rows += cnt[k];
+        if (!mul_ok(rows, row, &total))
+            return ATOM_ERR_INVALID_ARG;
+        for (int k = 0; k < P; ++k) {
+            if (!mul_ok(cnt[k], row, &tmp))
+                return ATOM_ERR_INVALID_ARG;
+            if (kind == ATOM_COLL_REDUCE_SCATTER_V) { in_el[k] = total; out_el[k] = tmp; }
+            else { in_el[k] = tmp; out_el[k] = total; }
+        }
+        break;
+    }
+    case ATOM_COLL_ALL_TO_ALL_V:
+        for (int r = 0; r < P; ++r) {
+            int64_t send = 0, recv = 0;
+            for (int j = 0; j < P; ++j) {
+                send += cnt[r * P + j];
+                recv += cnt[j * P + r];
+            }
+            if (!mul_ok(send, row, &in_el[r]) || !mul_ok(recv, row, &out_el[r]))
+                return ATOM_ERR_INVALID_ARG;
+        }
+        break;
+    default:
+        return ATOM_ERR_UNSUPPORTED;
+    }
+
+    // ---- buffers: element-aligned, non-NULL unless empty, outputs disjoint
+    Range ri[kMaxRanks], ro[kMaxRanks];
+    int64_t in_bytes_total = 0, out_bytes_total = 0;
+    for (int r = 0; r < P; ++r) {
+        int64_t bi, bo;
+        if (!mul_ok(in_el[r], es, &bi) || !mul_ok(out_el[r], es, &bo))
+            return ATOM_ERR_INVALID_ARG;
+        if (!buffer_ok(in->bufs[r], bi, es) || !buffer_ok(out->bufs[r], bo, es))
+            return ATOM_ERR_INVALID_ARG;
+        ri[r] = range_of(in->bufs[r], bi);
+        ro[r] = range_of(out->bufs[r], bo);
+        in_bytes_total += bi;
+        out_bytes_total += bo;
+        if (in_bytes_total < 0 || out_bytes_total < 0)
+            return ATOM_ERR_INVALID_ARG;
+    }
+    if (!disjoint(ri, P, ro, P))
+        return ATOM_ERR_INVALID_ARG;
+
+    const bool staged = (c.flags & ATOM_F_STAGED) != 0;
+    if (staged && kind != ATOM_COLL_ALL_GATHER)
+        return ATOM_ERR_UNSUPPORTED;
+
+    *p = Plan();
+    p->kind = kind;
+    p->dtype = in->dtype == ATOM_DT_BF16 ? DT_BF16 : DT_F32;
+    p->esize = es;
+    p->P = P;
+    p->in_elems = in_el[0];
+    for (int r = 0; r < P; ++r)
+        p->out_elems[r] = out_el[r];
+
+    // Credited (algorithmic) bytes: every input element read once, every
+    // output element written once; a reduced element counts its P reads.
+    switch (kind) {
+    case ATOM_COLL_REDUCE_SCATTER:
+    case ATOM_COLL_REDUCE_SCATTER_V:
+        p->credited_bytes = static_cast<int64_t>(P + 1) * total * es;
+        break;
+    case ATOM_COLL_ALL_REDUCE:
+        p->credited_bytes = 2 * static_cast<int64_t>(P) * total * es;
+        break;
+    case ATOM_COLL_ALL_GATHER:
+    case ATOM_COLL_ALL_GATHER_V:
+        p->credited_bytes = static_cast<int64_t>(1 + P) * total * es;
+        break;
+    default:
+        p->credited_bytes = in_bytes_total + out_bytes_total;
+        break;
+    }
+    if (in_bytes_total == 0 && out_bytes_total == 0)
+        return ATOM_OK;
+
+    // ---- the launch
+    int64_t off[kMaxRanks + 1];
+    switch (kind) {
+    case ATOM_COLL_REDUCE_SCATTER:
+    case ATOM_COLL_REDUCE_SCATTER_V: {
+        off[0] = 0;
+        for (int k = 0; k < P; ++k)
+            off[k + 1] = off[k] + (v ? cnt[k] * row : n);
+        build_reduce(p, P, in->bufs, P, out->bufs, P, off, RM_SCATTER, c);
+        break;
+    }
+    case ATOM_COLL_ALL_REDUCE: {
+        off[0] = 0;
+        off[1] = total;
+        build_reduce(p, P, in->bufs, P, out->bufs, 1, off, RM_FANOUT, c);
+        break;
+    }
+    case ATOM_COLL_ALL_GATHER:
+    case ATOM_COLL_ALL_GATHER_V: {
+        int64_t ones[kMaxRanks];
+        for (int k = 0; k < P; ++k)
+            ones[k] = 1;
+        const int64_t rb = v ? row_bytes : n * es;
+        if (ceil_div(total * es, 256 * kVecBytes) > kMaxTiles)
+            return ATOM_ERR_INVALID_ARG;
+        if (staged)
+            break;   // SNAC plan below
+        build_copy(p, CK_FANOUT, P, in->bufs, P, out->bufs, P, v ? cnt : ones, P, rb, es, c);
+        break;
+    }
+    case ATOM_COLL_ALL_TO_ALL:
+    case ATOM_COLL_ALL_TO_ALL_V: {
+        int64_t ones[kMaxSegs];
+        for (int s = 0; s < P * P; ++s)
+            ones[s] = 1;
+        const int64_t rb = v ? row_bytes : n * es;
+        if (ceil_div(in_bytes_total, 256 * kVecBytes) + P * P > kMaxTiles)
+            return ATOM_ERR_INVALID_ARG;
+        build_copy(p, CK_EXCHANGE, P, in->bufs, P, out->bufs, P, v ? cnt : ones, P * P, rb, es, c);
+        break;
+    }
+    default:
+        return ATOM_ERR_UNSUPPORTED;
+    }
+
+    if (staged) {
+        // SNAC AllGather: chunks of c.chunk bytes of each partition are
+        // staged into a ring of c.slots slots and fanned out from there.
+        const int64_t S = n * es;
+        bool vec = (S % kVecBytes) == 0;
+        for (int r = 0; r < P; ++r)
+            vec = vec && aligned(in->bufs[r], kVecBytes) && aligned(out->bufs[r], kVecBytes);
+        if (!vec)
+            return ATOM_ERR_UNSUPPORTED;
+        SnacArgs& a = p->sa;
+        std::memset(&a, 0, sizeof a);
+        for (int r = 0; r < P; ++r) {
+            a.src[r] = in->bufs[r];
+            a.dst[r] = out->bufs[r];
+        }
+        a.P = P;
+        a.part_bytes = S;
+        a.chunk_bytes = c.chunk;
+        a.piece_bytes = std::min<int64_t>(kPieceBytes, c.chunk);
+        a.pieces = static_cast<int32_t>(c.chunk / a.piece_bytes);
+        a.slots = c.slots;
+        a.nchunks_per_part = ceil_div(S, c.chunk);
+        a.nchunks = a.nchunks_per_part * P;
+        a.ntasks = 2 * a.nchunks * a.pieces;
+        a.spin_limit = int64_t(1) << 22;
+        a.dtype = p->dtype;
+        a.nt_store = (c.flags & ATOM_F_NO_NT) ? 0 : 1;
+        p->vec = 1;
+        p->U = 4;
+        p->wg = 256;
+        p->slots = c.slots;
+        p->chunk_bytes = c.chunk;
+        p->ring_bytes = c.chunk * c.slots;
+        p->grid = std::max<int64_t>(1, std::min<int64_t>(a.ntasks, c.num_wgs ? c.num_wgs : 1024));
+        p->exec = EX_SNAC_AG;
+    }
+    return ATOM_OK;
+}
+
+void plan_fill_info(const Plan& p, atom_plan_info* info)
+{
+    std::memset(info, 0, sizeof *info);
+    info->kind = p.kind;
+    info->nranks = p.P;
+    info->staged = (p.exec == EX_SNAC_AG || p.exec == EX_SNAC_AR) ? 1 : 0;
+    info->vector_path = p.vec;
+    info->elems_per_rank_in = p.in_elems;
+    for (int r = 0; r < kMaxRanks; ++r)
+        info->elems_per_rank_out[r] = p.out_elems[r];
+    info->credited_bytes = p.credited_bytes;
+    info->chunk_bytes = p.chunk_bytes;
+    info->num_chunks = info->staged ? p.sa.nchunks : 0;
+    info->ring_slots = p.slots;
+    info->num_wgs = p.exec == EX_NONE ? 0 : static_cast<int32_t>(p.grid);
+}
+
+// Table 3: R*tau rounded to the closest power of two (ties upward).
+int64_t bdp_chunk_bytes(double bytes_per_s, double round_trip_s)
+{
+    const double x = bytes_per_s * round_trip_s;
+    if (!(x >= 1.0) || !std::isfinite(x))
+        return 0;
+    if (x >= 4.0e18)
+        return int64_t(1) << 62;
+    int e;
+    std::frexp(x, &e);           // x = m * 2^e, m in [0.5, 1): 2^(e-1) <= x < 2^e
+    const double lo = std::ldexp(1.0, e - 1), hi = std::ldexp(1.0, e);
+    return static_cast<int64_t>((x - lo < hi - x) ? lo : hi);
+}
+
+}  // namespace atom

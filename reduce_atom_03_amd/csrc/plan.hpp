@@ -1,0 +1,59 @@
+// plan.hpp -- host planner: argument validation and derivation of the
+// collective, its sizes and its launch from a pair of layouts and an op.
+// Pure host C++ (no HIP calls), so every rule here is testable on a CPU.
+#pragma once
+
+#include "../../include/atom.h"
+#include "kargs.hpp"
+
+namespace atom {
+
+enum Exec : int32_t {
+    EX_NONE = 0,      // nothing to launch (zero-sized)
+    EX_REDUCE = 1,    // reduce family kernel (ReduceArgs)
+    EX_COPY = 2,      // copy family kernel (CopyArgs)
+    EX_SNAC_AG = 3,   // SNAC persistent AllGather (SnacArgs)
+    EX_SNAC_AR = 4    // SNAC composed AllReduce (ReduceArgs for RS + SnacArgs)
+};
+
+struct Plan {
+    atom_collective_kind kind = ATOM_COLL_NONE;
+    Exec exec = EX_NONE;
+    int32_t dtype = DT_BF16;
+    int32_t esize = 2;
+    int32_t P = 0;
+    int32_t vec = 0;          // 1: 128-bit vector path
+    int32_t U = 1;            // 16-byte slots per lane per tile
+    int32_t wg = 256;         // threads per workgroup
+    int64_t grid = 0;         // workgroups launched
+    int64_t credited_bytes = 0;
+    int64_t out_elems[kMaxRanks] = {};
+    int64_t in_elems = 0;
+    // SNAC
+    int32_t slots = 0;
+    int64_t chunk_bytes = 0;
+    int64_t ring_bytes = 0;
+    ReduceArgs ra;
+    CopyArgs ca;
+    SnacArgs sa;
+};
+
+// Defaults and limits.
+constexpr int64_t kDefaultChunk = 1 << 20;           // 1 MiB (Table 3, H200 row)
+constexpr int64_t kMinChunk = 64 << 10;
+constexpr int64_t kMaxChunk = 16 << 20;
+constexpr int32_t kDefaultSlots = 4;
+constexpr int32_t kMaxSlots = 16;
+constexpr int64_t kPieceBytes = 64 << 10;            // SNAC task granule
+constexpr int64_t kMaxGrid = 1 << 20;
+
+atom_status plan_copy(void* dst, const void* src, size_t bytes, const atom_config* cfg,
+                      Plan* p);
+atom_status plan_reduce(void* dst, const void* const* srcs, int32_t nsrcs, int64_t count,
+                        atom_dtype dtype, atom_op op, const atom_config* cfg, Plan* p);
+atom_status plan_collective(const atom_layout* in, const atom_layout* out, atom_op op,
+                            const atom_config* cfg, Plan* p);
+void plan_fill_info(const Plan& p, atom_plan_info* info);
+int64_t bdp_chunk_bytes(double bytes_per_s, double round_trip_s);
+
+}  // namespace atom

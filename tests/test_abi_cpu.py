@@ -1,0 +1,252 @@
+"""The C ABI without a GPU: the library loads and exports every declared
+symbol; validation and planning (which run before any HIP call) return the
+documented codes and plans; the BDP helper reproduces Table 3."""
+
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+from reduce_atom_03_amd import atom as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+BASE = 0x7F0000000000          # fake device addresses: never dereferenced
+MiB = 1 << 20
+
+
+def fake(P, nbytes, start=BASE, align_off=0):
+    """P disjoint fake device buffers of nbytes each."""
+    step = ((nbytes + 4095) // 4096 + 1) * 4096
+    return [start + r * step + align_off for r in range(P)]
+
+
+def test_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "atom.h")).read()
+    declared = set(re.findall(r"^\w[\w\s\*]*?\b(atom_\w+)\s*\(", hdr, re.M))
+    assert {"atom_copy", "atom_reduce", "atom_collective"} <= declared
+    lib = ctypes.CDLL(A.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), f"libatom does not export {name}"
+    assert declared == set(A.EXPORTS)
+
+
+def test_status_strings_and_version():
+    for s in range(6):
+        assert A.atom_status_string(s) not in ("", "unknown status")
+    assert A.atom_status_string(99) == "unknown status"
+    assert A.atom_version() >= 1
+
+
+def test_bdp_reproduces_table3(golden_dir):
+    with open(os.path.join(golden_dir, "table3_bdp.json")) as f:
+        rows = json.load(f)["rows"]
+    for row in rows:
+        assert A.atom_bdp_chunk_bytes(row["R_bytes_per_s"], row["tau_s"]) == row["bdp_bytes"], row
+        # the printed R*tau column rounds the same way
+        assert A.atom_bdp_chunk_bytes(row["rtau_printed_bytes"], 1.0) == row["bdp_bytes"], row
+
+
+def test_bdp_edges():
+    assert A.atom_bdp_chunk_bytes(0, 1e-6) == 0
+    assert A.atom_bdp_chunk_bytes(-1, 1) == 0
+    assert A.atom_bdp_chunk_bytes(float("nan"), 1) == 0
+    assert A.atom_bdp_chunk_bytes(3 * MiB, 1.0) == 4 * MiB      # tie goes up
+    assert A.atom_bdp_chunk_bytes(MiB, 1.0) == MiB
+    assert A.atom_bdp_chunk_bytes(MiB + 1, 1.0) == MiB
+
+
+# ---------------------------------------------------------------- validation
+
+def test_copy_validation():
+    assert A.atom_copy(0, 0, 0, stream=0, check=False) == A.OK     # nothing to do
+    assert A.atom_copy(0, BASE, 16, stream=0, check=False) == A.ERR_INVALID_ARG
+    assert A.atom_copy(BASE, 0, 16, stream=0, check=False) == A.ERR_INVALID_ARG
+    assert A.atom_copy(BASE + 8, BASE, 16, stream=0, check=False) == A.ERR_INVALID_ARG
+    assert A.atom_copy(BASE, BASE + 8, 16, stream=0, check=False) == A.ERR_INVALID_ARG
+
+
+def test_reduce_validation():
+    s = fake(3, 64)
+    d = fake(1, 64, start=BASE + (1 << 32))[0]
+    R = lambda *a, **k: A.atom_reduce(*a, stream=0, check=False, **k)
+    assert R(d, s, 0, dtype=A.DT_BF16) == A.OK                      # zero count
+    assert R(d, [], 4, dtype=A.DT_BF16) == A.ERR_INVALID_ARG
+    assert R(d, fake(17, 64), 4, dtype=A.DT_BF16) == A.ERR_INVALID_ARG
+    assert R(d, s, -1, dtype=A.DT_BF16) == A.ERR_INVALID_ARG
+    assert R(d, s, 4, dtype=7) == A.ERR_INVALID_ARG
+    assert R(d, s, 4, dtype=A.DT_BF16, op=5) == A.ERR_INVALID_ARG
+    assert R(d, s, 4, dtype=A.DT_BF16, op=A.OP_COPY) == A.ERR_UNSUPPORTED
+    assert R(d + 1, s, 4, dtype=A.DT_BF16) == A.ERR_INVALID_ARG     # not element-aligned
+    assert R(d + 2, s, 4, dtype=A.DT_F32) == A.ERR_INVALID_ARG
+    assert R(s[1] + 2, s, 4, dtype=A.DT_BF16) == A.ERR_INVALID_ARG  # dst overlaps a source
+    assert R(d, [s[0], 0], 4, dtype=A.DT_BF16) == A.ERR_INVALID_ARG
+
+
+def Q(kin, kout, op, P=4, n=64, ins=None, outs=None, cfg=None, counts=None, row=1,
+      dtype=A.DT_BF16, in_counts=True):
+    es = 2 if dtype == A.DT_BF16 else 4
+    ins = ins if ins is not None else fake(P, P * n * es * 4)
+    outs = outs if outs is not None else fake(P, P * n * es * 4, start=BASE + (1 << 36))
+    li = A.layout(kin, ins, n, counts if in_counts else None, row, dtype=dtype)
+    lo = A.layout(kout, outs, n, None, row, dtype=dtype)
+    return A.atom_plan_query(li, lo, op, cfg)
+
+
+def test_collective_derivation():
+    cases = {
+        (A.PARTITIONED, A.SHARD, A.OP_SUM): A.COLL_REDUCE_SCATTER,
+        (A.SHARD, A.GATHERED, A.OP_COPY): A.COLL_ALL_GATHER,
+        (A.PARTITIONED, A.TRANSPOSED, A.OP_COPY): A.COLL_ALL_TO_ALL,
+        (A.PARTITIONED, A.GATHERED, A.OP_SUM): A.COLL_ALL_REDUCE,
+    }
+    for kin in range(4):
+        for kout in range(4):
+            for op in (A.OP_COPY, A.OP_SUM):
+                st, info = Q(kin, kout, op)
+                want = cases.get((kin, kout, op))
+                if want is None:
+                    assert st == A.ERR_UNSUPPORTED, (kin, kout, op)
+                else:
+                    assert st == A.OK and info.kind == want, (kin, kout, op, st)
+
+
+def test_v_derivation():
+    P = 4
+    C = np.arange(P * P, dtype=np.int64).reshape(P, P)
+    st, info = Q(A.PARTITIONED, A.TRANSPOSED, A.OP_COPY, P=P, counts=C, row=8)
+    assert st == A.OK and info.kind == A.COLL_ALL_TO_ALL_V
+    assert info.elems_per_rank_in == int(C[0].sum()) * 8
+    for j in range(P):
+        assert info.elems_per_rank_out[j] == int(C[:, j].sum()) * 8
+    cnt = np.array([3, 0, 5, 1], dtype=np.int64)
+    st, info = Q(A.PARTITIONED, A.SHARD, A.OP_SUM, P=P, counts=cnt, row=2)
+    assert st == A.OK and info.kind == A.COLL_REDUCE_SCATTER_V
+    assert [info.elems_per_rank_out[k] for k in range(P)] == [6, 0, 10, 2]
+    st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=P, counts=cnt, row=2)
+    assert st == A.OK and info.kind == A.COLL_ALL_GATHER_V
+    assert info.elems_per_rank_out[0] == 18
+    # AllReduce has no V form
+    st, _ = Q(A.PARTITIONED, A.GATHERED, A.OP_SUM, P=P, counts=cnt, row=2)
+    assert st == A.ERR_UNSUPPORTED
+
+
+def test_collective_validation_errors():
+    P = 4
+    ins = fake(P, 4096)
+    outs = fake(P, 4096, start=BASE + (1 << 36))
+    ok = lambda st: st[0]
+    # mismatched rank counts
+    li = A.layout(A.PARTITIONED, ins, 64, dtype=A.DT_BF16)
+    lo = A.layout(A.SHARD, outs[:3], 64, dtype=A.DT_BF16)
+    assert A.atom_plan_query(li, lo, A.OP_SUM)[0] == A.ERR_INVALID_ARG
+    # too many ranks
+    li = A.layout(A.PARTITIONED, fake(17, 4096), 64, dtype=A.DT_BF16)
+    lo = A.layout(A.SHARD, fake(17, 4096, start=BASE + (1 << 36)), 64, dtype=A.DT_BF16)
+    assert A.atom_plan_query(li, lo, A.OP_SUM)[0] == A.ERR_INVALID_ARG
+    # dtype mismatch
+    li = A.layout(A.PARTITIONED, ins, 64, dtype=A.DT_BF16)
+    lo = A.layout(A.SHARD, outs, 64, dtype=A.DT_F32)
+    assert A.atom_plan_query(li, lo, A.OP_SUM)[0] == A.ERR_INVALID_ARG
+    # part size mismatch, negative size
+    assert ok(Q(A.PARTITIONED, A.SHARD, A.OP_SUM, n=-1)) == A.ERR_INVALID_ARG
+    li = A.layout(A.PARTITIONED, ins, 64, dtype=A.DT_BF16)
+    lo = A.layout(A.SHARD, outs, 65, dtype=A.DT_BF16)
+    assert A.atom_plan_query(li, lo, A.OP_SUM)[0] == A.ERR_INVALID_ARG
+    # misaligned (odd) bf16 pointer
+    bad = list(ins)
+    bad[2] += 1
+    assert ok(Q(A.PARTITIONED, A.SHARD, A.OP_SUM, ins=bad)) == A.ERR_INVALID_ARG
+    # output overlapping an input, outputs overlapping each other
+    assert ok(Q(A.PARTITIONED, A.SHARD, A.OP_SUM, outs=[ins[0] + 64] + outs[1:])) == A.ERR_INVALID_ARG
+    assert ok(Q(A.PARTITIONED, A.SHARD, A.OP_SUM, outs=[outs[0], outs[0] + 64] + outs[2:])) \
+        == A.ERR_INVALID_ARG
+    # NULL buffer with data
+    assert ok(Q(A.PARTITIONED, A.SHARD, A.OP_SUM, ins=[0] + ins[1:])) == A.ERR_INVALID_ARG
+    # negative count, count too large for a segment
+    C = np.ones((P, P), dtype=np.int64)
+    C[1, 2] = -3
+    assert ok(Q(A.PARTITIONED, A.TRANSPOSED, A.OP_COPY, counts=C, row=4)) == A.ERR_INVALID_ARG
+    C[1, 2] = 1 << 31
+    assert ok(Q(A.PARTITIONED, A.TRANSPOSED, A.OP_COPY, counts=C, row=4)) == A.ERR_INVALID_ARG
+    # bad row width
+    C[1, 2] = 1
+    assert ok(Q(A.PARTITIONED, A.TRANSPOSED, A.OP_COPY, counts=C, row=0)) == A.ERR_INVALID_ARG
+    # bad op, bad layout kind
+    assert ok(Q(A.PARTITIONED, A.SHARD, 9)) == A.ERR_INVALID_ARG
+    assert ok(Q(7, A.SHARD, A.OP_SUM)) == A.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("field,value", [
+    ("chunk_bytes", 3 * MiB), ("chunk_bytes", 32 << 10), ("chunk_bytes", 32 * MiB),
+    ("stages", 3), ("stages", 16), ("num_wgs", -1), ("flags", 0x80), ("ring_slots", 17),
+    ("ring_slots", -2)])
+def test_config_validation(field, value):
+    cfg = A.config(**{field: value})
+    assert Q(A.SHARD, A.GATHERED, A.OP_COPY, cfg=cfg)[0] == A.ERR_INVALID_ARG
+
+
+def test_staged_only_for_allgather():
+    cfg = A.config(flags=A.F_STAGED)
+    assert Q(A.SHARD, A.GATHERED, A.OP_COPY, cfg=cfg)[0] == A.OK
+    assert Q(A.PARTITIONED, A.SHARD, A.OP_SUM, cfg=cfg)[0] == A.ERR_UNSUPPORTED
+    assert Q(A.PARTITIONED, A.TRANSPOSED, A.OP_COPY, cfg=cfg)[0] == A.ERR_UNSUPPORTED
+    # the staged path needs 16-byte partitions
+    assert Q(A.SHARD, A.GATHERED, A.OP_COPY, n=63, cfg=cfg)[0] == A.ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------------------ planning
+
+def test_credited_bytes_of_the_workloads():
+    # ReduceScatter, P=4, 4 x 65536 fp32 per input: (P+1) * P * n * 4
+    st, info = Q(A.PARTITIONED, A.SHARD, A.OP_SUM, P=4, n=65536, dtype=A.DT_F32)
+    assert st == A.OK and info.credited_bytes == 5_242_880
+    # 8-way reduce of 8 x 256 MiB bf16 and the fused AllReduce of the same
+    n = 1 << 24
+    st, info = Q(A.PARTITIONED, A.SHARD, A.OP_SUM, P=8, n=n)
+    assert info.credited_bytes == 2_415_919_104
+    st, info = Q(A.PARTITIONED, A.GATHERED, A.OP_SUM, P=8, n=n)
+    assert info.credited_bytes == 4_294_967_296
+    # AllToAllV of 8 x 4096 x 7168 bf16: 448 MiB read + 448 MiB written
+    C = np.full((8, 8), 512, dtype=np.int64)
+    st, info = Q(A.PARTITIONED, A.TRANSPOSED, A.OP_COPY, P=8, counts=C, row=7168,
+                 ins=fake(8, 56 * MiB), outs=fake(8, 56 * MiB, start=BASE + (1 << 40)))
+    assert info.credited_bytes == 939_524_096
+    # AllGather at S bytes per partition: 72 S
+    S = 8 << 10
+    st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=8, n=S // 2)
+    assert info.credited_bytes == 72 * S
+    # decode AllReduce, b=1: 2 * 8 * 14336
+    st, info = Q(A.PARTITIONED, A.GATHERED, A.OP_SUM, P=8, n=896)
+    assert info.credited_bytes == 229_376
+
+
+def test_vector_path_selection():
+    st, info = Q(A.PARTITIONED, A.SHARD, A.OP_SUM, n=64)
+    assert info.vector_path == 1
+    st, info = Q(A.PARTITIONED, A.SHARD, A.OP_SUM, n=63)        # partitions off 16 bytes
+    assert info.vector_path == 0
+    ins = [b + 2 for b in fake(4, 4096)]                        # bases off 16 bytes
+    st, info = Q(A.PARTITIONED, A.SHARD, A.OP_SUM, ins=ins)
+    assert st == A.OK and info.vector_path == 0
+
+
+def test_snac_chunking():
+    for chunk in (512 << 10, MiB, 2 * MiB):
+        for S in (8 << 10, 3 * MiB + (64 << 10), 64 * MiB):
+            cfg = A.config(flags=A.F_STAGED, chunk_bytes=chunk, ring_slots=4)
+            st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=8, n=S // 2, cfg=cfg,
+                         ins=fake(8, S), outs=fake(8, 8 * S, start=BASE + (1 << 40)))
+            assert st == A.OK and info.staged == 1
+            assert info.chunk_bytes == chunk and info.ring_slots == 4
+            assert info.num_chunks == 8 * -(-S // chunk)
+
+
+def test_zero_sized_collective_launches_nothing():
+    st, info = Q(A.PARTITIONED, A.SHARD, A.OP_SUM, n=0)
+    assert st == A.OK and info.num_wgs == 0 and info.credited_bytes == 0
+    li = A.layout(A.PARTITIONED, fake(4, 64), 0, dtype=A.DT_BF16)
+    lo = A.layout(A.SHARD, fake(4, 64, start=BASE + (1 << 36)), 0, dtype=A.DT_BF16)
+    assert A.atom_collective(li, lo, A.OP_SUM, stream=0, check=False) == A.OK

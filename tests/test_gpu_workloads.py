@@ -1,0 +1,126 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (default plans):
+
+* 8-way ReduceScatter and fused AllReduce of 8 x 256 MiB bf16, N(0,1), seed 2:
+  every output element against the oracle (the oracle's OpenMP loops finish
+  in seconds at this size), and the 8 AllReduce outputs bitwise identical.
+* AllToAllV MoE dispatch, 8 x 4096 x 7168 bf16 with Dirichlet-multinomial
+  counts (seed 3): bit-exact against the oracle.
+* AllGather at 8 partitions of 1 GiB (the largest size), zero-staging and
+  SNAC with each chunk size: every output block equals its partition,
+  compared on the device.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from reduce_atom_03_amd import synth
+from tests._helpers import assert_bf16_close, assert_bits_equal
+from tests.gpu_util import empty_dev, from_dev, require_gpu, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def A():
+    require_gpu()
+    from reduce_atom_03_amd import atom
+    return atom
+
+
+@pytest.fixture(scope="module")
+def c2():
+    say("generating 8 x 256 MiB bf16 (seed 2)")
+    xs = synth.c2_inputs()
+    return xs
+
+
+def test_c2_reduce_scatter_full(A, c2):
+    import torch
+    P, n = 8, (1 << 27) // 8
+    say("c2 8-way ReduceScatter 8 x 256 MiB bf16")
+    want = oracle.reduce_scatter(c2)
+    dx = [to_dev(x)[1] for x in c2]
+    ys = [empty_dev(n, torch.bfloat16) for _ in range(P)]
+    A.reduce_scatter(dx, ys)
+    torch.cuda.synchronize()
+    for k in range(P):
+        got = from_dev(ys[k])
+        assert_bf16_close(got, want[k], 1, f"c2 RS y_{k}")
+        assert_bits_equal(got, want[k], f"c2 RS y_{k} bitwise")
+
+
+def test_c2_all_reduce_full(A, c2):
+    import torch
+    P, N = 8, 1 << 27
+    say("c2 fused AllReduce 8 x 256 MiB bf16")
+    want = np.concatenate(oracle.reduce_scatter(c2))      # AG(RS(x)) at any rank
+    dx = [to_dev(x)[1] for x in c2]
+    outs = [empty_dev(N, torch.bfloat16) for _ in range(P)]
+    A.all_reduce(dx, outs)
+    torch.cuda.synchronize()
+    got = from_dev(outs[0])
+    assert_bf16_close(got, want, 1, "c2 AR out_0")
+    assert_bits_equal(got, want, "c2 AR out_0 bitwise")
+    for j in range(1, P):
+        assert torch.equal(outs[j].view(torch.int16), outs[0].view(torch.int16)), f"AR out_{j}"
+
+
+def test_c3_all_to_all_v_full(A):
+    import torch
+    say("c3 AllToAllV 8 x 4096 x 7168 bf16")
+    C = synth.c3_counts()
+    xs = synth.c3_inputs()
+    want = oracle.all_to_all_v(xs, C, synth.HIDDEN)
+    dx = [to_dev(x)[1] for x in xs]
+    R = C.sum(axis=0)
+    outs = [empty_dev(int(R[j]) * synth.HIDDEN, torch.bfloat16) for j in range(8)]
+    A.all_to_all_v(dx, outs, C, synth.HIDDEN)
+    torch.cuda.synchronize()
+    for j in range(8):
+        assert_bits_equal(from_dev(outs[j]), want[j], f"c3 out_{j}", nan_by_class=False)
+
+
+def test_c3_uniform_all_to_all(A):
+    """The Ulysses shape: every pair exchanges 512 tokens."""
+    import torch
+    say("uniform A2A 8 x 4096 x 7168 bf16")
+    xs = synth.c3_inputs()
+    want = oracle.all_to_all(xs)
+    dx = [to_dev(x)[1] for x in xs]
+    outs = [empty_dev(4096 * synth.HIDDEN, torch.bfloat16) for _ in range(8)]
+    A.all_to_all(dx, outs)
+    torch.cuda.synchronize()
+    for j in range(8):
+        assert_bits_equal(from_dev(outs[j]), want[j], f"uniform A2A out_{j}", nan_by_class=False)
+
+
+@pytest.mark.parametrize("mode", ["zs", 512 << 10, 1 << 20, 2 << 20])
+def test_c4_all_gather_1gib(A, mode):
+    """8 partitions of 1 GiB: 8 GiB in, 64 GiB out (inputs drawn on the host
+    in 64 MiB slices to bound host memory)."""
+    import torch
+    P, S = 8, 1 << 30
+    n = S // 2
+    say(f"c4 AllGather S=1 GiB mode={mode}")
+    dz = []
+    for k in range(P):
+        z = empty_dev(n, torch.bfloat16)
+        g = synth.rank_rng(4, k)
+        step = 32 << 20
+        for o in range(0, n, step):
+            m = min(step, n - o)
+            part = synth._bf16_bits(g.random(m, dtype=np.float32) * np.float32(2) - np.float32(1))
+            z[o:o + m].copy_(torch.from_numpy(part.view(np.int16)).view(torch.bfloat16).cuda())
+        dz.append(z)
+    outs = [empty_dev(P * n, torch.bfloat16, 0xFFFF) for _ in range(P)]
+    cfg = None if mode == "zs" else A.config(flags=A.F_STAGED, chunk_bytes=mode, ring_slots=4)
+    A.all_gather(dz, outs, cfg)
+    assert A.atom_sync_status() == A.OK
+    for j in range(P):
+        for k in range(P):
+            assert torch.equal(outs[j][k * n:(k + 1) * n].view(torch.int16),
+                               dz[k].view(torch.int16)), f"out_{j} block {k}"
+    del outs, dz
+    torch.cuda.empty_cache()
