@@ -9,6 +9,7 @@ resident synthetic input (bf16):
   a2av    AllToAllV MoE dispatch, 8 x 4096 x 7168 (Dirichlet-multinomial counts, seed 3)
   ag_zs   AllGather, zero staging, 8 partitions of 64 MiB (U[-1,1], seed 4)
   ag_snac AllGather through SNAC, same input, 1 MiB chunks, 4-slot ring
+  ar_snac composed AllReduce through SNAC (Figure 6) of the 8 x 256 MiB
   dec     decode AllReduce, 8 x b x 7168 for b in 1, 2, 4, 8, 16 (N(0,0.02), seed 5)
   ag_8k   AllGather, zero staging, 8 partitions of 8 KiB
 
@@ -52,6 +53,8 @@ def parse():
     ap.add_argument("--ag-mib", type=int, default=64, help="AllGather partition size (MiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--no-snac", dest="snac", action="store_false",
+                    help="leave out the SNAC-staged AllGather and AllReduce")
     return ap.parse_args()
 
 
@@ -133,8 +136,12 @@ def main():
     lay = (L(A.SHARD, z4, S // 2), L(A.GATHERED, ag_out, S // 2))
     rows.append(("ag_zs", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_COPY),
                  plan_bytes(lay[0], lay[1], A.OP_COPY, name="ag_zs")))
-    rows.append(("ag_snac", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_COPY, snac_cfg),
-                 plan_bytes(lay[0], lay[1], A.OP_COPY, snac_cfg, name="ag_snac")))
+    if args.snac:
+        rows.append(("ag_snac", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_COPY, snac_cfg),
+                     plan_bytes(lay[0], lay[1], A.OP_COPY, snac_cfg, name="ag_snac")))
+        lay = (L(A.PARTITIONED, x2, n2), L(A.GATHERED, ar_out, n2))
+        rows.append(("ar_snac", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_SUM, snac_cfg),
+                     plan_bytes(lay[0], lay[1], A.OP_SUM, snac_cfg, name="ar_snac")))
     for b in (1, 2, 4, 8, 16):
         lay = (L(A.PARTITIONED, x5[b], b * 896), L(A.GATHERED, o5[b], b * 896))
         rows.append((f"dec_b{b}", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_SUM),
@@ -220,7 +227,9 @@ def main():
         "config": {
             "workload": ("one pass over: 8-way ReduceScatter and fused AllReduce of 8 x 256 MiB bf16; "
                          "AllToAllV 8 x 4096 x 7168 bf16 (Dirichlet-multinomial counts); "
-                         f"AllGather 8 x {args.ag_mib} MiB (zero-staging and SNAC, 1 MiB chunks, 4 slots); "
+                         f"AllGather 8 x {args.ag_mib} MiB (zero-staging"
+                         + (" and SNAC, 1 MiB chunks, 4 slots); SNAC-composed AllReduce of the "
+                            "8 x 256 MiB; " if args.snac else "); ") +
                          "decode AllReduce 8 x b x 7168 bf16, b = 1..16; AllGather 8 x 8 KiB"),
             "P": P, "step_credited_bytes": int(step_bytes),
         },
@@ -258,7 +267,9 @@ def cpu_baseline(args, C3, S, credited):
         oracle.all_reduce(c2)
         oracle.all_to_all_v(c3, C3, synth.HIDDEN)
         oracle.all_gather(z4)
-        oracle.all_gather(z4)
+        if args.snac:
+            oracle.all_gather(z4)
+            oracle.all_reduce(c2)
         for b in (1, 2, 4, 8, 16):
             oracle.all_reduce(x5[b])
         oracle.all_gather(z8)

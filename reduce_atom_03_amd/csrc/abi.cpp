@@ -27,6 +27,10 @@ atom_status workspace(int64_t ring_bytes, Workspace** out)
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace& ws = g_ws[dev];
     if (!ws.ready) {
+        int khz = 0;
+        if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
+            return ATOM_ERR_HIP;
+        ws.wall_khz = khz;
         // ready[kMaxSlots], freed[kMaxSlots], ticket, error in one block.
         char* flags = nullptr;
         const size_t fbytes = 2 * kMaxSlots * sizeof(unsigned long long) + 2 * sizeof(unsigned int);
@@ -73,12 +77,13 @@ atom_status run(const Plan& p, void* stream)
     case EX_COPY:
         e = launch_copy(p, s);
         break;
-    case EX_SNAC_AG: {
+    case EX_SNAC_AG:
+    case EX_SNAC_AR: {
         Workspace* ws = nullptr;
         atom_status st = workspace(p.ring_bytes, &ws);
         if (st != ATOM_OK)
             return st;
-        e = launch_snac_ag(p, *ws, s);
+        e = launch_snac(p, *ws, s);
         break;
     }
     default:

@@ -59,6 +59,62 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x)
     return static_cast<uint16_t>(pack_bf16x2(x, 0.0f) & 0xFFFFu);
 }
 
+// One 16-byte slot of binary32 sums: init from rank 0, add the others in
+// rank order, pack with one round-to-nearest-even narrowing.
+template <typename T> struct SlotAcc;
+
+template <> struct SlotAcc<uint16_t> {   // 8 bf16 per slot
+    float v[8];
+    __device__ __forceinline__ void init(u32x4 x)
+    {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            v[2 * w] = bf16_lo(x[w]);
+            v[2 * w + 1] = bf16_hi(x[w]);
+        }
+    }
+    __device__ __forceinline__ void add(u32x4 x)
+    {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            v[2 * w] = v[2 * w] + bf16_lo(x[w]);
+            v[2 * w + 1] = v[2 * w + 1] + bf16_hi(x[w]);
+        }
+    }
+    __device__ __forceinline__ u32x4 pack() const
+    {
+        u32x4 r;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            r[w] = pack_bf16x2(v[2 * w], v[2 * w + 1]);
+        return r;
+    }
+};
+
+template <> struct SlotAcc<float> {      // 4 fp32 per slot
+    float v[4];
+    __device__ __forceinline__ void init(u32x4 x)
+    {
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            v[w] = __uint_as_float(x[w]);
+    }
+    __device__ __forceinline__ void add(u32x4 x)
+    {
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            v[w] = v[w] + __uint_as_float(x[w]);
+    }
+    __device__ __forceinline__ u32x4 pack() const
+    {
+        u32x4 r;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            r[w] = __float_as_uint(v[w]);
+        return r;
+    }
+};
+
 // ---- element access for the element-wise (unaligned) paths ------------
 
 template <typename T> struct Elem;

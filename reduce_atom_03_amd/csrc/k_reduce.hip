@@ -24,60 +24,6 @@ namespace atom {
 
 namespace {
 
-template <typename T> struct Acc;
-
-template <> struct Acc<uint16_t> {   // 8 bf16 per slot
-    float v[8];
-    __device__ __forceinline__ void init(u32x4 x)
-    {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            v[2 * w] = bf16_lo(x[w]);
-            v[2 * w + 1] = bf16_hi(x[w]);
-        }
-    }
-    __device__ __forceinline__ void add(u32x4 x)
-    {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            v[2 * w] = v[2 * w] + bf16_lo(x[w]);
-            v[2 * w + 1] = v[2 * w + 1] + bf16_hi(x[w]);
-        }
-    }
-    __device__ __forceinline__ u32x4 pack() const
-    {
-        u32x4 r;
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-            r[w] = pack_bf16x2(v[2 * w], v[2 * w + 1]);
-        return r;
-    }
-};
-
-template <> struct Acc<float> {      // 4 fp32 per slot
-    float v[4];
-    __device__ __forceinline__ void init(u32x4 x)
-    {
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-            v[w] = __uint_as_float(x[w]);
-    }
-    __device__ __forceinline__ void add(u32x4 x)
-    {
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-            v[w] = v[w] + __uint_as_float(x[w]);
-    }
-    __device__ __forceinline__ u32x4 pack() const
-    {
-        u32x4 r;
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-            r[w] = __float_as_uint(v[w]);
-        return r;
-    }
-};
-
 // Part of tile t: the last part whose first tile is <= t.
 __device__ __forceinline__ int part_of_tile(const ReduceArgs& a, int64_t t)
 {
@@ -145,7 +91,7 @@ __global__ __launch_bounds__(256) void k_reduce_vec(const ReduceArgs a)
             const int64_t s = slot0 + u * nthr + lane;
             const uint32_t off = static_cast<uint32_t>(u * nthr + lane) * kVecBytes;
             if (s < nfull) {
-                Acc<T> acc;
+                SlotAcc<T> acc;
                 acc.init(x[u][0]);
 #pragma unroll
                 for (int r = 1; r < P; ++r)

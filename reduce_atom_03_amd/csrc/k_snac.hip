@@ -66,40 +66,115 @@ __device__ __forceinline__ Task decode_task(const SnacArgs& a, int64_t t)
     return k;
 }
 
-// Lane 0 waits until *flag >= target (bounded), then every wave acquires.
-// Returns false when the wait gave up (timeout here or elsewhere).
+// Lane 0 waits until *flag >= target, bounded in wall-clock time (the
+// per-wait bound and the workgroup's whole-kernel budget, both in ticks of
+// the constant-rate device clock); then every wave acquires. The result is
+// made wave-uniform with readfirstlane so every branch on it is uniform.
+// Returns false when the wait gave up (a timeout here or elsewhere).
 __device__ __forceinline__ bool wait_at_least(const SnacArgs& a, const unsigned long long* flag,
-                                              unsigned long long target, int* s_ok)
+                                              unsigned long long target, long long t_begin,
+                                              int* s_ok)
 {
     if (threadIdx.x == 0) {
         int ok = 1;
-        int64_t it = 0;
-        while (flag_load_relaxed(flag) < target) {
-            if (__hip_atomic_load(a.error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0 ||
-                ++it > a.spin_limit) {
-                __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                ok = 0;
-                break;
+        if (flag_load_relaxed(flag) < target) {
+            const long long w0 = wall_clock64();
+            unsigned int it = 0;
+            while (flag_load_relaxed(flag) < target) {
+                __builtin_amdgcn_s_sleep(1);
+                if ((++it & 15u) == 0) {
+                    const long long now = wall_clock64();
+                    if (__hip_atomic_load(a.error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0 ||
+                        now - w0 > a.wait_ticks || now - t_begin > a.budget_ticks) {
+                        __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        ok = 0;
+                        break;
+                    }
+                }
             }
-            __builtin_amdgcn_s_sleep(1);
         }
         *s_ok = ok;
     }
     __syncthreads();
-    const bool ok = *s_ok != 0;
+    const bool ok = __builtin_amdgcn_readfirstlane(*s_ok) != 0;
     if (ok)
         fence_acquire_agent();
     return ok;
 }
 
-// Copies `bytes` bytes (a multiple of 16) from src to dst (ndst == 1) or to
-// a.dst[q] + dst_off for every q < ndst (fan-out: one load, ndst stores).
+// Stage producers: fill `bytes` bytes (a multiple of 16) of a ring slot.
+// Copy: partition k of its own input (AllGather).
+struct StageCopy {
+    template <int U>
+    __device__ static void produce(const SnacArgs& a, int k, int64_t off, char* dst, int64_t bytes)
+    {
+        const char* src = static_cast<const char*>(a.src[k]) + off;
+        const int lane = threadIdx.x;
+        const int nthr = blockDim.x;
+        const int64_t step = static_cast<int64_t>(nthr) * U * kVecBytes;
+        for (int64_t b0 = 0; b0 < bytes; b0 += step) {
+            u32x4 x[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t o = b0 + static_cast<int64_t>(u * nthr + lane) * kVecBytes;
+                if (o < bytes)
+                    x[u] = ld16_stream(src + o);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t o = b0 + static_cast<int64_t>(u * nthr + lane) * kVecBytes;
+                if (o < bytes)
+                    st16(dst + o, x[u], false);
+            }
+        }
+    }
+};
+
+// Reduce: partition k summed over the P inputs in rank order, rounded once
+// (the ReduceScatter half of the composed AllReduce, Figure 6).
+template <typename T, int P>
+struct StageReduce {
+    template <int U>
+    __device__ static void produce(const SnacArgs& a, int k, int64_t off, char* dst, int64_t bytes)
+    {
+        const int64_t base = static_cast<int64_t>(k) * a.part_bytes + off;
+        const int lane = threadIdx.x;
+        const int nthr = blockDim.x;
+        const int64_t step = static_cast<int64_t>(nthr) * U * kVecBytes;
+        for (int64_t b0 = 0; b0 < bytes; b0 += step) {
+            u32x4 x[U][P];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t o = b0 + static_cast<int64_t>(u * nthr + lane) * kVecBytes;
+                if (o < bytes) {
+#pragma unroll
+                    for (int r = 0; r < P; ++r)
+                        x[u][r] = ld16_stream(static_cast<const char*>(a.src[r]) + base + o);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t o = b0 + static_cast<int64_t>(u * nthr + lane) * kVecBytes;
+                if (o < bytes) {
+                    SlotAcc<T> acc;
+                    acc.init(x[u][0]);
+#pragma unroll
+                    for (int r = 1; r < P; ++r)
+                        acc.add(x[u][r]);
+                    st16(dst + o, acc.pack(), false);
+                }
+            }
+        }
+    }
+};
+
+// Consume: one piece from the slot to every output (AllGather fan-out).
 template <int U>
-__device__ __forceinline__ void copy_piece(const SnacArgs& a, const char* src, char* dst, int ndst,
-                                           int64_t dst_off, int64_t bytes, bool nt)
+__device__ __forceinline__ void fan_out(const SnacArgs& a, const char* src, int64_t dst_off, int64_t bytes)
 {
     const int lane = threadIdx.x;
     const int nthr = blockDim.x;
+    const bool nt = a.nt_store != 0;
     const int64_t step = static_cast<int64_t>(nthr) * U * kVecBytes;
     for (int64_t b0 = 0; b0 < bytes; b0 += step) {
         u32x4 x[U];
@@ -112,33 +187,31 @@ __device__ __forceinline__ void copy_piece(const SnacArgs& a, const char* src, c
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t o = b0 + static_cast<int64_t>(u * nthr + lane) * kVecBytes;
-            if (o < bytes) {
-                if (dst) {
-                    st16(dst + o, x[u], nt);
-                } else {
-                    for (int q = 0; q < ndst; ++q)
-                        st16(static_cast<char*>(a.dst[q]) + dst_off + o, x[u], nt);
-                }
-            }
+            if (o < bytes)
+                for (int q = 0; q < a.P; ++q)
+                    st16(static_cast<char*>(a.dst[q]) + dst_off + o, x[u], nt);
         }
     }
 }
 
-template <int U>
-__global__ __launch_bounds__(256) void k_snac_allgather(const SnacArgs a)
+// The persistent SNAC kernel. Every branch that encloses a barrier depends
+// only on wave-uniform values (the ticket and the wait result are read with
+// readfirstlane), and lane 0's work at the end of a task (the notify and the
+// next ticket claim) is one divergent region closed by a barrier, so all
+// lanes of a workgroup run the same iterations.
+template <class Stage, int U>
+__global__ __launch_bounds__(256) void k_snac(const SnacArgs a)
 {
     __shared__ unsigned int s_ticket;
     __shared__ int s_ok;
+    const long long t_begin = wall_clock64();
     const int64_t S = a.part_bytes;
     const int64_t C = a.chunk_bytes;
-    for (;;) {
-        if (threadIdx.x == 0)
-            s_ticket = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __syncthreads();
-        const int64_t t = s_ticket;
-        __syncthreads();
-        if (t >= a.ntasks)
-            break;
+    if (threadIdx.x == 0)
+        s_ticket = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    int64_t t = static_cast<unsigned int>(__builtin_amdgcn_readfirstlane(static_cast<int>(s_ticket)));
+    while (t < a.ntasks) {
         const Task task = decode_task(a, t);
         const int64_t slot = task.chunk % a.slots;
         const int64_t use = task.chunk / a.slots;             // earlier chunks in this slot
@@ -150,27 +223,28 @@ __global__ __launch_bounds__(256) void k_snac_allgather(const SnacArgs a)
         int64_t plen = clen - pbeg;
         plen = plen < 0 ? 0 : (plen > a.piece_bytes ? a.piece_bytes : plen);
         char* slotp = a.ring + slot * C;
-        if (task.produce) {
-            // Stage: the slot's previous chunk must be fully consumed.
-            if (!wait_at_least(a, a.freed + slot, static_cast<unsigned long long>(use) * a.pieces, &s_ok))
-                continue;
-            copy_piece<U>(a, static_cast<const char*>(a.src[k]) + cbeg + pbeg, slotp + pbeg, 1, 0, plen,
-                          false);
-            // Notify: release this wave's stores at agent scope, then count the piece.
-            fence_release_agent();
-            __syncthreads();
-            if (threadIdx.x == 0)
-                flag_add_release(a.ready + slot, 1ull);
-        } else {
-            // Consume: the whole chunk must be staged.
-            if (!wait_at_least(a, a.ready + slot, static_cast<unsigned long long>(use + 1) * a.pieces, &s_ok))
-                continue;
-            copy_piece<U>(a, slotp + pbeg, nullptr, a.P, static_cast<int64_t>(k) * S + cbeg + pbeg, plen,
-                          a.nt_store != 0);
-            __syncthreads();   // every lane's slot reads have returned (their data was stored)
-            if (threadIdx.x == 0)
-                flag_add_release(a.freed + slot, 1ull);
+        // Stage waits for the slot's previous chunk to be consumed; Consume
+        // waits for every piece of its chunk to be staged.
+        const unsigned long long* wflag = task.produce ? a.freed + slot : a.ready + slot;
+        const unsigned long long target =
+            static_cast<unsigned long long>(task.produce ? use : use + 1) * a.pieces;
+        const bool ok = wait_at_least(a, wflag, target, t_begin, &s_ok);
+        if (ok) {
+            if (task.produce) {
+                Stage::template produce<U>(a, k, cbeg + pbeg, slotp + pbeg, plen);
+                fence_release_agent();           // this wave's staged stores, at agent scope
+            } else {
+                fan_out<U>(a, slotp + pbeg, static_cast<int64_t>(k) * S + cbeg + pbeg, plen);
+            }
         }
+        __syncthreads();                         // every wave staged (or read) its share
+        if (threadIdx.x == 0) {
+            if (ok)                              // Notify (ready) or release the slot (freed)
+                flag_add_release(task.produce ? a.ready + slot : a.freed + slot, 1ull);
+            s_ticket = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        t = static_cast<unsigned int>(__builtin_amdgcn_readfirstlane(static_cast<int>(s_ticket)));
     }
 }
 
@@ -189,12 +263,30 @@ __global__ void k_snac_reset(unsigned long long* ready, unsigned long long* free
         *ticket = 0;
 }
 
+template <typename T>
+hipError_t launch_ar_t(const SnacArgs& a, dim3 grid, hipStream_t stream)
+{
+    const dim3 block(256);
+    switch (a.P) {
+#define ATOM_SNAC_AR_CASE(PP) \
+    case PP: k_snac<StageReduce<T, PP>, (PP <= 8 ? 2 : 1)><<<grid, block, 0, stream>>>(a); break;
+    ATOM_SNAC_AR_CASE(1) ATOM_SNAC_AR_CASE(2) ATOM_SNAC_AR_CASE(3) ATOM_SNAC_AR_CASE(4)
+    ATOM_SNAC_AR_CASE(5) ATOM_SNAC_AR_CASE(6) ATOM_SNAC_AR_CASE(7) ATOM_SNAC_AR_CASE(8)
+    ATOM_SNAC_AR_CASE(9) ATOM_SNAC_AR_CASE(10) ATOM_SNAC_AR_CASE(11) ATOM_SNAC_AR_CASE(12)
+    ATOM_SNAC_AR_CASE(13) ATOM_SNAC_AR_CASE(14) ATOM_SNAC_AR_CASE(15) ATOM_SNAC_AR_CASE(16)
+#undef ATOM_SNAC_AR_CASE
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_snac_ag(const Plan& p, const Workspace& ws, hipStream_t stream)
+hipError_t launch_snac(const Plan& p, const Workspace& ws, hipStream_t stream)
 {
-    if (p.exec != EX_SNAC_AG || !ws.ring || ws.ring_bytes < p.ring_bytes || p.grid < 1 ||
-        p.sa.slots < 1 || p.sa.slots > kMaxSlots || p.sa.pieces < 1)
+    if ((p.exec != EX_SNAC_AG && p.exec != EX_SNAC_AR) || !ws.ring || ws.ring_bytes < p.ring_bytes ||
+        p.grid < 1 || p.sa.slots < 1 || p.sa.slots > kMaxSlots || p.sa.pieces < 1 || p.sa.P < 1 ||
+        p.sa.P > kMaxRanks || ws.wall_khz <= 0)
         return hipErrorInvalidValue;
     SnacArgs a = p.sa;
     a.ring = ws.ring;
@@ -202,12 +294,19 @@ hipError_t launch_snac_ag(const Plan& p, const Workspace& ws, hipStream_t stream
     a.freed = ws.freed;
     a.ticket = ws.ticket;
     a.error = ws.error;
+    // Bounds in device-clock ticks: ~1 s per wait, ~10 s per workgroup.
+    a.wait_ticks = static_cast<int64_t>(ws.wall_khz) * 1000;
+    a.budget_ticks = static_cast<int64_t>(ws.wall_khz) * 10000;
     k_snac_reset<<<1, 64, 0, stream>>>(ws.ready, ws.freed, ws.ticket, a.slots);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    k_snac_allgather<4><<<dim3(static_cast<unsigned>(p.grid)), dim3(256), 0, stream>>>(a);
-    return hipGetLastError();
+    const dim3 grid(static_cast<unsigned>(p.grid));
+    if (p.exec == EX_SNAC_AG) {
+        k_snac<StageCopy, 4><<<grid, dim3(256), 0, stream>>>(a);
+        return hipGetLastError();
+    }
+    return p.dtype == DT_BF16 ? launch_ar_t<uint16_t>(a, grid, stream) : launch_ar_t<float>(a, grid, stream);
 }
 
 }  // namespace atom

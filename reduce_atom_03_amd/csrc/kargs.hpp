@@ -60,7 +60,7 @@ struct CopyArgs {
     int32_t seg_tile_begin[kMaxSegs + 1];
 };
 
-// SNAC AllGather (and the AllGather half of a staged AllReduce).
+// SNAC: AllGather (stage = copy) and the composed AllReduce (stage = reduce).
 struct SnacArgs {
     const void* src[kMaxRanks];        // inputs (z_k, or x_r for AllReduce)
     void* dst[kMaxRanks];              // outputs out_j
@@ -75,7 +75,8 @@ struct SnacArgs {
     int64_t nchunks_per_part;
     int64_t nchunks;                   // P * nchunks_per_part
     int64_t ntasks;
-    int64_t spin_limit;                // bounded waits (iterations of a short sleep)
+    int64_t wait_ticks;                // bound of one wait, device-clock ticks
+    int64_t budget_ticks;              // bound of a workgroup's whole run
     int32_t P;
     int32_t pieces;                    // G pieces per chunk
     int32_t slots;                     // D

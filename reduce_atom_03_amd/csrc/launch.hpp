@@ -16,10 +16,11 @@ struct Workspace {
     unsigned long long* freed = nullptr;   // kMaxSlots counters
     unsigned int* ticket = nullptr;
     unsigned int* error = nullptr;
+    int wall_khz = 0;                      // rate of the device's constant clock
 };
 
 hipError_t launch_reduce(const Plan& p, hipStream_t stream);
 hipError_t launch_copy(const Plan& p, hipStream_t stream);
-hipError_t launch_snac_ag(const Plan& p, const Workspace& ws, hipStream_t stream);
+hipError_t launch_snac(const Plan& p, const Workspace& ws, hipStream_t stream);
 
 }  // namespace atom

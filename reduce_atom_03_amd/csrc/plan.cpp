@@ -449,7 +449,7 @@ atom_status plan_collective(const atom_layout* in, const atom_layout* out, atom_
         return ATOM_ERR_INVALID_ARG;
 
     const bool staged = (c.flags & ATOM_F_STAGED) != 0;
-    if (staged && kind != ATOM_COLL_ALL_GATHER)
+    if (staged && kind != ATOM_COLL_ALL_GATHER && kind != ATOM_COLL_ALL_REDUCE)
         return ATOM_ERR_UNSUPPORTED;
 
     *p = Plan();
@@ -494,6 +494,8 @@ atom_status plan_collective(const atom_layout* in, const atom_layout* out, atom_
         break;
     }
     case ATOM_COLL_ALL_REDUCE: {
+        if (staged)
+            break;   // SNAC plan below
         off[0] = 0;
         off[1] = total;
         build_reduce(p, P, in->bufs, P, out->bufs, 1, off, RM_FANOUT, c);
@@ -528,8 +530,10 @@ atom_status plan_collective(const atom_layout* in, const atom_layout* out, atom_
     }
 
     if (staged) {
-        // SNAC AllGather: chunks of c.chunk bytes of each partition are
-        // staged into a ring of c.slots slots and fanned out from there.
+        // SNAC: chunks of c.chunk bytes of each partition are staged into a
+        // ring of c.slots slots (AllGather: a copy of z_k; AllReduce: the
+        // rank-order sum of partition k over every input, Figure 6) and
+        // fanned out from there to every output.
         const int64_t S = n * es;
         bool vec = (S % kVecBytes) == 0;
         for (int r = 0; r < P; ++r)
@@ -551,7 +555,6 @@ atom_status plan_collective(const atom_layout* in, const atom_layout* out, atom_
         a.nchunks_per_part = ceil_div(S, c.chunk);
         a.nchunks = a.nchunks_per_part * P;
         a.ntasks = 2 * a.nchunks * a.pieces;
-        a.spin_limit = int64_t(1) << 22;
         a.dtype = p->dtype;
         a.nt_store = (c.flags & ATOM_F_NO_NT) ? 0 : 1;
         p->vec = 1;
@@ -561,7 +564,7 @@ atom_status plan_collective(const atom_layout* in, const atom_layout* out, atom_
         p->chunk_bytes = c.chunk;
         p->ring_bytes = c.chunk * c.slots;
         p->grid = std::max<int64_t>(1, std::min<int64_t>(a.ntasks, c.num_wgs ? c.num_wgs : 1024));
-        p->exec = EX_SNAC_AG;
+        p->exec = kind == ATOM_COLL_ALL_GATHER ? EX_SNAC_AG : EX_SNAC_AR;
     }
     return ATOM_OK;
 }

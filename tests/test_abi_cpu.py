@@ -188,9 +188,11 @@ def test_config_validation(field, value):
     assert Q(A.SHARD, A.GATHERED, A.OP_COPY, cfg=cfg)[0] == A.ERR_INVALID_ARG
 
 
-def test_staged_only_for_allgather():
+def test_staged_only_for_allgather_and_allreduce():
     cfg = A.config(flags=A.F_STAGED)
     assert Q(A.SHARD, A.GATHERED, A.OP_COPY, cfg=cfg)[0] == A.OK
+    st, info = Q(A.PARTITIONED, A.GATHERED, A.OP_SUM, cfg=cfg)
+    assert st == A.OK and info.staged == 1 and info.kind == A.COLL_ALL_REDUCE
     assert Q(A.PARTITIONED, A.SHARD, A.OP_SUM, cfg=cfg)[0] == A.ERR_UNSUPPORTED
     assert Q(A.PARTITIONED, A.TRANSPOSED, A.OP_COPY, cfg=cfg)[0] == A.ERR_UNSUPPORTED
     # the staged path needs 16-byte partitions

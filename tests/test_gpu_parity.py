@@ -265,6 +265,28 @@ def test_all_gather_snac_repeated(A):
             assert_bits_equal(from_dev(outs[j]), want, f"rep {rep} out_{j}", nan_by_class=False)
 
 
+@pytest.mark.parametrize("dtype", [synth.BF16, synth.F32])
+@pytest.mark.parametrize("P", [1, 2, 3, 8, 16])
+@pytest.mark.parametrize("n", [8, 40000, 300000])
+def test_all_reduce_snac(A, P, n, dtype):
+    """Composed AllReduce through SNAC (Figure 6): the reduced chunk of each
+    partition is staged once and fanned out; same bits as the oracle."""
+    es = 2 if dtype == synth.BF16 else 4
+    if (n * es) % 16:
+        pytest.skip("the staged path needs 16-byte partitions")
+    say(f"SNAC AR P={P} n={n} {dtype}")
+    xs = [synth.mixed_bits(39, r, P * n, dtype, specials=False) for r in range(P)]
+    want = oracle.all_reduce(xs)
+    dx = [to_dev(x)[1] for x in xs]
+    fulls, outs = out_buffers([P * n] * P, _torch_dtype(dtype), GUARD)
+    cfg = A.config(flags=A.F_STAGED, chunk_bytes=64 << 10, ring_slots=3)
+    A.all_reduce(dx, outs, cfg)
+    assert A.atom_sync_status() == A.OK
+    for j in range(P):
+        _assert_reduced(from_dev(outs[j]), want[j], f"SNAC AR out_{j}")
+    check_guards(fulls, [P * n] * P, GUARD)
+
+
 # ---------------------------------------------------------------- AllToAll
 
 @pytest.mark.parametrize("P", [1, 2, 3, 8, 16])

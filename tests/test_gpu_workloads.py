@@ -67,6 +67,22 @@ def test_c2_all_reduce_full(A, c2):
         assert torch.equal(outs[j].view(torch.int16), outs[0].view(torch.int16)), f"AR out_{j}"
 
 
+def test_c2_all_reduce_snac_full(A, c2):
+    """The composed AllReduce through SNAC (1 MiB chunks, 4 slots) at full size."""
+    import torch
+    P, N = 8, 1 << 27
+    say("c2 SNAC AllReduce 8 x 256 MiB bf16")
+    want = np.concatenate(oracle.reduce_scatter(c2))
+    dx = [to_dev(x)[1] for x in c2]
+    outs = [empty_dev(N, torch.bfloat16) for _ in range(P)]
+    A.all_reduce(dx, outs, A.config(flags=A.F_STAGED, chunk_bytes=1 << 20, ring_slots=4))
+    assert A.atom_sync_status() == A.OK
+    got = from_dev(outs[0])
+    assert_bits_equal(got, want, "c2 SNAC AR out_0")
+    for j in range(1, P):
+        assert torch.equal(outs[j].view(torch.int16), outs[0].view(torch.int16)), f"out_{j}"
+
+
 def test_c3_all_to_all_v_full(A):
     import torch
     say("c3 AllToAllV 8 x 4096 x 7168 bf16")

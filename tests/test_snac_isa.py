@@ -1,0 +1,60 @@
+"""Structure of the SNAC kernels in the gfx950 assembly (CPU only: hipcc
+cross-compiles).
+
+A persistent kernel whose loop contains barriers must leave that loop on a
+wave-uniform branch. If the compiler instead builds a divergent loop (lanes
+leave one at a time through `s_andn2_b64 exec, exec, ...`), lanes other than
+the one that claims the next task re-read a stale ticket and never leave:
+the kernel cannot terminate. The SNAC loop is written so that every branch
+around a barrier is uniform; this test keeps it that way."""
+
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "reduce_atom_03_amd", "csrc", "k_snac.hip")
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    out = tmp_path_factory.mktemp("isa") / "k_snac.s"
+    cmd = ["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I", os.path.join(ROOT, "include"), "-x", "hip", "--cuda-device-only", "-S",
+           SRC, "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        pytest.fail(r.stderr[-2000:])
+    return out.read_text()
+
+
+def _kernels(text):
+    """(name, body) of every k_snac kernel in the assembly."""
+    out = []
+    for m in re.finditer(r"^(_Z\S*k_snac\S*):", text, re.M):
+        end = text.find("s_endpgm", m.end())
+        out.append((m.group(1), text[m.end():end]))
+    return out
+
+
+def test_every_snac_kernel_is_present(asm):
+    names = [n for n, _ in _kernels(asm)]
+    assert any("StageCopy" in n for n in names)
+    assert sum("StageReduce" in n for n in names) == 32      # 2 dtypes x P = 1..16
+
+
+def test_no_divergent_loop_exit(asm):
+    for name, body in _kernels(asm):
+        if "k_snac_reset" in name:
+            continue
+        assert "s_barrier" in body
+        assert not re.search(r"s_andn2_b64\s+exec,\s*exec", body), \
+            f"{name}: a loop with barriers exits on a divergent branch"
+
+
+def test_no_scratch(asm):
+    for m in re.finditer(r"\.name:\s+(\S*k_snac\S*)\n(?:.*\n)*?\s+\.private_segment_fixed_size:\s+(\d+)", asm):
+        assert int(m.group(2)) == 0, m.group(1)
