@@ -4,11 +4,12 @@
 A step is one pass over every collective of the hot path, each on its own
 resident synthetic input (bf16):
 
+  copy    Atom copy of one 256 MiB input (also the counters' calibration kernel)
   rs8     8-way ReduceScatter, 8 x 256 MiB (N(0,1), seed 2)
   ar      fused one-shot AllReduce of the same 8 x 256 MiB
   a2av    AllToAllV MoE dispatch, 8 x 4096 x 7168 (Dirichlet-multinomial counts, seed 3)
   ag_zs   AllGather, zero staging, 8 partitions of 64 MiB (U[-1,1], seed 4)
-  ag_snac AllGather through SNAC, same input, 1 MiB chunks, 4-slot ring
+  ag_snac AllGather through SNAC, same input, 1 MiB chunks, 16-slot ring
   ar_snac composed AllReduce through SNAC (Figure 6) of the 8 x 256 MiB
   dec     decode AllReduce, 8 x b x 7168 for b in 1, 2, 4, 8, 16 (N(0,0.02), seed 5)
   ag_8k   AllGather, zero staging, 8 partitions of 8 KiB
@@ -102,7 +103,7 @@ def main():
     S = args.ag_mib * MiB
     z4 = [up(z) for z in synth.c4_inputs(S, P)]
     ag_out = [empty(P * S // 2) for _ in range(P)]
-    snac_cfg = A.config(flags=A.F_STAGED, chunk_bytes=1 * MiB, ring_slots=4)
+    snac_cfg = A.config(flags=A.F_STAGED, chunk_bytes=1 * MiB)     # ring and grid: defaults
     # decode AllReduce
     x5 = {b: [up(x) for x in synth.c5_inputs(b)] for b in (1, 2, 4, 8, 16)}
     o5 = {b: [empty(b * synth.HIDDEN) for _ in range(P)] for b in (1, 2, 4, 8, 16)}
@@ -124,6 +125,9 @@ def main():
 
     L = A.layout
     rows = []
+    copy_out = empty(N2)
+    rows.append(("copy", lambda: A.atom_copy(copy_out, x2[0]), 2 * N2 * 2))
+    cus["copy"] = 256
     lay = (L(A.PARTITIONED, x2, n2), L(A.SHARD, ys, n2))
     rows.append(("rs8", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_SUM),
                  plan_bytes(lay[0], lay[1], A.OP_SUM, name="rs8")))
@@ -192,6 +196,16 @@ def main():
         b.record(stream)
     torch.cuda.synchronize()
     lat = np.array([a.elapsed_time(b) * 1e3 for a, b in pairs])
+    # Launch floor: the same event pair around a 16-byte atom_copy.
+    tiny_src, tiny_dst = empty(8), empty(8)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.lat_iters)]
+    for a, b in pairs:
+        a.record(stream)
+        A.atom_copy(tiny_dst, tiny_src, 16)
+        b.record(stream)
+    torch.cuda.synchronize()
+    floor = np.array([a.elapsed_time(b) * 1e3 for a, b in pairs])
     # Host-side time per call of the same launch (submission cost).
     t = time.perf_counter()
     for _ in range(args.lat_iters):
@@ -205,7 +219,7 @@ def main():
     achieved = d["credited_bytes"] / (d["ms"] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(achieved * 1e9 / HBM_PEAK, 4),
-                "traffic": None}
+                "traffic": measured_traffic(dom)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -225,10 +239,10 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": ("one pass over: 8-way ReduceScatter and fused AllReduce of 8 x 256 MiB bf16; "
+            "workload": ("one pass over: copy of 256 MiB; 8-way ReduceScatter and fused AllReduce of 8 x 256 MiB bf16; "
                          "AllToAllV 8 x 4096 x 7168 bf16 (Dirichlet-multinomial counts); "
                          f"AllGather 8 x {args.ag_mib} MiB (zero-staging"
-                         + (" and SNAC, 1 MiB chunks, 4 slots); SNAC-composed AllReduce of the "
+                         + (" and SNAC, 1 MiB chunks, 16-slot ring); SNAC-composed AllReduce of the "
                             "8 x 256 MiB; " if args.snac else "); ") +
                          "decode AllReduce 8 x b x 7168 bf16, b = 1..16; AllGather 8 x 8 KiB"),
             "P": P, "step_credited_bytes": int(step_bytes),
@@ -240,12 +254,36 @@ def main():
         "p50_us_8KiB": round(float(np.percentile(lat, 50)), 2),
         "p99_us_8KiB": round(float(np.percentile(lat, 99)), 2),
         "host_us_per_call_8KiB": round(host_us, 2),
+        "p50_us_launch_floor_16B_copy": round(float(np.percentile(floor, 50)), 2),
         "cus_used": cus,
         "rows": per_row,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def measured_traffic(row):
+    """HBM bytes per launch of `row` from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by the copy calibration), or
+    None when the summary is missing or any kernel source changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    for fn, h in d.get("sources", {}).items():
+        src = os.path.join(ROOT, "reduce_atom_03_amd", "csrc", fn)
+        try:
+            with open(src, "rb") as f:
+                if hashlib.sha256(f.read()).hexdigest()[:16] != h:
+                    return None
+        except OSError:
+            return None
+    row_d = d.get("rows", {}).get(row)
+    return int(row_d["traffic_bytes"]) if row_d else None
 
 
 def cpu_baseline(args, C3, S, credited):
@@ -263,6 +301,7 @@ def cpu_baseline(args, C3, S, credited):
     times = []
     for _ in range(args.cpu_reps):
         t = time.perf_counter()
+        oracle.all_gather([c2[0]])          # P = 1 AllGather: a copy
         oracle.reduce_scatter(c2)
         oracle.all_reduce(c2)
         oracle.all_to_all_v(c3, C3, synth.HIDDEN)

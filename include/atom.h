@@ -108,10 +108,14 @@ typedef struct atom_layout {
 typedef struct atom_config {
     int64_t chunk_bytes;       /* SNAC chunk (notify unit); power of two in
                                   [64 KiB, 16 MiB]; default 1 MiB */
-    int32_t stages;            /* 16-byte vectors in flight per lane: 1, 2, 4 or 8 */
+    int32_t stages;            /* 16-byte vectors in flight per lane: 1, 2, 4 or 8
+                                  (0: chosen per collective) */
     int32_t num_wgs;           /* workgroups to launch; 0 = derived from size */
     uint32_t flags;            /* ATOM_F_* */
-    int32_t ring_slots;        /* SNAC ring depth D: 1..16; default 4 */
+    int32_t ring_slots;        /* SNAC ring depth D: 1..64; default: enough
+                                  slots for 16 MiB in flight (at least 4) */
+    int32_t piece_bytes;       /* SNAC task granule: a power of two in
+                                  [16 KiB, chunk]; 0: default */
 } atom_config;
 
 /* The collective that a pair of layouts and an op names (Figure 4/6,

@@ -31,9 +31,11 @@ atom_status workspace(int64_t ring_bytes, Workspace** out)
         if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
             return ATOM_ERR_HIP;
         ws.wall_khz = khz;
-        // ready[kMaxSlots], freed[kMaxSlots], ticket, error in one block.
+        // ready[kMaxSlots], freed[kMaxSlots] (each counter on its own 256-byte
+        // line), then the ticket and the error word on lines of their own.
         char* flags = nullptr;
-        const size_t fbytes = 2 * kMaxSlots * sizeof(unsigned long long) + 2 * sizeof(unsigned int);
+        const size_t line = kFlagStride * sizeof(unsigned long long);
+        const size_t fbytes = (2 * kMaxSlots + 2) * line;
         if (hipMalloc(&flags, fbytes) != hipSuccess)
             return ATOM_ERR_NOMEM;
         if (hipMemset(flags, 0, fbytes) != hipSuccess) {
@@ -41,9 +43,9 @@ atom_status workspace(int64_t ring_bytes, Workspace** out)
             return ATOM_ERR_HIP;
         }
         ws.ready = reinterpret_cast<unsigned long long*>(flags);
-        ws.freed = ws.ready + kMaxSlots;
-        ws.ticket = reinterpret_cast<unsigned int*>(ws.freed + kMaxSlots);
-        ws.error = ws.ticket + 1;
+        ws.freed = ws.ready + kMaxSlots * kFlagStride;
+        ws.ticket = reinterpret_cast<unsigned int*>(flags + 2 * kMaxSlots * line);
+        ws.error = reinterpret_cast<unsigned int*>(flags + (2 * kMaxSlots + 1) * line);
     }
     if (ws.ring_bytes < ring_bytes) {
         // Growing the ring: wait for work that may still use the old one.

@@ -68,9 +68,12 @@ __device__ __forceinline__ Task decode_task(const SnacArgs& a, int64_t t)
 
 // Lane 0 waits until *flag >= target, bounded in wall-clock time (the
 // per-wait bound and the workgroup's whole-kernel budget, both in ticks of
-// the constant-rate device clock); then every wave acquires. The result is
-// made wave-uniform with readfirstlane so every branch on it is uniform.
-// Returns false when the wait gave up (a timeout here or elsewhere).
+// the constant-rate device clock), then acquires at agent scope for the
+// workgroup: the invalidation covers the CU's vector L1, which every wave of
+// the workgroup shares, and the L2 lines the producer's XCD may have
+// written. The result is made wave-uniform with readfirstlane so every
+// branch on it is uniform. Returns false when the wait gave up (a timeout
+// here or elsewhere).
 __device__ __forceinline__ bool wait_at_least(const SnacArgs& a, const unsigned long long* flag,
                                               unsigned long long target, long long t_begin,
                                               int* s_ok)
@@ -81,7 +84,12 @@ __device__ __forceinline__ bool wait_at_least(const SnacArgs& a, const unsigned 
             const long long w0 = wall_clock64();
             unsigned int it = 0;
             while (flag_load_relaxed(flag) < target) {
-                __builtin_amdgcn_s_sleep(1);
+                // Back off: waiting workgroups poll one counter line, and a
+                // poll that misses costs the producers memory bandwidth.
+                if (it < 8)
+                    __builtin_amdgcn_s_sleep(2);
+                else
+                    __builtin_amdgcn_s_sleep(16);
                 if ((++it & 15u) == 0) {
                     const long long now = wall_clock64();
                     if (__hip_atomic_load(a.error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0 ||
@@ -93,13 +101,12 @@ __device__ __forceinline__ bool wait_at_least(const SnacArgs& a, const unsigned 
                 }
             }
         }
+        if (ok)
+            fence_acquire_agent();
         *s_ok = ok;
     }
     __syncthreads();
-    const bool ok = __builtin_amdgcn_readfirstlane(*s_ok) != 0;
-    if (ok)
-        fence_acquire_agent();
-    return ok;
+    return __builtin_amdgcn_readfirstlane(*s_ok) != 0;
 }
 
 // Stage producers: fill `bytes` bytes (a multiple of 16) of a ring slot.
@@ -225,22 +232,25 @@ __global__ __launch_bounds__(256) void k_snac(const SnacArgs a)
         char* slotp = a.ring + slot * C;
         // Stage waits for the slot's previous chunk to be consumed; Consume
         // waits for every piece of its chunk to be staged.
-        const unsigned long long* wflag = task.produce ? a.freed + slot : a.ready + slot;
+        const unsigned long long* wflag = (task.produce ? a.freed : a.ready) + slot * kFlagStride;
         const unsigned long long target =
             static_cast<unsigned long long>(task.produce ? use : use + 1) * a.pieces;
         const bool ok = wait_at_least(a, wflag, target, t_begin, &s_ok);
         if (ok) {
             if (task.produce) {
                 Stage::template produce<U>(a, k, cbeg + pbeg, slotp + pbeg, plen);
-                fence_release_agent();           // this wave's staged stores, at agent scope
             } else {
                 fan_out<U>(a, slotp + pbeg, static_cast<int64_t>(k) * S + cbeg + pbeg, plen);
             }
         }
-        __syncthreads();                         // every wave staged (or read) its share
+        // The barrier waits for every wave's stores to reach the L2 (and its
+        // slot reads to return); lane 0's agent-scope release then writes the
+        // XCD's L2 back before the counter moves, so a consumer on any XCD
+        // that sees the count also sees the staged bytes.
+        __syncthreads();
         if (threadIdx.x == 0) {
             if (ok)                              // Notify (ready) or release the slot (freed)
-                flag_add_release(task.produce ? a.ready + slot : a.freed + slot, 1ull);
+                flag_add_release((task.produce ? a.ready : a.freed) + slot * kFlagStride, 1ull);
             s_ticket = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
@@ -256,8 +266,8 @@ __global__ void k_snac_reset(unsigned long long* ready, unsigned long long* free
 {
     const int i = threadIdx.x;
     if (i < slots) {
-        ready[i] = 0;
-        freed[i] = 0;
+        ready[i * kFlagStride] = 0;
+        freed[i * kFlagStride] = 0;
     }
     if (i == 0)
         *ticket = 0;
@@ -303,7 +313,13 @@ hipError_t launch_snac(const Plan& p, const Workspace& ws, hipStream_t stream)
         return e;
     const dim3 grid(static_cast<unsigned>(p.grid));
     if (p.exec == EX_SNAC_AG) {
-        k_snac<StageCopy, 4><<<grid, dim3(256), 0, stream>>>(a);
+        switch (p.U) {
+        case 1: k_snac<StageCopy, 1><<<grid, dim3(256), 0, stream>>>(a); break;
+        case 2: k_snac<StageCopy, 2><<<grid, dim3(256), 0, stream>>>(a); break;
+        case 4: k_snac<StageCopy, 4><<<grid, dim3(256), 0, stream>>>(a); break;
+        case 8: k_snac<StageCopy, 8><<<grid, dim3(256), 0, stream>>>(a); break;
+        default: return hipErrorInvalidValue;
+        }
         return hipGetLastError();
     }
     return p.dtype == DT_BF16 ? launch_ar_t<uint16_t>(a, grid, stream) : launch_ar_t<float>(a, grid, stream);

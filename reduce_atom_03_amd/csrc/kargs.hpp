@@ -11,6 +11,7 @@ namespace atom {
 constexpr int kMaxRanks = 16;
 constexpr int kMaxSegs = kMaxRanks * kMaxRanks;
 constexpr int kVecBytes = 16;          // one global_load/store_dwordx4
+constexpr int kFlagStride = 32;        // SNAC counters sit 256 bytes apart (u64 units)
 
 enum DType : int32_t { DT_BF16 = 0, DT_F32 = 1 };
 
@@ -65,8 +66,8 @@ struct SnacArgs {
     const void* src[kMaxRanks];        // inputs (z_k, or x_r for AllReduce)
     void* dst[kMaxRanks];              // outputs out_j
     char* ring;                        // D slots of chunk_bytes
-    unsigned long long* ready;         // per slot: pieces staged (monotone in a call)
-    unsigned long long* freed;         // per slot: pieces consumed
+    unsigned long long* ready;         // per slot (stride kFlagStride): pieces staged
+    unsigned long long* freed;         // per slot (stride kFlagStride): pieces consumed
     unsigned int* ticket;              // task counter
     unsigned int* error;               // nonzero after a wait timed out
     int64_t part_bytes;                // bytes of each partition

@@ -12,8 +12,8 @@ namespace atom {
 struct Workspace {
     char* ring = nullptr;
     int64_t ring_bytes = 0;
-    unsigned long long* ready = nullptr;   // kMaxSlots counters
-    unsigned long long* freed = nullptr;   // kMaxSlots counters
+    unsigned long long* ready = nullptr;   // kMaxSlots counters, kFlagStride apart
+    unsigned long long* freed = nullptr;   // kMaxSlots counters, kFlagStride apart
     unsigned int* ticket = nullptr;
     unsigned int* error = nullptr;
     int wall_khz = 0;                      // rate of the device's constant clock

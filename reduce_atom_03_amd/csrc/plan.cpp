@@ -55,6 +55,8 @@ struct Cfg {
     int64_t num_wgs;   // 0 = pick by shape
     uint32_t flags;
     int32_t slots;
+    bool slots_set;    // ring depth given by the caller
+    int64_t piece;     // SNAC task granule; 0 = default
 };
 
 atom_status read_cfg(const atom_config* cfg, Cfg* c)
@@ -64,6 +66,8 @@ atom_status read_cfg(const atom_config* cfg, Cfg* c)
     c->num_wgs = 0;
     c->flags = 0;
     c->slots = kDefaultSlots;
+    c->slots_set = false;
+    c->piece = 0;
     if (!cfg)
         return ATOM_OK;
     if (cfg->chunk_bytes != 0) {
@@ -86,6 +90,12 @@ atom_status read_cfg(const atom_config* cfg, Cfg* c)
         if (cfg->ring_slots < 1 || cfg->ring_slots > kMaxSlots)
             return ATOM_ERR_INVALID_ARG;
         c->slots = cfg->ring_slots;
+        c->slots_set = true;
+    }
+    if (cfg->piece_bytes != 0) {
+        if (!is_pow2(cfg->piece_bytes) || cfg->piece_bytes < (16 << 10) || cfg->piece_bytes > kMaxChunk)
+            return ATOM_ERR_INVALID_ARG;
+        c->piece = cfg->piece_bytes;
     }
     return ATOM_OK;
 }
@@ -121,18 +131,28 @@ bool buffer_ok(const void* p, int64_t bytes, int esize)
     return p != nullptr && aligned(p, static_cast<uintptr_t>(esize));
 }
 
-// Vectors in flight per lane: enough loads outstanding to cover HBM latency
-// without exceeding the register file (U * nsrc 16-byte values per lane).
-// The reduce kernel is built for U in {1, 2, 4}.
-int32_t pick_u_reduce(int nsrc, int32_t stages)
+// 16-byte slots per lane per tile (the Atom pipeline depth). Measured on
+// MI355X with one tile per workgroup: small tiles and many workgroups keep
+// the most bytes in flight for the scatter-reduce and the fan-out copy,
+// while the fan-out reduce (P loads and P stores per slot) prefers deeper
+// tiles. The reduce kernel is built for U in {1, 2, 4} with U * P <= 32.
+int32_t pick_u_reduce(int nsrc, int32_t mode, int32_t stages)
 {
-    int32_t u = stages ? std::min<int32_t>(stages, 4) : (nsrc <= 2 ? 4 : (nsrc <= 8 ? 2 : 1));
+    int32_t u = stages ? std::min<int32_t>(stages, 4)
+                       : (mode == RM_FANOUT ? 4 : (nsrc <= 4 ? 2 : 1));
     while (u > 1 && u * nsrc > 32)
         u /= 2;
     return u;
 }
 
-int32_t pick_u_copy(int32_t stages) { return stages ? stages : 4; }
+int32_t pick_u_copy(int32_t kind, int nseg, int32_t stages)
+{
+    if (stages)
+        return stages;
+    if (nseg == 1)
+        return 4;                           // one flat copy
+    return kind == CK_FANOUT ? 1 : 2;       // AllGather fan-out / AllToAll(V) exchange
+}
 
 int64_t pick_grid(int64_t ntiles, int64_t num_wgs)
 {
@@ -162,8 +182,17 @@ void build_reduce(Plan* p, int nsrc, const void* const* srcs, int ndst, void* co
     }
     const int64_t ve = kVecBytes / es;   // elements per 16-byte slot
     p->vec = vec ? 1 : 0;
-    p->U = vec ? pick_u_reduce(nsrc, c.stages) : 1;
+    p->U = vec ? pick_u_reduce(nsrc, mode, c.stages) : 1;
     p->wg = 256;
+    int64_t slots = 0;
+    for (int k = 0; k < nparts; ++k)
+        slots += ceil_div(part_off[k + 1] - part_off[k], ve);
+    if (slots < kSmallSlots && !c.stages) {
+        // Latency path: spread a small message over as many CUs as it can
+        // use (one slot per lane, 64-lane workgroups).
+        p->U = 1;
+        p->wg = 64;
+    }
     const int64_t slots_per_tile = static_cast<int64_t>(p->wg) * p->U;
     int64_t t = 0;
     for (int k = 0; k < nparts; ++k) {
@@ -199,8 +228,15 @@ void build_copy(Plan* p, int32_t kind, int P, const void* const* srcs, int nsrc,
         vec = vec && aligned(dsts[q], kVecBytes);
     }
     p->vec = vec ? 1 : 0;
-    p->U = vec ? pick_u_copy(c.stages) : 1;
+    p->U = vec ? pick_u_copy(kind, nseg, c.stages) : 1;
     p->wg = 256;
+    int64_t bytes = 0;
+    for (int s = 0; s < nseg; ++s)
+        bytes += cnt[s] * row_bytes;
+    if (bytes < kSmallSlots * kVecBytes && !c.stages) {
+        p->U = 1;                 // latency path, as for the reduce family
+        p->wg = 64;
+    }
     a.tile_bytes = static_cast<int64_t>(p->wg) * p->U * kVecBytes;
     int64_t t = 0;
     for (int s = 0; s < nseg; ++s) {
@@ -549,21 +585,28 @@ atom_status plan_collective(const atom_layout* in, const atom_layout* out, atom_
         a.P = P;
         a.part_bytes = S;
         a.chunk_bytes = c.chunk;
-        a.piece_bytes = std::min<int64_t>(kPieceBytes, c.chunk);
+        a.piece_bytes = std::min<int64_t>(c.piece ? c.piece : kPieceBytes, c.chunk);
         a.pieces = static_cast<int32_t>(c.chunk / a.piece_bytes);
         a.slots = c.slots;
+        if (!c.slots_set) {
+            // Table 3's rule applied to one device: the ring holds at least
+            // one bandwidth-delay product of HBM (8 TB/s) times the cross-XCD
+            // notify round trip (~2 us), i.e. about 16 MiB in flight.
+            const int64_t want = ceil_div(kSnacInflightBytes, c.chunk);
+            a.slots = static_cast<int32_t>(std::max<int64_t>(kDefaultSlots, std::min<int64_t>(kMaxSlots, want)));
+        }
         a.nchunks_per_part = ceil_div(S, c.chunk);
         a.nchunks = a.nchunks_per_part * P;
         a.ntasks = 2 * a.nchunks * a.pieces;
         a.dtype = p->dtype;
         a.nt_store = (c.flags & ATOM_F_NO_NT) ? 0 : 1;
         p->vec = 1;
-        p->U = 4;
         p->wg = 256;
-        p->slots = c.slots;
+        p->U = c.stages ? c.stages : 4;
+        p->slots = a.slots;
         p->chunk_bytes = c.chunk;
-        p->ring_bytes = c.chunk * c.slots;
-        p->grid = std::max<int64_t>(1, std::min<int64_t>(a.ntasks, c.num_wgs ? c.num_wgs : 1024));
+        p->ring_bytes = c.chunk * a.slots;
+        p->grid = std::max<int64_t>(1, std::min<int64_t>(a.ntasks, c.num_wgs ? c.num_wgs : kSnacGrid));
         p->exec = kind == ATOM_COLL_ALL_GATHER ? EX_SNAC_AG : EX_SNAC_AR;
     }
     return ATOM_OK;
