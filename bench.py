@@ -9,9 +9,11 @@ resident synthetic input (bf16):
   ar      fused one-shot AllReduce of the same 8 x 256 MiB
   a2av    AllToAllV MoE dispatch, 8 x 4096 x 7168 (Dirichlet-multinomial counts, seed 3)
   ag_zs   AllGather, zero staging, 8 partitions of 64 MiB (U[-1,1], seed 4)
-  ag_snac AllGather through SNAC, same input, 1 MiB chunks, 16-slot ring
+  ag_snac AllGather through SNAC, same input, 1 MiB chunks, 32-slot ring
   ar_snac composed AllReduce through SNAC (Figure 6) of the 8 x 256 MiB
   dec     decode AllReduce, 8 x b x 7168 for b in 1, 2, 4, 8, 16 (N(0,0.02), seed 5)
+  rsv_zipf ReduceScatterV of the 8 x 256 MiB, Zipf(0.125) partitions (Figure 16)
+  agv_zipf AllGatherV of 512 MiB in Zipf(0.125) partitions
   ag_8k   AllGather, zero staging, 8 partitions of 8 KiB
 
 `value` is the step's credited bytes (every input element read once, every
@@ -54,6 +56,9 @@ def parse():
     ap.add_argument("--ag-mib", type=int, default=64, help="AllGather partition size (MiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--study", action="store_true",
+                    help="instead of the step: Atom copy bandwidth vs workgroups (CUs used) "
+                         "and vs pipeline depth, one JSON line per point")
     ap.add_argument("--no-snac", dest="snac", action="store_false",
                     help="leave out the SNAC-staged AllGather and AllReduce")
     return ap.parse_args()
@@ -74,6 +79,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+    if args.study:
+        study(A, synth, torch, dev)
+        return
 
     def up(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -104,6 +112,10 @@ def main():
     z4 = [up(z) for z in synth.c4_inputs(S, P)]
     ag_out = [empty(P * S // 2) for _ in range(P)]
     snac_cfg = A.config(flags=A.F_STAGED, chunk_bytes=1 * MiB)     # ring and grid: defaults
+    # AllGatherV: 8 x 64 MiB in total, Zipf(0.125) partitions
+    cnt_ag = synth.zipf_partition(P * S // 2, P, 0.125, 8) // 8
+    zv = [up(synth.draw(4, k, int(cnt_ag[k]) * 8, "uniform", synth.BF16)) for k in range(P)]
+    agv_out = [empty(P * S // 2) for _ in range(P)]
     # decode AllReduce
     x5 = {b: [up(x) for x in synth.c5_inputs(b)] for b in (1, 2, 4, 8, 16)}
     o5 = {b: [empty(b * synth.HIDDEN) for _ in range(P)] for b in (1, 2, 4, 8, 16)}
@@ -150,6 +162,15 @@ def main():
         lay = (L(A.PARTITIONED, x5[b], b * 896), L(A.GATHERED, o5[b], b * 896))
         rows.append((f"dec_b{b}", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_SUM),
                      plan_bytes(lay[0], lay[1], A.OP_SUM, name=f"dec_b{b}")))
+    # Variable-length ReduceScatter / AllGather with Zipf(0.125) partitions
+    cnt_rs = synth.zipf_partition(N2, P, 0.125, 8) // 8
+    rsv_out = [empty(int(c) * 8) for c in cnt_rs]
+    lay = (L(A.PARTITIONED, x2, 0, cnt_rs, 8), L(A.SHARD, rsv_out, 0, None, 8))
+    rows.append(("rsv_zipf", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_SUM),
+                 plan_bytes(lay[0], lay[1], A.OP_SUM, name="rsv_zipf")))
+    lay = (L(A.SHARD, zv, 0, cnt_ag, 8), L(A.GATHERED, agv_out, 0, None, 8))
+    rows.append(("agv_zipf", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_COPY),
+                 plan_bytes(lay[0], lay[1], A.OP_COPY, name="agv_zipf")))
     lay8 = (L(A.SHARD, z8, 4096), L(A.GATHERED, o8, 4096))
     ag8 = lambda l=lay8: A.atom_collective(l[0], l[1], A.OP_COPY)
     rows.append(("ag_8k", ag8, plan_bytes(lay8[0], lay8[1], A.OP_COPY, name="ag_8k")))
@@ -242,8 +263,9 @@ def main():
             "workload": ("one pass over: copy of 256 MiB; 8-way ReduceScatter and fused AllReduce of 8 x 256 MiB bf16; "
                          "AllToAllV 8 x 4096 x 7168 bf16 (Dirichlet-multinomial counts); "
                          f"AllGather 8 x {args.ag_mib} MiB (zero-staging"
-                         + (" and SNAC, 1 MiB chunks, 16-slot ring); SNAC-composed AllReduce of the "
+                         + (" and SNAC, 1 MiB chunks, 32-slot ring); SNAC-composed AllReduce of the "
                             "8 x 256 MiB; " if args.snac else "); ") +
+                         "ReduceScatterV and AllGatherV with Zipf(0.125) partitions of the same totals; "
                          "decode AllReduce 8 x b x 7168 bf16, b = 1..16; AllGather 8 x 8 KiB"),
             "P": P, "step_credited_bytes": int(step_bytes),
         },
@@ -261,6 +283,44 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def study(A, synth, torch, dev):
+    """Atom copy of 256 MiB (a one-rank AllGather, so the launch shape can be
+    set): GB/s against workgroups launched (CUs used = min(WGs, 256)) and
+    against pipeline depth (16-byte slots in flight per lane), the one-GPU
+    counterparts of the pages' SM-count and pipeline-depth studies
+    (Figures 3 and 11)."""
+    n = 1 << 27
+    src = torch.from_numpy(synth.draw(2, 0, n, "normal", synth.BF16).view(np.int16)).view(
+        torch.bfloat16).to(dev)
+    dst = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    lin, lout = A.layout(A.SHARD, [src], n), A.layout(A.GATHERED, [dst], n)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def point(wgs, stages):
+        cfg = A.config(num_wgs=wgs, stages=stages)
+        for _ in range(3):
+            A.atom_collective(lin, lout, A.OP_COPY, cfg)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(10):
+            A.atom_collective(lin, lout, A.OP_COPY, cfg)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        st, info = A.atom_plan_query(lin, lout, A.OP_COPY, cfg)
+        gbs = 4 * n / ms / 1e6
+        print(json.dumps({"study": "atom_copy_256MiB", "workgroups": info.num_wgs,
+                          "cus_used": min(256, info.num_wgs), "stages": stages,
+                          "ms": round(ms, 4), "GBps": round(gbs, 1),
+                          "frac_hbm": round(gbs * 1e9 / HBM_PEAK, 4)}), flush=True)
+
+    for wgs in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 0):
+        point(wgs, 4)
+    for wgs in (8, 16, 256, 0):
+        for stages in (1, 2, 4, 8):
+            point(wgs, stages)
 
 
 def measured_traffic(row):
@@ -298,6 +358,9 @@ def cpu_baseline(args, C3, S, credited):
     z4 = synth.c4_inputs(S, P)
     x5 = {b: synth.c5_inputs(b) for b in (1, 2, 4, 8, 16)}
     z8 = synth.c4_inputs(8 << 10, P)
+    cnt_rs = synth.zipf_partition(1 << 27, P, 0.125, 8) // 8
+    cnt_ag = synth.zipf_partition(P * S // 2, P, 0.125, 8) // 8
+    zv = [synth.draw(4, k, int(cnt_ag[k]) * 8, "uniform", synth.BF16) for k in range(P)]
     times = []
     for _ in range(args.cpu_reps):
         t = time.perf_counter()
@@ -311,6 +374,8 @@ def cpu_baseline(args, C3, S, credited):
             oracle.all_reduce(c2)
         for b in (1, 2, 4, 8, 16):
             oracle.all_reduce(x5[b])
+        oracle.reduce_scatter_v(c2, cnt_rs * 8)
+        oracle.all_gather_v(zv)
         oracle.all_gather(z8)
         times.append(time.perf_counter() - t)
     best = float(np.median(times))

@@ -113,9 +113,13 @@ typedef struct atom_config {
     int32_t num_wgs;           /* workgroups to launch; 0 = derived from size */
     uint32_t flags;            /* ATOM_F_* */
     int32_t ring_slots;        /* SNAC ring depth D: 1..64; default: enough
-                                  slots for 16 MiB in flight (at least 4) */
+                                  slots for 32 MiB in flight (at least 4) */
     int32_t piece_bytes;       /* SNAC task granule: a power of two in
                                   [16 KiB, chunk]; 0: default */
+    int32_t wait_us;           /* bound of one SNAC wait in microseconds; 0:
+                                  1 s. On expiry the kernel records a timeout
+                                  (see atom_sync_status), drops the waiting
+                                  task and drains; the output is incomplete. */
 } atom_config;
 
 /* The collective that a pair of layouts and an op names (Figure 4/6,

@@ -53,6 +53,7 @@ class AtomConfig(ctypes.Structure):
         ("flags", ctypes.c_uint32),
         ("ring_slots", ctypes.c_int32),
         ("piece_bytes", ctypes.c_int32),
+        ("wait_us", ctypes.c_int32),
     ]
 
 
@@ -182,9 +183,10 @@ def _flatten(c):
 
 
 def config(chunk_bytes: int = 0, stages: int = 0, num_wgs: int = 0, flags: int = 0,
-           ring_slots: int = 0, piece_bytes: int = 0) -> AtomConfig:
+           ring_slots: int = 0, piece_bytes: int = 0, wait_us: int = 0) -> AtomConfig:
     return AtomConfig(chunk_bytes=chunk_bytes, stages=stages, num_wgs=num_wgs,
-                      flags=flags, ring_slots=ring_slots, piece_bytes=piece_bytes)
+                      flags=flags, ring_slots=ring_slots, piece_bytes=piece_bytes,
+                      wait_us=wait_us)
 
 
 # --------------------------------------------------------- the C entry points

@@ -27,6 +27,8 @@
 // always proceed: no deadlock for any grid size or occupancy. Every wait is
 // bounded; on expiry the error word is set, the task is dropped, and later
 // waits give up at once, so the grid always drains.
+#include <algorithm>
+
 #include "atom_dev.hpp"
 #include "launch.hpp"
 
@@ -68,15 +70,15 @@ __device__ __forceinline__ Task decode_task(const SnacArgs& a, int64_t t)
 
 // Lane 0 waits until *flag >= target, bounded in wall-clock time (the
 // per-wait bound and the workgroup's whole-kernel budget, both in ticks of
-// the constant-rate device clock), then acquires at agent scope for the
-// workgroup: the invalidation covers the CU's vector L1, which every wave of
-// the workgroup shares, and the L2 lines the producer's XCD may have
-// written. The result is made wave-uniform with readfirstlane so every
+// the constant-rate device clock), then, when the wait guards data that the
+// workgroup will read, acquires at agent scope for the workgroup: the
+// invalidation covers the CU's vector L1, which every wave of the workgroup
+// shares, and the L2 lines the producer's XCD may have written. The result is made wave-uniform with readfirstlane so every
 // branch on it is uniform. Returns false when the wait gave up (a timeout
 // here or elsewhere).
 __device__ __forceinline__ bool wait_at_least(const SnacArgs& a, const unsigned long long* flag,
                                               unsigned long long target, long long t_begin,
-                                              int* s_ok)
+                                              bool acquire, int* s_ok)
 {
     if (threadIdx.x == 0) {
         int ok = 1;
@@ -101,7 +103,7 @@ __device__ __forceinline__ bool wait_at_least(const SnacArgs& a, const unsigned 
                 }
             }
         }
-        if (ok)
+        if (ok && acquire)
             fence_acquire_agent();
         *s_ok = ok;
     }
@@ -230,12 +232,13 @@ __global__ __launch_bounds__(256) void k_snac(const SnacArgs a)
         int64_t plen = clen - pbeg;
         plen = plen < 0 ? 0 : (plen > a.piece_bytes ? a.piece_bytes : plen);
         char* slotp = a.ring + slot * C;
-        // Stage waits for the slot's previous chunk to be consumed; Consume
-        // waits for every piece of its chunk to be staged.
+        // Stage waits for the slot's previous chunk to be consumed (no data
+        // to acquire: it only overwrites); Consume waits for every piece of
+        // its chunk to be staged and acquires the staged bytes.
         const unsigned long long* wflag = (task.produce ? a.freed : a.ready) + slot * kFlagStride;
         const unsigned long long target =
             static_cast<unsigned long long>(task.produce ? use : use + 1) * a.pieces;
-        const bool ok = wait_at_least(a, wflag, target, t_begin, &s_ok);
+        const bool ok = wait_at_least(a, wflag, target, t_begin, !task.produce, &s_ok);
         if (ok) {
             if (task.produce) {
                 Stage::template produce<U>(a, k, cbeg + pbeg, slotp + pbeg, plen);
@@ -243,14 +246,20 @@ __global__ __launch_bounds__(256) void k_snac(const SnacArgs a)
                 fan_out<U>(a, slotp + pbeg, static_cast<int64_t>(k) * S + cbeg + pbeg, plen);
             }
         }
-        // The barrier waits for every wave's stores to reach the L2 (and its
-        // slot reads to return); lane 0's agent-scope release then writes the
-        // XCD's L2 back before the counter moves, so a consumer on any XCD
-        // that sees the count also sees the staged bytes.
+        // The barrier waits for every wave's stores to reach the L2 and for
+        // its slot reads to return. Notify: lane 0's agent-scope release then
+        // writes the XCD's L2 back before `ready` moves, so a consumer on any
+        // XCD that sees the count also sees the staged bytes. Releasing the
+        // slot publishes no data: the slot reads have already returned (their
+        // values were stored before the barrier), so `freed` moves with a
+        // relaxed increment and no write-back.
         __syncthreads();
         if (threadIdx.x == 0) {
-            if (ok)                              // Notify (ready) or release the slot (freed)
-                flag_add_release((task.produce ? a.ready : a.freed) + slot * kFlagStride, 1ull);
+            if (ok && task.produce)
+                flag_add_release(a.ready + slot * kFlagStride, 1ull);
+            else if (ok)
+                __hip_atomic_fetch_add(a.freed + slot * kFlagStride, 1ull, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
             s_ticket = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
@@ -304,8 +313,9 @@ hipError_t launch_snac(const Plan& p, const Workspace& ws, hipStream_t stream)
     a.freed = ws.freed;
     a.ticket = ws.ticket;
     a.error = ws.error;
-    // Bounds in device-clock ticks: ~1 s per wait, ~10 s per workgroup.
-    a.wait_ticks = static_cast<int64_t>(ws.wall_khz) * 1000;
+    // Bounds in device-clock ticks (kHz x ms): the planned wait bound (1 s
+    // unless the caller shortened it) and ~10 s per workgroup.
+    a.wait_ticks = std::max<int64_t>(1, static_cast<int64_t>(ws.wall_khz) * p.sa.wait_ticks / 1000);
     a.budget_ticks = static_cast<int64_t>(ws.wall_khz) * 10000;
     k_snac_reset<<<1, 64, 0, stream>>>(ws.ready, ws.freed, ws.ticket, a.slots);
     hipError_t e = hipGetLastError();

@@ -76,7 +76,8 @@ struct SnacArgs {
     int64_t nchunks_per_part;
     int64_t nchunks;                   // P * nchunks_per_part
     int64_t ntasks;
-    int64_t wait_ticks;                // bound of one wait, device-clock ticks
+    int64_t wait_ticks;                // bound of one wait: microseconds when
+                                       // planned, device-clock ticks at launch
     int64_t budget_ticks;              // bound of a workgroup's whole run
     int32_t P;
     int32_t pieces;                    // G pieces per chunk

@@ -57,6 +57,7 @@ struct Cfg {
     int32_t slots;
     bool slots_set;    // ring depth given by the caller
     int64_t piece;     // SNAC task granule; 0 = default
+    int64_t wait_us;   // bound of one SNAC wait
 };
 
 atom_status read_cfg(const atom_config* cfg, Cfg* c)
@@ -68,6 +69,7 @@ atom_status read_cfg(const atom_config* cfg, Cfg* c)
     c->slots = kDefaultSlots;
     c->slots_set = false;
     c->piece = 0;
+    c->wait_us = kDefaultWaitUs;
     if (!cfg)
         return ATOM_OK;
     if (cfg->chunk_bytes != 0) {
@@ -97,6 +99,10 @@ atom_status read_cfg(const atom_config* cfg, Cfg* c)
             return ATOM_ERR_INVALID_ARG;
         c->piece = cfg->piece_bytes;
     }
+    if (cfg->wait_us < 0)
+        return ATOM_ERR_INVALID_ARG;
+    if (cfg->wait_us > 0)
+        c->wait_us = cfg->wait_us;
     return ATOM_OK;
 }
 
@@ -591,7 +597,7 @@ atom_status plan_collective(const atom_layout* in, const atom_layout* out, atom_
         if (!c.slots_set) {
             // Table 3's rule applied to one device: the ring holds at least
             // one bandwidth-delay product of HBM (8 TB/s) times the cross-XCD
-            // notify round trip (~2 us), i.e. about 16 MiB in flight.
+            // stage-notify-consume round trip (~4 us measured), about 32 MiB.
             const int64_t want = ceil_div(kSnacInflightBytes, c.chunk);
             a.slots = static_cast<int32_t>(std::max<int64_t>(kDefaultSlots, std::min<int64_t>(kMaxSlots, want)));
         }
@@ -600,6 +606,7 @@ atom_status plan_collective(const atom_layout* in, const atom_layout* out, atom_
         a.ntasks = 2 * a.nchunks * a.pieces;
         a.dtype = p->dtype;
         a.nt_store = (c.flags & ATOM_F_NO_NT) ? 0 : 1;
+        a.wait_ticks = c.wait_us;         // converted to clock ticks at launch
         p->vec = 1;
         p->wg = 256;
         p->U = c.stages ? c.stages : 4;

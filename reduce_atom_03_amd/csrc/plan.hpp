@@ -45,10 +45,11 @@ constexpr int64_t kMaxChunk = 16 << 20;
 constexpr int32_t kDefaultSlots = 4;
 constexpr int32_t kMaxSlots = 64;
 constexpr int64_t kPieceBytes = 64 << 10;            // SNAC task granule
-constexpr int64_t kSnacInflightBytes = 16 << 20;     // default ring: one on-chip BDP
-constexpr int64_t kSnacGrid = 512;                   // persistent SNAC workgroups
+constexpr int64_t kSnacInflightBytes = 32 << 20;     // default ring: one on-chip BDP
+constexpr int64_t kSnacGrid = 768;                   // persistent SNAC workgroups
 constexpr int64_t kMaxGrid = 1 << 20;
 constexpr int64_t kSmallSlots = 256 * 256;           // below: the latency path
+constexpr int64_t kDefaultWaitUs = 1000000;          // one SNAC wait: 1 s
 
 atom_status plan_copy(void* dst, const void* src, size_t bytes, const atom_config* cfg,
                       Plan* p);

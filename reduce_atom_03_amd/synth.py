@@ -189,3 +189,21 @@ def mixed_bits(seed: int, rank: int, count: int, dtype: str,
     if dtype == BF16:
         return bits.astype(np.uint16)
     return bits.view(np.float32)
+
+
+def zipf_partition(total: int, P: int, s: float = 0.125, unit: int = 1) -> np.ndarray:
+    """Sizes of P partitions in Zipf proportion: partition k gets a share
+    proportional to (k + 1) ** -s of `total` elements, in whole multiples of
+    `unit` (total must be a multiple of unit). Shares are floored and the
+    remainder goes to the largest fractional parts, so the sizes sum to
+    `total` exactly. s = 0 gives equal partitions."""
+    if total % unit:
+        raise ValueError("total must be a multiple of unit")
+    units = total // unit
+    w = (np.arange(1, P + 1, dtype=np.float64)) ** (-float(s))
+    share = units * w / w.sum()
+    base = np.floor(share).astype(np.int64)
+    rest = int(units - base.sum())
+    order = np.argsort(-(share - base), kind="stable")
+    base[order[:rest]] += 1
+    return base * unit

@@ -182,7 +182,7 @@ def test_collective_validation_errors():
 @pytest.mark.parametrize("field,value", [
     ("chunk_bytes", 3 * MiB), ("chunk_bytes", 32 << 10), ("chunk_bytes", 32 * MiB),
     ("stages", 3), ("stages", 16), ("num_wgs", -1), ("flags", 0x80), ("ring_slots", 65),
-    ("ring_slots", -2), ("piece_bytes", 3000), ("piece_bytes", 8 << 10)])
+    ("ring_slots", -2), ("piece_bytes", 3000), ("piece_bytes", 8 << 10), ("wait_us", -1)])
 def test_config_validation(field, value):
     cfg = A.config(**{field: value})
     assert Q(A.SHARD, A.GATHERED, A.OP_COPY, cfg=cfg)[0] == A.ERR_INVALID_ARG
@@ -255,9 +255,9 @@ def test_zero_sized_collective_launches_nothing():
 
 
 def test_snac_default_ring_holds_one_onchip_bdp():
-    """Without ring_slots the ring holds 16 MiB (HBM rate x notify round
-    trip), in at least 4 slots."""
-    for chunk, slots in ((512 << 10, 32), (MiB, 16), (2 * MiB, 8), (16 * MiB, 4), (64 << 10, 64)):
+    """Without ring_slots the ring holds 32 MiB (HBM rate x notify round
+    trip), in at least 4 and at most 64 slots."""
+    for chunk, slots in ((512 << 10, 64), (MiB, 32), (2 * MiB, 16), (16 * MiB, 4), (64 << 10, 64)):
         cfg = A.config(flags=A.F_STAGED, chunk_bytes=chunk)
         st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=8, n=(64 * MiB) // 2, cfg=cfg,
                      ins=fake(8, 64 * MiB), outs=fake(8, 512 * MiB, start=BASE + (1 << 40)))

@@ -287,6 +287,29 @@ def test_all_reduce_snac(A, P, n, dtype):
     check_guards(fulls, [P * n] * P, GUARD)
 
 
+def test_snac_timeout_is_reported_and_drains(A):
+    """Failure handling forced from the host: a 1-microsecond wait bound on a
+    one-slot ring makes producers and consumers give up. The kernel must
+    record the timeout, drain every task and exit; atom_sync_status reports
+    it once; the next call with the default bound is complete and correct."""
+    P, S = 8, 4 << 20
+    n = S // 2
+    zs = synth.c4_inputs(S, P)
+    dz = [to_dev(z)[1] for z in zs]
+    outs = [empty_dev(P * n, _torch_dtype(synth.BF16), 0xFFFF) for _ in range(P)]
+    say("SNAC AG with a 1 us wait bound (expected timeout)")
+    A.all_gather(dz, outs, A.config(flags=A.F_STAGED, chunk_bytes=64 << 10, ring_slots=1,
+                                    wait_us=1))
+    assert A.atom_sync_status() == A.ERR_TIMEOUT
+    assert A.atom_sync_status() == A.OK            # reported once, then cleared
+    say("SNAC AG with the default wait bound after a timeout")
+    A.all_gather(dz, outs, A.config(flags=A.F_STAGED, chunk_bytes=64 << 10, ring_slots=1))
+    assert A.atom_sync_status() == A.OK
+    want = np.concatenate(zs)
+    for j in range(P):
+        assert_bits_equal(from_dev(outs[j]), want, f"after timeout out_{j}", nan_by_class=False)
+
+
 # ---------------------------------------------------------------- AllToAll
 
 @pytest.mark.parametrize("P", [1, 2, 3, 8, 16])
@@ -364,6 +387,34 @@ def test_v_collectives(A, dtype, row):
     _sync()
     for j in range(P):
         assert_bits_equal(from_dev(outs[j]), want[j], f"AGV out_{j}", nan_by_class=False)
+
+
+@pytest.mark.parametrize("dtype", [synth.BF16, synth.F32])
+@pytest.mark.parametrize("P", [2, 8, 16])
+def test_v_collectives_zipf(A, dtype, P):
+    """Figure 16's variable-length workload shape: Zipf(s = 0.125) partition
+    sizes, in rows of 8 elements (16-byte partitions for bf16)."""
+    T = 8 * 5003 * P
+    cnt = synth.zipf_partition(T, P, 0.125, 8) // 8
+    say(f"Zipf RSV/AGV P={P} rows={cnt.tolist()} {dtype}")
+    xs = [synth.mixed_bits(73, r, T, dtype, specials=False) for r in range(P)]
+    want = oracle.reduce_scatter_v(xs, cnt * 8)
+    dx = [to_dev(x)[1] for x in xs]
+    fulls, ys = out_buffers([int(c) * 8 for c in cnt], _torch_dtype(dtype), GUARD)
+    A.reduce_scatter_v(dx, ys, cnt, 8)
+    _sync()
+    for k in range(P):
+        _assert_reduced(from_dev(ys[k]), want[k], f"Zipf RSV y_{k}")
+    check_guards(fulls, [int(c) * 8 for c in cnt], GUARD)
+    zs = [synth.mixed_bits(74, k, int(cnt[k]) * 8, dtype) for k in range(P)]
+    want = oracle.all_gather_v(zs)
+    dz = [to_dev(z)[1] for z in zs]
+    fulls, outs = out_buffers([T] * P, _torch_dtype(dtype), GUARD)
+    A.all_gather_v(dz, outs, cnt, 8)
+    _sync()
+    for j in range(P):
+        assert_bits_equal(from_dev(outs[j]), want[j], f"Zipf AGV out_{j}", nan_by_class=False)
+    check_guards(fulls, [T] * P, GUARD)
 
 
 # ------------------------------------------------------------- side stream

@@ -83,6 +83,40 @@ def test_c2_all_reduce_snac_full(A, c2):
         assert torch.equal(outs[j].view(torch.int16), outs[0].view(torch.int16)), f"out_{j}"
 
 
+def test_zipf_reduce_scatter_v_full(A, c2):
+    """ReduceScatterV of the 8 x 256 MiB inputs with Zipf(0.125) partitions
+    (Figure 16's shape), every output element against the oracle."""
+    import torch
+    P, N = 8, 1 << 27
+    cnt = synth.zipf_partition(N, P, 0.125, 8) // 8
+    say(f"Zipf RSV 8 x 256 MiB rows={cnt.tolist()}")
+    want = oracle.reduce_scatter_v(c2, cnt * 8)
+    dx = [to_dev(x)[1] for x in c2]
+    ys = [empty_dev(int(c) * 8, torch.bfloat16) for c in cnt]
+    A.reduce_scatter_v(dx, ys, cnt, 8)
+    torch.cuda.synchronize()
+    for k in range(P):
+        assert_bits_equal(from_dev(ys[k]), want[k], f"Zipf RSV y_{k}")
+
+
+def test_zipf_all_gather_v_full(A):
+    """AllGatherV of 512 MiB in Zipf(0.125) partitions: 8 outputs of 512 MiB,
+    every block compared on the device."""
+    import torch
+    P, T = 8, 1 << 28
+    cnt = synth.zipf_partition(T, P, 0.125, 8) // 8
+    say(f"Zipf AGV total 512 MiB rows={cnt.tolist()}")
+    zs = [to_dev(synth.draw(4, k, int(cnt[k]) * 8, "uniform", synth.BF16))[1] for k in range(P)]
+    outs = [empty_dev(T, torch.bfloat16, 0xFFFF) for _ in range(P)]
+    A.all_gather_v(zs, outs, cnt, 8)
+    torch.cuda.synchronize()
+    off = np.concatenate([[0], np.cumsum(cnt * 8)])
+    for j in range(P):
+        for k in range(P):
+            assert torch.equal(outs[j][off[k]:off[k + 1]].view(torch.int16),
+                               zs[k].view(torch.int16)), f"out_{j} block {k}"
+
+
 def test_c3_all_to_all_v_full(A):
     import torch
     say("c3 AllToAllV 8 x 4096 x 7168 bf16")
