@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--study", action="store_true",
                     help="instead of the step: Atom copy bandwidth vs workgroups (CUs used) "
                          "and vs pipeline depth, one JSON line per point")
+    ap.add_argument("--xcd-order", action="store_true",
+                    help="zero-staging kernels give each XCD one contiguous range of tiles")
     ap.add_argument("--no-snac", dest="snac", action="store_false",
                     help="leave out the SNAC-staged AllGather and AllReduce")
     return ap.parse_args()
@@ -136,22 +138,23 @@ def main():
         return info.credited_bytes
 
     L = A.layout
+    zs_cfg = A.config(flags=A.F_XCD_ORDER) if args.xcd_order else None
     rows = []
     copy_out = empty(N2)
     rows.append(("copy", lambda: A.atom_copy(copy_out, x2[0]), 2 * N2 * 2))
     cus["copy"] = 256
     lay = (L(A.PARTITIONED, x2, n2), L(A.SHARD, ys, n2))
-    rows.append(("rs8", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_SUM),
-                 plan_bytes(lay[0], lay[1], A.OP_SUM, name="rs8")))
+    rows.append(("rs8", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_SUM, zs_cfg),
+                 plan_bytes(lay[0], lay[1], A.OP_SUM, zs_cfg, name="rs8")))
     lay = (L(A.PARTITIONED, x2, n2), L(A.GATHERED, ar_out, n2))
-    rows.append(("ar", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_SUM),
-                 plan_bytes(lay[0], lay[1], A.OP_SUM, name="ar")))
+    rows.append(("ar", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_SUM, zs_cfg),
+                 plan_bytes(lay[0], lay[1], A.OP_SUM, zs_cfg, name="ar")))
     lay = (L(A.PARTITIONED, x3, 0, C3, synth.HIDDEN), L(A.TRANSPOSED, a2a_out, 0, None, synth.HIDDEN))
-    rows.append(("a2av", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_COPY),
-                 plan_bytes(lay[0], lay[1], A.OP_COPY, name="a2av")))
+    rows.append(("a2av", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_COPY, zs_cfg),
+                 plan_bytes(lay[0], lay[1], A.OP_COPY, zs_cfg, name="a2av")))
     lay = (L(A.SHARD, z4, S // 2), L(A.GATHERED, ag_out, S // 2))
-    rows.append(("ag_zs", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_COPY),
-                 plan_bytes(lay[0], lay[1], A.OP_COPY, name="ag_zs")))
+    rows.append(("ag_zs", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_COPY, zs_cfg),
+                 plan_bytes(lay[0], lay[1], A.OP_COPY, zs_cfg, name="ag_zs")))
     if args.snac:
         rows.append(("ag_snac", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_COPY, snac_cfg),
                      plan_bytes(lay[0], lay[1], A.OP_COPY, snac_cfg, name="ag_snac")))
@@ -166,11 +169,11 @@ def main():
     cnt_rs = synth.zipf_partition(N2, P, 0.125, 8) // 8
     rsv_out = [empty(int(c) * 8) for c in cnt_rs]
     lay = (L(A.PARTITIONED, x2, 0, cnt_rs, 8), L(A.SHARD, rsv_out, 0, None, 8))
-    rows.append(("rsv_zipf", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_SUM),
-                 plan_bytes(lay[0], lay[1], A.OP_SUM, name="rsv_zipf")))
+    rows.append(("rsv_zipf", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_SUM, zs_cfg),
+                 plan_bytes(lay[0], lay[1], A.OP_SUM, zs_cfg, name="rsv_zipf")))
     lay = (L(A.SHARD, zv, 0, cnt_ag, 8), L(A.GATHERED, agv_out, 0, None, 8))
-    rows.append(("agv_zipf", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_COPY),
-                 plan_bytes(lay[0], lay[1], A.OP_COPY, name="agv_zipf")))
+    rows.append(("agv_zipf", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_COPY, zs_cfg),
+                 plan_bytes(lay[0], lay[1], A.OP_COPY, zs_cfg, name="agv_zipf")))
     lay8 = (L(A.SHARD, z8, 4096), L(A.GATHERED, o8, 4096))
     ag8 = lambda l=lay8: A.atom_collective(l[0], l[1], A.OP_COPY)
     rows.append(("ag_8k", ag8, plan_bytes(lay8[0], lay8[1], A.OP_COPY, name="ag_8k")))

@@ -105,6 +105,9 @@ typedef struct atom_layout {
 /* Execution options; NULL means defaults. Zero fields take defaults too. */
 #define ATOM_F_STAGED 0x1u     /* run through SNAC with a staging ring */
 #define ATOM_F_NO_NT  0x2u     /* use ordinary (cached) stores for outputs */
+#define ATOM_F_XCD_ORDER 0x4u /* zero-staging kernels give each XCD one
+                                 contiguous range of tiles (default: plain
+                                 workgroup order; measured within noise) */
 typedef struct atom_config {
     int64_t chunk_bytes;       /* SNAC chunk (notify unit); power of two in
                                   [64 KiB, 16 MiB]; default 1 MiB */
@@ -199,6 +202,10 @@ int64_t atom_bdp_chunk_bytes(double bytes_per_s, double round_trip_s);
 
 /* A static, human-readable name for a status code. */
 const char* atom_status_string(atom_status s);
+
+/* The HIP runtime's description of the error behind this thread's last
+ * ATOM_ERR_HIP (a static string; "no HIP error" if there was none). */
+const char* atom_last_error(void);
 
 /* Library version, (major << 16) | minor. */
 int32_t atom_version(void);

@@ -26,7 +26,7 @@ OP_COPY, OP_SUM = 0, 1
 # atom_layout_kind
 PARTITIONED, SHARD, GATHERED, TRANSPOSED = 0, 1, 2, 3
 # atom_config flags
-F_STAGED, F_NO_NT = 0x1, 0x2
+F_STAGED, F_NO_NT, F_XCD_ORDER = 0x1, 0x2, 0x4
 # atom_collective_kind
 COLL_NONE, COLL_REDUCE_SCATTER, COLL_ALL_GATHER, COLL_ALL_TO_ALL, \
     COLL_ALL_TO_ALL_V, COLL_ALL_REDUCE, COLL_REDUCE_SCATTER_V, \
@@ -75,14 +75,30 @@ class AtomPlanInfo(ctypes.Structure):
 
 EXPORTS = ("atom_copy", "atom_reduce", "atom_collective", "atom_plan_query",
            "atom_sync_status", "atom_bdp_chunk_bytes", "atom_status_string",
-           "atom_version")
+           "atom_last_error", "atom_version")
+
+
+def _hip_runtimes() -> set:
+    """Paths of the HIP runtime libraries mapped into this process."""
+    try:
+        with open("/proc/self/maps") as f:
+            return {line.split()[-1] for line in f if "libamdhip64" in line}
+    except OSError:
+        return set()
 
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"libatom not built: {LIB_PATH} is missing (run __graft_entry__.build())")
+    # torch ships its own HIP runtime. Load it first so that libatom binds to
+    # that same runtime (same soname); loaded the other way round, the process
+    # would map two HIP/HSA runtimes and the second sees no device.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
+    if len(_hip_runtimes()) > 1:
+        raise ImportError("two HIP runtimes are mapped into this process: "
+                          + ", ".join(sorted(_hip_runtimes())))
     vp = ctypes.c_void_p
     lib.atom_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
     lib.atom_copy.restype = ctypes.c_int
@@ -101,6 +117,8 @@ def _load() -> ctypes.CDLL:
     lib.atom_bdp_chunk_bytes.restype = ctypes.c_int64
     lib.atom_status_string.argtypes = [ctypes.c_int]
     lib.atom_status_string.restype = ctypes.c_char_p
+    lib.atom_last_error.argtypes = []
+    lib.atom_last_error.restype = ctypes.c_char_p
     lib.atom_version.argtypes = []
     lib.atom_version.restype = ctypes.c_int32
     return lib
@@ -111,7 +129,8 @@ lib = _load()
 
 class AtomError(RuntimeError):
     def __init__(self, status: int, what: str):
-        super().__init__(f"{what}: {atom_status_string(status)} ({status})")
+        detail = f" [{atom_last_error()}]" if status == ERR_HIP else ""
+        super().__init__(f"{what}: {atom_status_string(status)} ({status}){detail}")
         self.status = status
 
 
@@ -193,6 +212,10 @@ def config(chunk_bytes: int = 0, stages: int = 0, num_wgs: int = 0, flags: int =
 
 def atom_status_string(status: int) -> str:
     return lib.atom_status_string(int(status)).decode()
+
+
+def atom_last_error() -> str:
+    return lib.atom_last_error().decode()
 
 
 def atom_version() -> int:

@@ -17,19 +17,33 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::mutex g_ws_mutex;
 Workspace g_ws[kMaxDevices];
+thread_local hipError_t t_last_hip = hipSuccess;   // detail of this thread's last ATOM_ERR_HIP
+
+atom_status hip_status(hipError_t e)
+{
+    if (e == hipSuccess)
+        return ATOM_OK;
+    t_last_hip = e;
+    return ATOM_ERR_HIP;
+}
 
 // The workspace of the current device, with a ring of at least ring_bytes.
 atom_status workspace(int64_t ring_bytes, Workspace** out)
 {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
-        return ATOM_ERR_HIP;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess)
+        return hip_status(e);
+    if (dev < 0 || dev >= kMaxDevices)
+        return ATOM_ERR_UNSUPPORTED;
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace& ws = g_ws[dev];
     if (!ws.ready) {
         int khz = 0;
-        if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
-            return ATOM_ERR_HIP;
+        if (hipError_t e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+            e != hipSuccess)
+            return hip_status(e);
+        if (khz <= 0)
+            return ATOM_ERR_UNSUPPORTED;
         ws.wall_khz = khz;
         // ready[kMaxSlots], freed[kMaxSlots] (each counter on its own 256-byte
         // line), then the ticket and the error word on lines of their own.
@@ -38,9 +52,9 @@ atom_status workspace(int64_t ring_bytes, Workspace** out)
         const size_t fbytes = (2 * kMaxSlots + 2) * line;
         if (hipMalloc(&flags, fbytes) != hipSuccess)
             return ATOM_ERR_NOMEM;
-        if (hipMemset(flags, 0, fbytes) != hipSuccess) {
+        if (hipError_t e = hipMemset(flags, 0, fbytes); e != hipSuccess) {
             (void)hipFree(flags);
-            return ATOM_ERR_HIP;
+            return hip_status(e);
         }
         ws.ready = reinterpret_cast<unsigned long long*>(flags);
         ws.freed = ws.ready + kMaxSlots * kFlagStride;
@@ -50,8 +64,8 @@ atom_status workspace(int64_t ring_bytes, Workspace** out)
     if (ws.ring_bytes < ring_bytes) {
         // Growing the ring: wait for work that may still use the old one.
         if (ws.ring) {
-            if (hipDeviceSynchronize() != hipSuccess)
-                return ATOM_ERR_HIP;
+            if (hipError_t e = hipDeviceSynchronize(); e != hipSuccess)
+                return hip_status(e);
             (void)hipFree(ws.ring);
             ws.ring = nullptr;
             ws.ring_bytes = 0;
@@ -70,6 +84,11 @@ atom_status run(const Plan& p, void* stream)
 {
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
+    // A launch is checked with hipGetLastError, which also returns an error
+    // left behind by an earlier runtime call of this thread (ours or another
+    // library's); clear it so the status describes this call only.
+    if (p.exec != EX_NONE)
+        (void)hipGetLastError();
     switch (p.exec) {
     case EX_NONE:
         return ATOM_OK;
@@ -91,7 +110,7 @@ atom_status run(const Plan& p, void* stream)
     default:
         return ATOM_ERR_UNSUPPORTED;
     }
-    return e == hipSuccess ? ATOM_OK : ATOM_ERR_HIP;
+    return hip_status(e);
 }
 
 }  // namespace
@@ -136,11 +155,13 @@ atom_status atom_plan_query(const atom_layout* in, const atom_layout* out, atom_
 
 atom_status atom_sync_status(void* stream)
 {
-    if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)
-        return ATOM_ERR_HIP;
+    if (hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream)); e != hipSuccess)
+        return atom::hip_status(e);
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= atom::kMaxDevices)
-        return ATOM_ERR_HIP;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess)
+        return atom::hip_status(e);
+    if (dev < 0 || dev >= atom::kMaxDevices)
+        return ATOM_ERR_UNSUPPORTED;
     unsigned int* err = nullptr;
     {
         std::lock_guard<std::mutex> lock(atom::g_ws_mutex);
@@ -149,14 +170,19 @@ atom_status atom_sync_status(void* stream)
     if (!err)
         return ATOM_OK;   // no SNAC call has run on this device
     unsigned int host = 0;
-    if (hipMemcpy(&host, err, sizeof host, hipMemcpyDeviceToHost) != hipSuccess)
-        return ATOM_ERR_HIP;
+    if (hipError_t e = hipMemcpy(&host, err, sizeof host, hipMemcpyDeviceToHost); e != hipSuccess)
+        return atom::hip_status(e);
     if (host == 0)
         return ATOM_OK;
     const unsigned int zero = 0;
-    if (hipMemcpy(err, &zero, sizeof zero, hipMemcpyHostToDevice) != hipSuccess)
-        return ATOM_ERR_HIP;
+    if (hipError_t e = hipMemcpy(err, &zero, sizeof zero, hipMemcpyHostToDevice); e != hipSuccess)
+        return atom::hip_status(e);
     return ATOM_ERR_TIMEOUT;
+}
+
+const char* atom_last_error(void)
+{
+    return atom::t_last_hip == hipSuccess ? "no HIP error" : hipGetErrorString(atom::t_last_hip);
 }
 
 int64_t atom_bdp_chunk_bytes(double bytes_per_s, double round_trip_s)

@@ -115,6 +115,28 @@ template <> struct SlotAcc<float> {      // 4 fp32 per slot
     }
 };
 
+// ---- XCD-aware tile order ----------------------------------------------
+// Workgroups are dispatched to the 8 XCDs round-robin (workgroup b runs on
+// XCD b mod 8). Renumbering so that XCD x's workgroups own one contiguous
+// eighth of the grid keeps each XCD's address translations and DRAM pages
+// local instead of every XCD touching every page. A bijection on [0, nb)
+// for any nb; if dispatch were not round-robin it is still a permutation.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int64_t xcd_slot(int64_t b, int64_t nb)
+{
+    const int64_t q = nb / kXcds, r = nb % kXcds;
+    const int64_t x = b % kXcds, i = b / kXcds;
+    return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
+
+// Tile of the workgroup in grid-stride round `round`.
+__device__ __forceinline__ int64_t tile_of(int64_t round_base, bool remap)
+{
+    const int64_t b = blockIdx.x, nb = gridDim.x;
+    return round_base + (remap ? xcd_slot(b, nb) : b);
+}
+
 // ---- element access for the element-wise (unaligned) paths ------------
 
 template <typename T> struct Elem;

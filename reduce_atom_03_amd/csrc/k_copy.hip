@@ -97,7 +97,11 @@ __global__ __launch_bounds__(256) void k_copy_vec(const CopyArgs a)
     const int lane = threadIdx.x;
     const int nthr = blockDim.x;
     const bool nt = a.nt_store != 0;
-    for (int64_t t = blockIdx.x; t < a.ntiles; t += gridDim.x) {
+    const bool remap = a.xcd_remap != 0;
+    for (int64_t base = 0; base < a.ntiles; base += gridDim.x) {
+        const int64_t t = tile_of(base, remap);
+        if (t >= a.ntiles)
+            continue;
         const int s = seg_of_tile(a, t);
         const Seg g = seg_geometry(a, s);
         const int64_t b0 = (t - a.seg_tile_begin[s]) * a.tile_bytes;   // tile start in segment
@@ -135,7 +139,11 @@ __global__ __launch_bounds__(256) void k_copy_elem(const CopyArgs a)
 {
     const int lane = threadIdx.x;
     const int nthr = blockDim.x;
-    for (int64_t t = blockIdx.x; t < a.ntiles; t += gridDim.x) {
+    const bool remap = a.xcd_remap != 0;
+    for (int64_t base = 0; base < a.ntiles; base += gridDim.x) {
+        const int64_t t = tile_of(base, remap);
+        if (t >= a.ntiles)
+            continue;
         const int s = seg_of_tile(a, t);
         const Seg g = seg_geometry(a, s);
         const int64_t o = (t - a.seg_tile_begin[s]) * a.tile_bytes + static_cast<int64_t>(lane) * kVecBytes;

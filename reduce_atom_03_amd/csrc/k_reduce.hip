@@ -62,7 +62,11 @@ __global__ __launch_bounds__(256) void k_reduce_vec(const ReduceArgs a)
     const int lane = threadIdx.x;
     const int nthr = blockDim.x;
     const bool nt = a.nt_store != 0;
-    for (int64_t t = blockIdx.x; t < a.ntiles; t += gridDim.x) {
+    const bool remap = a.xcd_remap != 0;
+    for (int64_t base = 0; base < a.ntiles; base += gridDim.x) {
+        const int64_t t = tile_of(base, remap);
+        if (t >= a.ntiles)
+            continue;
         const int k = part_of_tile(a, t);
         const int64_t pbeg = a.part_off[k];
         const int64_t plen = a.part_off[k + 1] - pbeg;
@@ -122,7 +126,11 @@ __global__ __launch_bounds__(256) void k_reduce_elem(const ReduceArgs a)
     constexpr int VE = kVecBytes / sizeof(T);
     const int lane = threadIdx.x;
     const int nthr = blockDim.x;
-    for (int64_t t = blockIdx.x; t < a.ntiles; t += gridDim.x) {
+    const bool remap = a.xcd_remap != 0;
+    for (int64_t base = 0; base < a.ntiles; base += gridDim.x) {
+        const int64_t t = tile_of(base, remap);
+        if (t >= a.ntiles)
+            continue;
         const int k = part_of_tile(a, t);
         const int64_t pbeg = a.part_off[k];
         const int64_t plen = a.part_off[k + 1] - pbeg;

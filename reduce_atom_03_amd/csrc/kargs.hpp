@@ -33,7 +33,7 @@ struct ReduceArgs {
     int32_t nparts;
     int32_t mode;
     int32_t nt_store;                  // 1: non-temporal output stores
-    int32_t pad_;
+    int32_t xcd_remap;                 // 1: XCD-contiguous tile order
 };
 
 // Copy family. Segments are derived in the kernel from row counts:
@@ -57,6 +57,8 @@ struct CopyArgs {
     int32_t ndst;                      // fan-out count (CK_FANOUT)
     int32_t esize;                     // element bytes for the element-wise path
     int32_t nt_store;
+    int32_t xcd_remap;                 // 1: XCD-contiguous tile order
+    int32_t pad_;
     int32_t cnt[kMaxSegs];             // rows per segment
     int32_t seg_tile_begin[kMaxSegs + 1];
 };

@@ -85,7 +85,7 @@ atom_status read_cfg(const atom_config* cfg, Cfg* c)
     if (cfg->num_wgs < 0)
         return ATOM_ERR_INVALID_ARG;
     c->num_wgs = std::min<int64_t>(cfg->num_wgs, kMaxGrid);
-    if (cfg->flags & ~(ATOM_F_STAGED | ATOM_F_NO_NT))
+    if (cfg->flags & ~(ATOM_F_STAGED | ATOM_F_NO_NT | ATOM_F_XCD_ORDER))
         return ATOM_ERR_INVALID_ARG;
     c->flags = cfg->flags;
     if (cfg->ring_slots != 0) {
@@ -213,6 +213,7 @@ void build_reduce(Plan* p, int nsrc, const void* const* srcs, int ndst, void* co
     a.nparts = nparts;
     a.mode = mode;
     a.nt_store = (c.flags & ATOM_F_NO_NT) ? 0 : 1;
+    a.xcd_remap = (c.flags & ATOM_F_XCD_ORDER) ? 1 : 0;
     p->grid = pick_grid(t, c.num_wgs);
     p->exec = t > 0 ? EX_REDUCE : EX_NONE;
 }
@@ -259,6 +260,7 @@ void build_copy(Plan* p, int32_t kind, int P, const void* const* srcs, int nsrc,
     a.ndst = ndst;
     a.esize = esize;
     a.nt_store = (c.flags & ATOM_F_NO_NT) ? 0 : 1;
+    a.xcd_remap = (c.flags & ATOM_F_XCD_ORDER) ? 1 : 0;
     p->grid = pick_grid(t, c.num_wgs);
     p->exec = t > 0 ? EX_COPY : EX_NONE;
 }

@@ -262,3 +262,15 @@ def test_snac_default_ring_holds_one_onchip_bdp():
         st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=8, n=(64 * MiB) // 2, cfg=cfg,
                      ins=fake(8, 64 * MiB), outs=fake(8, 512 * MiB, start=BASE + (1 << 40)))
         assert st == A.OK and info.ring_slots == slots, (chunk, info.ring_slots)
+
+
+def test_binding_maps_one_hip_runtime():
+    """Importing the binding (even before torch) leaves exactly one HIP
+    runtime in the process: libatom binds to the one torch brings."""
+    import subprocess
+    import sys
+    code = ("import reduce_atom_03_amd.atom as A, torch\n"
+            "print(len(A._hip_runtimes()))\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.strip().splitlines()[-1] == "1"

@@ -417,6 +417,32 @@ def test_v_collectives_zipf(A, dtype, P):
     check_guards(fulls, [T] * P, GUARD)
 
 
+@pytest.mark.parametrize("wgs", [1, 3, 8, 13, 0])
+def test_xcd_tile_order(A, wgs):
+    """The XCD-contiguous tile order (with and without a grid stride) covers
+    every tile exactly once: same bits as the oracle for reduce, fan-out and
+    exchange."""
+    P, n = 8, 40013 * 8
+    cfg = A.config(flags=A.F_XCD_ORDER, num_wgs=wgs)
+    say(f"XCD order wgs={wgs}")
+    xs = [synth.mixed_bits(75, r, P * n, synth.BF16, specials=False) for r in range(P)]
+    dx = [to_dev(x)[1] for x in xs]
+    ys = [empty_dev(n, _torch_dtype(synth.BF16)) for _ in range(P)]
+    A.reduce_scatter(dx, ys, cfg)
+    outs = [empty_dev(P * n, _torch_dtype(synth.BF16)) for _ in range(P)]
+    A.all_to_all(dx, outs, cfg)
+    _sync()
+    for k, w in enumerate(oracle.reduce_scatter(xs)):
+        _assert_reduced(from_dev(ys[k]), w, f"XCD order RS y_{k}")
+    for j, w in enumerate(oracle.all_to_all(xs)):
+        assert_bits_equal(from_dev(outs[j]), w, f"XCD order A2A out_{j}", nan_by_class=False)
+    A.all_gather(ys, outs, cfg)
+    _sync()
+    want = np.concatenate([from_dev(y) for y in ys])
+    for j in range(P):
+        assert_bits_equal(from_dev(outs[j]), want, f"XCD order AG out_{j}", nan_by_class=False)
+
+
 # ------------------------------------------------------------- side stream
 
 def test_side_stream(A):
