@@ -104,20 +104,29 @@ __global__ __launch_bounds__(256) void k_copy_vec(const CopyArgs a)
             continue;
         const int s = seg_of_tile(a, t);
         const Seg g = seg_geometry(a, s);
-        const int64_t b0 = (t - a.seg_tile_begin[s]) * a.tile_bytes;   // tile start in segment
+        // Tile start in the segment; the first tile may start before the
+        // segment (negative offsets are skipped) so that tiles are aligned
+        // at the destination.
+        int64_t b0 = (t - a.seg_tile_begin[s]) * a.tile_bytes;
+        if (a.align) {
+            const char* d = static_cast<const char*>(a.dst[g.dst >= 0 ? g.dst : 0]) + g.dst_off;
+            b0 -= seg_tile_shift(reinterpret_cast<uintptr_t>(d), a.tile_bytes);
+        }
         const char* sb = g.src + b0;
         u32x4 x[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t o = b0 + static_cast<int64_t>(u * nthr + lane) * kVecBytes;
-            if (o + kVecBytes <= g.bytes)
+            if (o >= 0 && o + kVecBytes <= g.bytes)
                 x[u] = ld16_stream(sb + static_cast<uint32_t>(u * nthr + lane) * kVecBytes);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t off = static_cast<uint32_t>(u * nthr + lane) * kVecBytes;
             const int64_t o = b0 + off;
-            if (o + kVecBytes <= g.bytes) {
+            if (o < 0) {
+                // before the segment: owned by no lane
+            } else if (o + kVecBytes <= g.bytes) {
                 if (g.dst >= 0) {
                     char* db = static_cast<char*>(a.dst[g.dst]) + g.dst_off + b0;
                     st16(db + off, x[u], nt);

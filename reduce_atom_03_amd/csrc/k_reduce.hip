@@ -71,7 +71,9 @@ __global__ __launch_bounds__(256) void k_reduce_vec(const ReduceArgs a)
         const int64_t pbeg = a.part_off[k];
         const int64_t plen = a.part_off[k + 1] - pbeg;
         const int64_t nfull = plen / VE;                       // whole slots in the part
-        const int64_t slot0 = (t - a.tile_begin[k]) * nthr * U; // first slot of the tile
+        // First slot of the tile; the part's first tile may start before the
+        // part (negative slots are skipped) so that tiles are aligned.
+        const int64_t slot0 = (t - a.tile_begin[k]) * nthr * U - a.shift[k];
         // Uniform bases of this tile; lanes add 32-bit offsets.
         const int64_t ebase = pbeg + slot0 * VE;                // absolute element index
         const char* sb[P];
@@ -84,7 +86,7 @@ __global__ __launch_bounds__(256) void k_reduce_vec(const ReduceArgs a)
         for (int u = 0; u < U; ++u) {
             const int64_t s = slot0 + u * nthr + lane;
             const uint32_t off = static_cast<uint32_t>(u * nthr + lane) * kVecBytes;
-            if (s < nfull) {
+            if (s >= 0 && s < nfull) {
 #pragma unroll
                 for (int r = 0; r < P; ++r)
                     x[u][r] = ld16_stream(sb[r] + off);
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(256) void k_reduce_vec(const ReduceArgs a)
         for (int u = 0; u < U; ++u) {
             const int64_t s = slot0 + u * nthr + lane;
             const uint32_t off = static_cast<uint32_t>(u * nthr + lane) * kVecBytes;
-            if (s < nfull) {
+            if (s >= 0 && s < nfull) {
                 SlotAcc<T> acc;
                 acc.init(x[u][0]);
 #pragma unroll

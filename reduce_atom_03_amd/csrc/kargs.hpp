@@ -6,6 +6,13 @@
 
 #include <stdint.h>
 
+// Helpers below are used by the host planner and by the kernels.
+#if defined(__HIPCC__) || defined(__HIP__)
+#define ATOM_HD __host__ __device__
+#else
+#define ATOM_HD
+#endif
+
 namespace atom {
 
 constexpr int kMaxRanks = 16;
@@ -28,6 +35,9 @@ struct ReduceArgs {
     int64_t part_off[kMaxRanks + 1];   // elements
     int64_t tile_begin[kMaxRanks + 1]; // first tile of each part; [nparts] = ntiles
     int64_t ntiles;
+    int32_t shift[kMaxRanks];          // per part: slots before its first slot in
+                                       // its first tile (tiles start at addresses
+                                       // aligned to the tile size in source 0)
     int32_t nsrc;
     int32_t ndst;
     int32_t nparts;
@@ -58,7 +68,9 @@ struct CopyArgs {
     int32_t esize;                     // element bytes for the element-wise path
     int32_t nt_store;
     int32_t xcd_remap;                 // 1: XCD-contiguous tile order
-    int32_t pad_;
+    int32_t align;                     // 1: tiles start at addresses aligned to
+                                       // tile_bytes in the destination (see
+                                       // seg_tile_shift)
     int32_t cnt[kMaxSegs];             // rows per segment
     int32_t seg_tile_begin[kMaxSegs + 1];
 };
@@ -88,5 +100,13 @@ struct SnacArgs {
     int32_t nt_store;
     int32_t pad_;
 };
+
+// Bytes before a segment's first byte in its first tile when tiles are
+// aligned to `tile_bytes` at the destination address `dst_addr` (the same
+// arithmetic on the host, to count tiles, and on the device, to place them).
+ATOM_HD inline int64_t seg_tile_shift(uint64_t dst_addr, int64_t tile_bytes)
+{
+    return static_cast<int64_t>(dst_addr % static_cast<uint64_t>(tile_bytes));
+}
 
 }  // namespace atom
