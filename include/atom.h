@@ -62,14 +62,22 @@ typedef enum atom_status {
     ATOM_ERR_NOMEM = 5         /* the workspace could not be allocated          */
 } atom_status;
 
+/* The input enums below carry range sentinels so that any 32-bit value a
+ * caller passes is a valid value of the type (and is rejected by
+ * validation) rather than undefined behaviour in the C++ implementation. */
+
 typedef enum atom_dtype {
     ATOM_DT_BF16 = 0,          /* 2-byte bfloat16 */
-    ATOM_DT_F32 = 1            /* 4-byte IEEE binary32 */
+    ATOM_DT_F32 = 1,           /* 4-byte IEEE binary32 */
+    ATOM_DT_ENUM_MIN = INT32_MIN,
+    ATOM_DT_ENUM_MAX = INT32_MAX
 } atom_dtype;
 
 typedef enum atom_op {
     ATOM_OP_COPY = 0,          /* move bits unchanged */
-    ATOM_OP_SUM = 1            /* binary32 sum in rank order, rounded once */
+    ATOM_OP_SUM = 1,           /* binary32 sum in rank order, rounded once */
+    ATOM_OP_ENUM_MIN = INT32_MIN,
+    ATOM_OP_ENUM_MAX = INT32_MAX
 } atom_op;
 
 /* How P buffers name a layout (Figure 4). n = part_elems (uniform case).
@@ -85,7 +93,9 @@ typedef enum atom_layout_kind {
     ATOM_LAYOUT_PARTITIONED = 0,
     ATOM_LAYOUT_SHARD = 1,
     ATOM_LAYOUT_GATHERED = 2,
-    ATOM_LAYOUT_TRANSPOSED = 3
+    ATOM_LAYOUT_TRANSPOSED = 3,
+    ATOM_LAYOUT_ENUM_MIN = INT32_MIN,
+    ATOM_LAYOUT_ENUM_MAX = INT32_MAX
 } atom_layout_kind;
 
 typedef struct atom_layout {

@@ -28,8 +28,8 @@ int esize_of(atom_dtype d)
     switch (d) {
     case ATOM_DT_BF16: return 2;
     case ATOM_DT_F32: return 4;
+    default: return 0;
     }
-    return 0;
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

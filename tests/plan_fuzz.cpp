@@ -1,0 +1,156 @@
+// plan_fuzz.cpp -- randomized checks of the host planner, built with
+// AddressSanitizer and UndefinedBehaviorSanitizer by test_plan_sanitizers.py
+// (host code only; no HIP call is made). Every plan that validates must tile
+// its work exactly: tile counts follow the part/segment sizes, tile ranges
+// are monotone, and launch shapes are within the kernels' limits.
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <random>
+
+#include "../reduce_atom_03_amd/csrc/plan.hpp"
+
+using namespace atom;
+
+namespace {
+
+int fails = 0;
+
+void check(bool ok, const char* what, int iter)
+{
+    if (!ok) {
+        std::fprintf(stderr, "iteration %d: %s\n", iter, what);
+        ++fails;
+    }
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+void check_reduce(const Plan& p, int iter)
+{
+    const ReduceArgs& a = p.ra;
+    const int64_t ve = kVecBytes / p.esize;
+    const int64_t ts = static_cast<int64_t>(p.wg) * p.U;
+    check(a.nparts >= 1 && a.nparts <= kMaxRanks, "reduce nparts", iter);
+    check(p.wg == 64 || p.wg == 256, "reduce wg", iter);
+    check(p.vec ? (p.U == 1 || p.U == 2 || p.U == 4) : p.U == 1, "reduce U", iter);
+    check(p.U * a.nsrc <= 32 || p.U == 1, "reduce registers", iter);
+    int64_t t = 0;
+    for (int k = 0; k < a.nparts; ++k) {
+        check(a.tile_begin[k] == t, "reduce tile_begin", iter);
+        const int64_t len = a.part_off[k + 1] - a.part_off[k];
+        check(len >= 0, "reduce part length", iter);
+        const int64_t shift = p.vec ? a.shift[k] : 0;
+        check(shift >= 0 && shift < ts, "reduce shift", iter);
+        t += cdiv(cdiv(len, ve) + shift, ts);
+    }
+    check(a.tile_begin[a.nparts] == t && a.ntiles == t, "reduce ntiles", iter);
+    check(p.grid >= 1 && p.grid <= std::max<int64_t>(1, t), "reduce grid", iter);
+}
+
+void check_copy(const Plan& p, int iter)
+{
+    const CopyArgs& a = p.ca;
+    check(a.tile_bytes == static_cast<int64_t>(p.wg) * p.U * kVecBytes, "copy tile bytes", iter);
+    check(a.nseg >= 1 && a.nseg <= kMaxSegs, "copy nseg", iter);
+    int64_t t = 0;
+    for (int s = 0; s < a.nseg; ++s) {
+        check(a.seg_tile_begin[s] == t, "copy seg_tile_begin", iter);
+        check(a.cnt[s] >= 0, "copy count", iter);
+        const int64_t bytes = static_cast<int64_t>(a.cnt[s]) * a.row_bytes;
+        // an aligned segment may need one extra (short) tile at its start
+        const int64_t lo = cdiv(bytes, a.tile_bytes), hi = bytes ? lo + 1 : 0;
+        const int64_t n = (s + 1 <= a.nseg ? a.seg_tile_begin[s + 1] : 0) - a.seg_tile_begin[s];
+        check(n >= lo && n <= hi, "copy tiles per segment", iter);
+        t = a.seg_tile_begin[s + 1];
+    }
+    check(a.ntiles == t, "copy ntiles", iter);
+    check(p.grid >= 1 && p.grid <= std::max<int64_t>(1, t), "copy grid", iter);
+}
+
+}  // namespace
+
+int main(int argc, char** argv)
+{
+    const int iters = argc > 1 ? std::atoi(argv[1]) : 20000;
+    std::mt19937_64 rng(12345);
+    auto pick = [&](int64_t lo, int64_t hi) {
+        return std::uniform_int_distribution<int64_t>(lo, hi)(rng);
+    };
+    int ok_plans = 0;
+    for (int iter = 0; iter < iters; ++iter) {
+        const bool valid_pair = pick(0, 9) < 7;             // mostly collectives that exist
+        const int P = static_cast<int>(valid_pair ? pick(1, 16) : pick(0, 18));
+        static const int pairs[4][3] = {{0, 1, 1}, {1, 2, 0}, {0, 3, 0}, {0, 2, 1}};
+        const int* pr = pairs[pick(0, 3)];
+        const atom_layout_kind kin = static_cast<atom_layout_kind>(valid_pair ? pr[0] : pick(-1, 4));
+        const atom_layout_kind kout = static_cast<atom_layout_kind>(valid_pair ? pr[1] : pick(0, 4));
+        const atom_op op = static_cast<atom_op>(valid_pair ? pr[2] : pick(-1, 2));
+        const atom_dtype dt = static_cast<atom_dtype>(valid_pair ? pick(0, 1) : pick(-1, 2));
+        void* ins[32];
+        void* outs[32];
+        const uint64_t base_in = 0x100000000000ull, base_out = 0x200000000000ull;
+        const uint64_t stride = 1ull << 36;                 // buffers never overlap
+        const int misalign = pick(0, 7) == 0 ? static_cast<int>(pick(1, 15)) : 0;
+        for (int r = 0; r < 32; ++r) {
+            ins[r] = reinterpret_cast<void*>(base_in + r * stride + (r == 1 ? misalign : 0));
+            outs[r] = reinterpret_cast<void*>(base_out + r * stride);
+        }
+        int64_t counts[kMaxSegs + 8];
+        const bool v = pick(0, 2) == 0;
+        for (auto& c : counts)
+            c = pick(0, 49) == 0 ? pick(-3, 0) : pick(0, 5000);
+        const int64_t n = pick(0, 4) == 0 ? pick(-2, 40) : pick(0, 1 << 22);
+        atom_layout li{kin, P, ins, n, v ? counts : nullptr, pick(0, 9) == 0 ? 0 : pick(1, 7168), dt};
+        atom_layout lo{kout, P, outs, n, nullptr, li.row_elems, dt};
+        atom_config cfg{};
+        const bool use_cfg = pick(0, 1) == 1;
+        if (use_cfg) {
+            cfg.chunk_bytes = pick(0, 3) == 0 ? pick(-1, 1 << 25) : (int64_t(1) << pick(16, 24));
+            cfg.stages = static_cast<int32_t>(pick(0, 4) == 0 ? pick(-1, 9) : (1 << pick(0, 3)));
+            cfg.num_wgs = static_cast<int32_t>(pick(0, 2) == 0 ? pick(-2, 3000) : 0);
+            cfg.flags = static_cast<uint32_t>(pick(0, 8));
+            cfg.ring_slots = static_cast<int32_t>(pick(0, 3) == 0 ? pick(-1, 70) : 0);
+            cfg.piece_bytes = static_cast<int32_t>(pick(0, 3) == 0 ? (1 << pick(13, 22)) : 0);
+            cfg.wait_us = static_cast<int32_t>(pick(0, 5) == 0 ? pick(-1, 10) : 0);
+        }
+        Plan p;
+        const atom_status st = plan_collective(&li, &lo, op, use_cfg ? &cfg : nullptr, &p);
+        check(st == ATOM_OK || st == ATOM_ERR_INVALID_ARG || st == ATOM_ERR_UNSUPPORTED,
+              "status", iter);
+        if (st != ATOM_OK)
+            continue;
+        ++ok_plans;
+        check(p.P == P && P >= 1 && P <= kMaxRanks, "ranks", iter);
+        check(p.credited_bytes >= 0, "credited bytes", iter);
+        if (p.exec == EX_REDUCE)
+            check_reduce(p, iter);
+        else if (p.exec == EX_COPY)
+            check_copy(p, iter);
+        else if (p.exec == EX_SNAC_AG || p.exec == EX_SNAC_AR) {
+            check(p.sa.slots >= 1 && p.sa.slots <= kMaxSlots, "snac slots", iter);
+            check(p.sa.pieces >= 1 && p.sa.piece_bytes * p.sa.pieces == p.sa.chunk_bytes,
+                  "snac pieces", iter);
+            check(p.sa.ntasks == 2 * p.sa.nchunks * p.sa.pieces, "snac tasks", iter);
+            check(p.ring_bytes == p.sa.chunk_bytes * p.sa.slots, "snac ring", iter);
+        }
+    }
+    // a few copies and flat reduces
+    for (int iter = 0; iter < iters / 10; ++iter) {
+        Plan p;
+        const size_t bytes = static_cast<size_t>(pick(0, 1 << 26));
+        void* d = reinterpret_cast<void*>(0x300000000000ull + pick(0, 15));
+        const void* s = reinterpret_cast<const void*>(0x400000000000ull + pick(0, 15));
+        if (plan_copy(d, s, bytes, nullptr, &p) == ATOM_OK && p.exec == EX_COPY)
+            check_copy(p, iter);
+        const void* srcs[kMaxRanks];
+        for (int r = 0; r < kMaxRanks; ++r)
+            srcs[r] = reinterpret_cast<const void*>(0x500000000000ull + r * (1ull << 34));
+        const int nsrc = static_cast<int>(pick(1, 16));
+        if (plan_reduce(d, srcs, nsrc, pick(0, 1 << 22), ATOM_DT_F32, ATOM_OP_SUM, nullptr, &p) ==
+                ATOM_OK && p.exec == EX_REDUCE)
+            check_reduce(p, iter);
+    }
+    std::printf("%d plans validated, %d failures\n", ok_plans, fails);
+    return fails ? 1 : 0;
+}
