@@ -337,8 +337,12 @@ def measured_traffic(row):
             d = json.load(f)
     except (OSError, ValueError):
         return None
-    for fn, h in d.get("sources", {}).items():
-        src = os.path.join(ROOT, "reduce_atom_03_amd", "csrc", fn)
+    csrc = os.path.join(ROOT, "reduce_atom_03_amd", "csrc")
+    hashes = d.get("sources", {})
+    if set(hashes) != set(os.listdir(csrc)):     # every source file must be covered
+        return None
+    for fn, h in hashes.items():
+        src = os.path.join(csrc, fn)
         try:
             with open(src, "rb") as f:
                 if hashlib.sha256(f.read()).hexdigest()[:16] != h:

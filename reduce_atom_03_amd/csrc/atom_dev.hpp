@@ -1,7 +1,7 @@
 // atom_dev.hpp -- device helpers for the gfx950 Atom kernels: 128-bit
 // global loads/stores (optionally non-temporal), bf16 widening and
-// round-to-nearest-even narrowing, and the agent-scope flag operations used
-// by SNAC.
+// round-to-nearest-even narrowing, and the agent-coherent ring accesses and
+// flag operations used by SNAC.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -157,27 +157,50 @@ template <> struct Elem<float> {
     __device__ static void store(void* base, int64_t i, float v) { static_cast<float*>(base)[i] = v; }
 };
 
-// ---- SNAC flags ----------------------------------------------------------
+// ---- SNAC hand-off ------------------------------------------------------
 // Staged data written by one workgroup is consumed by workgroups that may
-// run on another XCD (another L2). Agent-scope release/acquire makes the
-// compiler emit the L2 write-back / invalidate needed across XCDs.
+// run on another XCD, each XCD with its own L2. Rather than fence with the
+// agent-scope release/acquire (which writes back, then invalidates, a whole
+// L2 per task), the staging ring is accessed only with agent-coherent
+// 16-byte operations: buffer loads and stores carrying the sc1 cache-policy
+// bit. An sc1 store writes through the XCD's L2 and an sc1 load does not
+// return a line that an L2 kept from before; these are the cache policies
+// the compiler itself gives relaxed agent-scope atomic loads and stores, on
+// which the cross-XCD flag polling below already relies. The buffer
+// resource covers [base, base + bytes), and the hardware drops accesses
+// outside it.
 
-__device__ __forceinline__ unsigned long long flag_load_acquire(const unsigned long long* f)
+constexpr int kBufRsrcWord3 = 0x00020000;   // gfx9 raw buffer: 32-bit data format
+constexpr int kCpolSc1 = 16;                // cache-policy operand: sc1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ring_rsrc(const void* base, int64_t bytes)
 {
-    return __hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                             kBufRsrcWord3);
 }
+
+__device__ __forceinline__ u32x4 ld16_agent(__amdgpu_buffer_rsrc_t r, int64_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, kCpolSc1);
+}
+
+__device__ __forceinline__ void st16_agent(__amdgpu_buffer_rsrc_t r, int64_t off, u32x4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(off), 0, kCpolSc1);
+}
+
+// Waits until every vector memory operation of this wave has completed
+// (for sc1 stores: written through to the agent-coherent level).
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ unsigned long long flag_load_relaxed(const unsigned long long* f)
 {
     return __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void flag_add_release(unsigned long long* f, unsigned long long v)
+__device__ __forceinline__ void flag_add_relaxed(unsigned long long* f, unsigned long long v)
 {
-    __hip_atomic_fetch_add(f, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
-__device__ __forceinline__ void fence_acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
-__device__ __forceinline__ void fence_release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
 
 }  // namespace atom

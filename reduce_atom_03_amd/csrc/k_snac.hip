@@ -11,13 +11,16 @@
 // producer and its consumers crosses workgroups (and XCDs, each with its own
 // L2) through device memory:
 //   Stage   a producer workgroup copies one piece of a chunk of partition k
-//           into a slot of the staging ring;
-//   Notify  after its stores are released at agent scope it adds 1 to the
+//           into a slot of the staging ring with agent-coherent stores;
+//   Notify  once every wave's stores have completed it adds 1 to the
 //           slot's `ready` counter;
-//   Consume a consumer workgroup acquires `ready` == all pieces of the chunk,
-//           copies one piece from the slot to every output (AllGather
-//           fan-out) and adds 1 to the slot's `freed` counter, which the
-//           producer of the chunk D places later waits for before reuse.
+//   Consume a consumer workgroup waits for `ready` == all pieces of the
+//           chunk, reads one piece from the slot with agent-coherent loads,
+//           writes it to every output (AllGather fan-out) and adds 1 to the
+//           slot's `freed` counter, which the producer of the chunk D
+//           places later waits for before reuse.
+// The ring is never touched by ordinary (L2-cached) accesses, so no task
+// needs an L2 write-back or invalidation.
 //
 // Tasks are claimed from one atomic ticket in an order where every task
 // depends only on tasks with smaller tickets: producers of chunks 0..D-1,
@@ -70,15 +73,14 @@ __device__ __forceinline__ Task decode_task(const SnacArgs& a, int64_t t)
 
 // Lane 0 waits until *flag >= target, bounded in wall-clock time (the
 // per-wait bound and the workgroup's whole-kernel budget, both in ticks of
-// the constant-rate device clock), then, when the wait guards data that the
-// workgroup will read, acquires at agent scope for the workgroup: the
-// invalidation covers the CU's vector L1, which every wave of the workgroup
-// shares, and the L2 lines the producer's XCD may have written. The result is made wave-uniform with readfirstlane so every
-// branch on it is uniform. Returns false when the wait gave up (a timeout
-// here or elsewhere).
+// the constant-rate device clock). The barrier then holds every wave until
+// the count was seen, so the waves' ring loads are issued after it. The
+// result is made wave-uniform with readfirstlane so every branch on it is
+// uniform. Returns false when the wait gave up (a timeout here or
+// elsewhere).
 __device__ __forceinline__ bool wait_at_least(const SnacArgs& a, const unsigned long long* flag,
                                               unsigned long long target, long long t_begin,
-                                              bool acquire, int* s_ok)
+                                              int* s_ok)
 {
     if (threadIdx.x == 0) {
         int ok = 1;
@@ -103,8 +105,6 @@ __device__ __forceinline__ bool wait_at_least(const SnacArgs& a, const unsigned 
                 }
             }
         }
-        if (ok && acquire)
-            fence_acquire_agent();
         *s_ok = ok;
     }
     __syncthreads();
@@ -118,6 +118,7 @@ struct StageCopy {
     __device__ static void produce(const SnacArgs& a, int k, int64_t off, char* dst, int64_t bytes)
     {
         const char* src = static_cast<const char*>(a.src[k]) + off;
+        const auto ring = ring_rsrc(dst, bytes);
         const int lane = threadIdx.x;
         const int nthr = blockDim.x;
         const int64_t step = static_cast<int64_t>(nthr) * U * kVecBytes;
@@ -133,7 +134,7 @@ struct StageCopy {
             for (int u = 0; u < U; ++u) {
                 const int64_t o = b0 + static_cast<int64_t>(u * nthr + lane) * kVecBytes;
                 if (o < bytes)
-                    st16(dst + o, x[u], false);
+                    st16_agent(ring, o, x[u]);
             }
         }
     }
@@ -147,6 +148,7 @@ struct StageReduce {
     __device__ static void produce(const SnacArgs& a, int k, int64_t off, char* dst, int64_t bytes)
     {
         const int64_t base = static_cast<int64_t>(k) * a.part_bytes + off;
+        const auto ring = ring_rsrc(dst, bytes);
         const int lane = threadIdx.x;
         const int nthr = blockDim.x;
         const int64_t step = static_cast<int64_t>(nthr) * U * kVecBytes;
@@ -170,7 +172,7 @@ struct StageReduce {
 #pragma unroll
                     for (int r = 1; r < P; ++r)
                         acc.add(x[u][r]);
-                    st16(dst + o, acc.pack(), false);
+                    st16_agent(ring, o, acc.pack());
                 }
             }
         }
@@ -184,6 +186,7 @@ __device__ __forceinline__ void fan_out(const SnacArgs& a, const char* src, int6
     const int lane = threadIdx.x;
     const int nthr = blockDim.x;
     const bool nt = a.nt_store != 0;
+    const auto ring = ring_rsrc(src, bytes);
     const int64_t step = static_cast<int64_t>(nthr) * U * kVecBytes;
     for (int64_t b0 = 0; b0 < bytes; b0 += step) {
         u32x4 x[U];
@@ -191,7 +194,7 @@ __device__ __forceinline__ void fan_out(const SnacArgs& a, const char* src, int6
         for (int u = 0; u < U; ++u) {
             const int64_t o = b0 + static_cast<int64_t>(u * nthr + lane) * kVecBytes;
             if (o < bytes)
-                x[u] = ld16(src + o);
+                x[u] = ld16_agent(ring, o);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -232,13 +235,12 @@ __global__ __launch_bounds__(256) void k_snac(const SnacArgs a)
         int64_t plen = clen - pbeg;
         plen = plen < 0 ? 0 : (plen > a.piece_bytes ? a.piece_bytes : plen);
         char* slotp = a.ring + slot * C;
-        // Stage waits for the slot's previous chunk to be consumed (no data
-        // to acquire: it only overwrites); Consume waits for every piece of
-        // its chunk to be staged and acquires the staged bytes.
+        // Stage waits for the slot's previous chunk to be consumed; Consume
+        // waits for every piece of its chunk to be staged.
         const unsigned long long* wflag = (task.produce ? a.freed : a.ready) + slot * kFlagStride;
         const unsigned long long target =
             static_cast<unsigned long long>(task.produce ? use : use + 1) * a.pieces;
-        const bool ok = wait_at_least(a, wflag, target, t_begin, !task.produce, &s_ok);
+        const bool ok = wait_at_least(a, wflag, target, t_begin, &s_ok);
         if (ok) {
             if (task.produce) {
                 Stage::template produce<U>(a, k, cbeg + pbeg, slotp + pbeg, plen);
@@ -246,20 +248,19 @@ __global__ __launch_bounds__(256) void k_snac(const SnacArgs a)
                 fan_out<U>(a, slotp + pbeg, static_cast<int64_t>(k) * S + cbeg + pbeg, plen);
             }
         }
-        // The barrier waits for every wave's stores to reach the L2 and for
-        // its slot reads to return. Notify: lane 0's agent-scope release then
-        // writes the XCD's L2 back before `ready` moves, so a consumer on any
-        // XCD that sees the count also sees the staged bytes. Releasing the
-        // slot publishes no data: the slot reads have already returned (their
-        // values were stored before the barrier), so `freed` moves with a
-        // relaxed increment and no write-back.
+        // Notify: each wave of a producer waits until its write-through
+        // stores have completed, so once the barrier is passed the whole
+        // piece is agent-visible and `ready` moves with a relaxed increment;
+        // a consumer on any XCD that sees the count reads the staged bytes.
+        // Releasing the slot publishes no data: the slot loads have already
+        // returned (their values were stored before the barrier), so `freed`
+        // moves the same way.
+        if (task.produce)
+            wait_vmem();
         __syncthreads();
         if (threadIdx.x == 0) {
-            if (ok && task.produce)
-                flag_add_release(a.ready + slot * kFlagStride, 1ull);
-            else if (ok)
-                __hip_atomic_fetch_add(a.freed + slot * kFlagStride, 1ull, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
+            if (ok)
+                flag_add_relaxed((task.produce ? a.ready : a.freed) + slot * kFlagStride, 1ull);
             s_ticket = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();

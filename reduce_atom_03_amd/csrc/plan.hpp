@@ -46,7 +46,7 @@ constexpr int32_t kDefaultSlots = 4;
 constexpr int32_t kMaxSlots = 64;
 constexpr int64_t kPieceBytes = 64 << 10;            // SNAC task granule
 constexpr int64_t kSnacInflightBytes = 32 << 20;     // default ring: one on-chip BDP
-constexpr int64_t kSnacGrid = 768;                   // persistent SNAC workgroups
+constexpr int64_t kSnacGrid = 512;                   // persistent SNAC workgroups (2 per CU)
 constexpr int64_t kMaxGrid = 1 << 20;
 constexpr int64_t kSmallSlots = 256 * 256;           // below: the latency path
 constexpr int64_t kDefaultWaitUs = 1000000;          // one SNAC wait: 1 s

@@ -58,3 +58,30 @@ def test_no_divergent_loop_exit(asm):
 def test_no_scratch(asm):
     for m in re.finditer(r"\.name:\s+(\S*k_snac\S*)\n(?:.*\n)*?\s+\.private_segment_fixed_size:\s+(\d+)", asm):
         assert int(m.group(2)) == 0, m.group(1)
+
+
+def test_ring_hand_off_needs_no_l2_maintenance(asm):
+    """The ring is read and written only with agent-coherent (sc1) buffer
+    operations, so no SNAC kernel writes back or invalidates an L2; outputs
+    and inputs use ordinary global operations."""
+    for name, body in _kernels(asm):
+        if "k_snac_reset" in name:
+            continue
+        assert not re.search(r"buffer_wbl2|buffer_inv", body), name
+        ring_ops = re.findall(r"^\s*(buffer_(?:load|store)_dwordx4[^\n]*)", body, re.M)
+        assert ring_ops, f"{name}: no ring accesses"
+        for op in ring_ops:
+            assert re.search(r"\bsc1\b", op), f"{name}: ring access without sc1: {op}"
+
+
+def test_producer_waits_for_its_stores_before_notify(asm):
+    """Each wave waits for vmcnt(0) after its last ring store and before the
+    barrier that precedes the `ready` increment."""
+    for name, body in _kernels(asm):
+        if "k_snac_reset" in name:
+            continue
+        last_store = max(m.end() for m in re.finditer(r"buffer_store_dwordx4", body))
+        rest = body[last_store:]
+        wait = re.search(r"s_waitcnt vmcnt\(0\)", rest)
+        barrier = re.search(r"s_barrier", rest)
+        assert wait and barrier and wait.start() < barrier.start(), name
