@@ -14,6 +14,9 @@ Datapath of Collectives"):
 * AllToAll (Figure 4, bottom): rank j receives partition j of every source.
 * AllToAllV (Table 2, the variable-length variant): per-pair row counts.
 * AllReduce (Figure 6): AllGather composed with ReduceScatter.
+* MoE dispatch and combine (Table 2, expert parallelism): an AllToAllV
+  whose destinations are experts chosen per token by routing ids, and its
+  way back as a weighted sum over each token's k choices.
 
 The sum is binary32 accumulation in rank order, rounded once to the element
 type with round-to-nearest-even. Arrays are numpy: bf16 as raw ``uint16``,
@@ -54,6 +57,9 @@ def _load():
             "orc_all_reduce": [i32, i64, i32, vpp, vpp],
             "orc_reduce_scatter_v": [i32, i64p, i32, vpp, vpp],
             "orc_all_gather_v": [i32, i64p, i64, vpp, vpp],
+            "orc_moe_route": [i32, i32, i32, i64, vpp, vpp, ctypes.c_void_p, ctypes.c_void_p],
+            "orc_moe_dispatch": [i32, i32, i32, i64, vpp, vpp, i64, i64, vpp, vpp],
+            "orc_moe_combine": [i32, i32, i32, i64, vpp, vpp, vpp, i64, i64, i32, vpp, vpp],
         }
         for name, args in sig.items():
             f = getattr(lib, name)
@@ -188,4 +194,63 @@ def all_gather_v(zs):
     _check(_load().orc_all_gather_v(
         P, c.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), zs[0].itemsize,
         _ptrs(zs), _ptrs(outs)), "all_gather_v")
+    return outs
+
+
+# ---------------------------------------------------------------- MoE (Table 2)
+
+def _i32(arrays, n):
+    out = [np.ascontiguousarray(a, dtype=np.int32).reshape(-1) for a in arrays]
+    assert all(a.size == n for a in out)
+    return out
+
+
+def moe_route(ids, E: int, k: int):
+    """ids: P arrays of T*k expert ids (token-major). Returns (pos, counts,
+    recv): pos P arrays of T*k int32 rows (-1: invalid id), counts (P, E)
+    int32, recv (P,) int64 rows each rank receives."""
+    P = len(ids)
+    n = np.asarray(ids[0]).size
+    assert n % k == 0
+    T = n // k
+    ids = _i32(ids, n)
+    pos = [np.empty(n, dtype=np.int32) for _ in range(P)]
+    counts = np.zeros((P, E), dtype=np.int32)
+    recv = np.zeros(P, dtype=np.int64)
+    _check(_load().orc_moe_route(P, E, k, T, _ptrs(ids), _ptrs(pos), counts.ctypes.data,
+                                 recv.ctypes.data), "moe_route")
+    return pos, counts, recv
+
+
+def moe_dispatch(xs, ids, pos, E: int, k: int, row_elems: int, cap: int, fill=None):
+    """xs: P arrays of T*row_elems; returns P arrays of cap*row_elems
+    (rows no entry lands on hold ``fill``, default zeros)."""
+    P = len(xs)
+    xs = _contig(xs)
+    n = pos[0].size
+    T = n // k
+    ids = _i32(ids, n)
+    pos = _i32(pos, n)
+    outs = [np.zeros(cap * row_elems, dtype=xs[0].dtype) if fill is None else
+            np.full(cap * row_elems, fill, dtype=xs[0].dtype) for _ in range(P)]
+    _check(_load().orc_moe_dispatch(P, E, k, T, _ptrs(ids), _ptrs(pos), cap,
+                                    row_elems * xs[0].itemsize, _ptrs(xs), _ptrs(outs)),
+           "moe_dispatch")
+    return outs
+
+
+def moe_combine(ys, ids, pos, w, E: int, k: int, H: int, cap: int):
+    """ys: P arrays of cap*H (expert outputs in dispatch layout); w: P arrays
+    of T*k float32 weights. Returns P arrays of T*H."""
+    P = len(ys)
+    ys = _contig(ys)
+    dt = _dtype_code(ys[0])
+    n = pos[0].size
+    T = n // k
+    ids = _i32(ids, n)
+    pos = _i32(pos, n)
+    w = [np.ascontiguousarray(a, dtype=np.float32).reshape(-1) for a in w]
+    outs = [np.empty(T * H, dtype=_NP[dt]) for _ in range(P)]
+    _check(_load().orc_moe_combine(P, E, k, T, _ptrs(ids), _ptrs(pos), _ptrs(w), cap, H, dt,
+                                   _ptrs(ys), _ptrs(outs)), "moe_combine")
     return outs

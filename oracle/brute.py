@@ -194,5 +194,73 @@ def all_gather_v(zs: list[list[int]]) -> list[list[int]]:
     return [list(flat) for _ in range(P)]
 
 
+def fma_f32(a: Val, b: Val, c: Val) -> Val:
+    """One IEEE binary32 fused multiply-add a*b + c (round to nearest even):
+    the exact rational result, rounded once."""
+    if "nan" in (a.kind, b.kind, c.kind):
+        return Val("nan")
+    if a.kind == "inf" or b.kind == "inf":
+        other = b if a.kind == "inf" else a
+        if other.kind == "fin" and other.q == 0:
+            return Val("nan")                       # inf * 0
+        neg = (a.q < 0 or (a.q == 0 and a.neg)) if a.kind == "fin" else a.neg
+        neg ^= (b.q < 0 or (b.q == 0 and b.neg)) if b.kind == "fin" else b.neg
+        if c.kind == "inf" and c.neg != neg:
+            return Val("nan")
+        return Val("inf", neg=neg)
+    if c.kind == "inf":
+        return c
+    p = a.q * b.q
+    s = p + c.q
+    if s == 0:
+        pneg = (a.q < 0 or (a.q == 0 and a.neg)) != (b.q < 0 or (b.q == 0 and b.neg))
+        neg = p == 0 and c.q == 0 and pneg and c.neg
+        return Val("fin", Fraction(0), neg)
+    return decode(encode(Val("fin", s, s < 0), "f32"), "f32")
+
+
+def moe_route(ids: list[list[int]], E: int, k: int):
+    """Positions by sorting: the entries bound for the experts of rank j,
+    ordered by (expert, source rank, entry index), take rows 0, 1, ... in
+    that order. Returns (pos, counts, recv) as Python lists."""
+    P = len(ids)
+    per = E // P
+    pos = [[-1] * len(ids[r]) for r in range(P)]
+    counts = [[0] * E for _ in range(P)]
+    recv = [0] * P
+    for j in range(P):
+        keys = sorted((ids[r][i], r, i) for r in range(P) for i in range(len(ids[r]))
+                      if j * per <= ids[r][i] < (j + 1) * per)
+        for row, (e, r, i) in enumerate(keys):
+            pos[r][i] = row
+            counts[r][e] += 1
+        recv[j] = len(keys)
+    return pos, counts, recv
+
+
+def moe_combine(ys: list[list[int]], ids, pos, w_bits, E: int, k: int, H: int, cap: int, fmt: str):
+    """out_r[t][h] = fma chain over the token's k choices in order, from +0,
+    one rounding to the element type. w_bits: binary32 weight bit patterns."""
+    P = len(ys)
+    per = E // P
+    outs = []
+    for r in range(P):
+        T = len(ids[r]) // k
+        o = []
+        for t in range(T):
+            for h in range(H):
+                acc = Val("fin", Fraction(0), False)
+                for c in range(k):
+                    i = t * k + c
+                    e = ids[r][i]
+                    if not (0 <= e < E) or pos[r][i] < 0 or pos[r][i] >= cap:
+                        continue
+                    v = widen(ys[e // per][pos[r][i] * H + h], fmt)
+                    acc = fma_f32(decode(w_bits[r][i], "f32"), v, acc)
+                o.append(encode(acc, fmt))
+        outs.append(o)
+    return outs
+
+
 def is_nan_bits(bits: int, fmt: str) -> bool:
     return decode(bits, fmt).kind == "nan"

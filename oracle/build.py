@@ -21,7 +21,7 @@ CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off",
 
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
-    cmd = ["gcc", *CFLAGS, SRC, "-o", tmp]
+    cmd = ["gcc", *CFLAGS, SRC, "-o", tmp, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -6,11 +6,13 @@
  * blocking, fusion or reordering; see oracle.h for the conventions.
  *
  * Build without fast-math and without contraction so that every binary32
- * addition is one correctly rounded IEEE operation:
+ * addition is one correctly rounded IEEE operation (the MoE combine's fused
+ * multiply-add is the explicit C99 fmaf, one rounding by definition):
  *   gcc -O2 -fno-fast-math -ffp-contract=off -fopenmp -shared -fPIC
  */
 #include "oracle.h"
 
+#include <math.h>
 #include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
@@ -209,6 +211,85 @@ int orc_all_gather_v(int P, const int64_t* cnt, int64_t esize,
             memcpy((char*)out[j] + off * esize, z[k], (size_t)(cnt[k] * esize));
             off += cnt[k];
         }
+    }
+    return 0;
+}
+
+/* ---- MoE dispatch and combine ---------------------------------------- */
+
+static int orc_bad_moe(int P, int E, int k, int64_t T, const int32_t* const* ids)
+{
+    return orc_bad_p(P) || E < P || E % P != 0 || k < 1 || T < 0 || (T > 0 && !ids);
+}
+
+int orc_moe_route(int P, int E, int k, int64_t T, const int32_t* const* ids,
+                  int32_t* const* pos, int32_t* counts, int64_t* recv)
+{
+    if (orc_bad_moe(P, E, k, T, ids) || !pos || !counts || !recv)
+        return -1;
+    const int per = E / P;
+    const int64_t n = T * k;
+    for (int r = 0; r < P; ++r)
+        for (int64_t i = 0; i < n; ++i)
+            pos[r][i] = -1;
+    for (int j = 0; j < P; ++j) {
+        int64_t row = 0;
+        for (int e = j * per; e < (j + 1) * per; ++e)       /* experts in order */
+            for (int r = 0; r < P; ++r) {                   /* sources in order */
+                int32_t c = 0;
+                for (int64_t i = 0; i < n; ++i)             /* entries in order */
+                    if (ids[r][i] == e) {
+                        pos[r][i] = (int32_t)row++;
+                        ++c;
+                    }
+                counts[(int64_t)r * E + e] = c;
+            }
+        recv[j] = row;
+    }
+    return 0;
+}
+
+int orc_moe_dispatch(int P, int E, int k, int64_t T, const int32_t* const* ids,
+                     const int32_t* const* pos, int64_t cap, int64_t row_bytes,
+                     const void* const* x, void* const* out)
+{
+    if (orc_bad_moe(P, E, k, T, ids) || cap < 0 || row_bytes < 0)
+        return -1;
+    const int per = E / P;
+    for (int r = 0; r < P; ++r)
+        for (int64_t i = 0; i < T * k; ++i) {
+            const int32_t e = ids[r][i];
+            if (e < 0 || e >= E || pos[r][i] < 0 || pos[r][i] >= cap)
+                continue;
+            const int64_t t = i / k;
+            memcpy((char*)out[e / per] + (int64_t)pos[r][i] * row_bytes,
+                   (const char*)x[r] + t * row_bytes, (size_t)row_bytes);
+        }
+    return 0;
+}
+
+int orc_moe_combine(int P, int E, int k, int64_t T, const int32_t* const* ids,
+                    const int32_t* const* pos, const float* const* w, int64_t cap,
+                    int64_t H, int dtype, const void* const* y, void* const* out)
+{
+    if (orc_bad_moe(P, E, k, T, ids) || orc_bad_dtype(dtype) || cap < 0 || H < 0)
+        return -1;
+    const int per = E / P;
+    for (int r = 0; r < P; ++r) {
+#pragma omp parallel for schedule(static)
+        for (int64_t t = 0; t < T; ++t)
+            for (int64_t h = 0; h < H; ++h) {
+                float acc = 0.0f;
+                for (int c = 0; c < k; ++c) {
+                    const int64_t i = t * k + c;
+                    const int32_t e = ids[r][i];
+                    if (e < 0 || e >= E || pos[r][i] < 0 || pos[r][i] >= cap)
+                        continue;
+                    const float v = orc_load(y[e / per], dtype, (int64_t)pos[r][i] * H + h);
+                    acc = fmaf(w[r][i], v, acc);
+                }
+                orc_store(out[r], dtype, t * H + h, acc);
+            }
     }
     return 0;
 }

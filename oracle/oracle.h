@@ -66,6 +66,38 @@ int orc_reduce_scatter_v(int P, const int64_t* cnt, int dtype,
 int orc_all_gather_v(int P, const int64_t* cnt, int64_t esize,
                      const void* const* z, void* const* out);
 
+/* ---- Expert-parallel MoE dispatch and combine ------------------------
+ * Table 2 lists expert parallelism among the uses of AllToAll(V): tokens are
+ * dispatched to experts and the expert outputs combined. P ranks host E
+ * experts (E a multiple of P), rank j the experts [j*E/P, (j+1)*E/P). Every
+ * rank holds T tokens; token t of rank r picks k experts ids_r[t*k + c]
+ * (c = 0..k-1), entry i = t*k + c. An id outside [0, E) routes nowhere.
+ *
+ * Route: the dispatch is an AllToAllV whose destinations are the experts.
+ * Expert e receives one row per entry routed to it, from every source rank
+ * in rank order and, within a source, in entry order; rank j's buffer holds
+ * its experts' rows back to back in expert order. pos_r[i] is the row of
+ * entry i in the buffer of the rank hosting its expert (-1 if its id is
+ * invalid), counts[r*E + e] the rows r sends to e, recv[j] the rows rank j
+ * receives. */
+int orc_moe_route(int P, int E, int k, int64_t T, const int32_t* const* ids,
+                  int32_t* const* pos, int32_t* counts, int64_t* recv);
+
+/* Dispatch: out_j[pos_r[i]] = row t = i / k of x_r, for every entry with a
+ * valid id and pos_r[i] < cap (rows of row_bytes bytes; other rows of out_j
+ * are left as they are). */
+int orc_moe_dispatch(int P, int E, int k, int64_t T, const int32_t* const* ids,
+                     const int32_t* const* pos, int64_t cap, int64_t row_bytes,
+                     const void* const* x, void* const* out);
+
+/* Combine: out_r[t][h] = round_T(acc_k), acc_0 = +0, acc_{c+1} =
+ * fma_binary32(w_r[t*k + c], y_j[pos_r[t*k + c]][h], acc_c) in choice order
+ * c = 0..k-1, where j hosts the entry's expert; entries with an invalid id or
+ * pos_r[i] >= cap are skipped. Rows have H elements of dtype. */
+int orc_moe_combine(int P, int E, int k, int64_t T, const int32_t* const* ids,
+                    const int32_t* const* pos, const float* const* w, int64_t cap,
+                    int64_t H, int dtype, const void* const* y, void* const* out);
+
 /* Number of OpenMP threads the loops above use. */
 int orc_threads(void);
 

@@ -20,6 +20,9 @@ Workloads (P virtual ranks held in one GPU's HBM):
   from ``default_rng([3, 1000])``.
 * ``c4``: AllGather, P=8 partitions of S bytes bf16, U[-1,1], seed 4.
 * ``c5``: decode AllReduce, P=8, b x 7168 bf16, N(0, 0.02) (0.02 = std), seed 5.
+* ``moe``: expert-parallel dispatch and combine, P=8 ranks x 512 tokens x
+  7168 bf16, N(0,1), seed 6; E=256 experts (32 per rank), top-8 routing ids
+  and float32 gate weights from ``moe_routing`` (seed 6, stream 1002).
 """
 
 from __future__ import annotations
@@ -34,6 +37,10 @@ F32 = "f32"
 HIDDEN = 7168            # token width of the MoE / decode workloads
 C3_TOKENS = 4096         # tokens per source in the AllToAllV workload
 COUNTS_STREAM = 1000     # rank slot of the count-matrix stream
+ROUTING_STREAM = 1002    # rank slot of the MoE routing stream
+MOE_TOKENS = 512         # tokens per rank in the MoE workload (x top-8 = 4096 rows)
+MOE_EXPERTS = 256
+MOE_TOPK = 8
 
 
 def rank_rng(seed: int, rank: int) -> np.random.Generator:
@@ -207,3 +214,35 @@ def zipf_partition(total: int, P: int, s: float = 0.125, unit: int = 1) -> np.nd
     order = np.argsort(-(share - base), kind="stable")
     base[order[:rest]] += 1
     return base * unit
+
+
+def moe_routing(seed: int, P: int, tokens: int, experts: int, topk: int,
+                alpha: float = 1.0):
+    """Synthetic router output for P ranks of ``tokens`` tokens.
+
+    Expert popularity p ~ Dirichlet(alpha^E) (one draw shared by all ranks,
+    so some experts are hot and some receive nothing); every token then picks
+    ``topk`` distinct experts by Gumbel-top-k sampling from p (a draw without
+    replacement in proportion to p), listed in descending key order. Gate
+    weights are a softmax over ``topk`` N(0,1) logits, in float32. Returns
+    (ids, weights): P int32 arrays and P float32 arrays of tokens*topk,
+    token-major."""
+    g = rank_rng(seed, ROUTING_STREAM)
+    p = g.dirichlet(np.full(experts, alpha))
+    logp = np.log(np.maximum(p, 1e-300))
+    ids, weights = [], []
+    for r in range(P):
+        gr = rank_rng(seed, ROUTING_STREAM + 1 + r)
+        key = logp[None, :] + gr.gumbel(size=(tokens, experts))
+        top = np.argsort(-key, axis=1, kind="stable")[:, :topk]
+        ids.append(np.ascontiguousarray(top, dtype=np.int32).reshape(-1))
+        z = gr.standard_normal((tokens, topk)).astype(np.float32)
+        z = np.exp(z - z.max(axis=1, keepdims=True))
+        weights.append(np.ascontiguousarray(z / z.sum(axis=1, keepdims=True),
+                                            dtype=np.float32).reshape(-1))
+    return ids, weights
+
+
+def moe_inputs(P: int = 8, tokens: int = MOE_TOKENS, hidden: int = HIDDEN):
+    """Token rows of the MoE workload: P ranks of tokens x hidden bf16, N(0,1), seed 6."""
+    return ranks(6, P, tokens * hidden, "normal", BF16)
