@@ -15,6 +15,10 @@ resident synthetic input (bf16):
   rsv_zipf ReduceScatterV of the 8 x 256 MiB, Zipf(0.125) partitions (Figure 16)
   agv_zipf AllGatherV of 512 MiB in Zipf(0.125) partitions
   ag_8k   AllGather, zero staging, 8 partitions of 8 KiB
+  moe_route, moe_dispatch, moe_combine
+          expert-parallel MoE (Table 2): routing of 8 ranks x 512 tokens, top-8
+          of 256 experts (seed 6), dispatch of the 7168-wide bf16 token rows to
+          the experts and the weighted combine of same-shape expert outputs
 
 `value` is the step's credited bytes (every input element read once, every
 output element written once, a reduced element counted with its P reads)
@@ -124,6 +128,16 @@ def main():
     # 8 KiB AllGather
     z8 = [up(z) for z in synth.c4_inputs(8 << 10, P)]
     o8 = [empty(P * 4096) for _ in range(P)]
+    # MoE dispatch / combine
+    moe_ids, moe_w = synth.moe_routing(6, P, synth.MOE_TOKENS, synth.MOE_EXPERTS, synth.MOE_TOPK)
+    moe_rt = A.moe_alloc_routing([torch.from_numpy(a).to(dev) for a in moe_ids],
+                                 synth.MOE_EXPERTS, synth.MOE_TOPK)
+    A.atom_moe_route(moe_rt)
+    moe_cap = int(moe_rt.recv_t.max().item())
+    moe_x = [up(x) for x in synth.moe_inputs()]
+    moe_w = [torch.from_numpy(a).to(dev) for a in moe_w]
+    moe_disp = [empty(moe_cap * synth.HIDDEN) for _ in range(P)]
+    moe_out = [empty(synth.MOE_TOKENS * synth.HIDDEN) for _ in range(P)]
     torch.cuda.synchronize()
     log(f"inputs resident in HBM ({time.time() - t0:.1f} s)")
 
@@ -177,6 +191,18 @@ def main():
     lay8 = (L(A.SHARD, z8, 4096), L(A.GATHERED, o8, 4096))
     ag8 = lambda l=lay8: A.atom_collective(l[0], l[1], A.OP_COPY)
     rows.append(("ag_8k", ag8, plan_bytes(lay8[0], lay8[1], A.OP_COPY, name="ag_8k")))
+    # MoE: the routing (metadata only), then dispatch into the experts'
+    # buffers, then the combine of those buffers (standing in for the expert
+    # outputs, same shape) back to the tokens.
+    mb = moe_bytes(P, synth.MOE_TOKENS, synth.MOE_EXPERTS, synth.MOE_TOPK, synth.HIDDEN * 2)
+    rows.append(("moe_route", lambda: A.atom_moe_route(moe_rt), mb["route"]))
+    rows.append(("moe_dispatch", lambda: A.atom_moe_dispatch(moe_rt, moe_x, moe_disp, moe_cap,
+                                                             synth.HIDDEN), mb["dispatch"]))
+    rows.append(("moe_combine", lambda: A.atom_moe_combine(moe_rt, moe_disp, moe_w, moe_out, moe_cap,
+                                                           synth.HIDDEN), mb["combine"]))
+    nch = -(-synth.MOE_TOKENS * synth.MOE_TOPK // 1024)
+    cus.update({"moe_route": min(256, P * nch), "moe_dispatch": min(256, P * synth.MOE_TOKENS),
+                "moe_combine": min(256, P * synth.MOE_TOKENS)})
 
     step_bytes = sum(r[2] for r in rows)
 
@@ -269,7 +295,9 @@ def main():
                          + (" and SNAC, 1 MiB chunks, 32-slot ring); SNAC-composed AllReduce of the "
                             "8 x 256 MiB; " if args.snac else "); ") +
                          "ReduceScatterV and AllGatherV with Zipf(0.125) partitions of the same totals; "
-                         "decode AllReduce 8 x b x 7168 bf16, b = 1..16; AllGather 8 x 8 KiB"),
+                         "decode AllReduce 8 x b x 7168 bf16, b = 1..16; AllGather 8 x 8 KiB; "
+                         "MoE route, dispatch and combine of 8 x 512 tokens x 7168 bf16 "
+                         "(256 experts, top-8)"),
             "P": P, "step_credited_bytes": int(step_bytes),
         },
         "reduce8_GBps": per_row["rs8"]["GBps"],
@@ -353,6 +381,18 @@ def measured_traffic(row):
     return int(row_d["traffic_bytes"]) if row_d else None
 
 
+def moe_bytes(P, T, E, k, row_bytes):
+    """Algorithmic bytes of the MoE rows. Route: the ids read, the positions
+    written, the counts and rows-received written. Dispatch: each token row
+    read once and written once per choice, plus the ids and positions read.
+    Combine: each choice's row read once and the token row written once, plus
+    the ids, positions and weights read."""
+    n = P * T * k
+    return {"route": n * 8 + P * E * 4 + P * 8,
+            "dispatch": P * T * (k + 1) * row_bytes + n * 8,
+            "combine": P * T * (k + 1) * row_bytes + n * 12}
+
+
 def cpu_baseline(args, C3, S, credited):
     """The oracle, as it stands, on the same step (same seeds and shapes, its
     own OpenMP threads); GB/s on the same credited bytes."""
@@ -368,6 +408,8 @@ def cpu_baseline(args, C3, S, credited):
     cnt_rs = synth.zipf_partition(1 << 27, P, 0.125, 8) // 8
     cnt_ag = synth.zipf_partition(P * S // 2, P, 0.125, 8) // 8
     zv = [synth.draw(4, k, int(cnt_ag[k]) * 8, "uniform", synth.BF16) for k in range(P)]
+    moe_ids, moe_w = synth.moe_routing(6, P, synth.MOE_TOKENS, synth.MOE_EXPERTS, synth.MOE_TOPK)
+    moe_x = synth.moe_inputs()
     times = []
     for _ in range(args.cpu_reps):
         t = time.perf_counter()
@@ -384,6 +426,10 @@ def cpu_baseline(args, C3, S, credited):
         oracle.reduce_scatter_v(c2, cnt_rs * 8)
         oracle.all_gather_v(zv)
         oracle.all_gather(z8)
+        E, k, H = synth.MOE_EXPERTS, synth.MOE_TOPK, synth.HIDDEN
+        pos, _, recv = oracle.moe_route(moe_ids, E, k)
+        disp = oracle.moe_dispatch(moe_x, moe_ids, pos, E, k, H, int(recv.max()))
+        oracle.moe_combine(disp, moe_ids, pos, moe_w, E, k, H, int(recv.max()))
         times.append(time.perf_counter() - t)
     best = float(np.median(times))
     return {"value": round(credited / best / 1e9, 2), "unit": "GB/s", "cores": oracle.threads(),

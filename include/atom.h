@@ -217,6 +217,91 @@ const char* atom_status_string(atom_status s);
  * ATOM_ERR_HIP (a static string; "no HIP error" if there was none). */
 const char* atom_last_error(void);
 
+/* ---- Expert-parallel MoE dispatch and combine ---------------------------
+ * Table 2 lists expert parallelism among the uses of AllToAll(V): tokens are
+ * dispatched to experts and the expert outputs combined. P ranks host E
+ * experts (E a multiple of P): rank j hosts experts [j*E/P, (j+1)*E/P).
+ * Every rank holds T tokens; token t of rank r picks k experts, the ids
+ * expert_ids[r][t*k + c] for choice c = 0..k-1 (entry i = t*k + c). An id
+ * outside [0, E) routes nowhere.
+ *
+ * Dispatch is the AllToAllV whose destinations are the experts: expert e
+ * receives one row per entry routed to it, from every source rank in rank
+ * order and, within a source, in entry order; rank j's dispatch buffer holds
+ * its experts' rows back to back in expert order (each expert's rows are
+ * contiguous, ready for a grouped expert computation). Combine is its way
+ * back: out[r][t] = sum over c of weights[r][t*k + c] * (the row entry
+ * t*k + c was dispatched to), accumulated in binary32 from +0 by one fused
+ * multiply-add per choice in choice order, rounded once to the row dtype.
+ *
+ * All arrays named below are device memory owned by the caller. Calls are
+ * stream-ordered and asynchronous; arguments are validated on the host
+ * before anything is launched. Buffers may not overlap unless stated. */
+
+#define ATOM_MOE_MAX_EXPERTS 1024
+#define ATOM_MOE_MAX_TOPK 16
+#define ATOM_MOE_MAX_ENTRIES (1 << 20)   /* T*k per rank */
+
+typedef struct atom_moe_routing {
+    int32_t nranks;                    /* P, 1..ATOM_MAX_RANKS */
+    int32_t num_experts;               /* E, a multiple of P, at most
+                                          ATOM_MOE_MAX_EXPERTS */
+    int32_t topk;                      /* k, 1..ATOM_MOE_MAX_TOPK */
+    int32_t reserved;                  /* must be 0 */
+    int64_t tokens;                    /* T per rank, T*k <= ATOM_MOE_MAX_ENTRIES */
+    const int32_t* const* expert_ids;  /* host array of P device pointers, each
+                                          T*k int32 (token-major); read only */
+    int32_t* const* positions;         /* host array of P device pointers, each
+                                          T*k int32; written by atom_moe_route:
+                                          the row of entry i in the dispatch
+                                          buffer of the rank hosting its expert,
+                                          -1 for an invalid id */
+    int32_t* counts;                   /* P*E int32, written by atom_moe_route:
+                                          counts[r*E + e] = rows rank r sends
+                                          to expert e */
+    int64_t* recv_rows;                /* P int64, written by atom_moe_route:
+                                          rows rank j receives */
+    void* scratch;                     /* atom_moe_scratch_bytes(...) bytes,
+                                          16-byte aligned, used by
+                                          atom_moe_route only */
+} atom_moe_routing;
+
+/* Bytes of scratch atom_moe_route needs for this shape (0 for invalid
+ * arguments). */
+int64_t atom_moe_scratch_bytes(int32_t nranks, int32_t num_experts,
+                               int32_t topk, int64_t tokens);
+
+/* Routing: fills positions, counts and recv_rows from expert_ids (the
+ * layout of the dispatch). Returns ATOM_OK, ATOM_ERR_INVALID_ARG (a field
+ * out of range, a NULL pointer, misaligned scratch) or ATOM_ERR_HIP. */
+atom_status atom_moe_route(const atom_moe_routing* rt, void* stream);
+
+/* Dispatch: for every entry with a valid id whose position is below
+ * capacity_rows, copies row t of x[r] (row_elems elements of dtype) to row
+ * positions[r][i] of out[j], j the rank hosting the entry's expert. Each
+ * token row is read once and written once per choice. x: host array of P
+ * device pointers to T rows; out: host array of P device pointers to
+ * capacity_rows rows each (rows no entry lands on are not written). Uses
+ * the positions of the last atom_moe_route on rt. Rows at or beyond
+ * capacity_rows are dropped; recv_rows tells how many would land. Needs
+ * 16-byte aligned buffers and rows (else ATOM_ERR_UNSUPPORTED). Returns
+ * ATOM_OK, ATOM_ERR_INVALID_ARG, ATOM_ERR_UNSUPPORTED or ATOM_ERR_HIP. */
+atom_status atom_moe_dispatch(const atom_moe_routing* rt, const void* const* x,
+                              void* const* out, int64_t capacity_rows,
+                              int64_t row_elems, atom_dtype dtype, void* stream);
+
+/* Combine: out[r] row t = round(sum over c of weights[r][t*k + c] * y row),
+ * the y row being row positions[r][i] of y[j] for the entry's rank j;
+ * entries with an invalid id or a position at or beyond capacity_rows are
+ * skipped. y: host array of P device pointers to capacity_rows rows (the
+ * expert outputs, in dispatch layout); weights: host array of P device
+ * pointers to T*k float; out: host array of P device pointers to T rows.
+ * Same alignment rule and return codes as atom_moe_dispatch. */
+atom_status atom_moe_combine(const atom_moe_routing* rt, const void* const* y,
+                             const float* const* weights, void* const* out,
+                             int64_t capacity_rows, int64_t row_elems,
+                             atom_dtype dtype, void* stream);
+
 /* Library version, (major << 16) | minor. */
 int32_t atom_version(void);
 

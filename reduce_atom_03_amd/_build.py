@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libatom.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["abi.cpp", "plan.cpp", "k_reduce.hip", "k_copy.hip", "k_snac.hip"]
+SOURCES = ["abi.cpp", "plan.cpp", "k_reduce.hip", "k_copy.hip", "k_snac.hip", "k_moe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -73,9 +73,28 @@ class AtomPlanInfo(ctypes.Structure):
     ]
 
 
+MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_ENTRIES = 1024, 16, 1 << 20
+
+
+class AtomMoeRouting(ctypes.Structure):
+    _fields_ = [
+        ("nranks", ctypes.c_int32),
+        ("num_experts", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("tokens", ctypes.c_int64),
+        ("expert_ids", ctypes.POINTER(ctypes.c_void_p)),
+        ("positions", ctypes.POINTER(ctypes.c_void_p)),
+        ("counts", ctypes.c_void_p),
+        ("recv_rows", ctypes.c_void_p),
+        ("scratch", ctypes.c_void_p),
+    ]
+
+
 EXPORTS = ("atom_copy", "atom_reduce", "atom_collective", "atom_plan_query",
            "atom_sync_status", "atom_bdp_chunk_bytes", "atom_status_string",
-           "atom_last_error", "atom_version")
+           "atom_last_error", "atom_version", "atom_moe_scratch_bytes",
+           "atom_moe_route", "atom_moe_dispatch", "atom_moe_combine")
 
 
 def _hip_runtimes() -> set:
@@ -121,6 +140,18 @@ def _load() -> ctypes.CDLL:
     lib.atom_last_error.restype = ctypes.c_char_p
     lib.atom_version.argtypes = []
     lib.atom_version.restype = ctypes.c_int32
+    rp = ctypes.POINTER(AtomMoeRouting)
+    vpp = ctypes.POINTER(vp)
+    lib.atom_moe_scratch_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int64]
+    lib.atom_moe_scratch_bytes.restype = ctypes.c_int64
+    lib.atom_moe_route.argtypes = [rp, vp]
+    lib.atom_moe_route.restype = ctypes.c_int
+    lib.atom_moe_dispatch.argtypes = [rp, vpp, vpp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, vp]
+    lib.atom_moe_dispatch.restype = ctypes.c_int
+    lib.atom_moe_combine.argtypes = [rp, vpp, vpp, vpp, ctypes.c_int64, ctypes.c_int64,
+                                     ctypes.c_int, vp]
+    lib.atom_moe_combine.restype = ctypes.c_int
     return lib
 
 
@@ -322,3 +353,79 @@ def all_gather_v(zs: Sequence, outs: Sequence, counts, row_elems: int = 1, cfg=N
     return atom_collective(layout(SHARD, zs, 0, counts, row_elems),
                            layout(GATHERED, outs, 0, None, row_elems), OP_COPY, cfg,
                            _stream(stream, outs[0]), check)
+
+
+# ------------------------------------------- MoE dispatch / combine (Table 2)
+
+def _ptr_array(xs):
+    arr = (ctypes.c_void_p * max(len(xs), 1))(*[_ptr(x) for x in xs])
+    return arr, ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+
+
+def atom_moe_scratch_bytes(nranks: int, num_experts: int, topk: int, tokens: int) -> int:
+    return int(lib.atom_moe_scratch_bytes(int(nranks), int(num_experts), int(topk), int(tokens)))
+
+
+def moe_routing(expert_ids: Sequence, num_experts: int, topk: int, positions: Sequence,
+                counts, recv_rows, scratch, tokens: Optional[int] = None) -> AtomMoeRouting:
+    """An atom_moe_routing over caller-owned device arrays (tensors or int
+    addresses). The structure keeps its pointer arrays alive."""
+    P = len(expert_ids)
+    if tokens is None:
+        tokens = expert_ids[0].numel() // topk
+    ids_arr, ids_p = _ptr_array(expert_ids)
+    pos_arr, pos_p = _ptr_array(positions)
+    rt = AtomMoeRouting(nranks=P, num_experts=int(num_experts), topk=int(topk), reserved=0,
+                        tokens=int(tokens), expert_ids=ids_p, positions=pos_p,
+                        counts=_ptr(counts), recv_rows=_ptr(recv_rows), scratch=_ptr(scratch))
+    rt._keep = [ids_arr, pos_arr]
+    return rt
+
+
+def moe_alloc_routing(expert_ids: Sequence, num_experts: int, topk: int) -> AtomMoeRouting:
+    """moe_routing with its positions, counts, recv_rows and scratch
+    allocated by torch on the ids' device (kept alive by the structure as
+    .positions_t, .counts_t, .recv_t)."""
+    import torch
+    P = len(expert_ids)
+    dev = expert_ids[0].device
+    T = expert_ids[0].numel() // topk
+    pos = [torch.empty(T * topk, dtype=torch.int32, device=dev) for _ in range(P)]
+    counts = torch.empty(P * num_experts, dtype=torch.int32, device=dev)
+    recv = torch.empty(P, dtype=torch.int64, device=dev)
+    nbytes = atom_moe_scratch_bytes(P, num_experts, topk, T)
+    scratch = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    rt = moe_routing(expert_ids, num_experts, topk, pos, counts, recv, scratch, T)
+    rt._keep += [list(expert_ids), scratch]
+    rt.positions_t, rt.counts_t, rt.recv_t = pos, counts, recv
+    return rt
+
+
+def atom_moe_route(rt: AtomMoeRouting, stream=None, check: bool = True) -> int:
+    st = lib.atom_moe_route(ctypes.byref(rt), _stream(stream))
+    return _check(st, "atom_moe_route", check)
+
+
+def atom_moe_dispatch(rt: AtomMoeRouting, x: Sequence, out: Sequence, capacity_rows: int,
+                      row_elems: int, dtype: Optional[int] = None, stream=None,
+                      check: bool = True) -> int:
+    xa, xp = _ptr_array(x)
+    oa, op = _ptr_array(out)
+    if dtype is None:
+        dtype = _dtype_code(x[0])
+    st = lib.atom_moe_dispatch(ctypes.byref(rt), xp, op, int(capacity_rows), int(row_elems),
+                               dtype, _stream(stream, out[0] if out else None))
+    return _check(st, "atom_moe_dispatch", check)
+
+
+def atom_moe_combine(rt: AtomMoeRouting, y: Sequence, weights: Sequence, out: Sequence,
+                     capacity_rows: int, row_elems: int, dtype: Optional[int] = None,
+                     stream=None, check: bool = True) -> int:
+    ya, yp = _ptr_array(y)
+    wa, wp = _ptr_array(weights)
+    oa, op = _ptr_array(out)
+    if dtype is None:
+        dtype = _dtype_code(out[0])
+    st = lib.atom_moe_combine(ctypes.byref(rt), yp, wp, op, int(capacity_rows), int(row_elems),
+                              dtype, _stream(stream, out[0] if out else None))
+    return _check(st, "atom_moe_combine", check)

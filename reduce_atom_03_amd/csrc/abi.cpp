@@ -180,6 +180,44 @@ atom_status atom_sync_status(void* stream)
     return ATOM_ERR_TIMEOUT;
 }
 
+int64_t atom_moe_scratch_bytes(int32_t nranks, int32_t num_experts, int32_t topk, int64_t tokens)
+{
+    return atom::moe_scratch_bytes(nranks, num_experts, topk, tokens);
+}
+
+atom_status atom_moe_route(const atom_moe_routing* rt, void* stream)
+{
+    atom::MoeRoutePlan p;
+    atom_status st = atom::plan_moe_route(rt, &p);
+    if (st != ATOM_OK)
+        return st;
+    (void)hipGetLastError();
+    return atom::hip_status(atom::launch_moe_route(p, static_cast<hipStream_t>(stream)));
+}
+
+atom_status atom_moe_dispatch(const atom_moe_routing* rt, const void* const* x, void* const* out,
+                              int64_t capacity_rows, int64_t row_elems, atom_dtype dtype, void* stream)
+{
+    atom::MoeMovePlan p;
+    atom_status st = atom::plan_moe_move(rt, false, x, nullptr, out, capacity_rows, row_elems, dtype, &p);
+    if (st != ATOM_OK)
+        return st;
+    (void)hipGetLastError();
+    return atom::hip_status(atom::launch_moe_move(p, false, static_cast<hipStream_t>(stream)));
+}
+
+atom_status atom_moe_combine(const atom_moe_routing* rt, const void* const* y, const float* const* weights,
+                             void* const* out, int64_t capacity_rows, int64_t row_elems, atom_dtype dtype,
+                             void* stream)
+{
+    atom::MoeMovePlan p;
+    atom_status st = atom::plan_moe_move(rt, true, y, weights, out, capacity_rows, row_elems, dtype, &p);
+    if (st != ATOM_OK)
+        return st;
+    (void)hipGetLastError();
+    return atom::hip_status(atom::launch_moe_move(p, true, static_cast<hipStream_t>(stream)));
+}
+
 const char* atom_last_error(void)
 {
     return atom::t_last_hip == hipSuccess ? "no HIP error" : hipGetErrorString(atom::t_last_hip);

@@ -101,6 +101,47 @@ struct SnacArgs {
     int32_t pad_;
 };
 
+// Expert-parallel MoE routing (three kernels: rank within chunks, scan,
+// place). Entries i = t*k + c of rank r are cut into chunks of kMoeChunk.
+constexpr int kMoeChunk = 1024;        // entries one wave ranks in order
+constexpr int kMoeMaxTopk = 16;
+
+struct MoeRouteArgs {
+    const int32_t* ids[kMaxRanks];     // T*k expert ids per rank
+    int32_t* pos[kMaxRanks];           // T*k positions per rank (output)
+    int32_t* counts;                   // [P][E] rows rank r sends to expert e
+    int64_t* recv;                     // [P] rows rank j receives
+    int32_t* partial;                  // [P][nch][E]: chunk histograms, then
+                                       // rows of expert e before the chunk
+    int32_t* base;                     // [E]: rows of the earlier experts of
+                                       // the same rank
+    int64_t n;                         // entries per rank (T*k)
+    int32_t nch;                       // chunks per rank (at least 1)
+    int32_t P;
+    int32_t E;
+    int32_t per;                       // experts per rank
+};
+
+// MoE dispatch (token rows -> expert buffers) and combine (expert rows ->
+// weighted token rows). One tile is one token's row.
+struct MoeMoveArgs {
+    const char* src[kMaxRanks];        // dispatch: x_r; combine: y_j
+    char* dst[kMaxRanks];              // dispatch: out_j; combine: out_r
+    const int32_t* ids[kMaxRanks];
+    const int32_t* pos[kMaxRanks];
+    const float* w[kMaxRanks];         // combine: gate weights, T*k per rank
+    int64_t T;                         // tokens per rank
+    int64_t cap;                       // rows of each expert-side buffer
+    int64_t row_bytes;                 // multiple of 16
+    int64_t ntiles;                    // P * T
+    int32_t P;
+    int32_t E;
+    int32_t per;
+    int32_t k;
+    int32_t dtype;
+    int32_t nt_store;
+};
+
 // Bytes before a segment's first byte in its first tile when tiles are
 // aligned to `tile_bytes` at the destination address `dst_addr` (the same
 // arithmetic on the host, to count tiles, and on the device, to place them).

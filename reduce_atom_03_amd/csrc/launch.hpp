@@ -22,5 +22,7 @@ struct Workspace {
 hipError_t launch_reduce(const Plan& p, hipStream_t stream);
 hipError_t launch_copy(const Plan& p, hipStream_t stream);
 hipError_t launch_snac(const Plan& p, const Workspace& ws, hipStream_t stream);
+hipError_t launch_moe_route(const MoeRoutePlan& p, hipStream_t stream);
+hipError_t launch_moe_move(const MoeMovePlan& p, bool combine, hipStream_t stream);
 
 }  // namespace atom

@@ -656,6 +656,155 @@ atom_status plan_collective(const atom_layout* in, const atom_layout* out, atom_
     return ATOM_OK;
 }
 
+// ---- MoE (Table 2, expert parallelism) ----------------------------------
+
+namespace {
+
+// The routing fields every MoE call needs; T*k entries per rank.
+atom_status check_routing(const atom_moe_routing* rt)
+{
+    if (!rt || rt->reserved != 0)
+        return ATOM_ERR_INVALID_ARG;
+    const int64_t P = rt->nranks, E = rt->num_experts, k = rt->topk, T = rt->tokens;
+    if (P < 1 || P > kMaxRanks || E < P || E > ATOM_MOE_MAX_EXPERTS || E % P != 0 || k < 1 ||
+        k > kMoeMaxTopk || T < 0 || T > ATOM_MOE_MAX_ENTRIES || T * k > ATOM_MOE_MAX_ENTRIES)
+        return ATOM_ERR_INVALID_ARG;
+    if (T > 0) {
+        if (!rt->expert_ids || !rt->positions)
+            return ATOM_ERR_INVALID_ARG;
+        for (int r = 0; r < P; ++r)
+            if (!buffer_ok(rt->expert_ids[r], T * k * 4, 4) || !buffer_ok(rt->positions[r], T * k * 4, 4))
+                return ATOM_ERR_INVALID_ARG;
+    }
+    return ATOM_OK;
+}
+
+int32_t moe_chunks(int64_t n) { return static_cast<int32_t>(std::max<int64_t>(1, ceil_div(n, kMoeChunk))); }
+
+}  // namespace
+
+int64_t moe_scratch_bytes(int32_t P, int32_t E, int32_t k, int64_t T)
+{
+    if (P < 1 || P > kMaxRanks || E < P || E > ATOM_MOE_MAX_EXPERTS || E % P != 0 || k < 1 ||
+        k > kMoeMaxTopk || T < 0 || T > ATOM_MOE_MAX_ENTRIES || T * k > ATOM_MOE_MAX_ENTRIES)
+        return 0;
+    const int64_t ints = static_cast<int64_t>(P) * moe_chunks(T * k) * E + E;
+    return ceil_div(ints * 4, 256) * 256;
+}
+
+atom_status plan_moe_route(const atom_moe_routing* rt, MoeRoutePlan* p)
+{
+    if (!p)
+        return ATOM_ERR_INVALID_ARG;
+    if (atom_status st = check_routing(rt); st != ATOM_OK)
+        return st;
+    const int P = rt->nranks, E = rt->num_experts;
+    const int64_t n = rt->tokens * rt->topk;
+    if (!rt->counts || !rt->recv_rows || !rt->scratch || !aligned(rt->scratch, 16) ||
+        !aligned(rt->counts, 4) || !aligned(rt->recv_rows, 8))
+        return ATOM_ERR_INVALID_ARG;
+    const int64_t sbytes = moe_scratch_bytes(P, E, rt->topk, rt->tokens);
+    // Written ranges (positions, counts, recv, scratch) must be disjoint from
+    // each other and from the ids.
+    Range ins[kMaxRanks], outs[kMaxRanks + 3];
+    int nin = 0, nout = 0;
+    for (int r = 0; r < P && n > 0; ++r) {
+        ins[nin++] = range_of(rt->expert_ids[r], n * 4);
+        outs[nout++] = range_of(rt->positions[r], n * 4);
+    }
+    outs[nout++] = range_of(rt->counts, static_cast<int64_t>(P) * E * 4);
+    outs[nout++] = range_of(rt->recv_rows, static_cast<int64_t>(P) * 8);
+    outs[nout++] = range_of(rt->scratch, sbytes);
+    if (!disjoint(ins, nin, outs, nout))
+        return ATOM_ERR_INVALID_ARG;
+    MoeRouteArgs& a = p->a;
+    a = MoeRouteArgs{};
+    for (int r = 0; r < P; ++r) {
+        a.ids[r] = n > 0 ? rt->expert_ids[r] : nullptr;
+        a.pos[r] = n > 0 ? rt->positions[r] : nullptr;
+    }
+    a.counts = rt->counts;
+    a.recv = rt->recv_rows;
+    a.n = n;
+    a.nch = moe_chunks(n);
+    a.P = P;
+    a.E = E;
+    a.per = E / P;
+    a.partial = static_cast<int32_t*>(rt->scratch);
+    a.base = a.partial + static_cast<int64_t>(P) * a.nch * E;
+    p->scan_threads = static_cast<int32_t>(ceil_div(E, 64) * 64);
+    return ATOM_OK;
+}
+
+atom_status plan_moe_move(const atom_moe_routing* rt, bool combine, const void* const* src,
+                          const float* const* w, void* const* dst, int64_t cap, int64_t row_elems,
+                          atom_dtype dtype, MoeMovePlan* p)
+{
+    if (!p)
+        return ATOM_ERR_INVALID_ARG;
+    if (atom_status st = check_routing(rt); st != ATOM_OK)
+        return st;
+    const int es = esize_of(dtype);
+    const int P = rt->nranks;
+    const int64_t T = rt->tokens, k = rt->topk;
+    int64_t row_bytes = 0, tok_bytes = 0, cap_bytes = 0;
+    if (es == 0 || row_elems < 1 || cap < 0 || cap > INT32_MAX || !mul_ok(row_elems, es, &row_bytes) ||
+        !mul_ok(T, row_bytes, &tok_bytes) || !mul_ok(cap, row_bytes, &cap_bytes))
+        return ATOM_ERR_INVALID_ARG;
+    if (T > 0 && (!src || !dst || (combine && !w)))
+        return ATOM_ERR_INVALID_ARG;
+    // dispatch reads T rows per rank and writes cap rows per rank; combine
+    // reads cap rows per rank (and T*k weights) and writes T rows per rank.
+    const int64_t src_bytes = combine ? cap_bytes : tok_bytes;
+    const int64_t dst_bytes = combine ? tok_bytes : cap_bytes;
+    bool vec = row_bytes % kVecBytes == 0;
+    Range ins[2 * kMaxRanks + 2 * kMaxRanks], outs[kMaxRanks];
+    int nin = 0, nout = 0;
+    for (int r = 0; r < P && T > 0; ++r) {
+        if (!buffer_ok(src[r], src_bytes, es) || !buffer_ok(dst[r], dst_bytes, es))
+            return ATOM_ERR_INVALID_ARG;
+        if (combine && !buffer_ok(w[r], T * k * 4, 4))
+            return ATOM_ERR_INVALID_ARG;
+        vec = vec && aligned(src[r], kVecBytes) && aligned(dst[r], kVecBytes);
+        ins[nin++] = range_of(src[r], src_bytes);
+        if (combine)
+            ins[nin++] = range_of(w[r], T * k * 4);
+        ins[nin++] = range_of(rt->expert_ids[r], T * k * 4);
+        ins[nin++] = range_of(rt->positions[r], T * k * 4);
+        outs[nout++] = range_of(dst[r], dst_bytes);
+    }
+    if (!disjoint(ins, nin, outs, nout))
+        return ATOM_ERR_INVALID_ARG;
+    if (T > 0 && !vec)
+        return ATOM_ERR_UNSUPPORTED;
+    MoeMoveArgs& a = p->a;
+    a = MoeMoveArgs{};
+    for (int r = 0; r < P && T > 0; ++r) {
+        a.src[r] = static_cast<const char*>(src[r]);
+        a.dst[r] = static_cast<char*>(dst[r]);
+        a.ids[r] = rt->expert_ids[r];
+        a.pos[r] = rt->positions[r];
+        a.w[r] = combine ? w[r] : nullptr;
+    }
+    a.T = T;
+    a.cap = cap;
+    a.row_bytes = row_bytes;
+    a.ntiles = static_cast<int64_t>(P) * T;
+    a.P = P;
+    a.E = rt->num_experts;
+    a.per = rt->num_experts / P;
+    a.k = static_cast<int32_t>(k);
+    a.dtype = dtype == ATOM_DT_BF16 ? DT_BF16 : DT_F32;
+    a.nt_store = 1;
+    p->U = combine ? 1 : 4;
+    p->grid = a.ntiles > 0 ? pick_grid(a.ntiles, 0) : 0;
+    // Algorithmic bytes: every token row read once and written once per
+    // choice (dispatch), or every choice's row read once and the token row
+    // written once (combine); plus the ids, positions (and weights) read.
+    p->credited_bytes = a.ntiles * ((k + 1) * row_bytes + k * (combine ? 12 : 8));
+    return ATOM_OK;
+}
+
 void plan_fill_info(const Plan& p, atom_plan_info* info)
 {
     std::memset(info, 0, sizeof *info);

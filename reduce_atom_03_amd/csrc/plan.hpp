@@ -51,6 +51,27 @@ constexpr int64_t kMaxGrid = 1 << 20;
 constexpr int64_t kSmallSlots = 256 * 256;           // below: the latency path
 constexpr int64_t kDefaultWaitUs = 1000000;          // one SNAC wait: 1 s
 
+// MoE routing and movement plans.
+struct MoeRoutePlan {
+    MoeRouteArgs a;
+    int32_t scan_threads = 64;         // one workgroup, one thread per expert
+};
+
+struct MoeMovePlan {
+    MoeMoveArgs a;
+    int64_t grid = 0;
+    int32_t U = 1;                     // 16-byte slots per lane per step
+    int64_t credited_bytes = 0;        // when every id is valid and fits
+};
+
+int64_t moe_scratch_bytes(int32_t P, int32_t E, int32_t k, int64_t T);
+atom_status plan_moe_route(const atom_moe_routing* rt, MoeRoutePlan* p);
+// combine == false: dispatch (src = x, dst = out, w unused);
+// combine == true: combine (src = y, dst = out, w = weights).
+atom_status plan_moe_move(const atom_moe_routing* rt, bool combine, const void* const* src,
+                          const float* const* w, void* const* dst, int64_t cap, int64_t row_elems,
+                          atom_dtype dtype, MoeMovePlan* p);
+
 atom_status plan_copy(void* dst, const void* src, size_t bytes, const atom_config* cfg,
                       Plan* p);
 atom_status plan_reduce(void* dst, const void* const* srcs, int32_t nsrcs, int64_t count,

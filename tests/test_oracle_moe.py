@@ -16,7 +16,7 @@ as its way back, a weighted sum over each token's choices. Pins:
   expert order, rows of one (expert, source) pair keep entry order, and
   every dispatched row carries its own (rank, token) tag.
 * Closed forms: weights 1/k over identity experts give every token back
-  exactly; k = 1 with weight 1 is a gather.
+  exactly (-0 as +0); k = 1 with weight 1 is a gather.
 * Error bound against the float64 weighted sum (Higham, Accuracy and
   Stability of Numerical Algorithms, sec. 3.1 and 4.2).
 * Mutation checks: plausible mistakes planted in numpy copies fail a pin.
@@ -193,17 +193,21 @@ def pin_combine_brute(impl):
 
 def pin_combine_identity(impl):
     """Weights 1/k on identity experts: every partial sum c*x/k is exact in
-    binary32 for bf16 x, so each token comes back bit for bit."""
+    binary32 for bf16 x, so each token comes back bit for bit, except -0,
+    which comes back +0 because the sum starts from +0."""
     P, T, E, k, H = 4, 16, 8, 8, 32
     ids = random_ids(51, P, T, E, k)
     xs = synth.ranks(51, P, T * H, "normal", synth.BF16)
+    xs[1][7] = 0x8000
+    xs[2][9] = 0x0000
     pos, _, recv = impl.route(ids, E, k)
     cap = int(recv.max())
     ys = impl.dispatch(xs, ids, pos, E, k, H, cap)
     w = [np.full(T * k, 1.0 / k, dtype=np.float32) for _ in range(P)]
     out = impl.combine(ys, ids, pos, w, E, k, H, cap)
     for r in range(P):
-        assert_bits_equal(out[r], xs[r], f"rank {r}")
+        assert_bits_equal(out[r], np.where(xs[r] == 0x8000, 0, xs[r]).astype(np.uint16),
+                          f"rank {r}")
 
 
 def pin_combine_single_choice(impl):
