@@ -200,7 +200,7 @@ def main():
                                                              synth.HIDDEN), mb["dispatch"]))
     rows.append(("moe_combine", lambda: A.atom_moe_combine(moe_rt, moe_disp, moe_w, moe_out, moe_cap,
                                                            synth.HIDDEN), mb["combine"]))
-    nch = -(-synth.MOE_TOKENS * synth.MOE_TOPK // 1024)
+    nch = -(-synth.MOE_TOKENS * synth.MOE_TOPK // 256)
     cus.update({"moe_route": min(256, P * nch), "moe_dispatch": min(256, P * synth.MOE_TOKENS),
                 "moe_combine": min(256, P * synth.MOE_TOKENS)})
 

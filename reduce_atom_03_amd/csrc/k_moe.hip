@@ -9,16 +9,19 @@
 // combine is the way back, a weighted sum over each token's k choices.
 //
 // Routing (three small launches, metadata only):
-//   k_moe_rank   one wave per chunk of 1024 entries of one rank: the rank of
+//   k_moe_rank   one wave per chunk of 256 entries of one rank: the rank of
 //                every entry among the chunk's entries with the same expert,
-//                in entry order (wave ballots group equal ids; an LDS counter
-//                per expert carries over between 64-entry steps), and the
-//                chunk's histogram;
-//   k_moe_scan   one workgroup, one thread per expert: rows of expert e
-//                before each (rank, chunk) -- earlier ranks, earlier chunks --
-//                and, by a prefix sum over the experts of each rank, the
-//                rows of the earlier experts of the same rank;
-//   k_moe_place  position = expert base + chunk prefix + rank in chunk.
+//                in entry order (each 64-entry step sorts its (expert, lane)
+//                keys across the wave, so runs of equal experts give the
+//                ranks; an LDS counter per expert carries over between
+//                steps), and the chunk's histogram;
+//   k_moe_prefix one workgroup per rank, one thread per expert: rows of
+//                expert e in the rank's earlier chunks, and the rank's
+//                total for e (the counts);
+//   k_moe_place  one workgroup per chunk: from the counts, the rows of each
+//                expert from earlier ranks and (a prefix sum over the
+//                experts) the rows of the earlier experts of the same rank;
+//                position = those + chunk prefix + rank in chunk.
 // Movement (HBM bound, one tile per token row):
 //   k_moe_dispatch  the token row is loaded once (16-byte vectors) and
 //                   stored once per valid choice (non-temporal);
@@ -35,44 +38,65 @@ namespace {
 __global__ __launch_bounds__(64) void k_moe_rank(const MoeRouteArgs a)
 {
     extern __shared__ int32_t cnt[];                  // [E]: rows so far in this chunk
+    constexpr int kSteps = kMoeChunk / 64;
     const int r = blockIdx.x / a.nch;
     const int ch = blockIdx.x - r * a.nch;
     const int lane = threadIdx.x;
     for (int e = lane; e < a.E; e += 64)
         cnt[e] = 0;
-    __syncthreads();
     const int64_t i0 = static_cast<int64_t>(ch) * kMoeChunk;
     const int64_t i1 = i0 + kMoeChunk < a.n ? i0 + kMoeChunk : a.n;
-    for (int64_t b = i0; b < i1; b += 64) {
-        const int64_t i = b + lane;
-        const int e = i < i1 ? a.ids[r][i] : -1;
+    // The chunk's ids, all loads in flight at once.
+    int ids[kSteps];
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+        const int64_t i = i0 + s * 64 + lane;
+        ids[s] = i < i1 ? a.ids[r][i] : -1;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+        const int64_t i = i0 + s * 64 + lane;
+        const int e = ids[s];
         const bool valid = i < i1 && e >= 0 && e < a.E;
-        // Lanes with the same expert: peel one id per round (the lowest
-        // pending lane's) until every valid lane has its group mask.
-        uint64_t todo = __ballot(valid);
-        uint64_t mine = 0;
-        while (todo != 0) {
-            const int leader = __builtin_ctzll(todo);
-            const int v = __builtin_amdgcn_readlane(e, leader);
-            const bool hit = valid && e == v;
-            const uint64_t m = __ballot(hit);
-            if (hit)
-                mine = m;
-            todo &= ~m;
+        // Sort the wave's (expert, lane) keys (bitonic, 21 compare-exchange
+        // stages across lanes); entries routed nowhere sort last. Sorted slot
+        // q then holds one entry, and equal experts form runs in lane order.
+        int key = ((valid ? e : a.E) << 6) | lane;
+#pragma unroll
+        for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+            for (int j = k >> 1; j > 0; j >>= 1) {
+                const int other = __shfl_xor(key, j);
+                const bool keep_min = ((lane & k) == 0) == ((lane & j) == 0);
+                key = keep_min ? min(key, other) : max(key, other);
+            }
         }
+        const int se = key >> 6;                      // expert in sorted slot `lane`
+        const bool sv = se < a.E;
+        // The run of slot `lane` starts at the largest run start at or below it.
+        const int prev = __shfl_up(se, 1);
+        int start = (lane == 0 || prev != se) ? lane : 0;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int o = __shfl_up(start, d);
+            if (lane >= d)
+                start = max(start, o);
+        }
+        const int next = __shfl_down(se, 1);
+        const bool run_end = lane == 63 || next != se;
         int32_t before = 0;
-        if (valid)
-            before = cnt[e];
-        // Every lane has read its counter before any lane writes one: the
+        if (sv)
+            before = cnt[se];
+        // Every slot has read its counter before any slot writes one: the
         // wave's LDS operations complete in program order.
-        if (valid) {
-            const uint64_t lower = lane == 0 ? 0 : (mine & ((~0ull) >> (64 - lane)));
-            a.pos[r][i] = before + __popcll(lower);
-            if ((mine >> lane) == 1)                  // the group's highest lane
-                cnt[e] = before + __popcll(mine);
-        } else if (i < i1) {
-            a.pos[r][i] = -1;
-        }
+        if (sv && run_end)
+            cnt[se] = before + (lane - start) + 1;
+        const int32_t rank_here = sv ? before + (lane - start) : -1;
+        // Send each slot's rank back to the lane its entry came from.
+        const int32_t mine = __builtin_amdgcn_ds_permute((key & 63) << 2, rank_here);
+        if (i < i1)
+            a.pos[r][i] = valid ? mine : -1;
     }
     __syncthreads();
     int32_t* part = a.partial + (static_cast<int64_t>(r) * a.nch + ch) * a.E;
@@ -80,58 +104,99 @@ __global__ __launch_bounds__(64) void k_moe_rank(const MoeRouteArgs a)
         part[e] = cnt[e];
 }
 
-__global__ __launch_bounds__(1024) void k_moe_scan(const MoeRouteArgs a)
+__global__ __launch_bounds__(1024) void k_moe_prefix(const MoeRouteArgs a)
 {
-    extern __shared__ int32_t incl[];                 // [E]: totals, then inclusive prefix
+    constexpr int kBatch = 16;                        // histogram loads in flight per thread
+    const int r = blockIdx.x;
     const int e = threadIdx.x;
-    int32_t tot = 0;
-    if (e < a.E) {
-        for (int r = 0; r < a.P; ++r) {
-            int32_t from_r = 0;
-            for (int ch = 0; ch < a.nch; ++ch) {
-                int32_t* q = a.partial + (static_cast<int64_t>(r) * a.nch + ch) * a.E + e;
-                const int32_t v = *q;
-                *q = tot;                             // rows of e before this chunk
-                tot += v;
-                from_r += v;
+    if (e >= a.E)
+        return;                                       // (no barrier in this kernel)
+    // Walk rank r's chunk histograms of expert e in order, replacing each by
+    // the rows of e in the rank's earlier chunks; loads go kBatch at a time.
+    int32_t* col = a.partial + static_cast<int64_t>(r) * a.nch * a.E + e;
+    int32_t run = 0;
+    for (int c0 = 0; c0 < a.nch; c0 += kBatch) {
+        int32_t v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            v[u] = c0 + u < a.nch ? col[static_cast<int64_t>(c0 + u) * a.E] : 0;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            if (c0 + u < a.nch) {
+                col[static_cast<int64_t>(c0 + u) * a.E] = run;
+                run += v[u];
             }
-            a.counts[static_cast<int64_t>(r) * a.E + e] = from_r;
         }
-        incl[e] = tot;
     }
-    __syncthreads();
-    for (int d = 1; d < a.E; d <<= 1) {               // Hillis-Steele over the experts
-        int32_t v = 0;
-        if (e < a.E && e >= d)
-            v = incl[e - d];
-        __syncthreads();
-        if (e < a.E && e >= d)
-            incl[e] += v;
-        __syncthreads();
-    }
-    if (e < a.E) {
-        const int first = (e / a.per) * a.per;        // the rank's first expert
-        const int32_t before_rank = first > 0 ? incl[first - 1] : 0;
-        a.base[e] = incl[e] - tot - before_rank;
-        if (e - first == a.per - 1)
-            a.recv[e / a.per] = static_cast<int64_t>(incl[e] - before_rank);
-    }
+    a.counts[static_cast<int64_t>(r) * a.E + e] = run;
 }
 
 __global__ __launch_bounds__(256) void k_moe_place(const MoeRouteArgs a)
 {
+    // LDS: [E] rows of each expert from earlier ranks, [E] inclusive prefix
+    // over the experts of each expert's total rows, [256] thread partials.
+    extern __shared__ int32_t lds[];
+    int32_t* cross = lds;
+    int32_t* incl = lds + a.E;
+    int32_t* part = lds + 2 * a.E;
     const int r = blockIdx.x / a.nch;
     const int ch = blockIdx.x - r * a.nch;
-    const int32_t* before = a.partial + (static_cast<int64_t>(r) * a.nch + ch) * a.E;
+    const int tid = threadIdx.x;
+    const int nthr = blockDim.x;                      // 256
+    for (int e = tid; e < a.E; e += nthr) {
+        int32_t before = 0, tot = 0;
+        for (int q = 0; q < a.P; ++q) {
+            const int32_t c = a.counts[static_cast<int64_t>(q) * a.E + e];
+            before += q < r ? c : 0;
+            tot += c;
+        }
+        cross[e] = before;
+        incl[e] = tot;
+    }
+    __syncthreads();
+    // Inclusive prefix of the totals over the experts: each thread scans m
+    // consecutive experts, the thread sums are scanned in LDS, then added.
+    const int m = (a.E + nthr - 1) / nthr;
+    int32_t run = 0;
+    for (int u = 0; u < m; ++u) {
+        const int e = tid * m + u;
+        if (e < a.E) {
+            run += incl[e];
+            incl[e] = run;
+        }
+    }
+    part[tid] = run;
+    __syncthreads();
+    for (int d = 1; d < nthr; d <<= 1) {
+        const int32_t v = tid >= d ? part[tid - d] : 0;
+        __syncthreads();
+        part[tid] += v;
+        __syncthreads();
+    }
+    const int32_t off = tid > 0 ? part[tid - 1] : 0;
+    for (int u = 0; u < m; ++u) {
+        const int e = tid * m + u;
+        if (e < a.E)
+            incl[e] += off;
+    }
+    __syncthreads();
+    // position = earlier experts of the rank + earlier ranks + earlier
+    // chunks of this rank + rank within the chunk
+    const int32_t* chunk_before = a.partial + (static_cast<int64_t>(r) * a.nch + ch) * a.E;
     const int64_t i0 = static_cast<int64_t>(ch) * kMoeChunk;
     const int64_t i1 = i0 + kMoeChunk < a.n ? i0 + kMoeChunk : a.n;
-    for (int64_t i = i0 + threadIdx.x; i < i1; i += blockDim.x) {
+    for (int64_t i = i0 + tid; i < i1; i += nthr) {
         const int32_t p = a.pos[r][i];
         if (p >= 0) {
             const int e = a.ids[r][i];
-            a.pos[r][i] = p + a.base[e] + before[e];
+            const int first = (e / a.per) * a.per;
+            const int32_t base = (e > 0 ? incl[e - 1] : 0) - (first > 0 ? incl[first - 1] : 0);
+            a.pos[r][i] = p + base + cross[e] + chunk_before[e];
         }
     }
+    if (blockIdx.x == 0)
+        for (int j = tid; j < a.P; j += nthr)
+            a.recv[j] = static_cast<int64_t>(incl[(j + 1) * a.per - 1] - (j > 0 ? incl[j * a.per - 1] : 0));
 }
 
 // Token (r, t) of tile `tile`.
@@ -141,12 +206,46 @@ __device__ __forceinline__ void token_of(const MoeMoveArgs& a, int64_t tile, int
     *t = tile - static_cast<int64_t>(*r) * a.T;
 }
 
-__device__ __forceinline__ bool entry_ok(const MoeMoveArgs& a, int e, int32_t p)
+// The k choices of token (r, t), read once: lane c of every wave loads
+// choice c, then readlane makes each choice's expert-side row address (or
+// nullptr for a dropped entry) and weight wave-uniform, so the row loops
+// below issue their 16-byte accesses with no metadata load in between.
+// KMAX >= k bounds the registers the choices take.
+template <int KMAX>
+struct Choices {
+    char* row[KMAX];
+    float w[KMAX];
+    uint32_t live;                    // bit c: choice c lands (valid id, position < cap)
+};
+
+template <int KMAX>
+__device__ __forceinline__ Choices<KMAX> token_choices(const MoeMoveArgs& a, int r, int64_t t,
+                                                       char* const* side, bool weights)
 {
-    return e >= 0 && e < a.E && p >= 0 && p < a.cap;
+    const int wl = threadIdx.x & 63;
+    int my_e = -1, my_p = -1;
+    float my_w = 0.0f;
+    if (wl < a.k) {
+        my_e = a.ids[r][t * a.k + wl];
+        my_p = a.pos[r][t * a.k + wl];
+        if (weights)
+            my_w = a.w[r][t * a.k + wl];
+    }
+    Choices<KMAX> ch;
+    ch.live = 0;
+#pragma unroll
+    for (int c = 0; c < KMAX; ++c) {
+        const int e = __builtin_amdgcn_readlane(my_e, c);
+        const int p = __builtin_amdgcn_readlane(my_p, c);
+        ch.w[c] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), c));
+        const bool ok = c < a.k && e >= 0 && e < a.E && p >= 0 && p < a.cap;
+        ch.row[c] = ok ? side[e / a.per] + static_cast<int64_t>(p) * a.row_bytes : nullptr;
+        ch.live |= ok ? (1u << c) : 0u;
+    }
+    return ch;
 }
 
-template <int U>
+template <int KMAX, int U>
 __global__ __launch_bounds__(256) void k_moe_dispatch(const MoeMoveArgs a)
 {
     const int lane = threadIdx.x;
@@ -157,8 +256,9 @@ __global__ __launch_bounds__(256) void k_moe_dispatch(const MoeMoveArgs a)
         int r;
         int64_t t;
         token_of(a, tile, &r, &t);
-        const int32_t* ids = a.ids[r] + t * a.k;
-        const int32_t* pos = a.pos[r] + t * a.k;
+        const Choices<KMAX> ch = token_choices<KMAX>(a, r, t, a.dst, false);
+        if (ch.live == 0)
+            continue;
         const char* src = a.src[r] + t * a.row_bytes;
         for (int64_t b0 = 0; b0 < a.row_bytes; b0 += step) {
             u32x4 x[U];
@@ -168,17 +268,15 @@ __global__ __launch_bounds__(256) void k_moe_dispatch(const MoeMoveArgs a)
                 if (o < a.row_bytes)
                     x[u] = ld16_stream(src + o);
             }
-            for (int c = 0; c < a.k; ++c) {
-                const int e = ids[c];
-                const int32_t p = pos[c];
-                if (!entry_ok(a, e, p))
-                    continue;
-                char* dst = a.dst[e / a.per] + static_cast<int64_t>(p) * a.row_bytes;
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int64_t o = b0 + static_cast<int64_t>(u * nthr + lane) * kVecBytes;
-                    if (o < a.row_bytes)
-                        st16(dst + o, x[u], nt);
+            for (int c = 0; c < KMAX; ++c) {
+                if ((ch.live >> c) & 1u) {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int64_t o = b0 + static_cast<int64_t>(u * nthr + lane) * kVecBytes;
+                        if (o < a.row_bytes)
+                            st16(ch.row[c] + o, x[u], nt);
+                    }
                 }
             }
         }
@@ -238,7 +336,7 @@ template <> struct FmaAcc<float> {
     }
 };
 
-template <typename T>
+template <typename T, int KMAX>
 __global__ __launch_bounds__(256) void k_moe_combine(const MoeMoveArgs a)
 {
     const int lane = threadIdx.x;
@@ -248,31 +346,23 @@ __global__ __launch_bounds__(256) void k_moe_combine(const MoeMoveArgs a)
         int r;
         int64_t t;
         token_of(a, tile, &r, &t);
-        const int32_t* ids = a.ids[r] + t * a.k;
-        const int32_t* pos = a.pos[r] + t * a.k;
-        const float* w = a.w[r] + t * a.k;
+        const Choices<KMAX> ch = token_choices<KMAX>(a, r, t, const_cast<char* const*>(a.src), true);
         char* dst = a.dst[r] + t * a.row_bytes;
-        for (int64_t o = static_cast<int64_t>(lane) * kVecBytes; o - lane * kVecBytes < a.row_bytes;
-             o += static_cast<int64_t>(nthr) * kVecBytes) {
+        for (int64_t b0 = 0; b0 < a.row_bytes; b0 += static_cast<int64_t>(nthr) * kVecBytes) {
+            const int64_t o = b0 + static_cast<int64_t>(lane) * kVecBytes;
             const bool in_row = o < a.row_bytes;
             // All of the token's rows for this slot in flight at once.
-            u32x4 y[kMoeMaxTopk];
+            u32x4 y[KMAX];
 #pragma unroll
-            for (int c = 0; c < kMoeMaxTopk; ++c) {
-                if (c < a.k) {
-                    const int e = ids[c];
-                    const int32_t p = pos[c];
-                    if (entry_ok(a, e, p) && in_row)
-                        y[c] = ld16_stream(a.src[e / a.per] + static_cast<int64_t>(p) * a.row_bytes + o);
-                }
-            }
+            for (int c = 0; c < KMAX; ++c)
+                if (((ch.live >> c) & 1u) && in_row)
+                    y[c] = ld16_stream(ch.row[c] + o);
             FmaAcc<T> acc;
             acc.zero();
 #pragma unroll
-            for (int c = 0; c < kMoeMaxTopk; ++c) {
-                if (c < a.k && entry_ok(a, ids[c], pos[c]))
-                    acc.fma(w[c], y[c]);
-            }
+            for (int c = 0; c < KMAX; ++c)
+                if ((ch.live >> c) & 1u)
+                    acc.fma(ch.w[c], y[c]);
             if (in_row)
                 st16(dst + o, acc.pack(), nt);
         }
@@ -288,16 +378,15 @@ hipError_t launch_moe_route(const MoeRoutePlan& p, hipStream_t stream)
         p.scan_threads < a.E || p.scan_threads > 1024 || p.scan_threads % 64 != 0)
         return hipErrorInvalidValue;
     const unsigned nb = static_cast<unsigned>(a.P) * static_cast<unsigned>(a.nch);
-    const size_t lds = static_cast<size_t>(a.E) * sizeof(int32_t);
-    k_moe_rank<<<dim3(nb), dim3(64), lds, stream>>>(a);
+    k_moe_rank<<<dim3(nb), dim3(64), static_cast<size_t>(a.E) * sizeof(int32_t), stream>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    k_moe_scan<<<dim3(1), dim3(p.scan_threads), lds, stream>>>(a);
+    k_moe_prefix<<<dim3(a.P), dim3(p.scan_threads), 0, stream>>>(a);
     e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    k_moe_place<<<dim3(nb), dim3(256), 0, stream>>>(a);
+    k_moe_place<<<dim3(nb), dim3(256), static_cast<size_t>(2 * a.E + 256) * sizeof(int32_t), stream>>>(a);
     return hipGetLastError();
 }
 
@@ -309,15 +398,29 @@ hipError_t launch_moe_move(const MoeMovePlan& p, bool combine, hipStream_t strea
     if (p.grid < 1 || a.k < 1 || a.k > kMoeMaxTopk || a.per < 1 || a.row_bytes % kVecBytes != 0)
         return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>(p.grid)), block(256);
+    const int kmax = a.k <= 2 ? 2 : a.k <= 4 ? 4 : a.k <= 8 ? 8 : 16;
     if (combine) {
-        if (a.dtype == DT_BF16)
-            k_moe_combine<uint16_t><<<grid, block, 0, stream>>>(a);
-        else
-            k_moe_combine<float><<<grid, block, 0, stream>>>(a);
+        const bool bf = a.dtype == DT_BF16;
+        switch (kmax) {
+#define ATOM_MOE_COMBINE(KM)                                                         \
+    case KM:                                                                         \
+        if (bf)                                                                      \
+            k_moe_combine<uint16_t, KM><<<grid, block, 0, stream>>>(a);             \
+        else                                                                         \
+            k_moe_combine<float, KM><<<grid, block, 0, stream>>>(a);                \
+        break;
+        ATOM_MOE_COMBINE(2) ATOM_MOE_COMBINE(4) ATOM_MOE_COMBINE(8) ATOM_MOE_COMBINE(16)
+#undef ATOM_MOE_COMBINE
+        }
     } else {
         if (p.U != 4)
             return hipErrorInvalidValue;
-        k_moe_dispatch<4><<<grid, block, 0, stream>>>(a);
+        switch (kmax) {
+        case 2: k_moe_dispatch<2, 4><<<grid, block, 0, stream>>>(a); break;
+        case 4: k_moe_dispatch<4, 4><<<grid, block, 0, stream>>>(a); break;
+        case 8: k_moe_dispatch<8, 4><<<grid, block, 0, stream>>>(a); break;
+        default: k_moe_dispatch<16, 4><<<grid, block, 0, stream>>>(a); break;
+        }
     }
     return hipGetLastError();
 }

@@ -101,9 +101,9 @@ struct SnacArgs {
     int32_t pad_;
 };
 
-// Expert-parallel MoE routing (three kernels: rank within chunks, scan,
-// place). Entries i = t*k + c of rank r are cut into chunks of kMoeChunk.
-constexpr int kMoeChunk = 1024;        // entries one wave ranks in order
+// Expert-parallel MoE routing (three kernels: rank within chunks, per-rank
+// prefix, place). Entries i = t*k + c of rank r are cut into chunks of kMoeChunk.
+constexpr int kMoeChunk = 256;         // entries one wave ranks in order
 constexpr int kMoeMaxTopk = 16;
 
 struct MoeRouteArgs {
@@ -112,9 +112,8 @@ struct MoeRouteArgs {
     int32_t* counts;                   // [P][E] rows rank r sends to expert e
     int64_t* recv;                     // [P] rows rank j receives
     int32_t* partial;                  // [P][nch][E]: chunk histograms, then
-                                       // rows of expert e before the chunk
-    int32_t* base;                     // [E]: rows of the earlier experts of
-                                       // the same rank
+                                       // rows of expert e in the rank's
+                                       // earlier chunks
     int64_t n;                         // entries per rank (T*k)
     int32_t nch;                       // chunks per rank (at least 1)
     int32_t P;

@@ -688,7 +688,7 @@ int64_t moe_scratch_bytes(int32_t P, int32_t E, int32_t k, int64_t T)
     if (P < 1 || P > kMaxRanks || E < P || E > ATOM_MOE_MAX_EXPERTS || E % P != 0 || k < 1 ||
         k > kMoeMaxTopk || T < 0 || T > ATOM_MOE_MAX_ENTRIES || T * k > ATOM_MOE_MAX_ENTRIES)
         return 0;
-    const int64_t ints = static_cast<int64_t>(P) * moe_chunks(T * k) * E + E;
+    const int64_t ints = static_cast<int64_t>(P) * moe_chunks(T * k) * E;
     return ceil_div(ints * 4, 256) * 256;
 }
 
@@ -731,7 +731,6 @@ atom_status plan_moe_route(const atom_moe_routing* rt, MoeRoutePlan* p)
     a.E = E;
     a.per = E / P;
     a.partial = static_cast<int32_t*>(rt->scratch);
-    a.base = a.partial + static_cast<int64_t>(P) * a.nch * E;
     p->scan_threads = static_cast<int32_t>(ceil_div(E, 64) * 64);
     return ATOM_OK;
 }

@@ -54,7 +54,7 @@ constexpr int64_t kDefaultWaitUs = 1000000;          // one SNAC wait: 1 s
 // MoE routing and movement plans.
 struct MoeRoutePlan {
     MoeRouteArgs a;
-    int32_t scan_threads = 64;         // one workgroup, one thread per expert
+    int32_t scan_threads = 64;         // prefix workgroup: one thread per expert
 };
 
 struct MoeMovePlan {

@@ -2,7 +2,7 @@
 parallelism) against the CPU oracle, through the C ABI.
 
 * Route: positions, counts and rows received, bit-exact, over shapes that
-  cover one and many 1024-entry chunks with ragged tails, invalid ids,
+  cover one and many 256-entry chunks with ragged tails, invalid ids,
   repeated ids, one rank, one expert per rank, 1024 experts, k = 1 and 16,
   and no tokens at all.
 * Dispatch: every output row against the oracle (rows no entry lands on keep
@@ -80,12 +80,12 @@ def check_route(rt, ids, E, k, what):
 
 ROUTE_CASES = [  # (seed, P, T, E, k, invalid, dup)
     (1, 8, 512, 256, 8, 0.0, 0.0),
-    (2, 8, 700, 64, 3, 0.05, 0.0),      # 2100 entries: 3 chunks, ragged tail
+    (2, 8, 700, 64, 3, 0.05, 0.0),      # 2100 entries: 9 chunks, ragged tail
     (3, 4, 37, 8, 4, 0.0, 0.3),         # repeated ids within a token
     (4, 1, 300, 16, 2, 0.1, 0.0),       # one rank
     (5, 8, 129, 8, 1, 0.0, 0.0),        # one expert per rank, k = 1
     (6, 16, 64, 1024, 16, 0.02, 0.0),   # 1024 experts, k = 16, 16 ranks
-    (7, 3, 5000, 24, 5, 0.0, 0.0),      # 25000 entries: 25 chunks
+    (7, 3, 5000, 24, 5, 0.0, 0.0),      # 25000 entries: 98 chunks
     (8, 8, 0, 64, 4, 0.0, 0.0),         # no tokens
     (9, 2, 1, 2, 2, 0.0, 0.0),          # one token
 ]
@@ -182,7 +182,7 @@ def test_moe_workload_full(A):
 
 
 def test_moe_many_tokens_sampled(A):
-    """4096 tokens per rank (32768 entries: 32 chunks), 1024-wide rows:
+    """4096 tokens per rank (32768 entries: 128 chunks), 1024-wide rows:
     route in full, dispatch checked on every row against its token."""
     import torch
     P, T, E, k, H = 8, 4096, 256, 8, 1024

@@ -38,9 +38,10 @@ def test_routing_struct_matches_the_header(tmp_path):
 
 
 def test_scratch_bytes():
-    # P * chunks * E + E int32, rounded up to 256 bytes; chunks of 1024 entries
-    assert A.atom_moe_scratch_bytes(8, 256, 8, 512) == ((8 * 4 * 256 + 256) * 4 + 255) // 256 * 256
-    assert A.atom_moe_scratch_bytes(8, 256, 8, 0) == ((8 * 1 * 256 + 256) * 4 + 255) // 256 * 256
+    # P * chunks * E int32, rounded up to 256 bytes; chunks of 256 entries
+    assert A.atom_moe_scratch_bytes(8, 256, 8, 512) == 8 * 16 * 256 * 4
+    assert A.atom_moe_scratch_bytes(8, 256, 8, 0) == 8 * 1 * 256 * 4
+    assert A.atom_moe_scratch_bytes(3, 9, 1, 1) == 256
     assert A.atom_moe_scratch_bytes(4, 4, 1, 1) > 0
     for bad in [(0, 8, 2, 4), (17, 32, 2, 4), (8, 250, 8, 4), (8, 4, 2, 4), (8, 2048, 2, 4),
                 (8, 64, 0, 4), (8, 64, 17, 4), (8, 64, 2, -1), (8, 64, 2, (1 << 19) + 1)]:
