@@ -151,6 +151,72 @@ int main(int argc, char** argv)
                 ATOM_OK && p.exec == EX_REDUCE)
             check_reduce(p, iter);
     }
+    // MoE routing and movement plans
+    int ok_moe = 0;
+    for (int iter = 0; iter < iters / 4; ++iter) {
+        const bool sane = pick(0, 9) < 7;
+        const int P = static_cast<int>(sane ? pick(1, 16) : pick(-1, 18));
+        const int per = static_cast<int>(pick(1, 64));
+        const int E = sane ? P * per : static_cast<int>(pick(-1, 1100));
+        const int k = static_cast<int>(sane ? pick(1, 16) : pick(-1, 18));
+        const int64_t T = sane ? pick(0, 3000) : pick(-2, (1 << 21));
+        void* ids[kMaxRanks + 2];
+        void* pos[kMaxRanks + 2];
+        void* xs[kMaxRanks + 2];
+        void* outs[kMaxRanks + 2];
+        void* ws[kMaxRanks + 2];
+        const uint64_t stride = 1ull << 36;
+        const int mis = pick(0, 9) == 0 ? static_cast<int>(pick(1, 15)) : 0;
+        for (int r = 0; r < kMaxRanks + 2; ++r) {
+            ids[r] = reinterpret_cast<void*>(0x600000000000ull + r * stride);
+            pos[r] = reinterpret_cast<void*>(0x610000000000ull + r * stride);
+            xs[r] = reinterpret_cast<void*>(0x620000000000ull + r * stride + (r == 0 ? mis : 0));
+            outs[r] = reinterpret_cast<void*>(0x630000000000ull + r * stride);
+            ws[r] = reinterpret_cast<void*>(0x640000000000ull + r * stride);
+        }
+        atom_moe_routing rt{};
+        rt.nranks = P;
+        rt.num_experts = E;
+        rt.topk = k;
+        rt.reserved = pick(0, 19) == 0 ? 1 : 0;
+        rt.tokens = T;
+        rt.expert_ids = reinterpret_cast<const int32_t* const*>(ids);
+        rt.positions = reinterpret_cast<int32_t* const*>(pos);
+        rt.counts = reinterpret_cast<int32_t*>(0x650000000000ull);
+        rt.recv_rows = reinterpret_cast<int64_t*>(0x660000000000ull);
+        rt.scratch = reinterpret_cast<void*>(0x670000000000ull + (pick(0, 19) == 0 ? 4 : 0));
+        MoeRoutePlan rp;
+        if (plan_moe_route(&rt, &rp) == ATOM_OK) {
+            ++ok_moe;
+            const int64_t n = T * k;
+            check(rp.a.nch >= 1 && static_cast<int64_t>(rp.a.nch) * kMoeChunk >= n &&
+                      (n == 0 || static_cast<int64_t>(rp.a.nch - 1) * kMoeChunk < n),
+                  "moe chunks", iter);
+            check(rp.scan_threads >= E && rp.scan_threads <= 1024 && rp.scan_threads % 64 == 0,
+                  "moe scan threads", iter);
+            check(moe_scratch_bytes(P, E, k, T) >= static_cast<int64_t>(P) * rp.a.nch * E * 4,
+                  "moe scratch", iter);
+            check(rp.a.per * P == E, "moe experts per rank", iter);
+        }
+        const int64_t cap = pick(0, 9) == 0 ? pick(-1, 3) : pick(0, 40000);
+        const int64_t row = pick(0, 9) == 0 ? pick(-1, 9) : 8 * pick(1, 1024);
+        const atom_dtype dt = static_cast<atom_dtype>(pick(0, 9) == 0 ? pick(-1, 2) : pick(0, 1));
+        for (int combine = 0; combine < 2; ++combine) {
+            MoeMovePlan mp;
+            if (plan_moe_move(&rt, combine != 0, xs, reinterpret_cast<const float* const*>(ws), outs,
+                              cap, row, dt, &mp) != ATOM_OK)
+                continue;
+            ++ok_moe;
+            check(mp.a.ntiles == static_cast<int64_t>(P) * T, "moe tiles", iter);
+            check(mp.a.ntiles == 0 || (mp.grid >= 1 && mp.grid <= mp.a.ntiles), "moe grid", iter);
+            check(mp.a.ntiles == 0 || mp.a.row_bytes % kVecBytes == 0, "moe row alignment", iter);
+            check(mp.a.k == k && mp.a.per * P == E, "moe shape", iter);
+            check(mp.credited_bytes ==
+                      mp.a.ntiles * ((k + 1) * mp.a.row_bytes + k * (combine ? 12 : 8)),
+                  "moe credited bytes", iter);
+        }
+    }
+    std::printf("%d MoE plans validated\n", ok_moe);
     std::printf("%d plans validated, %d failures\n", ok_plans, fails);
     return fails ? 1 : 0;
 }
