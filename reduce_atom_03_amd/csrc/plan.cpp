@@ -323,7 +323,7 @@ atom_status plan_copy(void* dst, const void* src, size_t bytes, const atom_confi
         return ATOM_ERR_INVALID_ARG;
     if (c.flags & ATOM_F_STAGED)
         return ATOM_ERR_UNSUPPORTED;
-    *p = Plan();
+    p->reset();
     p->kind = ATOM_COLL_NONE;
     p->P = 1;
     uintptr_t bits = reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src) |
@@ -374,7 +374,7 @@ atom_status plan_reduce(void* dst, const void* const* srcs, int32_t nsrcs, int64
     Range ro = range_of(dst, bytes);
     if (!disjoint(ins, nsrcs, &ro, 1))
         return ATOM_ERR_INVALID_ARG;
-    *p = Plan();
+    p->reset();
     p->kind = ATOM_COLL_NONE;
     p->dtype = dtype == ATOM_DT_BF16 ? DT_BF16 : DT_F32;
     p->esize = es;
@@ -531,7 +531,7 @@ atom_status plan_collective(const atom_layout* in, const atom_layout* out, atom_
     if (staged && kind != ATOM_COLL_ALL_GATHER && kind != ATOM_COLL_ALL_REDUCE)
         return ATOM_ERR_UNSUPPORTED;
 
-    *p = Plan();
+    p->reset();
     p->kind = kind;
     p->dtype = in->dtype == ATOM_DT_BF16 ? DT_BF16 : DT_F32;
     p->esize = es;

@@ -16,7 +16,10 @@ enum Exec : int32_t {
     EX_SNAC_AR = 4    // SNAC composed AllReduce (ReduceArgs for RS + SnacArgs)
 };
 
-struct Plan {
+// The scalar part of a plan. Planning resets only this part (and the
+// output sizes); the one argument block a plan uses is filled by its
+// builder, so a call never clears the kilobytes of the other blocks.
+struct PlanHead {
     atom_collective_kind kind = ATOM_COLL_NONE;
     Exec exec = EX_NONE;
     int32_t dtype = DT_BF16;
@@ -27,15 +30,25 @@ struct Plan {
     int32_t wg = 256;         // threads per workgroup
     int64_t grid = 0;         // workgroups launched
     int64_t credited_bytes = 0;
-    int64_t out_elems[kMaxRanks] = {};
     int64_t in_elems = 0;
     // SNAC
     int32_t slots = 0;
     int64_t chunk_bytes = 0;
     int64_t ring_bytes = 0;
-    ReduceArgs ra;
-    CopyArgs ca;
-    SnacArgs sa;
+};
+
+struct Plan : PlanHead {
+    int64_t out_elems[kMaxRanks] = {};
+    ReduceArgs ra;            // exec == EX_REDUCE
+    CopyArgs ca;              // exec == EX_COPY
+    SnacArgs sa;              // exec == EX_SNAC_AG / EX_SNAC_AR
+
+    void reset()
+    {
+        static_cast<PlanHead&>(*this) = PlanHead();
+        for (int64_t& e : out_elems)
+            e = 0;
+    }
 };
 
 // Defaults and limits.
