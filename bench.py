@@ -256,6 +256,28 @@ def main():
         b.record(stream)
     torch.cuda.synchronize()
     floor = np.array([a.elapsed_time(b) * 1e3 for a, b in pairs])
+    # The same AllGather captured 100 times into one HIP graph: the per-call
+    # cost once launch overhead is amortized (a serving loop's view).
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(100):
+                ag8()
+    stream.wait_stream(side)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    gl = []
+    for _ in range(20):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        b.synchronize()
+        gl.append(a.elapsed_time(b) * 1e3 / 100)
+    graph_us = float(np.median(gl))
     # Host-side time per call of the same launch (submission cost).
     t = time.perf_counter()
     for _ in range(args.lat_iters):
@@ -307,6 +329,7 @@ def main():
         "p50_us_8KiB": round(float(np.percentile(lat, 50)), 2),
         "p99_us_8KiB": round(float(np.percentile(lat, 99)), 2),
         "host_us_per_call_8KiB": round(host_us, 2),
+        "graph_us_per_call_8KiB": round(graph_us, 2),
         "p50_us_launch_floor_16B_copy": round(float(np.percentile(floor, 50)), 2),
         "cus_used": cus,
         "rows": per_row,

@@ -1,0 +1,151 @@
+"""The C ABI under HIP graph capture.
+
+Every launch of libatom is a kernel on the caller's stream (no memset, no
+host synchronization; the SNAC counters are cleared by a kernel), so a
+sequence of calls can be captured once and replayed. One graph holds a
+decode AllReduce, a zero-staging and a SNAC AllGather, a ReduceScatter, an
+AllToAllV and a MoE route, dispatch and combine; it is replayed several
+times with new inputs written eagerly between replays (and other eager
+work), and every replay is checked against the oracle on those inputs.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from reduce_atom_03_amd import synth
+from tests._helpers import assert_bits_equal
+from tests.gpu_util import from_dev, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def A():
+    require_gpu()
+    from reduce_atom_03_amd import atom
+    return atom
+
+
+def _bits_to_dev(torch, a, out):
+    out.copy_(torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16))
+
+
+def test_captured_sequence_replays_match_the_oracle(A):
+    import torch
+    dev = torch.device("cuda:0")
+    P = 8
+    bf = torch.bfloat16
+
+    def buf(n):
+        return torch.zeros(n, dtype=bf, device=dev)
+
+    # shapes
+    n_dec = 4 * 896                      # decode AllReduce, b = 4
+    S_ag = 64 << 10                      # AllGather partitions of 64 KiB
+    n_rs = 3 * 4099                      # ReduceScatter, ragged partitions
+    C = synth.random_counts(11, P, 6)    # AllToAllV counts, rows of 128
+    H, T, E, k = 256, 24, 32, 4          # MoE
+    x_dec = [buf(P * n_dec) for _ in range(P)]
+    o_dec = [buf(P * n_dec) for _ in range(P)]
+    z_ag = [buf(S_ag // 2) for _ in range(P)]
+    o_ag = [buf(P * S_ag // 2) for _ in range(P)]
+    o_sn = [buf(P * S_ag // 2) for _ in range(P)]
+    x_rs = [buf(P * n_rs) for _ in range(P)]
+    y_rs = [buf(n_rs) for _ in range(P)]
+    rows = C.sum(axis=1)
+    R = C.sum(axis=0)
+    x_a2 = [buf(max(int(rows[r]), 1) * 128) for r in range(P)]
+    o_a2 = [buf(max(int(R[j]), 1) * 128) for j in range(P)]
+    ids_dev = [torch.zeros(T * k, dtype=torch.int32, device=dev) for _ in range(P)]
+    w_dev = [torch.zeros(T * k, dtype=torch.float32, device=dev) for _ in range(P)]
+    x_moe = [buf(T * H) for _ in range(P)]
+    cap = P * T * k                      # every entry fits
+    d_moe = [buf(cap * H) for _ in range(P)]
+    o_moe = [buf(T * H) for _ in range(P)]
+    rt = A.moe_alloc_routing(ids_dev, E, k)
+    snac = A.config(flags=A.F_STAGED, chunk_bytes=64 << 10, ring_slots=2)
+    L = A.layout
+    lay = {
+        "dec": (L(A.PARTITIONED, x_dec, n_dec), L(A.GATHERED, o_dec, n_dec), A.OP_SUM, None),
+        "ag": (L(A.SHARD, z_ag, S_ag // 2), L(A.GATHERED, o_ag, S_ag // 2), A.OP_COPY, None),
+        "snac": (L(A.SHARD, z_ag, S_ag // 2), L(A.GATHERED, o_sn, S_ag // 2), A.OP_COPY, snac),
+        "rs": (L(A.PARTITIONED, x_rs, n_rs), L(A.SHARD, y_rs, n_rs), A.OP_SUM, None),
+        "a2": (L(A.PARTITIONED, x_a2, 0, C, 128), L(A.TRANSPOSED, o_a2, 0, None, 128), A.OP_COPY,
+               None),
+    }
+
+    def sequence():
+        for li, lo, op, cfg in lay.values():
+            A.atom_collective(li, lo, op, cfg)
+        A.atom_moe_route(rt)
+        A.atom_moe_dispatch(rt, x_moe, d_moe, cap, H)
+        A.atom_moe_combine(rt, d_moe, w_dev, o_moe, cap, H)
+
+    def load_inputs(seed):
+        """New inputs (host arrays) written into the captured buffers."""
+        inp = {
+            "dec": [synth.draw(seed, r, P * n_dec, "normal", synth.BF16, 0.02) for r in range(P)],
+            "ag": synth.ranks(seed + 1, P, S_ag // 2, "uniform", synth.BF16),
+            "rs": [synth.mixed_bits(seed + 2, r, P * n_rs, synth.BF16, specials=False)
+                   for r in range(P)],
+            "a2": synth.tagged_rows(P, [int(t) for t in rows], 128, seed=seed + 3),
+            "moe_x": [synth.draw(seed + 4, r, T * H, "normal", synth.BF16) for r in range(P)],
+        }
+        inp["moe_ids"], inp["moe_w"] = synth.moe_routing(seed + 5, P, T, E, k)
+        for r in range(P):
+            _bits_to_dev(torch, inp["dec"][r], x_dec[r])
+            _bits_to_dev(torch, inp["ag"][r], z_ag[r])
+            _bits_to_dev(torch, inp["rs"][r], x_rs[r])
+            if rows[r]:
+                _bits_to_dev(torch, inp["a2"][r], x_a2[r][:int(rows[r]) * 128])
+            _bits_to_dev(torch, inp["moe_x"][r], x_moe[r])
+            ids_dev[r].copy_(torch.from_numpy(inp["moe_ids"][r]))
+            w_dev[r].copy_(torch.from_numpy(inp["moe_w"][r]))
+        return inp
+
+    def check(inp, what):
+        torch.cuda.synchronize()
+        want = oracle.all_reduce(inp["dec"])
+        for j in range(P):
+            assert_bits_equal(from_dev(o_dec[j]), want[j], f"{what}: decode AllReduce {j}")
+        want = oracle.all_gather(inp["ag"])
+        for j in range(P):
+            assert_bits_equal(from_dev(o_ag[j]), want[j], f"{what}: AllGather {j}")
+            assert_bits_equal(from_dev(o_sn[j]), want[j], f"{what}: SNAC AllGather {j}")
+        want = oracle.reduce_scatter(inp["rs"])
+        for k_ in range(P):
+            assert_bits_equal(from_dev(y_rs[k_]), want[k_], f"{what}: ReduceScatter {k_}")
+        want = oracle.all_to_all_v(inp["a2"], C, 128)
+        for j in range(P):
+            assert_bits_equal(from_dev(o_a2[j])[:int(R[j]) * 128], want[j], f"{what}: AllToAllV {j}")
+        pos, _, recv = oracle.moe_route(inp["moe_ids"], E, k)
+        disp = oracle.moe_dispatch(inp["moe_x"], inp["moe_ids"], pos, E, k, H, cap)
+        want = oracle.moe_combine(disp, inp["moe_ids"], pos, inp["moe_w"], E, k, H, cap)
+        for r in range(P):
+            assert_bits_equal(from_dev(o_moe[r]), want[r], f"{what}: MoE combine {r}")
+        assert A.atom_sync_status() == A.OK
+
+    # eager run first: allocates the SNAC workspace outside the capture
+    say("graph: eager run")
+    inp = load_inputs(100)
+    sequence()
+    check(inp, "eager")
+
+    say("graph: capture")
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            sequence()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    for rep, seed in enumerate((200, 300, 400)):
+        say(f"graph: replay {rep}")
+        inp = load_inputs(seed)
+        junk = torch.randn(1 << 20, device=dev).sum()       # unrelated eager work
+        g.replay()
+        check(inp, f"replay {rep}")
+        del junk
