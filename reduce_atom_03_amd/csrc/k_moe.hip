@@ -18,10 +18,11 @@
 //   k_moe_prefix one workgroup per rank, one thread per expert: rows of
 //                expert e in the rank's earlier chunks, and the rank's
 //                total for e (the counts);
-//   k_moe_place  one workgroup per chunk: from the counts, the rows of each
-//                expert from earlier ranks and (a prefix sum over the
-//                experts) the rows of the earlier experts of the same rank;
-//                position = those + chunk prefix + rank in chunk.
+//   k_moe_place  one workgroup per rank and group of chunks (at most ~1024
+//                in all): from the counts, the rows of each expert from
+//                earlier ranks and (a prefix sum over the experts) the rows
+//                of the earlier experts of the same rank, built once per
+//                workgroup; position = those + chunk prefix + rank in chunk.
 // Movement (HBM bound, one tile per token row):
 //   k_moe_dispatch  the token row is loaded once (16-byte vectors) and
 //                   stored once per valid choice (non-temporal);
@@ -139,8 +140,8 @@ __global__ __launch_bounds__(256) void k_moe_place(const MoeRouteArgs a)
     int32_t* cross = lds;
     int32_t* incl = lds + a.E;
     int32_t* part = lds + 2 * a.E;
-    const int r = blockIdx.x / a.nch;
-    const int ch = blockIdx.x - r * a.nch;
+    const int r = blockIdx.x / a.groups;              // rank; chunks g, g + groups, ...
+    const int g = blockIdx.x - r * a.groups;
     const int tid = threadIdx.x;
     const int nthr = blockDim.x;                      // 256
     for (int e = tid; e < a.E; e += nthr) {
@@ -182,16 +183,18 @@ __global__ __launch_bounds__(256) void k_moe_place(const MoeRouteArgs a)
     __syncthreads();
     // position = earlier experts of the rank + earlier ranks + earlier
     // chunks of this rank + rank within the chunk
-    const int32_t* chunk_before = a.partial + (static_cast<int64_t>(r) * a.nch + ch) * a.E;
-    const int64_t i0 = static_cast<int64_t>(ch) * kMoeChunk;
-    const int64_t i1 = i0 + kMoeChunk < a.n ? i0 + kMoeChunk : a.n;
-    for (int64_t i = i0 + tid; i < i1; i += nthr) {
-        const int32_t p = a.pos[r][i];
-        if (p >= 0) {
-            const int e = a.ids[r][i];
-            const int first = (e / a.per) * a.per;
-            const int32_t base = (e > 0 ? incl[e - 1] : 0) - (first > 0 ? incl[first - 1] : 0);
-            a.pos[r][i] = p + base + cross[e] + chunk_before[e];
+    for (int ch = g; ch < a.nch; ch += a.groups) {
+        const int32_t* chunk_before = a.partial + (static_cast<int64_t>(r) * a.nch + ch) * a.E;
+        const int64_t i0 = static_cast<int64_t>(ch) * kMoeChunk;
+        const int64_t i1 = i0 + kMoeChunk < a.n ? i0 + kMoeChunk : a.n;
+        for (int64_t i = i0 + tid; i < i1; i += nthr) {
+            const int32_t p = a.pos[r][i];
+            if (p >= 0) {
+                const int e = a.ids[r][i];
+                const int first = (e / a.per) * a.per;
+                const int32_t base = (e > 0 ? incl[e - 1] : 0) - (first > 0 ? incl[first - 1] : 0);
+                a.pos[r][i] = p + base + cross[e] + chunk_before[e];
+            }
         }
     }
     if (blockIdx.x == 0)
@@ -375,7 +378,8 @@ hipError_t launch_moe_route(const MoeRoutePlan& p, hipStream_t stream)
 {
     const MoeRouteArgs& a = p.a;
     if (a.P < 1 || a.P > kMaxRanks || a.E < 1 || a.E > 1024 || a.nch < 1 || a.per < 1 ||
-        p.scan_threads < a.E || p.scan_threads > 1024 || p.scan_threads % 64 != 0)
+        a.groups < 1 || a.groups > a.nch || p.scan_threads < a.E || p.scan_threads > 1024 ||
+        p.scan_threads % 64 != 0)
         return hipErrorInvalidValue;
     const unsigned nb = static_cast<unsigned>(a.P) * static_cast<unsigned>(a.nch);
     k_moe_rank<<<dim3(nb), dim3(64), static_cast<size_t>(a.E) * sizeof(int32_t), stream>>>(a);
@@ -386,7 +390,8 @@ hipError_t launch_moe_route(const MoeRoutePlan& p, hipStream_t stream)
     e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    k_moe_place<<<dim3(nb), dim3(256), static_cast<size_t>(2 * a.E + 256) * sizeof(int32_t), stream>>>(a);
+    const unsigned np = static_cast<unsigned>(a.P) * static_cast<unsigned>(a.groups);
+    k_moe_place<<<dim3(np), dim3(256), static_cast<size_t>(2 * a.E + 256) * sizeof(int32_t), stream>>>(a);
     return hipGetLastError();
 }
 

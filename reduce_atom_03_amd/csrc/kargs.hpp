@@ -116,6 +116,7 @@ struct MoeRouteArgs {
                                        // earlier chunks
     int64_t n;                         // entries per rank (T*k)
     int32_t nch;                       // chunks per rank (at least 1)
+    int32_t groups;                    // placing workgroups per rank (<= nch)
     int32_t P;
     int32_t E;
     int32_t per;                       // experts per rank

@@ -730,6 +730,9 @@ atom_status plan_moe_route(const atom_moe_routing* rt, MoeRoutePlan* p)
     a.recv = rt->recv_rows;
     a.n = n;
     a.nch = moe_chunks(n);
+    // Each placing workgroup rebuilds the per-expert offsets (E x P counts)
+    // once, so the placing grid is bounded (~1024) and strides over chunks.
+    a.groups = std::max(1, std::min(a.nch, 1024 / P));
     a.P = P;
     a.E = E;
     a.per = E / P;

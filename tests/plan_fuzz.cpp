@@ -197,6 +197,8 @@ int main(int argc, char** argv)
             check(moe_scratch_bytes(P, E, k, T) >= static_cast<int64_t>(P) * rp.a.nch * E * 4,
                   "moe scratch", iter);
             check(rp.a.per * P == E, "moe experts per rank", iter);
+            check(rp.a.groups >= 1 && rp.a.groups <= rp.a.nch && rp.a.groups * P <= 1024,
+                  "moe placing groups", iter);
         }
         const int64_t cap = pick(0, 9) == 0 ? pick(-1, 3) : pick(0, 40000);
         const int64_t row = pick(0, 9) == 0 ? pick(-1, 9) : 8 * pick(1, 1024);

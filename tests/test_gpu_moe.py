@@ -210,3 +210,57 @@ def test_moe_many_tokens_sampled(A):
         rows = all_rows[src_r[:int(recv[j])], src_t[:int(recv[j])]]
         assert_bits_equal(o[:int(recv[j])], rows, f"rank {j}")
         assert (o[int(recv[j]):] == 0xFFFF).all()
+
+
+def test_moe_maximum_entries_by_properties(A):
+    """The largest routing the ABI takes: 16 ranks x 65536 tokens x top-16
+    (2**20 entries per rank) over 1024 experts. The oracle's loops are too
+    slow here, so the layout is checked by what defines it, vectorized: per
+    destination rank the positions are a permutation of 0..recv-1 whose
+    order is (expert, source rank, entry); counts are the histogram of the
+    ids; and every dispatched 16-byte row carries its own (rank, token)."""
+    import torch
+    P, T, E, k, H = 16, 65536, 1024, 16, 8
+    say("moe maximum: 16 ranks x 65536 tokens x top-16, E=1024")
+    g = np.random.default_rng(77)
+    ids = [g.integers(0, E, size=T * k, dtype=np.int64).astype(np.int32) for _ in range(P)]
+    ids[3][::997] = -5                                  # some entries route nowhere
+    rt, _ = route_dev(A, ids, E, k)
+    torch.cuda.synchronize()
+    pos = [rt.positions_t[r].cpu().numpy() for r in range(P)]
+    cnt = rt.counts_t.cpu().numpy().reshape(P, E)
+    recv = rt.recv_t.cpu().numpy()
+    per = E // P
+    for r in range(P):
+        valid = (ids[r] >= 0) & (ids[r] < E)
+        assert (pos[r][~valid] == -1).all()
+        np.testing.assert_array_equal(cnt[r], np.bincount(ids[r][valid], minlength=E))
+    ent = np.arange(T * k, dtype=np.int64)
+    for j in range(P):
+        e_all, key_all, p_all = [], [], []
+        for r in range(P):
+            sel = (ids[r] >= j * per) & (ids[r] < (j + 1) * per)
+            e = ids[r][sel].astype(np.int64)
+            key_all.append((e << 24) | (r << 20) | ent[sel])     # (expert, rank, entry)
+            p_all.append(pos[r][sel].astype(np.int64))
+        key = np.concatenate(key_all)
+        p = np.concatenate(p_all)
+        assert recv[j] == key.size
+        order = np.argsort(p, kind="stable")
+        np.testing.assert_array_equal(p[order], np.arange(key.size))
+        assert (np.diff(key[order]) > 0).all(), f"rank {j}: rows out of (expert, source, entry) order"
+    # dispatch of self-identifying rows (element 0 = rank, element 1 = token)
+    cap = int(recv.max())
+    xs = synth.tagged_rows(P, [T] * P, H)
+    x_dev = [to_dev(x)[1] for x in xs]
+    out_dev = [empty_dev(cap * H, torch.bfloat16, 0xFFFF) for _ in range(P)]
+    A.atom_moe_dispatch(rt, x_dev, out_dev, cap, H)
+    outs = [from_dev(o).reshape(cap, H) for o in out_dev]
+    for r in range(P):
+        valid = pos[r] >= 0
+        j = ids[r][valid] // per
+        for jj in range(P):
+            m = j == jj
+            rows = outs[jj][pos[r][valid][m]]
+            assert (rows[:, 0] == r).all(), f"source {r} -> rank {jj}: wrong rank tag"
+            np.testing.assert_array_equal(rows[:, 1], (ent[valid][m] // k) & 0xFFFF)
