@@ -9,8 +9,9 @@ resident synthetic input (bf16):
   ar      fused one-shot AllReduce of the same 8 x 256 MiB
   a2av    AllToAllV MoE dispatch, 8 x 4096 x 7168 (Dirichlet-multinomial counts, seed 3)
   ag_zs   AllGather, zero staging, 8 partitions of 64 MiB (U[-1,1], seed 4)
-  ag_snac AllGather through SNAC, same input, 1 MiB chunks, 32-slot ring
-  ar_snac composed AllReduce through SNAC (Figure 6) of the 8 x 256 MiB
+  ag_snac AllGather through SNAC, same input, 512 KiB chunks, 64-slot ring
+  ar_snac composed AllReduce through SNAC (Figure 6) of the 8 x 256 MiB, 2 MiB
+          chunks, 16-slot ring
   dec     decode AllReduce, 8 x b x 7168 for b in 1, 2, 4, 8, 16 (N(0,0.02), seed 5)
   rsv_zipf ReduceScatterV of the 8 x 256 MiB, Zipf(0.125) partitions (Figure 16)
   agv_zipf AllGatherV of 512 MiB in Zipf(0.125) partitions
@@ -55,14 +56,18 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--lat-iters", type=int, default=2000,
-                    help="event-timed samples of the 8 KiB AllGather")
+    ap.add_argument("--lat-iters", type=int, default=10000,
+                    help="event-timed samples of the 8 KiB AllGather and of each decode AllReduce")
     ap.add_argument("--ag-mib", type=int, default=64, help="AllGather partition size (MiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--study", action="store_true",
                     help="instead of the step: Atom copy bandwidth vs workgroups (CUs used) "
                          "and vs pipeline depth, one JSON line per point")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the step: AllGather (zero-staging and SNAC with 512 KiB, "
+                         "1 MiB, 2 MiB chunks) over 8 KiB..1 GiB partitions, ReduceScatter and "
+                         "AllReduce over 8 KiB..256 MiB inputs; one JSON line per point")
     ap.add_argument("--xcd-order", action="store_true",
                     help="zero-staging kernels give each XCD one contiguous range of tiles")
     ap.add_argument("--no-snac", dest="snac", action="store_false",
@@ -87,6 +92,9 @@ def main():
     stream = torch.cuda.current_stream()
     if args.study:
         study(A, synth, torch, dev)
+        return
+    if args.sweep:
+        sweep(A, synth, torch, dev)
         return
 
     def up(a):
@@ -117,7 +125,7 @@ def main():
     S = args.ag_mib * MiB
     z4 = [up(z) for z in synth.c4_inputs(S, P)]
     ag_out = [empty(P * S // 2) for _ in range(P)]
-    snac_cfg = A.config(flags=A.F_STAGED, chunk_bytes=1 * MiB)     # ring and grid: defaults
+    snac_cfg = A.config(flags=A.F_STAGED)     # chunk, ring and grid: the library's defaults
     # AllGatherV: 8 x 64 MiB in total, Zipf(0.125) partitions
     cnt_ag = synth.zipf_partition(P * S // 2, P, 0.125, 8) // 8
     zv = [up(synth.draw(4, k, int(cnt_ag[k]) * 8, "uniform", synth.BF16)) for k in range(P)]
@@ -246,6 +254,20 @@ def main():
         b.record(stream)
     torch.cuda.synchronize()
     lat = np.array([a.elapsed_time(b) * 1e3 for a, b in pairs])
+    # Decode AllReduce latency per batch size (event pairs, as above).
+    dec_lat = {}
+    for b in (1, 2, 4, 8, 16):
+        lay = (L(A.PARTITIONED, x5[b], b * 896), L(A.GATHERED, o5[b], b * 896))
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(args.lat_iters)]
+        for a, e in pairs:
+            a.record(stream)
+            A.atom_collective(lay[0], lay[1], A.OP_SUM)
+            e.record(stream)
+        torch.cuda.synchronize()
+        v = np.array([a.elapsed_time(e) * 1e3 for a, e in pairs])
+        dec_lat[f"b{b}"] = {"p50_us": round(float(np.percentile(v, 50)), 2),
+                            "p99_us": round(float(np.percentile(v, 99)), 2)}
     # Launch floor: the same event pair around a 16-byte atom_copy.
     tiny_src, tiny_dst = empty(8), empty(8)
     pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -314,8 +336,8 @@ def main():
             "workload": ("one pass over: copy of 256 MiB; 8-way ReduceScatter and fused AllReduce of 8 x 256 MiB bf16; "
                          "AllToAllV 8 x 4096 x 7168 bf16 (Dirichlet-multinomial counts); "
                          f"AllGather 8 x {args.ag_mib} MiB (zero-staging"
-                         + (" and SNAC, 1 MiB chunks, 32-slot ring); SNAC-composed AllReduce of the "
-                            "8 x 256 MiB; " if args.snac else "); ") +
+                         + (" and SNAC, 512 KiB chunks, 64-slot ring); SNAC-composed AllReduce of the "
+                            "8 x 256 MiB (2 MiB chunks, 16-slot ring); " if args.snac else "); ") +
                          "ReduceScatterV and AllGatherV with Zipf(0.125) partitions of the same totals; "
                          "decode AllReduce 8 x b x 7168 bf16, b = 1..16; AllGather 8 x 8 KiB; "
                          "MoE route, dispatch and combine of 8 x 512 tokens x 7168 bf16 "
@@ -330,6 +352,8 @@ def main():
         "p99_us_8KiB": round(float(np.percentile(lat, 99)), 2),
         "host_us_per_call_8KiB": round(host_us, 2),
         "graph_us_per_call_8KiB": round(graph_us, 2),
+        "decode_allreduce_latency": dec_lat,
+        "latency_samples": args.lat_iters,
         "p50_us_launch_floor_16B_copy": round(float(np.percentile(floor, 50)), 2),
         "cus_used": cus,
         "rows": per_row,
@@ -375,6 +399,78 @@ def study(A, synth, torch, dev):
     for wgs in (8, 16, 256, 0):
         for stages in (1, 2, 4, 8):
             point(wgs, stages)
+
+
+def sweep(A, synth, torch, dev):
+    """Message-size sweeps of the pages' collective benchmarks (one JSON line
+    per point): AllGather of 8 partitions from 8 KiB to 1 GiB each, zero
+    staging and SNAC with 512 KiB, 1 MiB and 2 MiB chunks; ReduceScatter and
+    the fused and SNAC AllReduce of 8 inputs from 8 KiB to 256 MiB each.
+    Median of event-timed launches (more samples for small messages); GB/s
+    on credited bytes."""
+    P = 8
+    L = A.layout
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, nbytes):
+        reps = 200 if nbytes < (1 << 24) else (20 if nbytes < (1 << 30) else 5)
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        assert A.atom_sync_status() == A.OK
+        return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+    def emit(coll, mode, size, ms, credited):
+        print(json.dumps({"sweep": coll, "mode": mode, "bytes_per_rank": size,
+                          "us": round(ms * 1e3, 2), "GBps": round(credited / ms / 1e6, 1),
+                          "frac_hbm": round(credited / ms / 1e6 * 1e9 / HBM_PEAK, 4)}), flush=True)
+
+    # AllGather: inputs and outputs for the largest size, smaller sizes use views
+    top = 1 << 30
+    z = [torch.empty(top // 2, dtype=torch.bfloat16, device=dev).uniform_(-1, 1) for _ in range(P)]
+    out = [torch.empty(P * top // 2, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+    size = 8 << 10
+    while size <= top:
+        n = size // 2
+        zs = [t[:n] for t in z]
+        os_ = [t[:P * n] for t in out]
+        lin, lout = L(A.SHARD, zs, n), L(A.GATHERED, os_, n)
+        cred = (1 + P) * P * size
+        emit("allgather", "zero-staging", size, timed(lambda: A.atom_collective(lin, lout, A.OP_COPY), size * P), cred)
+        for chunk in (512 << 10, 1 << 20, 2 << 20):
+            cfg = A.config(flags=A.F_STAGED, chunk_bytes=chunk)
+            emit("allgather", f"snac_{chunk >> 10}KiB", size,
+                 timed(lambda: A.atom_collective(lin, lout, A.OP_COPY, cfg), size * P), cred)
+        size *= 2
+    del z, out
+    torch.cuda.empty_cache()
+    # ReduceScatter / AllReduce of P inputs of `size` bytes each
+    top = 256 << 20
+    x = [torch.randn(top // 2, dtype=torch.float32, device=dev).to(torch.bfloat16) for _ in range(P)]
+    ys = [torch.empty(top // 2 // P, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+    ar = [torch.empty(top // 2, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+    size = 8 << 10
+    while size <= top:
+        n = size // 2 // P
+        xs = [t[:P * n] for t in x]
+        lin = L(A.PARTITIONED, xs, n)
+        lrs, lar = L(A.SHARD, [t[:n] for t in ys], n), L(A.GATHERED, [t[:P * n] for t in ar], n)
+        emit("reducescatter", "zero-staging", size,
+             timed(lambda: A.atom_collective(lin, lrs, A.OP_SUM), size * P), (P + 1) * P * n * 2)
+        emit("allreduce", "fused", size,
+             timed(lambda: A.atom_collective(lin, lar, A.OP_SUM), size * P), 2 * P * P * n * 2)
+        for chunk in (512 << 10, 1 << 20, 2 << 20):
+            cfg = A.config(flags=A.F_STAGED, chunk_bytes=chunk)
+            emit("allreduce", f"snac_{chunk >> 10}KiB", size,
+                 timed(lambda: A.atom_collective(lin, lar, A.OP_SUM, cfg), size * P), 2 * P * P * n * 2)
+        size *= 2
 
 
 def measured_traffic(row):

@@ -120,7 +120,11 @@ typedef struct atom_layout {
                                  workgroup order; measured within noise) */
 typedef struct atom_config {
     int64_t chunk_bytes;       /* SNAC chunk (notify unit); power of two in
-                                  [64 KiB, 16 MiB]; default 1 MiB */
+                                  [64 KiB, 16 MiB]; default 512 KiB for
+                                  AllGather, 2 MiB for AllReduce. A partition
+                                  smaller than the chunk is staged as one
+                                  chunk of whole pieces (plan_query reports
+                                  the chunk used). */
     int32_t stages;            /* 16-byte vectors in flight per lane: 1, 2, 4 or 8
                                   (0: chosen per collective) */
     int32_t num_wgs;           /* workgroups to launch; 0 = derived from size */

@@ -51,6 +51,7 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out)
 
 struct Cfg {
     int64_t chunk;
+    bool chunk_set;    // chunk given by the caller
     int32_t stages;    // 0 = pick by shape
     int64_t num_wgs;   // 0 = pick by shape
     uint32_t flags;
@@ -62,7 +63,8 @@ struct Cfg {
 
 atom_status read_cfg(const atom_config* cfg, Cfg* c)
 {
-    c->chunk = kDefaultChunk;
+    c->chunk = 0;          // staged chunk: chosen per collective unless given
+    c->chunk_set = false;
     c->stages = 0;
     c->num_wgs = 0;
     c->flags = 0;
@@ -76,6 +78,7 @@ atom_status read_cfg(const atom_config* cfg, Cfg* c)
         if (!is_pow2(cfg->chunk_bytes) || cfg->chunk_bytes < kMinChunk || cfg->chunk_bytes > kMaxChunk)
             return ATOM_ERR_INVALID_ARG;
         c->chunk = cfg->chunk_bytes;
+        c->chunk_set = true;
     }
     if (cfg->stages != 0) {
         if (cfg->stages != 1 && cfg->stages != 2 && cfg->stages != 4 && cfg->stages != 8)
@@ -622,6 +625,28 @@ atom_status plan_collective(const atom_layout* in, const atom_layout* out, atom_
             vec = vec && aligned(in->bufs[r], kVecBytes) && aligned(out->bufs[r], kVecBytes);
         if (!vec)
             return ATOM_ERR_UNSUPPORTED;
+        // Chunk: the caller's, else the one measured best on MI355X for
+        // the collective (AllGather 512 KiB, AllReduce 2 MiB: both in the
+        // 512 KiB - 2 MiB range of Table 3's bandwidth-delay rule). A
+        // partition smaller than the chunk is staged as one chunk of just
+        // enough whole pieces, so no task handles an empty piece.
+        int64_t chunk = c.chunk_set ? c.chunk
+                                    : (kind == ATOM_COLL_ALL_GATHER ? kDefaultChunkAllGather
+                                                                    : kDefaultChunkAllReduce);
+        // Piece (the task granule): the caller's, else the largest power of
+        // two from 8 KiB to 64 KiB that still gives about one persistent
+        // grid's worth of staging tasks (P * S / piece >= 512), so a
+        // medium message is spread over many workgroups instead of a few
+        // (smaller pieces cost more in hand-offs than they gain).
+        int64_t piece = c.piece;
+        if (!piece) {
+            piece = kMinAutoPiece;
+            while (piece < kPieceBytes && static_cast<int64_t>(P) * S / (2 * piece) >= kSnacGrid)
+                piece *= 2;
+        }
+        piece = std::min(piece, chunk);
+        if (S < chunk)
+            chunk = std::max<int64_t>(1, ceil_div(S, piece)) * piece;
         SnacArgs& a = p->sa;
         std::memset(&a, 0, sizeof a);
         for (int r = 0; r < P; ++r) {
@@ -630,18 +655,18 @@ atom_status plan_collective(const atom_layout* in, const atom_layout* out, atom_
         }
         a.P = P;
         a.part_bytes = S;
-        a.chunk_bytes = c.chunk;
-        a.piece_bytes = std::min<int64_t>(c.piece ? c.piece : kPieceBytes, c.chunk);
-        a.pieces = static_cast<int32_t>(c.chunk / a.piece_bytes);
+        a.chunk_bytes = chunk;
+        a.piece_bytes = piece;
+        a.pieces = static_cast<int32_t>(chunk / piece);
         a.slots = c.slots;
         if (!c.slots_set) {
             // Table 3's rule applied to one device: the ring holds at least
             // one bandwidth-delay product of HBM (8 TB/s) times the cross-XCD
             // stage-notify-consume round trip (~4 us measured), about 32 MiB.
-            const int64_t want = ceil_div(kSnacInflightBytes, c.chunk);
+            const int64_t want = ceil_div(kSnacInflightBytes, chunk);
             a.slots = static_cast<int32_t>(std::max<int64_t>(kDefaultSlots, std::min<int64_t>(kMaxSlots, want)));
         }
-        a.nchunks_per_part = ceil_div(S, c.chunk);
+        a.nchunks_per_part = ceil_div(S, chunk);
         a.nchunks = a.nchunks_per_part * P;
         a.ntasks = 2 * a.nchunks * a.pieces;
         a.dtype = p->dtype;
@@ -651,8 +676,8 @@ atom_status plan_collective(const atom_layout* in, const atom_layout* out, atom_
         p->wg = 256;
         p->U = c.stages ? c.stages : 4;
         p->slots = a.slots;
-        p->chunk_bytes = c.chunk;
-        p->ring_bytes = c.chunk * a.slots;
+        p->chunk_bytes = chunk;
+        p->ring_bytes = chunk * a.slots;
         p->grid = std::max<int64_t>(1, std::min<int64_t>(a.ntasks, c.num_wgs ? c.num_wgs : kSnacGrid));
         p->exec = kind == ATOM_COLL_ALL_GATHER ? EX_SNAC_AG : EX_SNAC_AR;
     }

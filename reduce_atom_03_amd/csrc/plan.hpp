@@ -52,12 +52,14 @@ struct Plan : PlanHead {
 };
 
 // Defaults and limits.
-constexpr int64_t kDefaultChunk = 1 << 20;           // 1 MiB (Table 3, H200 row)
+constexpr int64_t kDefaultChunkAllGather = 512 << 10; // staged defaults, measured on MI355X
+constexpr int64_t kDefaultChunkAllReduce = 2 << 20;
 constexpr int64_t kMinChunk = 64 << 10;
 constexpr int64_t kMaxChunk = 16 << 20;
 constexpr int32_t kDefaultSlots = 4;
 constexpr int32_t kMaxSlots = 64;
 constexpr int64_t kPieceBytes = 64 << 10;            // SNAC task granule
+constexpr int64_t kMinAutoPiece = 8 << 10;           // smallest granule chosen for small partitions
 constexpr int64_t kSnacInflightBytes = 32 << 20;     // default ring: one on-chip BDP
 constexpr int64_t kSnacGrid = 512;                   // persistent SNAC workgroups (2 per CU)
 constexpr int64_t kMaxGrid = 1 << 20;

@@ -242,8 +242,35 @@ def test_snac_chunking():
             st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=8, n=S // 2, cfg=cfg,
                          ins=fake(8, S), outs=fake(8, 8 * S, start=BASE + (1 << 40)))
             assert st == A.OK and info.staged == 1
-            assert info.chunk_bytes == chunk and info.ring_slots == 4
-            assert info.num_chunks == 8 * -(-S // chunk)
+            # a partition smaller than the chunk is one chunk of whole pieces
+            # (8 KiB partition: one 8 KiB piece)
+            used = chunk if S >= chunk else 8 << 10
+            assert info.chunk_bytes == used and info.ring_slots == 4
+            assert info.num_chunks == 8 * -(-S // used)
+
+
+def test_snac_default_chunk_per_collective():
+    """Without chunk_bytes: 512 KiB chunks for AllGather, 2 MiB for AllReduce."""
+    S = 64 * MiB
+    st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=8, n=S // 2, cfg=A.config(flags=A.F_STAGED),
+                 ins=fake(8, S), outs=fake(8, 8 * S, start=BASE + (1 << 40)))
+    assert st == A.OK and info.chunk_bytes == 512 << 10 and info.ring_slots == 64
+    st, info = Q(A.PARTITIONED, A.GATHERED, A.OP_SUM, P=8, n=S // 2 // 8,
+                 cfg=A.config(flags=A.F_STAGED), ins=fake(8, S),
+                 outs=fake(8, S, start=BASE + (1 << 40)))
+    assert st == A.OK and info.chunk_bytes == 2 * MiB and info.ring_slots == 16
+    # a 24 KiB partition: one chunk of 8 KiB pieces (3 of them)
+    st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=8, n=12 << 10, cfg=A.config(flags=A.F_STAGED),
+                 ins=fake(8, 24 << 10), outs=fake(8, 8 * (24 << 10), start=BASE + (1 << 40)))
+    assert st == A.OK and info.chunk_bytes == 24 << 10 and info.num_chunks == 8
+    # a 64 KiB partition: 8 KiB pieces (the smallest chosen); a caller's piece is kept
+    st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=8, n=32 << 10, cfg=A.config(flags=A.F_STAGED),
+                 ins=fake(8, 64 << 10), outs=fake(8, 8 * (64 << 10), start=BASE + (1 << 40)))
+    assert st == A.OK and info.chunk_bytes == 64 << 10
+    st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=8, n=12 << 10,
+                 cfg=A.config(flags=A.F_STAGED, piece_bytes=16 << 10),
+                 ins=fake(8, 24 << 10), outs=fake(8, 8 * (24 << 10), start=BASE + (1 << 40)))
+    assert st == A.OK and info.chunk_bytes == 32 << 10
 
 
 def test_zero_sized_collective_launches_nothing():
@@ -274,3 +301,19 @@ def test_binding_maps_one_hip_runtime():
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     assert r.stdout.strip().splitlines()[-1] == "1"
+
+
+def test_snac_piece_spreads_medium_messages():
+    """Without piece_bytes the task granule is the largest power of two in
+    [8 KiB, 64 KiB] with P * S / piece >= 512 staging tasks."""
+    for S, piece in ((64 << 10, 8 << 10), (512 << 10, 8 << 10), (2 * MiB, 32 << 10),
+                     (4 * MiB, 64 << 10), (64 * MiB, 64 << 10)):
+        st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=8, n=S // 2,
+                     cfg=A.config(flags=A.F_STAGED, chunk_bytes=16 * MiB), ins=fake(8, S),
+                     outs=fake(8, 8 * S, start=BASE + (1 << 40)))
+        assert st == A.OK
+        # S < 16 MiB chunk: one chunk of S rounded to whole pieces
+        want_chunk = 16 * MiB if S >= 16 * MiB else -(-S // piece) * piece
+        assert info.chunk_bytes == want_chunk, (S, info.chunk_bytes)
+        tasks = 2 * info.num_chunks * (want_chunk // piece)
+        assert info.num_wgs == min(512, tasks), (S, info.num_wgs, tasks)
