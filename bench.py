@@ -66,8 +66,9 @@ def parse():
                          "and vs pipeline depth, one JSON line per point")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step: AllGather (zero-staging and SNAC with 512 KiB, "
-                         "1 MiB, 2 MiB chunks) over 8 KiB..1 GiB partitions, ReduceScatter and "
-                         "AllReduce over 8 KiB..256 MiB inputs; one JSON line per point")
+                         "1 MiB, 2 MiB chunks) over 8 KiB..1 GiB partitions, ReduceScatter, "
+                         "AllReduce and AllToAll over 8 KiB..256 MiB inputs, MoE over 1..4096 "
+                         "tokens per rank; one JSON line per point")
     ap.add_argument("--xcd-order", action="store_true",
                     help="zero-staging kernels give each XCD one contiguous range of tiles")
     ap.add_argument("--no-snac", dest="snac", action="store_false",
@@ -404,8 +405,10 @@ def study(A, synth, torch, dev):
 def sweep(A, synth, torch, dev):
     """Message-size sweeps of the pages' collective benchmarks (one JSON line
     per point): AllGather of 8 partitions from 8 KiB to 1 GiB each, zero
-    staging and SNAC with 512 KiB, 1 MiB and 2 MiB chunks; ReduceScatter and
-    the fused and SNAC AllReduce of 8 inputs from 8 KiB to 256 MiB each.
+    staging and SNAC with 512 KiB, 1 MiB and 2 MiB chunks; ReduceScatter,
+    the fused and SNAC AllReduce and the uniform AllToAll of 8 inputs from
+    8 KiB to 256 MiB each; the MoE route, dispatch and combine for 1 to 4096
+    tokens per rank (256 experts, top-8, 7168-wide rows).
     Median of event-timed launches (more samples for small messages); GB/s
     on credited bytes."""
     P = 8
@@ -427,8 +430,8 @@ def sweep(A, synth, torch, dev):
         assert A.atom_sync_status() == A.OK
         return float(np.median([a.elapsed_time(b) for a, b in ev]))
 
-    def emit(coll, mode, size, ms, credited):
-        print(json.dumps({"sweep": coll, "mode": mode, "bytes_per_rank": size,
+    def emit(coll, mode, size, ms, credited, unit="bytes_per_rank"):
+        print(json.dumps({"sweep": coll, "mode": mode, unit: size,
                           "us": round(ms * 1e3, 2), "GBps": round(credited / ms / 1e6, 1),
                           "frac_hbm": round(credited / ms / 1e6 * 1e9 / HBM_PEAK, 4)}), flush=True)
 
@@ -470,7 +473,31 @@ def sweep(A, synth, torch, dev):
             cfg = A.config(flags=A.F_STAGED, chunk_bytes=chunk)
             emit("allreduce", f"snac_{chunk >> 10}KiB", size,
                  timed(lambda: A.atom_collective(lin, lar, A.OP_SUM, cfg), size * P), 2 * P * P * n * 2)
+        # uniform AllToAll of the same inputs (partition j of every source to j)
+        lat = L(A.TRANSPOSED, [t[:P * n] for t in ar], n)
+        emit("alltoall", "zero-staging", size,
+             timed(lambda: A.atom_collective(lin, lat, A.OP_COPY), size * P), 2 * P * P * n * 2)
         size *= 2
+    del x, ys, ar
+    torch.cuda.empty_cache()
+    # MoE route, dispatch and combine by tokens per rank (256 experts, top-8,
+    # 7168-wide bf16 rows): decode-sized batches up to prefill-sized ones
+    E, k, H = synth.MOE_EXPERTS, synth.MOE_TOPK, synth.HIDDEN
+    for T in (1, 4, 16, 64, 256, 1024, 4096):
+        ids, w = synth.moe_routing(6, P, T, E, k)
+        rt = A.moe_alloc_routing([torch.from_numpy(a).to(dev) for a in ids], E, k)
+        A.atom_moe_route(rt)
+        cap = max(int(rt.recv_t.max().item()), 1)
+        xs = [torch.randn(T * H, device=dev).to(torch.bfloat16) for _ in range(P)]
+        ws = [torch.from_numpy(a).to(dev) for a in w]
+        disp = [torch.empty(cap * H, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+        outs = [torch.empty(T * H, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+        mb = moe_bytes(P, T, E, k, H * 2)
+        emit("moe", "route", T, timed(lambda: A.atom_moe_route(rt), 1), mb["route"], "tokens_per_rank")
+        emit("moe", "dispatch", T, timed(lambda: A.atom_moe_dispatch(rt, xs, disp, cap, H), mb["dispatch"] // P),
+             mb["dispatch"], "tokens_per_rank")
+        emit("moe", "combine", T, timed(lambda: A.atom_moe_combine(rt, disp, ws, outs, cap, H), mb["combine"] // P),
+             mb["combine"], "tokens_per_rank")
 
 
 def measured_traffic(row):

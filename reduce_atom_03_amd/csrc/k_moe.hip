@@ -8,7 +8,8 @@
 // rows in entry order; a rank's buffer holds its experts back to back);
 // combine is the way back, a weighted sum over each token's k choices.
 //
-// Routing (three small launches, metadata only):
+// Routing (metadata only): one workgroup when every rank's entries fit in
+// one chunk (k_moe_route_small, the decode case), else three launches:
 //   k_moe_rank   one wave per chunk of 256 entries of one rank: the rank of
 //                every entry among the chunk's entries with the same expert,
 //                in entry order (each 64-entry step sorts its (expert, lane)
@@ -36,6 +37,55 @@ namespace atom {
 
 namespace {
 
+// Ranks one 64-entry step of entries [i0 + s*64, ...) of rank r against the
+// per-expert counters `cnt` (LDS, this wave's own): each valid entry gets
+// the number of earlier entries with its expert (earlier steps included),
+// written to pos; invalid entries get -1. The wave's (expert, lane) keys are
+// sorted across lanes (bitonic, 21 compare-exchange stages; entries routed
+// nowhere sort last), so equal experts form runs in lane order and a slot's
+// rank is its offset in its run.
+__device__ __forceinline__ void rank_step(const MoeRouteArgs& a, int r, int64_t i, int64_t i1, int e,
+                                          int32_t* cnt)
+{
+    const int lane = threadIdx.x & 63;
+    const bool valid = i < i1 && e >= 0 && e < a.E;
+    int key = ((valid ? e : a.E) << 6) | lane;
+#pragma unroll
+    for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const int other = __shfl_xor(key, j);
+            const bool keep_min = ((lane & k) == 0) == ((lane & j) == 0);
+            key = keep_min ? min(key, other) : max(key, other);
+        }
+    }
+    const int se = key >> 6;                          // expert in sorted slot `lane`
+    const bool sv = se < a.E;
+    // The run of slot `lane` starts at the largest run start at or below it.
+    const int prev = __shfl_up(se, 1);
+    int start = (lane == 0 || prev != se) ? lane : 0;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(start, d);
+        if (lane >= d)
+            start = max(start, o);
+    }
+    const int next = __shfl_down(se, 1);
+    const bool run_end = lane == 63 || next != se;
+    int32_t before = 0;
+    if (sv)
+        before = cnt[se];
+    // Every slot has read its counter before any slot writes one: the wave's
+    // LDS operations complete in program order.
+    if (sv && run_end)
+        cnt[se] = before + (lane - start) + 1;
+    const int32_t rank_here = sv ? before + (lane - start) : -1;
+    // Send each slot's rank back to the lane its entry came from.
+    const int32_t mine = __builtin_amdgcn_ds_permute((key & 63) << 2, rank_here);
+    if (i < i1)
+        a.pos[r][i] = valid ? mine : -1;
+}
+
 __global__ __launch_bounds__(64) void k_moe_rank(const MoeRouteArgs a)
 {
     extern __shared__ int32_t cnt[];                  // [E]: rows so far in this chunk
@@ -56,53 +106,94 @@ __global__ __launch_bounds__(64) void k_moe_rank(const MoeRouteArgs a)
     }
     __syncthreads();
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-        const int64_t i = i0 + s * 64 + lane;
-        const int e = ids[s];
-        const bool valid = i < i1 && e >= 0 && e < a.E;
-        // Sort the wave's (expert, lane) keys (bitonic, 21 compare-exchange
-        // stages across lanes); entries routed nowhere sort last. Sorted slot
-        // q then holds one entry, and equal experts form runs in lane order.
-        int key = ((valid ? e : a.E) << 6) | lane;
-#pragma unroll
-        for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-            for (int j = k >> 1; j > 0; j >>= 1) {
-                const int other = __shfl_xor(key, j);
-                const bool keep_min = ((lane & k) == 0) == ((lane & j) == 0);
-                key = keep_min ? min(key, other) : max(key, other);
-            }
-        }
-        const int se = key >> 6;                      // expert in sorted slot `lane`
-        const bool sv = se < a.E;
-        // The run of slot `lane` starts at the largest run start at or below it.
-        const int prev = __shfl_up(se, 1);
-        int start = (lane == 0 || prev != se) ? lane : 0;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int o = __shfl_up(start, d);
-            if (lane >= d)
-                start = max(start, o);
-        }
-        const int next = __shfl_down(se, 1);
-        const bool run_end = lane == 63 || next != se;
-        int32_t before = 0;
-        if (sv)
-            before = cnt[se];
-        // Every slot has read its counter before any slot writes one: the
-        // wave's LDS operations complete in program order.
-        if (sv && run_end)
-            cnt[se] = before + (lane - start) + 1;
-        const int32_t rank_here = sv ? before + (lane - start) : -1;
-        // Send each slot's rank back to the lane its entry came from.
-        const int32_t mine = __builtin_amdgcn_ds_permute((key & 63) << 2, rank_here);
-        if (i < i1)
-            a.pos[r][i] = valid ? mine : -1;
-    }
+    for (int s = 0; s < kSteps; ++s)
+        rank_step(a, r, i0 + s * 64 + lane, i1, ids[s], cnt);
     __syncthreads();
     int32_t* part = a.partial + (static_cast<int64_t>(r) * a.nch + ch) * a.E;
     for (int e = lane; e < a.E; e += 64)
         part[e] = cnt[e];
+}
+
+// The whole routing in one workgroup when every rank's entries fit in one
+// chunk (decode-sized batches): wave r ranks rank r's entries into its own
+// LDS counters; then the block writes the counts, scans the expert totals
+// and places every entry (earlier experts of the rank + earlier ranks +
+// rank among the rank's entries).
+__global__ __launch_bounds__(1024) void k_moe_route_small(const MoeRouteArgs a)
+{
+    extern __shared__ int32_t lds[];                  // [P][E] counts, [E] prefix, [nthr] partials
+    const int nthr = blockDim.x;                      // 64 * P
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;                           // this wave's rank
+    int32_t* cnt = lds;
+    int32_t* incl = lds + a.P * a.E;
+    int32_t* part = incl + a.E;
+    for (int q = tid; q < a.P * a.E; q += nthr)
+        cnt[q] = 0;
+    constexpr int kSteps = kMoeChunk / 64;
+    int ids[kSteps];
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+        const int64_t i = s * 64 + (tid & 63);
+        ids[s] = i < a.n ? a.ids[w][i] : -1;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s)
+        rank_step(a, w, s * 64 + (tid & 63), a.n, ids[s], cnt + w * a.E);
+    __syncthreads();
+    // counts, and the totals of each expert over the ranks
+    for (int e = tid; e < a.E; e += nthr) {
+        int32_t tot = 0;
+        for (int r = 0; r < a.P; ++r) {
+            a.counts[static_cast<int64_t>(r) * a.E + e] = cnt[r * a.E + e];
+            tot += cnt[r * a.E + e];
+        }
+        incl[e] = tot;
+    }
+    __syncthreads();
+    // inclusive prefix of the totals over the experts
+    const int m = (a.E + nthr - 1) / nthr;
+    int32_t run = 0;
+    for (int u = 0; u < m; ++u) {
+        const int e = tid * m + u;
+        if (e < a.E) {
+            run += incl[e];
+            incl[e] = run;
+        }
+    }
+    part[tid] = run;
+    __syncthreads();
+    for (int d = 1; d < nthr; d <<= 1) {
+        const int32_t v = tid >= d ? part[tid - d] : 0;
+        __syncthreads();
+        part[tid] += v;
+        __syncthreads();
+    }
+    const int32_t off = tid > 0 ? part[tid - 1] : 0;
+    for (int u = 0; u < m; ++u) {
+        const int e = tid * m + u;
+        if (e < a.E)
+            incl[e] += off;
+    }
+    __syncthreads();
+    for (int s = 0; s < kSteps; ++s) {
+        const int64_t i = s * 64 + (tid & 63);
+        if (i < a.n) {
+            const int32_t p = a.pos[w][i];
+            if (p >= 0) {
+                const int e = ids[s];
+                const int first = (e / a.per) * a.per;
+                int32_t cross = 0;
+                for (int r = 0; r < w; ++r)
+                    cross += cnt[r * a.E + e];
+                const int32_t base = (e > 0 ? incl[e - 1] : 0) - (first > 0 ? incl[first - 1] : 0);
+                a.pos[w][i] = p + base + cross;
+            }
+        }
+    }
+    for (int j = tid; j < a.P; j += nthr)
+        a.recv[j] = static_cast<int64_t>(incl[(j + 1) * a.per - 1] - (j > 0 ? incl[j * a.per - 1] : 0));
 }
 
 __global__ __launch_bounds__(1024) void k_moe_prefix(const MoeRouteArgs a)
@@ -381,6 +472,13 @@ hipError_t launch_moe_route(const MoeRoutePlan& p, hipStream_t stream)
         a.groups < 1 || a.groups > a.nch || p.scan_threads < a.E || p.scan_threads > 1024 ||
         p.scan_threads % 64 != 0)
         return hipErrorInvalidValue;
+    if (p.small) {
+        const size_t lds = static_cast<size_t>(a.P * a.E + a.E + 64 * a.P) * sizeof(int32_t);
+        if (a.nch != 1 || a.n > kMoeChunk || lds > kMoeSmallLds)
+            return hipErrorInvalidValue;
+        k_moe_route_small<<<dim3(1), dim3(64 * a.P), lds, stream>>>(a);
+        return hipGetLastError();
+    }
     const unsigned nb = static_cast<unsigned>(a.P) * static_cast<unsigned>(a.nch);
     k_moe_rank<<<dim3(nb), dim3(64), static_cast<size_t>(a.E) * sizeof(int32_t), stream>>>(a);
     hipError_t e = hipGetLastError();

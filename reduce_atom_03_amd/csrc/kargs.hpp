@@ -105,6 +105,7 @@ struct SnacArgs {
 // prefix, place). Entries i = t*k + c of rank r are cut into chunks of kMoeChunk.
 constexpr int kMoeChunk = 256;         // entries one wave ranks in order
 constexpr int kMoeMaxTopk = 16;
+constexpr int kMoeSmallLds = 32 << 10;   // LDS bound of the one-workgroup routing
 
 struct MoeRouteArgs {
     const int32_t* ids[kMaxRanks];     // T*k expert ids per rank

@@ -70,6 +70,7 @@ constexpr int64_t kDefaultWaitUs = 1000000;          // one SNAC wait: 1 s
 struct MoeRoutePlan {
     MoeRouteArgs a;
     int32_t scan_threads = 64;         // prefix workgroup: one thread per expert
+    bool small = false;                // one-workgroup routing (one chunk per rank)
 };
 
 struct MoeMovePlan {
