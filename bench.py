@@ -369,7 +369,8 @@ def study(A, synth, torch, dev):
     set): GB/s against workgroups launched (CUs used = min(WGs, 256)) and
     against pipeline depth (16-byte slots in flight per lane), the one-GPU
     counterparts of the pages' SM-count and pipeline-depth studies
-    (Figures 3 and 11)."""
+    (Figures 3 and 11); then GB/s against workgroups for the 8-way reduce
+    and the 1 -> 8 fan-out."""
     n = 1 << 27
     src = torch.from_numpy(synth.draw(2, 0, n, "normal", synth.BF16).view(np.int16)).view(
         torch.bfloat16).to(dev)
@@ -400,6 +401,40 @@ def study(A, synth, torch, dev):
     for wgs in (8, 16, 256, 0):
         for stages in (1, 2, 4, 8):
             point(wgs, stages)
+
+    # The same CUs-used curve for the two other shapes of the hot path: the
+    # 8-way reduce (8 x 256 MiB -> 256 MiB, ReduceScatter layout) and the
+    # 1 -> 8 fan-out (AllGather of 8 x 64 MiB).
+    P = 8
+    del src, dst
+    xs = [torch.randn(n, device=dev).to(torch.bfloat16) for _ in range(P)]
+    ys = [torch.empty(n // P, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+    zs = [t[:n // 4] for t in xs]
+    ag = [torch.empty(P * n // 4, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+    shapes = {
+        "reduce8_8x256MiB": (A.layout(A.PARTITIONED, xs, n // P), A.layout(A.SHARD, ys, n // P),
+                             A.OP_SUM, (P + 1) * n * 2),
+        "fanout8_8x64MiB": (A.layout(A.SHARD, zs, n // 4), A.layout(A.GATHERED, ag, n // 4),
+                            A.OP_COPY, (1 + P) * P * (n // 4) * 2),
+    }
+    for name, (li, lo, op, nbytes) in shapes.items():
+        for wgs in (8, 16, 32, 64, 128, 256, 512, 1024, 4096, 0):
+            cfg = A.config(num_wgs=wgs)
+            for _ in range(2):
+                A.atom_collective(li, lo, op, cfg)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(5):
+                A.atom_collective(li, lo, op, cfg)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 5
+            st, info = A.atom_plan_query(li, lo, op, cfg)
+            gbs = nbytes / ms / 1e6
+            print(json.dumps({"study": name, "workgroups": info.num_wgs,
+                              "cus_used": min(256, info.num_wgs), "stages": 0,
+                              "ms": round(ms, 4), "GBps": round(gbs, 1),
+                              "frac_hbm": round(gbs * 1e9 / HBM_PEAK, 4)}), flush=True)
 
 
 def sweep(A, synth, torch, dev):
