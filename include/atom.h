@@ -4,10 +4,10 @@
  *
  * Source of the semantics: "Purlin: Separating Orchestration from the
  * Datapath of Collectives" (arXiv 2609.36954).
- *  - Abstract: a collective is a naming of an input layout and an output
- *    layout plus a copy or a reduction; the Atom datapath provides the two
- *    primitives copy and reduce; SNAC (Stage, Notify, And Consume) derives
- *    the coordination from the layouts.
+ *  - Abstract: a collective is defined by its input layout, its output
+ *    layout and one operation (copy or reduce); the Atom datapath supplies
+ *    those two primitives; SNAC (Stage, Notify, And Consume) derives the
+ *    coordination from the layouts.
  *  - Figure 4: ReduceScatter combines partition k of every input into y_k at
  *    rank k; AllGather places every y_k in rank order at every rank;
  *    AllToAll gives rank j partition j of every source.

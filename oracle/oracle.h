@@ -6,11 +6,11 @@
  * header, table or helper with the GPU library.
  *
  * Semantics follow "Purlin: Separating Orchestration from the Datapath of
- * Collectives" (arXiv 2609.36954): a collective is a naming of an input and
- * an output layout plus a copy or a reduction (abstract); Figure 4 gives the
- * ReduceScatter, AllGather and AllToAll layouts; Figure 6 composes AllReduce
- * from ReduceScatter and AllGather; Table 2 names the variable-length (V)
- * variants. The reduction is a sum.
+ * Collectives" (arXiv 2609.36954): a collective is defined by an input
+ * layout, an output layout and a copy or reduce operation (abstract);
+ * Figure 4 gives the ReduceScatter, AllGather and AllToAll layouts;
+ * Figure 6 composes AllReduce from ReduceScatter and AllGather; Table 2
+ * names the variable-length (V) variants. The reduction is a sum.
  *
  * Conventions
  *  - P virtual ranks, 1 <= P <= 64. Buffers are host arrays.

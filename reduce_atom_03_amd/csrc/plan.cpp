@@ -1,10 +1,10 @@
 // plan.cpp -- host planner of libatom.
 //
 // From "Purlin: Separating Orchestration from the Datapath of Collectives"
-// (arXiv 2609.36954): the abstract specifies a collective as a naming of an
-// input and an output layout plus a copy or a reduction, and Table 1's
-// "Derivability" row asks that the orchestration follow from that
-// specification with no explicit schedule. This file is that derivation:
+// (arXiv 2609.36954): the abstract defines a collective by its input
+// layout, its output layout and a copy or reduce operation, and the
+// derivability row of Table 1 wants the orchestration to follow from that
+// definition, with no hand-written schedule. This file is that derivation:
 // the layout pair and op select the collective (Figure 4, Figure 6,
 // Table 2), the buffer shapes follow from the partition size or the counts,
 // and the launch (tiles, grid, SNAC chunks) follows from the shapes.
