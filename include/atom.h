@@ -137,6 +137,9 @@ typedef struct atom_config {
                                   1 s. On expiry the kernel records a timeout
                                   (see atom_sync_status), drops the waiting
                                   task and drains; the output is incomplete. */
+    int32_t lanes;             /* threads per workgroup of the zero-staging
+                                  kernels: 64, 128 or 256 (0: chosen per
+                                  collective and size) */
 } atom_config;
 
 /* The collective that a pair of layouts and an op names (Figure 4/6,

@@ -54,6 +54,7 @@ class AtomConfig(ctypes.Structure):
         ("ring_slots", ctypes.c_int32),
         ("piece_bytes", ctypes.c_int32),
         ("wait_us", ctypes.c_int32),
+        ("lanes", ctypes.c_int32),
     ]
 
 
@@ -233,10 +234,11 @@ def _flatten(c):
 
 
 def config(chunk_bytes: int = 0, stages: int = 0, num_wgs: int = 0, flags: int = 0,
-           ring_slots: int = 0, piece_bytes: int = 0, wait_us: int = 0) -> AtomConfig:
+           ring_slots: int = 0, piece_bytes: int = 0, wait_us: int = 0,
+           lanes: int = 0) -> AtomConfig:
     return AtomConfig(chunk_bytes=chunk_bytes, stages=stages, num_wgs=num_wgs,
                       flags=flags, ring_slots=ring_slots, piece_bytes=piece_bytes,
-                      wait_us=wait_us)
+                      wait_us=wait_us, lanes=lanes)
 
 
 # --------------------------------------------------------- the C entry points

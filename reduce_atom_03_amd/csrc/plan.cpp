@@ -59,6 +59,7 @@ struct Cfg {
     bool slots_set;    // ring depth given by the caller
     int64_t piece;     // SNAC task granule; 0 = default
     int64_t wait_us;   // bound of one SNAC wait
+    int32_t lanes;     // threads per workgroup; 0 = pick by shape
 };
 
 atom_status read_cfg(const atom_config* cfg, Cfg* c)
@@ -72,6 +73,7 @@ atom_status read_cfg(const atom_config* cfg, Cfg* c)
     c->slots_set = false;
     c->piece = 0;
     c->wait_us = kDefaultWaitUs;
+    c->lanes = 0;
     if (!cfg)
         return ATOM_OK;
     if (cfg->chunk_bytes != 0) {
@@ -106,6 +108,9 @@ atom_status read_cfg(const atom_config* cfg, Cfg* c)
         return ATOM_ERR_INVALID_ARG;
     if (cfg->wait_us > 0)
         c->wait_us = cfg->wait_us;
+    if (cfg->lanes != 0 && cfg->lanes != 64 && cfg->lanes != 128 && cfg->lanes != 256)
+        return ATOM_ERR_INVALID_ARG;
+    c->lanes = cfg->lanes;
     return ATOM_OK;
 }
 
@@ -140,15 +145,17 @@ bool buffer_ok(const void* p, int64_t bytes, int esize)
     return p != nullptr && aligned(p, static_cast<uintptr_t>(esize));
 }
 
-// 16-byte slots per lane per tile (the Atom pipeline depth). Measured on
-// MI355X with one tile per workgroup: small tiles and many workgroups keep
-// the most bytes in flight for the scatter-reduce and the fan-out copy,
-// while the fan-out reduce (P loads and P stores per slot) prefers deeper
-// tiles. The reduce kernel is built for U in {1, 2, 4} with U * P <= 32.
+// 16-byte slots per lane per tile (the Atom pipeline depth), for the
+// 64-lane workgroups of the vector path. Measured on MI355X with one tile
+// per workgroup: many small tiles keep the most bytes in flight, so one
+// slot per lane wins for the scatter-reduce, the fused AllReduce and the
+// fan-out copy, two for the exchange (AllToAll(V)) and for reduces of at
+// most 4 sources; the flat copy keeps 256-lane tiles of four slots per
+// lane. The reduce kernel is built for U in {1, 2, 4} with U * P <= 32.
 int32_t pick_u_reduce(int nsrc, int32_t mode, int32_t stages)
 {
     int32_t u = stages ? std::min<int32_t>(stages, 4)
-                       : (mode == RM_FANOUT ? 4 : (nsrc <= 4 ? 2 : 1));
+                       : (mode == RM_FANOUT ? 1 : (nsrc <= 4 ? 2 : 1));
     while (u > 1 && u * nsrc > 32)
         u /= 2;
     return u;
@@ -159,7 +166,7 @@ int32_t pick_u_copy(int32_t kind, int nseg, int32_t stages)
     if (stages)
         return stages;
     if (nseg == 1)
-        return 4;                           // one flat copy
+        return 4;                           // one flat copy: 16 KiB tiles
     return kind == CK_FANOUT ? 1 : 2;       // AllGather fan-out / AllToAll(V) exchange
 }
 
@@ -192,10 +199,10 @@ void build_reduce(Plan* p, int nsrc, const void* const* srcs, int ndst, void* co
     const int64_t ve = kVecBytes / es;   // elements per 16-byte slot
     p->vec = vec ? 1 : 0;
     p->U = vec ? pick_u_reduce(nsrc, mode, c.stages) : 1;
-    // The scatter-reduce (P loads, one store per slot) streams best from many
-    // small tiles: 64-lane workgroups measured +8% over 256 lanes on a cold
-    // 8-way reduce on MI355X, while the fan-out forms are indifferent.
-    p->wg = (vec && mode == RM_SCATTER) ? 64 : 256;
+    // The vector path streams best from many small tiles: 64-lane
+    // workgroups measured +8% over 256 lanes on a cold 8-way reduce and +5%
+    // on the fused AllReduce on MI355X.
+    p->wg = vec ? 64 : 256;
     int64_t slots = 0;
     for (int k = 0; k < nparts; ++k)
         slots += ceil_div(part_off[k + 1] - part_off[k], ve);
@@ -205,6 +212,8 @@ void build_reduce(Plan* p, int nsrc, const void* const* srcs, int ndst, void* co
         p->U = 1;
         p->wg = 64;
     }
+    if (c.lanes)
+        p->wg = c.lanes;
     const int64_t slots_per_tile = static_cast<int64_t>(p->wg) * p->U;
     int64_t t = 0;
     for (int k = 0; k < nparts; ++k) {
@@ -252,7 +261,11 @@ void build_copy(Plan* p, int32_t kind, int P, const void* const* srcs, int nsrc,
     }
     p->vec = vec ? 1 : 0;
     p->U = vec ? pick_u_copy(kind, nseg, c.stages) : 1;
-    p->wg = 256;
+    // 64-lane tiles: +7% on the exchange and +2% on the fan-out, whose
+    // tiles write P times what they read; a flat copy keeps 256-lane,
+    // 16 KiB tiles so each tile's segment lookup is amortized over enough
+    // bytes.
+    p->wg = (vec && nseg > 1) ? 64 : 256;
     int64_t bytes = 0;
     for (int s = 0; s < nseg; ++s)
         bytes += cnt[s] * row_bytes;
@@ -260,6 +273,8 @@ void build_copy(Plan* p, int32_t kind, int P, const void* const* srcs, int nsrc,
         p->U = 1;                 // latency path, as for the reduce family
         p->wg = 64;
     }
+    if (c.lanes)
+        p->wg = c.lanes;
     a.tile_bytes = static_cast<int64_t>(p->wg) * p->U * kVecBytes;
     // Aligned tiles pay off for the fan-out (measured +2-10% on MI355X); the
     // exchange moves one byte out per byte in, and aligning its destination

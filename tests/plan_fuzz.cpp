@@ -32,7 +32,7 @@ void check_reduce(const Plan& p, int iter)
     const int64_t ve = kVecBytes / p.esize;
     const int64_t ts = static_cast<int64_t>(p.wg) * p.U;
     check(a.nparts >= 1 && a.nparts <= kMaxRanks, "reduce nparts", iter);
-    check(p.wg == 64 || p.wg == 256, "reduce wg", iter);
+    check(p.wg == 64 || p.wg == 128 || p.wg == 256, "reduce wg", iter);
     check(p.vec ? (p.U == 1 || p.U == 2 || p.U == 4) : p.U == 1, "reduce U", iter);
     check(p.U * a.nsrc <= 32 || p.U == 1, "reduce registers", iter);
     int64_t t = 0;
@@ -113,6 +113,8 @@ int main(int argc, char** argv)
             cfg.ring_slots = static_cast<int32_t>(pick(0, 3) == 0 ? pick(-1, 70) : 0);
             cfg.piece_bytes = static_cast<int32_t>(pick(0, 3) == 0 ? (1 << pick(13, 22)) : 0);
             cfg.wait_us = static_cast<int32_t>(pick(0, 5) == 0 ? pick(-1, 10) : 0);
+            static const int32_t lanes[] = {0, 64, 128, 256, 0, 32, 100, 512};
+            cfg.lanes = lanes[pick(0, 7)];
         }
         Plan p;
         const atom_status st = plan_collective(&li, &lo, op, use_cfg ? &cfg : nullptr, &p);

@@ -182,7 +182,8 @@ def test_collective_validation_errors():
 @pytest.mark.parametrize("field,value", [
     ("chunk_bytes", 3 * MiB), ("chunk_bytes", 32 << 10), ("chunk_bytes", 32 * MiB),
     ("stages", 3), ("stages", 16), ("num_wgs", -1), ("flags", 0x80), ("ring_slots", 65),
-    ("ring_slots", -2), ("piece_bytes", 3000), ("piece_bytes", 8 << 10), ("wait_us", -1)])
+    ("ring_slots", -2), ("piece_bytes", 3000), ("piece_bytes", 8 << 10), ("wait_us", -1),
+    ("lanes", 32), ("lanes", 100), ("lanes", 512), ("lanes", -64)])
 def test_config_validation(field, value):
     cfg = A.config(**{field: value})
     assert Q(A.SHARD, A.GATHERED, A.OP_COPY, cfg=cfg)[0] == A.ERR_INVALID_ARG
@@ -271,6 +272,19 @@ def test_snac_default_chunk_per_collective():
                  cfg=A.config(flags=A.F_STAGED, piece_bytes=16 << 10),
                  ins=fake(8, 24 << 10), outs=fake(8, 8 * (24 << 10), start=BASE + (1 << 40)))
     assert st == A.OK and info.chunk_bytes == 32 << 10
+
+
+def test_lanes_sets_the_tile_width():
+    """lanes picks the workgroup width of the zero-staging kernels; the tile
+    (and so the workgroup count) scales with it."""
+    grids = {}
+    for lanes in (0, 64, 128, 256):
+        st, info = Q(A.PARTITIONED, A.TRANSPOSED, A.OP_COPY, P=8, n=1 << 20,
+                     cfg=A.config(lanes=lanes), ins=fake(8, 16 * MiB),
+                     outs=fake(8, 16 * MiB, start=BASE + (1 << 40)))
+        assert st == A.OK
+        grids[lanes] = info.num_wgs
+    assert grids[64] == 2 * grids[128] == 4 * grids[256]
 
 
 def test_zero_sized_collective_launches_nothing():

@@ -443,6 +443,51 @@ def test_xcd_tile_order(A, wgs):
         assert_bits_equal(from_dev(outs[j]), want, f"XCD order AG out_{j}", nan_by_class=False)
 
 
+@pytest.mark.parametrize("lanes", [64, 128, 256])
+@pytest.mark.parametrize("stages", [0, 1, 4])
+def test_lanes_and_stages(A, lanes, stages):
+    """Every workgroup width and pipeline depth tiles every collective
+    exactly: ReduceScatter, fused AllReduce, AllToAllV (ragged counts),
+    AllGatherV (Zipf partitions) and the copy, against the oracle, with
+    parts that start mid-tile."""
+    P, n = 8, 40013 * 8
+    cfg = A.config(lanes=lanes, stages=stages)
+    say(f"lanes={lanes} stages={stages}")
+    xs = [synth.mixed_bits(76, r, P * n, synth.BF16, specials=False) for r in range(P)]
+    dx = [to_dev(x)[1] for x in xs]
+    ys = [empty_dev(n, _torch_dtype(synth.BF16)) for _ in range(P)]
+    A.reduce_scatter(dx, ys, cfg)
+    ar = [empty_dev(P * n, _torch_dtype(synth.BF16)) for _ in range(P)]
+    A.all_reduce(dx, ar, cfg)
+    _sync()
+    for k, w in enumerate(oracle.reduce_scatter(xs)):
+        _assert_reduced(from_dev(ys[k]), w, f"lanes RS y_{k}")
+    want = oracle.all_reduce(xs)
+    for j in range(P):
+        _assert_reduced(from_dev(ar[j]), want[j], f"lanes AR out_{j}")
+    C = synth.random_counts(77, P, 300)
+    rows = C.sum(axis=1)
+    tx = synth.tagged_rows(P, [int(t) for t in rows], 24)
+    dtx = [to_dev(x)[1] if x.size else empty_dev(24, _torch_dtype(synth.BF16)) for x in tx]
+    R = C.sum(axis=0)
+    outs = [empty_dev(max(int(R[j]), 1) * 24, _torch_dtype(synth.BF16)) for j in range(P)]
+    A.all_to_all_v(dtx, outs, C, 24, cfg)
+    _sync()
+    for j, w in enumerate(oracle.all_to_all_v(tx, C, 24)):
+        assert_bits_equal(from_dev(outs[j])[:int(R[j]) * 24], w, f"lanes A2AV out_{j}",
+                          nan_by_class=False)
+    cnt = synth.zipf_partition(P * 5003 * 8, P, 0.125, 8) // 8
+    zs = [synth.mixed_bits(78, k, int(cnt[k]) * 8, synth.BF16) for k in range(P)]
+    dz = [to_dev(z)[1] for z in zs]
+    tot = int(cnt.sum()) * 8
+    ag = [empty_dev(tot, _torch_dtype(synth.BF16)) for _ in range(P)]
+    A.all_gather_v(dz, ag, cnt, 8, cfg)
+    _sync()
+    want = oracle.all_gather_v(zs)
+    for j in range(P):
+        assert_bits_equal(from_dev(ag[j]), want[j], f"lanes AGV out_{j}", nan_by_class=False)
+
+
 # ------------------------------------------------------------- side stream
 
 def test_side_stream(A):
