@@ -206,12 +206,13 @@ __device__ __forceinline__ void fan_out(const SnacArgs& a, const char* src, int6
     }
 }
 
-// The persistent SNAC kernel. Every branch that encloses a barrier depends
+// The persistent SNAC kernel: UP 16-byte slots per lane in flight while
+// staging, UC while fanning out. Every branch that encloses a barrier depends
 // only on wave-uniform values (the ticket and the wait result are read with
 // readfirstlane), and lane 0's work at the end of a task (the notify and the
 // next ticket claim) is one divergent region closed by a barrier, so all
 // lanes of a workgroup run the same iterations.
-template <class Stage, int U>
+template <class Stage, int UP, int UC>
 __global__ __launch_bounds__(256) void k_snac(const SnacArgs a)
 {
     __shared__ unsigned int s_ticket;
@@ -243,9 +244,9 @@ __global__ __launch_bounds__(256) void k_snac(const SnacArgs a)
         const bool ok = wait_at_least(a, wflag, target, t_begin, &s_ok);
         if (ok) {
             if (task.produce) {
-                Stage::template produce<U>(a, k, cbeg + pbeg, slotp + pbeg, plen);
+                Stage::template produce<UP>(a, k, cbeg + pbeg, slotp + pbeg, plen);
             } else {
-                fan_out<U>(a, slotp + pbeg, static_cast<int64_t>(k) * S + cbeg + pbeg, plen);
+                fan_out<UC>(a, slotp + pbeg, static_cast<int64_t>(k) * S + cbeg + pbeg, plen);
             }
         }
         // Notify: each wave of a producer waits until its write-through
@@ -289,7 +290,7 @@ hipError_t launch_ar_t(const SnacArgs& a, dim3 grid, hipStream_t stream)
     const dim3 block(256);
     switch (a.P) {
 #define ATOM_SNAC_AR_CASE(PP) \
-    case PP: k_snac<StageReduce<T, PP>, (PP <= 8 ? 2 : 1)><<<grid, block, 0, stream>>>(a); break;
+    case PP: k_snac<StageReduce<T, PP>, (PP <= 8 ? 2 : 1), 8><<<grid, block, 0, stream>>>(a); break;
     ATOM_SNAC_AR_CASE(1) ATOM_SNAC_AR_CASE(2) ATOM_SNAC_AR_CASE(3) ATOM_SNAC_AR_CASE(4)
     ATOM_SNAC_AR_CASE(5) ATOM_SNAC_AR_CASE(6) ATOM_SNAC_AR_CASE(7) ATOM_SNAC_AR_CASE(8)
     ATOM_SNAC_AR_CASE(9) ATOM_SNAC_AR_CASE(10) ATOM_SNAC_AR_CASE(11) ATOM_SNAC_AR_CASE(12)
@@ -325,10 +326,10 @@ hipError_t launch_snac(const Plan& p, const Workspace& ws, hipStream_t stream)
     const dim3 grid(static_cast<unsigned>(p.grid));
     if (p.exec == EX_SNAC_AG) {
         switch (p.U) {
-        case 1: k_snac<StageCopy, 1><<<grid, dim3(256), 0, stream>>>(a); break;
-        case 2: k_snac<StageCopy, 2><<<grid, dim3(256), 0, stream>>>(a); break;
-        case 4: k_snac<StageCopy, 4><<<grid, dim3(256), 0, stream>>>(a); break;
-        case 8: k_snac<StageCopy, 8><<<grid, dim3(256), 0, stream>>>(a); break;
+        case 1: k_snac<StageCopy, 1, 1><<<grid, dim3(256), 0, stream>>>(a); break;
+        case 2: k_snac<StageCopy, 2, 2><<<grid, dim3(256), 0, stream>>>(a); break;
+        case 4: k_snac<StageCopy, 4, 4><<<grid, dim3(256), 0, stream>>>(a); break;
+        case 8: k_snac<StageCopy, 8, 8><<<grid, dim3(256), 0, stream>>>(a); break;
         default: return hipErrorInvalidValue;
         }
         return hipGetLastError();
