@@ -445,21 +445,36 @@ def sweep(A, synth, torch, dev):
     8 KiB to 256 MiB each; the MoE route, dispatch and combine for 1 to 4096
     tokens per rank (256 experts, top-8, 7168-wide rows).
     Median of event-timed launches (more samples for small messages); GB/s
-    on credited bytes."""
+    on credited bytes. Where one call's footprint is under 1 GiB, successive
+    launches rotate over several disjoint buffer sets (at least 4, enough for
+    1 GiB up to 64) so that the 256 MB memory-side cache does not serve a
+    call from the one before."""
     P = 8
     L = A.layout
     stream = torch.cuda.current_stream()
 
-    def timed(fn, nbytes):
+    def view(t, a, b):
+        """t[a:b], refusing a slice that would run past the allocation (the
+        library takes bare pointers and sizes)."""
+        if b > t.numel():
+            raise ValueError(f"view [{a}, {b}) past a buffer of {t.numel()} elements")
+        return t[a:b]
+
+    def nsets(footprint):
+        return 1 if footprint >= (1 << 30) else min(64, max(4, -(-(1 << 30) // footprint)))
+
+    def timed(fns, nbytes):
+        fns = fns if isinstance(fns, list) else [fns]
         reps = 200 if nbytes < (1 << 24) else (20 if nbytes < (1 << 30) else 5)
-        for _ in range(3):
+        reps = max(reps, len(fns))
+        for fn in fns + fns[:3]:
             fn()
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(reps)]
-        for a, b in ev:
+        for i, (a, b) in enumerate(ev):
             a.record(stream)
-            fn()
+            fns[i % len(fns)]()
             b.record(stream)
         torch.cuda.synchronize()
         assert A.atom_sync_status() == A.OK
@@ -477,15 +492,17 @@ def sweep(A, synth, torch, dev):
     size = 8 << 10
     while size <= top:
         n = size // 2
-        zs = [t[:n] for t in z]
-        os_ = [t[:P * n] for t in out]
-        lin, lout = L(A.SHARD, zs, n), L(A.GATHERED, os_, n)
         cred = (1 + P) * P * size
-        emit("allgather", "zero-staging", size, timed(lambda: A.atom_collective(lin, lout, A.OP_COPY), size * P), cred)
+        sets = [(L(A.SHARD, [view(t, i * n, (i + 1) * n) for t in z], n),
+                 L(A.GATHERED, [view(t, i * P * n, (i + 1) * P * n) for t in out], n))
+                for i in range(nsets(cred))]
+        emit("allgather", "zero-staging", size,
+             timed([lambda l=l: A.atom_collective(l[0], l[1], A.OP_COPY) for l in sets], size * P), cred)
         for chunk in (512 << 10, 1 << 20, 2 << 20):
             cfg = A.config(flags=A.F_STAGED, chunk_bytes=chunk)
             emit("allgather", f"snac_{chunk >> 10}KiB", size,
-                 timed(lambda: A.atom_collective(lin, lout, A.OP_COPY, cfg), size * P), cred)
+                 timed([lambda l=l: A.atom_collective(l[0], l[1], A.OP_COPY, cfg) for l in sets],
+                       size * P), cred)
         size *= 2
     del z, out
     torch.cuda.empty_cache()
@@ -497,22 +514,45 @@ def sweep(A, synth, torch, dev):
     size = 8 << 10
     while size <= top:
         n = size // 2 // P
-        xs = [t[:P * n] for t in x]
-        lin = L(A.PARTITIONED, xs, n)
-        lrs, lar = L(A.SHARD, [t[:n] for t in ys], n), L(A.GATHERED, [t[:P * n] for t in ar], n)
+        m = P * n                                   # elements per rank
+        cred_ar = 2 * P * P * n * 2
+        sets = []
+        for i in range(nsets(cred_ar)):
+            lin = L(A.PARTITIONED, [view(t, i * m, (i + 1) * m) for t in x], n)
+            sets.append((lin, L(A.SHARD, [view(t, i * n, (i + 1) * n) for t in ys], n),
+                         L(A.GATHERED, [view(t, i * m, (i + 1) * m) for t in ar], n),
+                         L(A.TRANSPOSED, [view(t, i * m, (i + 1) * m) for t in ar], n)))
         emit("reducescatter", "zero-staging", size,
-             timed(lambda: A.atom_collective(lin, lrs, A.OP_SUM), size * P), (P + 1) * P * n * 2)
+             timed([lambda l=l: A.atom_collective(l[0], l[1], A.OP_SUM) for l in sets], size * P),
+             (P + 1) * P * n * 2)
         emit("allreduce", "fused", size,
-             timed(lambda: A.atom_collective(lin, lar, A.OP_SUM), size * P), 2 * P * P * n * 2)
+             timed([lambda l=l: A.atom_collective(l[0], l[2], A.OP_SUM) for l in sets], size * P), cred_ar)
         for chunk in (512 << 10, 1 << 20, 2 << 20):
             cfg = A.config(flags=A.F_STAGED, chunk_bytes=chunk)
             emit("allreduce", f"snac_{chunk >> 10}KiB", size,
-                 timed(lambda: A.atom_collective(lin, lar, A.OP_SUM, cfg), size * P), 2 * P * P * n * 2)
+                 timed([lambda l=l: A.atom_collective(l[0], l[2], A.OP_SUM, cfg) for l in sets],
+                       size * P), cred_ar)
         # uniform AllToAll of the same inputs (partition j of every source to j)
-        lat = L(A.TRANSPOSED, [t[:P * n] for t in ar], n)
         emit("alltoall", "zero-staging", size,
-             timed(lambda: A.atom_collective(lin, lat, A.OP_COPY), size * P), 2 * P * P * n * 2)
+             timed([lambda l=l: A.atom_collective(l[0], l[3], A.OP_COPY) for l in sets], size * P), cred_ar)
         size *= 2
+    # the uniform AllToAll of 8 x 4096 rows of 7168 bf16 (512 rows from every
+    # source to every destination), plain and as a V call with uniform counts
+    H = synth.HIDDEN
+    rows = 512
+    m = P * rows * H
+    C = np.full((P, P), rows, dtype=np.int64)
+    sets = [(L(A.PARTITIONED, [view(t, i * m, (i + 1) * m) for t in x], rows * H),
+             L(A.TRANSPOSED, [view(t, i * m, (i + 1) * m) for t in ar], rows * H),
+             L(A.PARTITIONED, [view(t, i * m, (i + 1) * m) for t in x], 0, C, H),
+             L(A.TRANSPOSED, [view(t, i * m, (i + 1) * m) for t in ar], 0, None, H))
+            for i in range(nsets(2 * P * m * 2))]
+    emit("alltoall", "uniform", rows * H * 2 * P,
+         timed([lambda l=l: A.atom_collective(l[0], l[1], A.OP_COPY) for l in sets], m * 2 * P),
+         2 * P * m * 2)
+    emit("alltoall", "v_uniform_counts", rows * H * 2 * P,
+         timed([lambda l=l: A.atom_collective(l[2], l[3], A.OP_COPY) for l in sets], m * 2 * P),
+         2 * P * m * 2)
     del x, ys, ar
     torch.cuda.empty_cache()
     # MoE route, dispatch and combine by tokens per rank (256 experts, top-8,
@@ -591,8 +631,7 @@ def cpu_baseline(args, C3, S, credited):
     zv = [synth.draw(4, k, int(cnt_ag[k]) * 8, "uniform", synth.BF16) for k in range(P)]
     moe_ids, moe_w = synth.moe_routing(6, P, synth.MOE_TOKENS, synth.MOE_EXPERTS, synth.MOE_TOPK)
     moe_x = synth.moe_inputs()
-    times = []
-    for _ in range(args.cpu_reps):
+    def step():
         t = time.perf_counter()
         oracle.all_gather([c2[0]])          # P = 1 AllGather: a copy
         oracle.reduce_scatter(c2)
@@ -611,12 +650,21 @@ def cpu_baseline(args, C3, S, credited):
         pos, _, recv = oracle.moe_route(moe_ids, E, k)
         disp = oracle.moe_dispatch(moe_x, moe_ids, pos, E, k, H, int(recv.max()))
         oracle.moe_combine(disp, moe_ids, pos, moe_w, E, k, H, int(recv.max()))
-        times.append(time.perf_counter() - t)
-    best = float(np.median(times))
-    return {"value": round(credited / best / 1e9, 2), "unit": "GB/s", "cores": oracle.threads(),
+        return time.perf_counter() - t
+
+    best = float(np.median([step() for _ in range(args.cpu_reps)]))
+    cores = oracle.threads()
+    oracle.set_threads(1)                   # the same step once on one core
+    try:
+        one = step()
+    finally:
+        oracle.set_threads(cores)
+    return {"value": round(credited / best / 1e9, 2), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
             "sample": f"the full step (same shapes and seeds), median of {args.cpu_reps} runs, "
-                      f"{best:.2f} s per step"}
+                      f"{best:.2f} s per step",
+            "one_core": {"value": round(credited / one / 1e9, 2), "unit": "GB/s",
+                         "sample": f"the same step once on 1 thread, {one:.2f} s"}}
 
 
 if __name__ == "__main__":

@@ -67,6 +67,8 @@ def _load():
             f.restype = ctypes.c_int
         lib.orc_threads.argtypes = []
         lib.orc_threads.restype = ctypes.c_int
+        lib.orc_set_threads.argtypes = [ctypes.c_int]
+        lib.orc_set_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -95,6 +97,12 @@ def _contig(arrays):
 
 def threads() -> int:
     return int(_load().orc_threads())
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads for later calls; every result is independent of it
+    (each output element is computed by one thread, in the fixed order)."""
+    _check(_load().orc_set_threads(int(n)), "set_threads")
 
 
 def reduce(srcs) -> np.ndarray:

@@ -302,3 +302,13 @@ int orc_threads(void)
     return 1;
 #endif
 }
+
+int orc_set_threads(int n)
+{
+    if (n < 1)
+        return 1;
+#ifdef _OPENMP
+    omp_set_num_threads(n);
+#endif
+    return 0;
+}

@@ -100,6 +100,8 @@ int orc_moe_combine(int P, int E, int k, int64_t T, const int32_t* const* ids,
 
 /* Number of OpenMP threads the loops above use. */
 int orc_threads(void);
+/* Threads used by later calls (n >= 1); results do not depend on it. */
+int orc_set_threads(int n);
 
 #ifdef __cplusplus
 }

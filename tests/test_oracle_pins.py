@@ -273,6 +273,37 @@ def test_v_variants_reduce_to_uniform():
         assert_bits_equal(a[j], b[j], "AGV uniform", nan_by_class=False)
 
 
+def test_results_do_not_depend_on_thread_count():
+    """The CPU baseline is timed with one thread and with all of them; every
+    output element is produced by one thread in the fixed order, so the bits
+    must not move with the thread count."""
+    P, n = 8, 4099
+    xs = [synth.mixed_bits(23, r, P * n, synth.BF16, specials=False) for r in range(P)]
+    C = synth.random_counts(24, P, 9)
+    rows = C.sum(axis=1)
+    a2 = [synth.mixed_bits(25, r, int(rows[r]) * 16, synth.BF16) for r in range(P)]
+    ids, w = synth.moe_routing(26, P, 40, 32, 4)
+    mx = [synth.draw(27, r, 40 * 64, "normal", synth.BF16) for r in range(P)]
+
+    def run():
+        pos, _, recv = oracle.moe_route(ids, 32, 4)
+        cap = int(recv.max())
+        disp = oracle.moe_dispatch(mx, ids, pos, 32, 4, 64, cap)
+        return (oracle.reduce_scatter(xs) + oracle.all_reduce(xs) + oracle.all_to_all_v(a2, C, 16)
+                + list(pos) + disp + oracle.moe_combine(disp, ids, pos, w, 32, 4, 64, cap))
+
+    many = oracle.threads()
+    try:
+        oracle.set_threads(1)
+        one = run()
+    finally:
+        oracle.set_threads(many)
+    for i, (a, b) in enumerate(zip(one, run())):
+        np.testing.assert_array_equal(a.view(np.uint8), b.view(np.uint8), err_msg=f"output {i}")
+    with pytest.raises(ValueError):
+        oracle.set_threads(0)
+
+
 def test_counts_draw_shape():
     C = synth.c3_counts()
     assert C.shape == (8, 8) and (C >= 0).all()
