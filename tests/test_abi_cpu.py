@@ -331,3 +331,20 @@ def test_snac_piece_spreads_medium_messages():
         assert info.chunk_bytes == want_chunk, (S, info.chunk_bytes)
         tasks = 2 * info.num_chunks * (want_chunk // piece)
         assert info.num_wgs == min(512, tasks), (S, info.num_wgs, tasks)
+
+
+def test_snac_grid_follows_the_ring_window():
+    """Without num_wgs the staged launch uses one workgroup per piece the ring
+    can hold (slots * chunk / piece), at most 512; num_wgs overrides it."""
+    S = 64 * MiB
+    for chunk, slots, piece, want in ((512 << 10, 0, 0, 512), (64 << 10, 0, 0, 64),
+                                      (256 << 10, 0, 0, 256), (512 << 10, 8, 0, 64),
+                                      (2 * MiB, 8, 32 << 10, 512), (1 * MiB, 4, 16 << 10, 256)):
+        cfg = A.config(flags=A.F_STAGED, chunk_bytes=chunk, ring_slots=slots, piece_bytes=piece)
+        st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=8, n=S // 2, cfg=cfg, ins=fake(8, S),
+                     outs=fake(8, 8 * S, start=BASE + (1 << 40)))
+        assert st == A.OK and info.num_wgs == want, (chunk, slots, piece, info.num_wgs)
+    cfg = A.config(flags=A.F_STAGED, chunk_bytes=64 << 10, num_wgs=300)
+    st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=8, n=S // 2, cfg=cfg, ins=fake(8, S),
+                 outs=fake(8, 8 * S, start=BASE + (1 << 40)))
+    assert st == A.OK and info.num_wgs == 300
