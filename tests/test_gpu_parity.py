@@ -289,17 +289,20 @@ def test_all_reduce_snac(A, P, n, dtype):
 
 def test_snac_timeout_is_reported_and_drains(A):
     """Failure handling forced from the host: a 1-microsecond wait bound on a
-    one-slot ring makes producers and consumers give up. The kernel must
-    record the timeout, drain every task and exit; atom_sync_status reports
-    it once; the next call with the default bound is complete and correct."""
+    one-slot ring shared by 512 workgroups makes producers and consumers give
+    up. The kernel must record the timeout, drain every task and exit;
+    atom_sync_status reports it once; the next call with the default bound is
+    complete and correct."""
     P, S = 8, 4 << 20
     n = S // 2
     zs = synth.c4_inputs(S, P)
     dz = [to_dev(z)[1] for z in zs]
     outs = [empty_dev(P * n, _torch_dtype(synth.BF16), 0xFFFF) for _ in range(P)]
     say("SNAC AG with a 1 us wait bound (expected timeout)")
+    # num_wgs: without it the grid follows the ring window (2 workgroups
+    # here), which rarely waits long enough to expire a 1 us bound
     A.all_gather(dz, outs, A.config(flags=A.F_STAGED, chunk_bytes=64 << 10, ring_slots=1,
-                                    wait_us=1))
+                                    wait_us=1, num_wgs=512))
     assert A.atom_sync_status() == A.ERR_TIMEOUT
     assert A.atom_sync_status() == A.OK            # reported once, then cleared
     say("SNAC AG with the default wait bound after a timeout")
