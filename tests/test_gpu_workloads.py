@@ -6,9 +6,11 @@ benchmark times (default plans):
   in seconds at this size), and the 8 AllReduce outputs bitwise identical.
 * AllToAllV MoE dispatch, 8 x 4096 x 7168 bf16 with Dirichlet-multinomial
   counts (seed 3): bit-exact against the oracle.
-* AllGather at 8 partitions of 1 GiB (the largest size), zero-staging and
-  SNAC with each chunk size: every output block equals its partition,
-  compared on the device.
+* AllGather at 8 partitions of 64 MiB (the benchmarked size), zero-staging
+  and SNAC with the default plan, bit-exact on the host; and at 8 partitions
+  of 1 GiB (the largest size), zero-staging and SNAC with each chunk size
+  and the default ring: every output block equals its partition, compared
+  on the device.
 """
 
 import numpy as np
@@ -67,15 +69,20 @@ def test_c2_all_reduce_full(A, c2):
         assert torch.equal(outs[j].view(torch.int16), outs[0].view(torch.int16)), f"AR out_{j}"
 
 
-def test_c2_all_reduce_snac_full(A, c2):
-    """The composed AllReduce through SNAC (1 MiB chunks, 4 slots) at full size."""
+@pytest.mark.parametrize("shape", ["default", "1MiB-4slots"])
+def test_c2_all_reduce_snac_full(A, c2, shape):
+    """The composed AllReduce through SNAC at full size: the library's default
+    staged plan (2 MiB chunks, 16-slot ring, as benchmarked) and a small ring
+    of 1 MiB chunks whose slots are reused 64 times each."""
     import torch
     P, N = 8, 1 << 27
-    say("c2 SNAC AllReduce 8 x 256 MiB bf16")
+    say(f"c2 SNAC AllReduce 8 x 256 MiB bf16 ({shape})")
+    cfg = (A.config(flags=A.F_STAGED) if shape == "default"
+           else A.config(flags=A.F_STAGED, chunk_bytes=1 << 20, ring_slots=4))
     want = np.concatenate(oracle.reduce_scatter(c2))
     dx = [to_dev(x)[1] for x in c2]
     outs = [empty_dev(N, torch.bfloat16) for _ in range(P)]
-    A.all_reduce(dx, outs, A.config(flags=A.F_STAGED, chunk_bytes=1 << 20, ring_slots=4))
+    A.all_reduce(dx, outs, cfg)
     assert A.atom_sync_status() == A.OK
     got = from_dev(outs[0])
     assert_bits_equal(got, want, "c2 SNAC AR out_0")
@@ -146,6 +153,25 @@ def test_c3_uniform_all_to_all(A):
         assert_bits_equal(from_dev(outs[j]), want[j], f"uniform A2A out_{j}", nan_by_class=False)
 
 
+@pytest.mark.parametrize("mode", ["zs", "snac"])
+def test_c4_all_gather_64mib(A, mode):
+    """The benchmarked AllGather: 8 partitions of 64 MiB (U[-1,1] bf16, seed 4),
+    zero-staging and staged with the default plan (512 KiB chunks, 64-slot
+    ring, 512 workgroups); every output bit-exact against the partitions."""
+    import torch
+    P, S = 8, 64 << 20
+    n = S // 2
+    say(f"c4 AllGather S=64 MiB mode={mode}")
+    zs = synth.c4_inputs(S, P)
+    dz = [to_dev(z)[1] for z in zs]
+    outs = [empty_dev(P * n, torch.bfloat16, 0xFFFF) for _ in range(P)]
+    A.all_gather(dz, outs, A.config(flags=A.F_STAGED) if mode == "snac" else None)
+    assert A.atom_sync_status() == A.OK
+    want = np.concatenate(zs)
+    for j in range(P):
+        assert_bits_equal(from_dev(outs[j]), want, f"c4 AG out_{j}", nan_by_class=False)
+
+
 @pytest.mark.parametrize("mode", ["zs", 512 << 10, 1 << 20, 2 << 20])
 def test_c4_all_gather_1gib(A, mode):
     """8 partitions of 1 GiB: 8 GiB in, 64 GiB out (inputs drawn on the host
@@ -165,7 +191,7 @@ def test_c4_all_gather_1gib(A, mode):
             z[o:o + m].copy_(torch.from_numpy(part.view(np.int16)).view(torch.bfloat16).cuda())
         dz.append(z)
     outs = [empty_dev(P * n, torch.bfloat16, 0xFFFF) for _ in range(P)]
-    cfg = None if mode == "zs" else A.config(flags=A.F_STAGED, chunk_bytes=mode, ring_slots=4)
+    cfg = None if mode == "zs" else A.config(flags=A.F_STAGED, chunk_bytes=mode)
     A.all_gather(dz, outs, cfg)
     assert A.atom_sync_status() == A.OK
     for j in range(P):
