@@ -40,6 +40,15 @@
  *  - Calls that use the per-device workspace (the SNAC staging ring and its
  *    flags) are ordered by their stream; two such calls on different streams
  *    of one device must not overlap in time.
+ *  - HIP graph capture: every call only launches kernels on `stream` (no
+ *    memset, no host synchronization), so calls can be captured and
+ *    replayed. The workspace is allocated on a device's first staged call
+ *    and grows when a call needs a larger ring; a staged call that would
+ *    have to allocate while `stream` is being captured returns
+ *    ATOM_ERR_UNSUPPORTED and enqueues nothing, so make one eager call of
+ *    the largest staged configuration first. The workspace only grows, and
+ *    replaced rings stay allocated until the process ends, so a captured
+ *    graph stays valid after later calls.
  */
 #ifndef ATOM_H
 #define ATOM_H

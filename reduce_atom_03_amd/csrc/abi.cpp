@@ -6,7 +6,9 @@
 // use and kept until the process ends.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <mutex>
+#include <vector>
 
 #include "launch.hpp"
 #include "plan.hpp"
@@ -27,8 +29,25 @@ atom_status hip_status(hipError_t e)
     return ATOM_ERR_HIP;
 }
 
+// Rings replaced by a larger one. They are never freed: a HIP graph captured
+// earlier keeps the address of the ring it was captured with, and work still
+// in flight on any stream may use it. Rings grow at least twofold, so the
+// retired ones together are smaller than the current one.
+std::vector<char*> g_retired_rings;
+
+// True when `stream` is being captured into a HIP graph (allocation is not
+// allowed then; the caller is told to make one eager call first).
+atom_status capturing(hipStream_t stream, bool* yes)
+{
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipError_t e = hipStreamIsCapturing(stream, &cs); e != hipSuccess)
+        return hip_status(e);
+    *yes = cs != hipStreamCaptureStatusNone;
+    return ATOM_OK;
+}
+
 // The workspace of the current device, with a ring of at least ring_bytes.
-atom_status workspace(int64_t ring_bytes, Workspace** out)
+atom_status workspace(int64_t ring_bytes, hipStream_t stream, Workspace** out)
 {
     int dev = 0;
     if (hipError_t e = hipGetDevice(&dev); e != hipSuccess)
@@ -37,6 +56,13 @@ atom_status workspace(int64_t ring_bytes, Workspace** out)
         return ATOM_ERR_UNSUPPORTED;
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace& ws = g_ws[dev];
+    if (!ws.ready || ws.ring_bytes < ring_bytes) {
+        bool cap = false;
+        if (atom_status st = capturing(stream, &cap); st != ATOM_OK)
+            return st;
+        if (cap)
+            return ATOM_ERR_UNSUPPORTED;
+    }
     if (!ws.ready) {
         int khz = 0;
         if (hipError_t e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
@@ -62,19 +88,20 @@ atom_status workspace(int64_t ring_bytes, Workspace** out)
         ws.error = reinterpret_cast<unsigned int*>(flags + (2 * kMaxSlots + 1) * line);
     }
     if (ws.ring_bytes < ring_bytes) {
-        // Growing the ring: wait for work that may still use the old one.
-        if (ws.ring) {
-            if (hipError_t e = hipDeviceSynchronize(); e != hipSuccess)
-                return hip_status(e);
-            (void)hipFree(ws.ring);
-            ws.ring = nullptr;
-            ws.ring_bytes = 0;
-        }
+        const int64_t want = std::max(ring_bytes, 2 * ws.ring_bytes);
         char* ring = nullptr;
-        if (hipMalloc(&ring, static_cast<size_t>(ring_bytes)) != hipSuccess)
+        if (hipMalloc(&ring, static_cast<size_t>(want)) != hipSuccess)
             return ATOM_ERR_NOMEM;
+        if (ws.ring) {
+            try {
+                g_retired_rings.push_back(ws.ring);
+            } catch (...) {             // no exception crosses the C ABI
+                (void)hipFree(ring);
+                return ATOM_ERR_NOMEM;
+            }
+        }
         ws.ring = ring;
-        ws.ring_bytes = ring_bytes;
+        ws.ring_bytes = want;
     }
     *out = &ws;
     return ATOM_OK;
@@ -101,7 +128,7 @@ atom_status run(const Plan& p, void* stream)
     case EX_SNAC_AG:
     case EX_SNAC_AR: {
         Workspace* ws = nullptr;
-        atom_status st = workspace(p.ring_bytes, &ws);
+        atom_status st = workspace(p.ring_bytes, s, &ws);
         if (st != ATOM_OK)
             return st;
         e = launch_snac(p, *ws, s);

@@ -149,3 +149,87 @@ def test_captured_sequence_replays_match_the_oracle(A):
         g.replay()
         check(inp, f"replay {rep}")
         del junk
+
+
+def _ag_inputs(torch, P, n, seed):
+    zs = synth.ranks(seed, P, n, "uniform", synth.BF16)
+    dz = [torch.zeros(n, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    for k in range(P):
+        _bits_to_dev(torch, zs[k], dz[k])
+    return zs, dz
+
+
+def test_graph_survives_workspace_growth(A):
+    """A staged call captured with the current staging ring, then an eager call
+    that needs a larger ring (the workspace grows): the earlier ring stays
+    allocated, so the captured graph still replays correctly."""
+    import torch
+    P, n = 8, 32 << 10                                  # 64 KiB partitions
+    small = A.config(flags=A.F_STAGED, chunk_bytes=64 << 10, ring_slots=2)
+    outs = [torch.zeros(P * n, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    zs, dz = _ag_inputs(torch, P, n, 500)
+    say("graph growth: eager small-ring AllGather")
+    A.all_gather(dz, outs, small)
+    assert A.atom_sync_status() == A.OK
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            A.all_gather(dz, outs, small)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    # an eager call whose ring (8 slots of 1 MiB) is larger than any before
+    say("graph growth: eager large-ring AllGather")
+    m = 1 << 20
+    zb, dzb = _ag_inputs(torch, P, m, 501)
+    outb = [torch.zeros(P * m, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    A.all_gather(dzb, outb, A.config(flags=A.F_STAGED, chunk_bytes=1 << 20, ring_slots=8))
+    assert A.atom_sync_status() == A.OK
+    want = np.concatenate(zb)
+    for j in range(P):
+        assert_bits_equal(from_dev(outb[j]), want, f"large ring out_{j}", nan_by_class=False)
+    for rep, seed in enumerate((502, 503)):
+        say(f"graph growth: replay {rep}")
+        zs, new = _ag_inputs(torch, P, n, seed)
+        for k in range(P):
+            dz[k].copy_(new[k])
+        g.replay()
+        torch.cuda.synchronize()
+        assert A.atom_sync_status() == A.OK
+        want = np.concatenate(zs)
+        for j in range(P):
+            assert_bits_equal(from_dev(outs[j]), want, f"replay {rep} out_{j}", nan_by_class=False)
+
+
+def test_capture_refuses_workspace_allocation(A):
+    """A staged call that would have to allocate a larger ring while its stream
+    is being captured returns ATOM_ERR_UNSUPPORTED and enqueues nothing; the
+    same call made eagerly afterwards runs and is correct."""
+    import torch
+    P, n = 8, 8 << 20                                   # 16 MiB partitions
+    big = A.config(flags=A.F_STAGED, chunk_bytes=16 << 20, ring_slots=64)   # 1 GiB ring
+    zs, dz = _ag_inputs(torch, P, n, 510)
+    outs = [torch.zeros(P * n, dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    marker = torch.zeros(1, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    say("capture: staged call needing a 1 GiB ring")
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            st = A.all_gather(dz, outs, big, check=False)
+            marker.add_(1)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert st == A.ERR_UNSUPPORTED
+    g.replay()
+    torch.cuda.synchronize()
+    assert float(marker.item()) == 1.0
+    assert all(int(o.view(torch.int16).abs().sum().item()) == 0 for o in outs)   # nothing ran
+    say("capture: the same call eagerly")
+    A.all_gather(dz, outs, big)
+    assert A.atom_sync_status() == A.OK
+    want = np.concatenate(zs)
+    for j in range(P):
+        assert_bits_equal(from_dev(outs[j]), want, f"eager big ring out_{j}", nan_by_class=False)
