@@ -146,9 +146,12 @@ typedef struct atom_config {
                                   1 s. On expiry the kernel records a timeout
                                   (see atom_sync_status), drops the waiting
                                   task and drains; the output is incomplete. */
-    int32_t lanes;             /* threads per workgroup of the zero-staging
-                                  kernels: 64, 128 or 256 (0: chosen per
-                                  collective and size) */
+    int32_t lanes;             /* threads per workgroup: 64, 128 or 256, and
+                                  for staged calls also 512 (a wider
+                                  zero-staging request is
+                                  ATOM_ERR_UNSUPPORTED); 0: chosen per
+                                  collective and size (staged: 256 for
+                                  AllGather, 512 for AllReduce) */
 } atom_config;
 
 /* The collective that a pair of layouts and an op names (Figure 4/6,

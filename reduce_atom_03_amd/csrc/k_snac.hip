@@ -207,13 +207,14 @@ __device__ __forceinline__ void fan_out(const SnacArgs& a, const char* src, int6
 }
 
 // The persistent SNAC kernel: UP 16-byte slots per lane in flight while
-// staging, UC while fanning out. Every branch that encloses a barrier depends
+// staging, UC while fanning out, at most MAXT lanes per workgroup (256, or
+// 512 for the wide launches, so the default keeps its register budget). Every branch that encloses a barrier depends
 // only on wave-uniform values (the ticket and the wait result are read with
 // readfirstlane), and lane 0's work at the end of a task (the notify and the
 // next ticket claim) is one divergent region closed by a barrier, so all
 // lanes of a workgroup run the same iterations.
-template <class Stage, int UP, int UC>
-__global__ __launch_bounds__(256) void k_snac(const SnacArgs a)
+template <class Stage, int UP, int UC, int MAXT>
+__global__ __launch_bounds__(MAXT) void k_snac(const SnacArgs a)
 {
     __shared__ unsigned int s_ticket;
     __shared__ int s_ok;
@@ -284,13 +285,14 @@ __global__ void k_snac_reset(unsigned long long* ready, unsigned long long* free
         *ticket = 0;
 }
 
-template <typename T>
-hipError_t launch_ar_t(const SnacArgs& a, dim3 grid, hipStream_t stream)
+// The reducing stage keeps P * UP loads in flight per lane: UP = 2 up to
+// P = 8, 1 for more inputs.
+template <typename T, int MAXT>
+hipError_t launch_ar_t(const SnacArgs& a, dim3 grid, dim3 block, hipStream_t stream)
 {
-    const dim3 block(256);
     switch (a.P) {
 #define ATOM_SNAC_AR_CASE(PP) \
-    case PP: k_snac<StageReduce<T, PP>, (PP <= 8 ? 2 : 1), 8><<<grid, block, 0, stream>>>(a); break;
+    case PP: k_snac<StageReduce<T, PP>, (PP <= 8 ? 2 : 1), 8, MAXT><<<grid, block, 0, stream>>>(a); break;
     ATOM_SNAC_AR_CASE(1) ATOM_SNAC_AR_CASE(2) ATOM_SNAC_AR_CASE(3) ATOM_SNAC_AR_CASE(4)
     ATOM_SNAC_AR_CASE(5) ATOM_SNAC_AR_CASE(6) ATOM_SNAC_AR_CASE(7) ATOM_SNAC_AR_CASE(8)
     ATOM_SNAC_AR_CASE(9) ATOM_SNAC_AR_CASE(10) ATOM_SNAC_AR_CASE(11) ATOM_SNAC_AR_CASE(12)
@@ -307,7 +309,7 @@ hipError_t launch_snac(const Plan& p, const Workspace& ws, hipStream_t stream)
 {
     if ((p.exec != EX_SNAC_AG && p.exec != EX_SNAC_AR) || !ws.ring || ws.ring_bytes < p.ring_bytes ||
         p.grid < 1 || p.sa.slots < 1 || p.sa.slots > kMaxSlots || p.sa.pieces < 1 || p.sa.P < 1 ||
-        p.sa.P > kMaxRanks || ws.wall_khz <= 0)
+        p.sa.P > kMaxRanks || ws.wall_khz <= 0 || p.wg < 64 || p.wg > 512 || p.wg % 64 != 0)
         return hipErrorInvalidValue;
     SnacArgs a = p.sa;
     a.ring = ws.ring;
@@ -323,18 +325,28 @@ hipError_t launch_snac(const Plan& p, const Workspace& ws, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    const dim3 grid(static_cast<unsigned>(p.grid));
+    const dim3 grid(static_cast<unsigned>(p.grid)), block(static_cast<unsigned>(p.wg));
+    const bool wide = p.wg > 256;
     if (p.exec == EX_SNAC_AG) {
+#define ATOM_SNAC_AG_CASE(UU)                                                              \
+    case UU:                                                                               \
+        if (wide)                                                                          \
+            k_snac<StageCopy, UU, UU, 512><<<grid, block, 0, stream>>>(a);                 \
+        else                                                                               \
+            k_snac<StageCopy, UU, UU, 256><<<grid, block, 0, stream>>>(a);                 \
+        break;
         switch (p.U) {
-        case 1: k_snac<StageCopy, 1, 1><<<grid, dim3(256), 0, stream>>>(a); break;
-        case 2: k_snac<StageCopy, 2, 2><<<grid, dim3(256), 0, stream>>>(a); break;
-        case 4: k_snac<StageCopy, 4, 4><<<grid, dim3(256), 0, stream>>>(a); break;
-        case 8: k_snac<StageCopy, 8, 8><<<grid, dim3(256), 0, stream>>>(a); break;
+        ATOM_SNAC_AG_CASE(1) ATOM_SNAC_AG_CASE(2) ATOM_SNAC_AG_CASE(4) ATOM_SNAC_AG_CASE(8)
         default: return hipErrorInvalidValue;
         }
+#undef ATOM_SNAC_AG_CASE
         return hipGetLastError();
     }
-    return p.dtype == DT_BF16 ? launch_ar_t<uint16_t>(a, grid, stream) : launch_ar_t<float>(a, grid, stream);
+    if (p.dtype == DT_BF16)
+        return wide ? launch_ar_t<uint16_t, 512>(a, grid, block, stream)
+                    : launch_ar_t<uint16_t, 256>(a, grid, block, stream);
+    return wide ? launch_ar_t<float, 512>(a, grid, block, stream)
+                : launch_ar_t<float, 256>(a, grid, block, stream);
 }
 
 }  // namespace atom

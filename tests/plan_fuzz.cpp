@@ -113,8 +113,8 @@ int main(int argc, char** argv)
             cfg.ring_slots = static_cast<int32_t>(pick(0, 3) == 0 ? pick(-1, 70) : 0);
             cfg.piece_bytes = static_cast<int32_t>(pick(0, 3) == 0 ? (1 << pick(13, 22)) : 0);
             cfg.wait_us = static_cast<int32_t>(pick(0, 5) == 0 ? pick(-1, 10) : 0);
-            static const int32_t lanes[] = {0, 64, 128, 256, 0, 32, 100, 512};
-            cfg.lanes = lanes[pick(0, 7)];
+            static const int32_t lanes[] = {0, 64, 128, 256, 0, 32, 100, 512, 1024, 2048};
+            cfg.lanes = lanes[pick(0, 9)];
         }
         Plan p;
         const atom_status st = plan_collective(&li, &lo, op, use_cfg ? &cfg : nullptr, &p);
@@ -135,6 +135,8 @@ int main(int argc, char** argv)
                   "snac pieces", iter);
             check(p.sa.ntasks == 2 * p.sa.nchunks * p.sa.pieces, "snac tasks", iter);
             check(p.ring_bytes == p.sa.chunk_bytes * p.sa.slots, "snac ring", iter);
+            check(p.wg >= 64 && p.wg <= 512 && p.wg % 64 == 0, "snac wg", iter);
+            check(!use_cfg || cfg.lanes == 0 || p.wg == cfg.lanes, "snac lanes", iter);
         }
     }
     // a few copies and flat reduces

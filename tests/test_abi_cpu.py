@@ -183,7 +183,7 @@ def test_collective_validation_errors():
     ("chunk_bytes", 3 * MiB), ("chunk_bytes", 32 << 10), ("chunk_bytes", 32 * MiB),
     ("stages", 3), ("stages", 16), ("num_wgs", -1), ("flags", 0x80), ("ring_slots", 65),
     ("ring_slots", -2), ("piece_bytes", 3000), ("piece_bytes", 8 << 10), ("wait_us", -1),
-    ("lanes", 32), ("lanes", 100), ("lanes", 512), ("lanes", -64)])
+    ("lanes", 32), ("lanes", 100), ("lanes", 384), ("lanes", 1024), ("lanes", -64)])
 def test_config_validation(field, value):
     cfg = A.config(**{field: value})
     assert Q(A.SHARD, A.GATHERED, A.OP_COPY, cfg=cfg)[0] == A.ERR_INVALID_ARG
@@ -348,3 +348,14 @@ def test_snac_grid_follows_the_ring_window():
     st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=8, n=S // 2, cfg=cfg, ins=fake(8, S),
                  outs=fake(8, 8 * S, start=BASE + (1 << 40)))
     assert st == A.OK and info.num_wgs == 300
+
+
+def test_wide_workgroups_only_for_the_staged_kernel():
+    """512 lanes exist only for the staged kernel: accepted with
+    ATOM_F_STAGED, ATOM_ERR_UNSUPPORTED for the zero-staging kernels."""
+    for lanes in (512,):
+        assert Q(A.SHARD, A.GATHERED, A.OP_COPY, cfg=A.config(lanes=lanes))[0] == A.ERR_UNSUPPORTED
+        assert Q(A.PARTITIONED, A.SHARD, A.OP_SUM, cfg=A.config(lanes=lanes))[0] == A.ERR_UNSUPPORTED
+        for op, lin in ((A.OP_COPY, A.SHARD), (A.OP_SUM, A.PARTITIONED)):
+            st, info = Q(lin, A.GATHERED, op, cfg=A.config(flags=A.F_STAGED, lanes=lanes))
+            assert st == A.OK and info.staged == 1, (lanes, op)

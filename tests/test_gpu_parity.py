@@ -229,6 +229,26 @@ def test_all_gather_snac(A, S, chunk, slots):
                                dz[k].view(torch.int16)), f"SNAC AG out_{j} block {k}"
 
 
+@pytest.mark.parametrize("lanes", [64, 128, 512])
+@pytest.mark.parametrize("S", [64 << 10, (1 << 20) + (48 << 10)])
+@pytest.mark.parametrize("slots", [1, 4])
+def test_all_gather_snac_lanes(A, S, slots, lanes):
+    """The staged AllGather at every workgroup width other than its default."""
+    say(f"SNAC AG S={S} slots={slots} lanes={lanes}")
+    P = 8
+    n = S // 2
+    zs = synth.c4_inputs(S, P)
+    dz = [to_dev(z)[1] for z in zs]
+    fulls, outs = out_buffers([P * n] * P, _torch_dtype(synth.BF16), GUARD)
+    A.all_gather(dz, outs, A.config(flags=A.F_STAGED, chunk_bytes=512 << 10, ring_slots=slots,
+                                    lanes=lanes))
+    assert A.atom_sync_status() == A.OK
+    want = np.concatenate(zs)
+    for j in range(P):
+        assert_bits_equal(from_dev(outs[j]), want, f"SNAC AG lanes out_{j}", nan_by_class=False)
+    check_guards(fulls, [P * n] * P, GUARD)
+
+
 @pytest.mark.parametrize("wgs", [1, 2, 3, 7, 64])
 def test_all_gather_snac_small_grids(A, wgs):
     """Fewer workgroups than ring slots or pieces: ticket order must still
@@ -265,21 +285,23 @@ def test_all_gather_snac_repeated(A):
             assert_bits_equal(from_dev(outs[j]), want, f"rep {rep} out_{j}", nan_by_class=False)
 
 
+@pytest.mark.parametrize("lanes", [0, 256])
 @pytest.mark.parametrize("dtype", [synth.BF16, synth.F32])
 @pytest.mark.parametrize("P", [1, 2, 3, 8, 16])
 @pytest.mark.parametrize("n", [8, 40000, 300000])
-def test_all_reduce_snac(A, P, n, dtype):
+def test_all_reduce_snac(A, P, n, dtype, lanes):
     """Composed AllReduce through SNAC (Figure 6): the reduced chunk of each
-    partition is staged once and fanned out; same bits as the oracle."""
+    partition is staged once and fanned out; same bits as the oracle. Both
+    workgroup widths: the default (512 lanes) and 256."""
     es = 2 if dtype == synth.BF16 else 4
     if (n * es) % 16:
         pytest.skip("the staged path needs 16-byte partitions")
-    say(f"SNAC AR P={P} n={n} {dtype}")
+    say(f"SNAC AR P={P} n={n} {dtype} lanes={lanes}")
     xs = [synth.mixed_bits(39, r, P * n, dtype, specials=False) for r in range(P)]
     want = oracle.all_reduce(xs)
     dx = [to_dev(x)[1] for x in xs]
     fulls, outs = out_buffers([P * n] * P, _torch_dtype(dtype), GUARD)
-    cfg = A.config(flags=A.F_STAGED, chunk_bytes=64 << 10, ring_slots=3)
+    cfg = A.config(flags=A.F_STAGED, chunk_bytes=64 << 10, ring_slots=3, lanes=lanes)
     A.all_reduce(dx, outs, cfg)
     assert A.atom_sync_status() == A.OK
     for j in range(P):

@@ -42,8 +42,10 @@ def _kernels(text):
 
 def test_every_snac_kernel_is_present(asm):
     names = [n for n, _ in _kernels(asm)]
-    assert any("StageCopy" in n for n in names)
-    assert sum("StageReduce" in n for n in names) == 32      # 2 dtypes x P = 1..16
+    # 4 pipeline depths x 2 workgroup bounds (256, 512 lanes)
+    assert sum("StageCopy" in n for n in names) == 8
+    # 2 dtypes x P = 1..16 x 2 workgroup bounds
+    assert sum("StageReduce" in n for n in names) == 64
 
 
 def test_no_divergent_loop_exit(asm):
