@@ -303,11 +303,16 @@ atom_status atom_moe_route(const atom_moe_routing* rt, void* stream);
  * capacity_rows rows each (rows no entry lands on are not written). Uses
  * the positions of the last atom_moe_route on rt. Rows at or beyond
  * capacity_rows are dropped; recv_rows tells how many would land. Needs
- * 16-byte aligned buffers and rows (else ATOM_ERR_UNSUPPORTED). Returns
- * ATOM_OK, ATOM_ERR_INVALID_ARG, ATOM_ERR_UNSUPPORTED or ATOM_ERR_HIP. */
+ * 16-byte aligned buffers and rows (else ATOM_ERR_UNSUPPORTED). cfg may be
+ * NULL (defaults); of its fields lanes (64, 128, 256), stages (16-byte
+ * slots per lane per tile), num_wgs and ATOM_F_NO_NT apply, the SNAC fields
+ * are ignored, and ATOM_F_STAGED or ATOM_F_XCD_ORDER is
+ * ATOM_ERR_UNSUPPORTED. Returns ATOM_OK, ATOM_ERR_INVALID_ARG,
+ * ATOM_ERR_UNSUPPORTED or ATOM_ERR_HIP. */
 atom_status atom_moe_dispatch(const atom_moe_routing* rt, const void* const* x,
                               void* const* out, int64_t capacity_rows,
-                              int64_t row_elems, atom_dtype dtype, void* stream);
+                              int64_t row_elems, atom_dtype dtype,
+                              const atom_config* cfg, void* stream);
 
 /* Combine: out[r] row t = round(sum over c of weights[r][t*k + c] * y row),
  * the y row being row positions[r][i] of y[j] for the entry's rank j;
@@ -315,11 +320,11 @@ atom_status atom_moe_dispatch(const atom_moe_routing* rt, const void* const* x,
  * skipped. y: host array of P device pointers to capacity_rows rows (the
  * expert outputs, in dispatch layout); weights: host array of P device
  * pointers to T*k float; out: host array of P device pointers to T rows.
- * Same alignment rule and return codes as atom_moe_dispatch. */
+ * Same alignment rule, cfg fields and return codes as atom_moe_dispatch. */
 atom_status atom_moe_combine(const atom_moe_routing* rt, const void* const* y,
                              const float* const* weights, void* const* out,
                              int64_t capacity_rows, int64_t row_elems,
-                             atom_dtype dtype, void* stream);
+                             atom_dtype dtype, const atom_config* cfg, void* stream);
 
 /* Library version, (major << 16) | minor. */
 int32_t atom_version(void);

@@ -148,10 +148,11 @@ def _load() -> ctypes.CDLL:
     lib.atom_moe_scratch_bytes.restype = ctypes.c_int64
     lib.atom_moe_route.argtypes = [rp, vp]
     lib.atom_moe_route.restype = ctypes.c_int
-    lib.atom_moe_dispatch.argtypes = [rp, vpp, vpp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, vp]
+    lib.atom_moe_dispatch.argtypes = [rp, vpp, vpp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                      ctypes.POINTER(AtomConfig), vp]
     lib.atom_moe_dispatch.restype = ctypes.c_int
     lib.atom_moe_combine.argtypes = [rp, vpp, vpp, vpp, ctypes.c_int64, ctypes.c_int64,
-                                     ctypes.c_int, vp]
+                                     ctypes.c_int, ctypes.POINTER(AtomConfig), vp]
     lib.atom_moe_combine.restype = ctypes.c_int
     return lib
 
@@ -410,24 +411,26 @@ def atom_moe_route(rt: AtomMoeRouting, stream=None, check: bool = True) -> int:
 
 def atom_moe_dispatch(rt: AtomMoeRouting, x: Sequence, out: Sequence, capacity_rows: int,
                       row_elems: int, dtype: Optional[int] = None, stream=None,
-                      check: bool = True) -> int:
+                      check: bool = True, cfg: Optional[AtomConfig] = None) -> int:
     xa, xp = _ptr_array(x)
     oa, op = _ptr_array(out)
     if dtype is None:
         dtype = _dtype_code(x[0])
     st = lib.atom_moe_dispatch(ctypes.byref(rt), xp, op, int(capacity_rows), int(row_elems),
-                               dtype, _stream(stream, out[0] if out else None))
+                               dtype, ctypes.byref(cfg) if cfg is not None else None,
+                               _stream(stream, out[0] if out else None))
     return _check(st, "atom_moe_dispatch", check)
 
 
 def atom_moe_combine(rt: AtomMoeRouting, y: Sequence, weights: Sequence, out: Sequence,
                      capacity_rows: int, row_elems: int, dtype: Optional[int] = None,
-                     stream=None, check: bool = True) -> int:
+                     stream=None, check: bool = True, cfg: Optional[AtomConfig] = None) -> int:
     ya, yp = _ptr_array(y)
     wa, wp = _ptr_array(weights)
     oa, op = _ptr_array(out)
     if dtype is None:
         dtype = _dtype_code(out[0])
     st = lib.atom_moe_combine(ctypes.byref(rt), yp, wp, op, int(capacity_rows), int(row_elems),
-                              dtype, _stream(stream, out[0] if out else None))
+                              dtype, ctypes.byref(cfg) if cfg is not None else None,
+                              _stream(stream, out[0] if out else None))
     return _check(st, "atom_moe_combine", check)

@@ -223,10 +223,12 @@ atom_status atom_moe_route(const atom_moe_routing* rt, void* stream)
 }
 
 atom_status atom_moe_dispatch(const atom_moe_routing* rt, const void* const* x, void* const* out,
-                              int64_t capacity_rows, int64_t row_elems, atom_dtype dtype, void* stream)
+                              int64_t capacity_rows, int64_t row_elems, atom_dtype dtype,
+                              const atom_config* cfg, void* stream)
 {
     atom::MoeMovePlan p;
-    atom_status st = atom::plan_moe_move(rt, false, x, nullptr, out, capacity_rows, row_elems, dtype, &p);
+    atom_status st =
+        atom::plan_moe_move(rt, false, x, nullptr, out, capacity_rows, row_elems, dtype, cfg, &p);
     if (st != ATOM_OK)
         return st;
     (void)hipGetLastError();
@@ -235,10 +237,11 @@ atom_status atom_moe_dispatch(const atom_moe_routing* rt, const void* const* x, 
 
 atom_status atom_moe_combine(const atom_moe_routing* rt, const void* const* y, const float* const* weights,
                              void* const* out, int64_t capacity_rows, int64_t row_elems, atom_dtype dtype,
-                             void* stream)
+                             const atom_config* cfg, void* stream)
 {
     atom::MoeMovePlan p;
-    atom_status st = atom::plan_moe_move(rt, true, y, weights, out, capacity_rows, row_elems, dtype, &p);
+    atom_status st =
+        atom::plan_moe_move(rt, true, y, weights, out, capacity_rows, row_elems, dtype, cfg, &p);
     if (st != ATOM_OK)
         return st;
     (void)hipGetLastError();

@@ -24,7 +24,8 @@
 //                earlier ranks and (a prefix sum over the experts) the rows
 //                of the earlier experts of the same rank, built once per
 //                workgroup; position = those + chunk prefix + rank in chunk.
-// Movement (HBM bound, one tile per token row):
+// Movement (HBM bound; a tile is one piece of a token row, 64 lanes by
+// default, so that many small workgroups keep each CU's memory queue full):
 //   k_moe_dispatch  the token row is loaded once (16-byte vectors) and
 //                   stored once per valid choice (non-temporal);
 //   k_moe_combine   the k rows of a token are loaded together, then
@@ -339,38 +340,44 @@ __device__ __forceinline__ Choices<KMAX> token_choices(const MoeMoveArgs& a, int
     return ch;
 }
 
+// A tile is one piece of one token row: piece_bytes = blockDim.x * U * 16
+// bytes starting at piece * piece_bytes (the row's last piece may be short).
+__device__ __forceinline__ int64_t piece_of(const MoeMoveArgs& a, int64_t tile, int* r, int64_t* t)
+{
+    const int64_t tok = tile / a.pieces;
+    token_of(a, tok, r, t);
+    return (tile - tok * a.pieces) * a.piece_bytes;
+}
+
 template <int KMAX, int U>
 __global__ __launch_bounds__(256) void k_moe_dispatch(const MoeMoveArgs a)
 {
     const int lane = threadIdx.x;
     const int nthr = blockDim.x;
     const bool nt = a.nt_store != 0;
-    const int64_t step = static_cast<int64_t>(nthr) * U * kVecBytes;
     for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
         int r;
         int64_t t;
-        token_of(a, tile, &r, &t);
-        const Choices<KMAX> ch = token_choices<KMAX>(a, r, t, a.dst, false);
-        if (ch.live == 0)
-            continue;
+        const int64_t b0 = piece_of(a, tile, &r, &t);
+        // The token's own row does not depend on the routing: its loads are
+        // issued before the choices are read, so the two latencies overlap.
         const char* src = a.src[r] + t * a.row_bytes;
-        for (int64_t b0 = 0; b0 < a.row_bytes; b0 += step) {
-            u32x4 x[U];
+        u32x4 x[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t o = b0 + static_cast<int64_t>(u * nthr + lane) * kVecBytes;
-                if (o < a.row_bytes)
-                    x[u] = ld16_stream(src + o);
-            }
+        for (int u = 0; u < U; ++u) {
+            const int64_t o = b0 + static_cast<int64_t>(u * nthr + lane) * kVecBytes;
+            if (o < a.row_bytes)
+                x[u] = ld16_stream(src + o);
+        }
+        const Choices<KMAX> ch = token_choices<KMAX>(a, r, t, a.dst, false);
 #pragma unroll
-            for (int c = 0; c < KMAX; ++c) {
-                if ((ch.live >> c) & 1u) {
+        for (int c = 0; c < KMAX; ++c) {
+            if ((ch.live >> c) & 1u) {
 #pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        const int64_t o = b0 + static_cast<int64_t>(u * nthr + lane) * kVecBytes;
-                        if (o < a.row_bytes)
-                            st16(ch.row[c] + o, x[u], nt);
-                    }
+                for (int u = 0; u < U; ++u) {
+                    const int64_t o = b0 + static_cast<int64_t>(u * nthr + lane) * kVecBytes;
+                    if (o < a.row_bytes)
+                        st16(ch.row[c] + o, x[u], nt);
                 }
             }
         }
@@ -439,10 +446,11 @@ __global__ __launch_bounds__(256) void k_moe_combine(const MoeMoveArgs a)
     for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
         int r;
         int64_t t;
-        token_of(a, tile, &r, &t);
+        const int64_t p0 = piece_of(a, tile, &r, &t);
+        const int64_t p1 = p0 + a.piece_bytes < a.row_bytes ? p0 + a.piece_bytes : a.row_bytes;
         const Choices<KMAX> ch = token_choices<KMAX>(a, r, t, const_cast<char* const*>(a.src), true);
         char* dst = a.dst[r] + t * a.row_bytes;
-        for (int64_t b0 = 0; b0 < a.row_bytes; b0 += static_cast<int64_t>(nthr) * kVecBytes) {
+        for (int64_t b0 = p0; b0 < p1; b0 += static_cast<int64_t>(nthr) * kVecBytes) {
             const int64_t o = b0 + static_cast<int64_t>(lane) * kVecBytes;
             const bool in_row = o < a.row_bytes;
             // All of the token's rows for this slot in flight at once.
@@ -498,9 +506,12 @@ hipError_t launch_moe_move(const MoeMovePlan& p, bool combine, hipStream_t strea
     const MoeMoveArgs& a = p.a;
     if (a.ntiles == 0)
         return hipSuccess;
-    if (p.grid < 1 || a.k < 1 || a.k > kMoeMaxTopk || a.per < 1 || a.row_bytes % kVecBytes != 0)
+    if (p.grid < 1 || a.k < 1 || a.k > kMoeMaxTopk || a.per < 1 || a.row_bytes % kVecBytes != 0 ||
+        p.wg < 64 || p.wg > 256 || p.wg % 64 != 0 ||
+        a.piece_bytes != static_cast<int64_t>(p.wg) * p.U * kVecBytes || a.pieces < 1 ||
+        a.pieces * a.piece_bytes < a.row_bytes)
         return hipErrorInvalidValue;
-    const dim3 grid(static_cast<unsigned>(p.grid)), block(256);
+    const dim3 grid(static_cast<unsigned>(p.grid)), block(static_cast<unsigned>(p.wg));
     const int kmax = a.k <= 2 ? 2 : a.k <= 4 ? 4 : a.k <= 8 ? 8 : 16;
     if (combine) {
         const bool bf = a.dtype == DT_BF16;
@@ -516,14 +527,20 @@ hipError_t launch_moe_move(const MoeMovePlan& p, bool combine, hipStream_t strea
 #undef ATOM_MOE_COMBINE
         }
     } else {
-        if (p.U != 4)
-            return hipErrorInvalidValue;
-        switch (kmax) {
-        case 2: k_moe_dispatch<2, 4><<<grid, block, 0, stream>>>(a); break;
-        case 4: k_moe_dispatch<4, 4><<<grid, block, 0, stream>>>(a); break;
-        case 8: k_moe_dispatch<8, 4><<<grid, block, 0, stream>>>(a); break;
-        default: k_moe_dispatch<16, 4><<<grid, block, 0, stream>>>(a); break;
+#define ATOM_MOE_DISPATCH(UU)                                                        \
+    case UU:                                                                         \
+        switch (kmax) {                                                              \
+        case 2: k_moe_dispatch<2, UU><<<grid, block, 0, stream>>>(a); break;         \
+        case 4: k_moe_dispatch<4, UU><<<grid, block, 0, stream>>>(a); break;         \
+        case 8: k_moe_dispatch<8, UU><<<grid, block, 0, stream>>>(a); break;         \
+        default: k_moe_dispatch<16, UU><<<grid, block, 0, stream>>>(a); break;       \
+        }                                                                            \
+        break;
+        switch (p.U) {
+        ATOM_MOE_DISPATCH(1) ATOM_MOE_DISPATCH(2) ATOM_MOE_DISPATCH(4) ATOM_MOE_DISPATCH(8)
+        default: return hipErrorInvalidValue;
         }
+#undef ATOM_MOE_DISPATCH
     }
     return hipGetLastError();
 }

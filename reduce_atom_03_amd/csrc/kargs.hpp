@@ -134,7 +134,9 @@ struct MoeMoveArgs {
     int64_t T;                         // tokens per rank
     int64_t cap;                       // rows of each expert-side buffer
     int64_t row_bytes;                 // multiple of 16
-    int64_t ntiles;                    // P * T
+    int64_t piece_bytes;               // bytes of a row per tile: lanes * U * 16
+    int64_t pieces;                    // tiles per token row
+    int64_t ntiles;                    // P * T * pieces
     int32_t P;
     int32_t E;
     int32_t per;

@@ -76,7 +76,8 @@ struct MoeRoutePlan {
 struct MoeMovePlan {
     MoeMoveArgs a;
     int64_t grid = 0;
-    int32_t U = 1;                     // 16-byte slots per lane per step
+    int32_t wg = 64;                   // lanes per workgroup
+    int32_t U = 1;                     // 16-byte slots per lane per tile
     int64_t credited_bytes = 0;        // when every id is valid and fits
 };
 
@@ -86,7 +87,7 @@ atom_status plan_moe_route(const atom_moe_routing* rt, MoeRoutePlan* p);
 // combine == true: combine (src = y, dst = out, w = weights).
 atom_status plan_moe_move(const atom_moe_routing* rt, bool combine, const void* const* src,
                           const float* const* w, void* const* dst, int64_t cap, int64_t row_elems,
-                          atom_dtype dtype, MoeMovePlan* p);
+                          atom_dtype dtype, const atom_config* cfg, MoeMovePlan* p);
 
 atom_status plan_copy(void* dst, const void* src, size_t bytes, const atom_config* cfg,
                       Plan* p);

@@ -212,16 +212,36 @@ int main(int argc, char** argv)
         const atom_dtype dt = static_cast<atom_dtype>(pick(0, 9) == 0 ? pick(-1, 2) : pick(0, 1));
         for (int combine = 0; combine < 2; ++combine) {
             MoeMovePlan mp;
-            if (plan_moe_move(&rt, combine != 0, xs, reinterpret_cast<const float* const*>(ws), outs,
-                              cap, row, dt, &mp) != ATOM_OK)
+            atom_config mc{};
+            const bool mcfg = pick(0, 2) == 0;
+            if (mcfg) {
+                static const int32_t mlanes[] = {0, 64, 128, 256, 512, 100};
+                mc.lanes = mlanes[pick(0, 5)];
+                mc.stages = static_cast<int32_t>(pick(0, 4) == 0 ? pick(-1, 9) : (1 << pick(0, 3)));
+                mc.num_wgs = static_cast<int32_t>(pick(0, 2) == 0 ? pick(-2, 3000) : 0);
+                mc.flags = static_cast<uint32_t>(pick(0, 8));
+            }
+            const atom_status ms = plan_moe_move(&rt, combine != 0, xs,
+                                                 reinterpret_cast<const float* const*>(ws), outs, cap,
+                                                 row, dt, mcfg ? &mc : nullptr, &mp);
+            check(ms == ATOM_OK || ms == ATOM_ERR_INVALID_ARG || ms == ATOM_ERR_UNSUPPORTED,
+                  "moe status", iter);
+            if (ms != ATOM_OK)
                 continue;
             ++ok_moe;
-            check(mp.a.ntiles == static_cast<int64_t>(P) * T, "moe tiles", iter);
+            const int64_t ntok = static_cast<int64_t>(P) * T;
+            check(mp.wg >= 64 && mp.wg <= 256 && mp.wg % 64 == 0, "moe lanes", iter);
+            check(mp.U == 1 || mp.U == 2 || mp.U == 4 || mp.U == 8, "moe U", iter);
+            check(mp.a.piece_bytes == static_cast<int64_t>(mp.wg) * mp.U * kVecBytes, "moe piece", iter);
+            check(ntok == 0 || mp.a.row_bytes == 0 ||
+                      (mp.a.pieces * mp.a.piece_bytes >= mp.a.row_bytes &&
+                       (mp.a.pieces - 1) * mp.a.piece_bytes < mp.a.row_bytes),
+                  "moe pieces cover the row", iter);
+            check(mp.a.ntiles == ntok * mp.a.pieces, "moe tiles", iter);
             check(mp.a.ntiles == 0 || (mp.grid >= 1 && mp.grid <= mp.a.ntiles), "moe grid", iter);
             check(mp.a.ntiles == 0 || mp.a.row_bytes % kVecBytes == 0, "moe row alignment", iter);
             check(mp.a.k == k && mp.a.per * P == E, "moe shape", iter);
-            check(mp.credited_bytes ==
-                      mp.a.ntiles * ((k + 1) * mp.a.row_bytes + k * (combine ? 12 : 8)),
+            check(mp.credited_bytes == ntok * ((k + 1) * mp.a.row_bytes + k * (combine ? 12 : 8)),
                   "moe credited bytes", iter);
         }
     }

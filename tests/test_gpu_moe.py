@@ -115,9 +115,26 @@ MOVE_CASES = [  # (seed, P, T, E, k, H, dtype, invalid, cap_cut)
 
 @pytest.mark.parametrize("case", MOVE_CASES, ids=lambda c: f"seed{c[0]}-P{c[1]}-T{c[2]}-k{c[4]}-H{c[5]}-{c[6]}")
 def test_dispatch_and_combine_parity(A, case):
+    _move_case(A, case, None)
+
+
+# (lanes, slots per lane): tiles of 1-4 KiB (whole 7168-wide rows are 14 KiB,
+# so every shape leaves a short last piece), and every U instantiation
+TILE_SHAPES = [(64, 1), (64, 8), (128, 4), (256, 2)]
+
+
+@pytest.mark.parametrize("shape", TILE_SHAPES, ids=lambda s: f"lanes{s[0]}-U{s[1]}")
+@pytest.mark.parametrize("case", [MOVE_CASES[0], MOVE_CASES[1], MOVE_CASES[4]],
+                         ids=lambda c: f"seed{c[0]}-H{c[5]}-{c[6]}")
+def test_dispatch_and_combine_tile_shapes(A, case, shape):
+    _move_case(A, case, A.config(lanes=shape[0], stages=shape[1]))
+
+
+def _move_case(A, case, cfg):
     import torch
     seed, P, T, E, k, H, dt, inv, cut = case
-    say(f"moe dispatch/combine P={P} T={T} E={E} k={k} H={H} {dt} invalid={inv} cut={cut}")
+    say(f"moe dispatch/combine P={P} T={T} E={E} k={k} H={H} {dt} invalid={inv} cut={cut} "
+        f"cfg={None if cfg is None else (cfg.lanes, cfg.stages)}")
     ids = ids_for(seed, P, T, E, k, inv)
     rt, _ = route_dev(A, ids, E, k)
     pos, recv = check_route(rt, ids, E, k, "route")
@@ -127,7 +144,7 @@ def test_dispatch_and_combine_parity(A, case):
     xs = [synth.mixed_bits(seed, r, T * H, dt) for r in range(P)]
     x_dev = [to_dev(x)[1] for x in xs]
     out_dev = [empty_dev(max(cap, 1) * H, tdt, sentinel) for _ in range(P)]
-    A.atom_moe_dispatch(rt, x_dev, out_dev, cap, H)
+    A.atom_moe_dispatch(rt, x_dev, out_dev, cap, H, cfg=cfg)
     want = oracle.moe_dispatch(xs, ids, pos, E, k, H, cap, fill=sentinel if dt == synth.BF16 else
                                np.uint32(sentinel).view(np.float32))
     for j in range(P):
@@ -140,7 +157,7 @@ def test_dispatch_and_combine_parity(A, case):
     w = [(g.random(T * k, dtype=np.float32) * 3 - 1).astype(np.float32) for _ in range(P)]
     w_dev = [torch.from_numpy(a).to("cuda") if a.size else torch.zeros(1, device="cuda") for a in w]
     o_dev = [empty_dev(max(T, 1) * H, tdt, 0) for _ in range(P)]
-    A.atom_moe_combine(rt, y_dev, w_dev, o_dev, cap, H)
+    A.atom_moe_combine(rt, y_dev, w_dev, o_dev, cap, H, cfg=cfg)
     want = oracle.moe_combine([y[:cap * H] if cap else y[:0] for y in ys], ids, pos, w, E, k, H, cap)
     for r in range(P):
         assert_bits_equal(from_dev(o_dev[r])[:T * H], want[r], f"combine rank {r}")

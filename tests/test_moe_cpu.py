@@ -107,3 +107,29 @@ def test_move_validation(combine):
     if combine:
         assert _move(True, rt, src, dst, cap, H, w=[BASE + (9 << 32) + 2] * P) == A.ERR_INVALID_ARG
         assert _move(True, rt, src, [rt.positions[0]] + dst[1:], cap, H) == A.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("combine", [False, True])
+def test_move_config(combine):
+    """cfg: lanes (64-256), stages, num_wgs and ATOM_F_NO_NT apply; the staged
+    and XCD-order flags and 512 lanes are unsupported; malformed values are
+    invalid. All decided on the host."""
+    P, T, k, H, cap = 4, 16, 2, 64, 40
+    rt = routing(P=P, T=T, k=k)
+    rows_src = cap if combine else T
+    rows_dst = T if combine else cap
+    src = fake(P, 2 * H * rows_src, BASE + (5 << 32))
+    dst = fake(P, 2 * H * rows_dst, BASE + (6 << 32))
+
+    def call(cfg):
+        if combine:
+            w = fake(P, 4 * T * k, BASE + (9 << 32))
+            return A.atom_moe_combine(rt, src, w, dst, cap, H, A.DT_BF16, stream=0, check=False,
+                                      cfg=cfg)
+        return A.atom_moe_dispatch(rt, src, dst, cap, H, A.DT_BF16, stream=0, check=False, cfg=cfg)
+
+    for flags in (A.F_STAGED, A.F_XCD_ORDER):
+        assert call(A.config(flags=flags)) == A.ERR_UNSUPPORTED
+    assert call(A.config(lanes=512)) == A.ERR_UNSUPPORTED
+    for bad in (A.config(lanes=96), A.config(stages=3), A.config(num_wgs=-1), A.config(flags=0x80)):
+        assert call(bad) == A.ERR_INVALID_ARG
