@@ -72,10 +72,12 @@ atom_status workspace(int64_t ring_bytes, hipStream_t stream, Workspace** out)
             return ATOM_ERR_UNSUPPORTED;
         ws.wall_khz = khz;
         // ready[kMaxSlots], freed[kMaxSlots] (each counter on its own 256-byte
-        // line), then the ticket and the error word on lines of their own.
+        // line), then the ticket, the error word and the finished-workgroup
+        // count on lines of their own. All start at zero; every staged
+        // kernel leaves them at zero (the error word excepted).
         char* flags = nullptr;
         const size_t line = kFlagStride * sizeof(unsigned long long);
-        const size_t fbytes = (2 * kMaxSlots + 2) * line;
+        const size_t fbytes = (2 * kMaxSlots + 3) * line;
         if (hipMalloc(&flags, fbytes) != hipSuccess)
             return ATOM_ERR_NOMEM;
         if (hipError_t e = hipMemset(flags, 0, fbytes); e != hipSuccess) {
@@ -86,6 +88,7 @@ atom_status workspace(int64_t ring_bytes, hipStream_t stream, Workspace** out)
         ws.freed = ws.ready + kMaxSlots * kFlagStride;
         ws.ticket = reinterpret_cast<unsigned int*>(flags + 2 * kMaxSlots * line);
         ws.error = reinterpret_cast<unsigned int*>(flags + (2 * kMaxSlots + 1) * line);
+        ws.done = reinterpret_cast<unsigned int*>(flags + (2 * kMaxSlots + 2) * line);
     }
     if (ws.ring_bytes < ring_bytes) {
         const int64_t want = std::max(ring_bytes, 2 * ws.ring_bytes);

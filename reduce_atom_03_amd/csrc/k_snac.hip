@@ -268,21 +268,28 @@ __global__ __launch_bounds__(MAXT) void k_snac(const SnacArgs a)
         __syncthreads();
         t = static_cast<unsigned int>(__builtin_amdgcn_readfirstlane(static_cast<int>(s_ticket)));
     }
-}
-
-// Clears the ticket and the slot counters before a SNAC launch (the error
-// word is kept until the host reads it). A kernel, not a memset, so the
-// sequence can be captured into a graph.
-__global__ void k_snac_reset(unsigned long long* ready, unsigned long long* freed, unsigned int* ticket,
-                             int slots)
-{
-    const int i = threadIdx.x;
-    if (i < slots) {
-        ready[i * kFlagStride] = 0;
-        freed[i * kFlagStride] = 0;
+    // Every workgroup counts itself out; the last one clears the ticket, the
+    // slot counters and the count for the next staged call on this device,
+    // so a call is one launch and a captured graph replays from a clean
+    // state. Lane 0 made all of this workgroup's counter updates; it waits
+    // until they have completed before counting out, and the last workgroup
+    // clears only after its count returned, so every update of this call
+    // precedes the clearing. The error word is kept for the host.
+    if (threadIdx.x == 0) {
+        wait_vmem();
+        const unsigned int prev =
+            __hip_atomic_fetch_add(a.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (prev == gridDim.x - 1) {
+            for (int s = 0; s < a.slots; ++s) {
+                __hip_atomic_store(a.ready + s * kFlagStride, 0ull, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(a.freed + s * kFlagStride, 0ull, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
-    if (i == 0)
-        *ticket = 0;
 }
 
 // The reducing stage keeps P * UP loads in flight per lane: UP = 2 up to
@@ -309,7 +316,8 @@ hipError_t launch_snac(const Plan& p, const Workspace& ws, hipStream_t stream)
 {
     if ((p.exec != EX_SNAC_AG && p.exec != EX_SNAC_AR) || !ws.ring || ws.ring_bytes < p.ring_bytes ||
         p.grid < 1 || p.sa.slots < 1 || p.sa.slots > kMaxSlots || p.sa.pieces < 1 || p.sa.P < 1 ||
-        p.sa.P > kMaxRanks || ws.wall_khz <= 0 || p.wg < 64 || p.wg > 512 || p.wg % 64 != 0)
+        p.sa.P > kMaxRanks || ws.wall_khz <= 0 || p.wg < 64 || p.wg > 512 || p.wg % 64 != 0 ||
+        !ws.done)
         return hipErrorInvalidValue;
     SnacArgs a = p.sa;
     a.ring = ws.ring;
@@ -317,14 +325,11 @@ hipError_t launch_snac(const Plan& p, const Workspace& ws, hipStream_t stream)
     a.freed = ws.freed;
     a.ticket = ws.ticket;
     a.error = ws.error;
+    a.done = ws.done;
     // Bounds in device-clock ticks (kHz x ms): the planned wait bound (1 s
     // unless the caller shortened it) and ~10 s per workgroup.
     a.wait_ticks = std::max<int64_t>(1, static_cast<int64_t>(ws.wall_khz) * p.sa.wait_ticks / 1000);
     a.budget_ticks = static_cast<int64_t>(ws.wall_khz) * 10000;
-    k_snac_reset<<<1, 64, 0, stream>>>(ws.ready, ws.freed, ws.ticket, a.slots);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
     const dim3 grid(static_cast<unsigned>(p.grid)), block(static_cast<unsigned>(p.wg));
     const bool wide = p.wg > 256;
     if (p.exec == EX_SNAC_AG) {

@@ -84,6 +84,8 @@ struct SnacArgs {
     unsigned long long* freed;         // per slot (stride kFlagStride): pieces consumed
     unsigned int* ticket;              // task counter
     unsigned int* error;               // nonzero after a wait timed out
+    unsigned int* done;                // workgroups finished (the last one
+                                       // clears the counters for the next call)
     int64_t part_bytes;                // bytes of each partition
     int64_t chunk_bytes;
     int64_t piece_bytes;               // chunk_bytes / pieces

@@ -16,6 +16,7 @@ struct Workspace {
     unsigned long long* freed = nullptr;   // kMaxSlots counters, kFlagStride apart
     unsigned int* ticket = nullptr;
     unsigned int* error = nullptr;
+    unsigned int* done = nullptr;
     int wall_khz = 0;                      // rate of the device's constant clock
 };
 

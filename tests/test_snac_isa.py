@@ -50,8 +50,6 @@ def test_every_snac_kernel_is_present(asm):
 
 def test_no_divergent_loop_exit(asm):
     for name, body in _kernels(asm):
-        if "k_snac_reset" in name:
-            continue
         assert "s_barrier" in body
         assert not re.search(r"s_andn2_b64\s+exec,\s*exec", body), \
             f"{name}: a loop with barriers exits on a divergent branch"
@@ -67,8 +65,6 @@ def test_ring_hand_off_needs_no_l2_maintenance(asm):
     operations, so no SNAC kernel writes back or invalidates an L2; outputs
     and inputs use ordinary global operations."""
     for name, body in _kernels(asm):
-        if "k_snac_reset" in name:
-            continue
         assert not re.search(r"buffer_wbl2|buffer_inv", body), name
         ring_ops = re.findall(r"^\s*(buffer_(?:load|store)_dwordx4[^\n]*)", body, re.M)
         assert ring_ops, f"{name}: no ring accesses"
@@ -80,8 +76,6 @@ def test_producer_waits_for_its_stores_before_notify(asm):
     """Each wave waits for vmcnt(0) after its last ring store and before the
     barrier that precedes the `ready` increment."""
     for name, body in _kernels(asm):
-        if "k_snac_reset" in name:
-            continue
         last_store = max(m.end() for m in re.finditer(r"buffer_store_dwordx4", body))
         rest = body[last_store:]
         wait = re.search(r"s_waitcnt vmcnt\(0\)", rest)
