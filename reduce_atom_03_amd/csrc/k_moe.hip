@@ -38,53 +38,37 @@ namespace atom {
 
 namespace {
 
-// Ranks one 64-entry step of entries [i0 + s*64, ...) of rank r against the
-// per-expert counters `cnt` (LDS, this wave's own): each valid entry gets
-// the number of earlier entries with its expert (earlier steps included),
-// written to pos; invalid entries get -1. The wave's (expert, lane) keys are
-// sorted across lanes (bitonic, 21 compare-exchange stages; entries routed
-// nowhere sort last), so equal experts form runs in lane order and a slot's
-// rank is its offset in its run.
-__device__ __forceinline__ void rank_step(const MoeRouteArgs& a, int r, int64_t i, int64_t i1, int e,
-                                          int32_t* cnt)
+// Ranks one 64-entry step of entries [i0 + s*64, ...) of one rank against the
+// per-expert counters `cnt` (LDS, this wave's own): returns, for a valid
+// entry, the number of earlier entries with its expert (earlier steps
+// included), and -1 for an invalid one. The callers store a batch of steps'
+// ranks together, so no store's completion is waited for between steps. The lanes holding the same expert
+// are found with one ballot per bit of the expert id (a lane keeps the
+// lanes that agree with it on every bit), so an entry's rank within the
+// step is the number of such lanes below it, and the highest of them adds
+// the group's size to the expert's counter.
+__device__ __forceinline__ int32_t rank_step(const MoeRouteArgs& a, int64_t i, int64_t i1, int e,
+                                             int32_t* cnt)
 {
-    const int lane = threadIdx.x & 63;
     const bool valid = i < i1 && e >= 0 && e < a.E;
-    int key = ((valid ? e : a.E) << 6) | lane;
-#pragma unroll
-    for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            const int other = __shfl_xor(key, j);
-            const bool keep_min = ((lane & k) == 0) == ((lane & j) == 0);
-            key = keep_min ? min(key, other) : max(key, other);
-        }
+    unsigned long long same = __ballot(valid);
+    const int nbits = a.E > 1 ? 32 - __clz(a.E - 1) : 0;     // wave-uniform
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const unsigned long long ones = __ballot(valid && bit);
+        same &= bit ? ones : ~ones;
     }
-    const int se = key >> 6;                          // expert in sorted slot `lane`
-    const bool sv = se < a.E;
-    // The run of slot `lane` starts at the largest run start at or below it.
-    const int prev = __shfl_up(se, 1);
-    int start = (lane == 0 || prev != se) ? lane : 0;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int o = __shfl_up(start, d);
-        if (lane >= d)
-            start = max(start, o);
-    }
-    const int next = __shfl_down(se, 1);
-    const bool run_end = lane == 63 || next != se;
+    const int below = __builtin_amdgcn_mbcnt_hi(static_cast<unsigned int>(same >> 32),
+                                                __builtin_amdgcn_mbcnt_lo(static_cast<unsigned int>(same), 0u));
+    const int lane = threadIdx.x & 63;
     int32_t before = 0;
-    if (sv)
-        before = cnt[se];
-    // Every slot has read its counter before any slot writes one: the wave's
+    if (valid)
+        before = cnt[e];
+    // Every lane has read its counter before any lane writes one: the wave's
     // LDS operations complete in program order.
-    if (sv && run_end)
-        cnt[se] = before + (lane - start) + 1;
-    const int32_t rank_here = sv ? before + (lane - start) : -1;
-    // Send each slot's rank back to the lane its entry came from.
-    const int32_t mine = __builtin_amdgcn_ds_permute((key & 63) << 2, rank_here);
-    if (i < i1)
-        a.pos[r][i] = valid ? mine : -1;
+    if (valid && lane == 63 - __clzll(same))
+        cnt[e] = before + __popcll(same);
+    return valid ? before + below : -1;
 }
 
 __global__ __launch_bounds__(64) void k_moe_rank(const MoeRouteArgs a)
@@ -106,42 +90,67 @@ __global__ __launch_bounds__(64) void k_moe_rank(const MoeRouteArgs a)
         ids[s] = i < i1 ? a.ids[r][i] : -1;
     }
     __syncthreads();
+    int32_t rk[kSteps];
 #pragma unroll
     for (int s = 0; s < kSteps; ++s)
-        rank_step(a, r, i0 + s * 64 + lane, i1, ids[s], cnt);
+        rk[s] = rank_step(a, i0 + s * 64 + lane, i1, ids[s], cnt);
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+        const int64_t i = i0 + s * 64 + lane;
+        if (i < i1)
+            a.pos[r][i] = rk[s];
+    }
     __syncthreads();
     int32_t* part = a.partial + (static_cast<int64_t>(r) * a.nch + ch) * a.E;
     for (int e = lane; e < a.E; e += 64)
         part[e] = cnt[e];
 }
 
-// The whole routing in one workgroup when every rank's entries fit in one
-// chunk (decode-sized batches): wave r ranks rank r's entries into its own
-// LDS counters; then the block writes the counts, scans the expert totals
-// and places every entry (earlier experts of the rank + earlier ranks +
-// rank among the rank's entries).
+// The whole routing in one workgroup for decode-sized batches: wave r
+// ranks rank r's entries, 64 at a time in entry order, into its own LDS
+// counters (so each entry's rank counts every earlier entry of the rank,
+// with no chunk partials); then the block writes the counts, scans the
+// expert totals and places every entry (earlier experts of the rank +
+// earlier ranks + rank among the rank's entries). One launch instead of
+// three.
 __global__ __launch_bounds__(1024) void k_moe_route_small(const MoeRouteArgs a)
 {
     extern __shared__ int32_t lds[];                  // [P][E] counts, [E] prefix, [nthr] partials
     const int nthr = blockDim.x;                      // 64 * P
     const int tid = threadIdx.x;
-    const int w = tid >> 6;                           // this wave's rank
+    // This wave's rank, made provably wave-uniform so that its pointers are
+    // read once into scalar registers (a per-lane index would fetch the
+    // pointer from the argument block before every access).
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int32_t* const ids_w = a.ids[w];
+    int32_t* const pos_w = a.pos[w];
     int32_t* cnt = lds;
     int32_t* incl = lds + a.P * a.E;
     int32_t* part = incl + a.E;
     for (int q = tid; q < a.P * a.E; q += nthr)
         cnt[q] = 0;
-    constexpr int kSteps = kMoeChunk / 64;
-    int ids[kSteps];
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-        const int64_t i = s * 64 + (tid & 63);
-        ids[s] = i < a.n ? a.ids[w][i] : -1;
-    }
+    const int lane = tid & 63;
+    const int64_t nsteps = (a.n + 63) / 64;           // the same for every wave
+    constexpr int kB = 16;                            // steps whose loads are in flight together
     __syncthreads();
+    for (int64_t s0 = 0; s0 < nsteps; s0 += kB) {
+        int ev[kB];
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s)
-        rank_step(a, w, s * 64 + (tid & 63), a.n, ids[s], cnt + w * a.E);
+        for (int u = 0; u < kB; ++u) {
+            const int64_t i = (s0 + u) * 64 + lane;
+            ev[u] = i < a.n ? ids_w[i] : -1;
+        }
+        int32_t rk[kB];
+#pragma unroll
+        for (int u = 0; u < kB; ++u)
+            rk[u] = s0 + u < nsteps ? rank_step(a, (s0 + u) * 64 + lane, a.n, ev[u], cnt + w * a.E) : -1;
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            const int64_t i = (s0 + u) * 64 + lane;
+            if (i < a.n)
+                pos_w[i] = rk[u];
+        }
+    }
     __syncthreads();
     // counts, and the totals of each expert over the ranks
     for (int e = tid; e < a.E; e += nthr) {
@@ -178,18 +187,28 @@ __global__ __launch_bounds__(1024) void k_moe_route_small(const MoeRouteArgs a)
             incl[e] += off;
     }
     __syncthreads();
-    for (int s = 0; s < kSteps; ++s) {
-        const int64_t i = s * 64 + (tid & 63);
-        if (i < a.n) {
-            const int32_t p = a.pos[w][i];
-            if (p >= 0) {
-                const int e = ids[s];
+    // Each lane reads back the ranks it wrote itself in the ranking loop,
+    // kB steps of loads at a time.
+    for (int64_t s0 = 0; s0 < nsteps; s0 += kB) {
+        int32_t pv[kB];
+        int ev[kB];
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            const int64_t i = (s0 + u) * 64 + lane;
+            pv[u] = i < a.n ? pos_w[i] : -1;
+            ev[u] = i < a.n ? ids_w[i] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            const int64_t i = (s0 + u) * 64 + lane;
+            if (i < a.n && pv[u] >= 0) {
+                const int e = ev[u];
                 const int first = (e / a.per) * a.per;
                 int32_t cross = 0;
                 for (int r = 0; r < w; ++r)
                     cross += cnt[r * a.E + e];
                 const int32_t base = (e > 0 ? incl[e - 1] : 0) - (first > 0 ? incl[first - 1] : 0);
-                a.pos[w][i] = p + base + cross;
+                pos_w[i] = pv[u] + base + cross;
             }
         }
     }
@@ -482,7 +501,7 @@ hipError_t launch_moe_route(const MoeRoutePlan& p, hipStream_t stream)
         return hipErrorInvalidValue;
     if (p.small) {
         const size_t lds = static_cast<size_t>(a.P * a.E + a.E + 64 * a.P) * sizeof(int32_t);
-        if (a.nch != 1 || a.n > kMoeChunk || lds > kMoeSmallLds)
+        if (a.n > kMoeSmallEntries || lds > kMoeSmallLds)
             return hipErrorInvalidValue;
         k_moe_route_small<<<dim3(1), dim3(64 * a.P), lds, stream>>>(a);
         return hipGetLastError();

@@ -795,9 +795,9 @@ atom_status plan_moe_route(const atom_moe_routing* rt, MoeRoutePlan* p)
     a.per = E / P;
     a.partial = static_cast<int32_t*>(rt->scratch);
     p->scan_threads = static_cast<int32_t>(ceil_div(E, 64) * 64);
-    // Decode-sized routing (every rank's entries in one chunk) runs as one
+    // Small routings (up to kMoeSmallEntries entries per rank) run as one
     // workgroup of one wave per rank when its counters fit in LDS.
-    p->small = a.nch == 1 && n <= kMoeChunk &&
+    p->small = n <= kMoeSmallEntries &&
                (static_cast<int64_t>(P) * E + E + 64 * P) * 4 <= kMoeSmallLds;
     return ATOM_OK;
 }

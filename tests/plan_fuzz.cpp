@@ -203,8 +203,8 @@ int main(int argc, char** argv)
             check(rp.a.per * P == E, "moe experts per rank", iter);
             check(rp.a.groups >= 1 && rp.a.groups <= rp.a.nch && rp.a.groups * P <= 1024,
                   "moe placing groups", iter);
-            check(!rp.small || (rp.a.nch == 1 && n <= kMoeChunk &&
-                                (int64_t(P) * E + E + 64 * P) * 4 <= kMoeSmallLds),
+            check(rp.small == (n <= kMoeSmallEntries &&
+                               (int64_t(P) * E + E + 64 * P) * 4 <= kMoeSmallLds),
                   "moe small routing", iter);
         }
         const int64_t cap = pick(0, 9) == 0 ? pick(-1, 3) : pick(0, 40000);
