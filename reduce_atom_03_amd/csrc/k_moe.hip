@@ -8,14 +8,14 @@
 // rows in entry order; a rank's buffer holds its experts back to back);
 // combine is the way back, a weighted sum over each token's k choices.
 //
-// Routing (metadata only): one workgroup when every rank's entries fit in
-// one chunk (k_moe_route_small, the decode case), else three launches:
+// Routing (metadata only): one workgroup for up to 256 entries per rank
+// (k_moe_route_small, the decode case), else three launches:
 //   k_moe_rank   one wave per chunk of 256 entries of one rank: the rank of
 //                every entry among the chunk's entries with the same expert,
-//                in entry order (each 64-entry step sorts its (expert, lane)
-//                keys across the wave, so runs of equal experts give the
-//                ranks; an LDS counter per expert carries over between
-//                steps), and the chunk's histogram;
+//                in entry order (in each 64-entry step the lanes holding one
+//                expert are matched by ballots over the id's bits; an LDS
+//                counter per expert carries over between steps), and the
+//                chunk's histogram;
 //   k_moe_prefix one workgroup per rank, one thread per expert: rows of
 //                expert e in the rank's earlier chunks, and the rank's
 //                total for e (the counts);
