@@ -103,7 +103,20 @@ __global__ __launch_bounds__(256) void k_copy_vec(const CopyArgs a)
         if (t >= a.ntiles)
             continue;
         const int s = seg_of_tile(a, t);
-        const Seg g = seg_geometry(a, s);
+        Seg g = seg_geometry(a, s);
+        // The segment's head (bytes before the first 16-byte boundary, when
+        // its source and destinations are off alignment by the same amount)
+        // is copied element by element by the first lanes of its first tile;
+        // the tiles then cover the rest from that boundary.
+        const int h = a.head[s];
+        if (h > 0) {
+            if (t == a.seg_tile_begin[s] && lane * a.esize < h)
+                copy_bytes(a, g, static_cast<int64_t>(lane) * a.esize,
+                           static_cast<int64_t>(lane + 1) * a.esize);
+            g.src += h;
+            g.dst_off += h;
+            g.bytes -= h;
+        }
         // Tile start in the segment; the first tile may start before the
         // segment (negative offsets are skipped) so that tiles are aligned
         // at the destination.

@@ -68,9 +68,16 @@ __global__ __launch_bounds__(256) void k_reduce_vec(const ReduceArgs a)
         if (t >= a.ntiles)
             continue;
         const int k = part_of_tile(a, t);
-        const int64_t pbeg = a.part_off[k];
-        const int64_t plen = a.part_off[k + 1] - pbeg;
-        const int64_t nfull = plen / VE;                       // whole slots in the part
+        const int64_t pstart = a.part_off[k];                  // the part's first element
+        const int h = a.head[k];
+        const int64_t pbeg = pstart + h;                       // its first 16-byte boundary
+        const int64_t plen = a.part_off[k + 1] - pbeg;         // >= 0
+        const int64_t nfull = plen / VE;                       // whole slots after the head
+        // The head (elements before the boundary, when every stream of the
+        // part is off alignment by the same amount) is reduced element by
+        // element by the first lanes of the part's first tile.
+        if (t == a.tile_begin[k] && lane < h)
+            store_elem<T>(a, k, pstart, pstart + lane, sum_elem<T>(a, pstart + lane));
         // First slot of the tile; the part's first tile may start before the
         // part (negative slots are skipped) so that tiles are aligned.
         const int64_t slot0 = (t - a.tile_begin[k]) * nthr * U - a.shift[k];
@@ -104,7 +111,7 @@ __global__ __launch_bounds__(256) void k_reduce_vec(const ReduceArgs a)
                     acc.add(x[u][r]);
                 const u32x4 y = acc.pack();
                 if (a.mode == RM_SCATTER) {
-                    char* db = static_cast<char*>(a.dst[k]) + slot0 * kVecBytes;
+                    char* db = static_cast<char*>(a.dst[k]) + (h + slot0 * VE) * sizeof(T);
                     st16(db + off, y, nt);
                 } else {
                     for (int q = 0; q < a.ndst; ++q) {
@@ -115,7 +122,7 @@ __global__ __launch_bounds__(256) void k_reduce_vec(const ReduceArgs a)
             } else if (s == nfull && nfull * VE < plen) {
                 // The part's last, partial slot.
                 for (int64_t i = pbeg + nfull * VE; i < pbeg + plen; ++i)
-                    store_elem<T>(a, k, pbeg, i, sum_elem<T>(a, i));
+                    store_elem<T>(a, k, pstart, i, sum_elem<T>(a, i));
             }
         }
     }

@@ -38,6 +38,10 @@ struct ReduceArgs {
     int32_t shift[kMaxRanks];          // per part: slots before its first slot in
                                        // its first tile (tiles start at addresses
                                        // aligned to the tile size in source 0)
+    int32_t head[kMaxRanks];           // vector path, per part: elements before its
+                                       // first 16-byte boundary (every stream of
+                                       // the part is off alignment by the same
+                                       // amount); reduced element by element
     int32_t nsrc;
     int32_t ndst;
     int32_t nparts;
@@ -73,6 +77,10 @@ struct CopyArgs {
                                        // seg_tile_shift)
     int32_t cnt[kMaxSegs];             // rows per segment
     int32_t seg_tile_begin[kMaxSegs + 1];
+    uint8_t head[kMaxSegs];            // vector path, per segment: bytes before its
+                                       // first 16-byte boundary (source and every
+                                       // destination off alignment by the same
+                                       // amount); copied element by element
 };
 
 // SNAC: AllGather (stage = copy) and the composed AllReduce (stage = reduce).

@@ -187,19 +187,36 @@ void build_reduce(Plan* p, int nsrc, const void* const* srcs, int ndst, void* co
     ReduceArgs& a = p->ra;
     std::memset(&a, 0, sizeof a);
     const int es = p->esize;
-    bool vec = true;
-    for (int r = 0; r < nsrc; ++r) {
+    for (int r = 0; r < nsrc; ++r)
         a.src[r] = srcs[r];
-        vec = vec && aligned(srcs[r], kVecBytes);
-    }
-    for (int q = 0; q < ndst; ++q) {
+    for (int q = 0; q < ndst; ++q)
         a.dst[q] = dsts[q];
-        vec = vec && aligned(dsts[q], kVecBytes);
-    }
-    for (int k = 0; k <= nparts; ++k) {
+    for (int k = 0; k <= nparts; ++k)
         a.part_off[k] = part_off[k];
-        vec = vec && ((part_off[k] * es) % kVecBytes == 0);
+    // Vector path: within each part every stream (its P sources and its
+    // destinations) sits at the same offset from 16-byte alignment. Then the
+    // elements before the first boundary (the head) are reduced one by one
+    // and the rest in 16-byte slots; otherwise the element-wise kernel runs.
+    auto mis = [](const void* b, int64_t byte_off) {
+        return static_cast<unsigned>((reinterpret_cast<uintptr_t>(b) + static_cast<uint64_t>(byte_off)) %
+                                     kVecBytes);
+    };
+    bool vec = true;
+    for (int k = 0; k < nparts && vec; ++k) {
+        const int64_t off = part_off[k] * es;
+        const unsigned d = mis(srcs[0], off);
+        for (int r = 1; r < nsrc; ++r)
+            vec = vec && mis(srcs[r], off) == d;
+        if (mode == RM_SCATTER)
+            vec = vec && mis(dsts[k], 0) == d;
+        else
+            for (int q = 0; q < ndst; ++q)
+                vec = vec && mis(dsts[q], off) == d;
+        const int64_t len = part_off[k + 1] - part_off[k];
+        a.head[k] = static_cast<int32_t>(std::min<int64_t>(len, ((kVecBytes - d) % kVecBytes) / es));
     }
+    if (!vec)
+        std::memset(a.head, 0, sizeof a.head);
     const int64_t ve = kVecBytes / es;   // elements per 16-byte slot
     p->vec = vec ? 1 : 0;
     p->U = vec ? pick_u_reduce(nsrc, mode, c.stages) : 1;
@@ -222,18 +239,21 @@ void build_reduce(Plan* p, int nsrc, const void* const* srcs, int ndst, void* co
     int64_t t = 0;
     for (int k = 0; k < nparts; ++k) {
         a.tile_begin[k] = t;
-        const int64_t len = part_off[k + 1] - part_off[k];
+        const int64_t len = part_off[k + 1] - part_off[k] - a.head[k];
         // Vector path: start tiles at addresses aligned to the tile size in
         // source 0 (a part that starts mid-tile gets a short first tile), so
         // a tile's loads never straddle two tile-sized blocks of memory.
         int64_t shift = 0;
         if (vec) {
             const uint64_t addr = reinterpret_cast<uintptr_t>(srcs[0]) +
-                                  static_cast<uint64_t>(part_off[k] * es);
+                                  static_cast<uint64_t>((part_off[k] + a.head[k]) * es);
             shift = seg_tile_shift(addr, slots_per_tile * kVecBytes) / kVecBytes;
         }
         a.shift[k] = static_cast<int32_t>(shift);
-        t += ceil_div(ceil_div(len, ve) + shift, slots_per_tile);
+        int64_t tiles = ceil_div(ceil_div(len, ve) + shift, slots_per_tile);
+        if (a.head[k] > 0 && tiles == 0)
+            tiles = 1;                   // a part that is all head still needs its tile
+        t += tiles;
     }
     a.tile_begin[nparts] = t;
     a.ntiles = t;
@@ -254,15 +274,58 @@ void build_copy(Plan* p, int32_t kind, int P, const void* const* srcs, int nsrc,
 {
     CopyArgs& a = p->ca;
     std::memset(&a, 0, sizeof a);
-    bool vec = (row_bytes % kVecBytes == 0) || nseg == 1;
-    for (int r = 0; r < nsrc; ++r) {
+    for (int r = 0; r < nsrc; ++r)
         a.src[r] = srcs[r];
-        vec = vec && aligned(srcs[r], kVecBytes);
-    }
-    for (int q = 0; q < ndst; ++q) {
+    for (int q = 0; q < ndst; ++q)
         a.dst[q] = dsts[q];
-        vec = vec && aligned(dsts[q], kVecBytes);
+    // Segment geometry (as the kernel derives it): source address and
+    // destination byte offset of every segment.
+    uint64_t seg_src[kMaxSegs], seg_dst[kMaxSegs];    // dst: of dsts[0] (fan-out) or dsts[j]
+    if (kind == CK_FANOUT) {
+        int64_t rows_before = 0;
+        for (int s = 0; s < nseg; ++s) {
+            seg_src[s] = reinterpret_cast<uintptr_t>(srcs[s]);
+            seg_dst[s] = static_cast<uint64_t>(rows_before * row_bytes);
+            rows_before += cnt[s];
+        }
+    } else {
+        int64_t col_rows[kMaxRanks] = {};              // rows already bound for j
+        for (int r = 0; r < P; ++r) {
+            int64_t src_rows = 0;                      // rows of source r before j
+            for (int j = 0; j < P; ++j) {
+                const int s = r * P + j;
+                seg_src[s] = reinterpret_cast<uintptr_t>(srcs[r]) + static_cast<uint64_t>(src_rows * row_bytes);
+                seg_dst[s] = static_cast<uint64_t>(col_rows[j] * row_bytes);
+                src_rows += cnt[s];
+                col_rows[j] += cnt[s];
+            }
+        }
     }
+    // Vector path: within each segment the source and every destination sit
+    // at the same offset from 16-byte alignment; the bytes before the first
+    // boundary (the head) are copied element by element, the rest in 16-byte
+    // slots. Otherwise the element-wise kernel runs.
+    bool aligned_all = row_bytes % kVecBytes == 0 || nseg == 1;
+    for (int r = 0; r < nsrc; ++r)
+        aligned_all = aligned_all && aligned(srcs[r], kVecBytes);
+    for (int q = 0; q < ndst; ++q)
+        aligned_all = aligned_all && aligned(dsts[q], kVecBytes);
+    bool vec = true;
+    for (int s = 0; s < nseg && vec && !aligned_all; ++s) {
+        const int64_t bytes_s = cnt[s] * row_bytes;
+        if (bytes_s == 0)
+            continue;
+        const unsigned d = static_cast<unsigned>(seg_src[s] % kVecBytes);
+        if (kind == CK_FANOUT) {
+            for (int q = 0; q < ndst; ++q)
+                vec = vec && (reinterpret_cast<uintptr_t>(dsts[q]) + seg_dst[s]) % kVecBytes == d;
+        } else {
+            vec = vec && (reinterpret_cast<uintptr_t>(dsts[s % P]) + seg_dst[s]) % kVecBytes == d;
+        }
+        a.head[s] = static_cast<uint8_t>(std::min<int64_t>(bytes_s, (kVecBytes - d) % kVecBytes));
+    }
+    if (!vec)
+        std::memset(a.head, 0, sizeof a.head);
     p->vec = vec ? 1 : 0;
     p->U = vec ? pick_u_copy(kind, nseg, c.stages) : 1;
     // 64-lane tiles: +7% on the exchange and +2% on the fan-out, whose
@@ -285,31 +348,21 @@ void build_copy(Plan* p, int32_t kind, int P, const void* const* srcs, int nsrc,
     // misaligns its source (measured -3%), so it keeps segment-relative tiles.
     a.align = (vec && kind == CK_FANOUT) ? 1 : 0;
     int64_t t = 0;
-    int64_t rows_before[kMaxRanks] = {};     // CK_FANOUT: rows of earlier segments
     for (int s = 0; s < nseg; ++s) {
         a.cnt[s] = static_cast<int32_t>(cnt[s]);
         a.seg_tile_begin[s] = static_cast<int32_t>(t);
+        const int64_t h = a.head[s];
         // Fan-out vector path: tiles start at addresses aligned to the tile
         // size in the destination (P stores per load: the side with the most
-        // bytes).
+        // bytes), counted from the segment's first 16-byte boundary.
         int64_t shift = 0;
-        if (a.align) {
-            uint64_t dst_addr;
-            if (kind == CK_FANOUT) {
-                dst_addr = reinterpret_cast<uintptr_t>(dsts[0]) +
-                           static_cast<uint64_t>(rows_before[0] * row_bytes);
-                rows_before[0] += cnt[s];
-            } else {
-                const int r = s / P, j = s % P;
-                int64_t before = 0;
-                for (int rr = 0; rr < r; ++rr)
-                    before += cnt[rr * P + j];
-                dst_addr = reinterpret_cast<uintptr_t>(dsts[j]) + static_cast<uint64_t>(before * row_bytes);
-            }
-            shift = seg_tile_shift(dst_addr, a.tile_bytes);
-        }
-        const int64_t bytes_s = cnt[s] * row_bytes;
-        t += bytes_s ? ceil_div(bytes_s + shift, a.tile_bytes) : 0;
+        if (a.align)
+            shift = seg_tile_shift(reinterpret_cast<uintptr_t>(dsts[0]) + seg_dst[s] + h, a.tile_bytes);
+        const int64_t rest = cnt[s] * row_bytes - h;
+        int64_t tiles = rest ? ceil_div(rest + shift, a.tile_bytes) : 0;
+        if (h > 0 && tiles == 0)
+            tiles = 1;                   // a segment that is all head still needs its tile
+        t += tiles;
     }
     a.seg_tile_begin[nseg] = static_cast<int32_t>(t);
     a.ntiles = t;

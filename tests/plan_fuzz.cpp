@@ -42,7 +42,12 @@ void check_reduce(const Plan& p, int iter)
         check(len >= 0, "reduce part length", iter);
         const int64_t shift = p.vec ? a.shift[k] : 0;
         check(shift >= 0 && shift < ts, "reduce shift", iter);
-        t += cdiv(cdiv(len, ve) + shift, ts);
+        const int64_t h = a.head[k];
+        check(h >= 0 && h < ve && h <= len && (p.vec || h == 0), "reduce head", iter);
+        int64_t tiles = cdiv(cdiv(len - h, ve) + shift, ts);
+        if (h > 0 && tiles == 0)
+            tiles = 1;
+        t += tiles;
     }
     check(a.tile_begin[a.nparts] == t && a.ntiles == t, "reduce ntiles", iter);
     check(p.grid >= 1 && p.grid <= std::max<int64_t>(1, t), "reduce grid", iter);
@@ -57,9 +62,13 @@ void check_copy(const Plan& p, int iter)
     for (int s = 0; s < a.nseg; ++s) {
         check(a.seg_tile_begin[s] == t, "copy seg_tile_begin", iter);
         check(a.cnt[s] >= 0, "copy count", iter);
-        const int64_t bytes = static_cast<int64_t>(a.cnt[s]) * a.row_bytes;
-        // an aligned segment may need one extra (short) tile at its start
-        const int64_t lo = cdiv(bytes, a.tile_bytes), hi = bytes ? lo + 1 : 0;
+        const int64_t h = a.head[s];
+        const int64_t bytes = static_cast<int64_t>(a.cnt[s]) * a.row_bytes - h;
+        check(h >= 0 && h < kVecBytes && bytes >= 0 && (p.vec || h == 0), "copy head", iter);
+        // an aligned segment may need one extra (short) tile at its start; a
+        // segment that is all head has one tile
+        const int64_t lo = std::max<int64_t>(cdiv(bytes, a.tile_bytes), h > 0 ? 1 : 0);
+        const int64_t hi = bytes ? cdiv(bytes, a.tile_bytes) + 1 : lo;
         const int64_t n = (s + 1 <= a.nseg ? a.seg_tile_begin[s + 1] : 0) - a.seg_tile_begin[s];
         check(n >= lo && n <= hi, "copy tiles per segment", iter);
         t = a.seg_tile_begin[s + 1];

@@ -359,3 +359,24 @@ def test_wide_workgroups_only_for_the_staged_kernel():
         for op, lin in ((A.OP_COPY, A.SHARD), (A.OP_SUM, A.PARTITIONED)):
             st, info = Q(lin, A.GATHERED, op, cfg=A.config(flags=A.F_STAGED, lanes=lanes))
             assert st == A.OK and info.staged == 1, (lanes, op)
+
+
+def test_coaligned_offsets_plan_the_vector_path():
+    """Buffers all off 16-byte alignment by the same amount (and partitions
+    of 16-byte multiples) take the vector path with element-wise heads;
+    buffers off by different amounts, or partitions that change the offset,
+    take the element-wise path."""
+    P, n = 8, 4096
+    big = P * n * 2 * 4
+    for off in (2, 6, 14):
+        ins = fake(P, big, align_off=off)
+        outs = fake(P, big, start=BASE + (1 << 36), align_off=off)
+        for kin, kout, op in ((A.PARTITIONED, A.SHARD, A.OP_SUM), (A.PARTITIONED, A.GATHERED, A.OP_SUM),
+                              (A.SHARD, A.GATHERED, A.OP_COPY), (A.PARTITIONED, A.TRANSPOSED, A.OP_COPY)):
+            st, info = Q(kin, kout, op, P=P, n=n, ins=ins, outs=outs)
+            assert st == A.OK and info.vector_path == 1, (off, kin, kout)
+        st, info = Q(A.PARTITIONED, A.SHARD, A.OP_SUM, P=P, n=n, ins=ins,
+                     outs=fake(P, big, start=BASE + (1 << 36), align_off=(off + 2) % 16))
+        assert st == A.OK and info.vector_path == 0
+        st, info = Q(A.PARTITIONED, A.SHARD, A.OP_SUM, P=P, n=n + 1, ins=ins, outs=outs)
+        assert st == A.OK and info.vector_path == 0      # partition k moves the offset

@@ -529,3 +529,87 @@ def test_side_stream(A):
     s.synchronize()
     for j in range(P):
         _assert_reduced(from_dev(outs[j]), want[j], f"side stream out_{j}")
+
+
+# ------------------------------------------- co-aligned, off 16-byte alignment
+
+@pytest.mark.parametrize("dtype,skew", [(synth.BF16, 1), (synth.BF16, 3), (synth.BF16, 7),
+                                        (synth.F32, 1), (synth.F32, 3)])
+def test_coaligned_offsets_take_the_vector_path(A, dtype, skew):
+    """Every buffer `skew` elements past a 16-byte boundary, partitions of
+    16-byte multiples: each part's first elements (the head) are done one by
+    one and the rest in 16-byte slots, with a short last slot; every
+    collective and the flat copy and reduce match the oracle, and the plan
+    reports the vector path."""
+    import torch
+    P, n = 8, 8 * 4099                     # 16-byte partitions, ragged in tiles
+    tdt = _torch_dtype(dtype)
+    es = 2 if dtype == synth.BF16 else 4
+    say(f"co-aligned skew={skew} {dtype}")
+
+    def dev(a):
+        return to_dev(a, pad_before=skew)[1]
+
+    def outs(sizes):
+        return out_buffers(sizes, tdt, GUARD + skew)
+
+    xs = [synth.mixed_bits(81, r, P * n, dtype, specials=False) for r in range(P)]
+    dx = [dev(x) for x in xs]
+    fulls, ys = outs([n] * P)
+    st, info = A.atom_plan_query(A.layout(A.PARTITIONED, dx, n), A.layout(A.SHARD, ys, n), A.OP_SUM)
+    assert st == A.OK and info.vector_path == 1
+    A.reduce_scatter(dx, ys)
+    want = oracle.reduce_scatter(xs)
+    _sync()
+    for k in range(P):
+        _assert_reduced(from_dev(ys[k]), want[k], f"RS y_{k}")
+    check_guards(fulls, [n] * P, GUARD + skew)
+    fulls, ar = outs([P * n] * P)
+    A.all_reduce(dx, ar)
+    want = oracle.all_reduce(xs)
+    _sync()
+    for j in range(P):
+        _assert_reduced(from_dev(ar[j]), want[j], f"AR out_{j}")
+    check_guards(fulls, [P * n] * P, GUARD + skew)
+    fulls, a2 = outs([P * n] * P)
+    A.all_to_all(dx, a2)
+    want = oracle.all_to_all(xs)
+    _sync()
+    for j in range(P):
+        assert_bits_equal(from_dev(a2[j]), want[j], f"A2A out_{j}", nan_by_class=False)
+    check_guards(fulls, [P * n] * P, GUARD + skew)
+    zs = [synth.mixed_bits(82, k, n, dtype) for k in range(P)]
+    fulls, ag = outs([P * n] * P)
+    A.all_gather([dev(z) for z in zs], ag)
+    want = oracle.all_gather(zs)
+    _sync()
+    for j in range(P):
+        assert_bits_equal(from_dev(ag[j]), want[j], f"AG out_{j}", nan_by_class=False)
+    check_guards(fulls, [P * n] * P, GUARD + skew)
+    # AllToAllV in rows of 16 bytes
+    row = 16 // es
+    C = synth.random_counts(83, P, 700)
+    rows = C.sum(axis=1)
+    R = C.sum(axis=0)
+    vs = [synth.mixed_bits(84, r, int(rows[r]) * row, dtype) for r in range(P)]
+    fulls, av = outs([int(R[j]) * row for j in range(P)])
+    A.all_to_all_v([dev(v) if v.size else empty_dev(1, tdt) for v in vs], av, C, row)
+    want = oracle.all_to_all_v(vs, C, row)
+    _sync()
+    for j in range(P):
+        assert_bits_equal(from_dev(av[j]), want[j], f"A2AV out_{j}", nan_by_class=False)
+    check_guards(fulls, [int(R[j]) * row for j in range(P)], GUARD + skew)
+    # flat copy and flat reduce
+    m = 100003 * 8
+    src = synth.mixed_bits(85, 0, m, dtype)
+    fulls, cp = outs([m])
+    A.atom_copy(cp[0], dev(src))
+    _sync()
+    assert_bits_equal(from_dev(cp[0]), src, "copy", nan_by_class=False)
+    check_guards(fulls, [m], GUARD + skew)
+    rs = [synth.mixed_bits(86, r, m, dtype, specials=False) for r in range(3)]
+    fulls, rd = outs([m])
+    A.atom_reduce(rd[0], [dev(x) for x in rs])
+    _sync()
+    _assert_reduced(from_dev(rd[0]), oracle.reduce(rs), "reduce")
+    check_guards(fulls, [m], GUARD + skew)
