@@ -91,7 +91,9 @@ __device__ __forceinline__ void copy_bytes(const CopyArgs& a, const Seg& g, int6
     }
 }
 
-template <int U>
+// HEADS: some segment starts off a 16-byte boundary (instantiated apart so
+// that aligned plans run without the per-tile head check).
+template <int U, bool HEADS>
 __global__ __launch_bounds__(256) void k_copy_vec(const CopyArgs a)
 {
     const int lane = threadIdx.x;
@@ -108,8 +110,8 @@ __global__ __launch_bounds__(256) void k_copy_vec(const CopyArgs a)
         // its source and destinations are off alignment by the same amount)
         // is copied element by element by the first lanes of its first tile;
         // the tiles then cover the rest from that boundary.
-        const int h = a.head[s];
-        if (h > 0) {
+        const int h = HEADS ? a.head[s] : 0;
+        if (HEADS && h > 0) {
             if (t == a.seg_tile_begin[s] && lane * a.esize < h)
                 copy_bytes(a, g, static_cast<int64_t>(lane) * a.esize,
                            static_cast<int64_t>(lane + 1) * a.esize);
@@ -188,13 +190,21 @@ hipError_t launch_copy(const Plan& p, hipStream_t stream)
         k_copy_elem<<<grid, block, 0, stream>>>(p.ca);
         return hipGetLastError();
     }
+    bool heads = false;
+    for (int s = 0; s < p.ca.nseg; ++s)
+        heads = heads || p.ca.head[s] != 0;
+#define ATOM_COPY_VEC(UU)                                                  \
+    case UU:                                                               \
+        if (heads)                                                         \
+            k_copy_vec<UU, true><<<grid, block, 0, stream>>>(p.ca);        \
+        else                                                               \
+            k_copy_vec<UU, false><<<grid, block, 0, stream>>>(p.ca);       \
+        break;
     switch (p.U) {
-    case 1: k_copy_vec<1><<<grid, block, 0, stream>>>(p.ca); break;
-    case 2: k_copy_vec<2><<<grid, block, 0, stream>>>(p.ca); break;
-    case 4: k_copy_vec<4><<<grid, block, 0, stream>>>(p.ca); break;
-    case 8: k_copy_vec<8><<<grid, block, 0, stream>>>(p.ca); break;
+    ATOM_COPY_VEC(1) ATOM_COPY_VEC(2) ATOM_COPY_VEC(4) ATOM_COPY_VEC(8)
     default: return hipErrorInvalidValue;
     }
+#undef ATOM_COPY_VEC
     return hipGetLastError();
 }
 
