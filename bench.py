@@ -24,7 +24,8 @@ resident synthetic input (bf16):
 `value` is the step's credited bytes (every input element read once, every
 output element written once, a reduced element counted with its P reads)
 over the step time, in GB/s. Per-collective GB/s and fraction of the 8 TB/s
-HBM peak, the 8 KiB AllGather p50/p99 latency and the dominant kernel's
+HBM peak, the 8 KiB AllGather p50/p99 latency (an event pair around each
+launch), its time per call back to back and in a HIP graph, and the dominant kernel's
 roofline are reported alongside; the CPU oracle is timed on the same step
 as a baseline.
 """
@@ -301,6 +302,35 @@ def main():
         b.synchronize()
         gl.append(a.elapsed_time(b) * 1e3 / 100)
     graph_us = float(np.median(gl))
+    # Back to back: 400 calls queued behind a spin kernel (so that the host's
+    # submission, slower than the GPU per call, does not pace them) with one
+    # event pair around all of them: the GPU time per call of a loop of
+    # collectives, the convention of collective benchmarks' time per op.
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    torch.cuda._sleep(1000000)
+    e1.record(stream)
+    e1.synchronize()
+    spin = int(1e6 * 6.0 / max(e0.elapsed_time(e1), 1e-3))      # about 6 ms of spin
+
+    def back_to_back_us(fn, n=400, reps=9):
+        v = []
+        for _ in range(reps):
+            torch.cuda._sleep(spin)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(n):
+                fn()
+            b.record(stream)
+            b.synchronize()
+            v.append(a.elapsed_time(b) * 1e3 / n)
+        return round(float(np.median(v)), 2)
+
+    b2b = {"ag_8KiB": back_to_back_us(ag8),
+           "copy_16B": back_to_back_us(lambda: A.atom_copy(tiny_dst, tiny_src, 16))}
+    for b in (1, 2, 4, 8, 16):
+        lay = (L(A.PARTITIONED, x5[b], b * 896), L(A.GATHERED, o5[b], b * 896))
+        b2b[f"dec_b{b}"] = back_to_back_us(lambda l=lay: A.atom_collective(l[0], l[1], A.OP_SUM))
     # Host-side time per call of the same launch (submission cost).
     t = time.perf_counter()
     for _ in range(args.lat_iters):
@@ -353,6 +383,7 @@ def main():
         "p99_us_8KiB": round(float(np.percentile(lat, 99)), 2),
         "host_us_per_call_8KiB": round(host_us, 2),
         "graph_us_per_call_8KiB": round(graph_us, 2),
+        "back_to_back_us_per_call": b2b,
         "decode_allreduce_latency": dec_lat,
         "latency_samples": args.lat_iters,
         "p50_us_launch_floor_16B_copy": round(float(np.percentile(floor, 50)), 2),

@@ -144,11 +144,11 @@ __global__ __launch_bounds__(256) void k_copy_vec(const CopyArgs a)
             } else if (o + kVecBytes <= g.bytes) {
                 if (g.dst >= 0) {
                     char* db = static_cast<char*>(a.dst[g.dst]) + g.dst_off + b0;
-                    st16(db + off, x[u], nt);
+                    st16(db, off, x[u], nt);
                 } else {
                     for (int q = 0; q < a.ndst; ++q) {
                         char* db = static_cast<char*>(a.dst[q]) + g.dst_off + b0;
-                        st16(db + off, x[u], nt);
+                        st16(db, off, x[u], nt);
                     }
                 }
             } else if (o < g.bytes) {

@@ -394,9 +394,9 @@ __global__ __launch_bounds__(256) void k_moe_dispatch(const MoeMoveArgs a)
             if ((ch.live >> c) & 1u) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const int64_t o = b0 + static_cast<int64_t>(u * nthr + lane) * kVecBytes;
-                    if (o < a.row_bytes)
-                        st16(ch.row[c] + o, x[u], nt);
+                    const uint32_t off = static_cast<uint32_t>(u * nthr + lane) * kVecBytes;
+                    if (b0 + off < a.row_bytes)
+                        st16(ch.row[c] + b0, off, x[u], nt);
                 }
             }
         }
@@ -485,7 +485,7 @@ __global__ __launch_bounds__(256) void k_moe_combine(const MoeMoveArgs a)
                 if ((ch.live >> c) & 1u)
                     acc.fma(ch.w[c], y[c]);
             if (in_row)
-                st16(dst + o, acc.pack(), nt);
+                st16(dst + b0, static_cast<uint32_t>(lane) * kVecBytes, acc.pack(), nt);
         }
     }
 }

@@ -55,7 +55,12 @@ __device__ __forceinline__ void store_elem(const ReduceArgs& a, int k, int64_t p
     }
 }
 
-template <typename T, int P, int U>
+// GRID: the uniform form (grid_parts > 0). The part is blockIdx.y and the
+// tile within it blockIdx.x, every part has part_off[1] elements starting at
+// k * part_off[1], no head and the one shift shift[0]: nothing to look up
+// before the loads. Otherwise tiles are numbered along a one-dimensional
+// grid (grid-stride beyond its size) and each finds its part in tile_begin.
+template <typename T, int P, int U, bool GRID>
 __global__ __launch_bounds__(256) void k_reduce_vec(const ReduceArgs a)
 {
     constexpr int VE = kVecBytes / sizeof(T);
@@ -63,30 +68,50 @@ __global__ __launch_bounds__(256) void k_reduce_vec(const ReduceArgs a)
     const int nthr = blockDim.x;
     const bool nt = a.nt_store != 0;
     const bool remap = a.xcd_remap != 0;
-    for (int64_t base = 0; base < a.ntiles; base += gridDim.x) {
-        const int64_t t = tile_of(base, remap);
-        if (t >= a.ntiles)
-            continue;
-        const int k = part_of_tile(a, t);
-        const int64_t pstart = a.part_off[k];                  // the part's first element
-        const int h = a.head[k];
+    const int64_t nloop = GRID ? 1 : a.ntiles;
+    for (int64_t base = 0; base < nloop; base += gridDim.x) {
+        int k;
+        int64_t pstart, pend, tip;                             // tip: tile within the part
+        int h;
+        int32_t shift;
+        if (GRID) {
+            k = blockIdx.y;
+            const int64_t L = a.part_off[1];
+            pstart = static_cast<int64_t>(k) * L;
+            pend = pstart + L;
+            tip = blockIdx.x;
+            h = 0;
+            shift = a.shift[0];
+        } else {
+            const int64_t t = tile_of(base, remap);
+            if (t >= a.ntiles)
+                continue;
+            k = part_of_tile(a, t);
+            pstart = a.part_off[k];                            // the part's first element
+            pend = a.part_off[k + 1];
+            tip = t - a.tile_begin[k];
+            h = a.head[k];
+            shift = a.shift[k];
+        }
         const int64_t pbeg = pstart + h;                       // its first 16-byte boundary
-        const int64_t plen = a.part_off[k + 1] - pbeg;         // >= 0
+        const int64_t plen = pend - pbeg;                      // >= 0
         const int64_t nfull = plen / VE;                       // whole slots after the head
         // The head (elements before the boundary, when every stream of the
         // part is off alignment by the same amount) is reduced element by
         // element by the first lanes of the part's first tile.
-        if (t == a.tile_begin[k] && lane < h)
+        if (!GRID && tip == 0 && lane < h)
             store_elem<T>(a, k, pstart, pstart + lane, sum_elem<T>(a, pstart + lane));
         // First slot of the tile; the part's first tile may start before the
         // part (negative slots are skipped) so that tiles are aligned.
-        const int64_t slot0 = (t - a.tile_begin[k]) * nthr * U - a.shift[k];
-        // Uniform bases of this tile; lanes add 32-bit offsets.
+        const int64_t slot0 = tip * nthr * U - shift;
+        // Uniform bases of this tile (one buffer resource per source, in
+        // scalar registers, covering the tile); lanes add 32-bit offsets.
         const int64_t ebase = pbeg + slot0 * VE;                // absolute element index
-        const char* sb[P];
+        const uint32_t tile_bytes = static_cast<uint32_t>(nthr) * U * kVecBytes;
+        __amdgpu_buffer_rsrc_t rs[P];
 #pragma unroll
         for (int r = 0; r < P; ++r)
-            sb[r] = static_cast<const char*>(a.src[r]) + ebase * sizeof(T);
+            rs[r] = stream_rsrc(static_cast<const char*>(a.src[r]) + ebase * sizeof(T), tile_bytes);
 
         u32x4 x[U][P];
 #pragma unroll
@@ -96,7 +121,7 @@ __global__ __launch_bounds__(256) void k_reduce_vec(const ReduceArgs a)
             if (s >= 0 && s < nfull) {
 #pragma unroll
                 for (int r = 0; r < P; ++r)
-                    x[u][r] = ld16_stream(sb[r] + off);
+                    x[u][r] = ld16_stream(rs[r], off);
             }
         }
 #pragma unroll
@@ -112,11 +137,11 @@ __global__ __launch_bounds__(256) void k_reduce_vec(const ReduceArgs a)
                 const u32x4 y = acc.pack();
                 if (a.mode == RM_SCATTER) {
                     char* db = static_cast<char*>(a.dst[k]) + (h + slot0 * VE) * sizeof(T);
-                    st16(db + off, y, nt);
+                    st16(db, off, y, nt);
                 } else {
                     for (int q = 0; q < a.ndst; ++q) {
                         char* db = static_cast<char*>(a.dst[q]) + ebase * sizeof(T);
-                        st16(db + off, y, nt);
+                        st16(db, off, y, nt);
                     }
                 }
             } else if (s == nfull && nfull * VE < plen) {
@@ -157,13 +182,27 @@ template <typename T, int P>
 hipError_t launch_vec_p(const Plan& p, hipStream_t stream)
 {
     const dim3 grid(static_cast<unsigned>(p.grid)), block(p.wg);
+    if (p.ra.grid_parts > 0) {
+        const dim3 g2(static_cast<unsigned>(p.grid), static_cast<unsigned>(p.ra.grid_parts));
+        switch (p.U) {
+        case 1: k_reduce_vec<T, P, 1, true><<<g2, block, 0, stream>>>(p.ra); break;
+        case 2:
+            if constexpr (2 * P <= 32) { k_reduce_vec<T, P, 2, true><<<g2, block, 0, stream>>>(p.ra); break; }
+            else return hipErrorInvalidValue;
+        case 4:
+            if constexpr (4 * P <= 32) { k_reduce_vec<T, P, 4, true><<<g2, block, 0, stream>>>(p.ra); break; }
+            else return hipErrorInvalidValue;
+        default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     switch (p.U) {
-    case 1: k_reduce_vec<T, P, 1><<<grid, block, 0, stream>>>(p.ra); break;
+    case 1: k_reduce_vec<T, P, 1, false><<<grid, block, 0, stream>>>(p.ra); break;
     case 2:
-        if constexpr (2 * P <= 32) { k_reduce_vec<T, P, 2><<<grid, block, 0, stream>>>(p.ra); break; }
+        if constexpr (2 * P <= 32) { k_reduce_vec<T, P, 2, false><<<grid, block, 0, stream>>>(p.ra); break; }
         else return hipErrorInvalidValue;
     case 4:
-        if constexpr (4 * P <= 32) { k_reduce_vec<T, P, 4><<<grid, block, 0, stream>>>(p.ra); break; }
+        if constexpr (4 * P <= 32) { k_reduce_vec<T, P, 4, false><<<grid, block, 0, stream>>>(p.ra); break; }
         else return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
     }
@@ -199,6 +238,9 @@ hipError_t launch_vec(const Plan& p, hipStream_t stream)
 hipError_t launch_reduce(const Plan& p, hipStream_t stream)
 {
     if (p.ra.nsrc != p.P || p.grid < 1 || p.wg < 1 || p.wg > 256)
+        return hipErrorInvalidValue;
+    if (p.ra.grid_parts != 0 &&
+        (!p.vec || p.ra.grid_parts != p.ra.nparts || p.ra.grid_parts > 65535 || p.grid > 0x7fffffff))
         return hipErrorInvalidValue;
     if (p.vec) {
         // The vector path takes U from {1, 2, 4}; deeper requests are clamped

@@ -198,10 +198,10 @@ __device__ __forceinline__ void fan_out(const SnacArgs& a, const char* src, int6
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t o = b0 + static_cast<int64_t>(u * nthr + lane) * kVecBytes;
-            if (o < bytes)
+            const uint32_t off = static_cast<uint32_t>(u * nthr + lane) * kVecBytes;
+            if (b0 + off < bytes)
                 for (int q = 0; q < a.P; ++q)
-                    st16(static_cast<char*>(a.dst[q]) + dst_off + o, x[u], nt);
+                    st16(static_cast<char*>(a.dst[q]) + dst_off + b0, off, x[u], nt);
         }
     }
 }

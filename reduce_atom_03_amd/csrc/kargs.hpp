@@ -48,6 +48,14 @@ struct ReduceArgs {
     int32_t mode;
     int32_t nt_store;                  // 1: non-temporal output stores
     int32_t xcd_remap;                 // 1: XCD-contiguous tile order
+    int32_t grid_parts;                // 0: one-dimensional grid, each tile finds
+                                       // its part in tile_begin. Else (small
+                                       // messages) the uniform form: nparts parts
+                                       // of part_off[1] elements each (part k at
+                                       // k * part_off[1]), no heads, one shift
+                                       // (shift[0]) and gridDim.x tiles per part;
+                                       // part = blockIdx.y
+    int32_t pad_;
 };
 
 // Copy family. Segments are derived in the kernel from row counts:

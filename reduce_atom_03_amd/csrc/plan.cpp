@@ -265,6 +265,26 @@ void build_reduce(Plan* p, int nsrc, const void* const* srcs, int ndst, void* co
     a.xcd_remap = (c.flags & ATOM_F_XCD_ORDER) ? 1 : 0;
     p->grid = pick_grid(t, c.num_wgs);
     p->exec = t > 0 ? EX_REDUCE : EX_NONE;
+    // Uniform form of the latency path: equal parts laid end to end, no
+    // heads, one shift, one tile per workgroup. The grid is then
+    // tiles-per-part x parts and a workgroup knows its part and tile from
+    // its coordinates, with no walk through the part table before its first
+    // load. Measured on MI355X: the decode AllReduce (8 x b x 7168 bf16)
+    // went from 3.36 to 3.10 us per call back to back; large messages keep
+    // the one-dimensional grid, which was 3-6 % faster for the cold 8-way
+    // ReduceScatter and fused AllReduce of 8 x 256 MiB.
+    a.grid_parts = 0;
+    const int64_t L = part_off[1] - part_off[0];
+    const int64_t tpp = nparts > 0 ? a.tile_begin[1] : 0;
+    bool uniform = vec && t > 0 && slots < kSmallSlots && part_off[0] == 0 && !a.xcd_remap &&
+                   c.num_wgs == 0 && t <= kMaxGrid && nparts <= 65535;
+    for (int k = 0; k < nparts && uniform; ++k)
+        uniform = part_off[k] == k * L && a.head[k] == 0 && a.shift[k] == a.shift[0] &&
+                  a.tile_begin[k] == k * tpp;
+    if (uniform) {
+        a.grid_parts = nparts;
+        p->grid = tpp;
+    }
 }
 
 // Copy family launch. cnt[s] rows of row_bytes per segment.
@@ -955,7 +975,8 @@ void plan_fill_info(const Plan& p, atom_plan_info* info)
     info->chunk_bytes = p.chunk_bytes;
     info->num_chunks = info->staged ? p.sa.nchunks : 0;
     info->ring_slots = p.slots;
-    info->num_wgs = p.exec == EX_NONE ? 0 : static_cast<int32_t>(p.grid);
+    const int64_t rows = (p.exec == EX_REDUCE && p.ra.grid_parts > 0) ? p.ra.grid_parts : 1;
+    info->num_wgs = p.exec == EX_NONE ? 0 : static_cast<int32_t>(p.grid * rows);
 }
 
 // Table 3: R*tau rounded to the closest power of two (ties upward).

@@ -62,21 +62,31 @@ def test_no_scratch(asm):
 
 def test_ring_hand_off_needs_no_l2_maintenance(asm):
     """The ring is read and written only with agent-coherent (sc1) buffer
-    operations, so no SNAC kernel writes back or invalidates an L2; outputs
-    and inputs use ordinary global operations."""
+    operations, so no SNAC kernel writes back or invalidates an L2. Inputs
+    are read with ordinary global loads; outputs are written with buffer
+    stores whose policy is an immediate: nt (streaming, the default) or
+    none (ATOM_F_NO_NT), both present, never sc0 or sc1."""
     for name, body in _kernels(asm):
         assert not re.search(r"buffer_wbl2|buffer_inv", body), name
-        ring_ops = re.findall(r"^\s*(buffer_(?:load|store)_dwordx4[^\n]*)", body, re.M)
-        assert ring_ops, f"{name}: no ring accesses"
-        for op in ring_ops:
+        loads = re.findall(r"^\s*(buffer_load_dwordx4[^\n]*)", body, re.M)
+        stores = re.findall(r"^\s*(buffer_store_dwordx4[^\n]*)", body, re.M)
+        assert loads, f"{name}: no ring loads"
+        for op in loads:
             assert re.search(r"\bsc1\b", op), f"{name}: ring access without sc1: {op}"
+        ring = [op for op in stores if re.search(r"\bsc1\b", op)]
+        outs = [op for op in stores if not re.search(r"\bsc1\b", op)]
+        assert ring, f"{name}: no ring stores"
+        assert any(re.search(r"\bnt\b", op) for op in outs), f"{name}: no streaming output store"
+        assert any(not re.search(r"\bnt\b", op) for op in outs), f"{name}: no ordinary output store"
+        for op in outs:
+            assert not re.search(r"\bsc0\b", op), f"{name}: output store with sc0: {op}"
 
 
 def test_producer_waits_for_its_stores_before_notify(asm):
     """Each wave waits for vmcnt(0) after its last ring store and before the
     barrier that precedes the `ready` increment."""
     for name, body in _kernels(asm):
-        last_store = max(m.end() for m in re.finditer(r"buffer_store_dwordx4", body))
+        last_store = max(m.end() for m in re.finditer(r"buffer_store_dwordx4[^\n]*\bsc1\b", body))
         rest = body[last_store:]
         wait = re.search(r"s_waitcnt vmcnt\(0\)", rest)
         barrier = re.search(r"s_barrier", rest)
