@@ -150,8 +150,7 @@ typedef struct atom_config {
                                   for staged calls also 512 (a wider
                                   zero-staging request is
                                   ATOM_ERR_UNSUPPORTED); 0: chosen per
-                                  collective and size (staged: 256 for
-                                  AllGather, 512 for AllReduce) */
+                                  collective and size (staged: 512) */
 } atom_config;
 
 /* The collective that a pair of layouts and an op names (Figure 4/6,

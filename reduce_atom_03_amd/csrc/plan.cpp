@@ -154,8 +154,8 @@ bool buffer_ok(const void* p, int64_t bytes, int esize)
 // per workgroup: many small tiles keep the most bytes in flight, so one
 // slot per lane wins for the scatter-reduce, the fused AllReduce and the
 // fan-out copy, two for the exchange (AllToAll(V)) and for reduces of at
-// most 4 sources; the flat copy keeps 256-lane tiles of four slots per
-// lane. The reduce kernel is built for U in {1, 2, 4} with U * P <= 32.
+// most 4 sources; the flat copy uses 128-lane tiles of two slots per lane.
+// The reduce kernel is built for U in {1, 2, 4} with U * P <= 32.
 int32_t pick_u_reduce(int nsrc, int32_t mode, int32_t stages)
 {
     int32_t u = stages ? std::min<int32_t>(stages, 4)
@@ -170,7 +170,7 @@ int32_t pick_u_copy(int32_t kind, int nseg, int32_t stages)
     if (stages)
         return stages;
     if (nseg == 1)
-        return 4;                           // one flat copy: 16 KiB tiles
+        return 2;                           // one flat copy: 4 KiB tiles
     return kind == CK_FANOUT ? 1 : 2;       // AllGather fan-out / AllToAll(V) exchange
 }
 
@@ -349,10 +349,11 @@ void build_copy(Plan* p, int32_t kind, int P, const void* const* srcs, int nsrc,
     p->vec = vec ? 1 : 0;
     p->U = vec ? pick_u_copy(kind, nseg, c.stages) : 1;
     // 64-lane tiles: +7% on the exchange and +2% on the fan-out, whose
-    // tiles write P times what they read; a flat copy keeps 256-lane,
-    // 16 KiB tiles so each tile's segment lookup is amortized over enough
-    // bytes.
-    p->wg = (vec && nseg > 1) ? 64 : 256;
+    // tiles write P times what they read. A flat copy of 256 MiB with
+    // streaming stores, cold on MI355X: 128 lanes x 2 slots (4 KiB tiles)
+    // 6.33 TB/s, 256 x 2 6.25, 256 x 4 5.70, and 1 KiB tiles 4.7 (the
+    // workgroup dispatch rate bounds a grid of that many small tiles).
+    p->wg = !vec ? 256 : (nseg > 1 ? 64 : 128);
     int64_t bytes = 0;
     for (int s = 0; s < nseg; ++s)
         bytes += cnt[s] * row_bytes;
@@ -765,11 +766,11 @@ atom_status plan_collective(const atom_layout* in, const atom_layout* out, atom_
         a.nt_store = (c.flags & ATOM_F_NO_NT) ? 0 : 1;
         a.wait_ticks = c.wait_us;         // converted to clock ticks at launch
         p->vec = 1;
-        // Lanes per workgroup: 256 for the AllGather; 512 for the composed
-        // AllReduce, whose reducing stage reads P inputs per staged byte and
-        // gains from the extra waves (+5 % measured; the AllGather does not
-        // change).
-        p->wg = c.lanes ? c.lanes : (kind == ATOM_COLL_ALL_GATHER ? 256 : 512);
+        // Lanes per workgroup: 512 (two persistent workgroups of 8 waves per
+        // CU). Measured on MI355X with streaming output stores: the composed
+        // AllReduce, whose reducing stage reads P inputs per staged byte,
+        // +5 % over 256 lanes; the AllGather of 8 x 64 MiB +2 %.
+        p->wg = c.lanes ? c.lanes : 512;
         // 16-byte slots per lane in flight: 8 measured best for the staged
         // AllGather (+10% over 4); the AllReduce's depths are fixed by its
         // kernel (2 while reducing P <= 8 inputs, 8 while fanning out).
