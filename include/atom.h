@@ -123,7 +123,11 @@ typedef struct atom_layout {
 
 /* Execution options; NULL means defaults. Zero fields take defaults too. */
 #define ATOM_F_STAGED 0x1u     /* run through SNAC with a staging ring */
-#define ATOM_F_NO_NT  0x2u     /* use ordinary (cached) stores for outputs */
+#define ATOM_F_NO_NT  0x2u     /* use ordinary (cached) stores for every output.
+                                 Default: streaming (non-temporal) stores,
+                                 except for zero-staging messages under
+                                 1 MiB, whose outputs are kept in the caches
+                                 for the operation that reads them next */
 #define ATOM_F_XCD_ORDER 0x4u /* zero-staging kernels give each XCD one
                                  contiguous range of tiles (default: plain
                                  workgroup order; measured within noise) */
