@@ -183,7 +183,14 @@ typedef struct atom_plan_info {
     int64_t chunk_bytes;       /* SNAC chunk, when staged */
     int64_t num_chunks;        /* SNAC chunks, when staged */
     int32_t ring_slots;
-    int32_t num_wgs;           /* workgroups the launch would use */
+    int32_t num_wgs;           /* workgroups the launch would use (all rows) */
+    int32_t lanes;             /* threads per workgroup */
+    int32_t stages;            /* 16-byte slots per lane per tile (staged:
+                                  in flight while fanning out) */
+    int32_t streaming_stores;  /* 1: outputs written with non-temporal
+                                  stores; 0: ordinary stores */
+    int32_t grid_rows;         /* 1, or the parts of a small uniform reduce
+                                  launched as a tiles x parts grid */
 } atom_plan_info;
 
 /* Atom copy (abstract: the copy primitive). Copies `bytes` bytes from src to

@@ -71,6 +71,10 @@ class AtomPlanInfo(ctypes.Structure):
         ("num_chunks", ctypes.c_int64),
         ("ring_slots", ctypes.c_int32),
         ("num_wgs", ctypes.c_int32),
+        ("lanes", ctypes.c_int32),
+        ("stages", ctypes.c_int32),
+        ("streaming_stores", ctypes.c_int32),
+        ("grid_rows", ctypes.c_int32),
     ]
 
 

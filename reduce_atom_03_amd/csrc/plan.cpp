@@ -984,6 +984,16 @@ void plan_fill_info(const Plan& p, atom_plan_info* info)
     info->ring_slots = p.slots;
     const int64_t rows = (p.exec == EX_REDUCE && p.ra.grid_parts > 0) ? p.ra.grid_parts : 1;
     info->num_wgs = p.exec == EX_NONE ? 0 : static_cast<int32_t>(p.grid * rows);
+    if (p.exec == EX_NONE)
+        return;
+    info->lanes = p.wg;
+    info->stages = p.U;
+    info->grid_rows = static_cast<int32_t>(rows);
+    switch (p.exec) {
+    case EX_REDUCE: info->streaming_stores = p.ra.nt_store; break;
+    case EX_COPY: info->streaming_stores = p.ca.nt_store; break;
+    default: info->streaming_stores = p.sa.nt_store; break;
+    }
 }
 
 // Table 3: R*tau rounded to the closest power of two (ties upward).

@@ -380,3 +380,57 @@ def test_coaligned_offsets_plan_the_vector_path():
         assert st == A.OK and info.vector_path == 0
         st, info = Q(A.PARTITIONED, A.SHARD, A.OP_SUM, P=P, n=n + 1, ins=ins, outs=outs)
         assert st == A.OK and info.vector_path == 0      # partition k moves the offset
+
+
+def _plan(kin, kout, op, P, n, in_bytes, out_bytes, cfg=None):
+    st, info = Q(kin, kout, op, P=P, n=n, cfg=cfg, ins=fake(P, in_bytes),
+                 outs=fake(P, out_bytes, start=BASE + (1 << 40)))
+    assert st == A.OK
+    return info
+
+
+def test_launch_shapes_and_store_policy():
+    """The planner's measured defaults on MI355X: 64-lane one-tile workgroups
+    for the 8-way reduce (1 slot per lane), the fused AllReduce (1) and
+    AllToAll (2); 128 lanes x 2 slots for a flat copy; 512 lanes for staged
+    calls. Outputs of large messages are written with streaming stores,
+    those of the latency path (< 1 MiB per stream) with ordinary ones, and
+    ATOM_F_NO_NT makes every store ordinary."""
+    P, big = 8, 256 * MiB
+    rs = _plan(A.PARTITIONED, A.SHARD, A.OP_SUM, P, big // 2 // P, big, big // P)
+    assert (rs.lanes, rs.stages, rs.streaming_stores, rs.grid_rows) == (64, 1, 1, 1)
+    assert rs.num_wgs == big // 1024
+    ar = _plan(A.PARTITIONED, A.GATHERED, A.OP_SUM, P, big // 2 // P, big, big)
+    assert (ar.lanes, ar.stages, ar.streaming_stores) == (64, 1, 1)
+    a2a = _plan(A.PARTITIONED, A.TRANSPOSED, A.OP_COPY, P, big // 2 // P, big, big)
+    assert (a2a.lanes, a2a.stages, a2a.streaming_stores) == (64, 2, 1)
+    flat = _plan(A.SHARD, A.GATHERED, A.OP_COPY, 1, big // 2, big, big)
+    assert (flat.lanes, flat.stages, flat.streaming_stores) == (128, 2, 1)
+    assert flat.num_wgs == big // (128 * 2 * 16)
+    ag = _plan(A.SHARD, A.GATHERED, A.OP_COPY, P, 64 * MiB // 2, 64 * MiB, 512 * MiB,
+               cfg=A.config(flags=A.F_STAGED))
+    assert (ag.staged, ag.lanes, ag.stages, ag.streaming_stores) == (1, 512, 8, 1)
+    no_nt = _plan(A.PARTITIONED, A.SHARD, A.OP_SUM, P, big // 2 // P, big, big // P,
+                  cfg=A.config(flags=A.F_NO_NT))
+    assert no_nt.streaming_stores == 0
+    # latency path: the decode AllReduce (8 x 7168 bf16) and a small 8-way
+    # ReduceScatter; the latter as a tiles x parts grid
+    dec = _plan(A.PARTITIONED, A.GATHERED, A.OP_SUM, P, 7168 // P, 7168 * 2, 7168 * 2)
+    assert (dec.lanes, dec.stages, dec.streaming_stores, dec.num_wgs) == (64, 1, 0, 14)
+    small = _plan(A.PARTITIONED, A.SHARD, A.OP_SUM, P, 4096, P * 8192, 8192)
+    assert (small.grid_rows, small.streaming_stores) == (P, 0)
+    assert small.num_wgs == P * 8
+    ag8 = _plan(A.SHARD, A.GATHERED, A.OP_COPY, P, 4096, 8192, P * 8192)
+    assert (ag8.lanes, ag8.stages, ag8.streaming_stores, ag8.num_wgs) == (64, 1, 0, 64)
+
+
+def test_uniform_grid_only_for_equal_aligned_small_parts():
+    """A ReduceScatterV (unequal parts) and any large reduce keep the
+    one-dimensional grid that finds each tile's part in the part table."""
+    P = 8
+    counts = np.array([100, 3, 50, 7, 64, 1, 9, 22], dtype=np.int64)
+    st, info = Q(A.PARTITIONED, A.SHARD, A.OP_SUM, P=P, n=0, counts=counts, row=8,
+                 ins=fake(P, int(counts.sum()) * 16), outs=fake(P, 4096, start=BASE + (1 << 40)))
+    assert st == A.OK and info.grid_rows == 1
+    big = _plan(A.PARTITIONED, A.SHARD, A.OP_SUM, P, 1 << 21, P * (1 << 22), 1 << 22)
+    assert big.grid_rows == 1
