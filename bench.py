@@ -305,23 +305,34 @@ def main():
     # Back to back: 400 calls queued behind a spin kernel (so that the host's
     # submission, slower than the GPU per call, does not pace them) with one
     # event pair around all of them: the GPU time per call of a loop of
-    # collectives, the convention of collective benchmarks' time per op.
+    # collectives, the convention of collective benchmarks' time per op. The
+    # spin is about 20 ms at the calibrated rate, several times the ~3 ms
+    # the host takes to enqueue a batch; batches whose enqueue outlasted half
+    # the spin are counted (`back_to_back_host_paced_batches`, of
+    # `back_to_back_batches`); each figure is the median over its 9 batches.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1000000)
     e0.record(stream)
     torch.cuda._sleep(1000000)
     e1.record(stream)
     e1.synchronize()
-    spin = int(1e6 * 6.0 / max(e0.elapsed_time(e1), 1e-3))      # about 6 ms of spin
+    ms_per_mcycle = max(e0.elapsed_time(e1), 1e-3)
+    spin_ms = 20.0
+    spin = int(1e6 * spin_ms / ms_per_mcycle)
+    paced = []
 
     def back_to_back_us(fn, n=400, reps=9):
         v = []
         for _ in range(reps):
             torch.cuda._sleep(spin)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            h0 = time.perf_counter()
             a.record(stream)
             for _ in range(n):
                 fn()
             b.record(stream)
+            if (time.perf_counter() - h0) * 1e3 > spin_ms / 2:
+                paced.append(1)
             b.synchronize()
             v.append(a.elapsed_time(b) * 1e3 / n)
         return round(float(np.median(v)), 2)
@@ -384,6 +395,8 @@ def main():
         "host_us_per_call_8KiB": round(host_us, 2),
         "graph_us_per_call_8KiB": round(graph_us, 2),
         "back_to_back_us_per_call": b2b,
+        "back_to_back_host_paced_batches": len(paced),
+        "back_to_back_batches": 9 * len(b2b),
         "decode_allreduce_latency": dec_lat,
         "latency_samples": args.lat_iters,
         "p50_us_launch_floor_16B_copy": round(float(np.percentile(floor, 50)), 2),

@@ -91,28 +91,59 @@ __device__ __forceinline__ void copy_bytes(const CopyArgs& a, const Seg& g, int6
     }
 }
 
+// Geometry of segment s of the uniform form (every segment cnt[0] rows),
+// computed without walking the counts.
+__device__ __forceinline__ Seg seg_uniform(const CopyArgs& a, int s)
+{
+    Seg g;
+    g.bytes = static_cast<int64_t>(a.cnt[0]) * a.row_bytes;
+    if (a.kind == CK_FANOUT) {
+        g.src = static_cast<const char*>(a.src[s]);
+        g.dst_off = static_cast<int64_t>(s) * g.bytes;
+        g.dst = -1;
+    } else {
+        const int r = s / a.P, j = s - r * a.P;
+        g.src = static_cast<const char*>(a.src[r]) + static_cast<int64_t>(j) * g.bytes;
+        g.dst_off = static_cast<int64_t>(r) * g.bytes;
+        g.dst = j;
+    }
+    return g;
+}
+
 // HEADS: some segment starts off a 16-byte boundary (instantiated apart so
-// that aligned plans run without the per-tile head check).
-template <int U, bool HEADS>
+// that aligned plans run without the per-tile head check). GRID: the uniform
+// form (grid_segs > 0): the segment is blockIdx.y and the tile within it
+// blockIdx.x, so nothing is looked up before the loads.
+template <int U, bool HEADS, bool GRID>
 __global__ __launch_bounds__(256) void k_copy_vec(const CopyArgs a)
 {
+    static_assert(!(HEADS && GRID), "the uniform form has no heads");
     const int lane = threadIdx.x;
     const int nthr = blockDim.x;
     const bool nt = a.nt_store != 0;
     const bool remap = a.xcd_remap != 0;
-    for (int64_t base = 0; base < a.ntiles; base += gridDim.x) {
-        const int64_t t = tile_of(base, remap);
-        if (t >= a.ntiles)
-            continue;
-        const int s = seg_of_tile(a, t);
-        Seg g = seg_geometry(a, s);
+    const int64_t nloop = GRID ? 1 : a.ntiles;
+    for (int64_t base = 0; base < nloop; base += gridDim.x) {
+        int s;
+        int64_t tip;                                      // tile within the segment
+        if (GRID) {
+            s = blockIdx.y;
+            tip = blockIdx.x;
+        } else {
+            const int64_t t = tile_of(base, remap);
+            if (t >= a.ntiles)
+                continue;
+            s = seg_of_tile(a, t);
+            tip = t - a.seg_tile_begin[s];
+        }
+        Seg g = GRID ? seg_uniform(a, s) : seg_geometry(a, s);
         // The segment's head (bytes before the first 16-byte boundary, when
         // its source and destinations are off alignment by the same amount)
         // is copied element by element by the first lanes of its first tile;
         // the tiles then cover the rest from that boundary.
         const int h = HEADS ? a.head[s] : 0;
         if (HEADS && h > 0) {
-            if (t == a.seg_tile_begin[s] && lane * a.esize < h)
+            if (tip == 0 && lane * a.esize < h)
                 copy_bytes(a, g, static_cast<int64_t>(lane) * a.esize,
                            static_cast<int64_t>(lane + 1) * a.esize);
             g.src += h;
@@ -122,7 +153,7 @@ __global__ __launch_bounds__(256) void k_copy_vec(const CopyArgs a)
         // Tile start in the segment; the first tile may start before the
         // segment (negative offsets are skipped) so that tiles are aligned
         // at the destination.
-        int64_t b0 = (t - a.seg_tile_begin[s]) * a.tile_bytes;
+        int64_t b0 = tip * a.tile_bytes;
         if (a.align) {
             const char* d = static_cast<const char*>(a.dst[g.dst >= 0 ? g.dst : 0]) + g.dst_off;
             b0 -= seg_tile_shift(reinterpret_cast<uintptr_t>(d), a.tile_bytes);
@@ -193,12 +224,18 @@ hipError_t launch_copy(const Plan& p, hipStream_t stream)
     bool heads = false;
     for (int s = 0; s < p.ca.nseg; ++s)
         heads = heads || p.ca.head[s] != 0;
+    const int gs = p.ca.grid_segs;
+    if (gs != 0 && (gs != p.ca.nseg || gs > 65535 || heads || p.grid > 0x7fffffff))
+        return hipErrorInvalidValue;
+    const dim3 grid2(static_cast<unsigned>(p.grid), static_cast<unsigned>(gs > 0 ? gs : 1));
 #define ATOM_COPY_VEC(UU)                                                  \
     case UU:                                                               \
-        if (heads)                                                         \
-            k_copy_vec<UU, true><<<grid, block, 0, stream>>>(p.ca);        \
+        if (gs > 0)                                                        \
+            k_copy_vec<UU, false, true><<<grid2, block, 0, stream>>>(p.ca); \
+        else if (heads)                                                    \
+            k_copy_vec<UU, true, false><<<grid, block, 0, stream>>>(p.ca); \
         else                                                               \
-            k_copy_vec<UU, false><<<grid, block, 0, stream>>>(p.ca);       \
+            k_copy_vec<UU, false, false><<<grid, block, 0, stream>>>(p.ca); \
         break;
     switch (p.U) {
     ATOM_COPY_VEC(1) ATOM_COPY_VEC(2) ATOM_COPY_VEC(4) ATOM_COPY_VEC(8)

@@ -83,6 +83,12 @@ struct CopyArgs {
     int32_t align;                     // 1: tiles start at addresses aligned to
                                        // tile_bytes in the destination (see
                                        // seg_tile_shift)
+    int32_t grid_segs;                 // 0: one-dimensional grid, each tile finds
+                                       // its segment in seg_tile_begin. Else (small
+                                       // messages) the uniform form: grid_segs
+                                       // segments of cnt[0] rows, no heads, the same
+                                       // tile count each; segment = blockIdx.y, tile
+                                       // within it = blockIdx.x
     int32_t cnt[kMaxSegs];             // rows per segment
     int32_t seg_tile_begin[kMaxSegs + 1];
     uint8_t head[kMaxSegs];            // vector path, per segment: bytes before its

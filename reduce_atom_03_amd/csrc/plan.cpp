@@ -403,6 +403,19 @@ void build_copy(Plan* p, int32_t kind, int P, const void* const* srcs, int nsrc,
     a.xcd_remap = (c.flags & ATOM_F_XCD_ORDER) ? 1 : 0;
     p->grid = pick_grid(t, c.num_wgs);
     p->exec = t > 0 ? EX_COPY : EX_NONE;
+    // Uniform form of the latency path (as for the reduce family): equal
+    // segments, no heads, the same tile count each, one tile per workgroup;
+    // the grid is tiles-per-segment x segments.
+    a.grid_segs = 0;
+    const int64_t tps = nseg > 0 ? a.seg_tile_begin[1] : 0;
+    bool uniform = vec && t > 0 && bytes < kSmallSlots * kVecBytes && !a.xcd_remap &&
+                   c.num_wgs == 0 && nseg <= 65535;
+    for (int s = 0; s < nseg && uniform; ++s)
+        uniform = cnt[s] == cnt[0] && a.head[s] == 0 && a.seg_tile_begin[s] == s * tps;
+    if (uniform) {
+        a.grid_segs = nseg;
+        p->grid = tps;
+    }
 }
 
 // Limit that keeps per-segment tile indices in 32 bits.
@@ -982,7 +995,9 @@ void plan_fill_info(const Plan& p, atom_plan_info* info)
     info->chunk_bytes = p.chunk_bytes;
     info->num_chunks = info->staged ? p.sa.nchunks : 0;
     info->ring_slots = p.slots;
-    const int64_t rows = (p.exec == EX_REDUCE && p.ra.grid_parts > 0) ? p.ra.grid_parts : 1;
+    const int64_t rows = (p.exec == EX_REDUCE && p.ra.grid_parts > 0)  ? p.ra.grid_parts
+                         : (p.exec == EX_COPY && p.ca.grid_segs > 0) ? p.ca.grid_segs
+                                                                       : 1;
     info->num_wgs = p.exec == EX_NONE ? 0 : static_cast<int32_t>(p.grid * rows);
     if (p.exec == EX_NONE)
         return;

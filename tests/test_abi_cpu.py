@@ -422,6 +422,9 @@ def test_launch_shapes_and_store_policy():
     assert small.num_wgs == P * 8
     ag8 = _plan(A.SHARD, A.GATHERED, A.OP_COPY, P, 4096, 8192, P * 8192)
     assert (ag8.lanes, ag8.stages, ag8.streaming_stores, ag8.num_wgs) == (64, 1, 0, 64)
+    assert ag8.grid_rows == P                  # tiles x segments grid
+    a2a = _plan(A.PARTITIONED, A.TRANSPOSED, A.OP_COPY, P, 512, P * 1024, P * 1024)
+    assert (a2a.grid_rows, a2a.num_wgs) == (P * P, P * P)
 
 
 def test_uniform_grid_only_for_equal_aligned_small_parts():
@@ -434,3 +437,9 @@ def test_uniform_grid_only_for_equal_aligned_small_parts():
     assert st == A.OK and info.grid_rows == 1
     big = _plan(A.PARTITIONED, A.SHARD, A.OP_SUM, P, 1 << 21, P * (1 << 22), 1 << 22)
     assert big.grid_rows == 1
+    # the same for the copy family: an AllGatherV and a large AllGather
+    st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=P, n=0, counts=counts, row=8,
+                 ins=fake(P, 4096), outs=fake(P, int(counts.sum()) * 16, start=BASE + (1 << 40)))
+    assert st == A.OK and info.grid_rows == 1
+    ag = _plan(A.SHARD, A.GATHERED, A.OP_COPY, P, 1 << 21, 1 << 22, P * (1 << 22))
+    assert ag.grid_rows == 1
