@@ -306,10 +306,11 @@ def main():
     # submission, slower than the GPU per call, does not pace them) with one
     # event pair around all of them: the GPU time per call of a loop of
     # collectives, the convention of collective benchmarks' time per op. The
-    # spin is about 20 ms at the calibrated rate, several times the ~3 ms
-    # the host takes to enqueue a batch; batches whose enqueue outlasted half
-    # the spin are counted (`back_to_back_host_paced_batches`, of
-    # `back_to_back_batches`); each figure is the median over its 9 batches.
+    # spin is about 50 ms at the calibrated rate, many times the 3-10 ms the
+    # host takes to enqueue a batch; batches whose enqueue outlasted the spin
+    # (so the GPU may have waited for the host) are counted
+    # (`back_to_back_host_paced_batches`, of `back_to_back_batches`); each
+    # figure is the median over its 9 batches.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda._sleep(1000000)
     e0.record(stream)
@@ -317,7 +318,7 @@ def main():
     e1.record(stream)
     e1.synchronize()
     ms_per_mcycle = max(e0.elapsed_time(e1), 1e-3)
-    spin_ms = 20.0
+    spin_ms = 50.0
     spin = int(1e6 * spin_ms / ms_per_mcycle)
     paced = []
 
@@ -331,7 +332,7 @@ def main():
             for _ in range(n):
                 fn()
             b.record(stream)
-            if (time.perf_counter() - h0) * 1e3 > spin_ms / 2:
+            if (time.perf_counter() - h0) * 1e3 > spin_ms:
                 paced.append(1)
             b.synchronize()
             v.append(a.elapsed_time(b) * 1e3 / n)
