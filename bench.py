@@ -302,13 +302,14 @@ def main():
         b.synchronize()
         gl.append(a.elapsed_time(b) * 1e3 / 100)
     graph_us = float(np.median(gl))
-    # Back to back: 400 calls queued behind a spin kernel (so that the host's
+    # Back to back: 200 calls queued behind a spin kernel (so that the host's
     # submission, slower than the GPU per call, does not pace them) with one
     # event pair around all of them: the GPU time per call of a loop of
-    # collectives, the convention of collective benchmarks' time per op. The
-    # spin is about 50 ms at the calibrated rate, many times the 3-10 ms the
-    # host takes to enqueue a batch; batches whose enqueue outlasted the spin
-    # (so the GPU may have waited for the host) are counted
+    # collectives, the convention of collective benchmarks' time per op. A
+    # batch of 200 fits in the runtime's command queue (with 400 the host
+    # blocks until the spin ends and the batch's tail is host-paced); the
+    # spin is about 20 ms at the calibrated rate against ~1.5 ms of enqueue.
+    # Batches whose enqueue outlasted half the spin are counted
     # (`back_to_back_host_paced_batches`, of `back_to_back_batches`); each
     # figure is the median over its 9 batches.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -318,11 +319,11 @@ def main():
     e1.record(stream)
     e1.synchronize()
     ms_per_mcycle = max(e0.elapsed_time(e1), 1e-3)
-    spin_ms = 50.0
+    spin_ms = 20.0
     spin = int(1e6 * spin_ms / ms_per_mcycle)
     paced = []
 
-    def back_to_back_us(fn, n=400, reps=9):
+    def back_to_back_us(fn, n=200, reps=9):
         v = []
         for _ in range(reps):
             torch.cuda._sleep(spin)
@@ -332,7 +333,7 @@ def main():
             for _ in range(n):
                 fn()
             b.record(stream)
-            if (time.perf_counter() - h0) * 1e3 > spin_ms:
+            if (time.perf_counter() - h0) * 1e3 > spin_ms / 2:
                 paced.append(1)
             b.synchronize()
             v.append(a.elapsed_time(b) * 1e3 / n)
