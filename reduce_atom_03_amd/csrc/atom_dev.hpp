@@ -204,10 +204,9 @@ __device__ __forceinline__ void st16_agent(__amdgpu_buffer_rsrc_t r, int64_t off
 // Streaming 16-byte load through a buffer resource: the stream's base stays
 // in scalar registers and each lane supplies a 32-bit offset, so a kernel
 // reading P streams holds no 64-bit per-lane address per stream in VGPRs
-// (P = 8: 16 VGPRs, the difference between 7 and 8 waves per SIMD on
-// gfx950). The resource covers [base, base + bytes); the hardware drops
-// accesses outside it. Non-temporal, like ld16_stream.
-
+// (the 8-way reduce: 65 -> 50 VGPRs). The resource covers
+// [base, base + bytes); the hardware drops accesses outside it.
+// Non-temporal, like ld16_stream.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(const void* base, uint32_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
