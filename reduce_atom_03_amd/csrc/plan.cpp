@@ -275,9 +275,10 @@ void build_reduce(Plan* p, int nsrc, const void* const* srcs, int ndst, void* co
     // tiles-per-part x parts and a workgroup knows its part and tile from
     // its coordinates, with no walk through the part table before its first
     // load. Measured on MI355X: the decode AllReduce (8 x b x 7168 bf16)
-    // went from 3.36 to 3.10 us per call back to back; large messages keep
-    // the one-dimensional grid, which was 3-6 % faster for the cold 8-way
-    // ReduceScatter and fused AllReduce of 8 x 256 MiB.
+    // went from 3.36 to 3.10 us per call back to back. For large messages
+    // the two grids measured within noise of each other (8-way
+    // ReduceScatter of 8 x 256 MiB: 6.25-6.37 against 6.29-6.33 TB/s), so
+    // they keep the one-dimensional grid and its grid-stride loop.
     a.grid_parts = 0;
     const int64_t L = part_off[1] - part_off[0];
     const int64_t tpp = nparts > 0 ? a.tile_begin[1] : 0;
