@@ -354,8 +354,10 @@ void build_copy(Plan* p, int32_t kind, int P, const void* const* srcs, int nsrc,
         std::memset(a.head, 0, sizeof a.head);
     p->vec = vec ? 1 : 0;
     p->U = vec ? pick_u_copy(kind, nseg, c.stages) : 1;
-    // 64-lane tiles: +7% on the exchange and +2% on the fan-out, whose
-    // tiles write P times what they read. A flat copy of 256 MiB with
+    // 64-lane tiles over 256-lane ones, cold with streaming stores on
+    // MI355X: +2 % on the exchange (AllToAllV, 2 slots per lane) and +2 % on
+    // the fan-out (AllGather, 1 slot), whose tiles write P times what they
+    // read. A flat copy of 256 MiB with
     // streaming stores, cold on MI355X: 128 lanes x 2 slots (4 KiB tiles)
     // 6.33 TB/s, 256 x 2 6.25, 256 x 4 5.70, and 1 KiB tiles 4.7 (the
     // workgroup dispatch rate bounds a grid of that many small tiles).
