@@ -34,9 +34,13 @@
  *  - Zero-sized work returns ATOM_OK without launching anything.
  *  - Out of place only: an output byte range that overlaps any input range
  *    or another output range is ATOM_ERR_INVALID_ARG.
- *  - Any element-aligned pointer is accepted. 16-byte aligned buffers whose
- *    partitions keep 16-byte alignment take the 128-bit vector path; others
- *    take an element-wise path with the same results.
+ *  - Any element-aligned pointer is accepted, by every entry point. 16-byte
+ *    aligned buffers whose partitions keep 16-byte alignment take the
+ *    128-bit vector path; others take an element-wise path with the same
+ *    results (zero-staging calls: streams that sit at a common offset from
+ *    16-byte alignment stay vectorized with element-wise edges; staged
+ *    calls choose per segment, a segment being the bytes one source sends
+ *    to one destination).
  *  - Calls that use the per-device workspace (the SNAC staging ring and its
  *    flags) are ordered by their stream; two such calls on different streams
  *    of one device must not overlap in time.
@@ -155,6 +159,14 @@ typedef struct atom_config {
                                   zero-staging request is
                                   ATOM_ERR_UNSUPPORTED); 0: chosen per
                                   collective and size (staged: 512) */
+    int32_t jitter_us;         /* test hook of the staged path, 0..10000 (0:
+                                  off): before each notify and each consume,
+                                  the task's workgroup waits a pseudo-random
+                                  0..jitter_us microseconds drawn from
+                                  (jitter_seed, task), so that hand-offs run
+                                  at other than their natural timing. The
+                                  result is unchanged; only time is added. */
+    uint32_t jitter_seed;
 } atom_config;
 
 /* The collective that a pair of layouts and an op names (Figure 4/6,
@@ -213,14 +225,17 @@ atom_status atom_reduce(void* dst, const void* const* srcs, int32_t nsrcs,
  * Table 2). The pair (in->kind, out->kind, op) selects the collective as
  * listed at atom_collective_kind; other pairs return ATOM_ERR_UNSUPPORTED.
  * Both layouts must agree on nranks, dtype and (V forms) counts/row_elems;
- * out->counts may be NULL. With cfg->flags & ATOM_F_STAGED, AllGather and
- * AllReduce run through SNAC: chunks of cfg->chunk_bytes are staged in a
- * ring of cfg->ring_slots slots, notified through device-memory flags and
- * consumed by other workgroups; the staged path needs 16-byte aligned
- * buffers and partitions (else ATOM_ERR_UNSUPPORTED). Returns ATOM_OK,
- * ATOM_ERR_INVALID_ARG, ATOM_ERR_UNSUPPORTED, ATOM_ERR_NOMEM or
- * ATOM_ERR_HIP. A SNAC wait that runs out on the device is reported by
- * atom_sync_status, not here (the call returns before the kernel runs). */
+ * out->counts may be NULL. With cfg->flags & ATOM_F_STAGED every collective
+ * runs through SNAC (abstract; Figure 6; Figure 16 for the V forms on
+ * ordinary buffers): its layouts become a list of segments (the bytes one
+ * source sends to one or every destination), chunks of cfg->chunk_bytes of
+ * each are staged (copied, or reduced in rank order) in a ring of
+ * cfg->ring_slots slots, notified through device-memory flags and consumed
+ * by other workgroups; the result equals the zero-staging one bit for bit.
+ * Returns ATOM_OK, ATOM_ERR_INVALID_ARG, ATOM_ERR_UNSUPPORTED,
+ * ATOM_ERR_NOMEM or ATOM_ERR_HIP. A SNAC wait that runs out on the device is
+ * reported by atom_sync_status, not here (the call returns before the
+ * kernel runs); only the call whose wait ran out is incomplete. */
 atom_status atom_collective(const atom_layout* in, const atom_layout* out,
                             atom_op op, const atom_config* cfg, void* stream);
 
@@ -231,8 +246,13 @@ atom_status atom_plan_query(const atom_layout* in, const atom_layout* out,
                             atom_plan_info* info);
 
 /* Synchronizes `stream`, then reads and clears this device's SNAC error
- * word: ATOM_ERR_TIMEOUT if a wait timed out since the last check, else
- * ATOM_OK (ATOM_ERR_HIP if the synchronization fails). */
+ * word: ATOM_ERR_TIMEOUT if a wait timed out since the
+ * last check, else ATOM_OK (ATOM_ERR_HIP if the synchronization fails). A
+ * timeout leaves incomplete output in the call it happened in only; calls
+ * after it wait normally. (A HIP graph replays one captured call with one
+ * sequence number: after a timeout in a replay, the later replays of that
+ * same captured call give up their waits too until this check clears the
+ * word.) */
 atom_status atom_sync_status(void* stream);
 
 /* Table 3: bandwidth-delay product R*tau in bytes rounded to the closest

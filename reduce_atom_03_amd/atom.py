@@ -55,6 +55,8 @@ class AtomConfig(ctypes.Structure):
         ("piece_bytes", ctypes.c_int32),
         ("wait_us", ctypes.c_int32),
         ("lanes", ctypes.c_int32),
+        ("jitter_us", ctypes.c_int32),
+        ("jitter_seed", ctypes.c_uint32),
     ]
 
 
@@ -240,10 +242,11 @@ def _flatten(c):
 
 def config(chunk_bytes: int = 0, stages: int = 0, num_wgs: int = 0, flags: int = 0,
            ring_slots: int = 0, piece_bytes: int = 0, wait_us: int = 0,
-           lanes: int = 0) -> AtomConfig:
+           lanes: int = 0, jitter_us: int = 0, jitter_seed: int = 0) -> AtomConfig:
     return AtomConfig(chunk_bytes=chunk_bytes, stages=stages, num_wgs=num_wgs,
                       flags=flags, ring_slots=ring_slots, piece_bytes=piece_bytes,
-                      wait_us=wait_us, lanes=lanes)
+                      wait_us=wait_us, lanes=lanes, jitter_us=jitter_us,
+                      jitter_seed=jitter_seed)
 
 
 # --------------------------------------------------------- the C entry points

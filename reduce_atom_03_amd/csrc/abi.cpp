@@ -110,6 +110,17 @@ atom_status workspace(int64_t ring_bytes, hipStream_t stream, Workspace** out)
     return ATOM_OK;
 }
 
+// The next staged call's sequence number on a device (never 0, the error
+// word's "no timeout"): a wait that times out records it, and only waits of
+// the same call give up early because of it.
+uint32_t next_seq(Workspace* ws)
+{
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    if (++ws->seq == 0)
+        ws->seq = 1;
+    return ws->seq;
+}
+
 atom_status run(const Plan& p, void* stream)
 {
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -128,13 +139,13 @@ atom_status run(const Plan& p, void* stream)
     case EX_COPY:
         e = launch_copy(p, s);
         break;
-    case EX_SNAC_AG:
-    case EX_SNAC_AR: {
+    case EX_SNAC_COPY:
+    case EX_SNAC_REDUCE: {
         Workspace* ws = nullptr;
         atom_status st = workspace(p.ring_bytes, s, &ws);
         if (st != ATOM_OK)
             return st;
-        e = launch_snac(p, *ws, s);
+        e = launch_snac(p, *ws, next_seq(ws), s);
         break;
     }
     default:

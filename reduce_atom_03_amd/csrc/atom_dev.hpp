@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kargs.hpp"
 
 namespace atom {
@@ -184,6 +186,9 @@ template <> struct Elem<float> {
 // which the cross-XCD flag polling below already relies. The buffer
 // resource covers [base, base + bytes), and the hardware drops accesses
 // outside it.
+
+// Bytes rounded up to whole 16-byte vectors.
+__device__ __forceinline__ int64_t ceil16(int64_t bytes) { return (bytes + 15) & ~int64_t(15); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t ring_rsrc(const void* base, int64_t bytes)
 {

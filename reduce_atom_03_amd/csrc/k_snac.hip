@@ -5,20 +5,28 @@
 // shared by every collective, derived from the layouts; Figure 6 shows ranks
 // staging chunks incrementally while consumers gather them; Table 3 sizes a
 // chunk as the bandwidth-delay product; Figures 9 and 10 contrast ordinary
-// buffers (staged) with peer-accessible ones (zero staging).
+// buffers (staged) with peer-accessible ones (zero staging); Figure 16 runs
+// the variable-length collectives on ordinary buffers.
 //
-// On one device the P ranks are P buffers and the hand-off between a
-// producer and its consumers crosses workgroups (and XCDs, each with its own
-// L2) through device memory:
-//   Stage   a producer workgroup copies one piece of a chunk of partition k
-//           into a slot of the staging ring with agent-coherent stores;
+// On one device the P ranks are P buffers. The planner turns the layouts into
+// a list of segments (kargs.hpp: SnacKind), each a contiguous byte range that
+// one stage produces and one consume step delivers:
+//   AllGather(V)      copy z_k            -> every output, at z_k's place
+//   AllToAll(V)       copy x_r's block j  -> output j, after earlier sources
+//   ReduceScatter(V)  sum of partition k  -> output k
+//   AllReduce         sum of partition k  -> every output, at partition k
+// and the hand-off between a producer and its consumers crosses workgroups
+// (and XCDs, each with its own L2) through device memory:
+//   Stage   a producer workgroup copies (or reduces in rank order) one piece
+//           of a chunk into a slot of the staging ring with agent-coherent
+//           stores;
 //   Notify  once every wave's stores have completed it adds 1 to the
 //           slot's `ready` counter;
 //   Consume a consumer workgroup waits for `ready` == all pieces of the
 //           chunk, reads one piece from the slot with agent-coherent loads,
-//           writes it to every output (AllGather fan-out) and adds 1 to the
-//           slot's `freed` counter, which the producer of the chunk D
-//           places later waits for before reuse.
+//           writes it to its destination(s) and adds 1 to the slot's `freed`
+//           counter, which the producer of the chunk D places later waits
+//           for before reuse.
 // The ring is never touched by ordinary (L2-cached) accesses, so no task
 // needs an L2 write-back or invalidation.
 //
@@ -28,8 +36,9 @@
 // producers of chunk q, then the consumers of the last D chunks. A claimed
 // ticket belongs to a running workgroup, so the lowest unfinished task can
 // always proceed: no deadlock for any grid size or occupancy. Every wait is
-// bounded; on expiry the error word is set, the task is dropped, and later
-// waits give up at once, so the grid always drains.
+// bounded; on expiry the error word is set to the call's sequence number,
+// the task is dropped, and the call's later waits give up at once, so the
+// grid always drains (a later call, with another number, waits normally).
 #include <algorithm>
 
 #include "atom_dev.hpp"
@@ -71,13 +80,80 @@ __device__ __forceinline__ Task decode_task(const SnacArgs& a, int64_t t)
     return k;
 }
 
+// Where a segment's bytes come from and go to.
+struct SegGeo {
+    const char* src;   // copy stages: the segment's first source byte
+    int64_t src_off;   // reduce stages: byte offset of the segment in every source
+    int64_t dst_off;   // byte offset in the destination(s)
+    int64_t bytes;
+    int dst;           // destination index, or -1 for every destination
+};
+
+__device__ __forceinline__ SegGeo seg_geo(const SnacArgs& a, int s)
+{
+    SegGeo g;
+    g.bytes = static_cast<int64_t>(a.cnt[s]) * a.row_bytes;
+    g.src = nullptr;
+    g.src_off = 0;
+    if (a.kind == SK_EXCHANGE) {
+        const int r = s / a.P, j = s - r * a.P;
+        int64_t src_rows = 0, dst_rows = 0;
+        for (int jj = 0; jj < j; ++jj)       // source r's rows for earlier destinations
+            src_rows += a.cnt[r * a.P + jj];
+        for (int rr = 0; rr < r; ++rr)       // earlier sources' rows for destination j
+            dst_rows += a.cnt[rr * a.P + j];
+        g.src = static_cast<const char*>(a.src[r]) + src_rows * a.row_bytes;
+        g.dst_off = dst_rows * a.row_bytes;
+        g.dst = j;
+        return g;
+    }
+    int64_t rows = 0;                        // rows of the segments before s
+    for (int k = 0; k < s; ++k)
+        rows += a.cnt[k];
+    const int64_t off = rows * a.row_bytes;
+    if (a.kind == SK_GATHER) {
+        g.src = static_cast<const char*>(a.src[s]);
+        g.dst_off = off;
+        g.dst = -1;
+    } else if (a.kind == SK_SCATTER) {
+        g.src_off = off;
+        g.dst_off = 0;
+        g.dst = s;
+    } else {                                 // SK_ALLRED
+        g.src_off = off;
+        g.dst_off = off;
+        g.dst = -1;
+    }
+    return g;
+}
+
+// Segment and chunk-within-segment of chunk q.
+__device__ __forceinline__ void chunk_of(const SnacArgs& a, int64_t q, int* s, int64_t* c)
+{
+    if (a.interleave) {
+        *s = static_cast<int>(q % a.nseg);
+        *c = q / a.nseg;
+        return;
+    }
+    int lo = 0, hi = a.nseg - 1;           // largest s with chunk_begin[s] <= q
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a.chunk_begin[mid] <= q)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    *s = lo;
+    *c = q - a.chunk_begin[lo];
+}
+
 // Lane 0 waits until *flag >= target, bounded in wall-clock time (the
 // per-wait bound and the workgroup's whole-kernel budget, both in ticks of
 // the constant-rate device clock). The barrier then holds every wave until
 // the count was seen, so the waves' ring loads are issued after it. The
 // result is made wave-uniform with readfirstlane so every branch on it is
-// uniform. Returns false when the wait gave up (a timeout here or
-// elsewhere).
+// uniform. Returns false when the wait gave up (a timeout here, or earlier
+// in the same call).
 __device__ __forceinline__ bool wait_at_least(const SnacArgs& a, const unsigned long long* flag,
                                               unsigned long long target, long long t_begin,
                                               int* s_ok)
@@ -96,9 +172,9 @@ __device__ __forceinline__ bool wait_at_least(const SnacArgs& a, const unsigned 
                     __builtin_amdgcn_s_sleep(16);
                 if ((++it & 15u) == 0) {
                     const long long now = wall_clock64();
-                    if (__hip_atomic_load(a.error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0 ||
+                    if (__hip_atomic_load(a.error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.seq ||
                         now - w0 > a.wait_ticks || now - t_begin > a.budget_ticks) {
-                        __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_store(a.error, a.seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         ok = 0;
                         break;
                     }
@@ -111,14 +187,40 @@ __device__ __forceinline__ bool wait_at_least(const SnacArgs& a, const unsigned 
     return __builtin_amdgcn_readfirstlane(*s_ok) != 0;
 }
 
-// Stage producers: fill `bytes` bytes (a multiple of 16) of a ring slot.
-// Copy: partition k of its own input (AllGather).
+// Test hook (atom_config.jitter_us): lane 0 holds its workgroup for a
+// pseudo-random 0..jitter_ticks device-clock ticks, drawn from the seed, the
+// ticket and the point in the task, so that hand-offs are exercised at
+// timings other than the natural ones. The caller's barrier follows.
+__device__ __forceinline__ void jitter(const SnacArgs& a, int64_t ticket, uint32_t where)
+{
+    if (a.jitter_ticks > 0 && threadIdx.x == 0) {
+        uint32_t h = a.jitter_seed ^ (static_cast<uint32_t>(ticket) * 0x9E3779B9u) ^ (where * 0x85EBCA6Bu);
+        h ^= h >> 16;                      // integer finalizer (avalanche)
+        h *= 0x7FEB352Du;
+        h ^= h >> 15;
+        h *= 0x846CA68Bu;
+        h ^= h >> 16;
+        const long long d = static_cast<long long>(h % static_cast<uint32_t>(a.jitter_ticks + 1));
+        const long long t0 = wall_clock64();
+        while (wall_clock64() - t0 < d)
+            __builtin_amdgcn_s_sleep(4);
+    }
+}
+
+// ---- stages (vector path: every stream of the segment 16-byte aligned) ---
+// Each fills `bytes` bytes of a ring slot from segment byte `off`. A last
+// vector that runs past the segment's end is staged whole: its bytes beyond
+// the end are never consumed, and its load stays inside the 16-byte block of
+// the segment's last byte.
+
+// Copy: from the segment's source (AllGather, AllToAll).
 struct StageCopy {
     template <int U>
-    __device__ static void produce(const SnacArgs& a, int k, int64_t off, char* dst, int64_t bytes)
+    __device__ static void produce(const SnacArgs& a, const SegGeo& g, int64_t off, char* dst,
+                                   int64_t bytes)
     {
-        const char* src = static_cast<const char*>(a.src[k]) + off;
-        const auto ring = ring_rsrc(dst, bytes);
+        const char* src = g.src + off;
+        const auto ring = ring_rsrc(dst, ceil16(bytes));
         const int lane = threadIdx.x;
         const int nthr = blockDim.x;
         const int64_t step = static_cast<int64_t>(nthr) * U * kVecBytes;
@@ -140,15 +242,16 @@ struct StageCopy {
     }
 };
 
-// Reduce: partition k summed over the P inputs in rank order, rounded once
-// (the ReduceScatter half of the composed AllReduce, Figure 6).
+// Reduce: the segment's range summed over the P inputs in rank order,
+// rounded once (ReduceScatter, and its half of the composed AllReduce).
 template <typename T, int P>
 struct StageReduce {
     template <int U>
-    __device__ static void produce(const SnacArgs& a, int k, int64_t off, char* dst, int64_t bytes)
+    __device__ static void produce(const SnacArgs& a, const SegGeo& g, int64_t off, char* dst,
+                                   int64_t bytes)
     {
-        const int64_t base = static_cast<int64_t>(k) * a.part_bytes + off;
-        const auto ring = ring_rsrc(dst, bytes);
+        const int64_t base = g.src_off + off;
+        const auto ring = ring_rsrc(dst, ceil16(bytes));
         const int lane = threadIdx.x;
         const int nthr = blockDim.x;
         const int64_t step = static_cast<int64_t>(nthr) * U * kVecBytes;
@@ -179,14 +282,18 @@ struct StageReduce {
     }
 };
 
-// Consume: one piece from the slot to every output (AllGather fan-out).
+// Consume (vector path): one piece from the slot to its destination(s). A
+// last vector that ends past the segment is written in 2-byte units.
 template <int U>
-__device__ __forceinline__ void fan_out(const SnacArgs& a, const char* src, int64_t dst_off, int64_t bytes)
+__device__ __forceinline__ void consume_vec(const SnacArgs& a, const SegGeo& g, const char* src,
+                                            int64_t dst_off, int64_t bytes)
 {
     const int lane = threadIdx.x;
     const int nthr = blockDim.x;
     const bool nt = a.nt_store != 0;
-    const auto ring = ring_rsrc(src, bytes);
+    const auto ring = ring_rsrc(src, ceil16(bytes));
+    const int q0 = g.dst < 0 ? 0 : g.dst;
+    const int q1 = g.dst < 0 ? a.P : g.dst + 1;
     const int64_t step = static_cast<int64_t>(nthr) * U * kVecBytes;
     for (int64_t b0 = 0; b0 < bytes; b0 += step) {
         u32x4 x[U];
@@ -199,27 +306,104 @@ __device__ __forceinline__ void fan_out(const SnacArgs& a, const char* src, int6
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t off = static_cast<uint32_t>(u * nthr + lane) * kVecBytes;
-            if (b0 + off < bytes)
-                for (int q = 0; q < a.P; ++q)
+            const int64_t o = b0 + off;
+            if (o + kVecBytes <= bytes) {
+                for (int q = q0; q < q1; ++q)
                     st16(static_cast<char*>(a.dst[q]) + dst_off + b0, off, x[u], nt);
+            } else if (o < bytes) {
+                for (int q = q0; q < q1; ++q) {
+                    uint16_t* d = reinterpret_cast<uint16_t*>(static_cast<char*>(a.dst[q]) + dst_off + o);
+                    for (int h = 0; h < (bytes - o) / 2; ++h)
+                        d[h] = static_cast<uint16_t>(x[u][h >> 1] >> (16 * (h & 1)));
+                }
+            }
         }
     }
 }
 
+// ---- element-wise path: a segment with a stream off 16-byte alignment ----
+// Elements of E bytes (the element type's size) move one per lane at a time;
+// ring accesses keep the agent-coherent policy.
+
+template <typename E>
+__device__ __forceinline__ E ring_load(__amdgpu_buffer_rsrc_t r, int64_t off);
+template <>
+__device__ __forceinline__ uint16_t ring_load<uint16_t>(__amdgpu_buffer_rsrc_t r, int64_t off)
+{
+    return static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(off), 0, kCpolSc1));
+}
+template <>
+__device__ __forceinline__ uint32_t ring_load<uint32_t>(__amdgpu_buffer_rsrc_t r, int64_t off)
+{
+    return static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, kCpolSc1));
+}
+__device__ __forceinline__ void ring_store(__amdgpu_buffer_rsrc_t r, int64_t off, uint16_t v)
+{
+    __builtin_amdgcn_raw_buffer_store_b16(static_cast<short>(v), r, static_cast<int>(off), 0, kCpolSc1);
+}
+__device__ __forceinline__ void ring_store(__amdgpu_buffer_rsrc_t r, int64_t off, uint32_t v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(static_cast<int>(v), r, static_cast<int>(off), 0, kCpolSc1);
+}
+
+// Stage element by element: a copy, or the rank-order sum of the P inputs
+// (binary32, one rounding to T, as the vector path).
+template <typename T, bool REDUCE>
+__device__ __forceinline__ void produce_elem(const SnacArgs& a, const SegGeo& g, int64_t off,
+                                             char* dst, int64_t bytes)
+{
+    using E = typename std::conditional<sizeof(T) == 2, uint16_t, uint32_t>::type;
+    const auto ring = ring_rsrc(dst, ceil16(bytes));
+    const int64_t n = bytes / static_cast<int64_t>(sizeof(E));
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+        E v;
+        if (REDUCE) {
+            const int64_t e = (g.src_off + off) / static_cast<int64_t>(sizeof(T)) + i;
+            float acc = Elem<T>::load(a.src[0], e);
+            for (int r = 1; r < a.P; ++r)
+                acc = acc + Elem<T>::load(a.src[r], e);
+            if (sizeof(T) == 2)
+                v = static_cast<E>(f32_to_bf16_bits(acc));
+            else
+                v = static_cast<E>(__float_as_uint(acc));
+        } else {
+            v = reinterpret_cast<const E*>(g.src + off)[i];
+        }
+        ring_store(ring, i * static_cast<int64_t>(sizeof(E)), v);
+    }
+}
+
+template <typename E>
+__device__ __forceinline__ void consume_elem(const SnacArgs& a, const SegGeo& g, const char* src,
+                                             int64_t dst_off, int64_t bytes)
+{
+    const auto ring = ring_rsrc(src, ceil16(bytes));
+    const int q0 = g.dst < 0 ? 0 : g.dst;
+    const int q1 = g.dst < 0 ? a.P : g.dst + 1;
+    const int64_t n = bytes / static_cast<int64_t>(sizeof(E));
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+        const E v = ring_load<E>(ring, i * static_cast<int64_t>(sizeof(E)));
+        for (int q = q0; q < q1; ++q)
+            reinterpret_cast<E*>(static_cast<char*>(a.dst[q]) + dst_off)[i] = v;
+    }
+}
+
 // The persistent SNAC kernel: UP 16-byte slots per lane in flight while
-// staging, UC while fanning out, at most MAXT lanes per workgroup (256, or
-// 512 for the wide launches, so the default keeps its register budget). Every branch that encloses a barrier depends
-// only on wave-uniform values (the ticket and the wait result are read with
-// readfirstlane), and lane 0's work at the end of a task (the notify and the
-// next ticket claim) is one divergent region closed by a barrier, so all
-// lanes of a workgroup run the same iterations.
-template <class Stage, int UP, int UC, int MAXT>
+// staging, UC while consuming, at most MAXT lanes per workgroup (256, or
+// 512 for the wide launches, so the default keeps its register budget). T is
+// the element type (the reduce stage's, and the unit of the element-wise
+// path). Every branch that encloses a barrier depends only on wave-uniform
+// values (the ticket and the wait result are read with readfirstlane, the
+// segment's path follows from the ticket), and lane 0's work at the end of
+// a task (the notify and the next ticket claim) is one divergent region
+// closed by a barrier, so all lanes of a workgroup run the same iterations.
+template <class Stage, typename T, bool REDUCE, int UP, int UC, int MAXT>
 __global__ __launch_bounds__(MAXT) void k_snac(const SnacArgs a)
 {
+    using E = typename std::conditional<sizeof(T) == 2, uint16_t, uint32_t>::type;
     __shared__ unsigned int s_ticket;
     __shared__ int s_ok;
     const long long t_begin = wall_clock64();
-    const int64_t S = a.part_bytes;
     const int64_t C = a.chunk_bytes;
     if (threadIdx.x == 0)
         s_ticket = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -229,10 +413,13 @@ __global__ __launch_bounds__(MAXT) void k_snac(const SnacArgs a)
         const Task task = decode_task(a, t);
         const int64_t slot = task.chunk % a.slots;
         const int64_t use = task.chunk / a.slots;             // earlier chunks in this slot
-        const int k = static_cast<int>(task.chunk % a.P);     // partitions interleave
-        const int64_t c = task.chunk / a.P;                   // chunk index within partition k
+        int s;
+        int64_t c;
+        chunk_of(a, task.chunk, &s, &c);
+        const SegGeo g = seg_geo(a, s);
+        const bool elem = a.elem[s] != 0;
         const int64_t cbeg = c * C;
-        const int64_t clen = (S - cbeg < C) ? S - cbeg : C;
+        const int64_t clen = (g.bytes - cbeg < C) ? g.bytes - cbeg : C;
         const int64_t pbeg = task.piece * a.piece_bytes;
         int64_t plen = clen - pbeg;
         plen = plen < 0 ? 0 : (plen > a.piece_bytes ? a.piece_bytes : plen);
@@ -245,9 +432,18 @@ __global__ __launch_bounds__(MAXT) void k_snac(const SnacArgs a)
         const bool ok = wait_at_least(a, wflag, target, t_begin, &s_ok);
         if (ok) {
             if (task.produce) {
-                Stage::template produce<UP>(a, k, cbeg + pbeg, slotp + pbeg, plen);
+                if (elem)
+                    produce_elem<T, REDUCE>(a, g, cbeg + pbeg, slotp + pbeg, plen);
+                else
+                    Stage::template produce<UP>(a, g, cbeg + pbeg, slotp + pbeg, plen);
             } else {
-                fan_out<UC>(a, slotp + pbeg, static_cast<int64_t>(k) * S + cbeg + pbeg, plen);
+                jitter(a, t, 1u);
+                if (a.jitter_ticks > 0)
+                    __syncthreads();
+                if (elem)
+                    consume_elem<E>(a, g, slotp + pbeg, g.dst_off + cbeg + pbeg, plen);
+                else
+                    consume_vec<UC>(a, g, slotp + pbeg, g.dst_off + cbeg + pbeg, plen);
             }
         }
         // Notify: each wave of a producer waits until its write-through
@@ -257,8 +453,10 @@ __global__ __launch_bounds__(MAXT) void k_snac(const SnacArgs a)
         // Releasing the slot publishes no data: the slot loads have already
         // returned (their values were stored before the barrier), so `freed`
         // moves the same way.
-        if (task.produce)
+        if (task.produce) {
             wait_vmem();
+            jitter(a, t, 2u);
+        }
         __syncthreads();
         if (threadIdx.x == 0) {
             if (ok)
@@ -280,10 +478,10 @@ __global__ __launch_bounds__(MAXT) void k_snac(const SnacArgs a)
         const unsigned int prev =
             __hip_atomic_fetch_add(a.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (prev == gridDim.x - 1) {
-            for (int s = 0; s < a.slots; ++s) {
-                __hip_atomic_store(a.ready + s * kFlagStride, 0ull, __ATOMIC_RELAXED,
+            for (int sl = 0; sl < a.slots; ++sl) {
+                __hip_atomic_store(a.ready + sl * kFlagStride, 0ull, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(a.freed + s * kFlagStride, 0ull, __ATOMIC_RELAXED,
+                __hip_atomic_store(a.freed + sl * kFlagStride, 0ull, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
             }
             __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -295,16 +493,31 @@ __global__ __launch_bounds__(MAXT) void k_snac(const SnacArgs a)
 // The reducing stage keeps P * UP loads in flight per lane: UP = 2 up to
 // P = 8, 1 for more inputs.
 template <typename T, int MAXT>
-hipError_t launch_ar_t(const SnacArgs& a, dim3 grid, dim3 block, hipStream_t stream)
+hipError_t launch_reduce_t(const SnacArgs& a, dim3 grid, dim3 block, hipStream_t stream)
 {
     switch (a.P) {
-#define ATOM_SNAC_AR_CASE(PP) \
-    case PP: k_snac<StageReduce<T, PP>, (PP <= 8 ? 2 : 1), 8, MAXT><<<grid, block, 0, stream>>>(a); break;
-    ATOM_SNAC_AR_CASE(1) ATOM_SNAC_AR_CASE(2) ATOM_SNAC_AR_CASE(3) ATOM_SNAC_AR_CASE(4)
-    ATOM_SNAC_AR_CASE(5) ATOM_SNAC_AR_CASE(6) ATOM_SNAC_AR_CASE(7) ATOM_SNAC_AR_CASE(8)
-    ATOM_SNAC_AR_CASE(9) ATOM_SNAC_AR_CASE(10) ATOM_SNAC_AR_CASE(11) ATOM_SNAC_AR_CASE(12)
-    ATOM_SNAC_AR_CASE(13) ATOM_SNAC_AR_CASE(14) ATOM_SNAC_AR_CASE(15) ATOM_SNAC_AR_CASE(16)
-#undef ATOM_SNAC_AR_CASE
+#define ATOM_SNAC_RED_CASE(PP)                                                                  \
+    case PP:                                                                                    \
+        k_snac<StageReduce<T, PP>, T, true, (PP <= 8 ? 2 : 1), 8, MAXT><<<grid, block, 0, stream>>>(a); \
+        break;
+    ATOM_SNAC_RED_CASE(1) ATOM_SNAC_RED_CASE(2) ATOM_SNAC_RED_CASE(3) ATOM_SNAC_RED_CASE(4)
+    ATOM_SNAC_RED_CASE(5) ATOM_SNAC_RED_CASE(6) ATOM_SNAC_RED_CASE(7) ATOM_SNAC_RED_CASE(8)
+    ATOM_SNAC_RED_CASE(9) ATOM_SNAC_RED_CASE(10) ATOM_SNAC_RED_CASE(11) ATOM_SNAC_RED_CASE(12)
+    ATOM_SNAC_RED_CASE(13) ATOM_SNAC_RED_CASE(14) ATOM_SNAC_RED_CASE(15) ATOM_SNAC_RED_CASE(16)
+#undef ATOM_SNAC_RED_CASE
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <typename T, int MAXT>
+hipError_t launch_copy_t(const SnacArgs& a, int U, dim3 grid, dim3 block, hipStream_t stream)
+{
+    switch (U) {
+#define ATOM_SNAC_COPY_CASE(UU)                                                              \
+    case UU: k_snac<StageCopy, T, false, UU, UU, MAXT><<<grid, block, 0, stream>>>(a); break;
+    ATOM_SNAC_COPY_CASE(1) ATOM_SNAC_COPY_CASE(2) ATOM_SNAC_COPY_CASE(4) ATOM_SNAC_COPY_CASE(8)
+#undef ATOM_SNAC_COPY_CASE
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -312,12 +525,13 @@ hipError_t launch_ar_t(const SnacArgs& a, dim3 grid, dim3 block, hipStream_t str
 
 }  // namespace
 
-hipError_t launch_snac(const Plan& p, const Workspace& ws, hipStream_t stream)
+hipError_t launch_snac(const Plan& p, const Workspace& ws, uint32_t seq, hipStream_t stream)
 {
-    if ((p.exec != EX_SNAC_AG && p.exec != EX_SNAC_AR) || !ws.ring || ws.ring_bytes < p.ring_bytes ||
-        p.grid < 1 || p.sa.slots < 1 || p.sa.slots > kMaxSlots || p.sa.pieces < 1 || p.sa.P < 1 ||
-        p.sa.P > kMaxRanks || ws.wall_khz <= 0 || p.wg < 64 || p.wg > 512 || p.wg % 64 != 0 ||
-        !ws.done)
+    if ((p.exec != EX_SNAC_COPY && p.exec != EX_SNAC_REDUCE) || !ws.ring ||
+        ws.ring_bytes < p.ring_bytes || p.grid < 1 || p.sa.slots < 1 || p.sa.slots > kMaxSlots ||
+        p.sa.pieces < 1 || p.sa.P < 1 || p.sa.P > kMaxRanks || p.sa.nseg < 1 ||
+        p.sa.nseg > kMaxSegs || ws.wall_khz <= 0 || p.wg < 64 || p.wg > 512 || p.wg % 64 != 0 ||
+        !ws.done || seq == 0)
         return hipErrorInvalidValue;
     SnacArgs a = p.sa;
     a.ring = ws.ring;
@@ -326,32 +540,28 @@ hipError_t launch_snac(const Plan& p, const Workspace& ws, hipStream_t stream)
     a.ticket = ws.ticket;
     a.error = ws.error;
     a.done = ws.done;
+    a.seq = seq;
     // Bounds in device-clock ticks (kHz x ms): the planned wait bound (1 s
-    // unless the caller shortened it) and ~10 s per workgroup.
+    // unless the caller shortened it) and ~10 s per workgroup; the test
+    // hook's delay likewise.
     a.wait_ticks = std::max<int64_t>(1, static_cast<int64_t>(ws.wall_khz) * p.sa.wait_ticks / 1000);
     a.budget_ticks = static_cast<int64_t>(ws.wall_khz) * 10000;
+    a.jitter_ticks = static_cast<int64_t>(ws.wall_khz) * p.sa.jitter_ticks / 1000;
     const dim3 grid(static_cast<unsigned>(p.grid)), block(static_cast<unsigned>(p.wg));
     const bool wide = p.wg > 256;
-    if (p.exec == EX_SNAC_AG) {
-#define ATOM_SNAC_AG_CASE(UU)                                                              \
-    case UU:                                                                               \
-        if (wide)                                                                          \
-            k_snac<StageCopy, UU, UU, 512><<<grid, block, 0, stream>>>(a);                 \
-        else                                                                               \
-            k_snac<StageCopy, UU, UU, 256><<<grid, block, 0, stream>>>(a);                 \
-        break;
-        switch (p.U) {
-        ATOM_SNAC_AG_CASE(1) ATOM_SNAC_AG_CASE(2) ATOM_SNAC_AG_CASE(4) ATOM_SNAC_AG_CASE(8)
-        default: return hipErrorInvalidValue;
-        }
-#undef ATOM_SNAC_AG_CASE
-        return hipGetLastError();
+    const bool bf = p.dtype == DT_BF16;
+    if (p.exec == EX_SNAC_COPY) {
+        if (bf)
+            return wide ? launch_copy_t<uint16_t, 512>(a, p.U, grid, block, stream)
+                        : launch_copy_t<uint16_t, 256>(a, p.U, grid, block, stream);
+        return wide ? launch_copy_t<float, 512>(a, p.U, grid, block, stream)
+                    : launch_copy_t<float, 256>(a, p.U, grid, block, stream);
     }
-    if (p.dtype == DT_BF16)
-        return wide ? launch_ar_t<uint16_t, 512>(a, grid, block, stream)
-                    : launch_ar_t<uint16_t, 256>(a, grid, block, stream);
-    return wide ? launch_ar_t<float, 512>(a, grid, block, stream)
-                : launch_ar_t<float, 256>(a, grid, block, stream);
+    if (bf)
+        return wide ? launch_reduce_t<uint16_t, 512>(a, grid, block, stream)
+                    : launch_reduce_t<uint16_t, 256>(a, grid, block, stream);
+    return wide ? launch_reduce_t<float, 512>(a, grid, block, stream)
+                : launch_reduce_t<float, 256>(a, grid, block, stream);
 }
 
 }  // namespace atom

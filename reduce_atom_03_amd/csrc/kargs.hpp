@@ -97,32 +97,61 @@ struct CopyArgs {
                                        // amount); copied element by element
 };
 
-// SNAC: AllGather (stage = copy) and the composed AllReduce (stage = reduce).
+// SNAC: every collective staged through a ring. The work is a list of
+// segments, each a contiguous byte range staged chunk by chunk:
+//  SK_GATHER   segment k = source src[k] (cnt[k] rows), written to every
+//              dst[q] at byte offset sum_{k'<k} cnt[k'] * row_bytes
+//              (AllGather(V); stage = copy)
+//  SK_EXCHANGE segment s = r*P + j: cnt[s] rows of src[r] (after source r's
+//              rows for every j' < j) to dst[j] (after every source r' < r's
+//              rows for j)  (AllToAll(V); stage = copy)
+//  SK_SCATTER  segment k = rows [sum_{k'<k} cnt[k'], +cnt[k]) of every
+//              source, summed in rank order, written to dst[k] from byte 0
+//              (ReduceScatter(V); stage = reduce)
+//  SK_ALLRED   as SK_SCATTER, written to every dst[q] at the segment's own
+//              offset  (the composed AllReduce of Figure 6; stage = reduce)
+enum SnacKind : int32_t { SK_GATHER = 0, SK_EXCHANGE = 1, SK_SCATTER = 2, SK_ALLRED = 3 };
+
 struct SnacArgs {
-    const void* src[kMaxRanks];        // inputs (z_k, or x_r for AllReduce)
-    void* dst[kMaxRanks];              // outputs out_j
+    const void* src[kMaxRanks];        // inputs
+    void* dst[kMaxRanks];              // outputs
     char* ring;                        // D slots of chunk_bytes
     unsigned long long* ready;         // per slot (stride kFlagStride): pieces staged
     unsigned long long* freed;         // per slot (stride kFlagStride): pieces consumed
     unsigned int* ticket;              // task counter
-    unsigned int* error;               // nonzero after a wait timed out
+    unsigned int* error;               // sequence number of the last call whose
+                                       // wait timed out (0: none since cleared)
     unsigned int* done;                // workgroups finished (the last one
                                        // clears the counters for the next call)
-    int64_t part_bytes;                // bytes of each partition
+    int64_t row_bytes;                 // bytes per counted row
     int64_t chunk_bytes;
     int64_t piece_bytes;               // chunk_bytes / pieces
-    int64_t nchunks_per_part;
-    int64_t nchunks;                   // P * nchunks_per_part
-    int64_t ntasks;
+    int64_t nchunks;                   // chunks of every segment together
+    int64_t ntasks;                    // 2 * nchunks * pieces
     int64_t wait_ticks;                // bound of one wait: microseconds when
                                        // planned, device-clock ticks at launch
     int64_t budget_ticks;              // bound of a workgroup's whole run
+    int64_t jitter_ticks;              // test hook: largest pseudo-random delay
+                                       // before a notify or a consume (0: none);
+                                       // microseconds when planned, ticks at launch
+    uint32_t jitter_seed;
+    uint32_t seq;                      // this call's sequence number (never 0)
+    int32_t kind;                      // SnacKind
     int32_t P;
+    int32_t nseg;
     int32_t pieces;                    // G pieces per chunk
     int32_t slots;                     // D
-    int32_t dtype;                     // for the reducing consumer
+    int32_t dtype;                     // for the reducing stage
     int32_t nt_store;
-    int32_t pad_;
+    int32_t interleave;                // 1: every segment has the same number of
+                                       // chunks and chunk q belongs to segment
+                                       // q % nseg (sources staged side by side);
+                                       // 0: segment-major, found in chunk_begin
+    int32_t cnt[kMaxSegs];             // rows per segment
+    int32_t chunk_begin[kMaxSegs + 1]; // first chunk of each segment (segment-major)
+    uint8_t elem[kMaxSegs];            // 1: the segment has a stream off 16-byte
+                                       // alignment; it is staged and consumed
+                                       // element by element
 };
 
 // Expert-parallel MoE routing (three kernels: rank within chunks, per-rank
@@ -173,6 +202,11 @@ struct MoeMoveArgs {
     int32_t dtype;
     int32_t nt_store;
 };
+
+// Kernel arguments of a launch are limited to 4 KiB.
+static_assert(sizeof(ReduceArgs) <= 4096 && sizeof(CopyArgs) <= 4096 && sizeof(SnacArgs) <= 4096 &&
+                  sizeof(MoeRouteArgs) <= 4096 && sizeof(MoeMoveArgs) <= 4096,
+              "kernel argument block too large");
 
 // Bytes before a segment's first byte in its first tile when tiles are
 // aligned to `tile_bytes` at the destination address `dst_addr` (the same

@@ -15,14 +15,17 @@ struct Workspace {
     unsigned long long* ready = nullptr;   // kMaxSlots counters, kFlagStride apart
     unsigned long long* freed = nullptr;   // kMaxSlots counters, kFlagStride apart
     unsigned int* ticket = nullptr;
-    unsigned int* error = nullptr;
+    unsigned int* error = nullptr;         // last timed-out call's sequence number
     unsigned int* done = nullptr;
     int wall_khz = 0;                      // rate of the device's constant clock
+    uint32_t seq = 0;                      // sequence number of the last staged call
 };
 
 hipError_t launch_reduce(const Plan& p, hipStream_t stream);
 hipError_t launch_copy(const Plan& p, hipStream_t stream);
-hipError_t launch_snac(const Plan& p, const Workspace& ws, hipStream_t stream);
+// seq: the call's sequence number (nonzero), recorded in the error word if
+// one of its waits times out.
+hipError_t launch_snac(const Plan& p, const Workspace& ws, uint32_t seq, hipStream_t stream);
 hipError_t launch_moe_route(const MoeRoutePlan& p, hipStream_t stream);
 hipError_t launch_moe_move(const MoeMovePlan& p, bool combine, hipStream_t stream);
 

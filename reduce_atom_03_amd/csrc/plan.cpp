@@ -60,6 +60,8 @@ struct Cfg {
     int64_t piece;     // SNAC task granule; 0 = default
     int64_t wait_us;   // bound of one SNAC wait
     int32_t lanes;     // threads per workgroup; 0 = pick by shape
+    int64_t jitter_us; // SNAC test hook: largest delay before a notify or consume
+    uint32_t jitter_seed;
 };
 
 atom_status read_cfg(const atom_config* cfg, Cfg* c)
@@ -74,6 +76,8 @@ atom_status read_cfg(const atom_config* cfg, Cfg* c)
     c->piece = 0;
     c->wait_us = kDefaultWaitUs;
     c->lanes = 0;
+    c->jitter_us = 0;
+    c->jitter_seed = 0;
     if (!cfg)
         return ATOM_OK;
     if (cfg->chunk_bytes != 0) {
@@ -115,6 +119,10 @@ atom_status read_cfg(const atom_config* cfg, Cfg* c)
     if (cfg->lanes > 256 && !(cfg->flags & ATOM_F_STAGED))
         return ATOM_ERR_UNSUPPORTED;
     c->lanes = cfg->lanes;
+    if (cfg->jitter_us < 0 || cfg->jitter_us > kMaxJitterUs)
+        return ATOM_ERR_INVALID_ARG;
+    c->jitter_us = cfg->jitter_us;
+    c->jitter_seed = cfg->jitter_seed;
     return ATOM_OK;
 }
 
@@ -427,6 +435,144 @@ void build_copy(Plan* p, int32_t kind, int P, const void* const* srcs, int nsrc,
 // Limit that keeps per-segment tile indices in 32 bits.
 constexpr int64_t kMaxTiles = INT32_MAX;
 
+// SNAC launch over a segment list (kargs.hpp: SnacKind). cnt[s] rows of rb
+// bytes per segment.
+atom_status build_snac(Plan* p, int32_t sk, int P, void* const* ins, void* const* outs,
+                       const int64_t* cnt, int nseg, int64_t rb, const Cfg& c)
+{
+    SnacArgs& a = p->sa;
+    std::memset(&a, 0, sizeof a);
+    const bool reduce = sk == SK_SCATTER || sk == SK_ALLRED;
+    // Segment geometry, as the kernel derives it: bytes, source offset (of
+    // the segment's own source, or of every source for a reduce) and
+    // destination offset. A segment whose streams are all 16-byte aligned
+    // takes the vector path; otherwise it is staged element by element.
+    int64_t bytes[kMaxSegs], total = 0, largest = 0;
+    int64_t col_rows[kMaxRanks] = {}, run_rows = 0;
+    for (int r = 0; r < P; ++r) {
+        a.src[r] = ins[r];
+        a.dst[r] = outs[r];
+    }
+    for (int s = 0; s < nseg; ++s) {
+        bytes[s] = cnt[s] * rb;
+        total += bytes[s];
+        largest = std::max(largest, bytes[s]);
+        a.cnt[s] = static_cast<int32_t>(cnt[s]);
+        bool al = true;
+        auto at = [](const void* b, int64_t off) {
+            return (reinterpret_cast<uintptr_t>(b) + static_cast<uint64_t>(off)) % kVecBytes == 0;
+        };
+        if (sk == SK_EXCHANGE) {
+            const int r = s / P, j = s % P;
+            int64_t src_rows = 0;
+            for (int jj = 0; jj < j; ++jj)
+                src_rows += cnt[r * P + jj];
+            al = at(ins[r], src_rows * rb) && at(outs[j], col_rows[j] * rb);
+            col_rows[j] += cnt[s];
+        } else {
+            const int64_t off = run_rows * rb;
+            if (sk == SK_GATHER) {
+                al = at(ins[s], 0);
+            } else {
+                for (int r = 0; r < P; ++r)
+                    al = al && at(ins[r], off);
+            }
+            if (sk == SK_SCATTER) {
+                al = al && at(outs[s], 0);
+            } else {
+                for (int q = 0; q < P; ++q)
+                    al = al && at(outs[q], off);
+            }
+            run_rows += cnt[s];
+        }
+        a.elem[s] = al ? 0 : 1;
+    }
+    if (total == 0)
+        return ATOM_OK;
+    // Chunk: the caller's, else the one measured best on MI355X for the
+    // stage (a copying stage 512 KiB, a reducing one 2 MiB: both in the
+    // 512 KiB - 2 MiB range of Table 3's bandwidth-delay rule).
+    int64_t chunk = c.chunk_set ? c.chunk : (reduce ? kDefaultChunkAllReduce : kDefaultChunkAllGather);
+    // Piece (the task granule): the caller's, else the largest power of two
+    // from 8 KiB to 64 KiB that still gives about one persistent grid's
+    // worth of staging tasks (total / piece >= 2 * 512), so a medium message
+    // is spread over many workgroups instead of a few (smaller pieces cost
+    // more in hand-offs than they gain).
+    int64_t piece = c.piece;
+    if (!piece) {
+        piece = kMinAutoPiece;
+        while (piece < kPieceBytes && total / (2 * piece) >= kSnacGrid)
+            piece *= 2;
+    }
+    piece = std::min(piece, chunk);
+    // A largest segment smaller than the chunk: one chunk of just enough
+    // whole pieces, so no task handles an empty piece.
+    if (largest < chunk)
+        chunk = std::max<int64_t>(1, ceil_div(largest, piece)) * piece;
+    int64_t q = 0, per0 = -1;
+    bool same = true;
+    for (int s = 0; s < nseg; ++s) {
+        a.chunk_begin[s] = static_cast<int32_t>(q);
+        const int64_t nc = ceil_div(bytes[s], chunk);
+        same = same && (per0 < 0 || nc == per0);
+        per0 = nc;
+        q += nc;
+        if (q > INT32_MAX)
+            return ATOM_ERR_INVALID_ARG;
+    }
+    a.chunk_begin[nseg] = static_cast<int32_t>(q);
+    // Equal chunk counts (the uniform collectives): chunk q belongs to
+    // segment q % nseg, so the producers stream from every source at once.
+    a.interleave = same ? 1 : 0;
+    a.kind = sk;
+    a.P = P;
+    a.nseg = nseg;
+    a.row_bytes = rb;
+    a.chunk_bytes = chunk;
+    a.piece_bytes = piece;
+    a.pieces = static_cast<int32_t>(chunk / piece);
+    a.slots = c.slots;
+    if (!c.slots_set) {
+        // Table 3's rule applied to one device: the ring holds at least one
+        // bandwidth-delay product of HBM (8 TB/s) times the cross-XCD
+        // stage-notify-consume round trip (~4 us measured), about 32 MiB.
+        const int64_t want = ceil_div(kSnacInflightBytes, chunk);
+        a.slots = static_cast<int32_t>(std::max<int64_t>(kDefaultSlots, std::min<int64_t>(kMaxSlots, want)));
+    }
+    a.nchunks = q;
+    a.ntasks = 2 * a.nchunks * a.pieces;
+    a.dtype = p->dtype;
+    a.nt_store = (c.flags & ATOM_F_NO_NT) ? 0 : 1;
+    a.wait_ticks = c.wait_us;             // converted to clock ticks at launch
+    a.jitter_ticks = c.jitter_us;         // likewise
+    a.jitter_seed = c.jitter_seed;
+    bool any_elem = false;
+    for (int s = 0; s < nseg; ++s)
+        any_elem = any_elem || (a.elem[s] && bytes[s] > 0);
+    p->vec = any_elem ? 0 : 1;
+    // Lanes per workgroup: 512 (two persistent workgroups of 8 waves per
+    // CU). Measured on MI355X with streaming output stores: the composed
+    // AllReduce, whose reducing stage reads P inputs per staged byte, +5 %
+    // over 256 lanes; the AllGather of 8 x 64 MiB +2 %.
+    p->wg = c.lanes ? c.lanes : 512;
+    // 16-byte slots per lane in flight: 8 measured best for the staged
+    // AllGather (+10% over 4); a reducing stage's depths are fixed by its
+    // kernel (2 while reducing P <= 8 inputs, 8 while consuming).
+    p->U = c.stages ? c.stages : 8;
+    p->slots = a.slots;
+    p->chunk_bytes = chunk;
+    p->ring_bytes = chunk * a.slots;
+    // Workgroups: the caller's, else one per staged piece the ring can hold
+    // (slots * pieces per chunk), at most 512. A larger grid than the ring's
+    // window only adds waiting workgroups: measured 5-18 % slower when the
+    // window is smaller than the grid.
+    const int64_t window = static_cast<int64_t>(a.slots) * a.pieces;
+    p->grid = std::max<int64_t>(
+        1, std::min<int64_t>(a.ntasks, c.num_wgs ? c.num_wgs : std::min(kSnacGrid, window)));
+    p->exec = reduce ? EX_SNAC_REDUCE : EX_SNAC_COPY;
+    return ATOM_OK;
+}
+
 }  // namespace
 
 // --------------------------------------------------------------------------
@@ -652,8 +798,6 @@ atom_status plan_collective(const atom_layout* in, const atom_layout* out, atom_
         return ATOM_ERR_INVALID_ARG;
 
     const bool staged = (c.flags & ATOM_F_STAGED) != 0;
-    if (staged && kind != ATOM_COLL_ALL_GATHER && kind != ATOM_COLL_ALL_REDUCE)
-        return ATOM_ERR_UNSUPPORTED;
 
     p->reset();
     p->kind = kind;
@@ -686,6 +830,23 @@ atom_status plan_collective(const atom_layout* in, const atom_layout* out, atom_
         return ATOM_OK;
 
     // ---- the launch
+    int64_t ones[kMaxSegs];
+    for (int e = 0; e < kMaxSegs; ++e)
+        ones[e] = 1;
+    const int64_t rb = v ? row_bytes : n * es;           // bytes per counted row
+    if (staged) {
+        // Every collective runs through SNAC as a list of segments derived
+        // from its layouts (the abstract: one orchestration for all of them).
+        const bool a2a = kind == ATOM_COLL_ALL_TO_ALL || kind == ATOM_COLL_ALL_TO_ALL_V;
+        int32_t sk = SK_GATHER;
+        if (a2a)
+            sk = SK_EXCHANGE;
+        else if (kind == ATOM_COLL_REDUCE_SCATTER || kind == ATOM_COLL_REDUCE_SCATTER_V)
+            sk = SK_SCATTER;
+        else if (kind == ATOM_COLL_ALL_REDUCE)
+            sk = SK_ALLRED;
+        return build_snac(p, sk, P, in->bufs, out->bufs, v ? cnt : ones, a2a ? P * P : P, rb, c);
+    }
     int64_t off[kMaxRanks + 1];
     switch (kind) {
     case ATOM_COLL_REDUCE_SCATTER:
@@ -697,8 +858,6 @@ atom_status plan_collective(const atom_layout* in, const atom_layout* out, atom_
         break;
     }
     case ATOM_COLL_ALL_REDUCE: {
-        if (staged)
-            break;   // SNAC plan below
         off[0] = 0;
         off[1] = total;
         build_reduce(p, P, in->bufs, P, out->bufs, 1, off, RM_FANOUT, c);
@@ -706,23 +865,13 @@ atom_status plan_collective(const atom_layout* in, const atom_layout* out, atom_
     }
     case ATOM_COLL_ALL_GATHER:
     case ATOM_COLL_ALL_GATHER_V: {
-        int64_t ones[kMaxRanks];
-        for (int k = 0; k < P; ++k)
-            ones[k] = 1;
-        const int64_t rb = v ? row_bytes : n * es;
         if (ceil_div(total * es, 256 * kVecBytes) > kMaxTiles)
             return ATOM_ERR_INVALID_ARG;
-        if (staged)
-            break;   // SNAC plan below
         build_copy(p, CK_FANOUT, P, in->bufs, P, out->bufs, P, v ? cnt : ones, P, rb, es, c);
         break;
     }
     case ATOM_COLL_ALL_TO_ALL:
     case ATOM_COLL_ALL_TO_ALL_V: {
-        int64_t ones[kMaxSegs];
-        for (int s = 0; s < P * P; ++s)
-            ones[s] = 1;
-        const int64_t rb = v ? row_bytes : n * es;
         if (ceil_div(in_bytes_total, 256 * kVecBytes) + P * P > kMaxTiles)
             return ATOM_ERR_INVALID_ARG;
         build_copy(p, CK_EXCHANGE, P, in->bufs, P, out->bufs, P, v ? cnt : ones, P * P, rb, es, c);
@@ -730,87 +879,6 @@ atom_status plan_collective(const atom_layout* in, const atom_layout* out, atom_
     }
     default:
         return ATOM_ERR_UNSUPPORTED;
-    }
-
-    if (staged) {
-        // SNAC: chunks of c.chunk bytes of each partition are staged into a
-        // ring of c.slots slots (AllGather: a copy of z_k; AllReduce: the
-        // rank-order sum of partition k over every input, Figure 6) and
-        // fanned out from there to every output.
-        const int64_t S = n * es;
-        bool vec = (S % kVecBytes) == 0;
-        for (int r = 0; r < P; ++r)
-            vec = vec && aligned(in->bufs[r], kVecBytes) && aligned(out->bufs[r], kVecBytes);
-        if (!vec)
-            return ATOM_ERR_UNSUPPORTED;
-        // Chunk: the caller's, else the one measured best on MI355X for
-        // the collective (AllGather 512 KiB, AllReduce 2 MiB: both in the
-        // 512 KiB - 2 MiB range of Table 3's bandwidth-delay rule). A
-        // partition smaller than the chunk is staged as one chunk of just
-        // enough whole pieces, so no task handles an empty piece.
-        int64_t chunk = c.chunk_set ? c.chunk
-                                    : (kind == ATOM_COLL_ALL_GATHER ? kDefaultChunkAllGather
-                                                                    : kDefaultChunkAllReduce);
-        // Piece (the task granule): the caller's, else the largest power of
-        // two from 8 KiB to 64 KiB that still gives about one persistent
-        // grid's worth of staging tasks (P * S / piece >= 512), so a
-        // medium message is spread over many workgroups instead of a few
-        // (smaller pieces cost more in hand-offs than they gain).
-        int64_t piece = c.piece;
-        if (!piece) {
-            piece = kMinAutoPiece;
-            while (piece < kPieceBytes && static_cast<int64_t>(P) * S / (2 * piece) >= kSnacGrid)
-                piece *= 2;
-        }
-        piece = std::min(piece, chunk);
-        if (S < chunk)
-            chunk = std::max<int64_t>(1, ceil_div(S, piece)) * piece;
-        SnacArgs& a = p->sa;
-        std::memset(&a, 0, sizeof a);
-        for (int r = 0; r < P; ++r) {
-            a.src[r] = in->bufs[r];
-            a.dst[r] = out->bufs[r];
-        }
-        a.P = P;
-        a.part_bytes = S;
-        a.chunk_bytes = chunk;
-        a.piece_bytes = piece;
-        a.pieces = static_cast<int32_t>(chunk / piece);
-        a.slots = c.slots;
-        if (!c.slots_set) {
-            // Table 3's rule applied to one device: the ring holds at least
-            // one bandwidth-delay product of HBM (8 TB/s) times the cross-XCD
-            // stage-notify-consume round trip (~4 us measured), about 32 MiB.
-            const int64_t want = ceil_div(kSnacInflightBytes, chunk);
-            a.slots = static_cast<int32_t>(std::max<int64_t>(kDefaultSlots, std::min<int64_t>(kMaxSlots, want)));
-        }
-        a.nchunks_per_part = ceil_div(S, chunk);
-        a.nchunks = a.nchunks_per_part * P;
-        a.ntasks = 2 * a.nchunks * a.pieces;
-        a.dtype = p->dtype;
-        a.nt_store = (c.flags & ATOM_F_NO_NT) ? 0 : 1;
-        a.wait_ticks = c.wait_us;         // converted to clock ticks at launch
-        p->vec = 1;
-        // Lanes per workgroup: 512 (two persistent workgroups of 8 waves per
-        // CU). Measured on MI355X with streaming output stores: the composed
-        // AllReduce, whose reducing stage reads P inputs per staged byte,
-        // +5 % over 256 lanes; the AllGather of 8 x 64 MiB +2 %.
-        p->wg = c.lanes ? c.lanes : 512;
-        // 16-byte slots per lane in flight: 8 measured best for the staged
-        // AllGather (+10% over 4); the AllReduce's depths are fixed by its
-        // kernel (2 while reducing P <= 8 inputs, 8 while fanning out).
-        p->U = c.stages ? c.stages : 8;
-        p->slots = a.slots;
-        p->chunk_bytes = chunk;
-        p->ring_bytes = chunk * a.slots;
-        // Workgroups: the caller's, else one per staged piece the ring can
-        // hold (slots * pieces per chunk), at most 512. A larger grid than
-        // the ring's window only adds waiting workgroups: measured 5-18 %
-        // slower when the window is smaller than the grid.
-        const int64_t window = static_cast<int64_t>(a.slots) * a.pieces;
-        p->grid = std::max<int64_t>(
-            1, std::min<int64_t>(a.ntasks, c.num_wgs ? c.num_wgs : std::min(kSnacGrid, window)));
-        p->exec = kind == ATOM_COLL_ALL_GATHER ? EX_SNAC_AG : EX_SNAC_AR;
     }
     return ATOM_OK;
 }
@@ -992,7 +1060,7 @@ void plan_fill_info(const Plan& p, atom_plan_info* info)
     std::memset(info, 0, sizeof *info);
     info->kind = p.kind;
     info->nranks = p.P;
-    info->staged = (p.exec == EX_SNAC_AG || p.exec == EX_SNAC_AR) ? 1 : 0;
+    info->staged = (p.exec == EX_SNAC_COPY || p.exec == EX_SNAC_REDUCE) ? 1 : 0;
     info->vector_path = p.vec;
     info->elems_per_rank_in = p.in_elems;
     for (int r = 0; r < kMaxRanks; ++r)

@@ -12,8 +12,8 @@ enum Exec : int32_t {
     EX_NONE = 0,      // nothing to launch (zero-sized)
     EX_REDUCE = 1,    // reduce family kernel (ReduceArgs)
     EX_COPY = 2,      // copy family kernel (CopyArgs)
-    EX_SNAC_AG = 3,   // SNAC persistent AllGather (SnacArgs)
-    EX_SNAC_AR = 4    // SNAC composed AllReduce (ReduceArgs for RS + SnacArgs)
+    EX_SNAC_COPY = 3,   // SNAC with a copying stage (SnacArgs: AllGather(V), AllToAll(V))
+    EX_SNAC_REDUCE = 4  // SNAC with a reducing stage (SnacArgs: ReduceScatter(V), AllReduce)
 };
 
 // The scalar part of a plan. Planning resets only this part (and the
@@ -41,7 +41,7 @@ struct Plan : PlanHead {
     int64_t out_elems[kMaxRanks] = {};
     ReduceArgs ra;            // exec == EX_REDUCE
     CopyArgs ca;              // exec == EX_COPY
-    SnacArgs sa;              // exec == EX_SNAC_AG / EX_SNAC_AR
+    SnacArgs sa;              // exec == EX_SNAC_COPY / EX_SNAC_REDUCE
 
     void reset()
     {
@@ -65,6 +65,7 @@ constexpr int64_t kSnacGrid = 512;                   // persistent SNAC workgrou
 constexpr int64_t kMaxGrid = 1 << 20;
 constexpr int64_t kSmallSlots = 256 * 256;           // below: the latency path
 constexpr int64_t kDefaultWaitUs = 1000000;          // one SNAC wait: 1 s
+constexpr int64_t kMaxJitterUs = 10000;              // SNAC test hook: largest delay
 
 // MoE routing and movement plans.
 struct MoeRoutePlan {

@@ -138,7 +138,7 @@ int main(int argc, char** argv)
             check_reduce(p, iter);
         else if (p.exec == EX_COPY)
             check_copy(p, iter);
-        else if (p.exec == EX_SNAC_AG || p.exec == EX_SNAC_AR) {
+        else if (p.exec == EX_SNAC_COPY || p.exec == EX_SNAC_REDUCE) {
             check(p.sa.slots >= 1 && p.sa.slots <= kMaxSlots, "snac slots", iter);
             check(p.sa.pieces >= 1 && p.sa.piece_bytes * p.sa.pieces == p.sa.chunk_bytes,
                   "snac pieces", iter);

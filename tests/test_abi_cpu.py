@@ -189,15 +189,42 @@ def test_config_validation(field, value):
     assert Q(A.SHARD, A.GATHERED, A.OP_COPY, cfg=cfg)[0] == A.ERR_INVALID_ARG
 
 
-def test_staged_only_for_allgather_and_allreduce():
+def test_every_collective_can_be_staged():
+    """The abstract: SNAC is the orchestration of every collective. Each
+    layout pair plans a staged launch with the matching stage (copy or
+    reduce); partitions off 16-byte alignment are accepted and planned on
+    the element-wise path."""
     cfg = A.config(flags=A.F_STAGED)
-    assert Q(A.SHARD, A.GATHERED, A.OP_COPY, cfg=cfg)[0] == A.OK
-    st, info = Q(A.PARTITIONED, A.GATHERED, A.OP_SUM, cfg=cfg)
-    assert st == A.OK and info.staged == 1 and info.kind == A.COLL_ALL_REDUCE
-    assert Q(A.PARTITIONED, A.SHARD, A.OP_SUM, cfg=cfg)[0] == A.ERR_UNSUPPORTED
-    assert Q(A.PARTITIONED, A.TRANSPOSED, A.OP_COPY, cfg=cfg)[0] == A.ERR_UNSUPPORTED
-    # the staged path needs 16-byte partitions
-    assert Q(A.SHARD, A.GATHERED, A.OP_COPY, n=63, cfg=cfg)[0] == A.ERR_UNSUPPORTED
+    C = np.arange(16, dtype=np.int64).reshape(4, 4) % 5
+    cases = [
+        (A.SHARD, A.GATHERED, A.OP_COPY, {}, A.COLL_ALL_GATHER),
+        (A.PARTITIONED, A.GATHERED, A.OP_SUM, {}, A.COLL_ALL_REDUCE),
+        (A.PARTITIONED, A.SHARD, A.OP_SUM, {}, A.COLL_REDUCE_SCATTER),
+        (A.PARTITIONED, A.TRANSPOSED, A.OP_COPY, {}, A.COLL_ALL_TO_ALL),
+        (A.PARTITIONED, A.TRANSPOSED, A.OP_COPY, {"counts": C, "row": 8}, A.COLL_ALL_TO_ALL_V),
+        (A.PARTITIONED, A.SHARD, A.OP_SUM, {"counts": np.array([3, 0, 5, 1]), "row": 8},
+         A.COLL_REDUCE_SCATTER_V),
+        (A.SHARD, A.GATHERED, A.OP_COPY, {"counts": np.array([3, 0, 5, 1]), "row": 8},
+         A.COLL_ALL_GATHER_V),
+    ]
+    for lin, lout, op, kw, kind in cases:
+        st, info = Q(lin, lout, op, cfg=cfg, **kw)
+        assert st == A.OK and info.staged == 1 and info.kind == kind, (lin, lout, op, kw)
+        assert info.vector_path == 1
+    # 63-element partitions: off 16-byte alignment, staged element by element
+    st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, n=63, cfg=cfg)
+    assert st == A.OK and info.staged == 1 and info.vector_path == 0
+    st, info = Q(A.PARTITIONED, A.SHARD, A.OP_SUM, ins=[b + 2 for b in fake(4, 4096)], cfg=cfg)
+    assert st == A.OK and info.staged == 1 and info.vector_path == 0
+
+
+def test_jitter_hook_validation():
+    for v in (-1, 10001):
+        assert Q(A.SHARD, A.GATHERED, A.OP_COPY,
+                 cfg=A.config(flags=A.F_STAGED, jitter_us=v))[0] == A.ERR_INVALID_ARG
+    for v in (0, 1, 10000):
+        assert Q(A.SHARD, A.GATHERED, A.OP_COPY,
+                 cfg=A.config(flags=A.F_STAGED, jitter_us=v, jitter_seed=7))[0] == A.OK
 
 
 # ------------------------------------------------------------------ planning

@@ -293,9 +293,6 @@ def test_all_reduce_snac(A, P, n, dtype, lanes):
     """Composed AllReduce through SNAC (Figure 6): the reduced chunk of each
     partition is staged once and fanned out; same bits as the oracle. Both
     workgroup widths: the default (512 lanes) and 256."""
-    es = 2 if dtype == synth.BF16 else 4
-    if (n * es) % 16:
-        pytest.skip("the staged path needs 16-byte partitions")
     say(f"SNAC AR P={P} n={n} {dtype} lanes={lanes}")
     xs = [synth.mixed_bits(39, r, P * n, dtype, specials=False) for r in range(P)]
     want = oracle.all_reduce(xs)

@@ -42,17 +42,52 @@ def _kernels(text):
 
 def test_every_snac_kernel_is_present(asm):
     names = [n for n, _ in _kernels(asm)]
-    # 4 pipeline depths x 2 workgroup bounds (256, 512 lanes)
-    assert sum("StageCopy" in n for n in names) == 8
+    # 4 pipeline depths x 2 workgroup bounds (256, 512 lanes) x 2 element
+    # types (the unit of the element-wise path)
+    assert sum("StageCopy" in n for n in names) == 16
     # 2 dtypes x P = 1..16 x 2 workgroup bounds
     assert sum("StageReduce" in n for n in names) == 64
 
 
+def _loops(body):
+    """[start, end) character ranges of the loops in a kernel body: from a
+    label to a later branch back to it."""
+    labels = {m.group(1): m.start() for m in re.finditer(r"^(\.LBB\w+):", body, re.M)}
+    out = []
+    for m in re.finditer(r"^\s*s_(?:cbranch_\w+|branch)\s+(\.LBB\w+)", body, re.M):
+        start = labels.get(m.group(1))
+        if start is not None and start < m.start():
+            out.append((start, m.end()))
+    return out
+
+
 def test_no_divergent_loop_exit(asm):
+    """Lanes may leave a loop one at a time (the element-wise loops over a
+    segment's elements do), but never a loop that contains a barrier: the
+    innermost loop around every divergent exit (`s_andn2_b64 exec, exec`)
+    holds no s_barrier."""
     for name, body in _kernels(asm):
         assert "s_barrier" in body
-        assert not re.search(r"s_andn2_b64\s+exec,\s*exec", body), \
-            f"{name}: a loop with barriers exits on a divergent branch"
+        loops = _loops(body)
+        assert loops, f"{name}: no loop found"
+        for m in re.finditer(r"s_andn2_b64\s+exec,\s*exec", body):
+            around = [(a, b) for a, b in loops if a <= m.start() < b]
+            if not around:
+                continue
+            a, b = min(around, key=lambda r: r[1] - r[0])
+            assert "s_barrier" not in body[a:b], \
+                f"{name}: a loop with barriers exits on a divergent branch"
+
+
+def test_the_task_loop_is_uniform(asm):
+    """The loop that claims tasks (the outermost one, holding the barriers)
+    exits on a scalar condition, not on the exec mask."""
+    for name, body in _kernels(asm):
+        loops = [r for r in _loops(body) if "s_barrier" in body[r[0]:r[1]]]
+        assert loops, name
+        a, b = max(loops, key=lambda r: r[1] - r[0])
+        branch = body[a:b].rstrip().splitlines()[-1]
+        assert re.match(r"\s*s_(cbranch_scc[01]|branch)\b", branch), (name, branch)
 
 
 def test_no_scratch(asm):
@@ -68,10 +103,12 @@ def test_ring_hand_off_needs_no_l2_maintenance(asm):
     none (ATOM_F_NO_NT), both present, never sc0 or sc1."""
     for name, body in _kernels(asm):
         assert not re.search(r"buffer_wbl2|buffer_inv", body), name
-        loads = re.findall(r"^\s*(buffer_load_dwordx4[^\n]*)", body, re.M)
+        loads = re.findall(r"^\s*(buffer_load_\w+[^\n]*)", body, re.M)
         stores = re.findall(r"^\s*(buffer_store_dwordx4[^\n]*)", body, re.M)
+        narrow = re.findall(r"^\s*(buffer_store_(?:short|dword)\b[^\n]*)", body, re.M)
         assert loads, f"{name}: no ring loads"
-        for op in loads:
+        assert narrow, f"{name}: no element-wise ring stores"
+        for op in loads + narrow:
             assert re.search(r"\bsc1\b", op), f"{name}: ring access without sc1: {op}"
         ring = [op for op in stores if re.search(r"\bsc1\b", op)]
         outs = [op for op in stores if not re.search(r"\bsc1\b", op)]
@@ -86,7 +123,7 @@ def test_producer_waits_for_its_stores_before_notify(asm):
     """Each wave waits for vmcnt(0) after its last ring store and before the
     barrier that precedes the `ready` increment."""
     for name, body in _kernels(asm):
-        last_store = max(m.end() for m in re.finditer(r"buffer_store_dwordx4[^\n]*\bsc1\b", body))
+        last_store = max(m.end() for m in re.finditer(r"buffer_store_\w+[^\n]*\bsc1\b", body))
         rest = body[last_store:]
         wait = re.search(r"s_waitcnt vmcnt\(0\)", rest)
         barrier = re.search(r"s_barrier", rest)
