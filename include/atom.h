@@ -72,7 +72,9 @@ typedef enum atom_status {
     ATOM_ERR_UNSUPPORTED = 2,  /* a layout/op pair that names no collective    */
     ATOM_ERR_HIP = 3,          /* a HIP runtime call or a launch failed         */
     ATOM_ERR_TIMEOUT = 4,      /* a SNAC wait exceeded its bound on the device  */
-    ATOM_ERR_NOMEM = 5         /* the workspace could not be allocated          */
+    ATOM_ERR_NOMEM = 5,        /* the workspace could not be allocated          */
+    ATOM_ERR_LIMIT = 6         /* a staged call does not fit the fixed workspace
+                                  of atom_collective_noalloc                    */
 } atom_status;
 
 /* The input enums below carry range sentinels so that any 32-bit value a
@@ -239,6 +241,25 @@ atom_status atom_reduce(void* dst, const void* const* srcs, int32_t nsrcs,
 atom_status atom_collective(const atom_layout* in, const atom_layout* out,
                             atom_op op, const atom_config* cfg, void* stream);
 
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The same
+ * collective as atom_collective, but a staged call takes its ring and flags
+ * from a fixed array inside the library (ATOM_NOALLOC_RING_BYTES of ring per
+ * device, held from the library's load until the process ends) instead of
+ * the growing workspace, so no call allocates. Without cfg->ring_slots the
+ * ring depth is cut to what fits; a call whose chunk (as planned: a message
+ * smaller than the chunk is staged in a smaller one), or whose chunk times
+ * cfg->ring_slots, exceeds ATOM_NOALLOC_RING_BYTES returns ATOM_ERR_LIMIT
+ * before anything is launched. Zero-staging calls use no workspace and behave exactly as in
+ * atom_collective. Every staged call on one device shares that device's
+ * array: two such calls that overlap in time (different streams) race and
+ * give wrong results. The first call on a device also enqueues one small
+ * kernel that clears the array's flags. Same return codes as
+ * atom_collective, plus ATOM_ERR_LIMIT. */
+#define ATOM_NOALLOC_RING_BYTES (16 << 20)
+atom_status atom_collective_noalloc(const atom_layout* in, const atom_layout* out,
+                                    atom_op op, const atom_config* cfg, void* stream);
+
 /* Validation and planning only, no HIP call: fills *info with what
  * atom_collective would do. Same return codes as its validation step. */
 atom_status atom_plan_query(const atom_layout* in, const atom_layout* out,
@@ -246,7 +267,8 @@ atom_status atom_plan_query(const atom_layout* in, const atom_layout* out,
                             atom_plan_info* info);
 
 /* Synchronizes `stream`, then reads and clears this device's SNAC error
- * word: ATOM_ERR_TIMEOUT if a wait timed out since the
+ * words (of the workspace and of the fixed array of
+ * atom_collective_noalloc): ATOM_ERR_TIMEOUT if a wait timed out since the
  * last check, else ATOM_OK (ATOM_ERR_HIP if the synchronization fails). A
  * timeout leaves incomplete output in the call it happened in only; calls
  * after it wait normally. (A HIP graph replays one captured call with one

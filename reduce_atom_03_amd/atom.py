@@ -18,7 +18,9 @@ LIB_PATH = os.path.join(_HERE, "libatom.so")
 MAX_RANKS = 16
 
 # atom_status
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_TIMEOUT, ERR_NOMEM = range(6)
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_TIMEOUT, ERR_NOMEM, ERR_LIMIT = range(7)
+# ATOM_NOALLOC_RING_BYTES: ring of atom_collective_noalloc's fixed workspace
+NOALLOC_RING_BYTES = 16 << 20
 # atom_dtype
 DT_BF16, DT_F32 = 0, 1
 # atom_op
@@ -98,7 +100,8 @@ class AtomMoeRouting(ctypes.Structure):
     ]
 
 
-EXPORTS = ("atom_copy", "atom_reduce", "atom_collective", "atom_plan_query",
+EXPORTS = ("atom_copy", "atom_reduce", "atom_collective", "atom_collective_noalloc",
+           "atom_plan_query",
            "atom_sync_status", "atom_bdp_chunk_bytes", "atom_status_string",
            "atom_last_error", "atom_version", "atom_moe_scratch_bytes",
            "atom_moe_route", "atom_moe_dispatch", "atom_moe_combine")
@@ -134,6 +137,8 @@ def _load() -> ctypes.CDLL:
     lp = ctypes.POINTER(AtomLayout)
     lib.atom_collective.argtypes = [lp, lp, ctypes.c_int, ctypes.POINTER(AtomConfig), vp]
     lib.atom_collective.restype = ctypes.c_int
+    lib.atom_collective_noalloc.argtypes = [lp, lp, ctypes.c_int, ctypes.POINTER(AtomConfig), vp]
+    lib.atom_collective_noalloc.restype = ctypes.c_int
     lib.atom_plan_query.argtypes = [lp, lp, ctypes.c_int, ctypes.POINTER(AtomConfig),
                                     ctypes.POINTER(AtomPlanInfo)]
     lib.atom_plan_query.restype = ctypes.c_int
@@ -295,6 +300,17 @@ def atom_collective(inp: AtomLayout, out: AtomLayout, op: int, cfg: Optional[Ato
                              ctypes.byref(cfg) if cfg is not None else None,
                              _stream(stream))
     return _check(st, "atom_collective", check)
+
+
+def atom_collective_noalloc(inp: AtomLayout, out: AtomLayout, op: int,
+                            cfg: Optional[AtomConfig] = None, stream=None,
+                            check: bool = True) -> int:
+    """atom_collective whose staged calls use the library's fixed workspace
+    (no device allocation)."""
+    st = lib.atom_collective_noalloc(ctypes.byref(inp), ctypes.byref(out), op,
+                                     ctypes.byref(cfg) if cfg is not None else None,
+                                     _stream(stream))
+    return _check(st, "atom_collective_noalloc", check)
 
 
 def atom_plan_query(inp: AtomLayout, out: AtomLayout, op: int,

@@ -16,7 +16,6 @@
 namespace atom {
 namespace {
 
-constexpr int kMaxDevices = 64;
 std::mutex g_ws_mutex;
 Workspace g_ws[kMaxDevices];
 thread_local hipError_t t_last_hip = hipSuccess;   // detail of this thread's last ATOM_ERR_HIP
@@ -154,6 +153,42 @@ atom_status run(const Plan& p, void* stream)
     return hip_status(e);
 }
 
+// atom_collective_noalloc: staged plans bounded by the fixed ring, launched
+// on the fixed workspace; everything else as run().
+atom_status run_noalloc(const Plan& p, void* stream)
+{
+    if (p.exec != EX_SNAC_COPY && p.exec != EX_SNAC_REDUCE)
+        return run(p, stream);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    Workspace* ws = nullptr;
+    hipError_t e = hipSuccess;
+    atom_status st = static_workspace(s, &ws, &e);
+    if (st == ATOM_ERR_HIP)
+        return hip_status(e);
+    if (st != ATOM_OK)
+        return st;
+    return hip_status(launch_snac(p, *ws, ws->seq, s));
+}
+
+// Reads and clears one error word after the stream was synchronized.
+atom_status take_error(unsigned int* err, bool* set)
+{
+    *set = false;
+    if (!err)
+        return ATOM_OK;
+    unsigned int host = 0;
+    if (hipError_t e = hipMemcpy(&host, err, sizeof host, hipMemcpyDeviceToHost); e != hipSuccess)
+        return hip_status(e);
+    if (host == 0)
+        return ATOM_OK;
+    const unsigned int zero = 0;
+    if (hipError_t e = hipMemcpy(err, &zero, sizeof zero, hipMemcpyHostToDevice); e != hipSuccess)
+        return hip_status(e);
+    *set = true;
+    return ATOM_OK;
+}
+
 }  // namespace
 }  // namespace atom
 
@@ -182,6 +217,14 @@ atom_status atom_collective(const atom_layout* in, const atom_layout* out, atom_
     return st == ATOM_OK ? atom::run(p, stream) : st;
 }
 
+atom_status atom_collective_noalloc(const atom_layout* in, const atom_layout* out, atom_op op,
+                                    const atom_config* cfg, void* stream)
+{
+    atom::Plan p;
+    atom_status st = atom::plan_collective_ex(in, out, op, cfg, atom::kStaticRingBytes, &p);
+    return st == ATOM_OK ? atom::run_noalloc(p, stream) : st;
+}
+
 atom_status atom_plan_query(const atom_layout* in, const atom_layout* out, atom_op op,
                             const atom_config* cfg, atom_plan_info* info)
 {
@@ -208,17 +251,12 @@ atom_status atom_sync_status(void* stream)
         std::lock_guard<std::mutex> lock(atom::g_ws_mutex);
         err = atom::g_ws[dev].error;
     }
-    if (!err)
-        return ATOM_OK;   // no SNAC call has run on this device
-    unsigned int host = 0;
-    if (hipError_t e = hipMemcpy(&host, err, sizeof host, hipMemcpyDeviceToHost); e != hipSuccess)
-        return atom::hip_status(e);
-    if (host == 0)
-        return ATOM_OK;
-    const unsigned int zero = 0;
-    if (hipError_t e = hipMemcpy(err, &zero, sizeof zero, hipMemcpyHostToDevice); e != hipSuccess)
-        return atom::hip_status(e);
-    return ATOM_ERR_TIMEOUT;
+    bool a = false, b = false;
+    if (atom_status st = atom::take_error(err, &a); st != ATOM_OK)
+        return st;
+    if (atom_status st = atom::take_error(atom::static_error_word(dev), &b); st != ATOM_OK)
+        return st;
+    return (a || b) ? ATOM_ERR_TIMEOUT : ATOM_OK;
 }
 
 int64_t atom_moe_scratch_bytes(int32_t nranks, int32_t num_experts, int32_t topk, int64_t tokens)
@@ -281,6 +319,7 @@ const char* atom_status_string(atom_status s)
     case ATOM_ERR_HIP: return "HIP runtime error";
     case ATOM_ERR_TIMEOUT: return "SNAC wait timed out on the device";
     case ATOM_ERR_NOMEM: return "workspace allocation failed";
+    case ATOM_ERR_LIMIT: return "staged call exceeds the fixed workspace of atom_collective_noalloc";
     }
     return "unknown status";
 }

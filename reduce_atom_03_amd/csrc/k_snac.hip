@@ -40,6 +40,7 @@
 // the task is dropped, and the call's later waits give up at once, so the
 // grid always drains (a later call, with another number, waits normally).
 #include <algorithm>
+#include <mutex>
 
 #include "atom_dev.hpp"
 #include "launch.hpp"
@@ -523,7 +524,76 @@ hipError_t launch_copy_t(const SnacArgs& a, int U, dim3 grid, dim3 block, hipStr
     return hipGetLastError();
 }
 
+// ---- the fixed workspace of atom_collective_noalloc ---------------------
+// Flags (ready and freed counters, the ticket, the error word and the
+// finished-workgroup count, each on its own 256-byte line, as in the
+// allocated workspace) followed by a ring of kStaticRingBytes. Each device
+// holds its own copy from the library's load until the process ends.
+constexpr int64_t kFlagLine = kFlagStride * sizeof(unsigned long long);
+constexpr int64_t kStaticFlagBytes = 64 << 10;
+static_assert((2 * kMaxSlots + 3) * kFlagLine <= kStaticFlagBytes, "flags do not fit");
+static __device__ __align__(256) char scratch[kStaticFlagBytes + kStaticRingBytes];
+
+__global__ void k_clear_words(unsigned long long* p, int64_t n)
+{
+    for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        p[i] = 0;
+}
+
+std::mutex g_static_mutex;
+Workspace g_static_ws[kMaxDevices];   // .ring == NULL until set up on that device
+
 }  // namespace
+
+atom_status static_workspace(hipStream_t stream, Workspace** out, hipError_t* hip_err)
+{
+    int dev = 0;
+    if ((*hip_err = hipGetDevice(&dev)) != hipSuccess)
+        return ATOM_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices)
+        return ATOM_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_static_mutex);
+    Workspace& ws = g_static_ws[dev];
+    if (!ws.ring) {
+        // The array's name is a host-side stand-in: its device address on
+        // this device comes from the runtime, and only that address is used.
+        char* ptr = nullptr;
+        if ((*hip_err = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch))) != hipSuccess)
+            return ATOM_ERR_HIP;
+        if (!ptr)
+            return ATOM_ERR_UNSUPPORTED;
+        int khz = 0;
+        if ((*hip_err = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev)) != hipSuccess)
+            return ATOM_ERR_HIP;
+        if (khz <= 0)
+            return ATOM_ERR_UNSUPPORTED;
+        k_clear_words<<<16, 256, 0, stream>>>(reinterpret_cast<unsigned long long*>(ptr),
+                                              kStaticFlagBytes / 8);
+        if ((*hip_err = hipGetLastError()) != hipSuccess)
+            return ATOM_ERR_HIP;
+        ws.wall_khz = khz;
+        ws.ready = reinterpret_cast<unsigned long long*>(ptr);
+        ws.freed = ws.ready + kMaxSlots * kFlagStride;
+        ws.ticket = reinterpret_cast<unsigned int*>(ptr + 2 * kMaxSlots * kFlagLine);
+        ws.error = reinterpret_cast<unsigned int*>(ptr + (2 * kMaxSlots + 1) * kFlagLine);
+        ws.done = reinterpret_cast<unsigned int*>(ptr + (2 * kMaxSlots + 2) * kFlagLine);
+        ws.ring_bytes = kStaticRingBytes;
+        ws.ring = ptr + kStaticFlagBytes;
+    }
+    if (++ws.seq == 0)
+        ws.seq = 1;
+    *out = &ws;
+    return ATOM_OK;
+}
+
+unsigned int* static_error_word(int dev)
+{
+    if (dev < 0 || dev >= kMaxDevices)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(g_static_mutex);
+    return g_static_ws[dev].error;
+}
 
 hipError_t launch_snac(const Plan& p, const Workspace& ws, uint32_t seq, hipStream_t stream)
 {

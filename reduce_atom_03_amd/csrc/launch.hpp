@@ -21,6 +21,17 @@ struct Workspace {
     uint32_t seq = 0;                      // sequence number of the last staged call
 };
 
+constexpr int kMaxDevices = 64;
+
+// The fixed workspace of atom_collective_noalloc on the current device: the
+// library's static device array, its address looked up once per device. The
+// first call on a device enqueues a kernel on `stream` that clears the flags.
+// Returns ATOM_OK, ATOM_ERR_UNSUPPORTED (device index out of range) or
+// ATOM_ERR_HIP (*hip_err set).
+atom_status static_workspace(hipStream_t stream, Workspace** out, hipError_t* hip_err);
+// This device's fixed-workspace error word, or NULL before its first use.
+unsigned int* static_error_word(int dev);
+
 hipError_t launch_reduce(const Plan& p, hipStream_t stream);
 hipError_t launch_copy(const Plan& p, hipStream_t stream);
 // seq: the call's sequence number (nonzero), recorded in the error word if

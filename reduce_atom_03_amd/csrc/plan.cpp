@@ -436,9 +436,13 @@ void build_copy(Plan* p, int32_t kind, int P, const void* const* srcs, int nsrc,
 constexpr int64_t kMaxTiles = INT32_MAX;
 
 // SNAC launch over a segment list (kargs.hpp: SnacKind). cnt[s] rows of rb
-// bytes per segment.
+// bytes per segment. max_ring_bytes > 0 bounds the ring (the fixed
+// workspace of atom_collective_noalloc): without a caller's ring depth the
+// depth is cut to fit, a caller's depth or chunk that does not fit is
+// ATOM_ERR_LIMIT.
 atom_status build_snac(Plan* p, int32_t sk, int P, void* const* ins, void* const* outs,
-                       const int64_t* cnt, int nseg, int64_t rb, const Cfg& c)
+                       const int64_t* cnt, int nseg, int64_t rb, const Cfg& c,
+                       int64_t max_ring_bytes)
 {
     SnacArgs& a = p->sa;
     std::memset(&a, 0, sizeof a);
@@ -509,6 +513,8 @@ atom_status build_snac(Plan* p, int32_t sk, int P, void* const* ins, void* const
     // whole pieces, so no task handles an empty piece.
     if (largest < chunk)
         chunk = std::max<int64_t>(1, ceil_div(largest, piece)) * piece;
+    if (max_ring_bytes > 0 && chunk > max_ring_bytes)
+        return ATOM_ERR_LIMIT;
     int64_t q = 0, per0 = -1;
     bool same = true;
     for (int s = 0; s < nseg; ++s) {
@@ -538,6 +544,10 @@ atom_status build_snac(Plan* p, int32_t sk, int P, void* const* ins, void* const
         // stage-notify-consume round trip (~4 us measured), about 32 MiB.
         const int64_t want = ceil_div(kSnacInflightBytes, chunk);
         a.slots = static_cast<int32_t>(std::max<int64_t>(kDefaultSlots, std::min<int64_t>(kMaxSlots, want)));
+        if (max_ring_bytes > 0)
+            a.slots = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(a.slots, max_ring_bytes / chunk)));
+    } else if (max_ring_bytes > 0 && chunk * a.slots > max_ring_bytes) {
+        return ATOM_ERR_LIMIT;
     }
     a.nchunks = q;
     a.ntasks = 2 * a.nchunks * a.pieces;
@@ -660,8 +670,8 @@ atom_status plan_reduce(void* dst, const void* const* srcs, int32_t nsrcs, int64
     return ATOM_OK;
 }
 
-atom_status plan_collective(const atom_layout* in, const atom_layout* out, atom_op op,
-                            const atom_config* cfg, Plan* p)
+atom_status plan_collective_ex(const atom_layout* in, const atom_layout* out, atom_op op,
+                               const atom_config* cfg, int64_t max_ring_bytes, Plan* p)
 {
     Cfg c;
     atom_status st = read_cfg(cfg, &c);
@@ -845,7 +855,8 @@ atom_status plan_collective(const atom_layout* in, const atom_layout* out, atom_
             sk = SK_SCATTER;
         else if (kind == ATOM_COLL_ALL_REDUCE)
             sk = SK_ALLRED;
-        return build_snac(p, sk, P, in->bufs, out->bufs, v ? cnt : ones, a2a ? P * P : P, rb, c);
+        return build_snac(p, sk, P, in->bufs, out->bufs, v ? cnt : ones, a2a ? P * P : P, rb, c,
+                          max_ring_bytes);
     }
     int64_t off[kMaxRanks + 1];
     switch (kind) {
@@ -881,6 +892,12 @@ atom_status plan_collective(const atom_layout* in, const atom_layout* out, atom_
         return ATOM_ERR_UNSUPPORTED;
     }
     return ATOM_OK;
+}
+
+atom_status plan_collective(const atom_layout* in, const atom_layout* out, atom_op op,
+                            const atom_config* cfg, Plan* p)
+{
+    return plan_collective_ex(in, out, op, cfg, 0, p);
 }
 
 // ---- MoE (Table 2, expert parallelism) ----------------------------------

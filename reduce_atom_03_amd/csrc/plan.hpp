@@ -66,6 +66,8 @@ constexpr int64_t kMaxGrid = 1 << 20;
 constexpr int64_t kSmallSlots = 256 * 256;           // below: the latency path
 constexpr int64_t kDefaultWaitUs = 1000000;          // one SNAC wait: 1 s
 constexpr int64_t kMaxJitterUs = 10000;              // SNAC test hook: largest delay
+// Ring of the fixed workspace that atom_collective_noalloc uses.
+constexpr int64_t kStaticRingBytes = ATOM_NOALLOC_RING_BYTES;
 
 // MoE routing and movement plans.
 struct MoeRoutePlan {
@@ -96,6 +98,10 @@ atom_status plan_reduce(void* dst, const void* const* srcs, int32_t nsrcs, int64
                         atom_dtype dtype, atom_op op, const atom_config* cfg, Plan* p);
 atom_status plan_collective(const atom_layout* in, const atom_layout* out, atom_op op,
                             const atom_config* cfg, Plan* p);
+// max_ring_bytes > 0: a staged plan must fit a ring of that many bytes (the
+// ring depth is cut to fit unless the caller set it; else ATOM_ERR_LIMIT).
+atom_status plan_collective_ex(const atom_layout* in, const atom_layout* out, atom_op op,
+                               const atom_config* cfg, int64_t max_ring_bytes, Plan* p);
 void plan_fill_info(const Plan& p, atom_plan_info* info);
 int64_t bdp_chunk_bytes(double bytes_per_s, double round_trip_s);
 
