@@ -5,6 +5,8 @@ A step is one pass over every collective of the hot path, each on its own
 resident synthetic input (bf16):
 
   copy    Atom copy of one 256 MiB input (also the counters' calibration kernel)
+  rs_c1   ReduceScatter of Figure 4's layout at P = 4, 4 x 65536 fp32 per input
+          (U[-1,1], seed 1): cache-resident, timed for its microseconds
   rs8     8-way ReduceScatter, 8 x 256 MiB (N(0,1), seed 2)
   ar      fused one-shot AllReduce of the same 8 x 256 MiB
   a2av    AllToAllV MoE dispatch, 8 x 4096 x 7168 (Dirichlet-multinomial counts, seed 3)
@@ -24,10 +26,17 @@ resident synthetic input (bf16):
 `value` is the step's credited bytes (every input element read once, every
 output element written once, a reduced element counted with its P reads)
 over the step time, in GB/s. Per-collective GB/s and fraction of the 8 TB/s
-HBM peak, the 8 KiB AllGather p50/p99 latency (an event pair around each
-launch), its time per call back to back and in a HIP graph, and the dominant kernel's
-roofline are reported alongside; the CPU oracle is timed on the same step
-as a baseline.
+HBM peak (from the median of the row's event-timed samples; samples above
+1.5x the median are counted as outliers), the 8 KiB AllGather p50/p99
+latency (an event pair around each launch), its time per call back to back
+and in a HIP graph, and the dominant kernel's roofline are reported
+alongside; the CPU oracle is timed on the same step as a baseline, and on
+the P = 4 ReduceScatter alone.
+
+`--ceilings` measures instead the cold rate of each traffic pattern on this
+chip (streaming read, write, copy, 1 -> 8 fan-out and its variants) with
+the measurement kernels of libatom_ceiling.so, a 1 GiB streaming fill
+before each run.
 """
 
 from __future__ import annotations
@@ -70,6 +79,10 @@ def parse():
                          "1 MiB, 2 MiB chunks) over 8 KiB..1 GiB partitions, ReduceScatter, "
                          "AllReduce and AllToAll over 8 KiB..256 MiB inputs, MoE over 1..4096 "
                          "tokens per rank; one JSON line per point")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="instead of the step: cold HBM rates of streaming read, write, copy and "
+                         "1 -> 8 fan-out (plain, rotated store order, pure writes, one allocation "
+                         "at several spacings); one JSON line per point")
     ap.add_argument("--xcd-order", action="store_true",
                     help="zero-staging kernels give each XCD one contiguous range of tiles")
     ap.add_argument("--no-snac", dest="snac", action="store_false",
@@ -98,6 +111,9 @@ def main():
     if args.sweep:
         sweep(A, synth, torch, dev)
         return
+    if args.ceilings:
+        ceilings(torch, dev)
+        return
 
     def up(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -108,6 +124,10 @@ def main():
     P = 8
     t0 = time.time()
     log("generating inputs ...")
+    # ReduceScatter of Figure 4's layout, P = 4, 4 x 65536 fp32 per input
+    c1 = synth.c1_inputs()
+    x1 = [torch.from_numpy(x).to(dev) for x in c1]
+    y1 = [torch.empty(65536, dtype=torch.float32, device=dev) for _ in range(4)]
     # 8-way reduce / AllReduce: 8 x 256 MiB
     c2 = synth.c2_inputs()
     x2 = [up(x) for x in c2]
@@ -167,6 +187,9 @@ def main():
     copy_out = empty(N2)
     rows.append(("copy", lambda: A.atom_copy(copy_out, x2[0]), 2 * N2 * 2))
     cus["copy"] = 256
+    lay1 = (L(A.PARTITIONED, x1, 65536), L(A.SHARD, y1, 65536))
+    rs_c1 = lambda l=lay1: A.atom_collective(l[0], l[1], A.OP_SUM)
+    rows.append(("rs_c1", rs_c1, plan_bytes(lay1[0], lay1[1], A.OP_SUM, name="rs_c1")))
     lay = (L(A.PARTITIONED, x2, n2), L(A.SHARD, ys, n2))
     rows.append(("rs8", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_SUM, zs_cfg),
                  plan_bytes(lay[0], lay[1], A.OP_SUM, zs_cfg, name="rs8")))
@@ -238,11 +261,11 @@ def main():
     per_row = {}
     for i, (name, _, nbytes) in enumerate(rows):
         ms = np.array([ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(K)])
-        avg = float(ms.mean())
-        per_row[name] = {"ms": round(avg, 5), "ms_p50": round(float(np.median(ms)), 5),
-                         "credited_bytes": int(nbytes),
-                         "GBps": round(nbytes / (avg * 1e-3) / 1e9, 1),
-                         "frac_hbm": round(nbytes / (avg * 1e-3) / HBM_PEAK, 4)}
+        p50 = float(np.median(ms))
+        per_row[name] = {"ms": round(p50, 5), "ms_mean": round(float(ms.mean()), 5),
+                         "outliers": int((ms > 1.5 * p50).sum()), "credited_bytes": int(nbytes),
+                         "GBps": round(nbytes / (p50 * 1e-3) / 1e9, 1),
+                         "frac_hbm": round(nbytes / (p50 * 1e-3) / HBM_PEAK, 4)}
     ms_step = wall * 1e3 / K
     value = step_bytes / (ms_step * 1e-3) / 1e9
 
@@ -270,6 +293,15 @@ def main():
         v = np.array([a.elapsed_time(e) * 1e3 for a, e in pairs])
         dec_lat[f"b{b}"] = {"p50_us": round(float(np.percentile(v, 50)), 2),
                             "p99_us": round(float(np.percentile(v, 99)), 2)}
+    # The P = 4 ReduceScatter alone: event pairs around lone launches.
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.lat_iters)]
+    for a, b in pairs:
+        a.record(stream)
+        rs_c1()
+        b.record(stream)
+    torch.cuda.synchronize()
+    c1_us = np.array([a.elapsed_time(b) * 1e3 for a, b in pairs])
     # Launch floor: the same event pair around a 16-byte atom_copy.
     tiny_src, tiny_dst = empty(8), empty(8)
     pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -360,8 +392,10 @@ def main():
                 "traffic": measured_traffic(dom)}
 
     cpu = None
+    c1_oracle = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args, C3, S, step_bytes)
+        c1_oracle = c1_oracle_ms(c1)
 
     out = {
         "metric": "achieved HBM GB/s (% of peak) for 8-way reduce & AllToAll; p50 us at 8 KiB",
@@ -400,6 +434,11 @@ def main():
         "back_to_back_host_paced_batches": len(paced),
         "back_to_back_batches": 9 * len(b2b),
         "decode_allreduce_latency": dec_lat,
+        "c1_gpu_us": {"p50": round(float(np.percentile(c1_us, 50)), 2),
+                      "p99": round(float(np.percentile(c1_us, 99)), 2),
+                      "samples": int(c1_us.size),
+                      "workload": "ReduceScatter P=4, 4 x 65536 fp32 per input, event pair per launch"},
+        "c1_oracle_ms": c1_oracle,
         "latency_samples": args.lat_iters,
         "p50_us_launch_floor_16B_copy": round(float(np.percentile(floor, 50)), 2),
         "cus_used": cus,
@@ -621,6 +660,96 @@ def sweep(A, synth, torch, dev):
              mb["combine"], "tokens_per_rank")
 
 
+def ceilings(torch, dev):
+    """Cold HBM rates of the traffic patterns the Atom kernels move, measured
+    with libatom_ceiling.so's kernels (one tile per workgroup, non-temporal
+    loads and stores): streaming read and write of 2 GiB, a 2 GiB copy, the
+    1 -> 8 fan-out of 256 MiB into 8 separate allocations (stores in order,
+    and rotated by tile), the same 8 x 256 MiB as pure writes, the fan-out
+    in blocked order (one output at a time per block of 1-64 MiB, the source
+    block loaded once per output) and the fan-out into one allocation at
+    spacings of exactly 256 MiB and 256 MiB plus 4352 bytes. A 1 GiB streaming fill of another buffer precedes each
+    run, so no run starts with the previous one's data or dirty lines in the
+    caches; the median of 7 runs, event-timed, is reported."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "reduce_atom_03_amd", "libatom_ceiling.so"))
+    vp = ctypes.c_void_p
+    lib.ceil_fill.argtypes = [vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int, vp]
+    lib.ceil_read.argtypes = [vp, ctypes.c_int64, vp, ctypes.c_int, ctypes.c_int, vp]
+    lib.ceil_fanout.argtypes = [ctypes.POINTER(vp), ctypes.c_int, vp, ctypes.c_int64, ctypes.c_int,
+                                ctypes.c_int, ctypes.c_int, vp]
+    lib.ceil_fanout_blocked.argtypes = [ctypes.POINTER(vp), ctypes.c_int, vp, ctypes.c_int64,
+                                        ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+    stream = torch.cuda.current_stream()
+    sp = int(stream.cuda_stream)
+    GiB, MiB256 = 1 << 30, 256 << 20
+
+    def buf(nbytes):
+        return torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+    flush_buf = buf(GiB)
+    big_a, big_b = buf(2 * GiB), buf(2 * GiB)
+    big_b.fill_(1)
+    sink = buf(256)
+    outs = [buf(MiB256) for _ in range(8)]
+    one = buf(8 * MiB256 + 8 * 4352)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def chk(rc):
+        if rc != 0:
+            raise RuntimeError(f"ceiling kernel refused its arguments or failed ({rc})")
+
+    def timeit(fn, nbytes, **point):
+        t = []
+        for _ in range(7):
+            chk(lib.ceil_fill(flush_buf.data_ptr(), GiB, 256, 4, sp))
+            e0.record(stream)
+            chk(fn())
+            e1.record(stream)
+            e1.synchronize()
+            t.append(e0.elapsed_time(e1))
+        ms = float(np.median(t))
+        print(json.dumps({"ceiling": point.pop("pattern"), **point, "bytes": int(nbytes),
+                          "ms": round(ms, 4), "GBps": round(nbytes / ms / 1e6, 1),
+                          "frac_hbm": round(nbytes / ms / 1e6 * 1e9 / HBM_PEAK, 4)}), flush=True)
+
+    def ptrs(ts):
+        return (vp * len(ts))(*[int(t) if isinstance(t, int) else t.data_ptr() for t in ts])
+
+    for lanes in (64, 256):
+        for U in (1, 2, 4):
+            timeit(lambda: lib.ceil_read(big_b.data_ptr(), 2 * GiB, sink.data_ptr(), lanes, U, sp),
+                   2 * GiB, pattern="read", lanes=lanes, U=U)
+            timeit(lambda: lib.ceil_fill(big_a.data_ptr(), 2 * GiB, lanes, U, sp),
+                   2 * GiB, pattern="write", lanes=lanes, U=U)
+            dst = ptrs([big_a])
+            timeit(lambda: lib.ceil_fanout(dst, 1, big_b.data_ptr(), 2 * GiB, 0, lanes, U, sp),
+                   4 * GiB, pattern="copy", lanes=lanes, U=U)
+    src = big_b.data_ptr()
+    sep = ptrs(outs)
+    for lanes, U in ((64, 1), (64, 2), (256, 1)):
+        for rot in (0, 1):
+            timeit(lambda: lib.ceil_fanout(sep, 8, src, MiB256, rot, lanes, U, sp), 9 * MiB256,
+                   pattern="fanout8", lanes=lanes, U=U, rotate=rot, dst="8 allocations")
+            timeit(lambda: lib.ceil_fanout(sep, 8, None, MiB256, rot, lanes, U, sp), 8 * MiB256,
+                   pattern="write8", lanes=lanes, U=U, rotate=rot, dst="8 allocations")
+    # Blocked order: the chip writes one output at a time, block by block, and
+    # loads each source tile once per output (streaming loads, or ordinary
+    # ones that leave the block in the caches for the next output's loads).
+    for lanes, U in ((64, 1), (256, 1), (256, 2)):
+        for block in (1 << 20, 4 << 20, 16 << 20, 64 << 20):
+            for cached in (0, 1):
+                timeit(lambda: lib.ceil_fanout_blocked(sep, 8, src, MiB256, block, cached, lanes, U, sp),
+                       9 * MiB256, pattern="fanout8_blocked", lanes=lanes, U=U, block=block,
+                       cached_loads=cached, dst="8 allocations")
+    base = one.data_ptr()
+    base += (-base) % 4096
+    for spacing in (MiB256, MiB256 + 4352):
+        d = ptrs([base + q * spacing for q in range(8)])
+        timeit(lambda: lib.ceil_fanout(d, 8, src, MiB256 - 4096, 0, 64, 1, sp), 9 * (MiB256 - 4096),
+               pattern="fanout8", lanes=64, U=1, rotate=0, dst=f"one allocation, spacing {spacing}")
+
+
 def measured_traffic(row):
     """HBM bytes per launch of `row` from the committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE, scaled by the copy calibration), or
@@ -660,6 +789,27 @@ def moe_bytes(P, T, E, k, row_bytes):
             "combine": P * T * (k + 1) * row_bytes + n * 12}
 
 
+def c1_oracle_ms(c1):
+    """The oracle's P = 4 ReduceScatter (4 x 65536 fp32 per input) on this
+    host: median of 100 calls, with the threads it used and on one thread."""
+    import oracle
+    def med(reps=100):
+        t = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            oracle.reduce_scatter(c1)
+            t.append(time.perf_counter() - t0)
+        return float(np.median(t)) * 1e3
+    cores = oracle.threads()
+    many = med()
+    oracle.set_threads(1)
+    try:
+        one = med()
+    finally:
+        oracle.set_threads(cores)
+    return {"ms": round(many, 4), "cores": cores, "ms_one_core": round(one, 4)}
+
+
 def cpu_baseline(args, C3, S, credited):
     """The oracle, as it stands, on the same step (same seeds and shapes, its
     own OpenMP threads); GB/s on the same credited bytes."""
@@ -667,6 +817,7 @@ def cpu_baseline(args, C3, S, credited):
     from reduce_atom_03_amd import synth
     log("timing the CPU oracle ...")
     P = 8
+    c1 = synth.c1_inputs()
     c2 = synth.c2_inputs()
     c3 = synth.c3_inputs()
     z4 = synth.c4_inputs(S, P)
@@ -680,6 +831,7 @@ def cpu_baseline(args, C3, S, credited):
     def step():
         t = time.perf_counter()
         oracle.all_gather([c2[0]])          # P = 1 AllGather: a copy
+        oracle.reduce_scatter(c1)
         oracle.reduce_scatter(c2)
         oracle.all_reduce(c2)
         oracle.all_to_all_v(c3, C3, synth.HIDDEN)

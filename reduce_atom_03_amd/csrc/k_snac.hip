@@ -31,11 +31,14 @@
 // needs an L2 write-back or invalidation.
 //
 // Tasks are claimed from one atomic ticket in an order where every task
-// depends only on tasks with smaller tickets: producers of chunks 0..D-1,
-// then for each later chunk q the consumers of chunk q-D followed by the
-// producers of chunk q, then the consumers of the last D chunks. A claimed
-// ticket belongs to a running workgroup, so the lowest unfinished task can
-// always proceed: no deadlock for any grid size or occupancy. Every wait is
+// depends only on tasks with smaller tickets: producers of chunks 0..E-1,
+// then for each later chunk q the consumers of chunk q-E followed by the
+// producers of chunk q, then the consumers of the last E chunks, where the
+// lead E is at most the ring depth D. The producer of chunk q reuses the
+// slot of chunk q-D, whose consumers were claimed D-E chunk steps earlier
+// (E = D would make it wait for the consumers claimed just before it). A
+// claimed ticket belongs to a running workgroup, so the lowest unfinished
+// task can always proceed: no deadlock for any grid size or occupancy. Every wait is
 // bounded; on expiry the error word is set to the call's sequence number,
 // the task is dropped, and the call's later waits give up at once, so the
 // grid always drains (a later call, with another number, waits normally).
@@ -57,9 +60,9 @@ struct Task {
 
 __device__ __forceinline__ Task decode_task(const SnacArgs& a, int64_t t)
 {
-    const int64_t G = a.pieces, D = a.slots, Q = a.nchunks;
-    const int64_t warm = (Q < D ? Q : D) * G;              // producers of chunks 0..D-1
-    const int64_t mid = (Q > D ? Q - D : 0) * 2 * G;       // [consume q-D, produce q]
+    const int64_t G = a.pieces, E = a.lead, Q = a.nchunks;
+    const int64_t warm = (Q < E ? Q : E) * G;              // producers of chunks 0..E-1
+    const int64_t mid = (Q > E ? Q - E : 0) * 2 * G;       // [consume q-E, produce q]
     Task k;
     if (t < warm) {
         k.produce = true;
@@ -67,15 +70,15 @@ __device__ __forceinline__ Task decode_task(const SnacArgs& a, int64_t t)
         k.piece = t - k.chunk * G;
     } else if (t < warm + mid) {
         const int64_t u = t - warm;
-        const int64_t q = D + u / (2 * G);
-        const int64_t w = u - (q - D) * 2 * G;
+        const int64_t q = E + u / (2 * G);
+        const int64_t w = u - (q - E) * 2 * G;
         k.produce = w >= G;
-        k.chunk = k.produce ? q : q - D;
+        k.chunk = k.produce ? q : q - E;
         k.piece = k.produce ? w - G : w;
     } else {
         const int64_t u = t - warm - mid;
         k.produce = false;
-        k.chunk = (Q > D ? Q - D : 0) + u / G;
+        k.chunk = (Q > E ? Q - E : 0) + u / G;
         k.piece = u - (u / G) * G;
     }
     return k;
@@ -599,7 +602,8 @@ hipError_t launch_snac(const Plan& p, const Workspace& ws, uint32_t seq, hipStre
 {
     if ((p.exec != EX_SNAC_COPY && p.exec != EX_SNAC_REDUCE) || !ws.ring ||
         ws.ring_bytes < p.ring_bytes || p.grid < 1 || p.sa.slots < 1 || p.sa.slots > kMaxSlots ||
-        p.sa.pieces < 1 || p.sa.P < 1 || p.sa.P > kMaxRanks || p.sa.nseg < 1 ||
+        p.sa.pieces < 1 || p.sa.lead < 1 || p.sa.lead > p.sa.slots || p.sa.P < 1 ||
+        p.sa.P > kMaxRanks || p.sa.nseg < 1 ||
         p.sa.nseg > kMaxSegs || ws.wall_khz <= 0 || p.wg < 64 || p.wg > 512 || p.wg % 64 != 0 ||
         !ws.done || seq == 0)
         return hipErrorInvalidValue;

@@ -89,6 +89,14 @@ struct CopyArgs {
                                        // segments of cnt[0] rows, no heads, the same
                                        // tile count each; segment = blockIdx.y, tile
                                        // within it = blockIdx.x
+    int32_t block_shift;               // CK_FANOUT blocked order (k_copy_fan_blocked):
+                                       // log2 of the tiles per block (a power of
+                                       // two, at least the 8 XCDs); -1: every tile
+                                       // stores to all outputs
+    int64_t nwork;                     // blocked order: workgroup tasks,
+                                       // blocks * 2^block_shift * ndst
+    int64_t seg_off[kMaxRanks + 1];    // CK_FANOUT: byte offset of segment s in
+                                       // the outputs (seg_off[nseg] = their size)
     int32_t cnt[kMaxSegs];             // rows per segment
     int32_t seg_tile_begin[kMaxSegs + 1];
     uint8_t head[kMaxSegs];            // vector path, per segment: bytes before its
@@ -141,6 +149,10 @@ struct SnacArgs {
     int32_t nseg;
     int32_t pieces;                    // G pieces per chunk
     int32_t slots;                     // D
+    int32_t lead;                      // E, 1..D: chunks staged ahead of the
+                                       // consumers in the ticket order (the
+                                       // other D - E slots are slack, so a
+                                       // producer seldom waits for a slot)
     int32_t dtype;                     // for the reducing stage
     int32_t nt_store;
     int32_t interleave;                // 1: every segment has the same number of
@@ -211,9 +223,11 @@ static_assert(sizeof(ReduceArgs) <= 4096 && sizeof(CopyArgs) <= 4096 && sizeof(S
 // Bytes before a segment's first byte in its first tile when tiles are
 // aligned to `tile_bytes` at the destination address `dst_addr` (the same
 // arithmetic on the host, to count tiles, and on the device, to place them).
+// Tiles are lanes x slots x 16 bytes with both factors powers of two, so the
+// remainder is a mask (a 64-bit remainder costs a kernel ~100 instructions).
 ATOM_HD inline int64_t seg_tile_shift(uint64_t dst_addr, int64_t tile_bytes)
 {
-    return static_cast<int64_t>(dst_addr % static_cast<uint64_t>(tile_bytes));
+    return static_cast<int64_t>(dst_addr & (static_cast<uint64_t>(tile_bytes) - 1));
 }
 
 }  // namespace atom

@@ -62,7 +62,14 @@ constexpr int64_t kPieceBytes = 64 << 10;            // SNAC task granule
 constexpr int64_t kMinAutoPiece = 8 << 10;           // smallest granule chosen for small partitions
 constexpr int64_t kSnacInflightBytes = 32 << 20;     // default ring: one on-chip BDP
 constexpr int64_t kSnacGrid = 512;                   // persistent SNAC workgroups (2 per CU)
-constexpr int64_t kMaxGrid = 1 << 20;
+constexpr int64_t kMaxGrid = 1 << 20;                // a multiple of the XCD count
+constexpr int64_t kXcdCount = 8;                     // XCDs of an MI355X; workgroup w runs on XCD w mod 8
+constexpr int64_t kFanBlockBytes = 8 << 20;          // blocked fan-out: bytes of source per block
+// Blocked fan-out: one workgroup per task up to this grid. A grid stride
+// would send each finished workgroup 2^20 tasks ahead, spreading the chip's
+// work over many blocks and losing their L2 reuse (measured: 1 GiB
+// partitions at 4.1 instead of 5.3 TB/s).
+constexpr int64_t kMaxGridBlocked = int64_t(1) << 30;
 constexpr int64_t kSmallSlots = 256 * 256;           // below: the latency path
 constexpr int64_t kDefaultWaitUs = 1000000;          // one SNAC wait: 1 s
 constexpr int64_t kMaxJitterUs = 10000;              // SNAC test hook: largest delay

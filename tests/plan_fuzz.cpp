@@ -74,7 +74,25 @@ void check_copy(const Plan& p, int iter)
         t = a.seg_tile_begin[s + 1];
     }
     check(a.ntiles == t, "copy ntiles", iter);
-    check(p.grid >= 1 && p.grid <= std::max<int64_t>(1, t), "copy grid", iter);
+    if (a.block_shift >= 0) {
+        // blocked fan-out: (block, output, tile) workgroup tasks, a grid
+        // stride that keeps every workgroup on one XCD
+        check(a.kind == CK_FANOUT && a.ndst > 1 && a.grid_segs == 0 && a.nseg <= kMaxRanks,
+              "copy blocked kind", iter);
+        check(a.block_shift >= 3 && a.block_shift <= 30, "copy block shift", iter);
+        const int64_t bt = int64_t(1) << a.block_shift;
+        check(a.nwork == cdiv(t, bt) * bt * a.ndst && (a.nwork >> a.block_shift) <= 0xFFFFFFFFll,
+              "copy blocked tasks", iter);
+        check(p.grid >= 1 && p.grid <= std::min<int64_t>(a.nwork, kMaxGridBlocked), "copy blocked grid", iter);
+        int64_t off = 0;
+        for (int s = 0; s < a.nseg; ++s) {
+            check(a.seg_off[s] == off, "copy blocked offsets", iter);
+            off += static_cast<int64_t>(a.cnt[s]) * a.row_bytes;
+        }
+        check(a.seg_off[a.nseg] == off, "copy blocked size", iter);
+    } else {
+        check(p.grid >= 1 && p.grid <= std::max<int64_t>(1, t), "copy grid", iter);
+    }
 }
 
 }  // namespace

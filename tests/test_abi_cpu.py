@@ -437,6 +437,12 @@ def test_launch_shapes_and_store_policy():
     ag = _plan(A.SHARD, A.GATHERED, A.OP_COPY, P, 64 * MiB // 2, 64 * MiB, 512 * MiB,
                cfg=A.config(flags=A.F_STAGED))
     assert (ag.staged, ag.lanes, ag.stages, ag.streaming_stores) == (1, 512, 8, 1)
+    # zero-staging fan-out beyond the latency path: blocked order, 8 KiB
+    # tiles, one workgroup per (tile, output) pair (8 MiB blocks of 1024
+    # tiles divide the 8 x 64 MiB exactly)
+    agz = _plan(A.SHARD, A.GATHERED, A.OP_COPY, P, 64 * MiB // 2, 64 * MiB, 512 * MiB)
+    assert (agz.staged, agz.lanes, agz.stages, agz.streaming_stores) == (0, 256, 2, 1)
+    assert agz.num_wgs == P * (P * 64 * MiB // 8192)
     no_nt = _plan(A.PARTITIONED, A.SHARD, A.OP_SUM, P, big // 2 // P, big, big // P,
                   cfg=A.config(flags=A.F_NO_NT))
     assert no_nt.streaming_stores == 0

@@ -610,3 +610,46 @@ def test_coaligned_offsets_take_the_vector_path(A, dtype, skew):
     _sync()
     _assert_reduced(from_dev(rd[0]), oracle.reduce(rs), "reduce")
     check_guards(fulls, [m], GUARD + skew)
+
+
+# ------------------------------------------- blocked fan-out (AllGather(V))
+
+@pytest.mark.parametrize("P", [2, 3, 8, 16])
+@pytest.mark.parametrize("skew", [0, 1, 3])
+@pytest.mark.parametrize("wgs", [0, 13, 64])
+def test_all_gather_blocked_order(A, P, skew, wgs):
+    """AllGathers large enough for the blocked fan-out (one output at a
+    time per block of tiles): several blocks with a ragged last one, buffers
+    skewed off 16-byte alignment by the same amount (element-wise heads in
+    the blocked kernel), a caller's grid that is not a multiple of the XCDs
+    (grid stride), and the V form with uneven partitions; bit-exact with
+    guard canaries."""
+    n = (3 << 20) // 2 + 8 * 37          # ~3 MiB partitions, not a whole number of tiles
+    say(f"blocked AG P={P} skew={skew} wgs={wgs}")
+    tdt = _torch_dtype(synth.BF16)
+    zs = [synth.mixed_bits(95, k, n, synth.BF16) for k in range(P)]
+    dz = [to_dev(z, pad_before=skew)[1] for z in zs]
+    fulls, outs = out_buffers([P * n] * P, tdt, GUARD + skew)
+    cfg = A.config(num_wgs=wgs) if wgs else None
+    st, info = A.atom_plan_query(A.layout(A.SHARD, dz, n), A.layout(A.GATHERED, outs, n), A.OP_COPY, cfg)
+    assert st == A.OK and info.vector_path == 1 and info.lanes == 256
+    A.all_gather(dz, outs, cfg)
+    _sync()
+    want = np.concatenate(zs)
+    for j in range(P):
+        assert_bits_equal(from_dev(outs[j]), want, f"blocked AG out_{j}", nan_by_class=False)
+    check_guards(fulls, [P * n] * P, GUARD + skew)
+    # V form: uneven partitions in rows of 8 elements (one of them empty)
+    g = synth.rank_rng(96, P)
+    cnt = g.integers(0, 2 * n // 8, size=P).astype(np.int64)
+    cnt[P // 2] = 0
+    T = int(cnt.sum()) * 8
+    zv = [synth.mixed_bits(97, k, int(cnt[k]) * 8, synth.BF16) for k in range(P)]
+    dv = [to_dev(z, pad_before=skew)[1] if z.size else empty_dev(1, tdt)[:0] for z in zv]
+    fulls, outs = out_buffers([T] * P, tdt, GUARD + skew)
+    A.all_gather_v(dv, outs, cnt, 8, cfg)
+    _sync()
+    want = oracle.all_gather_v(zv)
+    for j in range(P):
+        assert_bits_equal(from_dev(outs[j]), want[j], f"blocked AGV out_{j}", nan_by_class=False)
+    check_guards(fulls, [T] * P, GUARD + skew)
