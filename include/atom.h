@@ -37,10 +37,13 @@
  *  - Any element-aligned pointer is accepted, by every entry point. 16-byte
  *    aligned buffers whose partitions keep 16-byte alignment take the
  *    128-bit vector path; others take an element-wise path with the same
- *    results (zero-staging calls: streams that sit at a common offset from
- *    16-byte alignment stay vectorized with element-wise edges; staged
- *    calls choose per segment, a segment being the bytes one source sends
- *    to one destination).
+ *    results. Zero-staging calls stay vectorized when the streams sit at a
+ *    common offset from 16-byte alignment (element-wise edges), and also
+ *    when a part's sources and its destinations sit at different offsets
+ *    (each 16-byte store assembled from two source vectors), as long as the
+ *    sources of one part (reduce) or the destinations of one segment
+ *    (fan-out) agree; staged calls and the MoE movement choose per segment,
+ *    a segment being the bytes one source sends to one destination.
  *  - Calls that use the per-device workspace (the SNAC staging ring and its
  *    flags) are ordered by their stream; two such calls on different streams
  *    of one device must not overlap in time.
@@ -189,7 +192,9 @@ typedef struct atom_plan_info {
     atom_collective_kind kind;
     int32_t nranks;
     int32_t staged;            /* 1 when the call would run through SNAC */
-    int32_t vector_path;       /* 1 when every stream is 16-byte aligned */
+    int32_t vector_path;       /* 1: the 128-bit vector path (every stream
+                                  16-byte aligned, at one common offset from
+                                  it, or shifted, see below); 0: element-wise */
     int64_t elems_per_rank_in; /* elements of each input buffer */
     int64_t elems_per_rank_out[ATOM_MAX_RANKS];  /* elements of each output */
     int64_t credited_bytes;    /* algorithmic bytes: each input element read
@@ -205,6 +210,11 @@ typedef struct atom_plan_info {
                                   stores; 0: ordinary stores */
     int32_t grid_rows;         /* 1, or the parts of a small uniform reduce
                                   launched as a tiles x parts grid */
+    int32_t shifted;           /* 1 when the vector path moves some part or
+                                  segment between a source and a destination
+                                  at different offsets from 16-byte alignment
+                                  (each 16-byte store assembled from two
+                                  neighbouring source vectors) */
 } atom_plan_info;
 
 /* Atom copy (abstract: the copy primitive). Copies `bytes` bytes from src to

@@ -79,6 +79,7 @@ class AtomPlanInfo(ctypes.Structure):
         ("stages", ctypes.c_int32),
         ("streaming_stores", ctypes.c_int32),
         ("grid_rows", ctypes.c_int32),
+        ("shifted", ctypes.c_int32),
     ]
 
 

@@ -132,6 +132,81 @@ template <> struct SlotAcc<float> {      // 4 fp32 per slot
     }
 };
 
+// ---- byte-shifted slots (a source and a destination off each other's
+// 16-byte alignment) ------------------------------------------------------
+// A lane holds the source vector v (bytes [16v, 16v + 16) of the address
+// space) and gets vector v - 1 from its neighbour; the destination slot it
+// writes is 16 bytes that straddle the two. funnel16(lo, hi, d): the 16
+// bytes that begin 16 - d bytes into the string lo | hi (lo's bytes first),
+// d in 0..15 (d = 0 gives hi). d is wave-uniform, so the dword selection is
+// a uniform branch and the shifts are v_alignbyte_b32.
+__device__ __forceinline__ u32x4 funnel16(u32x4 lo, u32x4 hi, int d)
+{
+    const int s = 16 - d;                          // 1..16 bytes into lo | hi
+    const uint32_t r = static_cast<uint32_t>(s & 3);
+    const uint32_t c0 = lo[0], c1 = lo[1], c2 = lo[2], c3 = lo[3];
+    const uint32_t c4 = hi[0], c5 = hi[1], c6 = hi[2], c7 = hi[3];
+    u32x4 o;
+    switch (s >> 2) {
+    case 0:
+        o = u32x4{__builtin_amdgcn_alignbyte(c1, c0, r), __builtin_amdgcn_alignbyte(c2, c1, r),
+                  __builtin_amdgcn_alignbyte(c3, c2, r), __builtin_amdgcn_alignbyte(c4, c3, r)};
+        break;
+    case 1:
+        o = u32x4{__builtin_amdgcn_alignbyte(c2, c1, r), __builtin_amdgcn_alignbyte(c3, c2, r),
+                  __builtin_amdgcn_alignbyte(c4, c3, r), __builtin_amdgcn_alignbyte(c5, c4, r)};
+        break;
+    case 2:
+        o = u32x4{__builtin_amdgcn_alignbyte(c3, c2, r), __builtin_amdgcn_alignbyte(c4, c3, r),
+                  __builtin_amdgcn_alignbyte(c5, c4, r), __builtin_amdgcn_alignbyte(c6, c5, r)};
+        break;
+    case 3:
+        o = u32x4{__builtin_amdgcn_alignbyte(c4, c3, r), __builtin_amdgcn_alignbyte(c5, c4, r),
+                  __builtin_amdgcn_alignbyte(c6, c5, r), __builtin_amdgcn_alignbyte(c7, c6, r)};
+        break;
+    default:
+        o = hi;
+        break;
+    }
+    return o;
+}
+
+// The vector of the lane below in the wave; lane 0 gets `carry` (the
+// previous row's lane 63, or a vector loaded for it). Every lane of the
+// wave must be active.
+__device__ __forceinline__ u32x4 from_lane_below(u32x4 v, u32x4 carry)
+{
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        r[i] = static_cast<uint32_t>(__shfl_up(static_cast<int>(v[i]), 1, 64));
+    return (threadIdx.x & 63) == 0 ? carry : r;
+}
+
+__device__ __forceinline__ u32x4 lane63(u32x4 v)
+{
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        r[i] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v[i]), 63));
+    return r;
+}
+
+// Bytes [p0, p1) of slot `v` to the 16-byte aligned address `slot`, in
+// units of es bytes (the element size; p0 and p1 are multiples of it).
+__device__ __forceinline__ void store_slot_part(char* slot, u32x4 v, int p0, int p1, int es)
+{
+    for (int p = p0; p < p1; p += es) {
+        const uint32_t w = v[p >> 2];
+        if (es == 4)
+            *reinterpret_cast<uint32_t*>(slot + p) = w;
+        else if (es == 2)
+            *reinterpret_cast<uint16_t*>(slot + p) = static_cast<uint16_t>(w >> (8 * (p & 3)));
+        else
+            *reinterpret_cast<uint8_t*>(slot + p) = static_cast<uint8_t>(w >> (8 * (p & 3)));
+    }
+}
+
 // ---- XCD-aware tile order ----------------------------------------------
 // Workgroups are dispatched to the 8 XCDs round-robin (workgroup b runs on
 // XCD b mod 8). Renumbering so that XCD x's workgroups own one contiguous

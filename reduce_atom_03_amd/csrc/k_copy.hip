@@ -269,6 +269,88 @@ __global__ __launch_bounds__(256) void k_copy_fan_blocked(const CopyArgs a)
     }
 }
 
+// Segments whose source and destinations sit at different offsets from
+// 16-byte alignment (a V collective with rows of any length, buffers off
+// alignment by different amounts). Tiles run over the segment's 16-byte
+// source vectors, aligned in the address space: vector v holds bytes
+// [16v, 16v + 16), from the one holding the segment's first byte to one past
+// the one holding its last. Each wave owns 64 * U consecutive vectors, lane
+// l of row u vector v = w0 + 64u + l; it loads v (ordinary 16-byte loads,
+// which stay inside blocks that hold segment bytes), takes v - 1 from the
+// lane below (lane 0 from the previous row, or a load of its own for the
+// wave's first vector), and writes the destination slot that holds the
+// tail of v - 1 and the head of v: a 16-byte aligned store, or element-wise
+// stores for the slots at the segment's two ends. Every destination of a
+// segment sits at the same offset d from the source modulo 16.
+template <int U>
+__global__ __launch_bounds__(256) void k_copy_shift(const CopyArgs a)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const bool nt = a.nt_store != 0;
+    for (int64_t base = 0; base < a.ntiles; base += gridDim.x) {
+        const int64_t t = base + blockIdx.x;
+        if (t >= a.ntiles)
+            continue;
+        const int s = seg_of_tile(a, t);
+        const int64_t tip = t - a.seg_tile_begin[s];
+        const Seg g = seg_geometry(a, s);
+        const int64_t A = static_cast<int64_t>(reinterpret_cast<uintptr_t>(g.src));
+        const int64_t vlo = A >> 4, vhi = (A + g.bytes - 1) >> 4;
+        // Tiles are aligned to the tile size in the address space, at the
+        // source (exchange) or at output 0 (fan-out: P stores per load), so
+        // a wave's 16-byte accesses on that side fill whole cache lines; the
+        // first tile may start before the segment.
+        const int64_t tv = static_cast<int64_t>(blockDim.x) * U;      // vectors per tile, a power of two
+        int64_t v0 = vlo & ~(tv - 1);
+        if (a.align) {
+            const int64_t m0 = static_cast<int64_t>(reinterpret_cast<uintptr_t>(static_cast<const char*>(a.dst[0]) + g.dst_off)) - A;
+            v0 = vlo - ((vlo + (m0 >> 4)) & (tv - 1));
+        }
+        const int64_t w0 = v0 + tip * tv + wave * 64 * U;
+        // vector v at g.src - (A & 15) + 16 (v - vlo): addresses derived from
+        // the argument pointer, so the loads are global (not flat) ones
+        const char* vb = g.src - (A & 15) + ((w0 - vlo) << 4);
+        u32x4 R[U], L[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t v = w0 + u * 64 + lane;
+            R[u] = v >= vlo && v <= vhi ? ld16(vb + (u * 64 + lane) * kVecBytes) : u32x4{0, 0, 0, 0};
+        }
+        u32x4 carry = {0, 0, 0, 0};
+        if (lane == 0 && w0 - 1 >= vlo && w0 - 1 <= vhi)
+            carry = ld16(vb - kVecBytes);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            L[u] = from_lane_below(R[u], u == 0 ? carry : lane63(R[u - 1]));
+        const int q0 = g.dst >= 0 ? g.dst : 0;
+        const int q1 = g.dst >= 0 ? g.dst + 1 : a.ndst;
+        for (int q = q0; q < q1; ++q) {
+            char* D = static_cast<char*>(a.dst[q]) + g.dst_off;
+            const int d = static_cast<int>((reinterpret_cast<uintptr_t>(D) - static_cast<uint64_t>(A)) & 15);
+            // slot of vector v: source bytes [16v - d, 16v - d + 16), written
+            // 16-byte aligned at D + 16 (v - vlo) - (A & 15) - d; wave-uniform base
+            char* wbase = D + ((w0 - vlo) << 4) - (A & 15) - d;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t v = w0 + u * 64 + lane;
+                const int64_t sa = (v << 4) - d;
+                const int64_t lo = A - sa, hi = A + g.bytes - sa;
+                const int p0 = lo > 0 ? static_cast<int>(lo) : 0;
+                const int p1 = hi < 16 ? static_cast<int>(hi) : 16;
+                if (v > vhi + 1 || p0 >= p1)
+                    continue;
+                const u32x4 slot = funnel16(L[u], R[u], d);
+                const uint32_t off = static_cast<uint32_t>(u * 64 + lane) * kVecBytes;
+                if (p0 == 0 && p1 == 16)
+                    st16(wbase, off, slot, nt);
+                else
+                    store_slot_part(wbase + off, slot, p0, p1, a.esize);
+            }
+        }
+    }
+}
+
 // Element-wise variant for unaligned buffers or rows (U = 1).
 __global__ __launch_bounds__(256) void k_copy_elem(const CopyArgs a)
 {
@@ -299,6 +381,18 @@ hipError_t launch_copy(const Plan& p, hipStream_t stream)
         if (p.U != 1)
             return hipErrorInvalidValue;
         k_copy_elem<<<grid, block, 0, stream>>>(p.ca);
+        return hipGetLastError();
+    }
+    if (p.ca.shifted) {
+        if (p.ca.block_shift >= 0 || p.ca.grid_segs != 0 || p.wg % 64 != 0)
+            return hipErrorInvalidValue;
+        switch (p.U) {
+        case 1: k_copy_shift<1><<<grid, block, 0, stream>>>(p.ca); break;
+        case 2: k_copy_shift<2><<<grid, block, 0, stream>>>(p.ca); break;
+        case 4: k_copy_shift<4><<<grid, block, 0, stream>>>(p.ca); break;
+        case 8: k_copy_shift<8><<<grid, block, 0, stream>>>(p.ca); break;
+        default: return hipErrorInvalidValue;
+        }
         return hipGetLastError();
     }
     bool heads = false;

@@ -153,6 +153,98 @@ __global__ __launch_bounds__(256) void k_reduce_vec(const ReduceArgs a)
     }
 }
 
+// Parts whose P sources sit at one offset from 16-byte alignment and whose
+// destination(s) at another (ReduceScatterV with partitions of any length,
+// outputs off alignment by a different amount): as k_copy_shift, tiles run
+// over the part's aligned 16-byte source vectors (plus one), each lane
+// reduces its vector of all P sources in rank order, takes the reduced
+// vector below from its neighbour and writes the destination slot that
+// straddles the two (element-wise at the part's two ends). Bytes of a vector
+// outside the part are reduced too and never stored.
+template <typename T, int P, int U>
+__global__ __launch_bounds__(256) void k_reduce_shift(const ReduceArgs a)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const bool nt = a.nt_store != 0;
+    for (int64_t base = 0; base < a.ntiles; base += gridDim.x) {
+        const int64_t t = base + blockIdx.x;
+        if (t >= a.ntiles)
+            continue;
+        const int k = part_of_tile(a, t);
+        const int64_t tip = t - a.tile_begin[k];
+        const int64_t pstart = a.part_off[k];
+        const int64_t bytes = (a.part_off[k + 1] - pstart) * static_cast<int64_t>(sizeof(T));
+        const char* s0 = static_cast<const char*>(a.src[0]) + pstart * sizeof(T);
+        const int64_t A = static_cast<int64_t>(reinterpret_cast<uintptr_t>(s0));
+        const int64_t vlo = A >> 4, vhi = (A + bytes - 1) >> 4;
+        // Tiles are aligned to the tile size in the sources' address space,
+        // so a wave's loads fill whole cache lines; the part's first tile may
+        // start before it.
+        const int64_t tv = static_cast<int64_t>(blockDim.x) * U;      // vectors per tile, a power of two
+        const int64_t w0 = (vlo & ~(tv - 1)) + tip * tv + wave * 64 * U;
+        const int64_t vofs = ((w0 - vlo) << 4) - (A & 15);     // source bytes of vector w0
+        __amdgpu_buffer_rsrc_t rs[P];
+#pragma unroll
+        for (int r = 0; r < P; ++r)
+            rs[r] = stream_rsrc(static_cast<const char*>(a.src[r]) + pstart * sizeof(T) + vofs,
+                                64u * U * kVecBytes);
+        u32x4 R[U], L[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t v = w0 + u * 64 + lane;
+            R[u] = u32x4{0, 0, 0, 0};
+            if (v >= vlo && v <= vhi) {
+                const uint32_t off = static_cast<uint32_t>(u * 64 + lane) * kVecBytes;
+                u32x4 x[P];
+#pragma unroll
+                for (int r = 0; r < P; ++r)
+                    x[r] = ld16_stream(rs[r], off);
+                SlotAcc<T> acc;
+                acc.init(x[0]);
+#pragma unroll
+                for (int r = 1; r < P; ++r)
+                    acc.add(x[r]);
+                R[u] = acc.pack();
+            }
+        }
+        u32x4 carry = {0, 0, 0, 0};
+        if (lane == 0 && w0 - 1 >= vlo && w0 - 1 <= vhi) {
+            SlotAcc<T> acc;
+            acc.init(ld16_stream(static_cast<const char*>(a.src[0]) + pstart * sizeof(T) + vofs - kVecBytes));
+            for (int r = 1; r < P; ++r)
+                acc.add(ld16_stream(static_cast<const char*>(a.src[r]) + pstart * sizeof(T) + vofs - kVecBytes));
+            carry = acc.pack();
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            L[u] = from_lane_below(R[u], u == 0 ? carry : lane63(R[u - 1]));
+        const int q0 = a.mode == RM_SCATTER ? k : 0;
+        const int q1 = a.mode == RM_SCATTER ? k + 1 : a.ndst;
+        for (int q = q0; q < q1; ++q) {
+            char* D = static_cast<char*>(a.dst[q]) + (a.mode == RM_SCATTER ? 0 : pstart * sizeof(T));
+            const int d = static_cast<int>((reinterpret_cast<uintptr_t>(D) - static_cast<uint64_t>(A)) & 15);
+            char* wbase = D + vofs - d;                          // 16-byte aligned
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t v = w0 + u * 64 + lane;
+                const int64_t sa = (v << 4) - d;
+                const int64_t lo = A - sa, hi = A + bytes - sa;
+                const int p0 = lo > 0 ? static_cast<int>(lo) : 0;
+                const int p1 = hi < 16 ? static_cast<int>(hi) : 16;
+                if (v > vhi + 1 || p0 >= p1)
+                    continue;
+                const u32x4 slot = funnel16(L[u], R[u], d);
+                const uint32_t off = static_cast<uint32_t>(u * 64 + lane) * kVecBytes;
+                if (p0 == 0 && p1 == 16)
+                    st16(wbase, off, slot, nt);
+                else
+                    store_slot_part(wbase + off, slot, p0, p1, static_cast<int>(sizeof(T)));
+            }
+        }
+    }
+}
+
 // Element-wise variant for buffers or partitions off 16-byte alignment.
 template <typename T>
 __global__ __launch_bounds__(256) void k_reduce_elem(const ReduceArgs a)
@@ -182,6 +274,21 @@ template <typename T, int P>
 hipError_t launch_vec_p(const Plan& p, hipStream_t stream)
 {
     const dim3 grid(static_cast<unsigned>(p.grid)), block(p.wg);
+    if (p.ra.shifted) {
+        if (p.ra.grid_parts != 0 || p.wg % 64 != 0)
+            return hipErrorInvalidValue;
+        switch (p.U) {
+        case 1: k_reduce_shift<T, P, 1><<<grid, block, 0, stream>>>(p.ra); break;
+        case 2:
+            if constexpr (2 * P <= 32) { k_reduce_shift<T, P, 2><<<grid, block, 0, stream>>>(p.ra); break; }
+            else return hipErrorInvalidValue;
+        case 4:
+            if constexpr (4 * P <= 32) { k_reduce_shift<T, P, 4><<<grid, block, 0, stream>>>(p.ra); break; }
+            else return hipErrorInvalidValue;
+        default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     if (p.ra.grid_parts > 0) {
         const dim3 g2(static_cast<unsigned>(p.grid), static_cast<unsigned>(p.ra.grid_parts));
         switch (p.U) {

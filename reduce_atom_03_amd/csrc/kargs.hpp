@@ -55,7 +55,10 @@ struct ReduceArgs {
                                        // k * part_off[1]), no heads, one shift
                                        // (shift[0]) and gridDim.x tiles per part;
                                        // part = blockIdx.y
-    int32_t pad_;
+    int32_t shifted;                   // 1: a part's sources sit at one offset from
+                                       // 16-byte alignment and its destination(s)
+                                       // at another: k_reduce_shift, tiles over the
+                                       // part's source vectors plus one
 };
 
 // Copy family. Segments are derived in the kernel from row counts:
@@ -93,6 +96,11 @@ struct CopyArgs {
                                        // log2 of the tiles per block (a power of
                                        // two, at least the 8 XCDs); -1: every tile
                                        // stores to all outputs
+    int32_t shifted;                   // 1: some segment's source and destination
+                                       // sit at different offsets from 16-byte
+                                       // alignment (each segment's destinations at
+                                       // the same one): k_copy_shift, tiles over
+                                       // the segment's source vectors plus one
     int64_t nwork;                     // blocked order: workgroup tasks,
                                        // blocks * 2^block_shift * ndst
     int64_t seg_off[kMaxRanks + 1];    // CK_FANOUT: byte offset of segment s in

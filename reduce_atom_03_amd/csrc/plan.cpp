@@ -225,6 +225,24 @@ void build_reduce(Plan* p, int nsrc, const void* const* srcs, int ndst, void* co
     }
     if (!vec)
         std::memset(a.head, 0, sizeof a.head);
+    // Shifted vector path (k_reduce_shift): each part's sources share one
+    // offset from 16-byte alignment and its destination(s) share another.
+    // Only when that fails for a part does the call run element by element.
+    bool shifted = false;
+    if (!vec) {
+        shifted = true;
+        for (int k = 0; k < nparts && shifted; ++k) {
+            const int64_t off = part_off[k] * es;
+            const unsigned d = mis(srcs[0], off);
+            for (int r = 1; r < nsrc; ++r)
+                shifted = shifted && mis(srcs[r], off) == d;
+            if (mode == RM_FANOUT)
+                for (int q = 1; q < ndst; ++q)
+                    shifted = shifted && mis(dsts[q], off) == mis(dsts[0], off);
+        }
+        vec = shifted;
+    }
+    a.shifted = shifted ? 1 : 0;
     const int64_t ve = kVecBytes / es;   // elements per 16-byte slot
     p->vec = vec ? 1 : 0;
     p->U = vec ? pick_u_reduce(nsrc, mode, c.stages) : 1;
@@ -232,6 +250,11 @@ void build_reduce(Plan* p, int nsrc, const void* const* srcs, int ndst, void* co
     // workgroups measured +8% over 256 lanes on a cold 8-way reduce and +5%
     // on the fused AllReduce on MI355X.
     p->wg = vec ? 64 : 256;
+    // The shifted path: 64 lanes x 2 slots measured best on MI355X (the
+    // Zipf ReduceScatterV of 8 x 256 MiB in single-element partitions:
+    // 5.68 TB/s, against 5.40 with one slot and 5.25-5.66 at 128-256 lanes).
+    if (shifted && !c.stages && 2 * nsrc <= 32)
+        p->U = 2;
     int64_t slots = 0;
     for (int k = 0; k < nparts; ++k)
         slots += ceil_div(part_off[k + 1] - part_off[k], ve);
@@ -252,7 +275,7 @@ void build_reduce(Plan* p, int nsrc, const void* const* srcs, int ndst, void* co
         // source 0 (a part that starts mid-tile gets a short first tile), so
         // a tile's loads never straddle two tile-sized blocks of memory.
         int64_t shift = 0;
-        if (vec) {
+        if (vec && !shifted) {
             const uint64_t addr = reinterpret_cast<uintptr_t>(srcs[0]) +
                                   static_cast<uint64_t>((part_off[k] + a.head[k]) * es);
             shift = seg_tile_shift(addr, slots_per_tile * kVecBytes) / kVecBytes;
@@ -261,6 +284,15 @@ void build_reduce(Plan* p, int nsrc, const void* const* srcs, int ndst, void* co
         int64_t tiles = ceil_div(ceil_div(len, ve) + shift, slots_per_tile);
         if (a.head[k] > 0 && tiles == 0)
             tiles = 1;                   // a part that is all head still needs its tile
+        if (shifted && len > 0) {
+            // the part's source vectors, plus one for the last slot, from the
+            // tile-aligned vector at or before its first
+            const uint64_t a0 = reinterpret_cast<uintptr_t>(srcs[0]) + static_cast<uint64_t>(part_off[k] * es);
+            const int64_t vlo = static_cast<int64_t>(a0 / kVecBytes);
+            const int64_t nv = static_cast<int64_t>((a0 + len * es - 1) / kVecBytes) + 2 -
+                               (vlo & ~(slots_per_tile - 1));
+            tiles = ceil_div(nv, slots_per_tile);
+        }
         t += tiles;
     }
     a.tile_begin[nparts] = t;
@@ -290,7 +322,7 @@ void build_reduce(Plan* p, int nsrc, const void* const* srcs, int ndst, void* co
     a.grid_parts = 0;
     const int64_t L = part_off[1] - part_off[0];
     const int64_t tpp = nparts > 0 ? a.tile_begin[1] : 0;
-    bool uniform = vec && t > 0 && slots < kSmallSlots && part_off[0] == 0 && !a.xcd_remap &&
+    bool uniform = vec && !shifted && t > 0 && slots < kSmallSlots && part_off[0] == 0 && !a.xcd_remap &&
                    c.num_wgs == 0 && t <= kMaxGrid && nparts <= 65535;
     for (int k = 0; k < nparts && uniform; ++k)
         uniform = part_off[k] == k * L && a.head[k] == 0 && a.shift[k] == a.shift[0] &&
@@ -360,6 +392,23 @@ void build_copy(Plan* p, int32_t kind, int P, const void* const* srcs, int nsrc,
     }
     if (!vec)
         std::memset(a.head, 0, sizeof a.head);
+    // Shifted vector path (k_copy_shift): a segment's source and its
+    // destinations sit at different offsets from 16-byte alignment, every
+    // destination of the segment at the same one. Only when that fails for a
+    // segment does the whole call run element by element.
+    bool shifted = false;
+    if (!vec) {
+        shifted = true;
+        for (int s = 0; s < nseg && shifted; ++s) {
+            if (cnt[s] * row_bytes == 0 || kind != CK_FANOUT)
+                continue;
+            const uint64_t d0 = (reinterpret_cast<uintptr_t>(dsts[0]) + seg_dst[s] - seg_src[s]) % kVecBytes;
+            for (int q = 1; q < ndst; ++q)
+                shifted = shifted && (reinterpret_cast<uintptr_t>(dsts[q]) + seg_dst[s] - seg_src[s]) % kVecBytes == d0;
+        }
+        vec = shifted;
+    }
+    a.shifted = shifted ? 1 : 0;
     p->vec = vec ? 1 : 0;
     p->U = vec ? pick_u_copy(kind, nseg, c.stages) : 1;
     // 64-lane tiles over 256-lane ones, cold with streaming stores on
@@ -370,6 +419,16 @@ void build_copy(Plan* p, int32_t kind, int P, const void* const* srcs, int nsrc,
     // 6.33 TB/s, 256 x 2 6.25, 256 x 4 5.70, and 1 KiB tiles 4.7 (the
     // workgroup dispatch rate bounds a grid of that many small tiles).
     p->wg = !vec ? 256 : (nseg > 1 ? 64 : 128);
+    // The shifted path, measured on MI355X: the fan-out best at 256 lanes x
+    // 1 slot (Zipf AllGatherV of 8 x 64 MiB in single-element partitions:
+    // 5.79 TB/s, 5.71 at 64 x 1, 4.8-5.4 deeper), the exchange at 128 x 2
+    // (AllToAllV of 8 x 4096 rows of 7167 bf16: 5.89 TB/s, 5.73 at 64 x 2,
+    // 3.5-3.7 with one slot).
+    if (shifted && nseg > 1) {
+        p->wg = kind == CK_FANOUT ? 256 : 128;
+        if (!c.stages)
+            p->U = kind == CK_FANOUT ? 1 : 2;
+    }
     int64_t bytes = 0;
     for (int s = 0; s < nseg; ++s)
         bytes += cnt[s] * row_bytes;
@@ -387,7 +446,7 @@ void build_copy(Plan* p, int32_t kind, int P, const void* const* srcs, int nsrc,
     // stores; 64 MiB blocks (8 MiB per XCD, beyond its 4 MB L2) fall to 4.1.
     // In the AllGather of 8 x 64 MiB: 256 x 2 with 8 MiB blocks 6.03 TB/s,
     // 4 and 16 MiB 5.95, 256 x 4 5.6-5.7, 256 x 8 4.8-5.3.
-    const bool blocked = vec && kind == CK_FANOUT && ndst > 1 && nseg <= kMaxRanks &&
+    const bool blocked = vec && !shifted && kind == CK_FANOUT && ndst > 1 && nseg <= kMaxRanks &&
                          bytes >= kSmallSlots * kVecBytes && !(c.flags & ATOM_F_XCD_ORDER);
     if (blocked) {
         if (!c.lanes)
@@ -418,6 +477,20 @@ void build_copy(Plan* p, int32_t kind, int P, const void* const* srcs, int nsrc,
         int64_t tiles = rest ? ceil_div(rest + shift, a.tile_bytes) : 0;
         if (h > 0 && tiles == 0)
             tiles = 1;                   // a segment that is all head still needs its tile
+        if (shifted && rest > 0) {
+            // the segment's source vectors, plus one for the last slot, from
+            // the vector that starts a tile at the source (exchange) or at
+            // output 0 (fan-out), as k_copy_shift places them
+            const int64_t tv = static_cast<int64_t>(p->wg) * p->U;
+            const int64_t vlo = static_cast<int64_t>(seg_src[s] / kVecBytes);
+            int64_t v0 = vlo & ~(tv - 1);
+            if (a.align) {
+                const int64_t m0 = static_cast<int64_t>(reinterpret_cast<uintptr_t>(dsts[0]) + seg_dst[s] - seg_src[s]);
+                v0 = vlo - ((vlo + (m0 >> 4)) & (tv - 1));
+            }
+            const int64_t nv = static_cast<int64_t>((seg_src[s] + rest - 1) / kVecBytes) + 2 - v0;
+            tiles = ceil_div(nv, tv);
+        }
         t += tiles;
     }
     a.seg_tile_begin[nseg] = static_cast<int32_t>(t);
@@ -456,7 +529,7 @@ void build_copy(Plan* p, int32_t kind, int P, const void* const* srcs, int nsrc,
     // the grid is tiles-per-segment x segments.
     a.grid_segs = 0;
     const int64_t tps = nseg > 0 ? a.seg_tile_begin[1] : 0;
-    bool uniform = vec && t > 0 && bytes < kSmallSlots * kVecBytes && !a.xcd_remap &&
+    bool uniform = vec && !shifted && t > 0 && bytes < kSmallSlots * kVecBytes && !a.xcd_remap &&
                    c.num_wgs == 0 && nseg <= 65535;
     for (int s = 0; s < nseg && uniform; ++s)
         uniform = cnt[s] == cnt[0] && a.head[s] == 0 && a.seg_tile_begin[s] == s * tps;
@@ -1130,6 +1203,7 @@ void plan_fill_info(const Plan& p, atom_plan_info* info)
     info->lanes = p.wg;
     info->stages = p.U;
     info->grid_rows = static_cast<int32_t>(rows);
+    info->shifted = (p.exec == EX_REDUCE && p.ra.shifted) || (p.exec == EX_COPY && p.ca.shifted) ? 1 : 0;
     switch (p.exec) {
     case EX_REDUCE: info->streaming_stores = p.ra.nt_store; break;
     case EX_COPY: info->streaming_stores = p.ca.nt_store; break;

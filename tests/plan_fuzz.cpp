@@ -47,6 +47,14 @@ void check_reduce(const Plan& p, int iter)
         int64_t tiles = cdiv(cdiv(len - h, ve) + shift, ts);
         if (h > 0 && tiles == 0)
             tiles = 1;
+        if (a.shifted && len > 0) {
+            // shifted path: the part's aligned source vectors plus one
+            check(p.vec && h == 0 && shift == 0, "reduce shifted shape", iter);
+            const uint64_t a0 = reinterpret_cast<uintptr_t>(a.src[0]) + static_cast<uint64_t>(a.part_off[k] * p.esize);
+            const int64_t vlo = static_cast<int64_t>(a0 / kVecBytes);
+            const int64_t nv = static_cast<int64_t>((a0 + len * p.esize - 1) / kVecBytes) + 2 - (vlo & ~(ts - 1));
+            tiles = cdiv(nv, ts);
+        }
         t += tiles;
     }
     check(a.tile_begin[a.nparts] == t && a.ntiles == t, "reduce ntiles", iter);
@@ -68,7 +76,9 @@ void check_copy(const Plan& p, int iter)
         // an aligned segment may need one extra (short) tile at its start; a
         // segment that is all head has one tile
         const int64_t lo = std::max<int64_t>(cdiv(bytes, a.tile_bytes), h > 0 ? 1 : 0);
-        const int64_t hi = bytes ? cdiv(bytes, a.tile_bytes) + 1 : lo;
+        // (a shifted segment also covers one vector past its end and may
+        // start up to a tile before its first)
+        const int64_t hi = bytes ? cdiv(bytes, a.tile_bytes) + (a.shifted ? 2 : 1) : lo;
         const int64_t n = (s + 1 <= a.nseg ? a.seg_tile_begin[s + 1] : 0) - a.seg_tile_begin[s];
         check(n >= lo && n <= hi, "copy tiles per segment", iter);
         t = a.seg_tile_begin[s + 1];

@@ -255,11 +255,27 @@ def test_credited_bytes_of_the_workloads():
 
 def test_vector_path_selection():
     st, info = Q(A.PARTITIONED, A.SHARD, A.OP_SUM, n=64)
-    assert info.vector_path == 1
-    st, info = Q(A.PARTITIONED, A.SHARD, A.OP_SUM, n=63)        # partitions off 16 bytes
-    assert info.vector_path == 0
-    ins = [b + 2 for b in fake(4, 4096)]                        # bases off 16 bytes
+    assert info.vector_path == 1 and info.shifted == 0
+    # partitions off 16 bytes: the sources of each part agree, the outputs
+    # start aligned: the shifted vector path
+    st, info = Q(A.PARTITIONED, A.SHARD, A.OP_SUM, n=63)
+    assert info.vector_path == 1 and info.shifted == 1
+    ins = [b + 2 for b in fake(4, 4096)]                        # bases off 16 bytes, together
     st, info = Q(A.PARTITIONED, A.SHARD, A.OP_SUM, ins=ins)
+    assert st == A.OK and info.vector_path == 1 and info.shifted == 1
+    # sources of one part at different offsets: element-wise
+    ins = [b + 2 * (r % 2) for r, b in enumerate(fake(4, 4096))]
+    st, info = Q(A.PARTITIONED, A.SHARD, A.OP_SUM, ins=ins)
+    assert st == A.OK and info.vector_path == 0
+    # copies: AllToAllV rows of 6 bytes and AllGatherV rows of one element
+    C = np.arange(16, dtype=np.int64).reshape(4, 4) % 7
+    st, info = Q(A.PARTITIONED, A.TRANSPOSED, A.OP_COPY, counts=C, row=3)
+    assert st == A.OK and info.vector_path == 1 and info.shifted == 1
+    st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, counts=np.array([5, 0, 9, 3]), row=1)
+    assert st == A.OK and info.vector_path == 1 and info.shifted == 1
+    # a fan-out whose outputs sit at different offsets: element-wise
+    outs = [b + 2 * (r % 2) for r, b in enumerate(fake(4, 4096, start=BASE + (1 << 36)))]
+    st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, n=63, outs=outs)
     assert st == A.OK and info.vector_path == 0
 
 
@@ -391,8 +407,8 @@ def test_wide_workgroups_only_for_the_staged_kernel():
 def test_coaligned_offsets_plan_the_vector_path():
     """Buffers all off 16-byte alignment by the same amount (and partitions
     of 16-byte multiples) take the vector path with element-wise heads;
-    buffers off by different amounts, or partitions that change the offset,
-    take the element-wise path."""
+    outputs off by a different amount, or partitions that change the offset,
+    take the shifted vector path."""
     P, n = 8, 4096
     big = P * n * 2 * 4
     for off in (2, 6, 14):
@@ -404,9 +420,9 @@ def test_coaligned_offsets_plan_the_vector_path():
             assert st == A.OK and info.vector_path == 1, (off, kin, kout)
         st, info = Q(A.PARTITIONED, A.SHARD, A.OP_SUM, P=P, n=n, ins=ins,
                      outs=fake(P, big, start=BASE + (1 << 36), align_off=(off + 2) % 16))
-        assert st == A.OK and info.vector_path == 0
+        assert st == A.OK and info.vector_path == 1 and info.shifted == 1
         st, info = Q(A.PARTITIONED, A.SHARD, A.OP_SUM, P=P, n=n + 1, ins=ins, outs=outs)
-        assert st == A.OK and info.vector_path == 0      # partition k moves the offset
+        assert st == A.OK and info.vector_path == 1 and info.shifted == 1  # partition k moves the offset
 
 
 def _plan(kin, kout, op, P, n, in_bytes, out_bytes, cfg=None):

@@ -653,3 +653,139 @@ def test_all_gather_blocked_order(A, P, skew, wgs):
     for j in range(P):
         assert_bits_equal(from_dev(outs[j]), want[j], f"blocked AGV out_{j}", nan_by_class=False)
     check_guards(fulls, [T] * P, GUARD + skew)
+
+
+# ------------------------ shifted vector path (sources and outputs disagree)
+
+@pytest.mark.parametrize("dtype", [synth.BF16, synth.F32])
+@pytest.mark.parametrize("sk_in,sk_out", [(0, 1), (1, 0), (1, 3), (3, 2)])
+def test_shifted_offsets(A, dtype, sk_in, sk_out):
+    """Inputs sk_in elements and outputs sk_out elements past a 16-byte
+    boundary: each part's sources agree, its destination does not, so every
+    collective (and the flat copy and reduce) takes the shifted vector path,
+    the 16-byte stores assembled from neighbouring source vectors, with
+    element-wise slots at the ends; bit-exact (reductions: also within the
+    ulp bar) with guard canaries."""
+    P = 8
+    es = 2 if dtype == synth.BF16 else 4
+    n = 8 * 4099 + (16 // es) // 2            # partitions off 16 bytes too
+    tdt = _torch_dtype(dtype)
+    say(f"shifted sk_in={sk_in} sk_out={sk_out} {dtype}")
+
+    def dev(a):
+        return to_dev(a, pad_before=sk_in)[1] if a.size else empty_dev(1, tdt)[:0]
+
+    def outs(sizes):
+        return out_buffers(sizes, tdt, GUARD + sk_out)
+
+    xs = [synth.mixed_bits(87, r, P * n, dtype, specials=False) for r in range(P)]
+    dx = [dev(x) for x in xs]
+    fulls, ys = outs([n] * P)
+    st, info = A.atom_plan_query(A.layout(A.PARTITIONED, dx, n), A.layout(A.SHARD, ys, n), A.OP_SUM)
+    assert st == A.OK and info.vector_path == 1 and info.shifted == 1
+    A.reduce_scatter(dx, ys)
+    want = oracle.reduce_scatter(xs)
+    _sync()
+    for k in range(P):
+        _assert_reduced(from_dev(ys[k]), want[k], f"RS y_{k}")
+    check_guards(fulls, [n] * P, GUARD + sk_out)
+    fulls, ar = outs([P * n] * P)
+    A.all_reduce(dx, ar)
+    want = oracle.all_reduce(xs)
+    _sync()
+    for j in range(P):
+        _assert_reduced(from_dev(ar[j]), want[j], f"AR out_{j}")
+    check_guards(fulls, [P * n] * P, GUARD + sk_out)
+    fulls, a2 = outs([P * n] * P)
+    A.all_to_all(dx, a2)
+    want = oracle.all_to_all(xs)
+    _sync()
+    for j in range(P):
+        assert_bits_equal(from_dev(a2[j]), want[j], f"A2A out_{j}", nan_by_class=False)
+    check_guards(fulls, [P * n] * P, GUARD + sk_out)
+    zs = [synth.mixed_bits(88, k, n, dtype) for k in range(P)]
+    fulls, ag = outs([P * n] * P)
+    A.all_gather([dev(z) for z in zs], ag)
+    want = oracle.all_gather(zs)
+    _sync()
+    for j in range(P):
+        assert_bits_equal(from_dev(ag[j]), want[j], f"AG out_{j}", nan_by_class=False)
+    check_guards(fulls, [P * n] * P, GUARD + sk_out)
+    # V forms in single-element rows: segments of any length, some empty,
+    # some shorter than 16 bytes
+    g = synth.rank_rng(89, P)
+    cnt = g.integers(0, 40000, size=P).astype(np.int64)
+    cnt[1], cnt[4] = 0, 3
+    T = int(cnt.sum())
+    xv = [synth.mixed_bits(90, r, T, dtype, specials=False) for r in range(P)]
+    fulls, yv = outs([int(c) for c in cnt])
+    A.reduce_scatter_v([dev(x) for x in xv], yv, cnt, 1)
+    want = oracle.reduce_scatter_v(xv, cnt)
+    _sync()
+    for k in range(P):
+        _assert_reduced(from_dev(yv[k]), want[k], f"RSV y_{k}")
+    check_guards(fulls, [int(c) for c in cnt], GUARD + sk_out)
+    zv = [synth.mixed_bits(91, k, int(cnt[k]), dtype) for k in range(P)]
+    fulls, agv = outs([T] * P)
+    A.all_gather_v([dev(z) for z in zv], agv, cnt, 1)
+    want = oracle.all_gather_v(zv)
+    _sync()
+    for j in range(P):
+        assert_bits_equal(from_dev(agv[j]), want[j], f"AGV out_{j}", nan_by_class=False)
+    check_guards(fulls, [T] * P, GUARD + sk_out)
+    for row in (1, 3, 5):
+        C = synth.random_counts(92 + row, P, 900)
+        C[2, :] = 0
+        C[:, 5] = 1
+        rows, R = C.sum(axis=1), C.sum(axis=0)
+        vs = [synth.mixed_bits(93, r, int(rows[r]) * row, dtype) for r in range(P)]
+        fulls, av = outs([int(R[j]) * row for j in range(P)])
+        A.all_to_all_v([dev(v) for v in vs], av, C, row)
+        want = oracle.all_to_all_v(vs, C, row)
+        _sync()
+        for j in range(P):
+            assert_bits_equal(from_dev(av[j]), want[j], f"A2AV row={row} out_{j}", nan_by_class=False)
+        check_guards(fulls, [int(R[j]) * row for j in range(P)], GUARD + sk_out)
+    # flat copy and flat reduce of lengths around the 16-byte boundaries
+    for m in (1, 7, 8, 9, 100003):
+        src = synth.mixed_bits(94, m, m, dtype)
+        fulls, cp = outs([m])
+        A.atom_copy(cp[0], dev(src))
+        _sync()
+        assert_bits_equal(from_dev(cp[0]), src, f"copy m={m}", nan_by_class=False)
+        check_guards(fulls, [m], GUARD + sk_out)
+        rs = [synth.mixed_bits(95, r, m, dtype, specials=False) for r in range(3)]
+        fulls, rd = outs([m])
+        A.atom_reduce(rd[0], [dev(x) for x in rs])
+        _sync()
+        _assert_reduced(from_dev(rd[0]), oracle.reduce(rs), f"reduce m={m}")
+        check_guards(fulls, [m], GUARD + sk_out)
+
+
+@pytest.mark.parametrize("lanes,stages", [(64, 1), (128, 2), (256, 4), (64, 8)])
+def test_shifted_launch_shapes(A, lanes, stages):
+    """The shifted kernels at every workgroup width and depth (several waves
+    per workgroup: the first vector of each wave is loaded by its lane 0),
+    on a ReduceScatterV and an AllGatherV of single-element rows."""
+    P = 8
+    say(f"shifted shapes lanes={lanes} stages={stages}")
+    cnt = synth.zipf_partition(8 * 50001, P, 0.125, 1)
+    T = int(cnt.sum())
+    tdt = _torch_dtype(synth.BF16)
+    xs = [synth.mixed_bits(98, r, T, synth.BF16, specials=False) for r in range(P)]
+    fulls, ys = out_buffers([int(c) for c in cnt], tdt, GUARD)
+    cfg = A.config(lanes=lanes, stages=min(stages, 4))
+    A.reduce_scatter_v([to_dev(x)[1] for x in xs], ys, cnt, 1, cfg)
+    want = oracle.reduce_scatter_v(xs, cnt)
+    _sync()
+    for k in range(P):
+        _assert_reduced(from_dev(ys[k]), want[k], f"RSV y_{k}")
+    check_guards(fulls, [int(c) for c in cnt], GUARD)
+    zs = [synth.mixed_bits(99, k, int(cnt[k]), synth.BF16) for k in range(P)]
+    fulls, outs = out_buffers([T] * P, tdt, GUARD)
+    A.all_gather_v([to_dev(z)[1] for z in zs], outs, cnt, 1, A.config(lanes=lanes, stages=stages))
+    want = oracle.all_gather_v(zs)
+    _sync()
+    for j in range(P):
+        assert_bits_equal(from_dev(outs[j]), want[j], f"AGV out_{j}", nan_by_class=False)
+    check_guards(fulls, [T] * P, GUARD)
