@@ -17,6 +17,8 @@ resident synthetic input (bf16):
   dec     decode AllReduce, 8 x b x 7168 for b in 1, 2, 4, 8, 16 (N(0,0.02), seed 5)
   rsv_zipf ReduceScatterV of the 8 x 256 MiB, Zipf(0.125) partitions (Figure 16)
   agv_zipf AllGatherV of 512 MiB in Zipf(0.125) partitions
+  rsv_zipf_snac, agv_zipf_snac
+          the same two through SNAC (the library's default staged plan)
   ag_8k   AllGather, zero staging, 8 partitions of 8 KiB
   moe_route, moe_dispatch, moe_combine
           expert-parallel MoE (Table 2): routing of 8 ranks x 512 tokens, top-8
@@ -83,6 +85,11 @@ def parse():
                     help="instead of the step: cold HBM rates of streaming read, write, copy and "
                          "1 -> 8 fan-out (plain, rotated store order, pure writes, one allocation "
                          "at several spacings); one JSON line per point")
+    ap.add_argument("--snac-trace", action="store_true",
+                    help="instead of the step: phase analysis of the staged (SNAC) path from its "
+                         "per-task device-clock stamps (AllGather 8 x 64 MiB and 8 x 1 GiB at each "
+                         "chunk size and lead, composed AllReduce, Zipf RSV/AGV, 8 KiB calls); one "
+                         "JSON line per run")
     ap.add_argument("--xcd-order", action="store_true",
                     help="zero-staging kernels give each XCD one contiguous range of tiles")
     ap.add_argument("--no-snac", dest="snac", action="store_false",
@@ -113,6 +120,9 @@ def main():
         return
     if args.ceilings:
         ceilings(torch, dev)
+        return
+    if args.snac_trace:
+        snac_trace(A, synth, torch, dev)
         return
 
     def up(a):
@@ -221,6 +231,14 @@ def main():
     lay = (L(A.SHARD, zv, 0, cnt_ag, 8), L(A.GATHERED, agv_out, 0, None, 8))
     rows.append(("agv_zipf", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_COPY, zs_cfg),
                  plan_bytes(lay[0], lay[1], A.OP_COPY, zs_cfg, name="agv_zipf")))
+    if args.snac:
+        # the same two through SNAC: Figure 16 runs them on ordinary buffers
+        lay = (L(A.PARTITIONED, x2, 0, cnt_rs, 8), L(A.SHARD, rsv_out, 0, None, 8))
+        rows.append(("rsv_zipf_snac", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_SUM, snac_cfg),
+                     plan_bytes(lay[0], lay[1], A.OP_SUM, snac_cfg, name="rsv_zipf_snac")))
+        lay = (L(A.SHARD, zv, 0, cnt_ag, 8), L(A.GATHERED, agv_out, 0, None, 8))
+        rows.append(("agv_zipf_snac", lambda l=lay: A.atom_collective(l[0], l[1], A.OP_COPY, snac_cfg),
+                     plan_bytes(lay[0], lay[1], A.OP_COPY, snac_cfg, name="agv_zipf_snac")))
     lay8 = (L(A.SHARD, z8, 4096), L(A.GATHERED, o8, 4096))
     ag8 = lambda l=lay8: A.atom_collective(l[0], l[1], A.OP_COPY)
     rows.append(("ag_8k", ag8, plan_bytes(lay8[0], lay8[1], A.OP_COPY, name="ag_8k")))
@@ -416,7 +434,8 @@ def main():
                          f"AllGather 8 x {args.ag_mib} MiB (zero-staging"
                          + (" and SNAC, 512 KiB chunks, 64-slot ring); SNAC-composed AllReduce of the "
                             "8 x 256 MiB (2 MiB chunks, 16-slot ring); " if args.snac else "); ") +
-                         "ReduceScatterV and AllGatherV with Zipf(0.125) partitions of the same totals; "
+                         "ReduceScatterV and AllGatherV with Zipf(0.125) partitions of the same totals"
+                         + (", zero-staging and SNAC; " if args.snac else "; ") +
                          "decode AllReduce 8 x b x 7168 bf16, b = 1..16; AllGather 8 x 8 KiB; "
                          "MoE route, dispatch and combine of 8 x 512 tokens x 7168 bf16 "
                          "(256 experts, top-8)"),
@@ -520,6 +539,174 @@ def study(A, synth, torch, dev):
                               "cus_used": min(256, info.num_wgs), "stages": 0,
                               "ms": round(ms, 4), "GBps": round(gbs, 1),
                               "frac_hbm": round(gbs * 1e9 / HBM_PEAK, 4)}), flush=True)
+
+
+def snac_decode(t, G, E, Q):
+    """(produce, chunk, piece) of tickets t in the staged kernel's ticket
+    order: producers of chunks 0..E-1; then, for each later chunk q, the
+    consumers of chunk q-E followed by the producers of chunk q; then the
+    consumers of the last E chunks (G pieces per chunk, Q chunks)."""
+    warm = min(Q, E) * G
+    mid = max(Q - E, 0) * 2 * G
+    prod = np.zeros(t.size, dtype=bool)
+    chunk = np.zeros(t.size, dtype=np.int64)
+    a = t < warm
+    prod[a], chunk[a] = True, t[a] // G
+    b = (t >= warm) & (t < warm + mid)
+    u = t[b] - warm
+    q = E + u // (2 * G)
+    w = u - (q - E) * 2 * G
+    prod[b] = w >= G
+    chunk[b] = np.where(w >= G, q, q - E)
+    c = t >= warm + mid
+    prod[c], chunk[c] = False, max(Q - E, 0) + (t[c] - warm - mid) // G
+    return prod, chunk
+
+
+def snac_trace(A, synth, torch, dev):
+    """Where a staged call spends its time, from the stamps each task writes
+    (atom_config.trace: ticket taken, wait over, work done, on the device's
+    constant-rate clock). Per run: the kernel span; workgroup-time shares of
+    producer and consumer waits and work and of the claim/notify gaps
+    between tasks; per-task work times; the hand-off latency of each chunk
+    (its last piece staged -> its first consumer past the wait) and of each
+    slot reuse (the chunk D places earlier fully consumed -> the producer
+    past its wait); the ramp (span start -> first consume) and the drain
+    (last stage -> span end). The same call without the trace is timed
+    alongside (event pairs, median), as is its credited rate."""
+    P = 8
+    L = A.layout
+    us = 1e3 / A.atom_device_clock_khz()           # microseconds per clock tick
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def timed(fn, reps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+    def q(x, p):
+        return round(float(np.percentile(x, p)), 2) if x.size else None
+
+    def run(name, li, lo, op, reps=5, **kw):
+        cfg = A.config(flags=A.F_STAGED, **kw)
+        st, info = A.atom_plan_query(li, lo, op, cfg)
+        assert st == A.OK and info.staged == 1, (name, st)
+        n = int(info.snac_tasks)
+        G, E, Q = n // (2 * int(info.num_chunks)), int(info.snac_lead), int(info.num_chunks)
+        fn = lambda: A.atom_collective(li, lo, op, cfg)
+        fn()
+        ms = timed(fn, reps)
+        tr = torch.zeros(4 * n, dtype=torch.int64, device=dev)
+        tcfg = A.config(flags=A.F_STAGED, trace=tr.data_ptr(), **kw)
+        tfn = lambda: A.atom_collective(li, lo, op, tcfg)
+        ms_traced = timed(tfn, 1)
+        assert A.atom_sync_status() == A.OK, name
+        e = tr.cpu().numpy().reshape(n, 4)
+        c0, c1, c2 = e[:, 0], e[:, 1], e[:, 2]
+        wg = e[:, 3] & 0xFFFFFFFF
+        prod = ((e[:, 3] >> 32) & 1).astype(bool)
+        assert not ((e[:, 3] >> 33) & 1).any() and (c0 > 0).all(), name
+        dprod, chunk = snac_decode(np.arange(n, dtype=np.int64), G, E, Q)
+        assert (dprod == prod).all(), name
+        t0 = c0.min()
+        span = (c2.max() - t0) * us
+        wait, work = (c1 - c0) * us, (c2 - c1) * us
+        # gaps between a workgroup's tasks: notify, next ticket, barriers
+        o = np.lexsort((c0, wg))
+        same = wg[o][1:] == wg[o][:-1]
+        gaps = ((c0[o][1:] - c2[o][:-1]) * us)[same]
+        nwg = int(np.unique(wg).size)
+        wg_time = span * nwg
+        staged_at = np.full(Q, -1, dtype=np.int64)
+        np.maximum.at(staged_at, chunk[prod], c2[prod])
+        cons_start = np.full(Q, np.iinfo(np.int64).max, dtype=np.int64)
+        np.minimum.at(cons_start, chunk[~prod], c1[~prod])
+        consumed_at = np.full(Q, -1, dtype=np.int64)
+        np.maximum.at(consumed_at, chunk[~prod], c2[~prod])
+        handoff = (cons_start - staged_at) * us
+        D = int(info.ring_slots)
+        reuse = np.array([], dtype=np.float64)
+        if Q > D:
+            pstart = np.full(Q, np.iinfo(np.int64).max, dtype=np.int64)
+            np.minimum.at(pstart, chunk[prod], c1[prod])
+            reuse = (pstart[D:] - consumed_at[:-D]) * us
+        line = {
+            "snac_trace": name, "chunk_bytes": int(info.chunk_bytes), "pieces": G,
+            "ring_slots": D, "lead": E, "workgroups": nwg, "lanes": int(info.lanes), "tasks": n,
+            "ms": round(ms, 4), "ms_traced": round(ms_traced, 4),
+            "credited_GBps": round(info.credited_bytes / ms / 1e6, 1),
+            "span_us": round(span, 1),
+            "share": {k: round(float(v) / wg_time, 4) for k, v in (
+                ("producer_wait", wait[prod].sum()), ("producer_work", work[prod].sum()),
+                ("consumer_wait", wait[~prod].sum()), ("consumer_work", work[~prod].sum()),
+                ("gaps", gaps.sum()))},
+            "producer_work_us": {"p50": q(work[prod], 50), "p90": q(work[prod], 90)},
+            "consumer_work_us": {"p50": q(work[~prod], 50), "p90": q(work[~prod], 90)},
+            "producer_wait_us": {"p50": q(wait[prod], 50), "p90": q(wait[prod], 90)},
+            "consumer_wait_us": {"p50": q(wait[~prod], 50), "p90": q(wait[~prod], 90)},
+            "gap_us": {"p50": q(gaps, 50), "p90": q(gaps, 90)},
+            "handoff_us": {"p50": q(handoff, 50), "p90": q(handoff, 90), "max": q(handoff, 100)},
+            "slot_reuse_us": {"p50": q(reuse, 50), "p90": q(reuse, 90)},
+            "ramp_us": round(float((cons_start.min() - t0) * us), 2),
+            "drain_us": round(float((c2.max() - staged_at.max()) * us), 2),
+            "first_stage_done_us": round(float((staged_at.min() - t0) * us), 2),
+        }
+        print(json.dumps(line), flush=True)
+
+    MiB = 1 << 20
+    # AllGather 8 x 64 MiB: each chunk size; the 512 KiB one at smaller leads
+    S = 64 * MiB
+    z = [up(a) for a in synth.c4_inputs(S, P)]
+    o = [torch.empty(P * S // 2, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+    li, lo = L(A.SHARD, z, S // 2), L(A.GATHERED, o, S // 2)
+    for chunk in (512 << 10, 1 << 20, 2 << 20):
+        run(f"ag_8x64MiB_chunk{chunk >> 10}K", li, lo, A.OP_COPY, chunk_bytes=chunk)
+    for lead in (32, 16, 8):
+        run(f"ag_8x64MiB_chunk512K_lead{lead}", li, lo, A.OP_COPY, chunk_bytes=512 << 10, snac_lead=lead)
+    for lead in (8, 4):
+        run(f"ag_8x64MiB_chunk2048K_lead{lead}", li, lo, A.OP_COPY, chunk_bytes=2 << 20, snac_lead=lead)
+    del z, o
+    # composed AllReduce 8 x 256 MiB, default plan
+    N2 = 1 << 27
+    x = [torch.randn(N2, device=dev).to(torch.bfloat16) for _ in range(P)]
+    ar = [torch.empty(N2, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+    run("ar_8x256MiB", L(A.PARTITIONED, x, N2 // P), L(A.GATHERED, ar, N2 // P), A.OP_SUM)
+    for lead in (8, 4):
+        run(f"ar_8x256MiB_lead{lead}", L(A.PARTITIONED, x, N2 // P), L(A.GATHERED, ar, N2 // P),
+            A.OP_SUM, snac_lead=lead)
+    del ar
+    # Zipf ReduceScatterV / AllGatherV, default staged plans
+    cnt = synth.zipf_partition(N2, P, 0.125, 8) // 8
+    ys = [torch.empty(int(c) * 8, dtype=torch.bfloat16, device=dev) for c in cnt]
+    run("rsv_zipf_8x256MiB", L(A.PARTITIONED, x, 0, cnt, 8), L(A.SHARD, ys, 0, None, 8), A.OP_SUM)
+    del ys, x
+    T = P * 64 * MiB // 2
+    cnt = synth.zipf_partition(T, P, 0.125, 8) // 8
+    zv = [torch.empty(int(c) * 8, dtype=torch.bfloat16, device=dev).uniform_(-1, 1) for c in cnt]
+    ov = [torch.empty(T, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+    run("agv_zipf_512MiB", L(A.SHARD, zv, 0, cnt, 8), L(A.GATHERED, ov, 0, None, 8), A.OP_COPY)
+    del zv, ov
+    # small calls: 8 KiB AllGather and AllReduce, default plans
+    z8 = [torch.empty(4096, dtype=torch.bfloat16, device=dev).uniform_(-1, 1) for _ in range(P)]
+    o8 = [torch.empty(P * 4096, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+    run("ag_8x8KiB", L(A.SHARD, z8, 4096), L(A.GATHERED, o8, 4096), A.OP_COPY, reps=200)
+    x8 = [torch.randn(4096, device=dev).to(torch.bfloat16) for _ in range(P)]
+    run("ar_8x8KiB", L(A.PARTITIONED, x8, 512), L(A.GATHERED, o8, 512), A.OP_SUM, reps=200)
+    del z8, o8, x8
+    # AllGather 8 x 1 GiB: each chunk size
+    S = 1024 * MiB
+    z = [torch.empty(S // 2, dtype=torch.bfloat16, device=dev).uniform_(-1, 1) for _ in range(P)]
+    o = [torch.empty(P * S // 2, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+    li, lo = L(A.SHARD, z, S // 2), L(A.GATHERED, o, S // 2)
+    for chunk in (512 << 10, 1 << 20, 2 << 20):
+        run(f"ag_8x1GiB_chunk{chunk >> 10}K", li, lo, A.OP_COPY, reps=3, chunk_bytes=chunk)
 
 
 def sweep(A, synth, torch, dev):
@@ -843,6 +1030,9 @@ def cpu_baseline(args, C3, S, credited):
             oracle.all_reduce(x5[b])
         oracle.reduce_scatter_v(c2, cnt_rs * 8)
         oracle.all_gather_v(zv)
+        if args.snac:
+            oracle.reduce_scatter_v(c2, cnt_rs * 8)
+            oracle.all_gather_v(zv)
         oracle.all_gather(z8)
         E, k, H = synth.MOE_EXPERTS, synth.MOE_TOPK, synth.HIDDEN
         pos, _, recv = oracle.moe_route(moe_ids, E, k)

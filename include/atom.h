@@ -42,8 +42,9 @@
  *    when a part's sources and its destinations sit at different offsets
  *    (each 16-byte store assembled from two source vectors), as long as the
  *    sources of one part (reduce) or the destinations of one segment
- *    (fan-out) agree; staged calls and the MoE movement choose per segment,
- *    a segment being the bytes one source sends to one destination.
+ *    (fan-out) agree; staged calls choose per segment, a segment being the
+ *    bytes one source sends to one destination; the MoE movement chooses
+ *    per call.
  *  - Calls that use the per-device workspace (the SNAC staging ring and its
  *    flags) are ordered by their stream; two such calls on different streams
  *    of one device must not overlap in time.
@@ -172,6 +173,25 @@ typedef struct atom_config {
                                   at other than their natural timing. The
                                   result is unchanged; only time is added. */
     uint32_t jitter_seed;
+    int32_t snac_lead;         /* SNAC ticket order: chunks staged ahead of
+                                  the first consumer, 0..64, clamped to the
+                                  ring depth (0: the ring depth). Smaller
+                                  leads leave slack
+                                  slots so a producer seldom waits for a
+                                  slot to be freed. */
+    uint64_t* trace;           /* measurement hook of the staged path (NULL:
+                                  off): a device array, caller-owned, of at
+                                  least 4 * atom_plan_info.snac_tasks
+                                  entries. Task t (its ticket) writes entry
+                                  4t: the device clock when its workgroup
+                                  took the ticket; 4t+1: when its wait
+                                  ended; 4t+2: when its work (stage, or
+                                  consume) had completed; 4t+3: its
+                                  workgroup index | producer flag << 32 |
+                                  wait given up << 33. The clock is the
+                                  device's constant-rate counter
+                                  (hipDeviceAttributeWallClockRate kHz).
+                                  Results are unchanged. */
 } atom_config;
 
 /* The collective that a pair of layouts and an op names (Figure 4/6,
@@ -215,6 +235,9 @@ typedef struct atom_plan_info {
                                   at different offsets from 16-byte alignment
                                   (each 16-byte store assembled from two
                                   neighbouring source vectors) */
+    int32_t snac_lead;         /* SNAC: chunks staged ahead of the consumers */
+    int64_t snac_tasks;        /* SNAC: stage + consume tasks (2 * chunks *
+                                  pieces per chunk); 0 when not staged */
 } atom_plan_info;
 
 /* Atom copy (abstract: the copy primitive). Copies `bytes` bytes from src to
@@ -364,13 +387,15 @@ atom_status atom_moe_route(const atom_moe_routing* rt, void* stream);
  * device pointers to T rows; out: host array of P device pointers to
  * capacity_rows rows each (rows no entry lands on are not written). Uses
  * the positions of the last atom_moe_route on rt. Rows at or beyond
- * capacity_rows are dropped; recv_rows tells how many would land. Needs
- * 16-byte aligned buffers and rows (else ATOM_ERR_UNSUPPORTED). cfg may be
- * NULL (defaults); of its fields lanes (64, 128, 256), stages (16-byte
- * slots per lane per tile), num_wgs and ATOM_F_NO_NT apply, the SNAC fields
- * are ignored, and ATOM_F_STAGED or ATOM_F_XCD_ORDER is
- * ATOM_ERR_UNSUPPORTED. Returns ATOM_OK, ATOM_ERR_INVALID_ARG,
- * ATOM_ERR_UNSUPPORTED or ATOM_ERR_HIP. */
+ * capacity_rows are dropped; recv_rows tells how many would land. Any
+ * element-aligned buffers are accepted: 16-byte aligned buffers with rows
+ * of a 16-byte multiple take the 128-bit kernels, others an element-wise
+ * kernel (one tile per token row, ordinary stores) with the same results.
+ * cfg may be NULL (defaults); of its fields lanes (64, 128, 256), stages
+ * (16-byte slots per lane per tile; ignored by the element-wise kernel),
+ * num_wgs and ATOM_F_NO_NT apply, the SNAC fields are ignored, and
+ * ATOM_F_STAGED or ATOM_F_XCD_ORDER is ATOM_ERR_UNSUPPORTED. Returns
+ * ATOM_OK, ATOM_ERR_INVALID_ARG, ATOM_ERR_UNSUPPORTED or ATOM_ERR_HIP. */
 atom_status atom_moe_dispatch(const atom_moe_routing* rt, const void* const* x,
                               void* const* out, int64_t capacity_rows,
                               int64_t row_elems, atom_dtype dtype,
@@ -387,6 +412,11 @@ atom_status atom_moe_combine(const atom_moe_routing* rt, const void* const* y,
                              const float* const* weights, void* const* out,
                              int64_t capacity_rows, int64_t row_elems,
                              atom_dtype dtype, const atom_config* cfg, void* stream);
+
+/* Rate of the device clock that atom_config.trace stamps count, in kHz,
+ * for the current HIP device. Returns ATOM_OK, ATOM_ERR_INVALID_ARG (khz
+ * NULL) or ATOM_ERR_HIP. */
+atom_status atom_device_clock_khz(int32_t* khz);
 
 /* Library version, (major << 16) | minor. */
 int32_t atom_version(void);

@@ -59,6 +59,8 @@ class AtomConfig(ctypes.Structure):
         ("lanes", ctypes.c_int32),
         ("jitter_us", ctypes.c_int32),
         ("jitter_seed", ctypes.c_uint32),
+        ("snac_lead", ctypes.c_int32),
+        ("trace", ctypes.c_void_p),
     ]
 
 
@@ -80,6 +82,8 @@ class AtomPlanInfo(ctypes.Structure):
         ("streaming_stores", ctypes.c_int32),
         ("grid_rows", ctypes.c_int32),
         ("shifted", ctypes.c_int32),
+        ("snac_lead", ctypes.c_int32),
+        ("snac_tasks", ctypes.c_int64),
     ]
 
 
@@ -105,7 +109,7 @@ EXPORTS = ("atom_copy", "atom_reduce", "atom_collective", "atom_collective_noall
            "atom_plan_query",
            "atom_sync_status", "atom_bdp_chunk_bytes", "atom_status_string",
            "atom_last_error", "atom_version", "atom_moe_scratch_bytes",
-           "atom_moe_route", "atom_moe_dispatch", "atom_moe_combine")
+           "atom_moe_route", "atom_moe_dispatch", "atom_moe_combine", "atom_device_clock_khz")
 
 
 def _hip_runtimes() -> set:
@@ -153,6 +157,8 @@ def _load() -> ctypes.CDLL:
     lib.atom_last_error.restype = ctypes.c_char_p
     lib.atom_version.argtypes = []
     lib.atom_version.restype = ctypes.c_int32
+    lib.atom_device_clock_khz.argtypes = [ctypes.POINTER(ctypes.c_int32)]
+    lib.atom_device_clock_khz.restype = ctypes.c_int
     rp = ctypes.POINTER(AtomMoeRouting)
     vpp = ctypes.POINTER(vp)
     lib.atom_moe_scratch_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -248,11 +254,12 @@ def _flatten(c):
 
 def config(chunk_bytes: int = 0, stages: int = 0, num_wgs: int = 0, flags: int = 0,
            ring_slots: int = 0, piece_bytes: int = 0, wait_us: int = 0,
-           lanes: int = 0, jitter_us: int = 0, jitter_seed: int = 0) -> AtomConfig:
+           lanes: int = 0, jitter_us: int = 0, jitter_seed: int = 0,
+           snac_lead: int = 0, trace: int = 0) -> AtomConfig:
     return AtomConfig(chunk_bytes=chunk_bytes, stages=stages, num_wgs=num_wgs,
                       flags=flags, ring_slots=ring_slots, piece_bytes=piece_bytes,
                       wait_us=wait_us, lanes=lanes, jitter_us=jitter_us,
-                      jitter_seed=jitter_seed)
+                      jitter_seed=jitter_seed, snac_lead=snac_lead, trace=trace or None)
 
 
 # --------------------------------------------------------- the C entry points
@@ -267,6 +274,15 @@ def atom_last_error() -> str:
 
 def atom_version() -> int:
     return int(lib.atom_version())
+
+
+def atom_device_clock_khz() -> int:
+    """Rate of the clock behind atom_config.trace stamps (kHz)."""
+    v = ctypes.c_int32(0)
+    st = int(lib.atom_device_clock_khz(ctypes.byref(v)))
+    if st != OK:
+        raise RuntimeError(f"atom_device_clock_khz: {atom_status_string(st)}")
+    return int(v.value)
 
 
 def atom_bdp_chunk_bytes(bytes_per_s: float, round_trip_s: float) -> int:

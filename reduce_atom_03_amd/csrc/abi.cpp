@@ -324,6 +324,19 @@ const char* atom_status_string(atom_status s)
     return "unknown status";
 }
 
+atom_status atom_device_clock_khz(int32_t* khz)
+{
+    if (!khz)
+        return ATOM_ERR_INVALID_ARG;
+    int dev = 0, v = 0;
+    if (hipError_t e = hipGetDevice(&dev); e != hipSuccess)
+        return atom::hip_status(e);
+    if (hipError_t e = hipDeviceGetAttribute(&v, hipDeviceAttributeWallClockRate, dev); e != hipSuccess)
+        return atom::hip_status(e);
+    *khz = v;
+    return ATOM_OK;
+}
+
 int32_t atom_version(void) { return (0 << 16) | 1; }
 
 }  // extern "C"

@@ -403,6 +403,29 @@ __global__ __launch_bounds__(256) void k_moe_dispatch(const MoeMoveArgs a)
     }
 }
 
+// Element-wise dispatch (a buffer or the row size off 16-byte alignment):
+// one tile per token row, each lane copying elements of E bytes (the
+// element size) with a stride of the workgroup.
+template <typename E, int KMAX>
+__global__ __launch_bounds__(256) void k_moe_dispatch_elem(const MoeMoveArgs a)
+{
+    const int64_t n = a.row_bytes / static_cast<int64_t>(sizeof(E));
+    for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+        int r;
+        int64_t t;
+        token_of(a, tile, &r, &t);
+        const Choices<KMAX> ch = token_choices<KMAX>(a, r, t, a.dst, false);
+        const E* src = reinterpret_cast<const E*>(a.src[r] + t * a.row_bytes);
+        for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+            const E v = src[i];
+#pragma unroll
+            for (int c = 0; c < KMAX; ++c)
+                if ((ch.live >> c) & 1u)
+                    reinterpret_cast<E*>(ch.row[c])[i] = v;
+        }
+    }
+}
+
 // Accumulators of one 16-byte slot: 8 bf16 or 4 fp32 elements.
 template <typename T> struct FmaAcc;
 
@@ -490,6 +513,30 @@ __global__ __launch_bounds__(256) void k_moe_combine(const MoeMoveArgs a)
     }
 }
 
+// Element-wise combine: one tile per token row; each element is the same
+// chain of binary32 fused multiply-adds in choice order from +0 as in the
+// vector path, rounded once.
+template <typename T, int KMAX>
+__global__ __launch_bounds__(256) void k_moe_combine_elem(const MoeMoveArgs a)
+{
+    const int64_t n = a.row_bytes / static_cast<int64_t>(sizeof(T));
+    for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+        int r;
+        int64_t t;
+        token_of(a, tile, &r, &t);
+        const Choices<KMAX> ch = token_choices<KMAX>(a, r, t, const_cast<char* const*>(a.src), true);
+        char* dst = a.dst[r] + t * a.row_bytes;
+        for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int c = 0; c < KMAX; ++c)
+                if ((ch.live >> c) & 1u)
+                    acc = __builtin_fmaf(ch.w[c], Elem<T>::load(ch.row[c], i), acc);
+            Elem<T>::store(dst, i, acc);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_moe_route(const MoeRoutePlan& p, hipStream_t stream)
@@ -525,13 +572,34 @@ hipError_t launch_moe_move(const MoeMovePlan& p, bool combine, hipStream_t strea
     const MoeMoveArgs& a = p.a;
     if (a.ntiles == 0)
         return hipSuccess;
+    const dim3 grid(static_cast<unsigned>(p.grid)), block(static_cast<unsigned>(p.wg));
+    const int kmax = a.k <= 2 ? 2 : a.k <= 4 ? 4 : a.k <= 8 ? 8 : 16;
+    if (a.elem) {
+        const int es = a.dtype == DT_BF16 ? 2 : 4;
+        if (p.grid < 1 || a.k < 1 || a.k > kMoeMaxTopk || a.per < 1 || a.row_bytes % es != 0 ||
+            p.wg < 64 || p.wg > 256 || p.wg % 64 != 0 || a.pieces != 1 || a.piece_bytes != a.row_bytes)
+            return hipErrorInvalidValue;
+        const bool bf = a.dtype == DT_BF16;
+#define ATOM_MOE_ELEM(KM)                                                                     \
+    case KM:                                                                                  \
+        if (combine)                                                                          \
+            bf ? k_moe_combine_elem<uint16_t, KM><<<grid, block, 0, stream>>>(a)              \
+               : k_moe_combine_elem<float, KM><<<grid, block, 0, stream>>>(a);                \
+        else                                                                                  \
+            bf ? k_moe_dispatch_elem<uint16_t, KM><<<grid, block, 0, stream>>>(a)             \
+               : k_moe_dispatch_elem<uint32_t, KM><<<grid, block, 0, stream>>>(a);            \
+        break;
+        switch (kmax) {
+        ATOM_MOE_ELEM(2) ATOM_MOE_ELEM(4) ATOM_MOE_ELEM(8) ATOM_MOE_ELEM(16)
+        }
+#undef ATOM_MOE_ELEM
+        return hipGetLastError();
+    }
     if (p.grid < 1 || a.k < 1 || a.k > kMoeMaxTopk || a.per < 1 || a.row_bytes % kVecBytes != 0 ||
         p.wg < 64 || p.wg > 256 || p.wg % 64 != 0 ||
         a.piece_bytes != static_cast<int64_t>(p.wg) * p.U * kVecBytes || a.pieces < 1 ||
         a.pieces * a.piece_bytes < a.row_bytes)
         return hipErrorInvalidValue;
-    const dim3 grid(static_cast<unsigned>(p.grid)), block(static_cast<unsigned>(p.wg));
-    const int kmax = a.k <= 2 ? 2 : a.k <= 4 ? 4 : a.k <= 8 ? 8 : 16;
     if (combine) {
         const bool bf = a.dtype == DT_BF16;
         switch (kmax) {

@@ -38,7 +38,13 @@
 // slot of chunk q-D, whose consumers were claimed D-E chunk steps earlier
 // (E = D would make it wait for the consumers claimed just before it). A
 // claimed ticket belongs to a running workgroup, so the lowest unfinished
-// task can always proceed: no deadlock for any grid size or occupancy. Every wait is
+// task can always proceed: no deadlock for any grid size or occupancy. A
+// workgroup claims its next ticket only when its task is done: claimed while
+// the task runs (to hide the atomic's round trip), the next ticket's task
+// waits for the current one, and since adjacent tickets depend on each
+// other (a chunk's consumers, then the producers that reuse their slots)
+// that chained the tasks; measured on MI355X, the staged AllGather of
+// 8 x 64 MiB took 2.7 ms instead of 0.98. Every wait is
 // bounded; on expiry the error word is set to the call's sequence number,
 // the task is dropped, and the call's later waits give up at once, so the
 // grid always drains (a later call, with another number, waits normally).
@@ -162,6 +168,10 @@ __device__ __forceinline__ bool wait_at_least(const SnacArgs& a, const unsigned 
                                               unsigned long long target, long long t_begin,
                                               int* s_ok)
 {
+    // A count of zero is always met (a slot's first use): no flag load, no
+    // barrier. `target` is wave-uniform, so this is a uniform branch.
+    if (target == 0)
+        return true;
     if (threadIdx.x == 0) {
         int ok = 1;
         if (flag_load_relaxed(flag) < target) {
@@ -413,6 +423,8 @@ __global__ __launch_bounds__(MAXT) void k_snac(const SnacArgs a)
         s_ticket = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     int64_t t = static_cast<unsigned int>(__builtin_amdgcn_readfirstlane(static_cast<int>(s_ticket)));
+    unsigned long long* const tr = a.trace;
+    long long t_claim = tr ? wall_clock64() : 0;
     while (t < a.ntasks) {
         const Task task = decode_task(a, t);
         const int64_t slot = task.chunk % a.slots;
@@ -434,6 +446,7 @@ __global__ __launch_bounds__(MAXT) void k_snac(const SnacArgs a)
         const unsigned long long target =
             static_cast<unsigned long long>(task.produce ? use : use + 1) * a.pieces;
         const bool ok = wait_at_least(a, wflag, target, t_begin, &s_ok);
+        const long long t_wait = tr ? wall_clock64() : 0;
         if (ok) {
             if (task.produce) {
                 if (elem)
@@ -463,12 +476,24 @@ __global__ __launch_bounds__(MAXT) void k_snac(const SnacArgs a)
         }
         __syncthreads();
         if (threadIdx.x == 0) {
+            if (tr) {
+                // measurement hook: this task's stamps (ordinary stores)
+                unsigned long long* e = tr + 4 * t;
+                e[0] = static_cast<unsigned long long>(t_claim);
+                e[1] = static_cast<unsigned long long>(t_wait);
+                e[2] = static_cast<unsigned long long>(wall_clock64());
+                e[3] = static_cast<unsigned long long>(blockIdx.x) |
+                       (static_cast<unsigned long long>(task.produce) << 32) |
+                       (static_cast<unsigned long long>(!ok) << 33);
+            }
             if (ok)
                 flag_add_relaxed((task.produce ? a.ready : a.freed) + slot * kFlagStride, 1ull);
             s_ticket = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
         t = static_cast<unsigned int>(__builtin_amdgcn_readfirstlane(static_cast<int>(s_ticket)));
+        if (tr)
+            t_claim = wall_clock64();
     }
     // Every workgroup counts itself out; the last one clears the ticket, the
     // slot counters and the count for the next staged call on this device,
@@ -477,17 +502,23 @@ __global__ __launch_bounds__(MAXT) void k_snac(const SnacArgs a)
     // until they have completed before counting out, and the last workgroup
     // clears only after its count returned, so every update of this call
     // precedes the clearing. The error word is kept for the host.
+    // Only the slots this call used (chunk q takes slot q mod D) have moved;
+    // the others are still zero from the call that last used them. The last
+    // workgroup clears them one per lane.
     if (threadIdx.x == 0) {
         wait_vmem();
         const unsigned int prev =
             __hip_atomic_fetch_add(a.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (prev == gridDim.x - 1) {
-            for (int sl = 0; sl < a.slots; ++sl) {
-                __hip_atomic_store(a.ready + sl * kFlagStride, 0ull, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(a.freed + sl * kFlagStride, 0ull, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            }
+        s_ok = prev == gridDim.x - 1 ? 1 : 0;
+    }
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(s_ok) != 0) {
+        const int used = static_cast<int>(a.nchunks < a.slots ? a.nchunks : a.slots);
+        for (int i = threadIdx.x; i < 2 * used; i += blockDim.x) {
+            unsigned long long* f = i < used ? a.ready + i * kFlagStride : a.freed + (i - used) * kFlagStride;
+            __hip_atomic_store(f, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (threadIdx.x == 0) {
             __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(a.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }

@@ -139,6 +139,8 @@ struct SnacArgs {
                                        // wait timed out (0: none since cleared)
     unsigned int* done;                // workgroups finished (the last one
                                        // clears the counters for the next call)
+    unsigned long long* trace;         // measurement hook: 4 clock stamps per
+                                       // task (NULL: off)
     int64_t row_bytes;                 // bytes per counted row
     int64_t chunk_bytes;
     int64_t piece_bytes;               // chunk_bytes / pieces
@@ -221,6 +223,9 @@ struct MoeMoveArgs {
     int32_t k;
     int32_t dtype;
     int32_t nt_store;
+    int32_t elem;                      // 1: a buffer or the row size is off 16-byte
+                                       // alignment: one tile per token row, moved
+                                       // element by element (piece = the row)
 };
 
 // Kernel arguments of a launch are limited to 4 KiB.

@@ -245,7 +245,7 @@ int main(int argc, char** argv)
                   "moe small routing", iter);
         }
         const int64_t cap = pick(0, 9) == 0 ? pick(-1, 3) : pick(0, 40000);
-        const int64_t row = pick(0, 9) == 0 ? pick(-1, 9) : 8 * pick(1, 1024);
+        const int64_t row = pick(0, 9) == 0 ? pick(-1, 9) : (pick(0, 3) == 0 ? pick(1, 8191) : 8 * pick(1, 1024));
         const atom_dtype dt = static_cast<atom_dtype>(pick(0, 9) == 0 ? pick(-1, 2) : pick(0, 1));
         for (int combine = 0; combine < 2; ++combine) {
             MoeMovePlan mp;
@@ -269,14 +269,21 @@ int main(int argc, char** argv)
             const int64_t ntok = static_cast<int64_t>(P) * T;
             check(mp.wg >= 64 && mp.wg <= 256 && mp.wg % 64 == 0, "moe lanes", iter);
             check(mp.U == 1 || mp.U == 2 || mp.U == 4 || mp.U == 8, "moe U", iter);
-            check(mp.a.piece_bytes == static_cast<int64_t>(mp.wg) * mp.U * kVecBytes, "moe piece", iter);
+            if (mp.a.elem) {
+                // element-wise: one tile per token row
+                check(mp.U == 1 && mp.a.piece_bytes == mp.a.row_bytes && mp.a.pieces == (mp.a.row_bytes > 0),
+                      "moe elem piece", iter);
+                check(mp.a.row_bytes % (dt == ATOM_DT_BF16 ? 2 : 4) == 0, "moe elem rows", iter);
+            } else {
+                check(mp.a.piece_bytes == static_cast<int64_t>(mp.wg) * mp.U * kVecBytes, "moe piece", iter);
+            }
             check(ntok == 0 || mp.a.row_bytes == 0 ||
                       (mp.a.pieces * mp.a.piece_bytes >= mp.a.row_bytes &&
                        (mp.a.pieces - 1) * mp.a.piece_bytes < mp.a.row_bytes),
                   "moe pieces cover the row", iter);
             check(mp.a.ntiles == ntok * mp.a.pieces, "moe tiles", iter);
             check(mp.a.ntiles == 0 || (mp.grid >= 1 && mp.grid <= mp.a.ntiles), "moe grid", iter);
-            check(mp.a.ntiles == 0 || mp.a.row_bytes % kVecBytes == 0, "moe row alignment", iter);
+            check(mp.a.ntiles == 0 || mp.a.elem || mp.a.row_bytes % kVecBytes == 0, "moe row alignment", iter);
             check(mp.a.k == k && mp.a.per * P == E, "moe shape", iter);
             check(mp.credited_bytes == ntok * ((k + 1) * mp.a.row_bytes + k * (combine ? 12 : 8)),
                   "moe credited bytes", iter);

@@ -492,3 +492,68 @@ def test_uniform_grid_only_for_equal_aligned_small_parts():
     assert st == A.OK and info.grid_rows == 1
     ag = _plan(A.SHARD, A.GATHERED, A.OP_COPY, P, 1 << 21, 1 << 22, P * (1 << 22))
     assert ag.grid_rows == 1
+
+
+def _c_layout(tmp_path, struct, fields):
+    """sizeof and field offsets of `struct` as the C compiler lays it out."""
+    import subprocess
+    src = tmp_path / f"{struct}.c"
+    fmt = " ".join(["%zu"] * (len(fields) + 1))
+    args = ", ".join([f"sizeof({struct})"] + [f"offsetof({struct}, {f})" for f in fields])
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "atom.h"\n'
+                   f'int main(void){{printf("{fmt}\\n", {args});return 0;}}\n')
+    exe = tmp_path / struct
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    subprocess.run(["gcc", "-I", os.path.join(root, "include"), str(src), "-o", str(exe)], check=True)
+    return [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                           check=True).stdout.split()]
+
+
+@pytest.mark.parametrize("struct,cls", [("atom_config", "AtomConfig"),
+                                        ("atom_plan_info", "AtomPlanInfo")])
+def test_structs_match_the_header(tmp_path, struct, cls):
+    C = getattr(A, cls)
+    names = [f[0] for f in C._fields_]
+    got = _c_layout(tmp_path, struct, names)
+    assert got == [ctypes.sizeof(C)] + [getattr(C, n).offset for n in names]
+
+
+def test_snac_lead_and_task_count():
+    """The ticket order's lead defaults to the ring depth, is clamped to it,
+    and out-of-range values are rejected; the task count is 2 * chunks *
+    pieces per chunk (the size of the trace array, in quadruples)."""
+    ins, outs = fake(8, 8 << 20), fake(8, 64 << 20, start=BASE + (1 << 36))
+    cfg = A.config(flags=A.F_STAGED, chunk_bytes=512 << 10, piece_bytes=64 << 10, ring_slots=16)
+    st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=8, ins=ins, outs=outs, n=(8 << 20) // 2, cfg=cfg)
+    assert st == A.OK and info.staged == 1
+    assert info.snac_lead == 16
+    assert info.snac_tasks == 2 * info.num_chunks * 8
+    cfg.snac_lead = 4
+    st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=8, ins=ins, outs=outs, n=(8 << 20) // 2, cfg=cfg)
+    assert st == A.OK and info.snac_lead == 4
+    cfg.snac_lead = 40
+    st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=8, ins=ins, outs=outs, n=(8 << 20) // 2, cfg=cfg)
+    assert st == A.OK and info.snac_lead == 16
+    for bad in (-1, 65):
+        cfg.snac_lead = bad
+        st, _ = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=8, ins=ins, outs=outs, n=(8 << 20) // 2, cfg=cfg)
+        assert st == A.ERR_INVALID_ARG, bad
+    st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=8, ins=ins, outs=outs, n=(8 << 20) // 2)
+    assert st == A.OK and info.staged == 0 and info.snac_tasks == 0 and info.snac_lead == 0
+
+
+def test_snac_default_lead_by_stage():
+    """A copying stage leads by the ring depth, a reducing one by half of it."""
+    P, n = 8, 1 << 20
+    ins = fake(P, P * n * 2)
+    outs = fake(P, P * n * 2, start=BASE + (1 << 36))
+    cfg = A.config(flags=A.F_STAGED, chunk_bytes=2 << 20, ring_slots=16)
+    st, info = Q(A.PARTITIONED, A.GATHERED, A.OP_SUM, P=P, n=n, ins=ins, outs=outs, cfg=cfg)
+    assert st == A.OK and info.staged == 1 and info.ring_slots == 16 and info.snac_lead == 8
+    st, info = Q(A.PARTITIONED, A.SHARD, A.OP_SUM, P=P, n=n, ins=ins, outs=outs, cfg=cfg)
+    assert st == A.OK and info.snac_lead == 8
+    st, info = Q(A.PARTITIONED, A.TRANSPOSED, A.OP_COPY, P=P, n=n, ins=ins, outs=outs, cfg=cfg)
+    assert st == A.OK and info.snac_lead == 16
+    cfg = A.config(flags=A.F_STAGED, chunk_bytes=2 << 20, ring_slots=1)
+    st, info = Q(A.PARTITIONED, A.GATHERED, A.OP_SUM, P=P, n=n, ins=ins, outs=outs, cfg=cfg)
+    assert st == A.OK and info.snac_lead == 1

@@ -10,6 +10,10 @@ parallelism) against the CPU oracle, through the C ABI.
   rows; payloads carry NaNs and subnormals and must move bit-exactly.
 * Combine: bit-exact against the oracle's binary32 fused multiply-add chain
   (NaN compared by class), bf16 and fp32, signed weights, dropped entries.
+* Dispatch and combine with buffers and rows off 16-byte alignment (odd row
+  lengths, buffers one to three elements off, rows under 16 bytes; the
+  element-wise kernels), with guard elements around every output; and the
+  full workload shape one element off.
 * The MoE workload at full size (8 ranks x 512 tokens x 7168 bf16, 256
   experts, top-8): route, dispatch and combine against the oracle, and
   combine(dispatch(x)) with weights 1/8 returns x bit for bit (-0 as +0).
@@ -130,11 +134,21 @@ def test_dispatch_and_combine_tile_shapes(A, case, shape):
     _move_case(A, case, A.config(lanes=shape[0], stages=shape[1]))
 
 
-def _move_case(A, case, cfg):
+GUARD = 37          # guard elements after each output (their sentinel must survive)
+
+
+def _out(n, tdt, fill, skew):
+    """n elements at `skew` elements into a buffer with GUARD sentinel
+    elements after them: (full buffer, view)."""
+    full = empty_dev(skew + max(n, 1) + GUARD, tdt, fill)
+    return full, full[skew:skew + max(n, 1)]
+
+
+def _move_case(A, case, cfg, skew_in=0, skew_out=0):
     import torch
     seed, P, T, E, k, H, dt, inv, cut = case
     say(f"moe dispatch/combine P={P} T={T} E={E} k={k} H={H} {dt} invalid={inv} cut={cut} "
-        f"cfg={None if cfg is None else (cfg.lanes, cfg.stages)}")
+        f"cfg={None if cfg is None else (cfg.lanes, cfg.stages)} skew={skew_in},{skew_out}")
     ids = ids_for(seed, P, T, E, k, inv)
     rt, _ = route_dev(A, ids, E, k)
     pos, recv = check_route(rt, ids, E, k, "route")
@@ -142,25 +156,80 @@ def _move_case(A, case, cfg):
     tdt = torch.bfloat16 if dt == synth.BF16 else torch.float32
     sentinel = 0x7E01 if dt == synth.BF16 else 0x3F812345     # a bf16 NaN; an fp32 number
     xs = [synth.mixed_bits(seed, r, T * H, dt) for r in range(P)]
-    x_dev = [to_dev(x)[1] for x in xs]
-    out_dev = [empty_dev(max(cap, 1) * H, tdt, sentinel) for _ in range(P)]
+    x_dev = [to_dev(x, pad_before=skew_in)[1] for x in xs]
+    outs = [_out(cap * H, tdt, sentinel, skew_out) for _ in range(P)]
+    out_dev = [o[1] for o in outs]
     A.atom_moe_dispatch(rt, x_dev, out_dev, cap, H, cfg=cfg)
     want = oracle.moe_dispatch(xs, ids, pos, E, k, H, cap, fill=sentinel if dt == synth.BF16 else
                                np.uint32(sentinel).view(np.float32))
     for j in range(P):
-        assert_bits_equal(from_dev(out_dev[j])[:cap * H], want[j], f"dispatch rank {j}",
+        full = from_dev(outs[j][0])
+        assert_bits_equal(full[skew_out:skew_out + cap * H], want[j], f"dispatch rank {j}",
                           nan_by_class=False)
+        guard = np.concatenate([full[:skew_out], full[skew_out + max(cap * H, 1):]])
+        assert (guard.view(np.uint16 if dt == synth.BF16 else np.uint32) ==
+                (sentinel if dt == synth.BF16 else np.uint32(sentinel))).all(), f"dispatch guard {j}"
     # combine: expert outputs of the dispatch shape, signed weights
     ys = [synth.mixed_bits(seed + 100, j, max(cap, 1) * H, dt) for j in range(P)]
-    y_dev = [to_dev(y)[1] for y in ys]
+    y_dev = [to_dev(y, pad_before=skew_in)[1] for y in ys]
     g = np.random.default_rng(seed)
     w = [(g.random(T * k, dtype=np.float32) * 3 - 1).astype(np.float32) for _ in range(P)]
     w_dev = [torch.from_numpy(a).to("cuda") if a.size else torch.zeros(1, device="cuda") for a in w]
-    o_dev = [empty_dev(max(T, 1) * H, tdt, 0) for _ in range(P)]
+    outs = [_out(T * H, tdt, sentinel, skew_out) for _ in range(P)]
+    o_dev = [o[1] for o in outs]
     A.atom_moe_combine(rt, y_dev, w_dev, o_dev, cap, H, cfg=cfg)
     want = oracle.moe_combine([y[:cap * H] if cap else y[:0] for y in ys], ids, pos, w, E, k, H, cap)
     for r in range(P):
-        assert_bits_equal(from_dev(o_dev[r])[:T * H], want[r], f"combine rank {r}")
+        full = from_dev(outs[r][0])
+        assert_bits_equal(full[skew_out:skew_out + T * H], want[r], f"combine rank {r}")
+        guard = np.concatenate([full[:skew_out], full[skew_out + max(T * H, 1):]])
+        assert (guard.view(np.uint16 if dt == synth.BF16 else np.uint32) ==
+                (sentinel if dt == synth.BF16 else np.uint32(sentinel))).all(), f"combine guard {r}"
+
+
+# Buffers and rows off 16-byte alignment: the element-wise kernels.
+ELEM_CASES = [  # (case, skew_in, skew_out)
+    ((21, 8, 64, 32, 4, 7167, synth.BF16, 0.0, 0), 0, 0),    # odd row length
+    ((11, 8, 64, 32, 4, 7168, synth.BF16, 0.0, 0), 1, 1),    # buffers one element off
+    ((11, 8, 64, 32, 4, 7168, synth.BF16, 0.0, 0), 0, 3),    # only the outputs off
+    ((22, 4, 33, 8, 3, 37, synth.F32, 0.1, 5), 1, 2),        # fp32, odd rows, drops
+    ((23, 3, 50, 6, 2, 5, synth.BF16, 0.05, 0), 2, 0),       # rows shorter than 16 bytes
+    ((24, 8, 40, 64, 16, 255, synth.BF16, 0.0, 2), 1, 1),    # k = 16
+]
+
+
+@pytest.mark.parametrize("case,skew_in,skew_out", ELEM_CASES,
+                         ids=lambda c: "x" if not isinstance(c, tuple) else f"H{c[5]}-{c[6]}")
+def test_dispatch_and_combine_off_alignment(A, case, skew_in, skew_out):
+    _move_case(A, case, None, skew_in, skew_out)
+
+
+def test_moe_workload_one_element_off(A):
+    """The full MoE workload shape (8 x 512 x 7168 bf16, 256 experts,
+    top-8) with every buffer one element off 16-byte alignment: route,
+    dispatch and combine against the oracle."""
+    import torch
+    P, T, E, k, H = 8, synth.MOE_TOKENS, synth.MOE_EXPERTS, synth.MOE_TOPK, synth.HIDDEN
+    say("moe workload, buffers one element off alignment")
+    ids, w = synth.moe_routing(6, P, T, E, k)
+    xs = synth.moe_inputs()
+    rt, _ = route_dev(A, ids, E, k)
+    pos, recv = check_route(rt, ids, E, k, "workload route")
+    cap = int(recv.max())
+    x_dev = [to_dev(x, pad_before=1)[1] for x in xs]
+    outs = [_out(cap * H, torch.bfloat16, 0x7E01, 1) for _ in range(P)]
+    A.atom_moe_dispatch(rt, x_dev, [o[1] for o in outs], cap, H)
+    want = oracle.moe_dispatch(xs, ids, pos, E, k, H, cap, fill=0x7E01)
+    for j in range(P):
+        assert_bits_equal(from_dev(outs[j][1]), want[j], f"dispatch rank {j}", nan_by_class=False)
+    ys = [synth.ranks(60 + j, 1, cap * H, "normal", synth.BF16)[0] for j in range(P)]
+    y_dev = [to_dev(y, pad_before=1)[1] for y in ys]
+    w_dev = [torch.from_numpy(a).to("cuda") for a in w]
+    outs = [_out(T * H, torch.bfloat16, 0, 1) for _ in range(P)]
+    A.atom_moe_combine(rt, y_dev, w_dev, [o[1] for o in outs], cap, H)
+    want = oracle.moe_combine(ys, ids, pos, w, E, k, H, cap)
+    for r in range(P):
+        assert_bits_equal(from_dev(outs[r][1]), want[r], f"combine rank {r}")
 
 
 def test_moe_workload_full(A):

@@ -11,6 +11,9 @@ benchmark times (default plans):
   of 1 GiB (the largest size), zero-staging and SNAC with each chunk size
   and the default ring: every output block equals its partition, compared
   on the device.
+* ReduceScatterV of the 8 x 256 MiB and AllGatherV of 512 MiB in Zipf(0.125)
+  partitions, zero-staging and SNAC, partitions in rows of 8 elements and in
+  single elements.
 """
 
 import numpy as np
@@ -90,38 +93,50 @@ def test_c2_all_reduce_snac_full(A, c2, shape):
         assert torch.equal(outs[j].view(torch.int16), outs[0].view(torch.int16)), f"out_{j}"
 
 
-def test_zipf_reduce_scatter_v_full(A, c2):
+@pytest.mark.parametrize("mode", ["zs", "zs-unit1", "snac", "snac-unit1"])
+def test_zipf_reduce_scatter_v_full(A, c2, mode):
     """ReduceScatterV of the 8 x 256 MiB inputs with Zipf(0.125) partitions
-    (Figure 16's shape), every output element against the oracle."""
+    (Figure 16's shape), every output element against the oracle: zero
+    staging and through SNAC (the default staged plan, as benchmarked), with
+    partitions counted in rows of 8 elements and in single elements (the
+    shifted vector path, and staged segments off 16-byte alignment)."""
     import torch
     P, N = 8, 1 << 27
-    cnt = synth.zipf_partition(N, P, 0.125, 8) // 8
-    say(f"Zipf RSV 8 x 256 MiB rows={cnt.tolist()}")
-    want = oracle.reduce_scatter_v(c2, cnt * 8)
+    unit = 1 if mode.endswith("unit1") else 8
+    cnt = synth.zipf_partition(N, P, 0.125, unit) // unit
+    cfg = A.config(flags=A.F_STAGED) if mode.startswith("snac") else None
+    say(f"Zipf RSV 8 x 256 MiB {mode} rows={cnt.tolist()}")
+    want = oracle.reduce_scatter_v(c2, cnt * unit)
     dx = [to_dev(x)[1] for x in c2]
-    ys = [empty_dev(int(c) * 8, torch.bfloat16) for c in cnt]
-    A.reduce_scatter_v(dx, ys, cnt, 8)
+    ys = [empty_dev(int(c) * unit, torch.bfloat16) for c in cnt]
+    A.reduce_scatter_v(dx, ys, cnt, unit, cfg)
+    assert A.atom_sync_status() == A.OK
     torch.cuda.synchronize()
     for k in range(P):
-        assert_bits_equal(from_dev(ys[k]), want[k], f"Zipf RSV y_{k}")
+        assert_bits_equal(from_dev(ys[k]), want[k], f"Zipf RSV {mode} y_{k}")
 
 
-def test_zipf_all_gather_v_full(A):
+@pytest.mark.parametrize("mode", ["zs", "zs-unit1", "snac", "snac-unit1"])
+def test_zipf_all_gather_v_full(A, mode):
     """AllGatherV of 512 MiB in Zipf(0.125) partitions: 8 outputs of 512 MiB,
-    every block compared on the device."""
+    every block compared on the device; zero staging and through SNAC, in
+    rows of 8 elements and in single elements."""
     import torch
     P, T = 8, 1 << 28
-    cnt = synth.zipf_partition(T, P, 0.125, 8) // 8
-    say(f"Zipf AGV total 512 MiB rows={cnt.tolist()}")
-    zs = [to_dev(synth.draw(4, k, int(cnt[k]) * 8, "uniform", synth.BF16))[1] for k in range(P)]
+    unit = 1 if mode.endswith("unit1") else 8
+    cnt = synth.zipf_partition(T, P, 0.125, unit) // unit
+    cfg = A.config(flags=A.F_STAGED) if mode.startswith("snac") else None
+    say(f"Zipf AGV total 512 MiB {mode} rows={cnt.tolist()}")
+    zs = [to_dev(synth.draw(4, k, int(cnt[k]) * unit, "uniform", synth.BF16))[1] for k in range(P)]
     outs = [empty_dev(T, torch.bfloat16, 0xFFFF) for _ in range(P)]
-    A.all_gather_v(zs, outs, cnt, 8)
+    A.all_gather_v(zs, outs, cnt, unit, cfg)
+    assert A.atom_sync_status() == A.OK
     torch.cuda.synchronize()
-    off = np.concatenate([[0], np.cumsum(cnt * 8)])
+    off = np.concatenate([[0], np.cumsum(cnt * unit)])
     for j in range(P):
         for k in range(P):
             assert torch.equal(outs[j][off[k]:off[k + 1]].view(torch.int16),
-                               zs[k].view(torch.int16)), f"out_{j} block {k}"
+                               zs[k].view(torch.int16)), f"{mode} out_{j} block {k}"
 
 
 def test_c3_all_to_all_v_full(A):
