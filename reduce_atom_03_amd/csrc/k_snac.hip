@@ -298,6 +298,17 @@ struct StageReduce {
 
 // Consume (vector path): one piece from the slot to its destination(s). A
 // last vector that ends past the segment is written in 2-byte units.
+// Stores are aligned to the destination's 128-byte lines: the piece's
+// destination starts D bytes past a line (D a multiple of 16, taken from the
+// first destination; every destination of an AllGather segment sits at the
+// same offset when the outputs share their alignment), and when the piece is
+// a whole number of lines, vector v of the loop takes piece byte
+// (16 v - D) mod bytes. Each wave's 64 stores then fill whole lines (the
+// first D / 16 vectors write the piece's last D bytes, which end on a line),
+// instead of every wave straddling one more line than it fills; the ring
+// loads take the offset instead, one line in eight. Measured on MI355X: the
+// staged AllGatherV of 512 MiB in Zipf(0.125) partitions (segments at
+// 16-byte offsets) 1.00 -> 0.90 ms, the time of the uniform AllGather.
 template <int U>
 __device__ __forceinline__ void consume_vec(const SnacArgs& a, const SegGeo& g, const char* src,
                                             int64_t dst_off, int64_t bytes)
@@ -309,22 +320,30 @@ __device__ __forceinline__ void consume_vec(const SnacArgs& a, const SegGeo& g, 
     const int q0 = g.dst < 0 ? 0 : g.dst;
     const int q1 = g.dst < 0 ? a.P : g.dst + 1;
     const int64_t step = static_cast<int64_t>(nthr) * U * kVecBytes;
+    constexpr int64_t kLine = 128;
+    const int64_t D = bytes % kLine == 0
+                          ? static_cast<int64_t>((reinterpret_cast<uintptr_t>(a.dst[q0]) + dst_off) & (kLine - 1))
+                          : 0;
     for (int64_t b0 = 0; b0 < bytes; b0 += step) {
         u32x4 x[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t o = b0 + static_cast<int64_t>(u * nthr + lane) * kVecBytes;
-            if (o < bytes)
+            const int64_t v = b0 + static_cast<int64_t>(u * nthr + lane) * kVecBytes;
+            const int64_t o = v - D < 0 ? v - D + bytes : v - D;
+            if (v < bytes)
                 x[u] = ld16_agent(ring, o);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const uint32_t off = static_cast<uint32_t>(u * nthr + lane) * kVecBytes;
-            const int64_t o = b0 + off;
-            if (o + kVecBytes <= bytes) {
+            const int64_t v = b0 + static_cast<int64_t>(u * nthr + lane) * kVecBytes;
+            const int64_t o = v - D < 0 ? v - D + bytes : v - D;
+            if (v >= bytes) {
+                // past the piece: owned by no lane
+            } else if (o + kVecBytes <= bytes) {
                 for (int q = q0; q < q1; ++q)
-                    st16(static_cast<char*>(a.dst[q]) + dst_off + b0, off, x[u], nt);
-            } else if (o < bytes) {
+                    st16(static_cast<char*>(a.dst[q]) + dst_off, static_cast<uint32_t>(o), x[u], nt);
+            } else {
+                // the segment's last, partial vector (only when D = 0)
                 for (int q = q0; q < q1; ++q) {
                     uint16_t* d = reinterpret_cast<uint16_t*>(static_cast<char*>(a.dst[q]) + dst_off + o);
                     for (int h = 0; h < (bytes - o) / 2; ++h)
