@@ -90,6 +90,10 @@ def parse():
                          "per-task device-clock stamps (AllGather 8 x 64 MiB and 8 x 1 GiB at each "
                          "chunk size and lead, composed AllReduce, Zipf RSV/AGV, 8 KiB calls); one "
                          "JSON line per run")
+    ap.add_argument("--snac-sweep", action="store_true",
+                    help="instead of the step: staged-path launch choices (chunk x lead x piece) "
+                         "for the AllGather 8 x 64 MiB, composed AllReduce 8 x 256 MiB, Zipf RSV/AGV, "
+                         "and the AllGather 8 x 1 GiB (chunk x lead), cold; one JSON line per point")
     ap.add_argument("--xcd-order", action="store_true",
                     help="zero-staging kernels give each XCD one contiguous range of tiles")
     ap.add_argument("--no-snac", dest="snac", action="store_false",
@@ -123,6 +127,9 @@ def main():
         return
     if args.snac_trace:
         snac_trace(A, synth, torch, dev)
+        return
+    if args.snac_sweep:
+        snac_sweep(A, synth, torch, dev)
         return
 
     def up(a):
@@ -709,6 +716,81 @@ def snac_trace(A, synth, torch, dev):
         run(f"ag_8x1GiB_chunk{chunk >> 10}K", li, lo, A.OP_COPY, reps=3, chunk_bytes=chunk)
 
 
+def snac_sweep(A, synth, torch, dev):
+    """Launch choices of the staged path, cold (a 1 GiB copy between calls;
+    median of event-timed calls): for each chunk size (512 KiB, 1 MiB,
+    2 MiB, the ring kept at 32 MiB), leads of D, D/2, D/4 and D/8 chunks and
+    pieces of 64, 128 and 256 KiB, on the AllGather of 8 x 64 MiB, the
+    composed AllReduce and the Zipf(0.125) ReduceScatterV of 8 x 256 MiB and
+    the Zipf AllGatherV of 512 MiB; then the AllGather of 8 x 1 GiB at each
+    chunk size and leads D, D/2, D/4 (default piece)."""
+    P, MiB = 8, 1 << 20
+    L = A.layout
+    scrub_a = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev)
+    scrub_b = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev)
+
+    def timed(fn, reps):
+        ts = []
+        for _ in range(reps):
+            scrub_b.copy_(scrub_a)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    def point(name, li, lo, op, reps, **kw):
+        cfg = A.config(flags=A.F_STAGED, **kw)
+        st, info = A.atom_plan_query(li, lo, op, cfg)
+        assert st == A.OK, (name, kw, st)
+        fn = lambda: A.atom_collective(li, lo, op, cfg)
+        fn()
+        ms = timed(fn, reps)
+        assert A.atom_sync_status() == A.OK, name
+        print(json.dumps({"snac_sweep": name, "chunk_bytes": int(info.chunk_bytes),
+                          "lead": int(info.snac_lead), "ring_slots": int(info.ring_slots),
+                          "piece_bytes": kw.get("piece_bytes", 0), "workgroups": int(info.num_wgs),
+                          "ms": round(ms, 4), "GBps": round(info.credited_bytes / ms / 1e6, 1)}), flush=True)
+
+    def grid(name, li, lo, op, reps):
+        for chunk in (512 << 10, 1 << 20, 2 << 20):
+            D = max(4, min(64, (32 << 20) // chunk))
+            for lead in (D, D // 2, D // 4, D // 8):
+                for piece in (64 << 10, 128 << 10, 256 << 10):
+                    point(name, li, lo, op, reps, chunk_bytes=chunk, snac_lead=lead, piece_bytes=piece)
+
+    S = 64 * MiB
+    z = [torch.empty(S // 2, dtype=torch.bfloat16, device=dev).uniform_(-1, 1) for _ in range(P)]
+    o = [torch.empty(P * S // 2, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+    grid("ag_8x64MiB", L(A.SHARD, z, S // 2), L(A.GATHERED, o, S // 2), A.OP_COPY, 7)
+    del z, o
+    N2 = 1 << 27
+    x = [torch.randn(N2, device=dev).to(torch.bfloat16) for _ in range(P)]
+    ar = [torch.empty(N2, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+    grid("ar_8x256MiB", L(A.PARTITIONED, x, N2 // P), L(A.GATHERED, ar, N2 // P), A.OP_SUM, 5)
+    del ar
+    cnt = synth.zipf_partition(N2, P, 0.125, 8) // 8
+    ys = [torch.empty(int(c) * 8, dtype=torch.bfloat16, device=dev) for c in cnt]
+    grid("rsv_zipf_8x256MiB", L(A.PARTITIONED, x, 0, cnt, 8), L(A.SHARD, ys, 0, None, 8), A.OP_SUM, 5)
+    del ys, x
+    T = P * 64 * MiB // 2
+    cnt = synth.zipf_partition(T, P, 0.125, 8) // 8
+    zv = [torch.empty(int(c) * 8, dtype=torch.bfloat16, device=dev).uniform_(-1, 1) for c in cnt]
+    ov = [torch.empty(T, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+    grid("agv_zipf_512MiB", L(A.SHARD, zv, 0, cnt, 8), L(A.GATHERED, ov, 0, None, 8), A.OP_COPY, 7)
+    del zv, ov
+    S = 1024 * MiB
+    z = [torch.empty(S // 2, dtype=torch.bfloat16, device=dev).uniform_(-1, 1) for _ in range(P)]
+    o = [torch.empty(P * S // 2, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+    for chunk in (512 << 10, 1 << 20, 2 << 20):
+        D = max(4, min(64, (32 << 20) // chunk))
+        for lead in (D, D // 2, D // 4):
+            point("ag_8x1GiB", L(A.SHARD, z, S // 2), L(A.GATHERED, o, S // 2), A.OP_COPY, 3,
+                  chunk_bytes=chunk, snac_lead=lead)
+
+
 def sweep(A, synth, torch, dev):
     """Message-size sweeps of the pages' collective benchmarks (one JSON line
     per point): AllGather of 8 partitions from 8 KiB to 1 GiB each, zero
@@ -939,8 +1021,10 @@ def ceilings(torch, dev):
 
 def measured_traffic(row):
     """HBM bytes per launch of `row` from the committed rocprofv3 counter
-    summary (FETCH_SIZE and WRITE_SIZE, scaled by the copy calibration), or
-    None when the summary is missing or any kernel source changed since."""
+    summary (bytes leaving the L2s, from the TCC_EA0 read and write request
+    counters by request size; the 256 MiB copy reads 1.0001x its bytes with
+    no calibration), or None when the summary is missing or any kernel
+    source changed since."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:

@@ -175,7 +175,7 @@ typedef struct atom_config {
     uint32_t jitter_seed;
     int32_t snac_lead;         /* SNAC ticket order: chunks staged ahead of
                                   the first consumer, 0..64, clamped to the
-                                  ring depth (0: the ring depth). Smaller
+                                  ring depth (0: half the ring depth). Smaller
                                   leads leave slack
                                   slots so a producer seldom waits for a
                                   slot to be freed. */

@@ -665,16 +665,15 @@ atom_status build_snac(Plan* p, int32_t sk, int P, void* const* ins, void* const
         return ATOM_ERR_LIMIT;
     }
     // Lead (chunks staged before the first consumer in the ticket order):
-    // the caller's, else the ring depth for a copying stage and half of it
-    // for a reducing one. A reducing producer reads P inputs per staged byte
-    // and is the long task, so with the full depth it waits for the slot's
-    // consumers claimed just before it; half the depth leaves those slots
-    // free. Measured on MI355X (cold, per-task clock stamps and a sweep of
-    // leads D..D/8): the Zipf ReduceScatterV of 8 x 256 MiB 0.570 -> 0.486
-    // ms, the composed AllReduce 0.818 -> 0.811 ms; the copying stages are
-    // within 1-2 % of their best at the full depth (AllGatherV 5 % better
-    // there than at a quarter).
-    a.lead = c.lead ? std::min(c.lead, a.slots) : (reduce ? std::max(1, a.slots / 2) : a.slots);
+    // the caller's, else half the ring depth. With the full depth a
+    // producer waits for the consumers of its slot, claimed just before it
+    // (per-task clock stamps on MI355X: 21-37 % of all workgroup time); half
+    // the depth leaves those slots free. Measured cold on MI355X over leads
+    // D..D/8: the Zipf ReduceScatterV of 8 x 256 MiB (a reducing producer is
+    // the long task) 0.547-0.570 -> 0.486-0.495 ms, the composed AllReduce
+    // 0.818 -> 0.811 ms, the AllGather of 8 x 1 GiB 14.95 -> 14.42 ms; the
+    // other copying rows moved by -2..+2 % between runs.
+    a.lead = c.lead ? std::min(c.lead, a.slots) : std::max(1, a.slots / 2);
     a.trace = c.trace;
     a.nchunks = q;
     a.ntasks = 2 * a.nchunks * a.pieces;

@@ -526,7 +526,7 @@ def test_snac_lead_and_task_count():
     cfg = A.config(flags=A.F_STAGED, chunk_bytes=512 << 10, piece_bytes=64 << 10, ring_slots=16)
     st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=8, ins=ins, outs=outs, n=(8 << 20) // 2, cfg=cfg)
     assert st == A.OK and info.staged == 1
-    assert info.snac_lead == 16
+    assert info.snac_lead == 8
     assert info.snac_tasks == 2 * info.num_chunks * 8
     cfg.snac_lead = 4
     st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=8, ins=ins, outs=outs, n=(8 << 20) // 2, cfg=cfg)
@@ -543,7 +543,7 @@ def test_snac_lead_and_task_count():
 
 
 def test_snac_default_lead_by_stage():
-    """A copying stage leads by the ring depth, a reducing one by half of it."""
+    """Every stage leads by half the ring depth (at least one chunk)."""
     P, n = 8, 1 << 20
     ins = fake(P, P * n * 2)
     outs = fake(P, P * n * 2, start=BASE + (1 << 36))
@@ -553,7 +553,7 @@ def test_snac_default_lead_by_stage():
     st, info = Q(A.PARTITIONED, A.SHARD, A.OP_SUM, P=P, n=n, ins=ins, outs=outs, cfg=cfg)
     assert st == A.OK and info.snac_lead == 8
     st, info = Q(A.PARTITIONED, A.TRANSPOSED, A.OP_COPY, P=P, n=n, ins=ins, outs=outs, cfg=cfg)
-    assert st == A.OK and info.snac_lead == 16
+    assert st == A.OK and info.snac_lead == 8
     cfg = A.config(flags=A.F_STAGED, chunk_bytes=2 << 20, ring_slots=1)
     st, info = Q(A.PARTITIONED, A.GATHERED, A.OP_SUM, P=P, n=n, ins=ins, outs=outs, cfg=cfg)
     assert st == A.OK and info.snac_lead == 1
