@@ -478,28 +478,43 @@ def main():
 def study(A, synth, torch, dev):
     """Atom copy of 256 MiB (a one-rank AllGather, so the launch shape can be
     set): GB/s against workgroups launched (CUs used = min(WGs, 256)) and
-    against pipeline depth (16-byte slots in flight per lane), the one-GPU
+    against pipeline depth (16-byte slots in flight per lane) at every grid
+    from 8 workgroups to the full one-tile-per-workgroup grid, the one-GPU
     counterparts of the pages' SM-count and pipeline-depth studies
     (Figures 3 and 11); then GB/s against workgroups for the 8-way reduce
-    and the 1 -> 8 fan-out."""
+    and the 1 -> 8 fan-out. Cold: a 1 GiB streaming fill of another buffer
+    (libatom_ceiling.so) precedes every timed call, so neither the caches
+    nor the memory-side cache hold the call's data; median of 7 calls."""
+    import ctypes
+    clib = ctypes.CDLL(os.path.join(ROOT, "reduce_atom_03_amd", "libatom_ceiling.so"))
+    clib.ceil_fill.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    stream = torch.cuda.current_stream()
+    sp = int(stream.cuda_stream)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def cold_ms(fn, reps=7):
+        t = []
+        for _ in range(reps):
+            if clib.ceil_fill(flush.data_ptr(), 1 << 30, 256, 4, sp) != 0:
+                raise RuntimeError("ceiling fill kernel failed")
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            t.append(e0.elapsed_time(e1))
+        return float(np.median(t))
+
     n = 1 << 27
     src = torch.from_numpy(synth.draw(2, 0, n, "normal", synth.BF16).view(np.int16)).view(
         torch.bfloat16).to(dev)
     dst = torch.empty(n, dtype=torch.bfloat16, device=dev)
     lin, lout = A.layout(A.SHARD, [src], n), A.layout(A.GATHERED, [dst], n)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     def point(wgs, stages):
         cfg = A.config(num_wgs=wgs, stages=stages)
-        for _ in range(3):
-            A.atom_collective(lin, lout, A.OP_COPY, cfg)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(10):
-            A.atom_collective(lin, lout, A.OP_COPY, cfg)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / 10
+        A.atom_collective(lin, lout, A.OP_COPY, cfg)
+        ms = cold_ms(lambda: A.atom_collective(lin, lout, A.OP_COPY, cfg))
         st, info = A.atom_plan_query(lin, lout, A.OP_COPY, cfg)
         gbs = 4 * n / ms / 1e6
         print(json.dumps({"study": "atom_copy_256MiB", "workgroups": info.num_wgs,
@@ -509,7 +524,7 @@ def study(A, synth, torch, dev):
 
     for wgs in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 0):
         point(wgs, 4)
-    for wgs in (8, 16, 256, 0):
+    for wgs in (8, 16, 64, 256, 1024, 4096, 16384, 65536, 0):
         for stages in (1, 2, 4, 8):
             point(wgs, stages)
 
@@ -531,15 +546,8 @@ def study(A, synth, torch, dev):
     for name, (li, lo, op, nbytes) in shapes.items():
         for wgs in (8, 16, 32, 64, 128, 256, 512, 1024, 4096, 0):
             cfg = A.config(num_wgs=wgs)
-            for _ in range(2):
-                A.atom_collective(li, lo, op, cfg)
-            torch.cuda.synchronize()
-            e0.record()
-            for _ in range(5):
-                A.atom_collective(li, lo, op, cfg)
-            e1.record()
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / 5
+            A.atom_collective(li, lo, op, cfg)
+            ms = cold_ms(lambda: A.atom_collective(li, lo, op, cfg), reps=5)
             st, info = A.atom_plan_query(li, lo, op, cfg)
             gbs = nbytes / ms / 1e6
             print(json.dumps({"study": name, "workgroups": info.num_wgs,
