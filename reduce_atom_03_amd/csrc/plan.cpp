@@ -613,14 +613,21 @@ atom_status build_snac(Plan* p, int32_t sk, int P, void* const* ins, void* const
     // 512 KiB - 2 MiB range of Table 3's bandwidth-delay rule).
     int64_t chunk = c.chunk_set ? c.chunk : (reduce ? kDefaultChunkAllReduce : kDefaultChunkAllGather);
     // Piece (the task granule): the caller's, else the largest power of two
-    // from 8 KiB to 64 KiB that still gives about one persistent grid's
-    // worth of staging tasks (total / piece >= 2 * 512), so a medium message
-    // is spread over many workgroups instead of a few (smaller pieces cost
-    // more in hand-offs than they gain).
+    // from 8 KiB to 64 KiB (32 KiB for a copying stage) that still gives
+    // about one persistent grid's worth of staging tasks (total / piece >=
+    // 2 * 512), so a medium message is spread over many workgroups instead
+    // of a few (smaller pieces cost more in hand-offs than they gain).
+    // Measured cold on MI355X with 512 lanes and the half-depth lead: the
+    // staged AllGather of 8 x 64 MiB 0.964 ms with 64 KiB pieces, 0.922-0.925
+    // with 32 KiB (16 KiB: 1.00), of 8 x 1 GiB 14.46 -> 13.73 ms; the
+    // composed AllReduce and the ReduceScatterV keep 64 KiB (32 KiB 1-3 %
+    // slower: a reducing piece reads P inputs, so it is already P times the
+    // work).
     int64_t piece = c.piece;
     if (!piece) {
+        const int64_t top = reduce ? kPieceBytes : kCopyPieceBytes;
         piece = kMinAutoPiece;
-        while (piece < kPieceBytes && total / (2 * piece) >= kSnacGrid)
+        while (piece < top && total / (2 * piece) >= kSnacGrid)
             piece *= 2;
     }
     piece = std::min(piece, chunk);

@@ -58,7 +58,8 @@ constexpr int64_t kMinChunk = 64 << 10;
 constexpr int64_t kMaxChunk = 16 << 20;
 constexpr int32_t kDefaultSlots = 4;
 constexpr int32_t kMaxSlots = 64;
-constexpr int64_t kPieceBytes = 64 << 10;            // SNAC task granule
+constexpr int64_t kPieceBytes = 64 << 10;            // SNAC task granule, reducing stage
+constexpr int64_t kCopyPieceBytes = 32 << 10;        // SNAC task granule, copying stage
 constexpr int64_t kMinAutoPiece = 8 << 10;           // smallest granule chosen for small partitions
 constexpr int64_t kSnacInflightBytes = 32 << 20;     // default ring: one on-chip BDP
 constexpr int64_t kSnacGrid = 512;                   // persistent SNAC workgroups (2 per CU)

@@ -362,9 +362,10 @@ def test_binding_maps_one_hip_runtime():
 
 def test_snac_piece_spreads_medium_messages():
     """Without piece_bytes the task granule is the largest power of two in
-    [8 KiB, 64 KiB] with P * S / piece >= 512 staging tasks."""
+    [8 KiB, 32 KiB] (a copying stage; 64 KiB for a reducing one) with
+    P * S / piece >= 512 staging tasks."""
     for S, piece in ((64 << 10, 8 << 10), (512 << 10, 8 << 10), (2 * MiB, 32 << 10),
-                     (4 * MiB, 64 << 10), (64 * MiB, 64 << 10)):
+                     (4 * MiB, 32 << 10), (64 * MiB, 32 << 10)):
         st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=8, n=S // 2,
                      cfg=A.config(flags=A.F_STAGED, chunk_bytes=16 * MiB), ins=fake(8, S),
                      outs=fake(8, 8 * S, start=BASE + (1 << 40)))
@@ -376,12 +377,28 @@ def test_snac_piece_spreads_medium_messages():
         assert info.num_wgs == min(512, tasks), (S, info.num_wgs, tasks)
 
 
+def test_snac_piece_of_a_reducing_stage():
+    """A reducing stage's granule goes up to 64 KiB."""
+    P = 8
+    for S, piece in ((512 << 10, 8 << 10), (8 * MiB, 16 << 10), (64 * MiB, 64 << 10), (256 * MiB, 64 << 10)):
+        n = S // 2 // P
+        st, info = Q(A.PARTITIONED, A.GATHERED, A.OP_SUM, P=P, n=n,
+                     cfg=A.config(flags=A.F_STAGED, chunk_bytes=16 * MiB), ins=fake(P, S),
+                     outs=fake(P, S, start=BASE + (1 << 40)))
+        assert st == A.OK and info.staged == 1
+        per_rank = n * 2
+        want_chunk = 16 * MiB if per_rank >= 16 * MiB else -(-per_rank // piece) * piece
+        assert info.chunk_bytes == want_chunk, (S, info.chunk_bytes)
+        assert info.snac_tasks == 2 * info.num_chunks * (want_chunk // piece), (S, info.snac_tasks)
+
+
 def test_snac_grid_follows_the_ring_window():
     """Without num_wgs the staged launch uses one workgroup per piece the ring
     can hold (slots * chunk / piece), at most 512; num_wgs overrides it."""
     S = 64 * MiB
-    for chunk, slots, piece, want in ((512 << 10, 0, 0, 512), (64 << 10, 0, 0, 64),
-                                      (256 << 10, 0, 0, 256), (512 << 10, 8, 0, 64),
+    # (default pieces of a copying stage: 32 KiB)
+    for chunk, slots, piece, want in ((512 << 10, 0, 0, 512), (64 << 10, 0, 0, 128),
+                                      (256 << 10, 0, 0, 512), (512 << 10, 8, 0, 128),
                                       (2 * MiB, 8, 32 << 10, 512), (1 * MiB, 4, 16 << 10, 256)):
         cfg = A.config(flags=A.F_STAGED, chunk_bytes=chunk, ring_slots=slots, piece_bytes=piece)
         st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=8, n=S // 2, cfg=cfg, ins=fake(8, S),
