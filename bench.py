@@ -30,8 +30,9 @@ output element written once, a reduced element counted with its P reads)
 over the step time, in GB/s. Per-collective GB/s and fraction of the 8 TB/s
 HBM peak (from the median of the row's event-timed samples; samples above
 1.5x the median are counted as outliers), the 8 KiB AllGather p50/p99
-latency (an event pair around each launch), its time per call back to back
-and in a HIP graph, and the dominant kernel's roofline are reported
+latency (an event pair around each launch), zero-staging and staged, their
+time per call back to back, the zero-staging one's in a HIP graph, and the
+dominant kernel's roofline are reported
 alongside; the CPU oracle is timed on the same step as a baseline, and on
 the P = 4 ReduceScatter alone.
 
@@ -304,6 +305,18 @@ def main():
         b.record(stream)
     torch.cuda.synchronize()
     lat = np.array([a.elapsed_time(b) * 1e3 for a, b in pairs])
+    # The same 8 KiB AllGather through SNAC (the staged path's latency).
+    snac8 = lambda l=lay8: A.atom_collective(l[0], l[1], A.OP_COPY, snac_cfg)
+    snac8()
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.lat_iters)]
+    for a, b in pairs:
+        a.record(stream)
+        snac8()
+        b.record(stream)
+    torch.cuda.synchronize()
+    assert A.atom_sync_status() == A.OK
+    lat_snac = np.array([a.elapsed_time(b) * 1e3 for a, b in pairs])
     # Decode AllReduce latency per batch size (event pairs, as above).
     dec_lat = {}
     for b in (1, 2, 4, 8, 16):
@@ -396,7 +409,7 @@ def main():
             v.append(a.elapsed_time(b) * 1e3 / n)
         return round(float(np.median(v)), 2)
 
-    b2b = {"ag_8KiB": back_to_back_us(ag8),
+    b2b = {"ag_8KiB": back_to_back_us(ag8), "ag_8KiB_snac": back_to_back_us(snac8),
            "copy_16B": back_to_back_us(lambda: A.atom_copy(tiny_dst, tiny_src, 16))}
     for b in (1, 2, 4, 8, 16):
         lay = (L(A.PARTITIONED, x5[b], b * 896), L(A.GATHERED, o5[b], b * 896))
@@ -454,6 +467,8 @@ def main():
         "a2a_frac": per_row["a2av"]["frac_hbm"],
         "p50_us_8KiB": round(float(np.percentile(lat, 50)), 2),
         "p99_us_8KiB": round(float(np.percentile(lat, 99)), 2),
+        "p50_us_8KiB_snac": round(float(np.percentile(lat_snac, 50)), 2),
+        "p99_us_8KiB_snac": round(float(np.percentile(lat_snac, 99)), 2),
         "host_us_per_call_8KiB": round(host_us, 2),
         "graph_us_per_call_8KiB": round(graph_us, 2),
         "back_to_back_us_per_call": b2b,

@@ -438,10 +438,17 @@ __global__ __launch_bounds__(MAXT) void k_snac(const SnacArgs a)
     __shared__ int s_ok;
     const long long t_begin = wall_clock64();
     const int64_t C = a.chunk_bytes;
-    if (threadIdx.x == 0)
+    // A small call with one workgroup per task (static_tasks) runs task
+    // blockIdx.x and no ticket: the grid is dispatched in index order and
+    // fits the chip at once, so every task's producers (smaller indices)
+    // are running or done. Otherwise tasks are claimed from the ticket.
+    const bool fixed = a.static_tasks != 0;
+    if (!fixed && threadIdx.x == 0)
         s_ticket = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    int64_t t = static_cast<unsigned int>(__builtin_amdgcn_readfirstlane(static_cast<int>(s_ticket)));
+    if (!fixed)
+        __syncthreads();
+    int64_t t = fixed ? static_cast<int64_t>(blockIdx.x)
+                      : static_cast<unsigned int>(__builtin_amdgcn_readfirstlane(static_cast<int>(s_ticket)));
     unsigned long long* const tr = a.trace;
     long long t_claim = tr ? wall_clock64() : 0;
     while (t < a.ntasks) {
@@ -507,10 +514,12 @@ __global__ __launch_bounds__(MAXT) void k_snac(const SnacArgs a)
             }
             if (ok)
                 flag_add_relaxed((task.produce ? a.ready : a.freed) + slot * kFlagStride, 1ull);
-            s_ticket = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (!fixed)
+                s_ticket = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
-        t = static_cast<unsigned int>(__builtin_amdgcn_readfirstlane(static_cast<int>(s_ticket)));
+        t = fixed ? a.ntasks
+                  : static_cast<unsigned int>(__builtin_amdgcn_readfirstlane(static_cast<int>(s_ticket)));
         if (tr)
             t_claim = wall_clock64();
     }

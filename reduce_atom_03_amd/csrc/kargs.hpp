@@ -165,6 +165,8 @@ struct SnacArgs {
                                        // producer seldom waits for a slot)
     int32_t dtype;                     // for the reducing stage
     int32_t nt_store;
+    int32_t static_tasks;              // 1: one workgroup per task, task = blockIdx.x
+                                       // (small calls); 0: tasks claimed by ticket
     int32_t interleave;                // 1: every segment has the same number of
                                        // chunks and chunk q belongs to segment
                                        // q % nseg (sources staged side by side);

@@ -712,6 +712,13 @@ atom_status build_snac(Plan* p, int32_t sk, int P, void* const* ins, void* const
     const int64_t window = static_cast<int64_t>(a.slots) * a.pieces;
     p->grid = std::max<int64_t>(
         1, std::min<int64_t>(a.ntasks, c.num_wgs ? c.num_wgs : std::min(kSnacGrid, window)));
+    // Small calls (at most kSnacStaticTasks tasks, one workgroup each, no
+    // caller grid) skip the ticket: workgroup b runs task b. Dispatch in
+    // index order puts every task's producers (smaller tickets) on the chip
+    // first, and a grid this small fits the chip at once; the waits stay
+    // bounded either way. Saves the ticket atomic's round trip before the
+    // first task and after the last.
+    a.static_tasks = (!c.num_wgs && p->grid == a.ntasks && a.ntasks <= kSnacStaticTasks) ? 1 : 0;
     p->exec = reduce ? EX_SNAC_REDUCE : EX_SNAC_COPY;
     return ATOM_OK;
 }
