@@ -310,3 +310,31 @@ def test_timeout_is_reported_and_only_its_call_is_incomplete(A):
     for j in range(P):
         assert_bits_equal(from_dev(outs2[j]), want, f"call after the timeout out_{j}",
                           nan_by_class=False)
+
+
+@pytest.mark.parametrize("coll,n", [("ag", 4096), ("ar", 512), ("ag", 32768), ("rs", 4096),
+                                    ("a2av", 1200), ("rsv", 3000)])
+@pytest.mark.parametrize("slots", [1, 2, 64])
+def test_small_calls_without_ticket(A, coll, n, slots):
+    """Small staged calls (at most 256 tasks, one workgroup each: the default
+    64-slot ring) run task blockIdx.x with no ticket; rings of 1 and 2 slots
+    hold fewer pieces than there are tasks, so the same calls there run
+    fewer workgroups on the ticket. Each is checked at natural timing and
+    with every notify and consume delayed by a pseudo-random 0-40 us, bit for
+    bit against the oracle, twice in a row."""
+    P = 8
+    c = Case(A, coll, P, n, synth.BF16, 0, seed=40 + slots)
+    base = dict(flags=A.F_STAGED, ring_slots=slots)
+    info = c.plan(A.config(**base))
+    say(f"small {coll} n={n} slots={slots} tasks={info.snac_tasks} wgs={info.num_wgs}")
+    assert 0 < info.snac_tasks <= 256
+    if slots < 64:
+        assert info.num_wgs < info.snac_tasks          # the ticket
+    elif coll != "a2av":
+        assert info.num_wgs == info.snac_tasks         # one workgroup per task, no ticket
+    for jit in (0, 40):
+        for rep in range(2):
+            cfg = A.config(**base, jitter_us=jit, jitter_seed=7 + rep)
+            c.run(cfg)
+            _check_status(A, f"small {coll} jitter={jit}")
+            c.check(f"small {coll} n={n} slots={slots} jitter={jit} rep={rep}")
