@@ -302,11 +302,12 @@ struct StageReduce {
 // destination starts D bytes past a line (D a multiple of 16, taken from the
 // first destination; every destination of an AllGather segment sits at the
 // same offset when the outputs share their alignment), and when the piece is
-// a whole number of lines, vector v of the loop takes piece byte
-// (16 v - D) mod bytes. Each wave's 64 stores then fill whole lines (the
-// first D / 16 vectors write the piece's last D bytes, which end on a line),
-// instead of every wave straddling one more line than it fills; the ring
-// loads take the offset instead, one line in eight. Measured on MI355X: the
+// a whole number of 16-byte vectors (and longer than D), vector v of the
+// loop takes piece byte (16 v - D) mod bytes, a rotation of the vectors.
+// Each wave's 64 stores then fill whole lines (the first D / 16 vectors
+// write the piece's last D bytes), instead of every wave straddling one more
+// line than it fills; the ring loads take the offset instead, one line in
+// eight. Measured on MI355X: the
 // staged AllGatherV of 512 MiB in Zipf(0.125) partitions (segments at
 // 16-byte offsets) 1.00 -> 0.90 ms, the time of the uniform AllGather.
 template <int U>
@@ -321,9 +322,11 @@ __device__ __forceinline__ void consume_vec(const SnacArgs& a, const SegGeo& g, 
     const int q1 = g.dst < 0 ? a.P : g.dst + 1;
     const int64_t step = static_cast<int64_t>(nthr) * U * kVecBytes;
     constexpr int64_t kLine = 128;
-    const int64_t D = bytes % kLine == 0
-                          ? static_cast<int64_t>((reinterpret_cast<uintptr_t>(a.dst[q0]) + dst_off) & (kLine - 1))
-                          : 0;
+    int64_t D = bytes % kVecBytes == 0
+                    ? static_cast<int64_t>((reinterpret_cast<uintptr_t>(a.dst[q0]) + dst_off) & (kLine - 1))
+                    : 0;
+    if (D >= bytes)
+        D = 0;
     for (int64_t b0 = 0; b0 < bytes; b0 += step) {
         u32x4 x[U];
 #pragma unroll
@@ -421,6 +424,54 @@ __device__ __forceinline__ void consume_elem(const SnacArgs& a, const SegGeo& g,
     }
 }
 
+// The two ends of a piece whose streams sit off 16-byte alignment: bytes
+// [0, h) and [t0, t0 + tl) of the piece, element by element in one pass
+// (one load round trip for both), staged at `dst` in the ring (as
+// produce_elem) or consumed from `src` (as consume_elem).
+template <typename T, bool REDUCE>
+__device__ __forceinline__ void produce_ends(const SnacArgs& a, const SegGeo& g, int64_t off,
+                                             char* dst, int64_t h, int64_t t0, int64_t tl)
+{
+    using E = typename std::conditional<sizeof(T) == 2, uint16_t, uint32_t>::type;
+    constexpr int64_t es = sizeof(E);
+    const auto ring = ring_rsrc(dst, ceil16(t0 + tl));
+    const int64_t nh = h / es, n = nh + tl / es;
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+        const int64_t b = i < nh ? i * es : t0 + (i - nh) * es;      // byte in the piece
+        E v;
+        if (REDUCE) {
+            const int64_t e = (g.src_off + off + b) / static_cast<int64_t>(sizeof(T));
+            float acc = Elem<T>::load(a.src[0], e);
+            for (int r = 1; r < a.P; ++r)
+                acc = acc + Elem<T>::load(a.src[r], e);
+            if (sizeof(T) == 2)
+                v = static_cast<E>(f32_to_bf16_bits(acc));
+            else
+                v = static_cast<E>(__float_as_uint(acc));
+        } else {
+            v = *reinterpret_cast<const E*>(g.src + off + b);
+        }
+        ring_store(ring, b, v);
+    }
+}
+
+template <typename E>
+__device__ __forceinline__ void consume_ends(const SnacArgs& a, const SegGeo& g, const char* src,
+                                             int64_t dst_off, int64_t h, int64_t t0, int64_t tl)
+{
+    constexpr int64_t es = sizeof(E);
+    const auto ring = ring_rsrc(src, ceil16(t0 + tl));
+    const int q0 = g.dst < 0 ? 0 : g.dst;
+    const int q1 = g.dst < 0 ? a.P : g.dst + 1;
+    const int64_t nh = h / es, n = nh + tl / es;
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+        const int64_t b = i < nh ? i * es : t0 + (i - nh) * es;
+        const E v = ring_load<E>(ring, b);
+        for (int q = q0; q < q1; ++q)
+            *reinterpret_cast<E*>(static_cast<char*>(a.dst[q]) + dst_off + b) = v;
+    }
+}
+
 // The persistent SNAC kernel: UP 16-byte slots per lane in flight while
 // staging, UC while consuming, at most MAXT lanes per workgroup (256, or
 // 512 for the wide launches, so the default keeps its register budget). T is
@@ -460,12 +511,13 @@ __global__ __launch_bounds__(MAXT) void k_snac(const SnacArgs a)
         chunk_of(a, task.chunk, &s, &c);
         const SegGeo g = seg_geo(a, s);
         const bool elem = a.elem[s] != 0;
+        const int d = a.head[s];                   // vector segments: common offset
         const int64_t cbeg = c * C;
         const int64_t clen = (g.bytes - cbeg < C) ? g.bytes - cbeg : C;
         const int64_t pbeg = task.piece * a.piece_bytes;
         int64_t plen = clen - pbeg;
         plen = plen < 0 ? 0 : (plen > a.piece_bytes ? a.piece_bytes : plen);
-        char* slotp = a.ring + slot * C;
+        char* slotp = a.ring + slot * a.slot_bytes;
         // Stage waits for the slot's previous chunk to be consumed; Consume
         // waits for every piece of its chunk to be staged.
         const unsigned long long* wflag = (task.produce ? a.freed : a.ready) + slot * kFlagStride;
@@ -474,19 +526,43 @@ __global__ __launch_bounds__(MAXT) void k_snac(const SnacArgs a)
         const bool ok = wait_at_least(a, wflag, target, t_begin, &s_ok);
         const long long t_wait = tr ? wall_clock64() : 0;
         if (ok) {
-            if (task.produce) {
-                if (elem)
-                    produce_elem<T, REDUCE>(a, g, cbeg + pbeg, slotp + pbeg, plen);
-                else
-                    Stage::template produce<UP>(a, g, cbeg + pbeg, slotp + pbeg, plen);
-            } else {
+            if (!task.produce) {
                 jitter(a, t, 1u);
                 if (a.jitter_ticks > 0)
                     __syncthreads();
-                if (elem)
+            }
+            if (elem) {
+                if (task.produce)
+                    produce_elem<T, REDUCE>(a, g, cbeg + pbeg, slotp + pbeg, plen);
+                else
                     consume_elem<E>(a, g, slotp + pbeg, g.dst_off + cbeg + pbeg, plen);
+            } else if (d == 0) {
+                if (task.produce)
+                    Stage::template produce<UP>(a, g, cbeg + pbeg, slotp + pbeg, plen);
                 else
                     consume_vec<UC>(a, g, slotp + pbeg, g.dst_off + cbeg + pbeg, plen);
+            } else {
+                // Every stream of the segment sits d bytes past a 16-byte
+                // boundary: the piece's first h = 16 - d bytes (to the
+                // boundary) and its last partial vector move element by
+                // element, the body between them as 16-byte vectors. In the
+                // ring the piece starts 112 + d bytes into its place (the slot
+                // padding holds the rest), so the body starts on a 128-byte
+                // line and the stage's stores fill whole lines.
+                char* const rp = slotp + pbeg + 112 + d;
+                const int64_t h = plen < kVecBytes - d ? plen : kVecBytes - d;
+                const int64_t body = (plen - h) & ~int64_t(kVecBytes - 1);
+                const int64_t tail = plen - h - body;
+                const int64_t o = cbeg + pbeg;
+                // (the body's accesses are issued first, then both ends in
+                // one element pass)
+                if (task.produce) {
+                    Stage::template produce<UP>(a, g, o + h, rp + h, body);
+                    produce_ends<T, REDUCE>(a, g, o, rp, h, h + body, tail);
+                } else {
+                    consume_vec<UC>(a, g, rp + h, g.dst_off + o + h, body);
+                    consume_ends<E>(a, g, rp, g.dst_off + o, h, h + body, tail);
+                }
             }
         }
         // Notify: each wave of a producer waits until its write-through
@@ -594,7 +670,10 @@ hipError_t launch_copy_t(const SnacArgs& a, int U, dim3 grid, dim3 block, hipStr
 constexpr int64_t kFlagLine = kFlagStride * sizeof(unsigned long long);
 constexpr int64_t kStaticFlagBytes = 64 << 10;
 static_assert((2 * kMaxSlots + 3) * kFlagLine <= kStaticFlagBytes, "flags do not fit");
-static __device__ __align__(256) char scratch[kStaticFlagBytes + kStaticRingBytes];
+// The ring part also holds each slot's padding (kSlotPad), so that a ring of
+// kStaticRingBytes of chunks fits at any depth up to kMaxSlots.
+constexpr int64_t kStaticRingAlloc = kStaticRingBytes + kMaxSlots * kSlotPad;
+static __device__ __align__(256) char scratch[kStaticFlagBytes + kStaticRingAlloc];
 
 __global__ void k_clear_words(unsigned long long* p, int64_t n)
 {
@@ -640,7 +719,7 @@ atom_status static_workspace(hipStream_t stream, Workspace** out, hipError_t* hi
         ws.ticket = reinterpret_cast<unsigned int*>(ptr + 2 * kMaxSlots * kFlagLine);
         ws.error = reinterpret_cast<unsigned int*>(ptr + (2 * kMaxSlots + 1) * kFlagLine);
         ws.done = reinterpret_cast<unsigned int*>(ptr + (2 * kMaxSlots + 2) * kFlagLine);
-        ws.ring_bytes = kStaticRingBytes;
+        ws.ring_bytes = kStaticRingAlloc;
         ws.ring = ptr + kStaticFlagBytes;
     }
     if (++ws.seq == 0)

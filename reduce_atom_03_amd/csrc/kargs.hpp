@@ -143,6 +143,7 @@ struct SnacArgs {
                                        // task (NULL: off)
     int64_t row_bytes;                 // bytes per counted row
     int64_t chunk_bytes;
+    int64_t slot_bytes;                // ring slot stride: chunk_bytes plus padding
     int64_t piece_bytes;               // chunk_bytes / pieces
     int64_t nchunks;                   // chunks of every segment together
     int64_t ntasks;                    // 2 * nchunks * pieces
@@ -173,9 +174,14 @@ struct SnacArgs {
                                        // 0: segment-major, found in chunk_begin
     int32_t cnt[kMaxSegs];             // rows per segment
     int32_t chunk_begin[kMaxSegs + 1]; // first chunk of each segment (segment-major)
-    uint8_t elem[kMaxSegs];            // 1: the segment has a stream off 16-byte
-                                       // alignment; it is staged and consumed
-                                       // element by element
+    uint8_t elem[kMaxSegs];            // 1: the segment's streams sit at different
+                                       // offsets from 16-byte alignment; it is
+                                       // staged and consumed element by element
+    uint8_t head[kMaxSegs];            // vector segments: the common offset d of its
+                                       // streams from 16-byte alignment (0..15); for
+                                       // d > 0 a piece is staged 112 + d bytes into
+                                       // its ring place, its first 16 - d bytes and
+                                       // its tail element by element
 };
 
 // Expert-parallel MoE routing (three kernels: rank within chunks, per-rank

@@ -63,6 +63,8 @@ constexpr int64_t kCopyPieceBytes = 32 << 10;        // SNAC task granule, copyi
 constexpr int64_t kMinAutoPiece = 8 << 10;           // smallest granule chosen for small partitions
 constexpr int64_t kSnacInflightBytes = 32 << 20;     // default ring: one on-chip BDP
 constexpr int64_t kSnacGrid = 512;                   // persistent SNAC workgroups (2 per CU)
+constexpr int64_t kSlotPad = 256;                    // bytes past each ring slot's chunk (room for a
+                                                     // piece staged 112 + d bytes in, d < 16)
 constexpr int64_t kSnacStaticTasks = 256;            // up to this many tasks: one workgroup each, no ticket
 constexpr int64_t kMaxGrid = 1 << 20;                // a multiple of the XCD count
 constexpr int64_t kXcdCount = 8;                     // XCDs of an MI355X; workgroup w runs on XCD w mod 8

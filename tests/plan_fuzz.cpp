@@ -171,7 +171,12 @@ int main(int argc, char** argv)
             check(p.sa.pieces >= 1 && p.sa.piece_bytes * p.sa.pieces == p.sa.chunk_bytes,
                   "snac pieces", iter);
             check(p.sa.ntasks == 2 * p.sa.nchunks * p.sa.pieces, "snac tasks", iter);
-            check(p.ring_bytes == p.sa.chunk_bytes * p.sa.slots, "snac ring", iter);
+            check(p.sa.slot_bytes == p.sa.chunk_bytes + kSlotPad &&
+                      p.ring_bytes == p.sa.slot_bytes * p.sa.slots, "snac ring", iter);
+            for (int s = 0; s < p.sa.nseg; ++s)
+                check(p.sa.head[s] < kVecBytes && (p.sa.elem[s] == 0 || p.sa.head[s] == 0) &&
+                          p.sa.head[s] % p.esize == 0,
+                      "snac segment offset", iter);
             check(p.wg >= 64 && p.wg <= 512 && p.wg % 64 == 0, "snac wg", iter);
             check(!use_cfg || cfg.lanes == 0 || p.wg == cfg.lanes, "snac lanes", iter);
         }

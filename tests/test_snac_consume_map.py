@@ -1,8 +1,9 @@
 """The staged consumer's line-aligned vector order (CPU only).
 
 A consumer moves one piece of `size` bytes; when the piece is a whole number
-of 128-byte lines and its destination starts D bytes past a line, vector v
-of the loop takes piece byte (16 v - D) mod size (k_snac.hip, consume_vec),
+of 16-byte vectors longer than D, its destination starting D bytes past a
+128-byte line, vector v of the loop takes piece byte (16 v - D) mod size
+(k_snac.hip, consume_vec),
 and lanes whose v lies past the piece store nothing. This model of that
 index arithmetic checks the invariant the kernel relies on: every piece byte
 is stored exactly once, from the same offset in the ring slot, for every
@@ -13,7 +14,9 @@ import pytest
 
 
 def consume_map(size, dst_addr, nthr, U):
-    D = (dst_addr & 127) if size % 128 == 0 else 0
+    D = (dst_addr & 127) if size % 16 == 0 else 0
+    if D >= size:
+        D = 0
     step = nthr * U * 16
     out = {}
     waves = []
@@ -36,7 +39,8 @@ def consume_map(size, dst_addr, nthr, U):
     return D, out, waves
 
 
-@pytest.mark.parametrize("size", [16, 130, 7232, 8192, 40000 - 4 * 8192, 65536, 196608])
+@pytest.mark.parametrize("size", [16, 48, 130, 7232, 8192, 8192 - 16, 40000 - 4 * 8192, 65536,
+                                  65536 - 32, 196608])
 @pytest.mark.parametrize("shape", [(512, 8), (256, 2), (64, 1)])
 def test_every_byte_once(size, shape):
     for dst_addr in range(0, 256, 16):
