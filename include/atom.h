@@ -43,8 +43,9 @@
  *    (each 16-byte store assembled from two source vectors), as long as the
  *    sources of one part (reduce) or the destinations of one segment
  *    (fan-out) agree; staged calls choose per segment, a segment being the
- *    bytes one source sends to one destination; the MoE movement chooses
- *    per call.
+ *    bytes one source sends to one or every destination (vectors when all
+ *    its streams share one offset from 16-byte alignment, with element-wise
+ *    ends); the MoE movement chooses per call.
  *  - Calls that use the per-device workspace (the SNAC staging ring and its
  *    flags) are ordered by their stream; two such calls on different streams
  *    of one device must not overlap in time.
