@@ -574,3 +574,19 @@ def test_snac_default_lead_by_stage():
     cfg = A.config(flags=A.F_STAGED, chunk_bytes=2 << 20, ring_slots=1)
     st, info = Q(A.PARTITIONED, A.GATHERED, A.OP_SUM, P=P, n=n, ins=ins, outs=outs, cfg=cfg)
     assert st == A.OK and info.snac_lead == 1
+
+
+def test_staged_segments_at_a_common_offset_stay_vectorized():
+    """Staged calls: a segment whose streams all sit at one offset from
+    16-byte alignment takes the vector path (element-wise ends); streams at
+    different offsets make the call element-wise."""
+    P, n = 8, 4096
+    st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=P, n=n, cfg=A.config(flags=A.F_STAGED),
+                 ins=fake(P, n * 2, align_off=2), outs=fake(P, P * n * 2, start=BASE + (1 << 36), align_off=2))
+    assert st == A.OK and info.staged == 1 and info.vector_path == 1
+    st, info = Q(A.PARTITIONED, A.GATHERED, A.OP_SUM, P=P, n=n, cfg=A.config(flags=A.F_STAGED),
+                 ins=fake(P, P * n * 2, align_off=6), outs=fake(P, P * n * 2, start=BASE + (1 << 36), align_off=6))
+    assert st == A.OK and info.staged == 1 and info.vector_path == 1
+    st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=P, n=n, cfg=A.config(flags=A.F_STAGED),
+                 ins=fake(P, n * 2, align_off=2), outs=fake(P, P * n * 2, start=BASE + (1 << 36), align_off=4))
+    assert st == A.OK and info.staged == 1 and info.vector_path == 0
