@@ -1,13 +1,13 @@
 """Seeded random launch configurations against the oracle.
 
 Each case draws, from its own seed, one collective (ReduceScatter(V),
-AllGather(V), AllToAll(V), AllReduce, staged AllGather or AllReduce), a rank
+AllGather(V), AllToAll(V), AllReduce, zero-staging or staged), a rank
 count, a length, the dtype, the buffer alignment and a random atom_config
 (lanes, stages, num_wgs, flags; chunk, ring slots and piece for staged
 calls), and compares every output with the oracle: copies bit-exact,
 reductions bitwise (and within 1 bf16 ulp / 1e-6). Guard canaries around
-every output must survive. The MoE cases draw routing shapes and tile
-settings the same way. The draws are fixed by the seeds, so a failure
+every output must survive. The MoE cases draw routing shapes, row lengths,
+buffer offsets and tile settings the same way. The draws are fixed by the seeds, so a failure
 names a reproducible case."""
 
 import numpy as np
@@ -21,7 +21,8 @@ from tests.gpu_util import check_guards, empty_dev, from_dev, out_buffers, requi
 pytestmark = pytest.mark.gpu
 
 GUARD = 24
-KINDS = ["rs", "ar", "ag", "a2a", "rsv", "agv", "a2av", "ag_snac", "ar_snac"]
+KINDS = ["rs", "ar", "ag", "a2a", "rsv", "agv", "a2av",
+         "ag_snac", "ar_snac", "rs_snac", "a2a_snac", "rsv_snac", "agv_snac", "a2av_snac"]
 
 
 @pytest.fixture(scope="module")
@@ -71,31 +72,28 @@ def _length(g, top):
     return int(np.exp(g.uniform(0, np.log(top)))) if g.random() < 0.9 else int(g.integers(0, 3))
 
 
-@pytest.mark.parametrize("case", range(180))
+@pytest.mark.parametrize("case", range(280))
 def test_random_collective(A, case):
     import torch
-    g = np.random.default_rng([911, case])
+    g = np.random.default_rng([913, case])
     kind = KINDS[case % len(KINDS)]
     staged = kind.endswith("_snac")
+    kind = kind[:-5] if staged else kind
     P = int(g.integers(1, 17))
     dtype = synth.BF16 if g.random() < 0.6 else synth.F32
-    es = 2 if dtype == synth.BF16 else 4
     cfg, desc = _config(A, g, staged)
-    # misaligned (element-aligned only) buffers on a third of the
-    # zero-staging cases; staged calls need 16-byte partitions
-    skew = 0 if staged or g.random() < 0.67 else 1
+    # buffers 1-3 elements past a 16-byte boundary (element-aligned only) on
+    # a third of the cases, staged or not; lengths of any size
+    skew = 0 if g.random() < 0.67 else int(g.integers(1, 4))
     seed = 5000 + case
-    if staged:
-        n = max(1, _length(g, 40000) // (16 // es)) * (16 // es)
-    else:
-        n = _length(g, 40000)
-    say(f"random case {case}: {kind} P={P} n={n} {dtype} skew={skew} cfg={desc}")
+    n = _length(g, 40000)
+    say(f"random case {case}: {kind}{' staged' if staged else ''} P={P} n={n} {dtype} skew={skew} cfg={desc}")
     tdt = _tdt(dtype)
 
     def dev(a):
-        return to_dev(a, pad_before=skew)[1] if a.size else empty_dev(1, tdt)
+        return to_dev(a, pad_before=skew)[1] if a.size else empty_dev(1, tdt)[:0]
 
-    if kind in ("rs", "ar", "ar_snac"):
+    if kind in ("rs", "ar"):
         xs = [synth.mixed_bits(seed, r, P * n, dtype, specials=False) for r in range(P)]
         dx = [dev(x) for x in xs]
         if kind == "rs":
@@ -110,7 +108,7 @@ def test_random_collective(A, case):
         for j in range(P):
             _reduced(from_dev(outs[j]), want[j], f"case {case} out_{j}")
         check_guards(fulls, [o.numel() for o in outs], GUARD + skew)
-    elif kind in ("ag", "ag_snac"):
+    elif kind == "ag":
         zs = [synth.mixed_bits(seed, k, n, dtype) for k in range(P)]
         want = oracle.all_gather(zs)
         fulls, outs = out_buffers([P * n] * P, tdt, GUARD + skew)
@@ -179,8 +177,13 @@ def test_random_moe(A, case):
     k = int(g.integers(1, 17))
     T = int(g.integers(0, 300))
     dt = synth.BF16 if g.random() < 0.6 else synth.F32
-    H = int(g.choice([8, 64, 520, 1032])) if dt == synth.BF16 else int(g.choice([4, 36, 260, 1028]))
+    # rows of 16-byte multiples (the 128-bit kernels) and of any length
+    # (element-wise), buffers aligned or 1-3 elements off
+    H = (int(g.choice([8, 64, 520, 1032, 7, 33, 257])) if dt == synth.BF16
+         else int(g.choice([4, 36, 260, 1028, 5, 37])))
     inv = float(g.choice([0.0, 0.05]))
     cut = int(g.integers(0, 4))
+    skew_in = 0 if g.random() < 0.7 else int(g.integers(1, 4))
+    skew_out = 0 if g.random() < 0.7 else int(g.integers(1, 4))
     cfg = A.config(lanes=int(g.choice([0, 64, 128, 256])), stages=int(g.choice([0, 1, 2, 4, 8])))
-    _move_case(A, (6000 + case, P, T, E, k, H, dt, inv, cut), cfg)
+    _move_case(A, (6000 + case, P, T, E, k, H, dt, inv, cut), cfg, skew_in, skew_out)
