@@ -302,6 +302,31 @@ __device__ __forceinline__ u32x4 ld16_stream(__amdgpu_buffer_rsrc_t r, uint32_t 
 // (for sc1 stores: written through to the agent-coherent level).
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Kernel arguments sit in memory written just before the launch, and the
+// scalar loads that read them form chains (a segment's source pointer is
+// read once its index is known, a count once the segment is), each link a
+// scalar-cache miss on a fresh launch. One load from each 64-byte line the
+// first steps read, all issued before anything waits, fills those lines at
+// once, so the chained loads that follow hit. The values are only consumed
+// by an empty asm statement. Measured on MI355X (median kernel durations in
+// a kernel trace): the staged AllGather and AllReduce of 8 x 8 KiB 8.72 ->
+// 8.08 us, the zero-staging AllGather of 8 x 8 KiB 3.44 -> 3.20 us.
+__device__ __forceinline__ void touch_arg_lines(const void* p0, const void* p1, const void* p2,
+                                                const void* p3, const void* p4, const void* p5,
+                                                const void* p6, const void* p7, const void* p8,
+                                                const void* p9)
+{
+    const auto ld = [](const void* p) { return *static_cast<const uint32_t*>(p); };
+    asm volatile("" ::"s"(ld(p0)), "s"(ld(p1)), "s"(ld(p2)), "s"(ld(p3)), "s"(ld(p4)), "s"(ld(p5)),
+                 "s"(ld(p6)), "s"(ld(p7)), "s"(ld(p8)), "s"(ld(p9)));
+}
+
+// The first line of the hidden launch arguments (grid and workgroup sizes).
+__device__ __forceinline__ const void* hidden_args()
+{
+    return (const void*)__builtin_amdgcn_implicitarg_ptr();
+}
+
 __device__ __forceinline__ unsigned long long flag_load_relaxed(const unsigned long long* f)
 {
     return __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -118,6 +118,8 @@ template <int U, bool HEADS, bool GRID>
 __global__ __launch_bounds__(256) void k_copy_vec(const CopyArgs a)
 {
     static_assert(!(HEADS && GRID), "the uniform form has no heads");
+    touch_arg_lines(&a.src[0], &a.src[8], &a.dst[0], &a.dst[8], &a.row_bytes, &a.seg_off[0],
+                    &a.cnt[0], &a.seg_tile_begin[0], &a.head[0], hidden_args());
     const int lane = threadIdx.x;
     const int nthr = blockDim.x;
     const bool nt = a.nt_store != 0;

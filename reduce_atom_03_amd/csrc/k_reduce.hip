@@ -64,6 +64,8 @@ template <typename T, int P, int U, bool GRID>
 __global__ __launch_bounds__(256) void k_reduce_vec(const ReduceArgs a)
 {
     constexpr int VE = kVecBytes / sizeof(T);
+    touch_arg_lines(&a.src[0], &a.src[8], &a.dst[0], &a.dst[8], &a.part_off[0], &a.tile_begin[0],
+                    &a.ntiles, &a.head[0], &a.nsrc, hidden_args());
     const int lane = threadIdx.x;
     const int nthr = blockDim.x;
     const bool nt = a.nt_store != 0;

@@ -487,6 +487,8 @@ __global__ __launch_bounds__(MAXT) void k_snac(const SnacArgs a)
     using E = typename std::conditional<sizeof(T) == 2, uint16_t, uint32_t>::type;
     __shared__ unsigned int s_ticket;
     __shared__ int s_ok;
+    touch_arg_lines(&a.src[0], &a.src[8], &a.dst[0], &a.dst[8], &a.ring, &a.chunk_bytes,
+                    &a.jitter_seed, &a.cnt[4], &a.elem[0], &a.head[0]);
     const long long t_begin = wall_clock64();
     const int64_t C = a.chunk_bytes;
     // A small call with one workgroup per task (static_tasks) runs task
