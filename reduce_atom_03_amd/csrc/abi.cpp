@@ -55,14 +55,14 @@ atom_status workspace(int64_t ring_bytes, hipStream_t stream, Workspace** out)
         return ATOM_ERR_UNSUPPORTED;
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace& ws = g_ws[dev];
-    if (!ws.ready || ws.ring_bytes < ring_bytes) {
+    if (!ws.counts || ws.ring_bytes < ring_bytes) {
         bool cap = false;
         if (atom_status st = capturing(stream, &cap); st != ATOM_OK)
             return st;
         if (cap)
             return ATOM_ERR_UNSUPPORTED;
     }
-    if (!ws.ready) {
+    if (!ws.counts) {
         int khz = 0;
         if (hipError_t e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
             e != hipSuccess)
@@ -70,24 +70,23 @@ atom_status workspace(int64_t ring_bytes, hipStream_t stream, Workspace** out)
         if (khz <= 0)
             return ATOM_ERR_UNSUPPORTED;
         ws.wall_khz = khz;
-        // ready[kMaxSlots], freed[kMaxSlots] (each counter on its own 256-byte
-        // line), then the ticket, the error word and the finished-workgroup
-        // count on lines of their own. All start at zero; every staged
-        // kernel leaves them at zero (the error word excepted).
+        // counts[kMaxSlots] (each slot's count on its own 256-byte line),
+        // then the ticket, the error word and the finished-workgroup count
+        // on lines of their own. All start at zero; every staged kernel
+        // leaves them at zero (the error word excepted).
         char* flags = nullptr;
         const size_t line = kFlagStride * sizeof(unsigned long long);
-        const size_t fbytes = (2 * kMaxSlots + 3) * line;
+        const size_t fbytes = (kMaxSlots + 3) * line;
         if (hipMalloc(&flags, fbytes) != hipSuccess)
             return ATOM_ERR_NOMEM;
         if (hipError_t e = hipMemset(flags, 0, fbytes); e != hipSuccess) {
             (void)hipFree(flags);
             return hip_status(e);
         }
-        ws.ready = reinterpret_cast<unsigned long long*>(flags);
-        ws.freed = ws.ready + kMaxSlots * kFlagStride;
-        ws.ticket = reinterpret_cast<unsigned int*>(flags + 2 * kMaxSlots * line);
-        ws.error = reinterpret_cast<unsigned int*>(flags + (2 * kMaxSlots + 1) * line);
-        ws.done = reinterpret_cast<unsigned int*>(flags + (2 * kMaxSlots + 2) * line);
+        ws.counts = reinterpret_cast<unsigned long long*>(flags);
+        ws.ticket = reinterpret_cast<unsigned int*>(flags + kMaxSlots * line);
+        ws.error = reinterpret_cast<unsigned int*>(flags + (kMaxSlots + 1) * line);
+        ws.done = reinterpret_cast<unsigned int*>(flags + (kMaxSlots + 2) * line);
     }
     if (ws.ring_bytes < ring_bytes) {
         const int64_t want = std::max(ring_bytes, 2 * ws.ring_bytes);

@@ -20,13 +20,17 @@
 //   Stage   a producer workgroup copies (or reduces in rank order) one piece
 //           of a chunk into a slot of the staging ring with agent-coherent
 //           stores;
-//   Notify  once every wave's stores have completed it adds 1 to the
-//           slot's `ready` counter;
-//   Consume a consumer workgroup waits for `ready` == all pieces of the
-//           chunk, reads one piece from the slot with agent-coherent loads,
-//           writes it to its destination(s) and adds 1 to the slot's `freed`
-//           counter, which the producer of the chunk D places later waits
-//           for before reuse.
+//   Notify  once every wave's stores have completed it counts one piece
+//           staged in the slot's count word;
+//   Consume a consumer workgroup waits until the word counts all pieces of
+//           the chunk staged, reads one piece from the slot with
+//           agent-coherent loads, writes it to its destination(s) and counts
+//           one piece consumed in the same word, which the producer of the
+//           chunk D places later waits for before reuse.
+// A slot's word holds both counts (staged in the low 32 bits, consumed in
+// the high 32 bits) over every chunk the slot holds in the call, so the
+// task that brings both to their final values knows that no other task of
+// the call will touch the word again.
 // The ring is never touched by ordinary (L2-cached) accesses, so no task
 // needs an L2 write-back or invalidation.
 //
@@ -57,6 +61,10 @@
 namespace atom {
 
 namespace {
+
+// A slot word counts staged pieces in its low 32 bits and consumed pieces
+// in its high 32 bits.
+constexpr unsigned long long kConsumedOne = 1ull << 32;
 
 struct Task {
     bool produce;
@@ -157,7 +165,8 @@ __device__ __forceinline__ void chunk_of(const SnacArgs& a, int64_t q, int* s, i
     *c = q - a.chunk_begin[lo];
 }
 
-// Lane 0 waits until *flag >= target, bounded in wall-clock time (the
+// Lane 0 waits until the count in the word (the low 32 bits, or the high 32
+// bits when `consumed`) is at least target, bounded in wall-clock time (the
 // per-wait bound and the workgroup's whole-kernel budget, both in ticks of
 // the constant-rate device clock). The barrier then holds every wave until
 // the count was seen, so the waves' ring loads are issued after it. The
@@ -165,8 +174,8 @@ __device__ __forceinline__ void chunk_of(const SnacArgs& a, int64_t q, int* s, i
 // uniform. Returns false when the wait gave up (a timeout here, or earlier
 // in the same call).
 __device__ __forceinline__ bool wait_at_least(const SnacArgs& a, const unsigned long long* flag,
-                                              unsigned long long target, long long t_begin,
-                                              int* s_ok)
+                                              bool consumed, unsigned long long target,
+                                              long long t_begin, int* s_ok)
 {
     // A count of zero is always met (a slot's first use): no flag load, no
     // barrier. `target` is wave-uniform, so this is a uniform branch.
@@ -174,10 +183,12 @@ __device__ __forceinline__ bool wait_at_least(const SnacArgs& a, const unsigned 
         return true;
     if (threadIdx.x == 0) {
         int ok = 1;
-        if (flag_load_relaxed(flag) < target) {
+        const int sh = consumed ? 32 : 0;
+        const auto count = [&] { return (flag_load_relaxed(flag) >> sh) & 0xFFFFFFFFull; };
+        if (count() < target) {
             const long long w0 = wall_clock64();
             unsigned int it = 0;
-            while (flag_load_relaxed(flag) < target) {
+            while (count() < target) {
                 // Back off: waiting workgroups poll one counter line, and a
                 // poll that misses costs the producers memory bandwidth.
                 if (it < 8)
@@ -522,10 +533,10 @@ __global__ __launch_bounds__(MAXT) void k_snac(const SnacArgs a)
         char* slotp = a.ring + slot * a.slot_bytes;
         // Stage waits for the slot's previous chunk to be consumed; Consume
         // waits for every piece of its chunk to be staged.
-        const unsigned long long* wflag = (task.produce ? a.freed : a.ready) + slot * kFlagStride;
+        unsigned long long* const word = a.counts + slot * kFlagStride;
         const unsigned long long target =
             static_cast<unsigned long long>(task.produce ? use : use + 1) * a.pieces;
-        const bool ok = wait_at_least(a, wflag, target, t_begin, &s_ok);
+        const bool ok = wait_at_least(a, word, task.produce, target, t_begin, &s_ok);
         const long long t_wait = tr ? wall_clock64() : 0;
         if (ok) {
             if (!task.produce) {
@@ -569,11 +580,11 @@ __global__ __launch_bounds__(MAXT) void k_snac(const SnacArgs a)
         }
         // Notify: each wave of a producer waits until its write-through
         // stores have completed, so once the barrier is passed the whole
-        // piece is agent-visible and `ready` moves with a relaxed increment;
-        // a consumer on any XCD that sees the count reads the staged bytes.
-        // Releasing the slot publishes no data: the slot loads have already
-        // returned (their values were stored before the barrier), so `freed`
-        // moves the same way.
+        // piece is agent-visible and the staged count moves with a relaxed
+        // increment; a consumer on any XCD that sees the count reads the
+        // staged bytes. Releasing the slot publishes no data: the slot loads
+        // have already returned (their values were stored before the
+        // barrier), so the consumed count moves the same way.
         if (task.produce) {
             wait_vmem();
             jitter(a, t, 2u);
@@ -590,8 +601,25 @@ __global__ __launch_bounds__(MAXT) void k_snac(const SnacArgs a)
                        (static_cast<unsigned long long>(task.produce) << 32) |
                        (static_cast<unsigned long long>(!ok) << 33);
             }
-            if (ok)
-                flag_add_relaxed((task.produce ? a.ready : a.freed) + slot * kFlagStride, 1ull);
+            const unsigned long long one = task.produce ? 1ull : kConsumedOne;
+            if (fixed) {
+                // A small call's workgroup ends with its one task. Its count
+                // is a returning add, and the task that brings both of the
+                // slot's counts to their final values (every piece of every
+                // chunk the slot holds, staged and consumed) clears the word
+                // for the next call: no other task of this call touches it
+                // again. Every task counts, also one whose wait gave up, so
+                // the word always reaches its final value.
+                const unsigned long long uses =
+                    static_cast<unsigned long long>((a.nchunks - 1 - slot) / a.slots + 1);
+                const unsigned long long fin = uses * static_cast<unsigned long long>(a.pieces) *
+                                               (kConsumedOne + 1ull);
+                if (__hip_atomic_fetch_add(word, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) +
+                        one == fin)
+                    __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else if (ok) {
+                flag_add_relaxed(word, one);
+            }
             if (!fixed)
                 s_ticket = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -601,8 +629,12 @@ __global__ __launch_bounds__(MAXT) void k_snac(const SnacArgs a)
         if (tr)
             t_claim = wall_clock64();
     }
+    // A small call has cleared its slot words in its tasks and used neither
+    // the ticket nor the finished-workgroup count.
+    if (fixed)
+        return;
     // Every workgroup counts itself out; the last one clears the ticket, the
-    // slot counters and the count for the next staged call on this device,
+    // slot words and the count for the next staged call on this device,
     // so a call is one launch and a captured graph replays from a clean
     // state. Lane 0 made all of this workgroup's counter updates; it waits
     // until they have completed before counting out, and the last workgroup
@@ -620,10 +652,9 @@ __global__ __launch_bounds__(MAXT) void k_snac(const SnacArgs a)
     __syncthreads();
     if (__builtin_amdgcn_readfirstlane(s_ok) != 0) {
         const int used = static_cast<int>(a.nchunks < a.slots ? a.nchunks : a.slots);
-        for (int i = threadIdx.x; i < 2 * used; i += blockDim.x) {
-            unsigned long long* f = i < used ? a.ready + i * kFlagStride : a.freed + (i - used) * kFlagStride;
-            __hip_atomic_store(f, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        for (int i = threadIdx.x; i < used; i += blockDim.x)
+            __hip_atomic_store(a.counts + i * kFlagStride, 0ull, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
         if (threadIdx.x == 0) {
             __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(a.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -665,13 +696,13 @@ hipError_t launch_copy_t(const SnacArgs& a, int U, dim3 grid, dim3 block, hipStr
 }
 
 // ---- the fixed workspace of atom_collective_noalloc ---------------------
-// Flags (ready and freed counters, the ticket, the error word and the
+// Flags (the slot count words, the ticket, the error word and the
 // finished-workgroup count, each on its own 256-byte line, as in the
 // allocated workspace) followed by a ring of kStaticRingBytes. Each device
 // holds its own copy from the library's load until the process ends.
 constexpr int64_t kFlagLine = kFlagStride * sizeof(unsigned long long);
 constexpr int64_t kStaticFlagBytes = 64 << 10;
-static_assert((2 * kMaxSlots + 3) * kFlagLine <= kStaticFlagBytes, "flags do not fit");
+static_assert((kMaxSlots + 3) * kFlagLine <= kStaticFlagBytes, "flags do not fit");
 // The ring part also holds each slot's padding (kSlotPad), so that a ring of
 // kStaticRingBytes of chunks fits at any depth up to kMaxSlots.
 constexpr int64_t kStaticRingAlloc = kStaticRingBytes + kMaxSlots * kSlotPad;
@@ -716,11 +747,10 @@ atom_status static_workspace(hipStream_t stream, Workspace** out, hipError_t* hi
         if ((*hip_err = hipGetLastError()) != hipSuccess)
             return ATOM_ERR_HIP;
         ws.wall_khz = khz;
-        ws.ready = reinterpret_cast<unsigned long long*>(ptr);
-        ws.freed = ws.ready + kMaxSlots * kFlagStride;
-        ws.ticket = reinterpret_cast<unsigned int*>(ptr + 2 * kMaxSlots * kFlagLine);
-        ws.error = reinterpret_cast<unsigned int*>(ptr + (2 * kMaxSlots + 1) * kFlagLine);
-        ws.done = reinterpret_cast<unsigned int*>(ptr + (2 * kMaxSlots + 2) * kFlagLine);
+        ws.counts = reinterpret_cast<unsigned long long*>(ptr);
+        ws.ticket = reinterpret_cast<unsigned int*>(ptr + kMaxSlots * kFlagLine);
+        ws.error = reinterpret_cast<unsigned int*>(ptr + (kMaxSlots + 1) * kFlagLine);
+        ws.done = reinterpret_cast<unsigned int*>(ptr + (kMaxSlots + 2) * kFlagLine);
         ws.ring_bytes = kStaticRingAlloc;
         ws.ring = ptr + kStaticFlagBytes;
     }
@@ -749,8 +779,7 @@ hipError_t launch_snac(const Plan& p, const Workspace& ws, uint32_t seq, hipStre
         return hipErrorInvalidValue;
     SnacArgs a = p.sa;
     a.ring = ws.ring;
-    a.ready = ws.ready;
-    a.freed = ws.freed;
+    a.counts = ws.counts;
     a.ticket = ws.ticket;
     a.error = ws.error;
     a.done = ws.done;

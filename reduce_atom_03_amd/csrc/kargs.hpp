@@ -132,8 +132,10 @@ struct SnacArgs {
     const void* src[kMaxRanks];        // inputs
     void* dst[kMaxRanks];              // outputs
     char* ring;                        // D slots of chunk_bytes
-    unsigned long long* ready;         // per slot (stride kFlagStride): pieces staged
-    unsigned long long* freed;         // per slot (stride kFlagStride): pieces consumed
+    unsigned long long* counts;        // per slot (stride kFlagStride), over every
+                                       // chunk the slot has held in this call:
+                                       // pieces staged (low 32 bits) and pieces
+                                       // consumed (high 32 bits)
     unsigned int* ticket;              // task counter
     unsigned int* error;               // sequence number of the last call whose
                                        // wait timed out (0: none since cleared)

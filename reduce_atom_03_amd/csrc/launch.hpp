@@ -12,8 +12,7 @@ namespace atom {
 struct Workspace {
     char* ring = nullptr;
     int64_t ring_bytes = 0;
-    unsigned long long* ready = nullptr;   // kMaxSlots counters, kFlagStride apart
-    unsigned long long* freed = nullptr;   // kMaxSlots counters, kFlagStride apart
+    unsigned long long* counts = nullptr;  // kMaxSlots slot counts, kFlagStride apart
     unsigned int* ticket = nullptr;
     unsigned int* error = nullptr;         // last timed-out call's sequence number
     unsigned int* done = nullptr;

@@ -698,6 +698,10 @@ atom_status build_snac(Plan* p, int32_t sk, int P, void* const* ins, void* const
     a.lead = c.lead ? std::min(c.lead, a.slots) : std::max(1, a.slots / 2);
     a.trace = c.trace;
     a.nchunks = q;
+    // A slot's count word holds the pieces of every chunk the slot takes in
+    // 32 bits each (staged, consumed).
+    if (ceil_div(q, a.slots) * a.pieces >= (int64_t(1) << 32))
+        return ATOM_ERR_LIMIT;
     a.ntasks = 2 * a.nchunks * a.pieces;
     a.dtype = p->dtype;
     a.nt_store = (c.flags & ATOM_F_NO_NT) ? 0 : 1;
