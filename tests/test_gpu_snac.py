@@ -312,6 +312,30 @@ def test_timeout_is_reported_and_only_its_call_is_incomplete(A):
                           nan_by_class=False)
 
 
+@pytest.mark.parametrize("coll,n", [("ag", 4096), ("ar", 512)])
+def test_small_call_timeout_leaves_clean_counts(A, coll, n):
+    """A small staged call (one workgroup per task, no ticket) clears each
+    slot's count word in the task that completes it, and every task counts,
+    also one whose wait gave up. Forced from the host: a 20 us wait bound
+    against notifies and consumes held up to 3 ms. The call reports the
+    timeout; the same call without the delay, issued right after it and
+    before the status check, and then the call on a 2-slot ring (ticket),
+    must both be complete and correct."""
+    P = 8
+    c = Case(A, coll, P, n, synth.BF16, 0, seed=60)
+    info = c.plan(A.config(flags=A.F_STAGED))
+    say(f"small {coll} n={n} forced to time out, tasks={info.snac_tasks} wgs={info.num_wgs}")
+    assert info.num_wgs == info.snac_tasks             # one workgroup per task, no ticket
+    c.run(A.config(flags=A.F_STAGED, wait_us=20, jitter_us=3000, jitter_seed=11))
+    c.run(A.config(flags=A.F_STAGED))
+    assert A.atom_sync_status() == A.ERR_TIMEOUT
+    assert A.atom_sync_status() == A.OK
+    c.check(f"small {coll} after a timed-out call")
+    c.run(A.config(flags=A.F_STAGED, ring_slots=2))
+    _check_status(A, f"small {coll} ring of 2 after the timeout")
+    c.check(f"small {coll} ring of 2 after the timeout")
+
+
 @pytest.mark.parametrize("coll,n", [("ag", 4096), ("ar", 512), ("ag", 32768), ("rs", 4096),
                                     ("a2av", 1200), ("rsv", 3000)])
 @pytest.mark.parametrize("slots", [1, 2, 64])
