@@ -614,9 +614,15 @@ __global__ __launch_bounds__(MAXT) void k_snac(const SnacArgs a)
                     static_cast<unsigned long long>((a.nchunks - 1 - slot) / a.slots + 1);
                 const unsigned long long fin = uses * static_cast<unsigned long long>(a.pieces) *
                                                (kConsumedOne + 1ull);
-                if (__hip_atomic_fetch_add(word, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) +
-                        one == fin)
+                if (!task.produce && ok && uses == 1 && a.pieces == 1) {
+                    // The slot's only consumer, past its wait: the only
+                    // producer has counted, so the word is clear to reset
+                    // without the add's round trip.
                     __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                } else if (__hip_atomic_fetch_add(word, one, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT) + one == fin) {
+                    __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
             } else if (ok) {
                 flag_add_relaxed(word, one);
             }
