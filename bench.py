@@ -819,8 +819,11 @@ def sweep(A, synth, torch, dev):
     per point): AllGather of 8 partitions from 8 KiB to 1 GiB each, zero
     staging and SNAC with 512 KiB, 1 MiB and 2 MiB chunks; ReduceScatter,
     the fused and SNAC AllReduce and the uniform AllToAll of 8 inputs from
-    8 KiB to 256 MiB each; the MoE route, dispatch and combine for 1 to 4096
-    tokens per rank (256 experts, top-8, 7168-wide rows).
+    8 KiB to 256 MiB each; the ReduceScatterV and AllGatherV with Zipf(0.125)
+    partitions in units of 8 and of 1 element, zero-staging and staged, at
+    16, 64 and 256 MiB per input (output); the MoE route, dispatch and
+    combine for 1 to 4096 tokens per rank (256 experts, top-8, 7168-wide
+    rows).
     Median of event-timed launches (more samples for small messages); GB/s
     on credited bytes. Where one call's footprint is under 1 GiB, successive
     launches rotate over several disjoint buffer sets (at least 4, enough for
@@ -930,7 +933,39 @@ def sweep(A, synth, torch, dev):
     emit("alltoall", "v_uniform_counts", rows * H * 2 * P,
          timed([lambda l=l: A.atom_collective(l[2], l[3], A.OP_COPY) for l in sets], m * 2 * P),
          2 * P * m * 2)
-    del x, ys, ar
+    # Zipf(0.125) partitions (Figure 16): the ReduceScatterV of the 8 inputs
+    # and the AllGatherV of the same total into the 8 outputs, partitions
+    # counted in units of 8 elements and of single elements (partitions off
+    # 16-byte alignment: the shifted vector path), zero-staging and staged.
+    top_n = top // 2
+    zv_all = torch.empty(top_n, dtype=torch.bfloat16, device=dev).uniform_(-1, 1)
+    yv_all = [torch.empty(top_n, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+    size = 16 << 20
+    while size <= top:
+        N = size // 2                                   # elements per input / output
+        for unit in (8, 1):
+            cnt = synth.zipf_partition(N, P, 0.125, unit) // unit
+            offs = np.concatenate([[0], np.cumsum(cnt * unit)])
+            cred_rs = (P + 1) * N * 2
+            cred_ag = (P + 1) * N * 2
+            sets = []
+            for i in range(nsets(cred_ag)):
+                lo_i = i * N
+                xs_v = [view(t, lo_i, lo_i + N) for t in x]
+                ys_v = [view(yv_all[k], lo_i, lo_i + int(cnt[k]) * unit) for k in range(P)]
+                zs_v = [view(zv_all, lo_i + int(offs[k]), lo_i + int(offs[k + 1])) for k in range(P)]
+                os_v = [view(t, lo_i, lo_i + N) for t in ar]
+                sets.append((L(A.PARTITIONED, xs_v, 0, cnt, unit), L(A.SHARD, ys_v, 0, None, unit),
+                             L(A.SHARD, zs_v, 0, cnt, unit), L(A.GATHERED, os_v, 0, None, unit)))
+            for mode, cfg in (("zero-staging", None), ("snac", A.config(flags=A.F_STAGED))):
+                emit("reducescatterv_zipf", f"{mode}_unit{unit}", size,
+                     timed([lambda l=l, c=cfg: A.atom_collective(l[0], l[1], A.OP_SUM, c) for l in sets],
+                           size * P), cred_rs)
+                emit("allgatherv_zipf", f"{mode}_unit{unit}", size,
+                     timed([lambda l=l, c=cfg: A.atom_collective(l[2], l[3], A.OP_COPY, c) for l in sets],
+                           size * P), cred_ag)
+        size *= 4
+    del x, ys, ar, zv_all, yv_all
     torch.cuda.empty_cache()
     # MoE route, dispatch and combine by tokens per rank (256 experts, top-8,
     # 7168-wide bf16 rows): decode-sized batches up to prefill-sized ones

@@ -45,7 +45,10 @@
  *    (fan-out) agree; staged calls choose per segment, a segment being the
  *    bytes one source sends to one or every destination (vectors when all
  *    its streams share one offset from 16-byte alignment, with element-wise
- *    ends); the MoE movement chooses per call.
+ *    ends; staged as vectors and consumed by the shifted path when its
+ *    sources share one offset and a destination sits at another;
+ *    element-wise when its sources disagree); the MoE movement chooses per
+ *    call.
  *  - Calls that use the per-device workspace (the SNAC staging ring and its
  *    flags) are ordered by their stream; two such calls on different streams
  *    of one device must not overlap in time.

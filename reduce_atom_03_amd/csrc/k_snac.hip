@@ -65,6 +65,9 @@ namespace {
 // A slot word counts staged pieces in its low 32 bits and consumed pieces
 // in its high 32 bits.
 constexpr unsigned long long kConsumedOne = 1ull << 32;
+// 16-byte ring vectors per lane in flight on the shifted consume path (two
+// arrays of them are live, so few keep the kernel's register budget).
+constexpr int kShiftSlots = 2;
 
 struct Task {
     bool produce;
@@ -368,6 +371,78 @@ __device__ __forceinline__ void consume_vec(const SnacArgs& a, const SegGeo& g, 
     }
 }
 
+// Consume (shifted path): the piece sits in the ring at `src`, at its
+// sources' offset from 16-byte alignment, and a destination at another. As
+// the zero-staging shifted copy: vector v holds ring bytes [16v, 16v + 16)
+// of the address space, from the one holding the piece's first byte to one
+// past the one holding its last; each lane loads its vector (agent-coherent,
+// never outside the ring: a slot's padding covers both ends), takes vector
+// v - 1 from the lane below (lane 0 from the previous row, or a load of its
+// own for the wave's first), and writes the destination slot holding the
+// tail of v - 1 and the head of v: one 16-byte store, or element-wise stores
+// for the slots at the piece's two ends. Each destination's offset d from
+// the ring is taken on its own (wave-uniform).
+template <int U>
+__device__ __forceinline__ void consume_shift(const SnacArgs& a, const SegGeo& g, const char* src,
+                                              int64_t dst_off, int64_t bytes, int es)
+{
+    if (bytes <= 0)
+        return;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t nwave = blockDim.x >> 6;
+    const bool nt = a.nt_store != 0;
+    const int q0 = g.dst < 0 ? 0 : g.dst;
+    const int q1 = g.dst < 0 ? a.P : g.dst + 1;
+    const int64_t A = static_cast<int64_t>(reinterpret_cast<uintptr_t>(src));
+    const int64_t vlo = A >> 4, vhi = (A + bytes - 1) >> 4;
+    const auto ring = ring_rsrc(src - (A & 15), (vhi - vlo + 1) * kVecBytes);
+    const u32x4 zero = {0, 0, 0, 0};
+    // Rows of 64 vectors start where the first destination's slots begin a
+    // 128-byte line (the slot of vector v sits at 16 v + (D - A - d)), so
+    // each wave's stores fill whole lines; the first row may start before
+    // the piece.
+    const int64_t m0 = static_cast<int64_t>(reinterpret_cast<uintptr_t>(a.dst[q0]) + dst_off) - A;
+    const int64_t vs = vlo - ((vlo + ((m0 - (m0 & 15)) >> 4)) & 7);
+    for (int64_t w0 = vs + wave * 64 * U; w0 <= vhi + 1; w0 += nwave * 64 * U) {
+        u32x4 R[U], L[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t v = w0 + u * 64 + lane;
+            R[u] = v >= vlo && v <= vhi ? ld16_agent(ring, (v - vlo) * kVecBytes) : zero;
+        }
+        u32x4 carry = zero;
+        if (lane == 0 && w0 - 1 >= vlo && w0 - 1 <= vhi)
+            carry = ld16_agent(ring, (w0 - 1 - vlo) * kVecBytes);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            L[u] = from_lane_below(R[u], u == 0 ? carry : lane63(R[u - 1]));
+        for (int q = q0; q < q1; ++q) {
+            char* const D = static_cast<char*>(a.dst[q]) + dst_off;
+            const int d = static_cast<int>((reinterpret_cast<uintptr_t>(D) - static_cast<uint64_t>(A)) & 15);
+            // slot of vector v: ring bytes [16v - d, 16v - d + 16), stored
+            // 16-byte aligned at D + (16v - d - A); wave-uniform base
+            char* const wbase = D + ((w0 - vlo) << 4) - (A & 15) - d;   // may precede D (unused)
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t v = w0 + u * 64 + lane;
+                const int64_t sa = (v << 4) - d;
+                const int64_t lo = A - sa, hi = A + bytes - sa;
+                const int p0 = lo > 0 ? static_cast<int>(lo) : 0;
+                const int p1 = hi < 16 ? static_cast<int>(hi) : 16;
+                if (v > vhi + 1 || p0 >= p1)
+                    continue;
+                const u32x4 slot = funnel16(L[u], R[u], d);
+                const uint32_t off = static_cast<uint32_t>(u * 64 + lane) * kVecBytes;
+                if (p0 == 0 && p1 == 16)
+                    st16(wbase, off, slot, nt);
+                else
+                    store_slot_part(wbase + off, slot, p0, p1, es);
+            }
+        }
+    }
+}
+
 // ---- element-wise path: a segment with a stream off 16-byte alignment ----
 // Elements of E bytes (the element type's size) move one per lane at a time;
 // ring accesses keep the agent-coherent policy.
@@ -523,8 +598,8 @@ __global__ __launch_bounds__(MAXT) void k_snac(const SnacArgs a)
         int64_t c;
         chunk_of(a, task.chunk, &s, &c);
         const SegGeo g = seg_geo(a, s);
-        const bool elem = a.elem[s] != 0;
-        const int d = a.head[s];                   // vector segments: common offset
+        const int path = a.elem[s];                // SnacSegPath
+        const int d = a.head[s];                   // the sources' offset (SE_VEC, SE_SHIFT)
         const int64_t cbeg = c * C;
         const int64_t clen = (g.bytes - cbeg < C) ? g.bytes - cbeg : C;
         const int64_t pbeg = task.piece * a.piece_bytes;
@@ -544,24 +619,29 @@ __global__ __launch_bounds__(MAXT) void k_snac(const SnacArgs a)
                 if (a.jitter_ticks > 0)
                     __syncthreads();
             }
-            if (elem) {
+            if (path == SE_ELEM) {
                 if (task.produce)
                     produce_elem<T, REDUCE>(a, g, cbeg + pbeg, slotp + pbeg, plen);
                 else
                     consume_elem<E>(a, g, slotp + pbeg, g.dst_off + cbeg + pbeg, plen);
             } else if (d == 0) {
+                // sources 16-byte aligned: staged at the piece's place
                 if (task.produce)
                     Stage::template produce<UP>(a, g, cbeg + pbeg, slotp + pbeg, plen);
+                else if (path == SE_SHIFT)
+                    consume_shift<kShiftSlots>(a, g, slotp + pbeg, g.dst_off + cbeg + pbeg, plen,
+                                               static_cast<int>(sizeof(T)));
                 else
                     consume_vec<UC>(a, g, slotp + pbeg, g.dst_off + cbeg + pbeg, plen);
             } else {
-                // Every stream of the segment sits d bytes past a 16-byte
-                // boundary: the piece's first h = 16 - d bytes (to the
-                // boundary) and its last partial vector move element by
-                // element, the body between them as 16-byte vectors. In the
-                // ring the piece starts 112 + d bytes into its place (the slot
-                // padding holds the rest), so the body starts on a 128-byte
-                // line and the stage's stores fill whole lines.
+                // The segment's sources (and on the vector path every
+                // destination) sit d bytes past a 16-byte boundary: the
+                // piece's first h = 16 - d bytes (to the boundary) and its
+                // last partial vector are staged element by element, the
+                // body between them as 16-byte vectors. In the ring the piece
+                // starts 112 + d bytes into its place (the slot padding holds
+                // the rest), so the body starts on a 128-byte line and the
+                // stage's stores fill whole lines.
                 char* const rp = slotp + pbeg + 112 + d;
                 const int64_t h = plen < kVecBytes - d ? plen : kVecBytes - d;
                 const int64_t body = (plen - h) & ~int64_t(kVecBytes - 1);
@@ -572,6 +652,10 @@ __global__ __launch_bounds__(MAXT) void k_snac(const SnacArgs a)
                 if (task.produce) {
                     Stage::template produce<UP>(a, g, o + h, rp + h, body);
                     produce_ends<T, REDUCE>(a, g, o, rp, h, h + body, tail);
+                } else if (path == SE_SHIFT) {
+                    // a destination at another offset: the whole piece,
+                    // ends included, through the shifted path
+                    consume_shift<kShiftSlots>(a, g, rp, g.dst_off + o, plen, static_cast<int>(sizeof(T)));
                 } else {
                     consume_vec<UC>(a, g, rp + h, g.dst_off + o + h, body);
                     consume_ends<E>(a, g, rp, g.dst_off + o, h, h + body, tail);

@@ -128,6 +128,12 @@ struct CopyArgs {
 //              offset  (the composed AllReduce of Figure 6; stage = reduce)
 enum SnacKind : int32_t { SK_GATHER = 0, SK_EXCHANGE = 1, SK_SCATTER = 2, SK_ALLRED = 3 };
 
+// How a segment moves: every stream at one offset d from 16-byte alignment
+// (vectors, element-wise ends when d > 0); its sources at one offset and a
+// destination at another (staged as SE_VEC, consumed by the shifted path);
+// sources at different offsets (element by element).
+enum SnacSegPath : uint8_t { SE_VEC = 0, SE_ELEM = 1, SE_SHIFT = 2 };
+
 struct SnacArgs {
     const void* src[kMaxRanks];        // inputs
     void* dst[kMaxRanks];              // outputs
@@ -176,14 +182,13 @@ struct SnacArgs {
                                        // 0: segment-major, found in chunk_begin
     int32_t cnt[kMaxSegs];             // rows per segment
     int32_t chunk_begin[kMaxSegs + 1]; // first chunk of each segment (segment-major)
-    uint8_t elem[kMaxSegs];            // 1: the segment's streams sit at different
-                                       // offsets from 16-byte alignment; it is
-                                       // staged and consumed element by element
-    uint8_t head[kMaxSegs];            // vector segments: the common offset d of its
-                                       // streams from 16-byte alignment (0..15); for
-                                       // d > 0 a piece is staged 112 + d bytes into
-                                       // its ring place, its first 16 - d bytes and
-                                       // its tail element by element
+    uint8_t elem[kMaxSegs];            // SnacSegPath of the segment
+    uint8_t head[kMaxSegs];            // SE_VEC and SE_SHIFT segments: the offset d
+                                       // of its sources from 16-byte alignment
+                                       // (0..15); for d > 0 a piece is staged
+                                       // 112 + d bytes into its ring place, its
+                                       // first 16 - d bytes and its tail element
+                                       // by element
 };
 
 // Expert-parallel MoE routing (three kernels: rank within chunks, per-rank

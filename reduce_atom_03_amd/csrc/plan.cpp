@@ -584,42 +584,55 @@ atom_status build_snac(Plan* p, int32_t sk, int P, void* const* ins, void* const
         largest = std::max(largest, bytes[s]);
         a.cnt[s] = static_cast<int32_t>(cnt[s]);
         // Offset from 16-byte alignment of every stream of the segment at
-        // its first byte: all equal (d) -> vector path, with element-wise
-        // heads and tails when d > 0; otherwise element-wise.
-        int common = -1;
-        bool same = true;
-        auto at = [&](const void* b, int64_t off) {
-            const int m = static_cast<int>((reinterpret_cast<uintptr_t>(b) + static_cast<uint64_t>(off)) % kVecBytes);
-            if (common < 0)
-                common = m;
-            same = same && m == common;
+        // its first byte. All equal (d): the vector path, staged d bytes
+        // past a 16-byte boundary, with element-wise heads and tails when
+        // d > 0. Sources equal (d) and some destination not: staged the
+        // same way, consumed by the shifted path. Sources unequal:
+        // element-wise.
+        int src_d = -1, dst_d = -1;
+        bool src_same = true, all_same = true;
+        auto mis = [](const void* b, int64_t off) {
+            return static_cast<int>((reinterpret_cast<uintptr_t>(b) + static_cast<uint64_t>(off)) % kVecBytes);
+        };
+        auto at_src = [&](const void* b, int64_t off) {
+            const int m = mis(b, off);
+            if (src_d < 0)
+                src_d = m;
+            src_same = src_same && m == src_d;
+        };
+        auto at_dst = [&](const void* b, int64_t off) {
+            const int m = mis(b, off);
+            if (dst_d < 0)
+                dst_d = m;
+            all_same = all_same && m == dst_d;
         };
         if (sk == SK_EXCHANGE) {
             const int r = s / P, j = s % P;
             int64_t src_rows = 0;
             for (int jj = 0; jj < j; ++jj)
                 src_rows += cnt[r * P + jj];
-            at(ins[r], src_rows * rb);
-            at(outs[j], col_rows[j] * rb);
+            at_src(ins[r], src_rows * rb);
+            at_dst(outs[j], col_rows[j] * rb);
             col_rows[j] += cnt[s];
         } else {
             const int64_t off = run_rows * rb;
             if (sk == SK_GATHER) {
-                at(ins[s], 0);
+                at_src(ins[s], 0);
             } else {
                 for (int r = 0; r < P; ++r)
-                    at(ins[r], off);
+                    at_src(ins[r], off);
             }
             if (sk == SK_SCATTER) {
-                at(outs[s], 0);
+                at_dst(outs[s], 0);
             } else {
                 for (int q = 0; q < P; ++q)
-                    at(outs[q], off);
+                    at_dst(outs[q], off);
             }
             run_rows += cnt[s];
         }
-        a.elem[s] = same ? 0 : 1;
-        a.head[s] = static_cast<uint8_t>(same ? common : 0);
+        all_same = all_same && src_same && src_d == dst_d;
+        a.elem[s] = static_cast<uint8_t>(all_same ? SE_VEC : (src_same ? SE_SHIFT : SE_ELEM));
+        a.head[s] = static_cast<uint8_t>(src_same ? src_d : 0);
     }
     if (total == 0)
         return ATOM_OK;
@@ -708,10 +721,13 @@ atom_status build_snac(Plan* p, int32_t sk, int P, void* const* ins, void* const
     a.wait_ticks = c.wait_us;             // converted to clock ticks at launch
     a.jitter_ticks = c.jitter_us;         // likewise
     a.jitter_seed = c.jitter_seed;
-    bool any_elem = false;
-    for (int s = 0; s < nseg; ++s)
-        any_elem = any_elem || (a.elem[s] && bytes[s] > 0);
+    bool any_elem = false, any_shift = false;
+    for (int s = 0; s < nseg; ++s) {
+        any_elem = any_elem || (a.elem[s] == SE_ELEM && bytes[s] > 0);
+        any_shift = any_shift || (a.elem[s] == SE_SHIFT && bytes[s] > 0);
+    }
     p->vec = any_elem ? 0 : 1;
+    p->snac_shifted = any_shift ? 1 : 0;
     // Lanes per workgroup: 512 (two persistent workgroups of 8 waves per
     // CU). Measured on MI355X with streaming output stores: the composed
     // AllReduce, whose reducing stage reads P inputs per staged byte, +5 %
@@ -1262,7 +1278,10 @@ void plan_fill_info(const Plan& p, atom_plan_info* info)
     info->lanes = p.wg;
     info->stages = p.U;
     info->grid_rows = static_cast<int32_t>(rows);
-    info->shifted = (p.exec == EX_REDUCE && p.ra.shifted) || (p.exec == EX_COPY && p.ca.shifted) ? 1 : 0;
+    info->shifted = (p.exec == EX_REDUCE && p.ra.shifted) || (p.exec == EX_COPY && p.ca.shifted) ||
+                            ((p.exec == EX_SNAC_COPY || p.exec == EX_SNAC_REDUCE) && p.snac_shifted)
+                        ? 1
+                        : 0;
     const bool staged = p.exec == EX_SNAC_COPY || p.exec == EX_SNAC_REDUCE;
     info->snac_lead = staged ? p.sa.lead : 0;
     info->snac_tasks = staged ? p.sa.ntasks : 0;

@@ -35,6 +35,7 @@ struct PlanHead {
     int32_t slots = 0;
     int64_t chunk_bytes = 0;
     int64_t ring_bytes = 0;
+    int32_t snac_shifted = 0; // 1: some segment is consumed by the shifted path
 };
 
 struct Plan : PlanHead {

@@ -174,7 +174,8 @@ int main(int argc, char** argv)
             check(p.sa.slot_bytes == p.sa.chunk_bytes + kSlotPad &&
                       p.ring_bytes == p.sa.slot_bytes * p.sa.slots, "snac ring", iter);
             for (int s = 0; s < p.sa.nseg; ++s)
-                check(p.sa.head[s] < kVecBytes && (p.sa.elem[s] == 0 || p.sa.head[s] == 0) &&
+                check(p.sa.head[s] < kVecBytes && p.sa.elem[s] <= SE_SHIFT &&
+                          (p.sa.elem[s] != SE_ELEM || p.sa.head[s] == 0) &&
                           p.sa.head[s] % p.esize == 0,
                       "snac segment offset", iter);
             check(p.wg >= 64 && p.wg <= 512 && p.wg % 64 == 0, "snac wg", iter);

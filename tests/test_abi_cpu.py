@@ -211,10 +211,15 @@ def test_every_collective_can_be_staged():
         st, info = Q(lin, lout, op, cfg=cfg, **kw)
         assert st == A.OK and info.staged == 1 and info.kind == kind, (lin, lout, op, kw)
         assert info.vector_path == 1
-    # 63-element partitions: off 16-byte alignment, staged element by element
+    # 63-element partitions: the outputs' segments off the sources' 16-byte
+    # phase, consumed by the shifted path
     st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, n=63, cfg=cfg)
-    assert st == A.OK and info.staged == 1 and info.vector_path == 0
+    assert st == A.OK and info.staged == 1 and info.vector_path == 1 and info.shifted == 1
     st, info = Q(A.PARTITIONED, A.SHARD, A.OP_SUM, ins=[b + 2 for b in fake(4, 4096)], cfg=cfg)
+    assert st == A.OK and info.staged == 1 and info.vector_path == 1 and info.shifted == 1
+    # sources of one partition at different offsets: element by element
+    st, info = Q(A.PARTITIONED, A.SHARD, A.OP_SUM, ins=[b + 2 * (r == 1) for r, b in enumerate(fake(4, 4096))],
+                 cfg=cfg)
     assert st == A.OK and info.staged == 1 and info.vector_path == 0
 
 
@@ -578,15 +583,28 @@ def test_snac_default_lead_by_stage():
 
 def test_staged_segments_at_a_common_offset_stay_vectorized():
     """Staged calls: a segment whose streams all sit at one offset from
-    16-byte alignment takes the vector path (element-wise ends); streams at
-    different offsets make the call element-wise."""
+    16-byte alignment takes the vector path (element-wise ends); one whose
+    sources agree and a destination does not is staged the same way and
+    consumed by the shifted path; sources at different offsets make the call
+    element-wise."""
     P, n = 8, 4096
     st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=P, n=n, cfg=A.config(flags=A.F_STAGED),
                  ins=fake(P, n * 2, align_off=2), outs=fake(P, P * n * 2, start=BASE + (1 << 36), align_off=2))
-    assert st == A.OK and info.staged == 1 and info.vector_path == 1
+    assert st == A.OK and info.staged == 1 and info.vector_path == 1 and info.shifted == 0
     st, info = Q(A.PARTITIONED, A.GATHERED, A.OP_SUM, P=P, n=n, cfg=A.config(flags=A.F_STAGED),
                  ins=fake(P, P * n * 2, align_off=6), outs=fake(P, P * n * 2, start=BASE + (1 << 36), align_off=6))
-    assert st == A.OK and info.staged == 1 and info.vector_path == 1
+    assert st == A.OK and info.staged == 1 and info.vector_path == 1 and info.shifted == 0
+    # one source per AllGather segment, outputs at another offset: shifted
     st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=P, n=n, cfg=A.config(flags=A.F_STAGED),
                  ins=fake(P, n * 2, align_off=2), outs=fake(P, P * n * 2, start=BASE + (1 << 36), align_off=4))
+    assert st == A.OK and info.staged == 1 and info.vector_path == 1 and info.shifted == 1
+    # ReduceScatter: the P sources agree, the outputs do not: shifted
+    st, info = Q(A.PARTITIONED, A.SHARD, A.OP_SUM, P=P, n=n, cfg=A.config(flags=A.F_STAGED),
+                 ins=fake(P, P * n * 2, align_off=2), outs=fake(P, n * 2, start=BASE + (1 << 36)))
+    assert st == A.OK and info.staged == 1 and info.vector_path == 1 and info.shifted == 1
+    # sources at different offsets: element-wise
+    ins = fake(P, P * n * 2)
+    ins[3] += 2
+    st, info = Q(A.PARTITIONED, A.SHARD, A.OP_SUM, P=P, n=n, cfg=A.config(flags=A.F_STAGED),
+                 ins=ins, outs=fake(P, n * 2, start=BASE + (1 << 36)))
     assert st == A.OK and info.staged == 1 and info.vector_path == 0
