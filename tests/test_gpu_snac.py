@@ -53,13 +53,15 @@ def _check_status(A, what):
 class Case:
     """Inputs, oracle results and device buffers of one collective call.
     skew: elements each input and output view sits past a 16-byte boundary
-    (a list gives one skew per rank)."""
+    (a list gives one skew per rank); out_skew, when given, the same for
+    the outputs alone."""
 
-    def __init__(self, A, coll, P, n, dtype, skew=0, seed=0):
+    def __init__(self, A, coll, P, n, dtype, skew=0, seed=0, out_skew=None):
         self.A, self.coll, self.P, self.dtype = A, coll, P, dtype
         tdt = _tdt(dtype)
         sk = skew if isinstance(skew, list) else [skew] * P
-        self.sk = sk
+        osk = sk if out_skew is None else (out_skew if isinstance(out_skew, list) else [out_skew] * P)
+        self.sk, self.osk = sk, osk
 
         def dev(a, r):
             if a.size == 0:
@@ -69,7 +71,7 @@ class Case:
         def outs(sizes):
             fulls, views = [], []
             for r, m in enumerate(sizes):
-                f, v = out_buffers([m], tdt, GUARD + sk[r])
+                f, v = out_buffers([m], tdt, GUARD + osk[r])
                 fulls.append(f[0])
                 views.append(v[0])
             self.fulls, self.sizes = fulls, list(sizes)
@@ -148,7 +150,7 @@ class Case:
                 _reduced(got, w, f"{what} out_{j}")
             else:
                 assert_bits_equal(got, w, f"{what} out_{j}", nan_by_class=False)
-        for f, m, s in zip(self.fulls, self.sizes, self.sk):
+        for f, m, s in zip(self.fulls, self.sizes, self.osk):
             check_guards([f], [m], GUARD + s)
 
 
@@ -177,6 +179,32 @@ def test_every_collective_staged(A, coll, shape, dtype):
     c.run(cfg)
     _check_status(A, f"staged {coll} {shape}")
     c.check(f"staged {coll} {shape}")
+
+
+@pytest.mark.parametrize("dtype", [synth.BF16, synth.F32])
+@pytest.mark.parametrize("coll", COLLS)
+@pytest.mark.parametrize("skews", [(0, 1), (3, 1), (2, 0), (1, "mixed")])
+def test_every_collective_staged_shifted(A, coll, skews, dtype):
+    """Inputs and outputs at different offsets from 16-byte alignment (in
+    elements; mixed: a different output offset per rank): every segment's
+    sources agree, so each is staged as vectors at its sources' offset and
+    consumed by the shifted path, bit for bit against the oracle; 64 KiB
+    chunks in a 3-slot ring with 16 KiB pieces, and the default plan."""
+    P = 8
+    n = 20000
+    sin, sout = skews
+    sout = [r % 4 for r in range(P)] if sout == "mixed" else sout
+    say(f"staged shifted {coll} in={sin} out={sout} {dtype}")
+    c = Case(A, coll, P, n, dtype, sin, seed=70 + COLLS.index(coll), out_skew=sout)
+    for cfg in (A.config(flags=A.F_STAGED, chunk_bytes=64 << 10, ring_slots=3, piece_bytes=16 << 10),
+                A.config(flags=A.F_STAGED)):
+        info = c.plan(cfg)
+        assert info.staged == 1 and info.vector_path == 1
+        if coll in ("rs", "ag", "ar", "a2a"):
+            assert info.shifted == 1
+        c.run(cfg)
+        _check_status(A, f"staged shifted {coll}")
+        c.check(f"staged shifted {coll} in={sin} out={sout}")
 
 
 @pytest.mark.parametrize("coll", COLLS)
