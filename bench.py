@@ -743,7 +743,7 @@ def snac_sweep(A, synth, torch, dev):
     """Launch choices of the staged path, cold (a 1 GiB copy between calls;
     median of event-timed calls): for each chunk size (512 KiB, 1 MiB,
     2 MiB, the ring kept at 32 MiB), leads of D, D/2, D/4 and D/8 chunks and
-    pieces of 64, 128 and 256 KiB, on the AllGather of 8 x 64 MiB, the
+    pieces of 32, 64 and 128 KiB, on the AllGather of 8 x 64 MiB, the
     composed AllReduce and the Zipf(0.125) ReduceScatterV of 8 x 256 MiB and
     the Zipf AllGatherV of 512 MiB; then the AllGather of 8 x 1 GiB at each
     chunk size and leads D, D/2, D/4 (default piece)."""
@@ -781,7 +781,7 @@ def snac_sweep(A, synth, torch, dev):
         for chunk in (512 << 10, 1 << 20, 2 << 20):
             D = max(4, min(64, (32 << 20) // chunk))
             for lead in (D, D // 2, D // 4, D // 8):
-                for piece in (64 << 10, 128 << 10, 256 << 10):
+                for piece in (32 << 10, 64 << 10, 128 << 10):
                     point(name, li, lo, op, reps, chunk_bytes=chunk, snac_lead=lead, piece_bytes=piece)
 
     S = 64 * MiB
