@@ -82,12 +82,16 @@ def test_random_collective(A, case):
     P = int(g.integers(1, 17))
     dtype = synth.BF16 if g.random() < 0.6 else synth.F32
     cfg, desc = _config(A, g, staged)
-    # buffers 1-3 elements past a 16-byte boundary (element-aligned only) on
-    # a third of the cases, staged or not; lengths of any size
+    # inputs and outputs 1-3 elements past a 16-byte boundary (element-aligned
+    # only), each on about a third of the cases and drawn apart, so that
+    # sources and destinations may sit at different offsets; lengths of any
+    # size
     skew = 0 if g.random() < 0.67 else int(g.integers(1, 4))
+    oskew = skew if g.random() < 0.5 else (0 if g.random() < 0.5 else int(g.integers(1, 4)))
     seed = 5000 + case
     n = _length(g, 40000)
-    say(f"random case {case}: {kind}{' staged' if staged else ''} P={P} n={n} {dtype} skew={skew} cfg={desc}")
+    say(f"random case {case}: {kind}{' staged' if staged else ''} P={P} n={n} {dtype} "
+        f"skew={skew}/{oskew} cfg={desc}")
     tdt = _tdt(dtype)
 
     def dev(a):
@@ -98,34 +102,34 @@ def test_random_collective(A, case):
         dx = [dev(x) for x in xs]
         if kind == "rs":
             want = oracle.reduce_scatter(xs)
-            fulls, outs = out_buffers([n] * P, tdt, GUARD + skew)
+            fulls, outs = out_buffers([n] * P, tdt, GUARD + oskew)
             A.reduce_scatter(dx, outs, cfg)
         else:
             want = oracle.all_reduce(xs)
-            fulls, outs = out_buffers([P * n] * P, tdt, GUARD + skew)
+            fulls, outs = out_buffers([P * n] * P, tdt, GUARD + oskew)
             A.all_reduce(dx, outs, cfg)
         assert A.atom_sync_status() == A.OK
         for j in range(P):
             _reduced(from_dev(outs[j]), want[j], f"case {case} out_{j}")
-        check_guards(fulls, [o.numel() for o in outs], GUARD + skew)
+        check_guards(fulls, [o.numel() for o in outs], GUARD + oskew)
     elif kind == "ag":
         zs = [synth.mixed_bits(seed, k, n, dtype) for k in range(P)]
         want = oracle.all_gather(zs)
-        fulls, outs = out_buffers([P * n] * P, tdt, GUARD + skew)
+        fulls, outs = out_buffers([P * n] * P, tdt, GUARD + oskew)
         A.all_gather([dev(z) for z in zs], outs, cfg)
         assert A.atom_sync_status() == A.OK
         for j in range(P):
             assert_bits_equal(from_dev(outs[j]), want[j], f"case {case} out_{j}", nan_by_class=False)
-        check_guards(fulls, [P * n] * P, GUARD + skew)
+        check_guards(fulls, [P * n] * P, GUARD + oskew)
     elif kind == "a2a":
         xs = [synth.mixed_bits(seed, r, P * n, dtype) for r in range(P)]
         want = oracle.all_to_all(xs)
-        fulls, outs = out_buffers([P * n] * P, tdt, GUARD + skew)
+        fulls, outs = out_buffers([P * n] * P, tdt, GUARD + oskew)
         A.all_to_all([dev(x) for x in xs], outs, cfg)
         torch.cuda.synchronize()
         for j in range(P):
             assert_bits_equal(from_dev(outs[j]), want[j], f"case {case} out_{j}", nan_by_class=False)
-        check_guards(fulls, [P * n] * P, GUARD + skew)
+        check_guards(fulls, [P * n] * P, GUARD + oskew)
     else:
         row = int(g.choice([1, 3, 8, 24, 64]))
         if kind == "a2av":
@@ -135,7 +139,7 @@ def test_random_collective(A, case):
             xs = [synth.mixed_bits(seed, r, int(rows[r]) * row, dtype) for r in range(P)]
             want = oracle.all_to_all_v(xs, C, row)
             sizes = [int(R[j]) * row for j in range(P)]
-            fulls, outs = out_buffers(sizes, tdt, GUARD + skew)
+            fulls, outs = out_buffers(sizes, tdt, GUARD + oskew)
             A.all_to_all_v([dev(x) for x in xs], outs, C, row, cfg)
             torch.cuda.synchronize()
             for j in range(P):
@@ -148,7 +152,7 @@ def test_random_collective(A, case):
                 xs = [synth.mixed_bits(seed, r, T, dtype, specials=False) for r in range(P)]
                 want = oracle.reduce_scatter_v(xs, cnt * row)
                 sizes = [int(c) * row for c in cnt]
-                fulls, outs = out_buffers(sizes, tdt, GUARD + skew)
+                fulls, outs = out_buffers(sizes, tdt, GUARD + oskew)
                 A.reduce_scatter_v([dev(x) for x in xs], outs, cnt, row, cfg)
                 torch.cuda.synchronize()
                 for k in range(P):
@@ -157,13 +161,13 @@ def test_random_collective(A, case):
                 zs = [synth.mixed_bits(seed, k, int(cnt[k]) * row, dtype) for k in range(P)]
                 want = oracle.all_gather_v(zs)
                 sizes = [T] * P
-                fulls, outs = out_buffers(sizes, tdt, GUARD + skew)
+                fulls, outs = out_buffers(sizes, tdt, GUARD + oskew)
                 A.all_gather_v([dev(z) for z in zs], outs, cnt, row, cfg)
                 torch.cuda.synchronize()
                 for j in range(P):
                     assert_bits_equal(from_dev(outs[j]), want[j], f"case {case} out_{j}",
                                       nan_by_class=False)
-        check_guards(fulls, sizes, GUARD + skew)
+        check_guards(fulls, sizes, GUARD + oskew)
 
 
 @pytest.mark.parametrize("case", range(40))
