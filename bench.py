@@ -1141,7 +1141,8 @@ def c1_oracle_ms(c1):
 
 def cpu_baseline(args, C3, S, credited):
     """The oracle, as it stands, on the same step (same seeds and shapes, its
-    own OpenMP threads); GB/s on the same credited bytes."""
+    own OpenMP threads, then once on one thread); GB/s on the same credited
+    bytes, with the host's CPU count, model and memory."""
     import oracle
     from reduce_atom_03_amd import synth
     log("timing the CPU oracle ...")
@@ -1194,7 +1195,30 @@ def cpu_baseline(args, C3, S, credited):
             "sample": f"the full step (same shapes and seeds), median of {args.cpu_reps} runs, "
                       f"{best:.2f} s per step",
             "one_core": {"value": round(credited / one / 1e9, 2), "unit": "GB/s",
-                         "sample": f"the same step once on 1 thread, {one:.2f} s"}}
+                         "sample": f"the same step once on 1 thread, {one:.2f} s"},
+            "host": host_info()}
+
+
+def host_info():
+    """The host the oracle ran on: logical CPUs, CPU model, memory."""
+    info = {"nproc": os.cpu_count()}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemTotal:"):
+                    info["mem_gib"] = round(int(line.split()[1]) / (1 << 20), 1)
+                    break
+    except OSError:
+        pass
+    return info
 
 
 if __name__ == "__main__":
