@@ -305,18 +305,26 @@ def main():
         b.record(stream)
     torch.cuda.synchronize()
     lat = np.array([a.elapsed_time(b) * 1e3 for a, b in pairs])
-    # The same 8 KiB AllGather through SNAC (the staged path's latency).
+    # The same 8 KiB AllGather through SNAC (the staged path's latency): a
+    # small call hands off through tagged words by default; ATOM_F_COUNTED
+    # gives the slot-count hand-off of larger calls, for comparison.
     snac8 = lambda l=lay8: A.atom_collective(l[0], l[1], A.OP_COPY, snac_cfg)
-    snac8()
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(args.lat_iters)]
-    for a, b in pairs:
-        a.record(stream)
-        snac8()
-        b.record(stream)
-    torch.cuda.synchronize()
-    assert A.atom_sync_status() == A.OK
-    lat_snac = np.array([a.elapsed_time(b) * 1e3 for a, b in pairs])
+    counted_cfg = A.config(flags=A.F_STAGED | A.F_COUNTED)
+    snac8c = lambda l=lay8: A.atom_collective(l[0], l[1], A.OP_COPY, counted_cfg)
+
+    def event_lat(fn):
+        fn()
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(args.lat_iters)]
+        for a, b in pairs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        assert A.atom_sync_status() == A.OK
+        return np.array([a.elapsed_time(b) * 1e3 for a, b in pairs])
+    lat_snac = event_lat(snac8)
+    lat_snac_counted = event_lat(snac8c)
     # Decode AllReduce latency per batch size (event pairs, as above).
     dec_lat = {}
     for b in (1, 2, 4, 8, 16):
@@ -410,6 +418,7 @@ def main():
         return round(float(np.median(v)), 2)
 
     b2b = {"ag_8KiB": back_to_back_us(ag8), "ag_8KiB_snac": back_to_back_us(snac8),
+           "ag_8KiB_snac_counted": back_to_back_us(snac8c),
            "copy_16B": back_to_back_us(lambda: A.atom_copy(tiny_dst, tiny_src, 16))}
     for b in (1, 2, 4, 8, 16):
         lay = (L(A.PARTITIONED, x5[b], b * 896), L(A.GATHERED, o5[b], b * 896))
@@ -469,6 +478,8 @@ def main():
         "p99_us_8KiB": round(float(np.percentile(lat, 99)), 2),
         "p50_us_8KiB_snac": round(float(np.percentile(lat_snac, 50)), 2),
         "p99_us_8KiB_snac": round(float(np.percentile(lat_snac, 99)), 2),
+        "p50_us_8KiB_snac_counted": round(float(np.percentile(lat_snac_counted, 50)), 2),
+        "p99_us_8KiB_snac_counted": round(float(np.percentile(lat_snac_counted, 99)), 2),
         "host_us_per_call_8KiB": round(host_us, 2),
         "graph_us_per_call_8KiB": round(graph_us, 2),
         "back_to_back_us_per_call": b2b,

@@ -145,6 +145,17 @@ typedef struct atom_layout {
 #define ATOM_F_XCD_ORDER 0x4u /* zero-staging kernels give each XCD one
                                  contiguous range of tiles (default: plain
                                  workgroup order; measured within noise) */
+#define ATOM_F_COUNTED 0x8u   /* staged calls: small calls, too, notify
+                                 through the ring slots' count words.
+                                 Default: a small staged call (one workgroup
+                                 per task, every segment 16-byte aligned, at
+                                 most 1 MiB staged) carries its notify in the
+                                 staged data itself: each staged 4-byte word
+                                 is written next to a tag holding the call's
+                                 sequence number, by one 64-bit store, and
+                                 the consumer waits for its words' tags
+                                 (atom_plan_info.snac_tagged). Same results;
+                                 ignored by zero-staging calls. */
 typedef struct atom_config {
     int64_t chunk_bytes;       /* SNAC chunk (notify unit); power of two in
                                   [64 KiB, 16 MiB]; default 512 KiB for
@@ -242,6 +253,10 @@ typedef struct atom_plan_info {
     int32_t snac_lead;         /* SNAC: chunks staged ahead of the consumers */
     int64_t snac_tasks;        /* SNAC: stage + consume tasks (2 * chunks *
                                   pieces per chunk); 0 when not staged */
+    int32_t snac_tagged;       /* SNAC: 1 when the call hands off through
+                                  tagged words (see ATOM_F_COUNTED), 0 through
+                                  the slot count words */
+    int32_t reserved;
 } atom_plan_info;
 
 /* Atom copy (abstract: the copy primitive). Copies `bytes` bytes from src to
@@ -269,8 +284,10 @@ atom_status atom_reduce(void* dst, const void* const* srcs, int32_t nsrcs,
  * ordinary buffers): its layouts become a list of segments (the bytes one
  * source sends to one or every destination), chunks of cfg->chunk_bytes of
  * each are staged (copied, or reduced in rank order) in a ring of
- * cfg->ring_slots slots, notified through device-memory flags and consumed
- * by other workgroups; the result equals the zero-staging one bit for bit.
+ * cfg->ring_slots slots, notified through device-memory flags (a small call:
+ * through a tag stored with each staged word, see ATOM_F_COUNTED) and
+ * consumed by other workgroups; the result equals the zero-staging one bit
+ * for bit.
  * Returns ATOM_OK, ATOM_ERR_INVALID_ARG, ATOM_ERR_UNSUPPORTED,
  * ATOM_ERR_NOMEM or ATOM_ERR_HIP. A SNAC wait that runs out on the device is
  * reported by atom_sync_status, not here (the call returns before the
@@ -281,8 +298,9 @@ atom_status atom_collective(const atom_layout* in, const atom_layout* out,
 /* For callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc. The same
  * collective as atom_collective, but a staged call takes its ring and flags
- * from a fixed array inside the library (ATOM_NOALLOC_RING_BYTES of ring per
- * device, held from the library's load until the process ends) instead of
+ * from a fixed array inside the library (ATOM_NOALLOC_RING_BYTES of ring, and
+ * 2 MiB for the tagged words of small calls, per device, held from the
+ * library's load until the process ends) instead of
  * the growing workspace, so no call allocates. Without cfg->ring_slots the
  * ring depth is cut to what fits; a call whose chunk (as planned: a message
  * smaller than the chunk is staged in a smaller one), or whose chunk times

@@ -28,7 +28,7 @@ OP_COPY, OP_SUM = 0, 1
 # atom_layout_kind
 PARTITIONED, SHARD, GATHERED, TRANSPOSED = 0, 1, 2, 3
 # atom_config flags
-F_STAGED, F_NO_NT, F_XCD_ORDER = 0x1, 0x2, 0x4
+F_STAGED, F_NO_NT, F_XCD_ORDER, F_COUNTED = 0x1, 0x2, 0x4, 0x8
 # atom_collective_kind
 COLL_NONE, COLL_REDUCE_SCATTER, COLL_ALL_GATHER, COLL_ALL_TO_ALL, \
     COLL_ALL_TO_ALL_V, COLL_ALL_REDUCE, COLL_REDUCE_SCATTER_V, \
@@ -84,6 +84,8 @@ class AtomPlanInfo(ctypes.Structure):
         ("shifted", ctypes.c_int32),
         ("snac_lead", ctypes.c_int32),
         ("snac_tasks", ctypes.c_int64),
+        ("snac_tagged", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 

@@ -72,11 +72,12 @@ atom_status workspace(int64_t ring_bytes, hipStream_t stream, Workspace** out)
         ws.wall_khz = khz;
         // counts[kMaxSlots] (each slot's count on its own 256-byte line),
         // then the ticket, the error word and the finished-workgroup count
-        // on lines of their own. All start at zero; every staged kernel
-        // leaves them at zero (the error word excepted).
+        // on lines of their own, then the tagged ring of small calls. All
+        // start at zero; every staged kernel leaves the flags at zero (the
+        // error word excepted) and the tagged pairs it consumed cleared.
         char* flags = nullptr;
         const size_t line = kFlagStride * sizeof(unsigned long long);
-        const size_t fbytes = (kMaxSlots + 3) * line;
+        const size_t fbytes = (kMaxSlots + 3) * line + kTagBytes;
         if (hipMalloc(&flags, fbytes) != hipSuccess)
             return ATOM_ERR_NOMEM;
         if (hipError_t e = hipMemset(flags, 0, fbytes); e != hipSuccess) {
@@ -87,6 +88,7 @@ atom_status workspace(int64_t ring_bytes, hipStream_t stream, Workspace** out)
         ws.ticket = reinterpret_cast<unsigned int*>(flags + kMaxSlots * line);
         ws.error = reinterpret_cast<unsigned int*>(flags + (kMaxSlots + 1) * line);
         ws.done = reinterpret_cast<unsigned int*>(flags + (kMaxSlots + 2) * line);
+        ws.tags = reinterpret_cast<unsigned long long*>(flags + (kMaxSlots + 3) * line);
     }
     if (ws.ring_bytes < ring_bytes) {
         const int64_t want = std::max(ring_bytes, 2 * ws.ring_bytes);
@@ -110,12 +112,17 @@ atom_status workspace(int64_t ring_bytes, hipStream_t stream, Workspace** out)
 
 // The next staged call's sequence number on a device (never 0, the error
 // word's "no timeout"): a wait that times out records it, and only waits of
-// the same call give up early because of it.
-uint32_t next_seq(Workspace* ws)
+// the same call give up early because of it. It is also the tag of the
+// call's words on the tagged ring; *wrapped is set when the numbers start
+// over, and the caller then clears that ring before the launch.
+uint32_t next_seq(Workspace* ws, bool* wrapped)
 {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
-    if (++ws->seq == 0)
+    *wrapped = false;
+    if (++ws->seq == 0) {
         ws->seq = 1;
+        *wrapped = true;
+    }
     return ws->seq;
 }
 
@@ -143,7 +150,11 @@ atom_status run(const Plan& p, void* stream)
         atom_status st = workspace(p.ring_bytes, s, &ws);
         if (st != ATOM_OK)
             return st;
-        e = launch_snac(p, *ws, next_seq(ws), s);
+        bool wrapped = false;
+        const uint32_t seq = next_seq(ws, &wrapped);
+        if (wrapped && (e = launch_clear_tags(*ws, s)) != hipSuccess)
+            break;
+        e = launch_snac(p, *ws, seq, s);
         break;
     }
     default:

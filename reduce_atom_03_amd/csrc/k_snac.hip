@@ -243,6 +243,11 @@ __device__ __forceinline__ void jitter(const SnacArgs& a, int64_t ticket, uint32
 
 // Copy: from the segment's source (AllGather, AllToAll).
 struct StageCopy {
+    // One 16-byte vector of the staged data, from segment byte o.
+    __device__ static u32x4 stage_vec(const SnacArgs& a, const SegGeo& g, int64_t o)
+    {
+        return ld16_stream(g.src + o);
+    }
     template <int U>
     __device__ static void produce(const SnacArgs& a, const SegGeo& g, int64_t off, char* dst,
                                    int64_t bytes)
@@ -274,6 +279,19 @@ struct StageCopy {
 // rounded once (ReduceScatter, and its half of the composed AllReduce).
 template <typename T, int P>
 struct StageReduce {
+    __device__ static u32x4 stage_vec(const SnacArgs& a, const SegGeo& g, int64_t o)
+    {
+        u32x4 x[P];
+#pragma unroll
+        for (int r = 0; r < P; ++r)
+            x[r] = ld16_stream(static_cast<const char*>(a.src[r]) + g.src_off + o);
+        SlotAcc<T> acc;
+        acc.init(x[0]);
+#pragma unroll
+        for (int r = 1; r < P; ++r)
+            acc.add(x[r]);
+        return acc.pack();
+    }
     template <int U>
     __device__ static void produce(const SnacArgs& a, const SegGeo& g, int64_t off, char* dst,
                                    int64_t bytes)
@@ -752,6 +770,204 @@ __global__ __launch_bounds__(MAXT) void k_snac(const SnacArgs a)
     }
 }
 
+// ---- small calls: the tagged ring --------------------------------------
+// A small call (one workgroup per task, so every chunk is staged once)
+// whose segments are all 16-byte aligned hands off through tagged words
+// instead of slot counts. Its piece's place in the tag region holds one
+// 64-bit pair per staged 4-byte word: the word in the low half, the call's
+// sequence number in the high half, written by one agent-scope 64-bit store
+// (a naturally aligned 64-bit access is single-copy atomic, and the
+// agent-scope policy writes it through the producer's L2). The notify is
+// the tag itself: a consumer that loads a pair carrying this call's number
+// (agent scope: never a stale L2 line) has that word. The producer neither
+// waits for its stores nor counts; the consumer polls its own pairs instead
+// of a count, and reads no ring after it. Each consumer then clears the
+// pairs it took, so the region keeps no pair with the call's number: a
+// replay of a captured call, which keeps its number, waits for its own
+// producers. Pairs that a consumer which gave up left behind carry that
+// call's number, which no later call takes until the numbers start over,
+// when the host clears the region (launch_clear_tags).
+//
+// Pairs are laid out so that one instruction of a wave moves 64 adjacent
+// pairs: word j of vector v of a piece is pair 256 * (v / 64) + 64 * j +
+// v mod 64 of the piece's place (a piece is a multiple of 1 KiB, so its
+// pairs stay inside its own place). Each wave polls on its own, with no
+// barrier inside a loop; a wave's loop exits on a ballot over its lanes, so
+// its lanes leave together. Waits are bounded as in the persistent kernel.
+constexpr int kTagVecs = 2;   // 16-byte vectors per lane per round
+// A waiting lane polls all four words of its vectors while the call has at
+// most this many consumer tasks; with more, it polls only each vector's
+// first word and loads the other three once that word carries the tag, so
+// that the polls of many waiting consumers do not crowd the producers'
+// stores. Measured on MI355X, back to back, all words / first word: the
+// staged AllGather of 8 x 8 KiB 4.93 / 5.16 us, AllReduce of 8 x 16 KiB
+// 4.98 / 5.49 us (16 consumers); AllGather of 8 x 64 KiB 6.10 / 5.98 us
+// (64), of 8 x 128 KiB 7.3 / 6.78 us (128).
+constexpr int64_t kTagPollAllTasks = 32;
+
+__device__ __forceinline__ int64_t tag_pair(int64_t v, int j)
+{
+    return ((v >> 6) << 8) + (j << 6) + (v & 63);
+}
+
+template <class Stage, int MAXT>
+__global__ __launch_bounds__(MAXT) void k_snac_tagged(const SnacArgs a)
+{
+    touch_arg_lines(&a.src[0], &a.src[8], &a.dst[0], &a.dst[8], &a.ring, &a.chunk_bytes,
+                    &a.jitter_seed, &a.cnt[4], &a.elem[0], &a.head[0]);
+    const long long t_begin = wall_clock64();
+    const int64_t t = blockIdx.x;
+    if (t >= a.ntasks)
+        return;
+    const Task task = decode_task(a, t);
+    int s;
+    int64_t c;
+    chunk_of(a, task.chunk, &s, &c);
+    const SegGeo g = seg_geo(a, s);
+    const int64_t C = a.chunk_bytes;
+    const int64_t cbeg = c * C;
+    const int64_t clen = (g.bytes - cbeg < C) ? g.bytes - cbeg : C;
+    const int64_t pbeg = task.piece * a.piece_bytes;
+    int64_t plen = clen - pbeg;
+    plen = plen < 0 ? 0 : (plen > a.piece_bytes ? a.piece_bytes : plen);
+    unsigned long long* const pairs = a.tags + (task.chunk * C + pbeg) / 4;
+    const uint32_t seq = a.seq;
+    const unsigned long long tag = static_cast<unsigned long long>(seq) << 32;
+    if (a.jitter_ticks > 0) {
+        jitter(a, t, task.produce ? 2u : 1u);
+        __syncthreads();
+    }
+    const int lane = threadIdx.x;
+    const int64_t nthr = blockDim.x;
+    // vectors of the piece; a last vector that runs past the segment is
+    // staged whole (its load stays inside the 16-byte block of the
+    // segment's last byte) and only its piece bytes are written out
+    const int64_t nv = (plen + kVecBytes - 1) / kVecBytes;
+    bool ok = true;
+    long long t_wait = t_begin;
+    if (task.produce) {
+        for (int64_t v0 = 0; v0 < nv; v0 += nthr * kTagVecs) {
+            u32x4 x[kTagVecs];
+#pragma unroll
+            for (int u = 0; u < kTagVecs; ++u) {
+                const int64_t v = v0 + u * nthr + lane;
+                if (v < nv)
+                    x[u] = Stage::stage_vec(a, g, cbeg + pbeg + v * kVecBytes);
+            }
+#pragma unroll
+            for (int u = 0; u < kTagVecs; ++u) {
+                const int64_t v = v0 + u * nthr + lane;
+                if (v < nv) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        __hip_atomic_store(pairs + tag_pair(v, j), tag | x[u][j], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+        }
+    } else {
+        const bool nt = a.nt_store != 0;
+        const int q0 = g.dst < 0 ? 0 : g.dst;
+        const int q1 = g.dst < 0 ? a.P : g.dst + 1;
+        const int64_t dst_off = g.dst_off + cbeg + pbeg;
+        const bool all_words = a.nchunks * a.pieces <= kTagPollAllTasks;
+        for (int64_t v0 = 0; v0 < nv && ok; v0 += nthr * kTagVecs) {
+            unsigned long long w[kTagVecs][4];
+#pragma unroll
+            for (int u = 0; u < kTagVecs; ++u) {
+                const int64_t v = v0 + u * nthr + lane;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    w[u][j] = v >= nv ? tag
+                              : (j == 0 || all_words)
+                                  ? __hip_atomic_load(pairs + tag_pair(v, j), __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT)
+                                  : 0ull;    // not yet loaded (no call's tag is 0)
+            }
+            long long w0 = 0;
+            for (unsigned int it = 0;; ++it) {
+                bool ready = true;
+#pragma unroll
+                for (int u = 0; u < kTagVecs; ++u)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        ready = ready && static_cast<uint32_t>(w[u][j] >> 32) == seq;
+                if (__builtin_amdgcn_ballot_w64(!ready) == 0)
+                    break;
+                if (it == 0)
+                    w0 = wall_clock64();
+                if (it < 8)
+                    __builtin_amdgcn_s_sleep(1);
+                else
+                    __builtin_amdgcn_s_sleep(8);
+                if ((it & 15u) == 15u) {
+                    const long long now = wall_clock64();
+                    const uint32_t err = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(
+                        __hip_atomic_load(a.error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))));
+                    if (err == seq || now - w0 > a.wait_ticks || now - t_begin > a.budget_ticks) {
+                        if ((threadIdx.x & 63) == 0)
+                            __hip_atomic_store(a.error, seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        ok = false;
+                        break;
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kTagVecs; ++u) {
+                    const int64_t v = v0 + u * nthr + lane;
+                    const bool first = static_cast<uint32_t>(w[u][0] >> 32) == seq;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (v < nv && static_cast<uint32_t>(w[u][j] >> 32) != seq &&
+                            (j == 0 || first || all_words))
+                            w[u][j] = __hip_atomic_load(pairs + tag_pair(v, j), __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+            if (!ok)
+                break;
+            if (v0 == 0)
+                t_wait = wall_clock64();
+#pragma unroll
+            for (int u = 0; u < kTagVecs; ++u) {
+                const int64_t v = v0 + u * nthr + lane;
+                if (v >= nv)
+                    continue;
+                const u32x4 x = {static_cast<uint32_t>(w[u][0]), static_cast<uint32_t>(w[u][1]),
+                                 static_cast<uint32_t>(w[u][2]), static_cast<uint32_t>(w[u][3])};
+                const int64_t o = v * kVecBytes;
+                if (o + kVecBytes <= plen) {
+                    for (int q = q0; q < q1; ++q)
+                        st16(static_cast<char*>(a.dst[q]) + dst_off, static_cast<uint32_t>(o), x, nt);
+                } else {
+                    // the segment's last, partial vector
+                    for (int q = q0; q < q1; ++q) {
+                        uint16_t* d = reinterpret_cast<uint16_t*>(static_cast<char*>(a.dst[q]) + dst_off + o);
+                        for (int h = 0; h < (plen - o) / 2; ++h)
+                            d[h] = static_cast<uint16_t>(x[h >> 1] >> (16 * (h & 1)));
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    __hip_atomic_store(pairs + tag_pair(v, j), 0ull, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+    if (a.trace) {
+        // measurement hook: this task's stamps, taken when every wave is done
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            unsigned long long* e = a.trace + 4 * t;
+            e[0] = static_cast<unsigned long long>(t_begin);
+            e[1] = static_cast<unsigned long long>(t_wait);
+            e[2] = static_cast<unsigned long long>(wall_clock64());
+            e[3] = static_cast<unsigned long long>(blockIdx.x) |
+                   (static_cast<unsigned long long>(task.produce) << 32) |
+                   (static_cast<unsigned long long>(!ok) << 33);
+        }
+    }
+}
+
 // The reducing stage keeps P * UP loads in flight per lane: UP = 2 up to
 // P = 8, 1 for more inputs.
 template <typename T, int MAXT>
@@ -767,6 +983,23 @@ hipError_t launch_reduce_t(const SnacArgs& a, dim3 grid, dim3 block, hipStream_t
     ATOM_SNAC_RED_CASE(9) ATOM_SNAC_RED_CASE(10) ATOM_SNAC_RED_CASE(11) ATOM_SNAC_RED_CASE(12)
     ATOM_SNAC_RED_CASE(13) ATOM_SNAC_RED_CASE(14) ATOM_SNAC_RED_CASE(15) ATOM_SNAC_RED_CASE(16)
 #undef ATOM_SNAC_RED_CASE
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// The tagged kernels are built for up to 512 lanes (the staged default).
+template <typename T>
+hipError_t launch_tagged_reduce_t(const SnacArgs& a, dim3 grid, dim3 block, hipStream_t stream)
+{
+    switch (a.P) {
+#define ATOM_SNAC_TAG_CASE(PP)                                                                  \
+    case PP: k_snac_tagged<StageReduce<T, PP>, 512><<<grid, block, 0, stream>>>(a); break;
+    ATOM_SNAC_TAG_CASE(1) ATOM_SNAC_TAG_CASE(2) ATOM_SNAC_TAG_CASE(3) ATOM_SNAC_TAG_CASE(4)
+    ATOM_SNAC_TAG_CASE(5) ATOM_SNAC_TAG_CASE(6) ATOM_SNAC_TAG_CASE(7) ATOM_SNAC_TAG_CASE(8)
+    ATOM_SNAC_TAG_CASE(9) ATOM_SNAC_TAG_CASE(10) ATOM_SNAC_TAG_CASE(11) ATOM_SNAC_TAG_CASE(12)
+    ATOM_SNAC_TAG_CASE(13) ATOM_SNAC_TAG_CASE(14) ATOM_SNAC_TAG_CASE(15) ATOM_SNAC_TAG_CASE(16)
+#undef ATOM_SNAC_TAG_CASE
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -788,15 +1021,16 @@ hipError_t launch_copy_t(const SnacArgs& a, int U, dim3 grid, dim3 block, hipStr
 // ---- the fixed workspace of atom_collective_noalloc ---------------------
 // Flags (the slot count words, the ticket, the error word and the
 // finished-workgroup count, each on its own 256-byte line, as in the
-// allocated workspace) followed by a ring of kStaticRingBytes. Each device
-// holds its own copy from the library's load until the process ends.
+// allocated workspace), the tagged ring of small calls (kTagBytes), then a
+// ring of kStaticRingBytes. Each device holds its own copy from the
+// library's load until the process ends.
 constexpr int64_t kFlagLine = kFlagStride * sizeof(unsigned long long);
 constexpr int64_t kStaticFlagBytes = 64 << 10;
 static_assert((kMaxSlots + 3) * kFlagLine <= kStaticFlagBytes, "flags do not fit");
 // The ring part also holds each slot's padding (kSlotPad), so that a ring of
 // kStaticRingBytes of chunks fits at any depth up to kMaxSlots.
 constexpr int64_t kStaticRingAlloc = kStaticRingBytes + kMaxSlots * kSlotPad;
-static __device__ __align__(256) char scratch[kStaticFlagBytes + kStaticRingAlloc];
+static __device__ __align__(256) char scratch[kStaticFlagBytes + kTagBytes + kStaticRingAlloc];
 
 __global__ void k_clear_words(unsigned long long* p, int64_t n)
 {
@@ -832,8 +1066,8 @@ atom_status static_workspace(hipStream_t stream, Workspace** out, hipError_t* hi
             return ATOM_ERR_HIP;
         if (khz <= 0)
             return ATOM_ERR_UNSUPPORTED;
-        k_clear_words<<<16, 256, 0, stream>>>(reinterpret_cast<unsigned long long*>(ptr),
-                                              kStaticFlagBytes / 8);
+        k_clear_words<<<64, 256, 0, stream>>>(reinterpret_cast<unsigned long long*>(ptr),
+                                              (kStaticFlagBytes + kTagBytes) / 8);
         if ((*hip_err = hipGetLastError()) != hipSuccess)
             return ATOM_ERR_HIP;
         ws.wall_khz = khz;
@@ -841,13 +1075,26 @@ atom_status static_workspace(hipStream_t stream, Workspace** out, hipError_t* hi
         ws.ticket = reinterpret_cast<unsigned int*>(ptr + kMaxSlots * kFlagLine);
         ws.error = reinterpret_cast<unsigned int*>(ptr + (kMaxSlots + 1) * kFlagLine);
         ws.done = reinterpret_cast<unsigned int*>(ptr + (kMaxSlots + 2) * kFlagLine);
+        ws.tags = reinterpret_cast<unsigned long long*>(ptr + kStaticFlagBytes);
         ws.ring_bytes = kStaticRingAlloc;
-        ws.ring = ptr + kStaticFlagBytes;
+        ws.ring = ptr + kStaticFlagBytes + kTagBytes;
     }
-    if (++ws.seq == 0)
+    if (++ws.seq == 0) {
+        // the numbers start over: no stale pair may carry one of them
         ws.seq = 1;
+        if ((*hip_err = launch_clear_tags(ws, stream)) != hipSuccess)
+            return ATOM_ERR_HIP;
+    }
     *out = &ws;
     return ATOM_OK;
+}
+
+hipError_t launch_clear_tags(const Workspace& ws, hipStream_t stream)
+{
+    if (!ws.tags)
+        return hipErrorInvalidValue;
+    k_clear_words<<<64, 256, 0, stream>>>(ws.tags, kTagBytes / 8);
+    return hipGetLastError();
 }
 
 unsigned int* static_error_word(int dev)
@@ -867,8 +1114,13 @@ hipError_t launch_snac(const Plan& p, const Workspace& ws, uint32_t seq, hipStre
         p.sa.nseg > kMaxSegs || ws.wall_khz <= 0 || p.wg < 64 || p.wg > 512 || p.wg % 64 != 0 ||
         !ws.done || seq == 0)
         return hipErrorInvalidValue;
+    if (p.sa.tagged && (!ws.tags || !p.sa.static_tasks || p.grid != p.sa.ntasks ||
+                        2 * p.sa.nchunks * p.sa.chunk_bytes > kTagBytes ||
+                        p.sa.piece_bytes % 1024 != 0 || p.sa.chunk_bytes % p.sa.piece_bytes != 0))
+        return hipErrorInvalidValue;
     SnacArgs a = p.sa;
     a.ring = ws.ring;
+    a.tags = ws.tags;
     a.counts = ws.counts;
     a.ticket = ws.ticket;
     a.error = ws.error;
@@ -883,6 +1135,14 @@ hipError_t launch_snac(const Plan& p, const Workspace& ws, uint32_t seq, hipStre
     const dim3 grid(static_cast<unsigned>(p.grid)), block(static_cast<unsigned>(p.wg));
     const bool wide = p.wg > 256;
     const bool bf = p.dtype == DT_BF16;
+    if (a.tagged) {
+        if (p.exec == EX_SNAC_COPY) {
+            k_snac_tagged<StageCopy, 512><<<grid, block, 0, stream>>>(a);
+            return hipGetLastError();
+        }
+        return bf ? launch_tagged_reduce_t<uint16_t>(a, grid, block, stream)
+                  : launch_tagged_reduce_t<float>(a, grid, block, stream);
+    }
     if (p.exec == EX_SNAC_COPY) {
         if (bf)
             return wide ? launch_copy_t<uint16_t, 512>(a, p.U, grid, block, stream)

@@ -13,6 +13,7 @@ struct Workspace {
     char* ring = nullptr;
     int64_t ring_bytes = 0;
     unsigned long long* counts = nullptr;  // kMaxSlots slot counts, kFlagStride apart
+    unsigned long long* tags = nullptr;    // tagged ring of small calls, kTagBytes
     unsigned int* ticket = nullptr;
     unsigned int* error = nullptr;         // last timed-out call's sequence number
     unsigned int* done = nullptr;
@@ -36,6 +37,10 @@ hipError_t launch_copy(const Plan& p, hipStream_t stream);
 // seq: the call's sequence number (nonzero), recorded in the error word if
 // one of its waits times out.
 hipError_t launch_snac(const Plan& p, const Workspace& ws, uint32_t seq, hipStream_t stream);
+// Zeroes the workspace's tagged ring on `stream` (a kernel, so it may be
+// captured): done when the sequence numbers wrap, so that no pair left by a
+// call whose consumer gave up carries a number a later call takes.
+hipError_t launch_clear_tags(const Workspace& ws, hipStream_t stream);
 hipError_t launch_moe_route(const MoeRoutePlan& p, hipStream_t stream);
 hipError_t launch_moe_move(const MoeMovePlan& p, bool combine, hipStream_t stream);
 

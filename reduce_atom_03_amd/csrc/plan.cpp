@@ -98,7 +98,7 @@ atom_status read_cfg(const atom_config* cfg, Cfg* c)
     if (cfg->num_wgs < 0)
         return ATOM_ERR_INVALID_ARG;
     c->num_wgs = std::min<int64_t>(cfg->num_wgs, kMaxGrid);
-    if (cfg->flags & ~(ATOM_F_STAGED | ATOM_F_NO_NT | ATOM_F_XCD_ORDER))
+    if (cfg->flags & ~(ATOM_F_STAGED | ATOM_F_NO_NT | ATOM_F_XCD_ORDER | ATOM_F_COUNTED))
         return ATOM_ERR_INVALID_ARG;
     c->flags = cfg->flags;
     if (cfg->ring_slots != 0) {
@@ -755,6 +755,17 @@ atom_status build_snac(Plan* p, int32_t sk, int P, void* const* ins, void* const
     // bounded either way. Saves the ticket atomic's round trip before the
     // first task and after the last.
     a.static_tasks = (!c.num_wgs && p->grid == a.ntasks && a.ntasks <= kSnacStaticTasks) ? 1 : 0;
+    // A small call stages each chunk once (its grid holds every task, so
+    // the ring holds every chunk). When every segment is 16-byte aligned
+    // and the staged bytes fit the tagged ring, the notify travels in the
+    // staged words' tags (k_snac_tagged): the producer neither waits for
+    // its stores to complete nor counts, and the consumer reads its words
+    // as it sees them instead of reading the ring after a count.
+    bool tag_ok = a.static_tasks && !(c.flags & ATOM_F_COUNTED) && piece % 1024 == 0 &&
+                  chunk % piece == 0 && 2 * q * chunk <= kTagBytes;
+    for (int s = 0; s < nseg && tag_ok; ++s)
+        tag_ok = bytes[s] == 0 || (a.elem[s] == SE_VEC && a.head[s] == 0);
+    a.tagged = tag_ok ? 1 : 0;
     p->exec = reduce ? EX_SNAC_REDUCE : EX_SNAC_COPY;
     return ATOM_OK;
 }
@@ -1285,6 +1296,7 @@ void plan_fill_info(const Plan& p, atom_plan_info* info)
     const bool staged = p.exec == EX_SNAC_COPY || p.exec == EX_SNAC_REDUCE;
     info->snac_lead = staged ? p.sa.lead : 0;
     info->snac_tasks = staged ? p.sa.ntasks : 0;
+    info->snac_tagged = staged ? p.sa.tagged : 0;
     switch (p.exec) {
     case EX_REDUCE: info->streaming_stores = p.ra.nt_store; break;
     case EX_COPY: info->streaming_stores = p.ca.nt_store; break;

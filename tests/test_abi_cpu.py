@@ -608,3 +608,49 @@ def test_staged_segments_at_a_common_offset_stay_vectorized():
     st, info = Q(A.PARTITIONED, A.SHARD, A.OP_SUM, P=P, n=n, cfg=A.config(flags=A.F_STAGED),
                  ins=ins, outs=fake(P, n * 2, start=BASE + (1 << 36)))
     assert st == A.OK and info.staged == 1 and info.vector_path == 0
+
+
+def test_small_aligned_staged_calls_hand_off_through_tagged_words():
+    """A small staged call (one workgroup per task) whose segments are all
+    16-byte aligned hands off through tagged words; ATOM_F_COUNTED, any
+    segment off alignment, a ticketed launch (a ring too short to hold every
+    chunk, or a caller's grid) or more than 1 MiB staged keep the slot
+    counts."""
+    P = 8
+
+    def ag(n, cfg, off_in=0, off_out=0):
+        return Q(A.SHARD, A.GATHERED, A.OP_COPY, P=P, n=n, cfg=cfg,
+                 ins=fake(P, n * 2, align_off=off_in),
+                 outs=fake(P, P * n * 2, start=BASE + (1 << 36), align_off=off_out))
+
+    for n in (4096, 65536):          # 8 KiB and 128 KiB per rank
+        st, info = ag(n, A.config(flags=A.F_STAGED))
+        assert st == A.OK and info.staged == 1 and info.snac_tagged == 1, n
+        assert info.num_wgs == info.snac_tasks <= 256
+        st, info = ag(n, A.config(flags=A.F_STAGED | A.F_COUNTED))
+        assert st == A.OK and info.staged == 1 and info.snac_tagged == 0
+        assert info.num_wgs == info.snac_tasks                 # still one workgroup per task
+    for reduce_coll in ((A.PARTITIONED, A.GATHERED), (A.PARTITIONED, A.SHARD)):
+        st, info = Q(*reduce_coll, A.OP_SUM, P=P, n=512, cfg=A.config(flags=A.F_STAGED))
+        assert st == A.OK and info.snac_tagged == 1, reduce_coll
+    st, info = Q(A.PARTITIONED, A.GATHERED, A.OP_SUM, P=P, n=512, dtype=A.DT_F32,
+                 cfg=A.config(flags=A.F_STAGED))
+    assert st == A.OK and info.snac_tagged == 1
+    # off alignment (common offset, or shifted): the slot counts
+    assert ag(4096, A.config(flags=A.F_STAGED), 2, 2)[1].snac_tagged == 0
+    assert ag(4096, A.config(flags=A.F_STAGED), 0, 2)[1].snac_tagged == 0
+    # the ticket: a 2-slot ring, or a caller's grid
+    st, info = ag(4096, A.config(flags=A.F_STAGED, ring_slots=2))
+    assert st == A.OK and info.num_wgs < info.snac_tasks and info.snac_tagged == 0
+    st, info = ag(4096, A.config(flags=A.F_STAGED, num_wgs=16))
+    assert st == A.OK and info.snac_tagged == 0
+    # beyond the static task count (256 KiB per rank): the ticket
+    st, info = ag(131072, A.config(flags=A.F_STAGED))
+    assert st == A.OK and info.snac_tasks > 256 and info.snac_tagged == 0
+    # a caller's larger piece keeps the task count small but stages more than
+    # the tagged ring holds (8 x 256 KiB = 2 MiB)
+    st, info = ag(131072, A.config(flags=A.F_STAGED, piece_bytes=64 << 10))
+    assert st == A.OK and info.num_wgs == info.snac_tasks and info.snac_tagged == 0
+    # zero staging ignores the flag
+    st, info = ag(4096, A.config(flags=A.F_COUNTED))
+    assert st == A.OK and info.staged == 0 and info.snac_tagged == 0

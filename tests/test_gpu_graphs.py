@@ -65,11 +65,23 @@ def test_captured_sequence_replays_match_the_oracle(A):
     o_moe = [buf(T * H) for _ in range(P)]
     rt = A.moe_alloc_routing(ids_dev, E, k)
     snac = A.config(flags=A.F_STAGED, chunk_bytes=64 << 10, ring_slots=2)
+    # small staged calls on the tagged ring: every replay keeps the captured
+    # sequence number, so each must wait for its own producers
+    small = A.config(flags=A.F_STAGED)
+    n_sm = 4096
+    o_sm = [buf(P * n_sm) for _ in range(P)]
+    m_sm = 512                           # small staged AllReduce: 8 x 512 per rank
+    assert P * m_sm <= P * n_dec
+    o_smr = [buf(P * m_sm) for _ in range(P)]
     L = A.layout
     lay = {
         "dec": (L(A.PARTITIONED, x_dec, n_dec), L(A.GATHERED, o_dec, n_dec), A.OP_SUM, None),
         "ag": (L(A.SHARD, z_ag, S_ag // 2), L(A.GATHERED, o_ag, S_ag // 2), A.OP_COPY, None),
         "snac": (L(A.SHARD, z_ag, S_ag // 2), L(A.GATHERED, o_sn, S_ag // 2), A.OP_COPY, snac),
+        "small": (L(A.SHARD, [z[:n_sm] for z in z_ag], n_sm), L(A.GATHERED, o_sm, n_sm), A.OP_COPY,
+                  small),
+        "smallr": (L(A.PARTITIONED, [x[:P * m_sm] for x in x_dec], m_sm), L(A.GATHERED, o_smr, m_sm),
+                   A.OP_SUM, small),
         "rs": (L(A.PARTITIONED, x_rs, n_rs), L(A.SHARD, y_rs, n_rs), A.OP_SUM, None),
         "a2": (L(A.PARTITIONED, x_a2, 0, C, 128), L(A.TRANSPOSED, o_a2, 0, None, 128), A.OP_COPY,
                None),
@@ -113,6 +125,12 @@ def test_captured_sequence_replays_match_the_oracle(A):
         for j in range(P):
             assert_bits_equal(from_dev(o_ag[j]), want[j], f"{what}: AllGather {j}")
             assert_bits_equal(from_dev(o_sn[j]), want[j], f"{what}: SNAC AllGather {j}")
+        want = oracle.all_gather([a[:n_sm] for a in inp["ag"]])
+        for j in range(P):
+            assert_bits_equal(from_dev(o_sm[j]), want[j], f"{what}: small staged AllGather {j}")
+        want = oracle.all_reduce([a[:P * m_sm] for a in inp["dec"]])
+        for j in range(P):
+            assert_bits_equal(from_dev(o_smr[j]), want[j], f"{what}: small staged AllReduce {j}")
         want = oracle.reduce_scatter(inp["rs"])
         for k_ in range(P):
             assert_bits_equal(from_dev(y_rs[k_]), want[k_], f"{what}: ReduceScatter {k_}")

@@ -340,53 +340,95 @@ def test_timeout_is_reported_and_only_its_call_is_incomplete(A):
                           nan_by_class=False)
 
 
+@pytest.mark.parametrize("counted", [False, True])
 @pytest.mark.parametrize("coll,n", [("ag", 4096), ("ar", 512)])
-def test_small_call_timeout_leaves_clean_counts(A, coll, n):
+def test_small_call_timeout_leaves_clean_counts(A, coll, n, counted):
     """A small staged call (one workgroup per task, no ticket) clears each
     slot's count word in the task that completes it, and every task counts,
-    also one whose wait gave up. Forced from the host: a 20 us wait bound
+    also one whose wait gave up; on the tagged ring (the default for such a
+    call), a consumer that gave up leaves its words with that call's tag,
+    which no later call takes. Forced from the host: a 20 us wait bound
     against notifies and consumes held up to 3 ms. The call reports the
     timeout; the same call without the delay, issued right after it and
     before the status check, and then the call on a 2-slot ring (ticket),
     must both be complete and correct."""
     P = 8
+    flags = A.F_STAGED | (A.F_COUNTED if counted else 0)
     c = Case(A, coll, P, n, synth.BF16, 0, seed=60)
-    info = c.plan(A.config(flags=A.F_STAGED))
-    say(f"small {coll} n={n} forced to time out, tasks={info.snac_tasks} wgs={info.num_wgs}")
+    info = c.plan(A.config(flags=flags))
+    say(f"small {coll} n={n} counted={counted} forced to time out, tasks={info.snac_tasks} "
+        f"wgs={info.num_wgs}")
     assert info.num_wgs == info.snac_tasks             # one workgroup per task, no ticket
-    c.run(A.config(flags=A.F_STAGED, wait_us=20, jitter_us=3000, jitter_seed=11))
-    c.run(A.config(flags=A.F_STAGED))
+    assert info.snac_tagged == (0 if counted else 1)
+    c.run(A.config(flags=flags, wait_us=20, jitter_us=3000, jitter_seed=11))
+    c.run(A.config(flags=flags))
     assert A.atom_sync_status() == A.ERR_TIMEOUT
     assert A.atom_sync_status() == A.OK
     c.check(f"small {coll} after a timed-out call")
-    c.run(A.config(flags=A.F_STAGED, ring_slots=2))
+    c.run(A.config(flags=flags, ring_slots=2))
     _check_status(A, f"small {coll} ring of 2 after the timeout")
     c.check(f"small {coll} ring of 2 after the timeout")
 
 
+@pytest.mark.parametrize("counted", [False, True])
 @pytest.mark.parametrize("coll,n", [("ag", 4096), ("ar", 512), ("ag", 32768), ("rs", 4096),
                                     ("a2av", 1200), ("rsv", 3000)])
 @pytest.mark.parametrize("slots", [1, 2, 64])
-def test_small_calls_without_ticket(A, coll, n, slots):
+def test_small_calls_without_ticket(A, coll, n, slots, counted):
     """Small staged calls (at most 256 tasks, one workgroup each: the default
-    64-slot ring) run task blockIdx.x with no ticket; rings of 1 and 2 slots
+    64-slot ring) run task blockIdx.x with no ticket, on the tagged ring
+    unless ATOM_F_COUNTED asks for the slot counts; rings of 1 and 2 slots
     hold fewer pieces than there are tasks, so the same calls there run
     fewer workgroups on the ticket. Each is checked at natural timing and
     with every notify and consume delayed by a pseudo-random 0-40 us, bit for
     bit against the oracle, twice in a row."""
     P = 8
     c = Case(A, coll, P, n, synth.BF16, 0, seed=40 + slots)
-    base = dict(flags=A.F_STAGED, ring_slots=slots)
+    base = dict(flags=A.F_STAGED | (A.F_COUNTED if counted else 0), ring_slots=slots)
     info = c.plan(A.config(**base))
-    say(f"small {coll} n={n} slots={slots} tasks={info.snac_tasks} wgs={info.num_wgs}")
+    say(f"small {coll} n={n} slots={slots} counted={counted} tasks={info.snac_tasks} "
+        f"wgs={info.num_wgs} tagged={info.snac_tagged}")
     assert 0 < info.snac_tasks <= 256
     if slots < 64:
         assert info.num_wgs < info.snac_tasks          # the ticket
+        assert info.snac_tagged == 0
     elif coll != "a2av":
         assert info.num_wgs == info.snac_tasks         # one workgroup per task, no ticket
+    if counted or info.num_wgs < info.snac_tasks:
+        assert info.snac_tagged == 0
+    elif coll in ("ag", "ar", "rs"):
+        assert info.snac_tagged == 1                   # every segment 16-byte aligned
     for jit in (0, 40):
         for rep in range(2):
             cfg = A.config(**base, jitter_us=jit, jitter_seed=7 + rep)
             c.run(cfg)
             _check_status(A, f"small {coll} jitter={jit}")
             c.check(f"small {coll} n={n} slots={slots} jitter={jit} rep={rep}")
+
+
+def test_tagged_calls_back_to_back(A):
+    """Small staged calls on the tagged ring, back to back and interleaved
+    with calls that reuse the same workspace through the slot counts (small
+    ones with ATOM_F_COUNTED, and a large AllGather that fills the ring with
+    other bytes): every call must wait for its own producers, whatever an
+    earlier call left in the tagged ring or the ring. Each result is checked
+    bit for bit against the oracle; the status is checked at the end."""
+    P = 8
+    cases = [Case(A, coll, P, n, dt, 0, seed=70 + i)
+             for i, (coll, n, dt) in enumerate([("ag", 4096, synth.BF16), ("ar", 512, synth.BF16),
+                                                ("rs", 4096, synth.F32), ("a2a", 512, synth.BF16),
+                                                ("ag", 65536, synth.BF16), ("rsv", 3000, synth.BF16),
+                                                ("ag", 1000, synth.F32)])]
+    big = Case(A, "ag", P, 1 << 20, synth.BF16, 0, seed=79)
+    tagged = [c.plan(A.config(flags=A.F_STAGED)).snac_tagged for c in cases]
+    say(f"tagged back to back: tagged={tagged}")
+    assert sum(tagged) >= 5
+    for rep in range(3):
+        for i, c in enumerate(cases):
+            c.run(A.config(flags=A.F_STAGED))
+            c.check(f"rep {rep} case {i} {c.coll} tagged")
+            c.run(A.config(flags=A.F_STAGED | A.F_COUNTED))
+            c.check(f"rep {rep} case {i} {c.coll} counted")
+        big.run(A.config(flags=A.F_STAGED))
+        big.check(f"rep {rep} large staged AllGather")
+    _check_status(A, "tagged back to back")

@@ -32,10 +32,22 @@ def asm(tmp_path_factory):
 
 
 def _kernels(text):
-    """(name, body) of every k_snac kernel in the assembly."""
+    """(name, body) of every persistent k_snac kernel in the assembly."""
     out = []
     for m in re.finditer(r"^(_Z\S*k_snac\S*):", text, re.M):
+        if "k_snac_tagged" in m.group(1):
+            continue
         end = text.find("s_endpgm", m.end())
+        out.append((m.group(1), text[m.end():end]))
+    return out
+
+
+def _tagged_kernels(text):
+    """(name, whole body) of every k_snac_tagged kernel (small calls on the
+    tagged ring)."""
+    out = []
+    for m in re.finditer(r"^(_Z\S*k_snac_tagged\S*):", text, re.M):
+        end = text.find(".Lfunc_end", m.end())
         out.append((m.group(1), text[m.end():end]))
     return out
 
@@ -128,3 +140,55 @@ def test_producer_waits_for_its_stores_before_notify(asm):
         wait = re.search(r"s_waitcnt vmcnt\(0\)", rest)
         barrier = re.search(r"s_barrier", rest)
         assert wait and barrier and wait.start() < barrier.start(), name
+
+
+def test_every_tagged_kernel_is_present(asm):
+    names = [n for n, _ in _tagged_kernels(asm)]
+    assert sum("StageCopy" in n for n in names) == 1
+    # 2 dtypes x P = 1..16, built for up to 512 lanes
+    assert sum("StageReduce" in n for n in names) == 32
+
+
+def _blocks(body):
+    """(label line, instructions) of each basic block; the compiler marks a
+    block that belongs to a loop in its label's comment ("Loop Header",
+    "in Loop: Header=...", "Parent Loop ...")."""
+    out, cur = [], None
+    for line in body.splitlines():
+        if re.match(r"^\.LBB\w+:", line):
+            cur = [line, []]
+            out.append(cur)
+        elif cur is not None:
+            cur[1].append(line)
+    return out
+
+
+def test_tagged_kernels_have_no_barrier_in_a_loop(asm):
+    """The tagged kernel's waves poll on their own: the only barriers (the
+    test hooks' jitter and clock stamps) sit in blocks that belong to no
+    loop, so a wave that leaves a loop early can never hold up another at a
+    barrier."""
+    for name, body in _tagged_kernels(asm):
+        assert "s_barrier" in body, name
+        for label, ins in _blocks(body):
+            if "Loop" in label:
+                assert not any("s_barrier" in i for i in ins), f"{name}: a barrier inside a loop: {label}"
+
+
+def test_tagged_words_are_agent_coherent(asm):
+    """Every access to the tagged ring is a 64-bit agent-scope (sc1) load or
+    store (single-copy atomic: a word and its tag are seen together; written
+    through the L2, never read from a stale L2 line), the error word's too;
+    no L2 write-back or invalidation; no ring (buffer) loads at all. Inputs
+    are read with streaming loads, outputs written with stores without sc0
+    or sc1."""
+    for name, body in _tagged_kernels(asm):
+        assert not re.search(r"buffer_wbl2|buffer_inv|buffer_load", body), name
+        pairs = re.findall(r"^\s*(global_(?:load|store)_dwordx2[^\n]*)", body, re.M)
+        assert any("load" in op for op in pairs) and any("store" in op for op in pairs), name
+        for op in pairs + re.findall(r"^\s*(global_(?:load|store)_dword\s[^\n]*)", body, re.M):
+            assert re.search(r"\bsc1\b", op), f"{name}: tag or error access without sc1: {op}"
+        for op in re.findall(r"^\s*(global_load_dwordx4[^\n]*)", body, re.M):
+            assert re.search(r"\bnt\b", op), f"{name}: input load that is not streaming: {op}"
+        for op in re.findall(r"^\s*((?:buffer|global)_store_(?:dwordx4|short)[^\n]*)", body, re.M):
+            assert not re.search(r"\bsc[01]\b", op), f"{name}: output store with sc0/sc1: {op}"

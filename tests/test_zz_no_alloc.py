@@ -119,3 +119,44 @@ def test_noalloc_zero_staging_and_limits(A):
     assert A.atom_collective_noalloc(li, lo, A.OP_COPY, one, check=False) == A.OK
     assert A.atom_sync_status() == A.OK
     assert A.NOALLOC_RING_BYTES == 16 << 20
+
+
+@pytest.mark.parametrize("counted", [False, True])
+def test_noalloc_small_staged_calls_match(A, counted):
+    """Small staged calls (one workgroup per task), which hand off through
+    the tagged ring of the fixed array unless ATOM_F_COUNTED asks for the
+    slot counts: an AllGather and an AllReduce, two calls each with the
+    second smaller, equal to atom_collective and to the oracle bit for
+    bit."""
+    P = 8
+    cfg = A.config(flags=A.F_STAGED | (A.F_COUNTED if counted else 0))
+    for call, n in enumerate((32768, 4096)):
+        say(f"noalloc small staged AG/AR call {call} n={n} counted={counted}")
+        zs = [synth.mixed_bits(920 + call, k, n, synth.BF16) for k in range(P)]
+        dz = [to_dev(z)[1] for z in zs]
+        lin = A.layout(A.SHARD, dz, n)
+
+        def mk_ag():
+            outs = [empty_dev(P * n, _bf16(), 0xFFFF) for _ in range(P)]
+            return A.layout(A.GATHERED, outs, n), outs
+        st, info = A.atom_plan_query(lin, mk_ag()[0], A.OP_COPY, cfg)
+        assert st == A.OK and info.snac_tagged == (0 if counted else 1)
+        got_a, got_b = _pair(A, lin, mk_ag, A.OP_COPY, cfg, "small AG")
+        want = oracle.all_gather(zs)
+        for j in range(P):
+            assert_bits_equal(got_b[j], got_a[j], f"small AG noalloc vs atom_collective out_{j}",
+                              nan_by_class=False)
+            assert_bits_equal(got_b[j], want[j], f"small AG noalloc vs oracle out_{j}",
+                              nan_by_class=False)
+        m = n // 8
+        xs = [synth.mixed_bits(930 + call, r, P * m, synth.BF16, specials=False) for r in range(P)]
+        dx = [to_dev(x)[1] for x in xs]
+
+        def mk_ar():
+            outs = [empty_dev(P * m, _bf16(), 0xFFFF) for _ in range(P)]
+            return A.layout(A.GATHERED, outs, m), outs
+        got_a, got_b = _pair(A, A.layout(A.PARTITIONED, dx, m), mk_ar, A.OP_SUM, cfg, "small AR")
+        want = oracle.all_reduce(xs)
+        for j in range(P):
+            assert_bits_equal(got_b[j], got_a[j], f"small AR noalloc vs atom_collective out_{j}")
+            assert_bits_equal(got_b[j], want[j], f"small AR noalloc vs oracle out_{j}")
