@@ -635,8 +635,8 @@ def snac_trace(A, synth, torch, dev):
     def q(x, p):
         return round(float(np.percentile(x, p)), 2) if x.size else None
 
-    def run(name, li, lo, op, reps=5, **kw):
-        cfg = A.config(flags=A.F_STAGED, **kw)
+    def run(name, li, lo, op, reps=5, flags=0, **kw):
+        cfg = A.config(flags=A.F_STAGED | flags, **kw)
         st, info = A.atom_plan_query(li, lo, op, cfg)
         assert st == A.OK and info.staged == 1, (name, st)
         n = int(info.snac_tasks)
@@ -645,7 +645,7 @@ def snac_trace(A, synth, torch, dev):
         fn()
         ms = timed(fn, reps)
         tr = torch.zeros(4 * n, dtype=torch.int64, device=dev)
-        tcfg = A.config(flags=A.F_STAGED, trace=tr.data_ptr(), **kw)
+        tcfg = A.config(flags=A.F_STAGED | flags, trace=tr.data_ptr(), **kw)
         tfn = lambda: A.atom_collective(li, lo, op, tcfg)
         ms_traced = timed(tfn, 1)
         assert A.atom_sync_status() == A.OK, name
@@ -734,12 +734,15 @@ def snac_trace(A, synth, torch, dev):
     ov = [torch.empty(T, dtype=torch.bfloat16, device=dev) for _ in range(P)]
     run("agv_zipf_512MiB", L(A.SHARD, zv, 0, cnt, 8), L(A.GATHERED, ov, 0, None, 8), A.OP_COPY)
     del zv, ov
-    # small calls: 8 KiB AllGather and AllReduce, default plans
+    # small calls: 8 KiB AllGather and AllReduce, default plans (tagged
+    # words), and through the slot counts
     z8 = [torch.empty(4096, dtype=torch.bfloat16, device=dev).uniform_(-1, 1) for _ in range(P)]
     o8 = [torch.empty(P * 4096, dtype=torch.bfloat16, device=dev) for _ in range(P)]
-    run("ag_8x8KiB", L(A.SHARD, z8, 4096), L(A.GATHERED, o8, 4096), A.OP_COPY, reps=200)
     x8 = [torch.randn(4096, device=dev).to(torch.bfloat16) for _ in range(P)]
-    run("ar_8x8KiB", L(A.PARTITIONED, x8, 512), L(A.GATHERED, o8, 512), A.OP_SUM, reps=200)
+    for sfx, fl in (("", 0), ("_counted", A.F_COUNTED)):
+        run("ag_8x8KiB" + sfx, L(A.SHARD, z8, 4096), L(A.GATHERED, o8, 4096), A.OP_COPY, reps=200, flags=fl)
+        run("ar_8x8KiB" + sfx, L(A.PARTITIONED, x8, 512), L(A.GATHERED, o8, 512), A.OP_SUM, reps=200,
+            flags=fl)
     del z8, o8, x8
     # AllGather 8 x 1 GiB: each chunk size
     S = 1024 * MiB
