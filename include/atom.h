@@ -145,13 +145,15 @@ typedef struct atom_layout {
 #define ATOM_F_XCD_ORDER 0x4u /* zero-staging kernels give each XCD one
                                  contiguous range of tiles (default: plain
                                  workgroup order; measured within noise) */
-#define ATOM_F_COUNTED 0x8u   /* staged calls: small calls, too, notify
-                                 through the ring slots' count words.
-                                 Default: a small staged call (one workgroup
-                                 per task, every segment 16-byte aligned, at
-                                 most 1 MiB staged) carries its notify in the
-                                 staged data itself: each staged 4-byte word
-                                 is written next to a tag holding the call's
+#define ATOM_F_COUNTED 0x8u   /* staged calls: always notify through the
+                                 ring slots' count words. Default: a staged
+                                 call whose ring holds every chunk (each
+                                 staged once), whose segments are all
+                                 16-byte aligned, which stages at most
+                                 8 MiB and sets no num_wgs carries its
+                                 notify in the staged
+                                 data itself: each staged 4-byte word is
+                                 written next to a tag holding the call's
                                  sequence number, by one 64-bit store, and
                                  the consumer waits for its words' tags
                                  (atom_plan_info.snac_tagged). Same results;
@@ -284,8 +286,9 @@ atom_status atom_reduce(void* dst, const void* const* srcs, int32_t nsrcs,
  * ordinary buffers): its layouts become a list of segments (the bytes one
  * source sends to one or every destination), chunks of cfg->chunk_bytes of
  * each are staged (copied, or reduced in rank order) in a ring of
- * cfg->ring_slots slots, notified through device-memory flags (a small call:
- * through a tag stored with each staged word, see ATOM_F_COUNTED) and
+ * cfg->ring_slots slots, notified through device-memory flags (a call that
+ * stages each chunk once: through a tag stored with each staged word, see
+ * ATOM_F_COUNTED) and
  * consumed by other workgroups; the result equals the zero-staging one bit
  * for bit.
  * Returns ATOM_OK, ATOM_ERR_INVALID_ARG, ATOM_ERR_UNSUPPORTED,
@@ -299,7 +302,7 @@ atom_status atom_collective(const atom_layout* in, const atom_layout* out,
  * capture, tight serving loops, harnesses that forbid hipMalloc. The same
  * collective as atom_collective, but a staged call takes its ring and flags
  * from a fixed array inside the library (ATOM_NOALLOC_RING_BYTES of ring, and
- * 2 MiB for the tagged words of small calls, per device, held from the
+ * 16 MiB for the tagged words, per device, held from the
  * library's load until the process ends) instead of
  * the growing workspace, so no call allocates. Without cfg->ring_slots the
  * ring depth is cut to what fits; a call whose chunk (as planned: a message

@@ -770,10 +770,10 @@ __global__ __launch_bounds__(MAXT) void k_snac(const SnacArgs a)
     }
 }
 
-// ---- small calls: the tagged ring --------------------------------------
-// A small call (one workgroup per task, so every chunk is staged once)
-// whose segments are all 16-byte aligned hands off through tagged words
-// instead of slot counts. Its piece's place in the tag region holds one
+// ---- calls that stage each chunk once: the tagged ring ------------------
+// A call whose ring would hold every chunk (no slot is reused; one
+// workgroup per task) and whose segments are all 16-byte aligned hands off
+// through tagged words instead of slot counts. Its piece's place in the tag region holds one
 // 64-bit pair per staged 4-byte word: the word in the low half, the call's
 // sequence number in the high half, written by one agent-scope 64-bit store
 // (a naturally aligned 64-bit access is single-copy atomic, and the
@@ -1021,7 +1021,7 @@ hipError_t launch_copy_t(const SnacArgs& a, int U, dim3 grid, dim3 block, hipStr
 // ---- the fixed workspace of atom_collective_noalloc ---------------------
 // Flags (the slot count words, the ticket, the error word and the
 // finished-workgroup count, each on its own 256-byte line, as in the
-// allocated workspace), the tagged ring of small calls (kTagBytes), then a
+// allocated workspace), the tagged ring (kTagBytes), then a
 // ring of kStaticRingBytes. Each device holds its own copy from the
 // library's load until the process ends.
 constexpr int64_t kFlagLine = kFlagStride * sizeof(unsigned long long);

@@ -138,7 +138,7 @@ struct SnacArgs {
     const void* src[kMaxRanks];        // inputs
     void* dst[kMaxRanks];              // outputs
     char* ring;                        // D slots of chunk_bytes
-    unsigned long long* tags;          // tagged ring of small calls (tagged): one
+    unsigned long long* tags;          // tagged ring (tagged calls): one
                                        // 64-bit pair per staged 4-byte word, the
                                        // word of chunk q's piece at byte b at pair
                                        // (q * chunk_bytes + b) / 4, the call's seq
@@ -181,10 +181,11 @@ struct SnacArgs {
     int32_t nt_store;
     int32_t static_tasks;              // 1: one workgroup per task, task = blockIdx.x
                                        // (small calls); 0: tasks claimed by ticket
-    int32_t tagged;                    // 1: small call on the tagged ring (one
-                                       // workgroup per task, every segment
-                                       // 16-byte aligned): the notify is the tag
-                                       // of each staged word; 0: ring + slot counts
+    int32_t tagged;                    // 1: a call on the tagged ring (each chunk
+                                       // staged once, one workgroup per task,
+                                       // every segment 16-byte aligned): the
+                                       // notify is the tag of each staged word;
+                                       // 0: ring + slot counts
     int32_t interleave;                // 1: every segment has the same number of
                                        // chunks and chunk q belongs to segment
                                        // q % nseg (sources staged side by side);

@@ -755,17 +755,27 @@ atom_status build_snac(Plan* p, int32_t sk, int P, void* const* ins, void* const
     // bounded either way. Saves the ticket atomic's round trip before the
     // first task and after the last.
     a.static_tasks = (!c.num_wgs && p->grid == a.ntasks && a.ntasks <= kSnacStaticTasks) ? 1 : 0;
-    // A small call stages each chunk once (its grid holds every task, so
-    // the ring holds every chunk). When every segment is 16-byte aligned
-    // and the staged bytes fit the tagged ring, the notify travels in the
-    // staged words' tags (k_snac_tagged): the producer neither waits for
-    // its stores to complete nor counts, and the consumer reads its words
-    // as it sees them instead of reading the ring after a count.
-    bool tag_ok = a.static_tasks && !(c.flags & ATOM_F_COUNTED) && piece % 1024 == 0 &&
+    // A call whose ring holds every chunk (no slot is reused), whose
+    // segments are all 16-byte aligned and whose staged bytes fit the
+    // tagged ring hands off through tagged words (k_snac_tagged): the notify
+    // travels in the staged words' tags, the producer neither waits for its
+    // stores to complete nor counts, and the consumer holds its words as it
+    // sees them instead of reading the ring after a count. One workgroup
+    // per task, task = blockIdx.x: producers never wait, and a consumer
+    // waits only for producers with smaller indices, which the in-order
+    // dispatch has started before it, so the grid need not fit the chip.
+    // Measured on MI355X (event-timed, staged AllGather): 256 KiB, 512 KiB
+    // and 1 MiB per rank 19.5, 23.4 and 26.9 us through the ticket and the
+    // counts.
+    bool tag_ok = !c.num_wgs && !(c.flags & ATOM_F_COUNTED) && q <= a.slots && piece % 1024 == 0 &&
                   chunk % piece == 0 && 2 * q * chunk <= kTagBytes;
     for (int s = 0; s < nseg && tag_ok; ++s)
         tag_ok = bytes[s] == 0 || (a.elem[s] == SE_VEC && a.head[s] == 0);
     a.tagged = tag_ok ? 1 : 0;
+    if (tag_ok) {
+        p->grid = a.ntasks;
+        a.static_tasks = 1;
+    }
     p->exec = reduce ? EX_SNAC_REDUCE : EX_SNAC_COPY;
     return ATOM_OK;
 }

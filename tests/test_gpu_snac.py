@@ -418,11 +418,12 @@ def test_tagged_calls_back_to_back(A):
              for i, (coll, n, dt) in enumerate([("ag", 4096, synth.BF16), ("ar", 512, synth.BF16),
                                                 ("rs", 4096, synth.F32), ("a2a", 512, synth.BF16),
                                                 ("ag", 65536, synth.BF16), ("rsv", 3000, synth.BF16),
-                                                ("ag", 1000, synth.F32)])]
+                                                ("ag", 1000, synth.F32), ("ag", 131072, synth.BF16),
+                                                ("ar", 65536, synth.F32), ("a2a", 16384, synth.BF16)])]
     big = Case(A, "ag", P, 1 << 20, synth.BF16, 0, seed=79)
     tagged = [c.plan(A.config(flags=A.F_STAGED)).snac_tagged for c in cases]
     say(f"tagged back to back: tagged={tagged}")
-    assert sum(tagged) >= 5
+    assert sum(tagged) >= 8
     for rep in range(3):
         for i, c in enumerate(cases):
             c.run(A.config(flags=A.F_STAGED))
@@ -432,3 +433,23 @@ def test_tagged_calls_back_to_back(A):
         big.run(A.config(flags=A.F_STAGED))
         big.check(f"rep {rep} large staged AllGather")
     _check_status(A, "tagged back to back")
+
+
+@pytest.mark.parametrize("coll,n", [("ag", 524288), ("ar", 131072), ("rs", 131072), ("a2a", 65536)])
+def test_tagged_medium_calls_under_jitter(A, coll, n):
+    """Calls of up to 8 MiB staged on the tagged ring run one workgroup per
+    task (here 512-1024 workgroups of 512 lanes, up to twice what the chip holds
+    at once): producers never wait, and a consumer waits only for producers
+    with smaller workgroup indices. Checked at natural timing and with every
+    producer and consumer delayed by a pseudo-random 0-40 us, twice each,
+    bit for bit against the oracle."""
+    P = 8
+    c = Case(A, coll, P, n, synth.BF16, 0, seed=90)
+    info = c.plan(A.config(flags=A.F_STAGED))
+    say(f"tagged medium {coll} n={n} tasks={info.snac_tasks} wgs={info.num_wgs}")
+    assert info.snac_tagged == 1 and info.num_wgs == info.snac_tasks > 256
+    for jit in (0, 40):
+        for rep in range(2):
+            c.run(A.config(flags=A.F_STAGED, jitter_us=jit, jitter_seed=31 + rep))
+            _check_status(A, f"tagged medium {coll} jitter={jit}")
+            c.check(f"tagged medium {coll} n={n} jitter={jit} rep={rep}")
