@@ -453,3 +453,54 @@ def test_tagged_medium_calls_under_jitter(A, coll, n):
             c.run(A.config(flags=A.F_STAGED, jitter_us=jit, jitter_seed=31 + rep))
             _check_status(A, f"tagged medium {coll} jitter={jit}")
             c.check(f"tagged medium {coll} n={n} jitter={jit} rep={rep}")
+
+
+@pytest.mark.parametrize("counted", [False, True])
+@pytest.mark.parametrize("dtype", [synth.BF16, synth.F32])
+def test_staged_ragged_last_segment(A, dtype, counted):
+    """A Zipf-like AllGatherV and ReduceScatterV whose partitions all start
+    16-byte aligned but whose last partition ends inside a 16-byte vector
+    (and one partition is empty): such a call stays on the vector path, on
+    the tagged ring unless ATOM_F_COUNTED asks for the counts, and the
+    consumer writes the last partial vector element by element. Bit for bit
+    against the oracle, with guard canaries around every output."""
+    P = 8
+    tdt = _tdt(dtype)
+    unit = 16 // (2 if dtype == synth.BF16 else 4)           # elements per 16 bytes
+    cnt = np.array([8, 16, 1, 0, 5, 2, 3, 0], np.int64) * unit
+    cnt[-1] = 13 if dtype == synth.BF16 else 7
+    T = int(cnt.sum())
+    cfg = A.config(flags=A.F_STAGED | (A.F_COUNTED if counted else 0))
+
+    def dev(a):
+        return empty_dev(1, tdt)[:0] if a.size == 0 else to_dev(a)[1]
+
+    # AllGatherV
+    zs = [synth.mixed_bits(950, k, int(cnt[k]), dtype) for k in range(P)]
+    dz = [dev(z) for z in zs]
+    fulls, outs = out_buffers([T] * P, tdt, GUARD)
+    st, info = A.atom_plan_query(A.layout(A.SHARD, dz, 0, cnt, 1), A.layout(A.GATHERED, outs, 0, None, 1),
+                                 A.OP_COPY, cfg)
+    say(f"ragged AGV dtype={dtype} counted={counted} tagged={info.snac_tagged}")
+    assert st == A.OK and info.vector_path == 1 and info.shifted == 0
+    assert info.snac_tagged == (0 if counted else 1)
+    A.all_gather_v(dz, outs, cnt, 1, cfg)
+    _check_status(A, "ragged AGV")
+    want = oracle.all_gather_v(zs)
+    for j in range(P):
+        assert_bits_equal(from_dev(outs[j]), want[j], f"ragged AGV out_{j}", nan_by_class=False)
+    check_guards(fulls, [T] * P, GUARD)
+    # ReduceScatterV
+    xs = [synth.mixed_bits(960, r, T, dtype, specials=False) for r in range(P)]
+    dx = [dev(x) for x in xs]
+    fulls, ys = out_buffers([int(c) for c in cnt], tdt, GUARD)
+    st, info = A.atom_plan_query(A.layout(A.PARTITIONED, dx, 0, cnt, 1), A.layout(A.SHARD, ys, 0, None, 1),
+                                 A.OP_SUM, cfg)
+    say(f"ragged RSV dtype={dtype} counted={counted} tagged={info.snac_tagged}")
+    assert st == A.OK and info.vector_path == 1 and info.snac_tagged == (0 if counted else 1)
+    A.reduce_scatter_v(dx, ys, cnt, 1, cfg)
+    _check_status(A, "ragged RSV")
+    want = oracle.reduce_scatter_v(xs, cnt)
+    for k in range(P):
+        _reduced(from_dev(ys[k]), want[k], f"ragged RSV y_{k}")
+    check_guards(fulls, [int(c) for c in cnt], GUARD)
