@@ -91,6 +91,10 @@ def parse():
                          "per-task device-clock stamps (AllGather 8 x 64 MiB and 8 x 1 GiB at each "
                          "chunk size and lead, composed AllReduce, Zipf RSV/AGV, 8 KiB calls); one "
                          "JSON line per run")
+    ap.add_argument("--ring-sweep", action="store_true",
+                    help="instead of the step: the staged AllGather of 8 x 64 MiB and 8 x 1 GiB "
+                         "at ring depths 2, 4, 8 and the default, each chunk size; one JSON line "
+                         "per point")
     ap.add_argument("--snac-sweep", action="store_true",
                     help="instead of the step: staged-path launch choices (chunk x lead x piece) "
                          "for the AllGather 8 x 64 MiB, composed AllReduce 8 x 256 MiB, Zipf RSV/AGV, "
@@ -128,6 +132,9 @@ def main():
         return
     if args.snac_trace:
         snac_trace(A, synth, torch, dev)
+        return
+    if args.ring_sweep:
+        ring_sweep(A, synth, torch, dev)
         return
     if args.snac_sweep:
         snac_sweep(A, synth, torch, dev)
@@ -826,6 +833,44 @@ def snac_sweep(A, synth, torch, dev):
         for lead in (D, D // 2, D // 4):
             point("ag_8x1GiB", L(A.SHARD, z, S // 2), L(A.GATHERED, o, S // 2), A.OP_COPY, 3,
                   chunk_bytes=chunk, snac_lead=lead)
+
+
+def ring_sweep(A, synth, torch, dev):
+    """Ring depth of the staged AllGather (the SNAC slots; the lead is half
+    the depth, pieces the default), cold as in snac_sweep: 8 x 64 MiB and
+    8 x 1 GiB partitions, chunks of 512 KiB, 1 MiB and 2 MiB, depths 2, 4, 8
+    and the library's default (a 32 MiB ring)."""
+    P, MiB = 8, 1 << 20
+    L = A.layout
+    scrub_a = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev)
+    scrub_b = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev)
+    for S, reps in ((64 * MiB, 7), (1024 * MiB, 3)):
+        z = [torch.empty(S // 2, dtype=torch.bfloat16, device=dev).uniform_(-1, 1) for _ in range(P)]
+        o = [torch.empty(P * S // 2, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+        li, lo = L(A.SHARD, z, S // 2), L(A.GATHERED, o, S // 2)
+        for chunk in (512 << 10, 1 << 20, 2 << 20):
+            for D in (2, 4, 8, 0):
+                cfg = A.config(flags=A.F_STAGED, chunk_bytes=chunk, ring_slots=D)
+                st, info = A.atom_plan_query(li, lo, A.OP_COPY, cfg)
+                assert st == A.OK, (S, chunk, D, st)
+                A.atom_collective(li, lo, A.OP_COPY, cfg)
+                ts = []
+                for _ in range(reps):
+                    scrub_b.copy_(scrub_a)
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    A.atom_collective(li, lo, A.OP_COPY, cfg)
+                    b.record()
+                    torch.cuda.synchronize()
+                    ts.append(a.elapsed_time(b))
+                assert A.atom_sync_status() == A.OK, (S, chunk, D)
+                ms = float(np.median(ts))
+                print(json.dumps({"ring_sweep": f"ag_8x{S >> 20}MiB", "chunk_bytes": chunk,
+                                  "ring_slots": int(info.ring_slots), "default_depth": D == 0,
+                                  "lead": int(info.snac_lead), "workgroups": int(info.num_wgs),
+                                  "ms": round(ms, 4),
+                                  "GBps": round(info.credited_bytes / ms / 1e6, 1)}), flush=True)
+        del z, o
 
 
 def sweep(A, synth, torch, dev):
