@@ -150,7 +150,7 @@ typedef struct atom_layout {
                                  call whose ring holds every chunk (each
                                  staged once), whose segments are all
                                  16-byte aligned, which stages at most
-                                 8 MiB and sets no num_wgs carries its
+                                 16 MiB and sets no num_wgs carries its
                                  notify in the staged
                                  data itself: each staged 4-byte word is
                                  written next to a tag holding the call's
@@ -302,7 +302,7 @@ atom_status atom_collective(const atom_layout* in, const atom_layout* out,
  * capture, tight serving loops, harnesses that forbid hipMalloc. The same
  * collective as atom_collective, but a staged call takes its ring and flags
  * from a fixed array inside the library (ATOM_NOALLOC_RING_BYTES of ring, and
- * 16 MiB for the tagged words, per device, held from the
+ * 32 MiB for the tagged words, per device, held from the
  * library's load until the process ends) instead of
  * the growing workspace, so no call allocates. Without cfg->ring_slots the
  * ring depth is cut to what fits; a call whose chunk (as planned: a message

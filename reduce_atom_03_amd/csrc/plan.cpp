@@ -766,7 +766,10 @@ atom_status build_snac(Plan* p, int32_t sk, int P, void* const* ins, void* const
     // dispatch has started before it, so the grid need not fit the chip.
     // Measured on MI355X (event-timed, staged AllGather): 256 KiB, 512 KiB
     // and 1 MiB per rank 19.5, 23.4 and 26.9 us through the ticket and the
-    // counts.
+    // counts. A staged word takes 8 bytes on the tagged ring instead of 4,
+    // so larger calls keep the counts: tagged / counted, AllGather of 8 x 2
+    // MiB (16 MiB staged) 41.3 / 44.8 us, of 8 x 4 MiB 77.6 / 72.2 us;
+    // AllReduce of 16 MiB 58.1 / 62.4 us, of 32 MiB 132.7 / 122.1 us.
     bool tag_ok = !c.num_wgs && !(c.flags & ATOM_F_COUNTED) && q <= a.slots && piece % 1024 == 0 &&
                   chunk % piece == 0 && 2 * q * chunk <= kTagBytes;
     for (int s = 0; s < nseg && tag_ok; ++s)

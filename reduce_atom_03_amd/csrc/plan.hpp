@@ -67,8 +67,8 @@ constexpr int64_t kSnacGrid = 512;                   // persistent SNAC workgrou
 constexpr int64_t kSlotPad = 256;                    // bytes past each ring slot's chunk (room for a
                                                      // piece staged 112 + d bytes in, d < 16)
 constexpr int64_t kSnacStaticTasks = 256;            // up to this many tasks: one workgroup each, no ticket
-constexpr int64_t kTagBytes = 16 << 20;              // tagged ring of staged calls that stage each
-                                                     // chunk once (8 bytes per staged 4): 8 MiB of
+constexpr int64_t kTagBytes = 32 << 20;              // tagged ring of staged calls that stage each
+                                                     // chunk once (8 bytes per staged 4): 16 MiB of
                                                      // staged data
 constexpr int64_t kMaxGrid = 1 << 20;                // a multiple of the XCD count
 constexpr int64_t kXcdCount = 8;                     // XCDs of an MI355X; workgroup w runs on XCD w mod 8

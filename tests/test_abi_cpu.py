@@ -379,9 +379,9 @@ def test_snac_piece_spreads_medium_messages():
         want_chunk = 16 * MiB if S >= 16 * MiB else -(-S // piece) * piece
         assert info.chunk_bytes == want_chunk, (S, info.chunk_bytes)
         tasks = 2 * info.num_chunks * (want_chunk // piece)
-        # the tagged hand-off (each chunk staged once, up to 8 MiB staged)
+        # the tagged hand-off (each chunk staged once, up to 16 MiB staged)
         # runs one workgroup per task; through the counts at most 512
-        assert info.snac_tagged == (8 * S <= 8 * MiB), (S, info.snac_tagged)
+        assert info.snac_tagged == (8 * S <= 16 * MiB), (S, info.snac_tagged)
         want = tasks if info.snac_tagged else min(512, tasks)
         assert info.num_wgs == want, (S, info.num_wgs, tasks)
 
@@ -618,7 +618,7 @@ def test_small_aligned_staged_calls_hand_off_through_tagged_words():
     """A staged call whose ring holds every chunk and whose segments are all
     16-byte aligned hands off through tagged words, one workgroup per task;
     ATOM_F_COUNTED, any segment off alignment, a ring too short to hold every
-    chunk, a caller's grid or more than 8 MiB staged keep the slot
+    chunk, a caller's grid or more than 16 MiB staged keep the slot
     counts."""
     P = 8
 
@@ -648,17 +648,17 @@ def test_small_aligned_staged_calls_hand_off_through_tagged_words():
     assert st == A.OK and info.num_wgs < info.snac_tasks and info.snac_tagged == 0
     st, info = ag(4096, A.config(flags=A.F_STAGED, num_wgs=16))
     assert st == A.OK and info.snac_tagged == 0
-    # beyond 256 tasks (256 KiB and 1 MiB per rank): still one workgroup
-    # per task on the tagged ring, which holds 8 MiB of staged data
-    for n in (131072, 524288):
+    # beyond 256 tasks (256 KiB, 1 MiB and 2 MiB per rank): still one
+    # workgroup per task on the tagged ring, which holds 16 MiB of staged data
+    for n in (131072, 524288, 1 << 20):
         st, info = ag(n, A.config(flags=A.F_STAGED))
         assert st == A.OK and info.snac_tasks > 256 and info.snac_tagged == 1, n
         assert info.num_wgs == info.snac_tasks
     # through the counts they take the ticket (more than 256 tasks)
     st, info = ag(131072, A.config(flags=A.F_STAGED | A.F_COUNTED))
     assert st == A.OK and info.snac_tasks > 256 and info.snac_tagged == 0
-    # more than the tagged ring holds (8 x 2 MiB = 16 MiB staged): the ticket
-    st, info = ag(1 << 20, A.config(flags=A.F_STAGED))
+    # more than the tagged ring holds (8 x 4 MiB = 32 MiB staged): the ticket
+    st, info = ag(2 << 20, A.config(flags=A.F_STAGED))
     assert st == A.OK and info.snac_tagged == 0 and info.num_wgs < info.snac_tasks
     # a staged AllReduce of 8 MiB per rank stages 8 MiB: tagged
     st, info = Q(A.PARTITIONED, A.GATHERED, A.OP_SUM, P=P, n=(8 << 20) // 2 // P,

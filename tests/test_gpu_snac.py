@@ -435,9 +435,10 @@ def test_tagged_calls_back_to_back(A):
     _check_status(A, "tagged back to back")
 
 
-@pytest.mark.parametrize("coll,n", [("ag", 524288), ("ar", 131072), ("rs", 131072), ("a2a", 65536)])
+@pytest.mark.parametrize("coll,n", [("ag", 524288), ("ag", 1048576), ("ar", 131072), ("rs", 131072),
+                                    ("a2a", 65536)])
 def test_tagged_medium_calls_under_jitter(A, coll, n):
-    """Calls of up to 8 MiB staged on the tagged ring run one workgroup per
+    """Calls of up to 16 MiB staged on the tagged ring run one workgroup per
     task (here 512-1024 workgroups of 512 lanes, up to twice what the chip holds
     at once): producers never wait, and a consumer waits only for producers
     with smaller workgroup indices. Checked at natural timing and with every

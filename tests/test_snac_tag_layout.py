@@ -6,7 +6,7 @@ in 64-bit pair 256 * (v // 64) + 64 * j + v % 64 of the piece's place
 pair (q * chunk + b) / 4. This model replays that arithmetic and checks that
 every staged word of a call has a pair of its own, that a piece's pairs stay
 inside its place (so two pieces never share a pair), that the whole call
-fits the tagged ring (16 MiB: 8 bytes per staged 4), and that each wave-wide
+fits the tagged ring (32 MiB: 8 bytes per staged 4), and that each wave-wide
 access (64 lanes, one word j) covers 64 adjacent pairs, i.e. whole 128-byte
 lines."""
 
@@ -14,7 +14,7 @@ import random
 
 import pytest
 
-TAG_BYTES = 16 << 20
+TAG_BYTES = 32 << 20
 
 
 def tag_pair(v, j):
