@@ -148,8 +148,9 @@ typedef struct atom_layout {
 #define ATOM_F_COUNTED 0x8u   /* staged calls: always notify through the
                                  ring slots' count words. Default: a staged
                                  call whose ring holds every chunk (each
-                                 staged once), whose segments are all
-                                 16-byte aligned, which stages at most
+                                 staged once), each of whose segments has
+                                 its sources and destinations at one offset
+                                 from 16-byte alignment, which stages at most
                                  16 MiB and sets no num_wgs carries its
                                  notify in the staged
                                  data itself: each staged 4-byte word is

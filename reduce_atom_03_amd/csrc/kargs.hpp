@@ -140,9 +140,8 @@ struct SnacArgs {
     char* ring;                        // D slots of chunk_bytes
     unsigned long long* tags;          // tagged ring (tagged calls): one
                                        // 64-bit pair per staged 4-byte word, the
-                                       // word of chunk q's piece at byte b at pair
-                                       // (q * chunk_bytes + b) / 4, the call's seq
-                                       // in the high half
+                                       // call's seq in the high half; piece i of
+                                       // chunk q at pair (q * pieces + i) * tag_place
     unsigned long long* counts;        // per slot (stride kFlagStride), over every
                                        // chunk the slot has held in this call:
                                        // pieces staged (low 32 bits) and pieces
@@ -159,6 +158,9 @@ struct SnacArgs {
     int64_t slot_bytes;                // ring slot stride: chunk_bytes plus padding
     int64_t piece_bytes;               // chunk_bytes / pieces
     int64_t nchunks;                   // chunks of every segment together
+    int64_t tag_place;                 // tagged calls: pairs per piece place, 4 per
+                                       // 16-byte vector (a piece's vectors, plus 64
+                                       // when a segment sits off 16-byte alignment)
     int64_t ntasks;                    // 2 * nchunks * pieces
     int64_t wait_ticks;                // bound of one wait: microseconds when
                                        // planned, device-clock ticks at launch
@@ -183,7 +185,7 @@ struct SnacArgs {
                                        // (small calls); 0: tasks claimed by ticket
     int32_t tagged;                    // 1: a call on the tagged ring (each chunk
                                        // staged once, one workgroup per task,
-                                       // every segment 16-byte aligned): the
+                                       // every segment on the vector path): the
                                        // notify is the tag of each staged word;
                                        // 0: ring + slot counts
     int32_t interleave;                // 1: every segment has the same number of

@@ -755,9 +755,10 @@ atom_status build_snac(Plan* p, int32_t sk, int P, void* const* ins, void* const
     // bounded either way. Saves the ticket atomic's round trip before the
     // first task and after the last.
     a.static_tasks = (!c.num_wgs && p->grid == a.ntasks && a.ntasks <= kSnacStaticTasks) ? 1 : 0;
-    // A call whose ring holds every chunk (no slot is reused), whose
-    // segments are all 16-byte aligned and whose staged bytes fit the
-    // tagged ring hands off through tagged words (k_snac_tagged): the notify
+    // A call whose ring holds every chunk (no slot is reused), each of whose
+    // segments has every stream at one offset from 16-byte alignment (the
+    // vector path, SE_VEC) and whose staged bytes fit the tagged ring hands
+    // off through tagged words (k_snac_tagged): the notify
     // travels in the staged words' tags, the producer neither waits for its
     // stores to complete nor counts, and the consumer holds its words as it
     // sees them instead of reading the ring after a count. One workgroup
@@ -770,10 +771,18 @@ atom_status build_snac(Plan* p, int32_t sk, int P, void* const* ins, void* const
     // so larger calls keep the counts: tagged / counted, AllGather of 8 x 2
     // MiB (16 MiB staged) 41.3 / 44.8 us, of 8 x 4 MiB 77.6 / 72.2 us;
     // AllReduce of 16 MiB 58.1 / 62.4 us, of 32 MiB 132.7 / 122.1 us.
+    // A segment whose streams share an offset d from 16-byte alignment is
+    // staged in the aligned vectors enclosing each piece: one vector more
+    // than the piece at most, so its place gets one more group of 64.
     bool tag_ok = !c.num_wgs && !(c.flags & ATOM_F_COUNTED) && q <= a.slots && piece % 1024 == 0 &&
-                  chunk % piece == 0 && 2 * q * chunk <= kTagBytes;
-    for (int s = 0; s < nseg && tag_ok; ++s)
-        tag_ok = bytes[s] == 0 || (a.elem[s] == SE_VEC && a.head[s] == 0);
+                  chunk % piece == 0;
+    bool off = false;
+    for (int s = 0; s < nseg && tag_ok; ++s) {
+        tag_ok = bytes[s] == 0 || a.elem[s] == SE_VEC;
+        off = off || (bytes[s] > 0 && a.head[s] != 0);
+    }
+    a.tag_place = 4 * (piece / kVecBytes + (off ? 64 : 0));
+    tag_ok = tag_ok && q * (chunk / piece) * a.tag_place * 8 <= kTagBytes;
     a.tagged = tag_ok ? 1 : 0;
     if (tag_ok) {
         p->grid = a.ntasks;

@@ -615,9 +615,10 @@ def test_staged_segments_at_a_common_offset_stay_vectorized():
 
 
 def test_small_aligned_staged_calls_hand_off_through_tagged_words():
-    """A staged call whose ring holds every chunk and whose segments are all
-    16-byte aligned hands off through tagged words, one workgroup per task;
-    ATOM_F_COUNTED, any segment off alignment, a ring too short to hold every
+    """A staged call whose ring holds every chunk and whose segments each
+    have every stream at one offset from 16-byte alignment hands off through
+    tagged words, one workgroup per task; ATOM_F_COUNTED, a segment whose
+    streams sit at different offsets, a ring too short to hold every
     chunk, a caller's grid or more than 16 MiB staged keep the slot
     counts."""
     P = 8
@@ -640,8 +641,10 @@ def test_small_aligned_staged_calls_hand_off_through_tagged_words():
     st, info = Q(A.PARTITIONED, A.GATHERED, A.OP_SUM, P=P, n=512, dtype=A.DT_F32,
                  cfg=A.config(flags=A.F_STAGED))
     assert st == A.OK and info.snac_tagged == 1
-    # off alignment (common offset, or shifted): the slot counts
-    assert ag(4096, A.config(flags=A.F_STAGED), 2, 2)[1].snac_tagged == 0
+    # every stream at one common offset: still tagged (the aligned vectors
+    # enclosing each piece are staged); sources and outputs at different
+    # offsets (the shifted path): the slot counts
+    assert ag(4096, A.config(flags=A.F_STAGED), 2, 2)[1].snac_tagged == 1
     assert ag(4096, A.config(flags=A.F_STAGED), 0, 2)[1].snac_tagged == 0
     # the ticket: a 2-slot ring, or a caller's grid
     st, info = ag(4096, A.config(flags=A.F_STAGED, ring_slots=2))

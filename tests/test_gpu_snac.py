@@ -505,3 +505,69 @@ def test_staged_ragged_last_segment(A, dtype, counted):
     for k in range(P):
         _reduced(from_dev(ys[k]), want[k], f"ragged RSV y_{k}")
     check_guards(fulls, [int(c) for c in cnt], GUARD)
+
+
+@pytest.mark.parametrize("coll,n,dtype,skew", [("ag", 4096, synth.BF16, 1), ("ag", 4096, synth.BF16, 3),
+                                               ("ar", 512, synth.BF16, 1), ("rs", 4096, synth.F32, 1),
+                                               ("a2a", 2048, synth.BF16, 3), ("ag", 131072, synth.BF16, 5),
+                                               ("ar", 131072, synth.F32, 3)])
+def test_tagged_calls_off_alignment(A, coll, n, dtype, skew):
+    """Every buffer the same few elements off 16-byte alignment: the staged
+    call stays on the tagged ring, staging the aligned vectors that enclose
+    each piece and writing only the piece's bytes. At natural timing and
+    with a 0-40 us jitter, bit for bit against the oracle, guard canaries
+    intact."""
+    P = 8
+    c = Case(A, coll, P, n, dtype, skew, seed=95)
+    info = c.plan(A.config(flags=A.F_STAGED))
+    say(f"tagged off-alignment {coll} n={n} skew={skew} tagged={info.snac_tagged} tasks={info.snac_tasks}")
+    assert info.snac_tagged == 1 and info.vector_path == 1 and info.shifted == 0
+    for jit in (0, 40):
+        c.run(A.config(flags=A.F_STAGED, jitter_us=jit, jitter_seed=3))
+        _check_status(A, f"tagged off-alignment {coll} skew={skew}")
+        c.check(f"tagged off-alignment {coll} n={n} skew={skew} jitter={jit}")
+
+
+@pytest.mark.parametrize("skew", [1, 3])
+def test_tagged_offset_uneven_segments(A, skew):
+    """An AllGatherV and a ReduceScatterV whose every buffer sits skew
+    elements off 16-byte alignment and whose partitions differ in size (in
+    multiples of 16 bytes, so every partition starts at that offset): the
+    call is tagged, short partitions have empty pieces in their chunk (they
+    stage nothing), and every output matches the oracle bit for bit with its
+    guard canaries intact."""
+    P = 8
+    tdt = _tdt(synth.BF16)
+    cnt = np.array([32768, 8, 512, 0, 64, 3000, 24, 1000], np.int64) // 8 * 8
+    T = int(cnt.sum())
+    cfg = A.config(flags=A.F_STAGED)
+
+    def dev(a):
+        return empty_dev(1, tdt)[:0] if a.size == 0 else to_dev(a, pad_before=skew)[1]
+
+    zs = [synth.mixed_bits(970 + skew, k, int(cnt[k]), synth.BF16) for k in range(P)]
+    dz = [dev(z) for z in zs]
+    fulls, outs = out_buffers([T] * P, tdt, GUARD + skew)
+    st, info = A.atom_plan_query(A.layout(A.SHARD, dz, 0, cnt, 1), A.layout(A.GATHERED, outs, 0, None, 1),
+                                 A.OP_COPY, cfg)
+    say(f"tagged offset uneven AGV skew={skew} tagged={info.snac_tagged} chunk={info.chunk_bytes}")
+    assert st == A.OK and info.snac_tagged == 1 and info.shifted == 0
+    A.all_gather_v(dz, outs, cnt, 1, cfg)
+    _check_status(A, "tagged offset uneven AGV")
+    want = oracle.all_gather_v(zs)
+    for j in range(P):
+        assert_bits_equal(from_dev(outs[j]), want[j], f"uneven AGV out_{j}", nan_by_class=False)
+    check_guards(fulls, [T] * P, GUARD + skew)
+    xs = [synth.mixed_bits(980 + skew, r, T, synth.BF16, specials=False) for r in range(P)]
+    dx = [dev(x) for x in xs]
+    fulls, ys = out_buffers([int(c) for c in cnt], tdt, GUARD + skew)
+    st, info = A.atom_plan_query(A.layout(A.PARTITIONED, dx, 0, cnt, 1), A.layout(A.SHARD, ys, 0, None, 1),
+                                 A.OP_SUM, cfg)
+    say(f"tagged offset uneven RSV skew={skew} tagged={info.snac_tagged}")
+    assert st == A.OK and info.snac_tagged == 1 and info.shifted == 0
+    A.reduce_scatter_v(dx, ys, cnt, 1, cfg)
+    _check_status(A, "tagged offset uneven RSV")
+    want = oracle.reduce_scatter_v(xs, cnt)
+    for k in range(P):
+        _reduced(from_dev(ys[k]), want[k], f"uneven RSV y_{k}")
+    check_guards(fulls, [int(c) for c in cnt], GUARD + skew)

@@ -64,3 +64,48 @@ def test_a_wave_access_covers_whole_lines():
             ps = sorted(tag_pair(64 * w + lane, j) for lane in range(64))
             assert ps == list(range(ps[0], ps[0] + 64))
             assert (8 * ps[0]) % 128 == 0           # 512 bytes from a line start
+
+
+def stage_and_consume(seg_bytes, chunk, piece, d):
+    """A segment whose streams sit d bytes past a 16-byte boundary: each piece
+    is staged in the aligned 16-byte vectors that enclose it (vector v holds
+    piece bytes [16 v - d, 16 v - d + 16)), in pairs tag_pair(v, j) of a
+    place of tag_place pairs, and the consumer writes piece bytes [p0, p1)
+    of each vector. Returns {segment byte: (pair, byte in pair)} of every
+    byte written, and the largest pair used per place."""
+    place = 4 * (piece // 16 + (64 if d else 0))
+    written, top = {}, 0
+    for q, cbeg in enumerate(range(0, seg_bytes, chunk)):
+        clen = min(chunk, seg_bytes - cbeg)
+        for i, pbeg in enumerate(range(0, chunk, piece)):
+            plen = max(0, min(piece, clen - pbeg))
+            base = (q * (chunk // piece) + i) * place
+            nv = (d + plen + 15) // 16 if plen > 0 else 0
+            for v in range(nv):
+                # the enclosing vector's 16 source bytes hold a segment byte
+                lo = cbeg + pbeg + 16 * v - d
+                assert lo + 16 > 0 and lo < seg_bytes
+            for v in range(nv):
+                p0 = d if v == 0 else 0
+                p1 = min(16, d + plen - 16 * v)
+                for b in range(p0, p1):
+                    pair = base + tag_pair(v, b // 4)
+                    assert base <= pair < base + place
+                    top = max(top, pair - base)
+                    sb = cbeg + pbeg + 16 * v - d + b     # segment byte
+                    assert sb not in written
+                    written[sb] = (pair, b % 4)
+    return written, top, place
+
+
+@pytest.mark.parametrize("d", [0, 2, 4, 6, 8, 14])
+def test_offset_segments_write_every_byte_once(d):
+    rng = random.Random(d)
+    for _ in range(25):
+        piece = rng.choice([8 << 10, 16 << 10])
+        chunk = piece * rng.choice([1, 2, 4])
+        seg = 2 * rng.randrange(1, 2 * chunk)           # last chunks short: empty pieces
+        written, top, place = stage_and_consume(seg, chunk, piece, d)
+        assert sorted(written) == list(range(seg))
+        # the enclosing vectors need the extra group only when d > 0
+        assert top < place and (d == 0 or top >= 4 * (piece // 16) - 1 or seg < piece)
