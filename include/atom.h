@@ -161,8 +161,10 @@ typedef struct atom_layout {
                                  ignored by zero-staging calls. */
 typedef struct atom_config {
     int64_t chunk_bytes;       /* SNAC chunk (notify unit); power of two in
-                                  [64 KiB, 16 MiB]; default 512 KiB for
-                                  AllGather, 2 MiB for AllReduce. A partition
+                                  [64 KiB, 16 MiB]; default: a copying stage
+                                  (AllGather(V), AllToAll(V)) 512 KiB, 2 MiB
+                                  when its largest segment is at least
+                                  256 MiB; a reducing one 2 MiB. A partition
                                   smaller than the chunk is staged as one
                                   chunk of whole pieces (plan_query reports
                                   the chunk used). */

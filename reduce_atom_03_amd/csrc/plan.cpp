@@ -637,9 +637,16 @@ atom_status build_snac(Plan* p, int32_t sk, int P, void* const* ins, void* const
     if (total == 0)
         return ATOM_OK;
     // Chunk: the caller's, else the one measured best on MI355X for the
-    // stage (a copying stage 512 KiB, a reducing one 2 MiB: both in the
-    // 512 KiB - 2 MiB range of Table 3's bandwidth-delay rule).
-    int64_t chunk = c.chunk_set ? c.chunk : (reduce ? kDefaultChunkAllReduce : kDefaultChunkAllGather);
+    // stage (a copying stage 512 KiB, 2 MiB once its largest segment reaches
+    // 256 MiB; a reducing one 2 MiB: all in the 512 KiB - 2 MiB range of
+    // Table 3's bandwidth-delay rule). The staged AllGather, 512 KiB / 2 MiB
+    // chunks: 8 x 64 MiB 0.924 / 0.926 ms cold; 8 x 1 GiB 13.77 / 13.72 ms
+    // cold and 13.95 / 13.69 ms in a warm size sweep; 8 x 256 MiB 3.51 /
+    // 3.44 ms warm.
+    int64_t chunk = c.chunk_set ? c.chunk
+                    : reduce    ? kDefaultChunkAllReduce
+                    : largest >= kHugeCopySegment ? kHugeCopyChunk
+                                                  : kDefaultChunkAllGather;
     // Piece (the task granule): the caller's, else the largest power of two
     // from 8 KiB to 64 KiB (32 KiB for a copying stage) that still gives
     // about one persistent grid's worth of staging tasks (total / piece >=

@@ -54,6 +54,8 @@ struct Plan : PlanHead {
 
 // Defaults and limits.
 constexpr int64_t kDefaultChunkAllGather = 512 << 10; // staged defaults, measured on MI355X
+constexpr int64_t kHugeCopySegment = 256 << 20;      // copying stage: from this largest segment up,
+constexpr int64_t kHugeCopyChunk = 2 << 20;          // 2 MiB chunks
 constexpr int64_t kDefaultChunkAllReduce = 2 << 20;
 constexpr int64_t kMinChunk = 64 << 10;
 constexpr int64_t kMaxChunk = 16 << 20;

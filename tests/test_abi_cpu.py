@@ -304,6 +304,11 @@ def test_snac_default_chunk_per_collective():
     st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=8, n=S // 2, cfg=A.config(flags=A.F_STAGED),
                  ins=fake(8, S), outs=fake(8, 8 * S, start=BASE + (1 << 40)))
     assert st == A.OK and info.chunk_bytes == 512 << 10 and info.ring_slots == 64
+    # a copying stage whose largest segment reaches 256 MiB: 2 MiB chunks
+    for Sk, chunk in ((128 * MiB, 512 << 10), (256 * MiB - 2, 512 << 10), (256 * MiB, 2 * MiB)):
+        st, info = Q(A.SHARD, A.GATHERED, A.OP_COPY, P=8, n=Sk // 2, cfg=A.config(flags=A.F_STAGED),
+                     ins=fake(8, Sk), outs=fake(8, 8 * Sk, start=BASE + (1 << 40)))
+        assert st == A.OK and info.chunk_bytes == chunk, Sk
     st, info = Q(A.PARTITIONED, A.GATHERED, A.OP_SUM, P=8, n=S // 2 // 8,
                  cfg=A.config(flags=A.F_STAGED), ins=fake(8, S),
                  outs=fake(8, S, start=BASE + (1 << 40)))
